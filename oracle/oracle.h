@@ -1,0 +1,122 @@
+/*
+ * oracle.h — plain, slow, single-threaded CPU reference of one MoE layer's
+ * routed-expert FFN with int4 experts and Q8_0-style int8 activations.
+ *
+ * TEST INFRASTRUCTURE ONLY. Only the tests, the smoke check and the CPU
+ * baseline leg of the benchmark may load or call this library. The GPU
+ * library never calls it, includes it or shares code with it.
+ *
+ * Sources (the pages on the colibri engine):
+ *   [P1 s3.1]  colibri architecture overview, section 3.1 "extreme quantisation":
+ *              int4 packed = two 4-bit values per byte, one f32 scale per row;
+ *              dequantise on use; the IDOT path quantises activations to int8
+ *              and takes integer dot products (dot_i4i8).
+ *   [P1 s4]    same page, section 4 layer figure: moe = sigmoid routing + expert
+ *              compute + shared expert; kernel layer matmul_i4, dot_i4i8, rmsnorm.
+ *   [P1 s5]    same page, section 5 token lifecycle: sigmoid route top-8,
+ *              gate/up/SiLU/down expert matmuls on the IDOT path, shared expert.
+ *   [P2 how]   README (zh-TW), "how it works": a batch reads each distinct expert
+ *              once (batch union); placement never changes routing or precision.
+ *   [P3 impl]  ai4coding.ru summary, "what is implemented": DeepSeek-V3-style
+ *              sigmoid router, shared expert, Q8_0-style int8 activations.
+ * Where the pages leave a step open, the reading taken is stated at the
+ * function. Summations run in double, in index order.
+ *
+ * Parity pins (tests/test_oracle_*.py) tie every function here to something
+ * other than itself: exact round trips, exactly representable special cases
+ * that reduce to an integer matmul, brute force over all expert subsets,
+ * closed forms and the statistical rounding-error law.
+ */
+#ifndef COLI_ORACLE_H
+#define COLI_ORACLE_H
+#include <stdint.h>
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* O1 [P1 s3.1] int4 pack, per row: d = absmax/7 (f32), id = 1/d (0 if d == 0),
+ * code = clamp(rint(w*id), -8, 7), w*id a single f32 product and rint
+ * rounding half to even (an infinite product clamps; a NaN product, only
+ * possible for w == 0 with id == inf, gives 0). Byte j of a row holds element 2j
+ * in bits 0-3 and element 2j+1 in bits 4-7, as 4-bit two's complement.
+ * q: [rows][cols/2], s: [rows]. cols must be even. */
+void oracle_pack_int4_rows(const float *w, int rows, int cols, uint8_t *q, float *s);
+
+/* O2 [P1 s3.1] decode one nibble: hi = 0 -> bits 0-3, hi = 1 -> bits 4-7. */
+int oracle_nibble(uint8_t byte, int hi);
+
+/* O2 [P1 s3.1] dequantise on use: w~[r][c] = s[r] * code[r][c] (double). */
+void oracle_unpack_int4_rows(const uint8_t *q, const float *s, int rows, int cols, double *w);
+
+/* O3 [P3 impl] Q8_0-style activation quantisation in 32-wide blocks:
+ * d_b = absmax_b/127 (f32), id = 1/d_b (0 if d_b == 0),
+ * code = clamp(rint(x*id), -127, 127) (same rounding and NaN rule as O1).
+ * q: [n], d: [n/32]. n must be a multiple of 32. */
+void oracle_quant_q8(const float *x, int n, int8_t *q, float *d);
+
+/* O4 [P1 s3.1, dot_i4i8] exact int32 block dots S[r][b] = sum_{k in block b}
+ * code4[r][k] * q8[k]. S: [rows][cols/32]. */
+void oracle_block_dots(const uint8_t *q4, const int8_t *q8, int rows, int cols, int32_t *S);
+
+/* O5 [P1 s3.1] IDOT row product: out[r] = (float)(s4[r] * sum_b d8[b]*S[r][b]),
+ * the block sum taken in double in block order. */
+void oracle_rowdot(const uint8_t *q4, const float *s4, const int8_t *q8, const float *d8,
+                   int rows, int cols, float *out);
+
+/* O6 [P3 impl, P1 s5] DeepSeek-V3-style sigmoid router for T tokens:
+ * z = W x (double), s = 1/(1+exp(-z)), key = s + b (bias used for selection
+ * only). With n_group > 1, E is split into n_group equal groups, a group's
+ * score is the sum of its two largest keys, the topk_group best groups are
+ * kept and experts of the others are not eligible. The top_k eligible keys
+ * are taken, largest first, equal keys to the lower expert index. Weights:
+ * w_j = route_scale * s_{e_j} / sum_j s_{e_j} (double, then f32).
+ * W: [E][H], b: [E], x: [T][H]; idx, w: [T][top_k]; keys (optional): [T][E]. */
+int oracle_route(const float *W, const float *b, const float *x, int T, int H, int E, int top_k,
+                 int n_group, int topk_group, float route_scale, int32_t *idx, float *w,
+                 double *keys);
+
+/* O7 [P1 s5] one expert on one token, IDOT path: g = O5(gate, Q8(x)),
+ * u = O5(up, Q8(x)), h = (float)(silu(g)*u) with silu(g) = g/(1+exp(-g)) in
+ * double, hq = O3(h), y = O5(down, hq). xq/xs are the token's Q8(x).
+ * gate/up: [I][H/2] + [I] scales; down: [H][I/2] + [H] scales.
+ * g, u, h, hq, hs may be NULL; otherwise g,u,h: [I], hq: [I], hs: [I/32]. */
+void oracle_expert(const uint8_t *gate_q, const float *gate_s, const uint8_t *up_q, const float *up_s,
+                   const uint8_t *down_q, const float *down_s, int H, int I,
+                   const int8_t *xq, const float *xs, float *y,
+                   float *g, float *u, float *h, int8_t *hq, float *hs);
+
+/* O8 [P1 s5, P3 impl] combine for one token: y = (float)(sum_j w_j*y_j + y_shared),
+ * summed in double in j order, the shared expert (weight 1) last; y_shared may
+ * be NULL (no shared expert). y_routed: [k][H]. */
+void oracle_combine(const float *y_routed, const float *w, int k, const float *y_shared, int H,
+                    float *y);
+
+/* O9 [P1 s4, rmsnorm] out = (float)(x * gamma / sqrt(mean(x^2) + eps)) per token,
+ * mean in double. */
+void oracle_rmsnorm(const float *x, const float *gamma, int T, int H, float eps, float *out);
+
+/* O10 [P1 s3.1] fp reference without activation quantisation: dequantised
+ * weights (double), unquantised x and h, all in double. Measures the IDOT
+ * error; not a parity target. y: [H] double. */
+void oracle_expert_dense(const uint8_t *gate_q, const float *gate_s, const uint8_t *up_q,
+                         const float *up_s, const uint8_t *down_q, const float *down_s, int H, int I,
+                         const float *x, double *y);
+
+/* A whole layer, every expert in host memory. Expert e's matrices start at
+ * gate_q + e*I*H/2 (etc.); the shared expert is index E when has_shared. */
+typedef struct oracle_layer {
+    int H, I, E, top_k, n_group, topk_group, has_shared;
+    float route_scale;
+    const float *router_w, *router_b;
+    const uint8_t *gate_q, *up_q, *down_q;
+    const float *gate_s, *up_s, *down_s;
+} oracle_layer;
+
+/* O6 -> O3 -> O7 per selected expert (+ shared) -> O8, for T tokens.
+ * idx/w (optional) receive the routing. Returns 0, or -1 on bad arguments. */
+int oracle_moe_forward(const oracle_layer *L, const float *x, int T, float *y, int32_t *idx, float *w);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

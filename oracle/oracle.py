@@ -1,0 +1,208 @@
+"""ctypes wrapper of the CPU oracle (liboracle.so) with numpy conveniences.
+
+TEST INFRASTRUCTURE ONLY: imported by the tests, the smoke check and the
+benchmark's CPU-baseline leg. The GPU library and its Python binding never
+import this module.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+_L = None
+
+
+def _lib():
+    global _L
+    if _L is None:
+        path = os.path.join(HERE, "liboracle.so")
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is not built; run __graft_entry__.build()")
+        L = ctypes.CDLL(path)
+        P = ctypes.c_void_p
+        i, f = ctypes.c_int, ctypes.c_float
+        L.oracle_pack_int4_rows.argtypes = [P, i, i, P, P]
+        L.oracle_nibble.argtypes = [ctypes.c_uint8, i]
+        L.oracle_nibble.restype = i
+        L.oracle_unpack_int4_rows.argtypes = [P, P, i, i, P]
+        L.oracle_quant_q8.argtypes = [P, i, P, P]
+        L.oracle_block_dots.argtypes = [P, P, i, i, P]
+        L.oracle_rowdot.argtypes = [P, P, P, P, i, i, P]
+        L.oracle_route.argtypes = [P, P, P, i, i, i, i, i, i, f, P, P, P]
+        L.oracle_route.restype = i
+        L.oracle_expert.argtypes = [P, P, P, P, P, P, i, i, P, P, P, P, P, P, P, P]
+        L.oracle_combine.argtypes = [P, P, i, P, i, P]
+        L.oracle_rmsnorm.argtypes = [P, P, i, i, f, P]
+        L.oracle_expert_dense.argtypes = [P, P, P, P, P, P, i, i, P, P]
+        L.oracle_moe_forward.argtypes = [P, P, i, P, P, P]
+        L.oracle_moe_forward.restype = i
+        _L = L
+    return _L
+
+
+def _p(a: Optional[np.ndarray]):
+    return None if a is None else ctypes.c_void_p(a.ctypes.data)
+
+
+def _c(a, dtype):
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+# ------------------------------------------------------------------ O1 / O2
+def pack_int4_rows(w: np.ndarray):
+    w = _c(w, np.float32)
+    rows, cols = w.shape
+    q = np.empty((rows, cols // 2), dtype=np.uint8)
+    s = np.empty(rows, dtype=np.float32)
+    _lib().oracle_pack_int4_rows(_p(w), rows, cols, _p(q), _p(s))
+    return q, s
+
+
+def nibble(byte: int, hi: int) -> int:
+    return int(_lib().oracle_nibble(byte, hi))
+
+
+def unpack_int4_rows(q: np.ndarray, s: np.ndarray) -> np.ndarray:
+    q = _c(q, np.uint8)
+    s = _c(s, np.float32)
+    rows, half = q.shape
+    out = np.empty((rows, 2 * half), dtype=np.float64)
+    _lib().oracle_unpack_int4_rows(_p(q), _p(s), rows, 2 * half, _p(out))
+    return out
+
+
+# ----------------------------------------------------------------------- O3
+def quant_q8(x: np.ndarray):
+    x = _c(x, np.float32)
+    n = x.size
+    q = np.empty(x.shape, dtype=np.int8)
+    d = np.empty(x.shape[:-1] + (x.shape[-1] // 32,), dtype=np.float32)
+    _lib().oracle_quant_q8(_p(x), n, _p(q), _p(d))
+    return q, d
+
+
+# ------------------------------------------------------------------ O4 / O5
+def block_dots(q4: np.ndarray, q8: np.ndarray) -> np.ndarray:
+    q4 = _c(q4, np.uint8)
+    q8 = _c(q8, np.int8)
+    rows, half = q4.shape
+    S = np.empty((rows, 2 * half // 32), dtype=np.int32)
+    _lib().oracle_block_dots(_p(q4), _p(q8), rows, 2 * half, _p(S))
+    return S
+
+
+def rowdot(q4, s4, q8, d8) -> np.ndarray:
+    q4 = _c(q4, np.uint8)
+    rows, half = q4.shape
+    out = np.empty(rows, dtype=np.float32)
+    _lib().oracle_rowdot(_p(q4), _p(_c(s4, np.float32)), _p(_c(q8, np.int8)), _p(_c(d8, np.float32)),
+                         rows, 2 * half, _p(out))
+    return out
+
+
+# ----------------------------------------------------------------------- O6
+def route(W, b, x, top_k: int, n_group: int = 1, topk_group: int = 1, route_scale: float = 1.0,
+          want_keys: bool = False):
+    W = _c(W, np.float32)
+    b = _c(b, np.float32)
+    x = _c(np.atleast_2d(x), np.float32)
+    E, H = W.shape
+    T = x.shape[0]
+    idx = np.empty((T, top_k), dtype=np.int32)
+    w = np.empty((T, top_k), dtype=np.float32)
+    keys = np.empty((T, E), dtype=np.float64) if want_keys else None
+    rc = _lib().oracle_route(_p(W), _p(b), _p(x), T, H, E, top_k, n_group, topk_group,
+                             route_scale, _p(idx), _p(w), _p(keys))
+    if rc != 0:
+        raise ValueError("oracle_route rejected its arguments")
+    return (idx, w, keys) if want_keys else (idx, w)
+
+
+# ----------------------------------------------------------------------- O7
+@dataclass
+class ExpertOut:
+    y: np.ndarray
+    g: np.ndarray
+    u: np.ndarray
+    h: np.ndarray
+    hq: np.ndarray
+    hs: np.ndarray
+
+
+def expert(gate_q, gate_s, up_q, up_s, down_q, down_s, xq, xs) -> ExpertOut:
+    gate_q = _c(gate_q, np.uint8)
+    I, Hh = gate_q.shape
+    H = 2 * Hh
+    o = ExpertOut(y=np.empty(H, np.float32), g=np.empty(I, np.float32), u=np.empty(I, np.float32),
+                  h=np.empty(I, np.float32), hq=np.empty(I, np.int8), hs=np.empty(I // 32, np.float32))
+    _lib().oracle_expert(_p(gate_q), _p(_c(gate_s, np.float32)), _p(_c(up_q, np.uint8)),
+                         _p(_c(up_s, np.float32)), _p(_c(down_q, np.uint8)), _p(_c(down_s, np.float32)),
+                         H, I, _p(_c(xq, np.int8)), _p(_c(xs, np.float32)), _p(o.y), _p(o.g), _p(o.u),
+                         _p(o.h), _p(o.hq), _p(o.hs))
+    return o
+
+
+def expert_dense(gate_q, gate_s, up_q, up_s, down_q, down_s, x) -> np.ndarray:
+    gate_q = _c(gate_q, np.uint8)
+    I, Hh = gate_q.shape
+    H = 2 * Hh
+    y = np.empty(H, np.float64)
+    _lib().oracle_expert_dense(_p(gate_q), _p(_c(gate_s, np.float32)), _p(_c(up_q, np.uint8)),
+                               _p(_c(up_s, np.float32)), _p(_c(down_q, np.uint8)),
+                               _p(_c(down_s, np.float32)), H, I, _p(_c(x, np.float32)), _p(y))
+    return y
+
+
+# ----------------------------------------------------------------------- O8
+def combine(y_routed, w, y_shared=None) -> np.ndarray:
+    y_routed = _c(np.atleast_2d(y_routed), np.float32)
+    k, H = y_routed.shape
+    y = np.empty(H, np.float32)
+    _lib().oracle_combine(_p(y_routed), _p(_c(w, np.float32)), k,
+                          None if y_shared is None else _p(_c(y_shared, np.float32)), H, _p(y))
+    return y
+
+
+# ----------------------------------------------------------------------- O9
+def rmsnorm(x, gamma, eps: float = 1e-6) -> np.ndarray:
+    x = _c(np.atleast_2d(x), np.float32)
+    T, H = x.shape
+    out = np.empty((T, H), np.float32)
+    _lib().oracle_rmsnorm(_p(x), _p(_c(gamma, np.float32)), T, H, eps, _p(out))
+    return out
+
+
+# --------------------------------------------------------------- whole layer
+class _CLayer(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int) for n in ("H", "I", "E", "top_k", "n_group", "topk_group", "has_shared")] + [
+        ("route_scale", ctypes.c_float),
+        ("router_w", ctypes.c_void_p), ("router_b", ctypes.c_void_p),
+        ("gate_q", ctypes.c_void_p), ("up_q", ctypes.c_void_p), ("down_q", ctypes.c_void_p),
+        ("gate_s", ctypes.c_void_p), ("up_s", ctypes.c_void_p), ("down_s", ctypes.c_void_p)]
+
+
+def moe_forward(layer, x):
+    """layer: object with H, I, E, top_k, n_group, topk_group, has_shared, route_scale and
+    numpy arrays router_w [E][H], router_b [E], gate_q/up_q [E+s][I][H/2], down_q [E+s][H][I/2],
+    gate_s/up_s [E+s][I], down_s [E+s][H]. Returns y [T][H], idx [T][k], w [T][k]."""
+    x = _c(np.atleast_2d(x), np.float32)
+    T = x.shape[0]
+    arrs = {n: _c(getattr(layer, n), dt) for n, dt in (
+        ("router_w", np.float32), ("router_b", np.float32), ("gate_q", np.uint8), ("up_q", np.uint8),
+        ("down_q", np.uint8), ("gate_s", np.float32), ("up_s", np.float32), ("down_s", np.float32))}
+    cl = _CLayer(layer.H, layer.I, layer.E, layer.top_k, layer.n_group, layer.topk_group,
+                 layer.has_shared, layer.route_scale,
+                 *[arrs[n].ctypes.data for n in ("router_w", "router_b", "gate_q", "up_q", "down_q",
+                                                 "gate_s", "up_s", "down_s")])
+    y = np.empty((T, layer.H), np.float32)
+    idx = np.empty((T, layer.top_k), np.int32)
+    w = np.empty((T, layer.top_k), np.float32)
+    rc = _lib().oracle_moe_forward(ctypes.byref(cl), _p(x), T, _p(y), _p(idx), _p(w))
+    if rc != 0:
+        raise ValueError("oracle_moe_forward rejected its arguments")
+    return y, idx, w
