@@ -1,0 +1,236 @@
+"""Benchmark of the MoE expert-FFN layer on one MI355X.
+
+Default workload: the GLM-5.2-shaped MoE layer at decode, T = 1 token
+(H=6144, I=2048, 256 routed experts + 1 shared, sigmoid router top-8, int4
+experts, Q8_0-style activations). A step is one pass of the whole hot path
+for one token through one layer: Q8(x) + router logits, top-k + batch union,
+gate/up IDOT GEMV + SwiGLU + Q8(h), down IDOT GEMV, combine with the shared
+expert. Inputs (weights, tokens) are resident in HBM before timing starts.
+
+The 256 MB Infinity Cache would hold one layer's 170 MB: steps therefore walk
+round-robin over 16 independently seeded layer instances of that exact shape
+(78 GB resident), so every step streams its experts from HBM as a real
+multi-layer decode does. The steps are captured once in a HIP graph (16
+steps, one per layer instance, 16 different tokens) and replayed.
+
+Prints ONE JSON line (metric, value, roofline of the dominant kernel,
+cpu_baseline of the oracle on a bounded sample).
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+STAGES = ["q8_logits", "select_union", "gateup_gemv", "down_gemv", "combine"]
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=4096)
+    p.add_argument("--warmup", type=int, default=64)
+    p.add_argument("--workload", default="glm52_decode_T1")
+    p.add_argument("--instances", type=int, default=16, help="resident layer instances (MALL defeat)")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-graph", action="store_true", help="launch every step eagerly")
+    return p.parse_args()
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def cpu_baseline(spec, tokens_np, n_tokens=3, reps=3):
+    """The oracle (single thread, as it stands) on a bounded sample: n_tokens
+    decode tokens through layer instance 0, each timed reps times (median)."""
+    import numpy as np
+    from oracle import layers as OL
+    from synth import synth as S
+
+    W, b = S.router(spec, 0, 0)
+    cache = OL.ExpertCache(spec, 0, 0)
+    times = []
+    for t in range(n_tokens):
+        OL.forward_token(spec, cache, W, b, tokens_np[t])          # regenerate experts (untimed)
+        per = []
+        for _ in range(reps):
+            t0 = time.perf_counter()
+            OL.forward_token(spec, cache, W, b, tokens_np[t])
+            per.append(time.perf_counter() - t0)
+        times.append(sorted(per)[len(per) // 2])
+    sec_per_token = float(np.mean(times))
+    return {"value": 1.0 / sec_per_token, "unit": "tokens*layers/s", "cores": 1, "kind": "oracle",
+            "sample": f"{n_tokens} decode tokens through one GLM-5.2-shaped layer, median of {reps} runs each "
+                      f"({sec_per_token:.2f} s/token, single-threaded C oracle, -O2)"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(sharding is described in DESIGN.md); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from int4_quantized_expert_sigmoid_amd import api
+    from int4_quantized_expert_sigmoid_amd._lib import lib
+    from int4_quantized_expert_sigmoid_amd.synthetic import device_layer
+    from synth import synth as S
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    wl = S.WORKLOADS[args.workload]
+    spec, T = wl.layer, wl.tokens.T
+    assert T <= 8, "this bench line covers the decode/verify workloads"
+    n_inst = args.instances
+    log(f"bench: {args.workload} T={T}, building {n_inst} layer instances on device")
+    t0 = time.time()
+    scratch = torch.empty(spec.H * spec.I, dtype=torch.float32, device="cuda")
+    layers = [device_layer(spec, wl.seed, li, scratch=scratch) for li in range(n_inst)]
+    del scratch
+    torch.cuda.synchronize()
+    log(f"bench: layers ready in {time.time() - t0:.1f} s "
+        f"({n_inst * spec.n_experts_stored * spec.expert_bytes / 1e9:.1f} GB int4 resident)")
+
+    G = n_inst                                   # steps per captured graph: one per instance
+    from dataclasses import replace
+    toks = S.tokens(replace(wl.tokens, T=T * G), spec.H, wl.seed)
+    x_all = torch.from_numpy(toks).cuda().view(G, T, spec.H)
+    y_all = torch.empty_like(x_all)
+    ws = [api.workspace(L, T) for L in layers]
+    cls = [L.c() for L in layers]
+    stream = torch.cuda.Stream()
+
+    def step(i, s):
+        j = i % G
+        api.moe_forward(layers[j], x_all[j], ws[j], y=y_all[j], stream=s, c_layer=cls[j])
+
+    # algorithmic bytes: every distinct selected expert (+ shared) once per step
+    routes = []
+    with torch.cuda.stream(stream):
+        for j in range(G):
+            idx, _ = api.moe_route(layers[j], x_all[j], ws[j], stream=stream)
+            routes.append(idx.cpu().numpy())
+    union = [len(set(r.reshape(-1).tolist())) for r in routes]
+    bytes_step = [(u + spec.has_shared) * spec.expert_bytes for u in union]
+    gateup_bytes = [(u + spec.has_shared) * 2 * spec.I * (spec.H // 2 + 4) for u in union]
+    down_bytes = [(u + spec.has_shared) * spec.H * (spec.I // 2 + 4) for u in union]
+
+    # ---------------- timed region: K steps (graph replays of G steps)
+    K = max(G, (args.steps + G - 1) // G * G)
+    W = max(G, (args.warmup + G - 1) // G * G)
+    use_graph = not args.no_graph
+    if use_graph:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(stream):
+            for i in range(G):                   # warm the code objects before capture
+                step(i, stream)
+        stream.synchronize()
+        with torch.cuda.graph(g, stream=stream):
+            for i in range(G):
+                step(i, torch.cuda.current_stream())
+        run = lambda n: [g.replay() for _ in range(n // G)]
+    else:
+        def run(n):
+            with torch.cuda.stream(stream):
+                for i in range(n):
+                    step(i, stream)
+    with torch.cuda.stream(stream):
+        run(W)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        ev0.record(stream)
+        t_wall = time.perf_counter()
+        run(K)
+        ev1.record(stream)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    ms_total = ev0.elapsed_time(ev1)
+    ms_step = ms_total / K
+    value = K * T / (ms_total / 1e3)
+
+    # ---------------- per-stage durations with HIP events (eager, same steps)
+    hip = ctypes.CDLL("libamdhip64.so")
+    hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+    hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+    hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+    KP = min(K, 256)
+    evs = []
+    for _ in range(KP):
+        arr = (ctypes.c_void_p * 6)()
+        for k in range(6):
+            e = ctypes.c_void_p()
+            assert hip.hipEventCreate(ctypes.byref(e)) == 0
+            arr[k] = e
+        evs.append(arr)
+    for i in range(KP):
+        j = i % G
+        rc = lib().coli_moe_forward_profiled(ctypes.byref(cls[j]), ctypes.c_void_p(x_all[j].data_ptr()), T,
+                                             ctypes.c_void_p(y_all[j].data_ptr()), 0,
+                                             ctypes.c_void_p(ws[j].data_ptr()), ws[j].numel(),
+                                             ctypes.c_void_p(stream.cuda_stream), evs[i], 6)
+        assert rc == 0, rc
+    stream.synchronize()
+    stage_ms = np.zeros((KP, 5))
+    for i in range(KP):
+        hip.hipEventSynchronize(evs[i][5])
+        for k in range(5):
+            f = ctypes.c_float()
+            hip.hipEventElapsedTime(ctypes.byref(f), evs[i][k], evs[i][k + 1])
+            stage_ms[i, k] = f.value
+    stage_avg = stage_ms.mean(axis=0)
+    gu_bytes_avg = float(np.mean([gateup_bytes[i % G] for i in range(KP)]))
+    gu_gbs = gu_bytes_avg / (stage_avg[2] * 1e-3) / 1e9
+    dn_gbs = float(np.mean([down_bytes[i % G] for i in range(KP)])) / (stage_avg[3] * 1e-3) / 1e9
+    step_gbs = float(np.mean(bytes_step)) / (ms_step * 1e-3) / 1e9
+    log("bench: stage averages (ms): " + ", ".join(f"{n}={v:.4f}" for n, v in zip(STAGES, stage_avg)))
+    log(f"bench: gate/up {gu_gbs:.0f} GB/s, down {dn_gbs:.0f} GB/s, whole step {step_gbs:.0f} GB/s "
+        f"on int4 expert bytes; {ms_step * 1e3:.2f} us/step (graph={use_graph}), wall {t_wall:.3f} s")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("bench: timing the oracle on a CPU sample")
+        cpu = cpu_baseline(spec, toks.reshape(G * T, spec.H))
+
+    out = {
+        "metric": "MoE-layer tokens*layers/s (GLM-5.2-shaped layer, int4 experts, decode)",
+        "value": round(value, 1),
+        "unit": "tokens*layers/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int4xint8->int32, f64 block sums",
+        "data": "synthetic (seeded Philox weights and tokens, no trained checkpoint)",
+        "config": {"workload": args.workload, "H": spec.H, "I": spec.I, "E": spec.E, "top_k": spec.top_k,
+                   "shared_experts": spec.has_shared, "T": T, "layer_instances": n_inst,
+                   "hip_graph": use_graph, "mean_union_experts": float(np.mean(union)),
+                   "expert_bytes_per_step": float(np.mean(bytes_step)),
+                   "step_hbm_gbs": round(step_gbs, 1),
+                   "stage_ms": {n: round(float(v), 5) for n, v in zip(STAGES, stage_avg)}},
+        "roofline": {"bound": "hbm", "kernel": "k_gateup_gemv", "achieved": round(gu_gbs, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gu_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": None,
+                     "bytes_per_launch": gu_bytes_avg, "avg_launch_ms": round(float(stage_avg[2]), 5)},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,183 @@
+"""Torch-facing binding of the C ABI: same names as include/coli_moe.h.
+
+PyTorch provides device memory and streams only. Every function checks the
+tensor shapes/dtypes it marshals, passes raw pointers to the library and
+raises ColiError on a non-zero status.
+"""
+from __future__ import annotations
+
+import ctypes
+from dataclasses import dataclass
+from typing import Optional, Tuple
+
+import numpy as np
+import torch
+
+from ._lib import (CLayer, CWsLayout, COLI_ACCUMULATE, COLI_PATH_GEMV, COLI_PATH_GROUPED, ColiError,
+                   check, lib)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _dev(t: torch.Tensor, dtype, name: str):
+    if not t.is_cuda or t.dtype != dtype or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous {dtype} device tensor")
+
+
+@dataclass
+class MoELayer:
+    """Device tensors of one MoE layer plus the C struct that points at them."""
+    H: int
+    I: int
+    E: int
+    top_k: int
+    has_shared: int
+    n_group: int
+    topk_group: int
+    route_scale: float
+    router_w: torch.Tensor   # [E][H] f32
+    router_b: torch.Tensor   # [E] f32
+    gate_q: torch.Tensor     # [E+s][I][H/2] u8
+    up_q: torch.Tensor
+    down_q: torch.Tensor     # [E+s][H][I/2] u8
+    gate_s: torch.Tensor     # [E+s][I] f32
+    up_s: torch.Tensor
+    down_s: torch.Tensor     # [E+s][H] f32
+
+    @classmethod
+    def empty(cls, H, I, E, top_k, has_shared=1, n_group=1, topk_group=1, route_scale=1.0, device="cuda"):
+        n = E + has_shared
+        u8, f32 = torch.uint8, torch.float32
+        return cls(H, I, E, top_k, has_shared, n_group, topk_group, route_scale,
+                   torch.empty((E, H), dtype=f32, device=device), torch.empty(E, dtype=f32, device=device),
+                   torch.empty((n, I, H // 2), dtype=u8, device=device),
+                   torch.empty((n, I, H // 2), dtype=u8, device=device),
+                   torch.empty((n, H, I // 2), dtype=u8, device=device),
+                   torch.empty((n, I), dtype=f32, device=device), torch.empty((n, I), dtype=f32, device=device),
+                   torch.empty((n, H), dtype=f32, device=device))
+
+    def c(self) -> CLayer:
+        return CLayer(self.H, self.I, self.E, self.top_k, self.n_group, self.topk_group, self.has_shared,
+                      self.route_scale, *(t.data_ptr() for t in (
+                          self.router_w, self.router_b, self.gate_q, self.up_q, self.down_q,
+                          self.gate_s, self.up_s, self.down_s)))
+
+    @property
+    def expert_bytes(self) -> int:
+        return 3 * self.H * self.I // 2 + 4 * (2 * self.I + self.H)
+
+
+def version() -> str:
+    return lib().coli_version().decode()
+
+
+def quant_act_q8(x: torch.Tensor, stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    _dev(x, torch.float32, "x")
+    T, H = x.shape
+    xq = torch.empty((T, H), dtype=torch.int8, device=x.device)
+    xs = torch.empty((T, H // 32), dtype=torch.float32, device=x.device)
+    check("coli_quant_act_q8", lib().coli_quant_act_q8(_ptr(x), T, H, _ptr(xq), _ptr(xs), _stream(stream)))
+    return xq, xs
+
+
+def workspace_bytes(layer: MoELayer, T: int) -> int:
+    cl = layer.c()
+    return int(lib().coli_moe_workspace_bytes(ctypes.byref(cl), T))
+
+
+def workspace(layer: MoELayer, T: int, stream=None) -> torch.Tensor:
+    n = workspace_bytes(layer, T)
+    if n == 0:
+        raise ColiError("coli_moe_workspace_bytes", -1)
+    ws = torch.empty(n, dtype=torch.uint8, device=layer.router_w.device)
+    check("coli_moe_workspace_init", lib().coli_moe_workspace_init(_ptr(ws), n, _stream(stream)))
+    return ws
+
+
+def workspace_layout(layer: MoELayer, T: int, flags: int = 0) -> CWsLayout:
+    cl = layer.c()
+    out = CWsLayout()
+    check("coli_moe_workspace_layout", lib().coli_moe_workspace_layout(ctypes.byref(cl), T, flags, ctypes.byref(out)))
+    return out
+
+
+def moe_route(layer: MoELayer, x: torch.Tensor, ws: torch.Tensor, stream=None):
+    _dev(x, torch.float32, "x")
+    T = x.shape[0]
+    idx = torch.empty((T, layer.top_k), dtype=torch.int32, device=x.device)
+    w = torch.empty((T, layer.top_k), dtype=torch.float32, device=x.device)
+    cl = layer.c()
+    check("coli_moe_route", lib().coli_moe_route(ctypes.byref(cl), _ptr(x), T, _ptr(idx), _ptr(w), _ptr(ws),
+                                                 ws.numel(), _stream(stream)))
+    return idx, w
+
+
+def moe_forward(layer: MoELayer, x: torch.Tensor, ws: torch.Tensor, y: Optional[torch.Tensor] = None,
+                flags: int = 0, stream=None, c_layer: Optional[CLayer] = None) -> torch.Tensor:
+    _dev(x, torch.float32, "x")
+    T = x.shape[0]
+    if y is None:
+        y = torch.empty_like(x)
+    cl = c_layer if c_layer is not None else layer.c()
+    check("coli_moe_forward", lib().coli_moe_forward(ctypes.byref(cl), _ptr(x), T, _ptr(y), flags, _ptr(ws),
+                                                     ws.numel(), _stream(stream)))
+    return y
+
+
+def moe_experts(layer: MoELayer, xq: torch.Tensor, xs: torch.Tensor, idx: torch.Tensor, w: torch.Tensor,
+                ws: torch.Tensor, y: Optional[torch.Tensor] = None, flags: int = 0, stream=None) -> torch.Tensor:
+    _dev(xq, torch.int8, "xq"); _dev(xs, torch.float32, "xs")
+    _dev(idx, torch.int32, "idx"); _dev(w, torch.float32, "w")
+    T = xq.shape[0]
+    if y is None:
+        y = torch.empty((T, layer.H), dtype=torch.float32, device=xq.device)
+    cl = layer.c()
+    check("coli_moe_experts", lib().coli_moe_experts(ctypes.byref(cl), _ptr(xq), _ptr(xs), _ptr(idx), _ptr(w), T,
+                                                     _ptr(y), flags, _ptr(ws), ws.numel(), _stream(stream)))
+    return y
+
+
+def rmsnorm(x: torch.Tensor, gamma: torch.Tensor, eps: float = 1e-6, out: Optional[torch.Tensor] = None,
+            stream=None) -> torch.Tensor:
+    _dev(x, torch.float32, "x"); _dev(gamma, torch.float32, "gamma")
+    T, H = x.shape
+    if out is None:
+        out = torch.empty_like(x)
+    check("coli_rmsnorm", lib().coli_rmsnorm(_ptr(x), _ptr(gamma), T, H, eps, _ptr(out), _stream(stream)))
+    return out
+
+
+def pack_int4_rows(w: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+    """Host packer (synchronous, host memory)."""
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    rows, cols = w.shape
+    q = np.empty((rows, cols // 2), dtype=np.uint8)
+    s = np.empty(rows, dtype=np.float32)
+    check("coli_pack_int4_rows", lib().coli_pack_int4_rows(ctypes.c_void_p(w.ctypes.data), rows, cols,
+                                                           ctypes.c_void_p(q.ctypes.data),
+                                                           ctypes.c_void_p(s.ctypes.data)))
+    return q, s
+
+
+def pack_int4_rows_dev(w: torch.Tensor, q: torch.Tensor, s: torch.Tensor, stream=None) -> None:
+    _dev(w, torch.float32, "w")
+    rows, cols = w.shape
+    check("coli_pack_int4_rows_dev", lib().coli_pack_int4_rows_dev(_ptr(w), rows, cols, _ptr(q), _ptr(s),
+                                                                   _stream(stream)))
+
+
+def debug_block_dots(q4: torch.Tensor, q8: torch.Tensor, stream=None) -> torch.Tensor:
+    _dev(q4, torch.uint8, "q4"); _dev(q8, torch.int8, "q8")
+    rows, half = q4.shape
+    S = torch.empty((rows, 2 * half // 32), dtype=torch.int32, device=q4.device)
+    check("coli_debug_block_dots", lib().coli_debug_block_dots(_ptr(q4), _ptr(q8), rows, 2 * half, _ptr(S),
+                                                               _stream(stream)))
+    return S

@@ -1,0 +1,288 @@
+// abi.cpp — the C ABI of include/coli_moe.h: argument validation, workspace
+// layout, path dispatch and the host int4 packer. No C++ exception crosses
+// the boundary; every failure is a status code returned before any launch.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+#include "internal.hpp"
+
+namespace coli {
+namespace {
+
+constexpr size_t ALIGN = 256;
+inline size_t up(size_t v) { return (v + ALIGN - 1) / ALIGN * ALIGN; }
+inline bool al16(const void *p) { return p != nullptr && (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+inline bool al4(const void *p) { return p != nullptr && (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+bool layer_ok(const coli_moe_layer *L)
+{
+    if (!L) return false;
+    if (L->H <= 0 || L->I <= 0 || L->H % 32 || L->I % 32 || L->H > 65536 || L->I > 65536) return false;
+    if (L->E < 1 || L->E > 1024) return false;
+    if (L->top_k < 1 || L->top_k > COLI_MAX_TOPK || L->top_k > L->E) return false;
+    if (L->n_group < 1 || L->n_group > 64 || L->E % L->n_group) return false;
+    if (L->topk_group < 1 || L->topk_group > L->n_group) return false;
+    if (L->n_group > 1 && L->top_k > L->topk_group * (L->E / L->n_group)) return false;
+    if (L->has_shared != 0 && L->has_shared != 1) return false;
+    if (!std::isfinite(L->route_scale)) return false;
+    if (!al4(L->router_w) || !al4(L->router_b)) return false;
+    if (!al16(L->gate_q) || !al16(L->up_q) || !al16(L->down_q)) return false;
+    if (!al4(L->gate_s) || !al4(L->up_s) || !al4(L->down_s)) return false;
+    return true;
+}
+
+bool gemv_shape_ok(const coli_moe_layer &L) { return L.H <= 8192 && L.I <= 2048; }
+
+int choose_path(const coli_moe_layer &L, int T, int flags)
+{
+    if (flags & COLI_PATH_GROUPED) return 1;
+    if (flags & COLI_PATH_GEMV) return 0;
+    return (T <= COLI_GEMV_MAX_T && gemv_shape_ok(L)) ? 0 : 1;
+}
+
+int status(hipError_t e) { return e == hipSuccess ? COLI_OK : COLI_EDEVICE; }
+
+} // namespace
+
+WsLayout make_layout(const coli_moe_layer &L, int T, int path)
+{
+    WsLayout o;
+    std::memset(&o, 0, sizeof(o));
+    o.path = path;
+    o.T = T;
+    const size_t H = (size_t)L.H, I = (size_t)L.I, k = (size_t)L.top_k, E = (size_t)L.E, t = (size_t)T;
+    size_t n_pairs, n_tiles = 0;
+    if (path == 0) {
+        o.max_items = (int)(t * k + (size_t)L.has_shared);
+        n_pairs = (size_t)o.max_items * MAX_SLOTS;
+    } else {
+        o.max_items = 0;
+        n_pairs = t * k + t * (size_t)L.has_shared;
+        n_tiles = (n_pairs + 31) / 32 + E + 1;
+    }
+    o.n_pairs = (int)n_pairs;
+    size_t p = 0;
+    o.ctrl = p; p = up(p + CTRL_WORDS * 4);
+    o.xq = p; p = up(p + t * H);
+    o.xs = p; p = up(p + t * (H / 32) * 4);
+    o.logits = p; p = up(p + t * E * 8);
+    o.idx = p; p = up(p + t * k * 4);
+    o.w = p; p = up(p + t * k * 4);
+    o.item_expert = p; p = up(p + (size_t)o.max_items * 4);
+    o.item_ntok = p; p = up(p + (size_t)o.max_items * 4);
+    o.item_tok = p; p = up(p + (size_t)o.max_items * MAX_SLOTS * 4);
+    o.pair_of = p; p = up(p + t * k * 4);
+    o.shared_pair = p; p = up(p + t * 4);
+    o.pair_tok = p; p = up(p + (path == 1 ? n_pairs * 4 : 0));
+    o.expert_off = p; p = up(p + (path == 1 ? (E + 2) * 4 : 0));
+    o.tiles = p; p = up(p + n_tiles * 8);
+    o.h = p; p = up(p + n_pairs * I * 4);
+    o.hq = p; p = up(p + n_pairs * I);
+    o.hs = p; p = up(p + n_pairs * (I / 32) * 4);
+    o.ye = p; p = up(p + n_pairs * H * 4);
+    o.total = p;
+    return o;
+}
+
+} // namespace coli
+
+using namespace coli;
+
+extern "C" {
+
+const char *coli_version(void) { return "coli-moe-mi355x 0.1 (gfx950)"; }
+
+int coli_quant_act_q8(const float *x, int T, int H, int8_t *xq, float *xs, void *stream)
+{
+    if (T < 1 || T > COLI_MAX_T || H <= 0 || H % 32 || !al16(x) || !al16(xq) || !al4(xs)) return COLI_EINVAL;
+    return status(launch_quant_q8(x, T, H, xq, xs, false, (hipStream_t)stream));
+}
+
+size_t coli_moe_workspace_bytes(const coli_moe_layer *L, int T)
+{
+    if (!layer_ok(L) || T < 1 || T > COLI_MAX_T) return 0;
+    size_t b = make_layout(*L, T, 1).total;
+    if (T <= COLI_GEMV_MAX_T && gemv_shape_ok(*L)) {
+        const size_t g = make_layout(*L, T, 0).total;
+        if (g > b) b = g;
+    }
+    return b;
+}
+
+int coli_moe_workspace_init(void *ws, size_t ws_bytes, void *stream)
+{
+    if (!al16(ws) || ws_bytes == 0) return COLI_EINVAL;
+    return status(launch_zero(ws, ws_bytes, (hipStream_t)stream));
+}
+
+int coli_moe_workspace_layout(const coli_moe_layer *L, int T, int flags, coli_moe_ws_layout *out)
+{
+    if (!layer_ok(L) || T < 1 || T > COLI_MAX_T || !out) return COLI_EINVAL;
+    if (flags & ~(COLI_ACCUMULATE | COLI_PATH_GEMV | COLI_PATH_GROUPED)) return COLI_EINVAL;
+    const int path = choose_path(*L, T, flags);
+    const WsLayout l = make_layout(*L, T, path);
+    out->xq = l.xq; out->xs = l.xs; out->idx = l.idx; out->w = l.w;
+    out->pair_of = l.pair_of; out->shared_pair = l.shared_pair;
+    out->h = l.h; out->hq = l.hq; out->hs = l.hs; out->ye = l.ye;
+    out->n_pairs_max = (size_t)l.n_pairs;
+    out->path = path;
+    return COLI_OK;
+}
+
+static int check_common(const coli_moe_layer *L, int T, int flags, void *ws, size_t ws_bytes, int &path,
+                        WsLayout &lay)
+{
+    if (!layer_ok(L) || T < 1 || T > COLI_MAX_T) return COLI_EINVAL;
+    if (flags & ~(COLI_ACCUMULATE | COLI_PATH_GEMV | COLI_PATH_GROUPED)) return COLI_EINVAL;
+    if ((flags & COLI_PATH_GEMV) && (flags & COLI_PATH_GROUPED)) return COLI_EINVAL;
+    if ((flags & COLI_PATH_GEMV) && (T > COLI_GEMV_MAX_T || !gemv_shape_ok(*L))) return COLI_EINVAL;
+    if (!al16(ws)) return COLI_EINVAL;
+    path = choose_path(*L, T, flags);
+    lay = make_layout(*L, T, path);
+    if (ws_bytes < lay.total) return COLI_EWORKSPACE;
+    return COLI_OK;
+}
+
+static int record(void *const *ev, int i, hipStream_t s)
+{
+    if (!ev) return COLI_OK;
+    return hipEventRecord((hipEvent_t)ev[i], s) == hipSuccess ? COLI_OK : COLI_EDEVICE;
+}
+
+static int run_experts(const coli_moe_layer *L, int T, const WsLayout &lay, char *ws, float *y, int flags,
+                       hipStream_t s, void *const *ev)
+{
+    hipError_t e;
+    if (lay.path == 0) {
+        if ((e = launch_gateup_gemv(*L, T, lay, ws, s)) != hipSuccess) return COLI_EDEVICE;
+        if (record(ev, 3, s)) return COLI_EDEVICE;
+        if ((e = launch_down_gemv(*L, T, lay, ws, s)) != hipSuccess) return COLI_EDEVICE;
+        if (record(ev, 4, s)) return COLI_EDEVICE;
+    } else {
+        if ((e = launch_gateup_grouped(*L, T, lay, ws, s)) != hipSuccess) return COLI_EDEVICE;
+        if (record(ev, 3, s)) return COLI_EDEVICE;
+        if ((e = launch_down_grouped(*L, T, lay, ws, s)) != hipSuccess) return COLI_EDEVICE;
+        if (record(ev, 4, s)) return COLI_EDEVICE;
+    }
+    e = launch_combine(*L, T, lay, ws, reinterpret_cast<const float *>(ws + lay.w), y,
+                       (flags & COLI_ACCUMULATE) != 0, s);
+    if (e != hipSuccess) return COLI_EDEVICE;
+    return record(ev, 5, s);
+}
+
+static int forward_impl(const coli_moe_layer *L, const float *x, int T, float *y, int flags, void *ws,
+                        size_t ws_bytes, void *stream, void *const *ev)
+{
+    int path;
+    WsLayout lay;
+    int rc = check_common(L, T, flags, ws, ws_bytes, path, lay);
+    if (rc != COLI_OK) return rc;
+    if (!al16(x) || !al16(y)) return COLI_EINVAL;
+    hipStream_t s = (hipStream_t)stream;
+    char *base = static_cast<char *>(ws);
+    if (record(ev, 0, s)) return COLI_EDEVICE;
+    if (launch_quant_q8(x, T, L->H, reinterpret_cast<int8_t *>(base + lay.xq),
+                        reinterpret_cast<float *>(base + lay.xs), true, s) != hipSuccess)
+        return COLI_EDEVICE;
+    if (launch_logits(*L, x, T, reinterpret_cast<double *>(base + lay.logits), s) != hipSuccess) return COLI_EDEVICE;
+    if (record(ev, 1, s)) return COLI_EDEVICE;
+    if (launch_select(*L, T, lay, base, nullptr, nullptr, nullptr, nullptr, s) != hipSuccess) return COLI_EDEVICE;
+    if (record(ev, 2, s)) return COLI_EDEVICE;
+    return run_experts(L, T, lay, base, y, flags, s, ev);
+}
+
+int coli_moe_route(const coli_moe_layer *L, const float *x, int T, int32_t *idx, float *w, void *ws,
+                   size_t ws_bytes, void *stream)
+{
+    int path;
+    WsLayout lay;
+    int rc = check_common(L, T, 0, ws, ws_bytes, path, lay);
+    if (rc != COLI_OK) return rc;
+    if (!al16(x) || !al4(idx) || !al4(w)) return COLI_EINVAL;
+    hipStream_t s = (hipStream_t)stream;
+    char *base = static_cast<char *>(ws);
+    if (launch_logits(*L, x, T, reinterpret_cast<double *>(base + lay.logits), s) != hipSuccess) return COLI_EDEVICE;
+    return status(launch_select(*L, T, lay, base, nullptr, nullptr, idx, w, s));
+}
+
+int coli_moe_forward(const coli_moe_layer *L, const float *x, int T, float *y, int flags, void *ws,
+                     size_t ws_bytes, void *stream)
+{
+    return forward_impl(L, x, T, y, flags, ws, ws_bytes, stream, nullptr);
+}
+
+int coli_moe_forward_profiled(const coli_moe_layer *L, const float *x, int T, float *y, int flags, void *ws,
+                              size_t ws_bytes, void *stream, void *const *events, int n_events)
+{
+    if (!events || n_events < COLI_PROFILE_EVENTS) return COLI_EINVAL;
+    for (int i = 0; i < COLI_PROFILE_EVENTS; ++i)
+        if (!events[i]) return COLI_EINVAL;
+    return forward_impl(L, x, T, y, flags, ws, ws_bytes, stream, events);
+}
+
+int coli_moe_experts(const coli_moe_layer *L, const int8_t *xq, const float *xs, const int32_t *idx,
+                     const float *w, int T, float *y, int flags, void *ws, size_t ws_bytes, void *stream)
+{
+    int path;
+    WsLayout lay;
+    int rc = check_common(L, T, flags, ws, ws_bytes, path, lay);
+    if (rc != COLI_OK) return rc;
+    if (!al16(xq) || !al4(xs) || !al4(idx) || !al4(w) || !al16(y)) return COLI_EINVAL;
+    hipStream_t s = (hipStream_t)stream;
+    char *base = static_cast<char *>(ws);
+    if (launch_reorder_q8(xq, T * L->H, reinterpret_cast<int8_t *>(base + lay.xq), s) != hipSuccess)
+        return COLI_EDEVICE;
+    if (launch_copy_f32(xs, reinterpret_cast<float *>(base + lay.xs), (size_t)T * (L->H / 32), s) != hipSuccess)
+        return COLI_EDEVICE;
+    if (launch_select(*L, T, lay, base, idx, w, nullptr, nullptr, s) != hipSuccess) return COLI_EDEVICE;
+    return run_experts(L, T, lay, base, y, flags, s, nullptr);
+}
+
+int coli_rmsnorm(const float *x, const float *gamma, int T, int H, float eps, float *out, void *stream)
+{
+    if (T < 1 || T > COLI_MAX_T || H <= 0 || !al4(x) || !al4(gamma) || !al4(out)) return COLI_EINVAL;
+    if (!(eps >= 0.0f) || !std::isfinite(eps)) return COLI_EINVAL;
+    return status(launch_rmsnorm(x, gamma, T, H, eps, out, (hipStream_t)stream));
+}
+
+int coli_pack_int4_rows(const float *w, int rows, int cols, uint8_t *q, float *s)
+{
+    if (!w || !q || !s || rows < 1 || cols < 2 || (cols & 1)) return COLI_EINVAL;
+    for (int r = 0; r < rows; ++r) {
+        const float *src = w + (size_t)r * cols;
+        float amax = 0.0f;
+        for (int c = 0; c < cols; ++c) amax = std::fmax(amax, std::fabs(src[c]));
+        const float d = amax / 7.0f;
+        const float id = (d != 0.0f) ? 1.0f / d : 0.0f;
+        s[r] = d;
+        uint8_t *dst = q + (size_t)r * (cols / 2);
+        for (int j = 0; j < cols / 2; ++j) {
+            int code[2];
+            for (int h = 0; h < 2; ++h) {
+                const float v = src[2 * j + h] * id;
+                float rv = std::isnan(v) ? 0.0f : std::rint(v);
+                rv = rv < -8.0f ? -8.0f : (rv > 7.0f ? 7.0f : rv);
+                code[h] = (int)rv;
+            }
+            dst[j] = (uint8_t)((code[0] & 0xF) | ((code[1] & 0xF) << 4));
+        }
+    }
+    return COLI_OK;
+}
+
+int coli_pack_int4_rows_dev(const float *w, int rows, int cols, uint8_t *q, float *s, void *stream)
+{
+    if (!al4(w) || !q || !al4(s) || rows < 1 || cols < 2 || (cols & 1)) return COLI_EINVAL;
+    return status(launch_pack_int4(w, rows, cols, q, s, (hipStream_t)stream));
+}
+
+int coli_debug_block_dots(const uint8_t *q4, const int8_t *q8, int rows, int cols, int32_t *S, void *stream)
+{
+    if (!al16(q4) || !al16(q8) || !al4(S) || rows < 1 || cols < 32 || cols % 32) return COLI_EINVAL;
+    return status(launch_block_dots(q4, q8, rows, cols, S, (hipStream_t)stream));
+}
+
+} // extern "C"

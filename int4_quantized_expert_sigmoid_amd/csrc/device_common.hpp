@@ -1,0 +1,143 @@
+// device_common.hpp — device helpers shared by every kernel of the layer.
+//
+// Data formats (colibri architecture overview, section 3.1):
+//  * int4 rows: byte j holds element 2j in bits 0-3 and element 2j+1 in bits
+//    4-7, 4-bit two's complement; one f32 scale per row.
+//  * Q8 activations: 32-wide blocks, int8 codes plus one f32 scale per block.
+//
+// Nibble trick: for a packed dword w (elements 8m..8m+7),
+//   (w << 4) & 0xF0F0F0F0  = the four even elements, each times 16, as int8;
+//    w       & 0xF0F0F0F0  = the four odd elements, each times 16, as int8.
+// So one 16-byte load of a row is one 32-wide block, and eight v_dot4 against
+// activations stored with every 8-group reordered as (0,2,4,6,1,3,5,7) give
+// 16 * S_b exactly (|16 S_b| <= 16*32*8*127 < 2^20). The factor 16 is folded
+// into the block scale (an exact power-of-two multiply in f64).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "internal.hpp"
+
+namespace coli {
+
+// Position of element i (0..7) of an 8-group in the reordered activation layout.
+__host__ __device__ constexpr int perm8(int i) { return (i & 1) ? 4 + (i >> 1) : (i >> 1); }
+
+struct Blk8 { int v[8]; };      // one 32-wide activation block, reordered, 8 dwords
+
+__device__ __forceinline__ void unpack_nibbles(const uint4 w, int (&lo)[4], int (&hi)[4])
+{
+    const uint32_t m = 0xF0F0F0F0u;
+    lo[0] = (int)((w.x << 4) & m); hi[0] = (int)(w.x & m);
+    lo[1] = (int)((w.y << 4) & m); hi[1] = (int)(w.y & m);
+    lo[2] = (int)((w.z << 4) & m); hi[2] = (int)(w.z & m);
+    lo[3] = (int)((w.w << 4) & m); hi[3] = (int)(w.w & m);
+}
+
+// 16 * S_b for one block: unpacked weight nibbles against one reordered block.
+__device__ __forceinline__ int dot_block16(const int (&lo)[4], const int (&hi)[4], const Blk8 &a)
+{
+    int s = 0;
+    s = __builtin_amdgcn_sdot4(lo[0], a.v[0], s, false);
+    s = __builtin_amdgcn_sdot4(hi[0], a.v[1], s, false);
+    s = __builtin_amdgcn_sdot4(lo[1], a.v[2], s, false);
+    s = __builtin_amdgcn_sdot4(hi[1], a.v[3], s, false);
+    s = __builtin_amdgcn_sdot4(lo[2], a.v[4], s, false);
+    s = __builtin_amdgcn_sdot4(hi[2], a.v[5], s, false);
+    s = __builtin_amdgcn_sdot4(lo[3], a.v[6], s, false);
+    s = __builtin_amdgcn_sdot4(hi[3], a.v[7], s, false);
+    return s;
+}
+
+__device__ __forceinline__ Blk8 load_blk8(const int8_t *p)
+{
+    const int4 a = *reinterpret_cast<const int4 *>(p);
+    const int4 b = *reinterpret_cast<const int4 *>(p + 16);
+    Blk8 r;
+    r.v[0] = a.x; r.v[1] = a.y; r.v[2] = a.z; r.v[3] = a.w;
+    r.v[4] = b.x; r.v[5] = b.y; r.v[6] = b.z; r.v[7] = b.w;
+    return r;
+}
+
+__device__ __forceinline__ uint4 load_u4(const uint8_t *p)
+{
+    return *reinterpret_cast<const uint4 *>(p);
+}
+
+// Streaming (use-once) 16-byte load: weights are read once per call.
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint4 load_u4_stream(const uint8_t *p)
+{
+    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// Round half to even and clamp, the rule shared by both quantisers; a NaN
+// product (0 * inf) gives 0.
+__device__ __forceinline__ int round_clamp(float v, float lo, float hi)
+{
+    if (v != v) return 0;
+    float r = __builtin_rintf(v);
+    r = r < lo ? lo : r;
+    r = r > hi ? hi : r;
+    return (int)r;
+}
+
+// Scale of a Q8 block from its absmax: IEEE f32 divisions, no reciprocal
+// approximation.
+__device__ __forceinline__ void q8_scale(float amax, float &d, float &id)
+{
+    d = __fdiv_rn(amax, 127.0f);
+    id = (d != 0.0f) ? __fdiv_rn(1.0f, d) : 0.0f;
+}
+
+template <typename T>
+__device__ __forceinline__ T wave_max(T v, int width = 64)
+{
+    for (int o = width >> 1; o > 0; o >>= 1) {
+        T u = __shfl_xor(v, o, width);
+        v = u > v ? u : v;
+    }
+    return v;
+}
+
+template <typename T>
+__device__ __forceinline__ T wave_sum(T v, int width = 64)
+{
+    for (int o = width >> 1; o > 0; o >>= 1) v += __shfl_xor(v, o, width);
+    return v;
+}
+
+// Transposing reduction of N values per lane over a 64-lane wave (N a power
+// of two, N <= 64): afterwards lane l holds the wave-wide sum of value
+// (l >> (6 - log2 N)) & (N - 1) in v[0]. Each halving step sends the half a
+// lane does not keep to its partner, so N values cost N - 1 exchanges.
+template <int N>
+__device__ __forceinline__ void wave_transpose_reduce(double (&v)[N])
+{
+    const int lane = threadIdx.x & 63;
+    int d = 32;
+#pragma unroll
+    for (int n = N; n > 1; n >>= 1, d >>= 1) {
+        const bool upper = (lane & d) != 0;
+#pragma unroll
+        for (int i = 0; i < n / 2; ++i) {
+            const double keep = upper ? v[i + n / 2] : v[i];
+            const double send = upper ? v[i] : v[i + n / 2];
+            v[i] = keep + __shfl_xor(send, d);
+        }
+    }
+    for (; d >= 1; d >>= 1) v[0] += __shfl_xor(v[0], d);
+}
+
+template <int N>
+__device__ __forceinline__ constexpr int log2i() { return N <= 1 ? 0 : 1 + log2i<N / 2>(); }
+
+template <int N>
+__device__ __forceinline__ int transpose_index(int lane) { return (lane >> (6 - log2i<N>())) & (N - 1); }
+
+// Sigmoid-weighted linear unit on f64 inputs: silu(g) = g / (1 + exp(-g)).
+__device__ __forceinline__ double silu_f64(double g) { return g / (1.0 + exp(-g)); }
+
+} // namespace coli

@@ -1,0 +1,63 @@
+// internal.hpp — kernel launchers of the layer and the workspace layout.
+// Host-side declarations only; every launcher enqueues on `s` and returns
+// the HIP status of its launch.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/coli_moe.h"
+
+namespace coli {
+
+constexpr int QK = 32;          // activation block width (Q8_0-style)
+constexpr int MAX_SLOTS = 8;    // token slots of one expert item on the GEMV path
+
+// Byte offsets of every workspace region for one (layer, T, path).
+struct WsLayout {
+    int path;            // 0 GEMV, 1 grouped
+    int T, max_items, n_pairs;
+    size_t ctrl, xq, xs, logits, idx, w;
+    size_t item_expert, item_ntok, item_tok;     // GEMV path items
+    size_t pair_of, shared_pair;
+    size_t pair_tok, expert_off, tiles;          // grouped path buckets and tile list
+    size_t h, hq, hs, ye;
+    size_t total;
+};
+
+WsLayout make_layout(const coli_moe_layer &L, int T, int path);
+
+// Control words at the start of the workspace.
+enum CtrlWord { CTRL_N_ITEMS = 0, CTRL_N_TILES_GU = 1, CTRL_N_TILES_DN = 2, CTRL_WORDS = 64 };
+
+// ---- quantisation, packing, norms (kernels_quant.hip)
+hipError_t launch_quant_q8(const float *x, int T, int H, int8_t *xq, float *xs, bool reorder, hipStream_t s);
+hipError_t launch_reorder_q8(const int8_t *xq_nat, int n, int8_t *xq_perm, hipStream_t s);
+hipError_t launch_pack_int4(const float *w, int rows, int cols, uint8_t *q, float *sc, hipStream_t s);
+hipError_t launch_rmsnorm(const float *x, const float *g, int T, int H, float eps, float *out, hipStream_t s);
+hipError_t launch_block_dots(const uint8_t *q4, const int8_t *q8, int rows, int cols, int32_t *S, hipStream_t s);
+hipError_t launch_zero(void *p, size_t bytes, hipStream_t s);
+hipError_t launch_copy_f32(const float *src, float *dst, size_t n, hipStream_t s);
+
+// ---- router (kernels_route.hip)
+hipError_t launch_logits(const coli_moe_layer &L, const float *x, int T, double *z, hipStream_t s);
+// Top-k of every token from logits (or, with given_idx, from the caller's
+// routing), then the batch union of experts (GEMV path) or the per-expert
+// buckets and tile lists (grouped path).
+hipError_t launch_select(const coli_moe_layer &L, int T, const WsLayout &lay, char *ws,
+                         const int32_t *given_idx, const float *given_w,
+                         int32_t *idx_out, float *w_out, hipStream_t s);
+
+// ---- experts, GEMV path (kernels_gemv.hip)
+hipError_t launch_gateup_gemv(const coli_moe_layer &L, int T, const WsLayout &lay, char *ws, hipStream_t s);
+hipError_t launch_down_gemv(const coli_moe_layer &L, int T, const WsLayout &lay, char *ws, hipStream_t s);
+
+// ---- experts, grouped int8-MFMA path (kernels_grouped.hip)
+hipError_t launch_gateup_grouped(const coli_moe_layer &L, int T, const WsLayout &lay, char *ws, hipStream_t s);
+hipError_t launch_down_grouped(const coli_moe_layer &L, int T, const WsLayout &lay, char *ws, hipStream_t s);
+
+// ---- combine (kernels_combine.hip)
+hipError_t launch_combine(const coli_moe_layer &L, int T, const WsLayout &lay, const char *ws,
+                          const float *w, float *y, bool accumulate, hipStream_t s);
+
+} // namespace coli

@@ -1,0 +1,228 @@
+// kernels_grouped.hip — grouped int8-MFMA expert GEMMs for large batches
+// (prefill, T > 8).
+//
+// The same IDOT arithmetic as the GEMV path (colibri architecture overview,
+// section 3.1: int4 weights dequantised on use, int8 activations, integer
+// dot products), batched over the union of selected experts (colibri README
+// zh-TW, "how it works": a batch reads each distinct expert once). Pairs
+// (token, expert) are bucketed per expert and cut into tiles of 32 pairs.
+//
+// One wave computes a 32-row x 32-pair output tile. For every 32-wide block
+// b it issues v_mfma_i32_32x32x32_i8 with
+//   A = 32 weight rows x 32 k (lane l: row l%32, half l/32 holds 16 k),
+//   B = 32 k x 32 pairs     (lane l: pair l%32, the same 16 k),
+// unpacking the nibbles in registers (x16, exact), then adds
+// C * (d_b/16) to an f64 accumulator per element: the block scale is per
+// (token, block), so each block's int32 result is rescaled on its own.
+// Both operands list their 16 k in the same order (the reordered 8-groups),
+// so the product sums exactly the block's 32 k whatever order the matrix
+// core uses inside a lane. Output element (row, pair) sits in lane
+// pair + 32*((row/4)&1), register (row/8)*4 + row%4.
+#include "device_common.hpp"
+#include "internal.hpp"
+
+namespace coli {
+namespace {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+
+constexpr int TILE_N = 32;     // pairs per tile (matches the bucket kernel)
+constexpr int WAVES = 4;       // row tiles per workgroup
+
+struct GroupedArgs {
+    const uint8_t *q_a, *q_b;  // gate/up (both) or down (q_a)
+    const float *s_a, *s_b;
+    int H, I;
+    const int8_t *act;         // gate/up: reordered Q8(x) [T][H]; down: reordered hq [pairs][I]
+    const float *act_s;        // xs [T][H/32] or hs [pairs][I/32]
+    const int *ctrl;
+    const int2 *tiles;
+    const int *expert_off, *pair_tok;
+    float *h;
+    int8_t *hq;
+    float *hs;
+    float *ye;
+};
+
+__device__ __forceinline__ v4i unpack8(uint2 w)
+{
+    const uint32_t m = 0xF0F0F0F0u;
+    v4i a;
+    a[0] = (int)((w.x << 4) & m);
+    a[1] = (int)(w.x & m);
+    a[2] = (int)((w.y << 4) & m);
+    a[3] = (int)(w.y & m);
+    return a;
+}
+
+__device__ __forceinline__ int tile_row(int i, int half) { return 8 * (i >> 2) + 4 * half + (i & 3); }
+
+__global__ void __launch_bounds__(256) k_gateup_mfma(GroupedArgs a)
+{
+    const int n_rt = a.I / QK;
+    const int nrg = (n_rt + WAVES - 1) / WAVES;
+    const int tile = blockIdx.x / nrg, rg = blockIdx.x % nrg;
+    if (tile >= a.ctrl[CTRL_N_TILES_GU]) return;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int rt = rg * WAVES + wave;
+    if (rt >= n_rt) return;
+    const int2 td = a.tiles[tile];
+    const int e = td.x, p0 = td.y;
+    const int np = min(TILE_N, a.expert_off[e + 1] - p0);
+    const int n = lane & 31, half = lane >> 5;
+    const bool valid = n < np;
+    const int pair = p0 + n;
+    const int tok = valid ? a.pair_tok[pair] : 0;
+    const int nblk = a.H / QK;
+    const long rowb = a.H / 2;
+    const long wrow = (long)e * a.I + (long)rt * QK + n;
+    const uint8_t *pg = a.q_a + wrow * rowb + 8 * half;
+    const uint8_t *pu = a.q_b + wrow * rowb + 8 * half;
+    const int8_t *px = a.act + (long)tok * a.H + 16 * half;
+    const float *ps = a.act_s + (long)tok * nblk;
+
+    double acc_g[16], acc_u[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) { acc_g[i] = 0.0; acc_u[i] = 0.0; }
+    const v16i zero = {};
+
+    for (int b = 0; b < nblk; ++b) {
+        const uint2 wg = *reinterpret_cast<const uint2 *>(pg + 16 * b);
+        const uint2 wu = *reinterpret_cast<const uint2 *>(pu + 16 * b);
+        v4i B = {0, 0, 0, 0};
+        double d = 0.0;
+        if (valid) {
+            const int4 xb = *reinterpret_cast<const int4 *>(px + 32 * b);
+            B[0] = xb.x; B[1] = xb.y; B[2] = xb.z; B[3] = xb.w;
+            d = (double)ps[b] * 0.0625;
+        }
+        const v16i cg = __builtin_amdgcn_mfma_i32_32x32x32_i8(unpack8(wg), B, zero, 0, 0, 0);
+        const v16i cu = __builtin_amdgcn_mfma_i32_32x32x32_i8(unpack8(wu), B, zero, 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            acc_g[i] = fma((double)cg[i], d, acc_g[i]);
+            acc_u[i] = fma((double)cu[i], d, acc_u[i]);
+        }
+    }
+    // epilogue: g, u, h = silu(g)*u, Q8 over the tile's 32 rows per pair
+    float hv[16];
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const long grow = (long)e * a.I + (long)rt * QK + tile_row(i, half);
+        const float gf = (float)((double)a.s_a[grow] * acc_g[i]);
+        const float uf = (float)((double)a.s_b[grow] * acc_u[i]);
+        hv[i] = (float)(silu_f64((double)gf) * (double)uf);
+        amax = fmaxf(amax, fabsf(hv[i]));
+    }
+    amax = fmaxf(amax, __shfl_xor(amax, 32));
+    if (!valid) return;
+    float d, id;
+    q8_scale(amax, d, id);
+    const long base = (long)pair * a.I + (long)rt * QK;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const int r = tile_row(i, half);
+        a.h[base + r] = hv[i];
+        a.hq[base + (r & ~7) + perm8(r & 7)] = (int8_t)round_clamp(__fmul_rn(hv[i], id), -127.0f, 127.0f);
+    }
+    if (half == 0) a.hs[(long)pair * n_rt + rt] = d;
+}
+
+__global__ void __launch_bounds__(256) k_down_mfma(GroupedArgs a)
+{
+    const int n_rt = a.H / QK;
+    const int nrg = (n_rt + WAVES - 1) / WAVES;
+    const int tile = blockIdx.x / nrg, rg = blockIdx.x % nrg;
+    if (tile >= a.ctrl[CTRL_N_TILES_GU]) return;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int rt = rg * WAVES + wave;
+    if (rt >= n_rt) return;
+    const int2 td = a.tiles[tile];
+    const int e = td.x, p0 = td.y;
+    const int np = min(TILE_N, a.expert_off[e + 1] - p0);
+    const int n = lane & 31, half = lane >> 5;
+    const bool valid = n < np;
+    const int pair = p0 + n;
+    const int nblk = a.I / QK;
+    const long rowb = a.I / 2;
+    const long wrow = (long)e * a.H + (long)rt * QK + n;
+    const uint8_t *pd = a.q_a + wrow * rowb + 8 * half;
+    const int8_t *ph = a.act + (long)(valid ? pair : p0) * a.I + 16 * half;
+    const float *ps = a.act_s + (long)(valid ? pair : p0) * nblk;
+
+    double acc[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[i] = 0.0;
+    const v16i zero = {};
+
+    for (int b = 0; b < nblk; ++b) {
+        const uint2 wd = *reinterpret_cast<const uint2 *>(pd + 16 * b);
+        v4i B = {0, 0, 0, 0};
+        double d = 0.0;
+        if (valid) {
+            const int4 hb = *reinterpret_cast<const int4 *>(ph + 32 * b);
+            B[0] = hb.x; B[1] = hb.y; B[2] = hb.z; B[3] = hb.w;
+            d = (double)ps[b] * 0.0625;
+        }
+        const v16i c = __builtin_amdgcn_mfma_i32_32x32x32_i8(unpack8(wd), B, zero, 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[i] = fma((double)c[i], d, acc[i]);
+    }
+    if (!valid) return;
+    const long base = (long)pair * a.H + (long)rt * QK;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const int r = tile_row(i, half);
+        a.ye[base + r] = (float)((double)a.s_a[(long)e * a.H + (long)rt * QK + r] * acc[i]);
+    }
+}
+
+GroupedArgs make_args(const WsLayout &lay, char *ws, const coli_moe_layer &L)
+{
+    GroupedArgs a;
+    a.H = L.H; a.I = L.I;
+    a.ctrl = reinterpret_cast<const int *>(ws + lay.ctrl);
+    a.tiles = reinterpret_cast<const int2 *>(ws + lay.tiles);
+    a.expert_off = reinterpret_cast<const int *>(ws + lay.expert_off);
+    a.pair_tok = reinterpret_cast<const int *>(ws + lay.pair_tok);
+    a.h = reinterpret_cast<float *>(ws + lay.h);
+    a.hq = reinterpret_cast<int8_t *>(ws + lay.hq);
+    a.hs = reinterpret_cast<float *>(ws + lay.hs);
+    a.ye = reinterpret_cast<float *>(ws + lay.ye);
+    return a;
+}
+
+int max_tiles(const WsLayout &lay, const coli_moe_layer &L)
+{
+    return (lay.n_pairs + TILE_N - 1) / TILE_N + L.E + 1;
+}
+
+} // namespace
+
+hipError_t launch_gateup_grouped(const coli_moe_layer &L, int T, const WsLayout &lay, char *ws, hipStream_t s)
+{
+    (void)T;
+    GroupedArgs a = make_args(lay, ws, L);
+    a.q_a = L.gate_q; a.s_a = L.gate_s; a.q_b = L.up_q; a.s_b = L.up_s;
+    a.act = reinterpret_cast<const int8_t *>(ws + lay.xq);
+    a.act_s = reinterpret_cast<const float *>(ws + lay.xs);
+    const int nrg = (L.I / QK + WAVES - 1) / WAVES;
+    hipLaunchKernelGGL(k_gateup_mfma, dim3((unsigned)(max_tiles(lay, L) * nrg)), dim3(64 * WAVES), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_down_grouped(const coli_moe_layer &L, int T, const WsLayout &lay, char *ws, hipStream_t s)
+{
+    (void)T;
+    GroupedArgs a = make_args(lay, ws, L);
+    a.q_a = L.down_q; a.s_a = L.down_s; a.q_b = nullptr; a.s_b = nullptr;
+    a.act = reinterpret_cast<const int8_t *>(ws + lay.hq);
+    a.act_s = reinterpret_cast<const float *>(ws + lay.hs);
+    const int nrg = (L.H / QK + WAVES - 1) / WAVES;
+    hipLaunchKernelGGL(k_down_mfma, dim3((unsigned)(max_tiles(lay, L) * nrg)), dim3(64 * WAVES), 0, s, a);
+    return hipGetLastError();
+}
+
+} // namespace coli

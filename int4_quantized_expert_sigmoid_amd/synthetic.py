@@ -1,0 +1,40 @@
+"""Synthetic MoE layers resident in HBM.
+
+Weights come from the seeded generator (synth/, counter-addressed, its device
+twin writes f32 rows straight into HBM) and are packed to int4 on the GPU by
+the library's own packer (coli_pack_int4_rows_dev). Router weights, bias,
+tokens and RMSNorm gains are small and generated on the host.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from synth import synth as S
+
+from .api import MoELayer, pack_int4_rows_dev
+
+
+def device_layer(spec: S.LayerSpec, seed: int = 0, layer: int = 0, device: str = "cuda",
+                 scratch: torch.Tensor = None) -> MoELayer:
+    L = MoELayer.empty(spec.H, spec.I, spec.E, spec.top_k, spec.has_shared, spec.n_group, spec.topk_group,
+                       spec.route_scale, device=device)
+    W, b = S.router(spec, seed, layer)
+    L.router_w.copy_(torch.from_numpy(W))
+    L.router_b.copy_(torch.from_numpy(b))
+    n = spec.H * spec.I
+    if scratch is None or scratch.numel() < n:
+        scratch = torch.empty(n, dtype=torch.float32, device=device)
+    stream = torch.cuda.current_stream().cuda_stream
+    for e in range(spec.n_experts_stored):
+        for m, q, s, shape in ((S.GATE, L.gate_q, L.gate_s, (spec.I, spec.H)),
+                               (S.UP, L.up_q, L.up_s, (spec.I, spec.H)),
+                               (S.DOWN, L.down_q, L.down_s, (spec.H, spec.I))):
+            buf = scratch[:n].view(shape)
+            S.dev_expert_matrix(buf.data_ptr(), spec, seed, layer, e, m, hip_stream=stream)
+            pack_int4_rows_dev(buf, q[e], s[e])
+    return L
+
+
+def host_tokens(tspec: S.TokenSpec, H: int, seed: int = 0) -> np.ndarray:
+    return S.tokens(tspec, H, seed)

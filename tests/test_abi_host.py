@@ -1,0 +1,133 @@
+"""Host-side checks of the C ABI (no GPU): the library loads and exports every
+function include/coli_moe.h declares, argument validation returns its status
+codes before anything is launched, workspace sizing, and the host int4 packer
+produces the oracle packer's bytes."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from int4_quantized_expert_sigmoid_amd import _lib
+from int4_quantized_expert_sigmoid_amd._lib import CLayer, CWsLayout, lib
+from oracle import oracle as O
+from synth import synth as S
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_functions():
+    names = set()
+    for fn in os.listdir(os.path.join(ROOT, "include")):
+        if fn.endswith(".h"):
+            text = open(os.path.join(ROOT, "include", fn)).read()
+            text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+            names |= set(re.findall(r"^\s*(?:const\s+)?[\w\s\*]+?\b(coli_\w+)\s*\(", text, flags=re.M))
+    return names
+
+
+def test_library_exports_every_declared_function():
+    names = header_functions()
+    assert {"coli_moe_route", "coli_quant_act_q8", "coli_moe_forward"} <= names
+    L = lib()
+    for n in sorted(names):
+        assert hasattr(L, n), n
+    assert set(_lib.EXPORTS) == names
+    assert b"gfx950" in L.coli_version()
+
+
+def fake_layer(H=6144, I=2048, E=256, k=8, **kw):
+    p = 1 << 20     # aligned dummy address: never dereferenced by the checks below
+    args = dict(H=H, I=I, E=E, top_k=k, n_group=1, topk_group=1, has_shared=1, route_scale=1.0)
+    args.update(kw)
+    return CLayer(args["H"], args["I"], args["E"], args["top_k"], args["n_group"], args["topk_group"],
+                  args["has_shared"], args["route_scale"], p, p, p, p, p, p, p, p)
+
+
+def ws_bytes(layer, T):
+    return lib().coli_moe_workspace_bytes(ctypes.byref(layer), T)
+
+
+def test_workspace_sizes():
+    L = fake_layer()
+    b1 = ws_bytes(L, 1)
+    assert 0 < b1 < 8 * 2 ** 20
+    b512 = ws_bytes(L, 512)
+    n_pairs = 512 * 8 + 512
+    assert b512 >= n_pairs * (6144 + 2048) * 4       # per-pair h and y
+    assert ws_bytes(fake_layer(H=100), 1) == 0        # H not a multiple of 32
+    assert ws_bytes(L, 0) == 0
+
+
+@pytest.mark.parametrize("bad", [
+    dict(H=48), dict(I=40), dict(E=0), dict(E=2000), dict(top_k=0), dict(top_k=17), dict(top_k=9, E=8),
+    dict(n_group=3), dict(n_group=8, topk_group=9), dict(n_group=8, topk_group=1, top_k=33),
+    dict(has_shared=2), dict(route_scale=float("nan")),
+])
+def test_invalid_layers_rejected(bad):
+    L = fake_layer(**bad)
+    p = ctypes.c_void_p(1 << 20)
+    assert ws_bytes(L, 1) == 0
+    rc = lib().coli_moe_forward(ctypes.byref(L), p, 1, p, 0, p, 1 << 30, None)
+    assert rc == _lib.COLI_EINVAL
+
+
+def test_forward_argument_errors_before_launch():
+    L = fake_layer()
+    p = ctypes.c_void_p(1 << 20)
+    F = lib().coli_moe_forward
+    assert F(ctypes.byref(L), p, 0, p, 0, p, 1 << 30, None) == _lib.COLI_EINVAL          # T = 0
+    assert F(ctypes.byref(L), p, 70000, p, 0, p, 1 << 40, None) == _lib.COLI_EINVAL      # T > max
+    assert F(ctypes.byref(L), p, 1, p, 64, p, 1 << 30, None) == _lib.COLI_EINVAL         # unknown flag
+    assert F(ctypes.byref(L), p, 1, p, 6, p, 1 << 30, None) == _lib.COLI_EINVAL          # two paths
+    assert F(ctypes.byref(L), p, 9, p, 2, p, 1 << 30, None) == _lib.COLI_EINVAL          # GEMV needs T <= 8
+    assert F(ctypes.byref(L), ctypes.c_void_p((1 << 20) + 4), 1, p, 0, p, 1 << 30, None) == _lib.COLI_EINVAL
+    assert F(ctypes.byref(L), p, 1, p, 0, p, 100, None) == _lib.COLI_EWORKSPACE
+    assert F(None, p, 1, p, 0, p, 1 << 30, None) == _lib.COLI_EINVAL
+    R = lib().coli_moe_route
+    assert R(ctypes.byref(L), p, 1, p, p, p, 10, None) == _lib.COLI_EWORKSPACE
+    Q = lib().coli_quant_act_q8
+    assert Q(p, 1, 100, p, p, None) == _lib.COLI_EINVAL
+    assert Q(p, 0, 64, p, p, None) == _lib.COLI_EINVAL
+    N = lib().coli_rmsnorm
+    assert N(p, p, 1, 64, ctypes.c_float(-1.0), p, None) == _lib.COLI_EINVAL
+    D = lib().coli_debug_block_dots
+    assert D(p, p, 4, 48, p, None) == _lib.COLI_EINVAL
+
+
+def test_workspace_layout_paths():
+    L = fake_layer()
+    out = CWsLayout()
+    assert lib().coli_moe_workspace_layout(ctypes.byref(L), 1, 0, ctypes.byref(out)) == 0
+    assert out.path == 0 and out.n_pairs_max == (8 + 1) * 8
+    assert lib().coli_moe_workspace_layout(ctypes.byref(L), 512, 0, ctypes.byref(out)) == 0
+    assert out.path == 1 and out.n_pairs_max == 512 * 9
+    assert lib().coli_moe_workspace_layout(ctypes.byref(L), 4, _lib.COLI_PATH_GROUPED, ctypes.byref(out)) == 0
+    assert out.path == 1
+    for f in ("xq", "xs", "idx", "w", "h", "hq", "hs", "ye"):
+        assert getattr(out, f) % 256 == 0
+
+
+def host_pack(w):
+    w = np.ascontiguousarray(w, np.float32)
+    q = np.empty((w.shape[0], w.shape[1] // 2), np.uint8)
+    s = np.empty(w.shape[0], np.float32)
+    rc = lib().coli_pack_int4_rows(ctypes.c_void_p(w.ctypes.data), w.shape[0], w.shape[1],
+                                   ctypes.c_void_p(q.ctypes.data), ctypes.c_void_p(s.ctypes.data))
+    assert rc == 0
+    return q, s
+
+
+def test_host_packer_matches_oracle_packer():
+    w = S.expert_matrix(S.GLM52, 0, 0, 7, S.DOWN)
+    q, s = host_pack(w)
+    qo, so = O.pack_int4_rows(w)
+    assert np.array_equal(q, qo) and np.array_equal(s, so)
+    edge = np.zeros((4, 64), np.float32)
+    edge[1, :] = 1e-40                      # subnormal row: 1/d overflows
+    edge[2, 5] = -3.5                       # single nonzero
+    edge[3, :] = np.linspace(-7, 7, 64)     # ties at .5 after scaling
+    q, s = host_pack(edge)
+    qo, so = O.pack_int4_rows(edge)
+    assert np.array_equal(q, qo) and np.array_equal(s, so)
