@@ -21,7 +21,7 @@ bool layer_ok(const coli_moe_layer *L)
 {
     if (!L) return false;
     if (L->H <= 0 || L->I <= 0 || L->H % 32 || L->I % 32 || L->H > 65536 || L->I > 65536) return false;
-    if (L->E < 1 || L->E > 1024) return false;
+    if (L->E < 1 || L->E > 512) return false;
     if (L->top_k < 1 || L->top_k > COLI_MAX_TOPK || L->top_k > L->E) return false;
     if (L->n_group < 1 || L->n_group > 64 || L->E % L->n_group) return false;
     if (L->topk_group < 1 || L->topk_group > L->n_group) return false;
@@ -184,10 +184,10 @@ static int forward_impl(const coli_moe_layer *L, const float *x, int T, float *y
     hipStream_t s = (hipStream_t)stream;
     char *base = static_cast<char *>(ws);
     if (record(ev, 0, s)) return COLI_EDEVICE;
-    if (launch_quant_q8(x, T, L->H, reinterpret_cast<int8_t *>(base + lay.xq),
-                        reinterpret_cast<float *>(base + lay.xs), true, s) != hipSuccess)
+    if (launch_logits(*L, x, T, reinterpret_cast<double *>(base + lay.logits),
+                      reinterpret_cast<int8_t *>(base + lay.xq), reinterpret_cast<float *>(base + lay.xs),
+                      s) != hipSuccess)
         return COLI_EDEVICE;
-    if (launch_logits(*L, x, T, reinterpret_cast<double *>(base + lay.logits), s) != hipSuccess) return COLI_EDEVICE;
     if (record(ev, 1, s)) return COLI_EDEVICE;
     if (launch_select(*L, T, lay, base, nullptr, nullptr, nullptr, nullptr, s) != hipSuccess) return COLI_EDEVICE;
     if (record(ev, 2, s)) return COLI_EDEVICE;
@@ -204,7 +204,8 @@ int coli_moe_route(const coli_moe_layer *L, const float *x, int T, int32_t *idx,
     if (!al16(x) || !al4(idx) || !al4(w)) return COLI_EINVAL;
     hipStream_t s = (hipStream_t)stream;
     char *base = static_cast<char *>(ws);
-    if (launch_logits(*L, x, T, reinterpret_cast<double *>(base + lay.logits), s) != hipSuccess) return COLI_EDEVICE;
+    if (launch_logits(*L, x, T, reinterpret_cast<double *>(base + lay.logits), nullptr, nullptr, s) != hipSuccess)
+        return COLI_EDEVICE;
     return status(launch_select(*L, T, lay, base, nullptr, nullptr, idx, w, s));
 }
 

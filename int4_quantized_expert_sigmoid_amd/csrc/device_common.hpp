@@ -109,26 +109,91 @@ __device__ __forceinline__ T wave_sum(T v, int width = 64)
     return v;
 }
 
+// 64-bit lane exchanges built from 32-bit cross-lane primitives.
+__device__ __forceinline__ int dlo(double v) { return __double2loint(v); }
+__device__ __forceinline__ int dhi(double v) { return __double2hiint(v); }
+__device__ __forceinline__ double dmk(int lo, int hi) { return __hiloint2double(hi, lo); }
+
+// v_permlane32_swap on a pair of doubles: returns (a + b') where, for lanes
+// 0..31, the sum is a[l] + a[l+32] and for lanes 32..63 it is b[l-32] + b[l].
+__device__ __forceinline__ double swap_add32(double a, double b)
+{
+    const auto lo = __builtin_amdgcn_permlane32_swap(dlo(a), dlo(b), false, false);
+    const auto hi = __builtin_amdgcn_permlane32_swap(dhi(a), dhi(b), false, false);
+    return dmk(lo[0], hi[0]) + dmk(lo[1], hi[1]);
+}
+
+// v_permlane16_swap: rows of 16 lanes; even rows get a[l] + a[l+16], odd rows
+// get b[l-16] + b[l].
+__device__ __forceinline__ double swap_add16(double a, double b)
+{
+    const auto lo = __builtin_amdgcn_permlane16_swap(dlo(a), dlo(b), false, false);
+    const auto hi = __builtin_amdgcn_permlane16_swap(dhi(a), dhi(b), false, false);
+    return dmk(lo[0], hi[0]) + dmk(lo[1], hi[1]);
+}
+
+// DPP move of a double (both halves with the same control).
+template <int CTRL>
+__device__ __forceinline__ double dpp_d(double v)
+{
+    return dmk(__builtin_amdgcn_mov_dpp(dlo(v), CTRL, 0xF, 0xF, false),
+               __builtin_amdgcn_mov_dpp(dhi(v), CTRL, 0xF, 0xF, false));
+}
+constexpr int DPP_XOR1 = 0xB1;    // quad_perm [1,0,3,2]
+constexpr int DPP_XOR2 = 0x4E;    // quad_perm [2,3,0,1]
+constexpr int DPP_ROR8 = 0x128;   // row_ror:8 == lane ^ 8 inside a 16-lane row
+
+template <int D>
+__device__ __forceinline__ double xor_lane(double v)
+{
+    if constexpr (D == 1) return dpp_d<DPP_XOR1>(v);
+    else if constexpr (D == 2) return dpp_d<DPP_XOR2>(v);
+    else if constexpr (D == 8) return dpp_d<DPP_ROR8>(v);
+    else return __shfl_xor(v, D);
+}
+
+// One halving step of the transposing reduction at lane distance D on N
+// values: lanes with bit D clear keep the lower half, the others the upper.
+template <int N, int D>
+__device__ __forceinline__ void tr_step(double *v, int lane)
+{
+#pragma unroll
+    for (int i = 0; i < N / 2; ++i) {
+        if constexpr (D == 32) {
+            v[i] = swap_add32(v[i], v[i + N / 2]);
+        } else if constexpr (D == 16) {
+            v[i] = swap_add16(v[i], v[i + N / 2]);
+        } else {
+            const bool upper = (lane & D) != 0;
+            const double lo = v[i], hi = v[i + N / 2];
+            const double keep = upper ? hi : lo;
+            const double send = upper ? lo : hi;
+            v[i] = keep + xor_lane<D>(send);
+        }
+    }
+}
+
+template <int N, int D>
+__device__ __forceinline__ void tr_rec(double *v, int lane)
+{
+    if constexpr (N > 1) {
+        tr_step<N, D>(v, lane);
+        tr_rec<N / 2, D / 2>(v, lane);
+    } else if constexpr (D >= 1) {
+        v[0] += xor_lane<D>(v[0]);
+        tr_rec<1, D / 2>(v, lane);
+    }
+}
+
 // Transposing reduction of N values per lane over a 64-lane wave (N a power
 // of two, N <= 64): afterwards lane l holds the wave-wide sum of value
 // (l >> (6 - log2 N)) & (N - 1) in v[0]. Each halving step sends the half a
-// lane does not keep to its partner, so N values cost N - 1 exchanges.
+// lane does not keep to its partner, so N values cost N - 1 exchanges; the
+// distance-32/16 steps use the gfx950 permlane swaps, which need no select.
 template <int N>
 __device__ __forceinline__ void wave_transpose_reduce(double (&v)[N])
 {
-    const int lane = threadIdx.x & 63;
-    int d = 32;
-#pragma unroll
-    for (int n = N; n > 1; n >>= 1, d >>= 1) {
-        const bool upper = (lane & d) != 0;
-#pragma unroll
-        for (int i = 0; i < n / 2; ++i) {
-            const double keep = upper ? v[i + n / 2] : v[i];
-            const double send = upper ? v[i] : v[i + n / 2];
-            v[i] = keep + __shfl_xor(send, d);
-        }
-    }
-    for (; d >= 1; d >>= 1) v[0] += __shfl_xor(v[0], d);
+    tr_rec<N, 32>(v, threadIdx.x & 63);
 }
 
 template <int N>

@@ -40,7 +40,9 @@ hipError_t launch_zero(void *p, size_t bytes, hipStream_t s);
 hipError_t launch_copy_f32(const float *src, float *dst, size_t n, hipStream_t s);
 
 // ---- router (kernels_route.hip)
-hipError_t launch_logits(const coli_moe_layer &L, const float *x, int T, double *z, hipStream_t s);
+// Router logits z [T][E] (f64); with xq != nullptr also Q8(x) in the reordered layout.
+hipError_t launch_logits(const coli_moe_layer &L, const float *x, int T, double *z, int8_t *xq, float *xs,
+                         hipStream_t s);
 // Top-k of every token from logits (or, with given_idx, from the caller's
 // routing), then the batch union of experts (GEMV path) or the per-expert
 // buckets and tile lists (grouped path).

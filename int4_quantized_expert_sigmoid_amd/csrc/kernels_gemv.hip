@@ -61,20 +61,17 @@ __global__ void __launch_bounds__(256) k_gateup_gemv(GemvArgs a)
         }
     }
     const long row0 = (long)e * a.I + (long)rb * QK;
-    const uint8_t *pg = a.q_a + row0 * rowb + tid * 16;
-    const uint8_t *pu = a.q_b + row0 * rowb + tid * 16;
+    // threads past the row's last block read block 0 and multiply it by zero
+    const int tb = active ? tid : 0;
+    const uint8_t *pg = a.q_a + row0 * rowb + tb * 16;
+    const uint8_t *pu = a.q_b + row0 * rowb + tb * 16;
 
     for (int c = 0; c < QK / RC; ++c) {
         uint4 wg[RC], wu[RC];
 #pragma unroll
         for (int r = 0; r < RC; ++r) {
-            if (active) {
-                wg[r] = load_u4_stream(pg + (long)(c * RC + r) * rowb);
-                wu[r] = load_u4_stream(pu + (long)(c * RC + r) * rowb);
-            } else {
-                wg[r] = make_uint4(0, 0, 0, 0);
-                wu[r] = make_uint4(0, 0, 0, 0);
-            }
+            wg[r] = load_u4_stream(pg + (long)(c * RC + r) * rowb);
+            wu[r] = load_u4_stream(pu + (long)(c * RC + r) * rowb);
         }
         double v[NT][NV];
 #pragma unroll
@@ -147,12 +144,12 @@ __global__ void __launch_bounds__(256) k_down_gemv(GemvArgs a)
     }
     const int rows_per_wave = QK / (blockDim.x >> 6);
     const long row0 = (long)grp * QK + wave * rows_per_wave;
-    const uint8_t *pd = a.q_a + ((long)e * a.H + row0) * rowb + lane * 16;
+    const uint8_t *pd = a.q_a + ((long)e * a.H + row0) * rowb + (active ? lane : 0) * 16;
     for (int c = 0; c < rows_per_wave / RD; ++c) {
         uint4 wd[RD];
 #pragma unroll
         for (int r = 0; r < RD; ++r)
-            wd[r] = active ? load_u4_stream(pd + (long)(c * RD + r) * rowb) : make_uint4(0, 0, 0, 0);
+            wd[r] = load_u4_stream(pd + (long)(c * RD + r) * rowb);
         double v[NT][RD];
 #pragma unroll
         for (int r = 0; r < RD; ++r) {

@@ -17,26 +17,74 @@
 namespace coli {
 namespace {
 
-constexpr int MAX_E = 1024;
-constexpr int EPL = MAX_E / 64;     // experts per lane in a one-wave selection
+constexpr int MAX_E = 512;
+constexpr int SEL_T = 8;            // tokens one selection workgroup handles
 constexpr int TILE_M = 32;          // tokens per grouped-GEMM tile
 
 // ---------------------------------------------------------------- logits
+// Q8 of one 32-wide activation block (reordered layout), the rule of the
+// Q8_0-style quantiser: d = absmax/127, codes rint(x * (1/d)) clamped.
+__device__ __forceinline__ void q8_block_reordered(const float *__restrict__ src, int8_t *__restrict__ dst,
+                                                   float *__restrict__ dsc)
+{
+    float v[QK];
+#pragma unroll
+    for (int i = 0; i < QK / 4; ++i) {
+        const float4 f = reinterpret_cast<const float4 *>(src)[i];
+        v[4 * i] = f.x; v[4 * i + 1] = f.y; v[4 * i + 2] = f.z; v[4 * i + 3] = f.w;
+    }
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < QK; ++i) amax = fmaxf(amax, fabsf(v[i]));
+    float d, id;
+    q8_scale(amax, d, id);
+    int c[QK];
+#pragma unroll
+    for (int i = 0; i < QK; ++i) c[i] = round_clamp(__fmul_rn(v[i], id), -127.0f, 127.0f) & 0xFF;
+    uint32_t o[8];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        o[2 * m] = (uint32_t)(c[8 * m] | (c[8 * m + 2] << 8) | (c[8 * m + 4] << 16) | (c[8 * m + 6] << 24));
+        o[2 * m + 1] = (uint32_t)(c[8 * m + 1] | (c[8 * m + 3] << 8) | (c[8 * m + 5] << 16) | (c[8 * m + 7] << 24));
+    }
+    reinterpret_cast<uint4 *>(dst)[0] = make_uint4(o[0], o[1], o[2], o[3]);
+    reinterpret_cast<uint4 *>(dst)[1] = make_uint4(o[4], o[5], o[6], o[7]);
+    *dsc = d;
+}
+
+// T <= 8: one workgroup per expert computes that expert's logits for every
+// token (f64 sums over float4 loads); the workgroups also share the Q8 of x.
 template <int NT>
 __global__ void __launch_bounds__(256) k_logits_small(const float *__restrict__ W, const float *__restrict__ x,
-                                                      int T, int H, int E, double *__restrict__ z)
+                                                      int T, int H, int E, double *__restrict__ z,
+                                                      int8_t *__restrict__ xq, float *__restrict__ xs)
 {
     __shared__ double red[4][NT];
     const int e = blockIdx.x;
-    const float *we = W + (long)e * H;
+    if (xq != nullptr) {
+        const long nb = (long)T * (H / QK);
+        for (long b = (long)e * blockDim.x + threadIdx.x; b < nb; b += (long)gridDim.x * blockDim.x)
+            q8_block_reordered(x + b * QK, xq + b * QK, xs + b);
+    }
+    typedef float f32x4 __attribute__((ext_vector_type(4)));
+    const f32x4 *we = reinterpret_cast<const f32x4 *>(W + (long)e * H);
     double acc[NT];
 #pragma unroll
     for (int t = 0; t < NT; ++t) acc[t] = 0.0;
-    for (int h = threadIdx.x; h < H; h += blockDim.x) {
-        const double wv = (double)we[h];
+    const int H4 = H / 4;
+#pragma unroll 4
+    for (int h = threadIdx.x; h < H4; h += blockDim.x) {
+        const f32x4 wv = __builtin_nontemporal_load(&we[h]);
 #pragma unroll
-        for (int t = 0; t < NT; ++t)
-            if (t < T) acc[t] = fma(wv, (double)x[(long)t * H + h], acc[t]);
+        for (int t = 0; t < NT; ++t) {
+            if (t < T) {
+                const float4 xv = reinterpret_cast<const float4 *>(x + (long)t * H)[h];
+                acc[t] = fma((double)wv.x, (double)xv.x, acc[t]);
+                acc[t] = fma((double)wv.y, (double)xv.y, acc[t]);
+                acc[t] = fma((double)wv.z, (double)xv.z, acc[t]);
+                acc[t] = fma((double)wv.w, (double)xv.w, acc[t]);
+            }
+        }
     }
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
@@ -89,104 +137,6 @@ __global__ void __launch_bounds__(256) k_logits_tiled(const float *__restrict__ 
 }
 
 // ------------------------------------------------------------- selection
-struct KeyIdx { double key; int idx; };
-
-__device__ __forceinline__ bool better(double ka, int ia, double kb, int ib)
-{
-    return ka > kb || (ka == kb && ia < ib);
-}
-
-// One wave selects the top_k experts of one token from its logits row.
-// Writes idx/w (global) and leaves nothing else behind.
-__device__ void select_topk_wave(const double *__restrict__ zt, const float *__restrict__ bias, int E,
-                                 int top_k, int n_group, int topk_group, float route_scale,
-                                 int32_t *__restrict__ idx_out, float *__restrict__ w_out)
-{
-    const int lane = threadIdx.x & 63;
-    double s[EPL], key[EPL];
-    bool elig[EPL];
-#pragma unroll
-    for (int m = 0; m < EPL; ++m) {
-        const int e = lane + 64 * m;
-        elig[m] = e < E;
-        if (e < E) {
-            s[m] = 1.0 / (1.0 + exp(-zt[e]));
-            key[m] = s[m] + (double)bias[e];
-        } else {
-            s[m] = 0.0; key[m] = 0.0;
-        }
-    }
-    if (n_group > 1) {
-        // group score = sum of the two largest keys of the group
-        const int gsize = E / n_group;
-        unsigned long long kept = 0ull;     // groups kept (n_group <= 64)
-        double gscore_lane = -INFINITY;     // lane g holds the score of group g
-        for (int g = 0; g < n_group; ++g) {
-            double b1 = -INFINITY; int i1 = MAX_E;
-#pragma unroll
-            for (int m = 0; m < EPL; ++m) {
-                const int e = lane + 64 * m;
-                if (e < E && e / gsize == g && better(key[m], e, b1, i1)) { b1 = key[m]; i1 = e; }
-            }
-            for (int o = 32; o > 0; o >>= 1) {
-                const double ob = __shfl_xor(b1, o); const int oi = __shfl_xor(i1, o);
-                if (better(ob, oi, b1, i1)) { b1 = ob; i1 = oi; }
-            }
-            double b2 = -INFINITY;
-#pragma unroll
-            for (int m = 0; m < EPL; ++m) {
-                const int e = lane + 64 * m;
-                if (e < E && e / gsize == g && e != i1 && key[m] > b2) b2 = key[m];
-            }
-            b2 = wave_max(b2);
-            const double score = gsize >= 2 ? b1 + b2 : b1;
-            if (lane == g) gscore_lane = score;
-        }
-        for (int pick = 0; pick < topk_group; ++pick) {
-            double bs = (lane < n_group && !((kept >> lane) & 1ull)) ? gscore_lane : -INFINITY;
-            int bi = (lane < n_group && !((kept >> lane) & 1ull)) ? lane : MAX_E;
-            for (int o = 32; o > 0; o >>= 1) {
-                const double ob = __shfl_xor(bs, o); const int oi = __shfl_xor(bi, o);
-                if (better(ob, oi, bs, bi)) { bs = ob; bi = oi; }
-            }
-            kept |= 1ull << bi;
-        }
-#pragma unroll
-        for (int m = 0; m < EPL; ++m) {
-            const int e = lane + 64 * m;
-            if (e < E) elig[m] = (kept >> (e / gsize)) & 1ull;
-        }
-    }
-    double ssel[COLI_MAX_TOPK];
-    int isel[COLI_MAX_TOPK];
-    double ssum = 0.0;
-    for (int j = 0; j < top_k; ++j) {
-        double bk = -INFINITY; int bi = MAX_E; double bs = 0.0;
-#pragma unroll
-        for (int m = 0; m < EPL; ++m) {
-            const int e = lane + 64 * m;
-            if (elig[m] && (bi == MAX_E || better(key[m], e, bk, bi))) { bk = key[m]; bi = e; bs = s[m]; }
-        }
-        for (int o = 32; o > 0; o >>= 1) {
-            const double ok = __shfl_xor(bk, o); const int oi = __shfl_xor(bi, o);
-            const double os = __shfl_xor(bs, o);
-            if (oi != MAX_E && (bi == MAX_E || better(ok, oi, bk, bi))) { bk = ok; bi = oi; bs = os; }
-        }
-#pragma unroll
-        for (int m = 0; m < EPL; ++m)
-            if (lane + 64 * m == bi) elig[m] = false;
-        isel[j < COLI_MAX_TOPK ? j : 0] = bi;
-        ssel[j < COLI_MAX_TOPK ? j : 0] = bs;
-        ssum += bs;
-    }
-    for (int j = 0; j < top_k; ++j) {
-        if (lane == j) {
-            idx_out[j] = isel[j];
-            w_out[j] = (float)((double)route_scale * ssel[j] / ssum);
-        }
-    }
-}
-
 struct SelArgs {
     const double *z;
     const float *bias;
@@ -201,9 +151,80 @@ struct SelArgs {
     int *pair_of, *shared_pair;
 };
 
-// T <= 8: top-k of every token (one wave per token), then the batch union.
-__global__ void __launch_bounds__(256) k_select_union(SelArgs a)
+struct SelShared {
+    double key[SEL_T][MAX_E];      // selection keys; -inf where the group is not kept
+    double gscore[SEL_T][64];
+    double ssel[SEL_T][COLI_MAX_TOPK];
+    int isel[SEL_T][COLI_MAX_TOPK];
+};
+
+// Top-k of nt tokens (t0 ..) by rank: expert e is chosen at position
+// rank(e) = #{e' : key_e' > key_e, or key_e' == key_e and e' < e} when that
+// rank is below top_k. This is the largest-first order with ties to the lower
+// index; every rank is computed independently, so no serial argmax chain.
+__device__ void select_tokens_block(const SelArgs &a, int t0, int nt, SelShared &sh)
 {
+    const int E = a.E, k = a.top_k;
+    const int tid = threadIdx.x, nth = blockDim.x;
+    for (int i = tid; i < nt * E; i += nth) {
+        const int t = i / E, e = i % E;
+        const double s = 1.0 / (1.0 + exp(-a.z[(long)(t0 + t) * E + e]));
+        sh.key[t][e] = s + (double)a.bias[e];
+    }
+    __syncthreads();
+    if (a.n_group > 1) {
+        const int gsize = E / a.n_group;
+        for (int i = tid; i < nt * a.n_group; i += nth) {
+            const int t = i / a.n_group, g = i % a.n_group;
+            double m1 = -INFINITY, m2 = -INFINITY;       // two largest keys, in index order
+            for (int e = g * gsize; e < (g + 1) * gsize; ++e) {
+                const double v = sh.key[t][e];
+                if (v > m1) { m2 = m1; m1 = v; }
+                else if (v > m2) { m2 = v; }
+            }
+            sh.gscore[t][g] = gsize >= 2 ? m1 + m2 : m1;
+        }
+        __syncthreads();
+        for (int i = tid; i < nt * E; i += nth) {
+            const int t = i / E, e = i % E, g = e / gsize;
+            const double gs = sh.gscore[t][g];
+            int r = 0;
+            for (int g2 = 0; g2 < a.n_group; ++g2) {
+                const double o = sh.gscore[t][g2];
+                r += (o > gs) || (o == gs && g2 < g);
+            }
+            if (r >= a.topk_group) sh.key[t][e] = -INFINITY;   // keys stay finite otherwise
+        }
+        __syncthreads();
+    }
+    for (int i = tid; i < nt * E; i += nth) {
+        const int t = i / E, e = i % E;
+        const double ke = sh.key[t][e];
+        if (ke == -INFINITY) continue;
+        int r = 0;
+        for (int e2 = 0; e2 < E; ++e2) {
+            const double o = sh.key[t][e2];
+            r += (o > ke) || (o == ke && e2 < e);
+        }
+        if (r < k) {
+            sh.isel[t][r] = e;
+            sh.ssel[t][r] = 1.0 / (1.0 + exp(-a.z[(long)(t0 + t) * E + e]));
+        }
+    }
+    __syncthreads();
+    for (int i = tid; i < nt * k; i += nth) {
+        const int t = i / k, j = i % k;
+        double ssum = 0.0;
+        for (int jj = 0; jj < k; ++jj) ssum += sh.ssel[t][jj];
+        a.idx[(long)(t0 + t) * k + j] = sh.isel[t][j];
+        a.w[(long)(t0 + t) * k + j] = (float)((double)a.route_scale * sh.ssel[t][j] / ssum);
+    }
+}
+
+// T <= 8: top-k of every token, then the batch union.
+__global__ void __launch_bounds__(1024) k_select_union(SelArgs a)
+{
+    __shared__ SelShared sh;
     __shared__ int item_of[MAX_E + 1];
     __shared__ int slot_count[8 * COLI_MAX_TOPK + 1];
     __shared__ int n_items_s;
@@ -217,9 +238,7 @@ __global__ void __launch_bounds__(256) k_select_union(SelArgs a)
             a.w[i] = a.given_w[i];
         }
     } else {
-        for (int t = wave; t < a.T; t += (int)(blockDim.x >> 6))
-            select_topk_wave(a.z + (long)t * a.E, a.bias, a.E, a.top_k, a.n_group, a.topk_group,
-                             a.route_scale, a.idx + t * a.top_k, a.w + t * a.top_k);
+        select_tokens_block(a, 0, a.T, sh);
     }
     __syncthreads();
     if (a.idx_user)
@@ -276,22 +295,22 @@ __global__ void __launch_bounds__(256) k_select_union(SelArgs a)
     if (threadIdx.x == 0) a.ctrl[CTRL_N_ITEMS] = n_items;
 }
 
-// T > 8: one wave per token.
+// T > 8: one workgroup per token.
 __global__ void __launch_bounds__(256) k_select_tokens(SelArgs a)
 {
-    const int t = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
-    if (t >= a.T) return;
+    __shared__ SelShared sh;
+    const int t = blockIdx.x;
     if (a.given_idx) {
-        for (int j = threadIdx.x & 63; j < a.top_k; j += 64) {
+        for (int j = threadIdx.x; j < a.top_k; j += blockDim.x) {
             a.idx[t * a.top_k + j] = a.given_idx[t * a.top_k + j];
             a.w[t * a.top_k + j] = a.given_w[t * a.top_k + j];
         }
+        __syncthreads();
     } else {
-        select_topk_wave(a.z + (long)t * a.E, a.bias, a.E, a.top_k, a.n_group, a.topk_group,
-                         a.route_scale, a.idx + t * a.top_k, a.w + t * a.top_k);
+        select_tokens_block(a, t, 1, sh);
     }
     if (a.idx_user)
-        for (int j = threadIdx.x & 63; j < a.top_k; j += 64) {
+        for (int j = threadIdx.x; j < a.top_k; j += blockDim.x) {
             a.idx_user[t * a.top_k + j] = a.idx[t * a.top_k + j];
             a.w_user[t * a.top_k + j] = a.w[t * a.top_k + j];
         }
@@ -359,19 +378,25 @@ __global__ void __launch_bounds__(1024) k_bucket(BucketArgs a)
 
 } // namespace
 
-hipError_t launch_logits(const coli_moe_layer &L, const float *x, int T, double *z, hipStream_t s)
+hipError_t launch_logits(const coli_moe_layer &L, const float *x, int T, double *z, int8_t *xq, float *xs,
+                         hipStream_t s)
 {
-    if (T <= 1)
-        hipLaunchKernelGGL(k_logits_small<1>, dim3(L.E), dim3(256), 0, s, L.router_w, x, T, L.H, L.E, z);
-    else if (T <= 2)
-        hipLaunchKernelGGL(k_logits_small<2>, dim3(L.E), dim3(256), 0, s, L.router_w, x, T, L.H, L.E, z);
-    else if (T <= 4)
-        hipLaunchKernelGGL(k_logits_small<4>, dim3(L.E), dim3(256), 0, s, L.router_w, x, T, L.H, L.E, z);
-    else if (T <= 8)
-        hipLaunchKernelGGL(k_logits_small<8>, dim3(L.E), dim3(256), 0, s, L.router_w, x, T, L.H, L.E, z);
-    else
+    if (T > 8) {
+        if (xq) {
+            hipError_t e = launch_quant_q8(x, T, L.H, xq, xs, true, s);
+            if (e != hipSuccess) return e;
+        }
         hipLaunchKernelGGL(k_logits_tiled, dim3((T + 31) / 32, (L.E + 31) / 32), dim3(256), 0, s, L.router_w,
                            x, T, L.H, L.E, z);
+    } else if (T <= 1) {
+        hipLaunchKernelGGL(k_logits_small<1>, dim3(L.E), dim3(256), 0, s, L.router_w, x, T, L.H, L.E, z, xq, xs);
+    } else if (T <= 2) {
+        hipLaunchKernelGGL(k_logits_small<2>, dim3(L.E), dim3(256), 0, s, L.router_w, x, T, L.H, L.E, z, xq, xs);
+    } else if (T <= 4) {
+        hipLaunchKernelGGL(k_logits_small<4>, dim3(L.E), dim3(256), 0, s, L.router_w, x, T, L.H, L.E, z, xq, xs);
+    } else {
+        hipLaunchKernelGGL(k_logits_small<8>, dim3(L.E), dim3(256), 0, s, L.router_w, x, T, L.H, L.E, z, xq, xs);
+    }
     return hipGetLastError();
 }
 
@@ -395,10 +420,10 @@ hipError_t launch_select(const coli_moe_layer &L, int T, const WsLayout &lay, ch
     a.pair_of = reinterpret_cast<int *>(ws + lay.pair_of);
     a.shared_pair = reinterpret_cast<int *>(ws + lay.shared_pair);
     if (lay.path == 0) {
-        hipLaunchKernelGGL(k_select_union, dim3(1), dim3(256), 0, s, a);
+        hipLaunchKernelGGL(k_select_union, dim3(1), dim3(1024), 0, s, a);
         return hipGetLastError();
     }
-    hipLaunchKernelGGL(k_select_tokens, dim3((T + 3) / 4), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(k_select_tokens, dim3(T), dim3(256), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     BucketArgs b;

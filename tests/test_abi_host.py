@@ -61,7 +61,7 @@ def test_workspace_sizes():
 
 
 @pytest.mark.parametrize("bad", [
-    dict(H=48), dict(I=40), dict(E=0), dict(E=2000), dict(top_k=0), dict(top_k=17), dict(top_k=9, E=8),
+    dict(H=48), dict(I=40), dict(E=0), dict(E=600), dict(top_k=0), dict(top_k=17), dict(top_k=9, E=8),
     dict(n_group=3), dict(n_group=8, topk_group=9), dict(n_group=8, topk_group=1, top_k=33),
     dict(has_shared=2), dict(route_scale=float("nan")),
 ])
