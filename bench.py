@@ -30,7 +30,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
-STAGES = ["q8_logits", "select_union", "gateup_gemv", "down_gemv", "combine"]
+STAGES = ["route_shared_gateup", "select_shared_down", "gateup_gemv", "down_gemv", "combine"]
 
 
 def parse():
@@ -124,8 +124,10 @@ def main():
             routes.append(idx.cpu().numpy())
     union = [len(set(r.reshape(-1).tolist())) for r in routes]
     bytes_step = [(u + spec.has_shared) * spec.expert_bytes for u in union]
-    gateup_bytes = [(u + spec.has_shared) * 2 * spec.I * (spec.H // 2 + 4) for u in union]
-    down_bytes = [(u + spec.has_shared) * spec.H * (spec.I // 2 + 4) for u in union]
+    # the routed gate/up and down launches stream the U routed experts only
+    # (the shared expert's matrices ride along the two router launches)
+    gateup_bytes = [u * 2 * spec.I * (spec.H // 2 + 4) for u in union]
+    down_bytes = [u * spec.H * (spec.I // 2 + 4) for u in union]
 
     # ---------------- timed region: K steps (graph replays of G steps)
     K = max(G, (args.steps + G - 1) // G * G)

@@ -36,6 +36,8 @@ bool layer_ok(const coli_moe_layer *L)
 
 bool gemv_shape_ok(const coli_moe_layer &L) { return L.H <= 8192 && L.I <= 2048; }
 
+constexpr int KNOWN_FLAGS = COLI_ACCUMULATE | COLI_PATH_GEMV | COLI_PATH_GROUPED | COLI_PATH_FUSED;
+
 int choose_path(const coli_moe_layer &L, int T, int flags)
 {
     if (flags & COLI_PATH_GROUPED) return 1;
@@ -83,6 +85,7 @@ WsLayout make_layout(const coli_moe_layer &L, int T, int path)
     o.hq = p; p = up(p + n_pairs * I);
     o.hs = p; p = up(p + n_pairs * (I / 32) * 4);
     o.ye = p; p = up(p + n_pairs * H * 4);
+    o.sync = p; p = up(p + (path == 0 ? sizeof(FusedSync) : 0));
     o.total = p;
     return o;
 }
@@ -121,13 +124,14 @@ int coli_moe_workspace_init(void *ws, size_t ws_bytes, void *stream)
 int coli_moe_workspace_layout(const coli_moe_layer *L, int T, int flags, coli_moe_ws_layout *out)
 {
     if (!layer_ok(L) || T < 1 || T > COLI_MAX_T || !out) return COLI_EINVAL;
-    if (flags & ~(COLI_ACCUMULATE | COLI_PATH_GEMV | COLI_PATH_GROUPED)) return COLI_EINVAL;
+    if (flags & ~KNOWN_FLAGS) return COLI_EINVAL;
     const int path = choose_path(*L, T, flags);
     const WsLayout l = make_layout(*L, T, path);
     out->xq = l.xq; out->xs = l.xs; out->idx = l.idx; out->w = l.w;
     out->pair_of = l.pair_of; out->shared_pair = l.shared_pair;
     out->h = l.h; out->hq = l.hq; out->hs = l.hs; out->ye = l.ye;
     out->n_pairs_max = (size_t)l.n_pairs;
+    out->sync = l.sync;
     out->path = path;
     return COLI_OK;
 }
@@ -136,11 +140,12 @@ static int check_common(const coli_moe_layer *L, int T, int flags, void *ws, siz
                         WsLayout &lay)
 {
     if (!layer_ok(L) || T < 1 || T > COLI_MAX_T) return COLI_EINVAL;
-    if (flags & ~(COLI_ACCUMULATE | COLI_PATH_GEMV | COLI_PATH_GROUPED)) return COLI_EINVAL;
+    if (flags & ~KNOWN_FLAGS) return COLI_EINVAL;
     if ((flags & COLI_PATH_GEMV) && (flags & COLI_PATH_GROUPED)) return COLI_EINVAL;
     if ((flags & COLI_PATH_GEMV) && (T > COLI_GEMV_MAX_T || !gemv_shape_ok(*L))) return COLI_EINVAL;
     if (!al16(ws)) return COLI_EINVAL;
     path = choose_path(*L, T, flags);
+    if ((flags & COLI_PATH_FUSED) && path != 0) return COLI_EINVAL;
     lay = make_layout(*L, T, path);
     if (ws_bytes < lay.total) return COLI_EWORKSPACE;
     return COLI_OK;
@@ -152,14 +157,15 @@ static int record(void *const *ev, int i, hipStream_t s)
     return hipEventRecord((hipEvent_t)ev[i], s) == hipSuccess ? COLI_OK : COLI_EDEVICE;
 }
 
+// Expert launches from item0 on (item0 = 1: the shared expert already ran).
 static int run_experts(const coli_moe_layer *L, int T, const WsLayout &lay, char *ws, float *y, int flags,
-                       hipStream_t s, void *const *ev)
+                       int item0, hipStream_t s, void *const *ev)
 {
     hipError_t e;
     if (lay.path == 0) {
-        if ((e = launch_gateup_gemv(*L, T, lay, ws, s)) != hipSuccess) return COLI_EDEVICE;
+        if ((e = launch_gateup_gemv(*L, T, lay, ws, item0, s)) != hipSuccess) return COLI_EDEVICE;
         if (record(ev, 3, s)) return COLI_EDEVICE;
-        if ((e = launch_down_gemv(*L, T, lay, ws, s)) != hipSuccess) return COLI_EDEVICE;
+        if ((e = launch_down_gemv(*L, T, lay, ws, item0, s)) != hipSuccess) return COLI_EDEVICE;
         if (record(ev, 4, s)) return COLI_EDEVICE;
     } else {
         if ((e = launch_gateup_grouped(*L, T, lay, ws, s)) != hipSuccess) return COLI_EDEVICE;
@@ -184,6 +190,21 @@ static int forward_impl(const coli_moe_layer *L, const float *x, int T, float *y
     hipStream_t s = (hipStream_t)stream;
     char *base = static_cast<char *>(ws);
     if (record(ev, 0, s)) return COLI_EDEVICE;
+    if (path == 0 && (flags & COLI_PATH_FUSED)) {
+        if (launch_decode_fused(*L, x, T, lay, base, y, (flags & COLI_ACCUMULATE) != 0, s) != hipSuccess)
+            return COLI_EDEVICE;
+        for (int i = 1; i < COLI_PROFILE_EVENTS; ++i)
+            if (record(ev, i, s)) return COLI_EDEVICE;
+        return COLI_OK;
+    }
+    if (path == 0) {
+        // the shared expert rides along with the router launches
+        if (launch_route_shared_gateup(*L, x, T, lay, base, s) != hipSuccess) return COLI_EDEVICE;
+        if (record(ev, 1, s)) return COLI_EDEVICE;
+        if (launch_select_shared_down(*L, T, lay, base, s) != hipSuccess) return COLI_EDEVICE;
+        if (record(ev, 2, s)) return COLI_EDEVICE;
+        return run_experts(L, T, lay, base, y, flags, L->has_shared, s, ev);
+    }
     if (launch_logits(*L, x, T, reinterpret_cast<double *>(base + lay.logits),
                       reinterpret_cast<int8_t *>(base + lay.xq), reinterpret_cast<float *>(base + lay.xs),
                       s) != hipSuccess)
@@ -191,7 +212,7 @@ static int forward_impl(const coli_moe_layer *L, const float *x, int T, float *y
     if (record(ev, 1, s)) return COLI_EDEVICE;
     if (launch_select(*L, T, lay, base, nullptr, nullptr, nullptr, nullptr, s) != hipSuccess) return COLI_EDEVICE;
     if (record(ev, 2, s)) return COLI_EDEVICE;
-    return run_experts(L, T, lay, base, y, flags, s, ev);
+    return run_experts(L, T, lay, base, y, flags, 0, s, ev);
 }
 
 int coli_moe_route(const coli_moe_layer *L, const float *x, int T, int32_t *idx, float *w, void *ws,
@@ -239,7 +260,7 @@ int coli_moe_experts(const coli_moe_layer *L, const int8_t *xq, const float *xs,
     if (launch_copy_f32(xs, reinterpret_cast<float *>(base + lay.xs), (size_t)T * (L->H / 32), s) != hipSuccess)
         return COLI_EDEVICE;
     if (launch_select(*L, T, lay, base, idx, w, nullptr, nullptr, s) != hipSuccess) return COLI_EDEVICE;
-    return run_experts(L, T, lay, base, y, flags, s, nullptr);
+    return run_experts(L, T, lay, base, y, flags, 0, s, nullptr);
 }
 
 int coli_rmsnorm(const float *x, const float *gamma, int T, int H, float eps, float *out, void *stream)

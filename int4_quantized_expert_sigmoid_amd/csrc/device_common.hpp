@@ -73,6 +73,37 @@ __device__ __forceinline__ uint4 load_u4_stream(const uint8_t *p)
     return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+// Device-coherent relaxed accesses for data one workgroup hands to another in
+// the same launch: they reach the device coherence point without an L2-wide
+// writeback or invalidate, so no agent-scope fence is needed around them.
+__device__ __forceinline__ void st_dev(float *p, float v)
+{
+    __hip_atomic_store(reinterpret_cast<unsigned *>(p), __float_as_uint(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_dev(int *p, int v)
+{
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_dev(double *p, double v)
+{
+    __hip_atomic_store(reinterpret_cast<unsigned long long *>(p), (unsigned long long)__double_as_longlong(v),
+                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_dev(const float *p)
+{
+    return __uint_as_float(__hip_atomic_load(reinterpret_cast<const unsigned *>(p), __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT));
+}
+__device__ __forceinline__ int ld_dev(const int *p)
+{
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ double ld_dev(const double *p)
+{
+    return __longlong_as_double((long long)__hip_atomic_load(reinterpret_cast<const unsigned long long *>(p),
+                                                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+}
+
 // Round half to even and clamp, the rule shared by both quantisers; a NaN
 // product (0 * inf) gives 0.
 __device__ __forceinline__ int round_clamp(float v, float lo, float hi)
@@ -90,6 +121,43 @@ __device__ __forceinline__ void q8_scale(float amax, float &d, float &id)
 {
     d = __fdiv_rn(amax, 127.0f);
     id = (d != 0.0f) ? __fdiv_rn(1.0f, d) : 0.0f;
+}
+
+// Q8 of one 32-wide activation block into registers in the reordered layout:
+// the Q8_0-style rule d = absmax/127, codes rint(x * (1/d)) clamped to +-127.
+__device__ __forceinline__ void q8_block_regs(const float *__restrict__ src, uint32_t (&o)[8], float &dsc)
+{
+    float v[QK];
+#pragma unroll
+    for (int i = 0; i < QK / 4; ++i) {
+        const float4 f = reinterpret_cast<const float4 *>(src)[i];
+        v[4 * i] = f.x; v[4 * i + 1] = f.y; v[4 * i + 2] = f.z; v[4 * i + 3] = f.w;
+    }
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < QK; ++i) amax = fmaxf(amax, fabsf(v[i]));
+    float d, id;
+    q8_scale(amax, d, id);
+    int c[QK];
+#pragma unroll
+    for (int i = 0; i < QK; ++i) c[i] = round_clamp(__fmul_rn(v[i], id), -127.0f, 127.0f) & 0xFF;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        o[2 * m] = (uint32_t)(c[8 * m] | (c[8 * m + 2] << 8) | (c[8 * m + 4] << 16) | (c[8 * m + 6] << 24));
+        o[2 * m + 1] = (uint32_t)(c[8 * m + 1] | (c[8 * m + 3] << 8) | (c[8 * m + 5] << 16) | (c[8 * m + 7] << 24));
+    }
+    dsc = d;
+}
+
+__device__ __forceinline__ void q8_block_reordered(const float *__restrict__ src, int8_t *__restrict__ dst,
+                                                   float *__restrict__ dsc)
+{
+    uint32_t o[8];
+    float d;
+    q8_block_regs(src, o, d);
+    reinterpret_cast<uint4 *>(dst)[0] = make_uint4(o[0], o[1], o[2], o[3]);
+    reinterpret_cast<uint4 *>(dst)[1] = make_uint4(o[4], o[5], o[6], o[7]);
+    *dsc = d;
 }
 
 template <typename T>

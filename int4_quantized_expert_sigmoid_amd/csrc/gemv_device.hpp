@@ -1,0 +1,272 @@
+// gemv_device.hpp — device bodies of the token-GEMV expert path (T <= 8),
+// shared by the standalone GEMV kernels and the fused decode kernel.
+//
+// What is computed (colibri architecture overview, sections 3.1 and 5; the
+// IDOT path dot_i4i8): for every item (a distinct expert of the batch, read
+// once, with up to 8 token slots) and every row,
+//   g_row = d_row * sum_b d_b * S_b,  S_b = sum_{k in b} code4 * q8   (int32),
+// the block sum in f64; h = silu(g) * u (f64, stored f32); Q8(h) in 32-row
+// blocks; then the down projection the same way.
+//
+// Gate/up mapping: a workgroup owns 32 consecutive rows of one item. Thread
+// b owns the 32-wide block column b of every row and streams that 16-byte
+// piece (lanes of a wave read 1 KB contiguous per load); the activation block
+// of each token slot stays in registers. Rows are taken in chunks with the
+// next chunk's loads in flight while the current one is reduced. Per-row
+// partials are folded with a transposing wave reduction, then across waves
+// through LDS in wave order.
+// Down mapping: each wave owns 8 rows; lane l owns block column l.
+#pragma once
+#include "device_common.hpp"
+
+namespace coli {
+
+struct GemvArgs {
+    const uint8_t *q_a, *q_b;      // gate, up (gate/up) or down (down)
+    const float *s_a, *s_b;
+    int H, I, E, T;
+    int item0;                     // first item of a launch that covers items item0.. only
+    const float *x;                // [T][H] layer input (coherent mode quantises it on the fly)
+    const int8_t *xq;              // [T][H] reordered Q8(x)
+    const float *xs;               // [T][H/32]
+    const int *ctrl, *item_expert, *item_ntok, *item_tok;
+    float *h;                      // [pairs][I]
+    int8_t *hq;                    // [pairs][I] reordered
+    float *hs;                     // [pairs][I/32]
+    float *ye;                     // [pairs][H]
+};
+
+struct ItemDesc {
+    int item, e, nt;
+    int tok[MAX_SLOTS];
+};
+
+// A value another workgroup of the same launch may have written.
+__device__ __forceinline__ int ld_shared_int(const int *p) { return ld_dev(p); }
+
+// The item's expert and token slots from the union lists.
+__device__ __forceinline__ ItemDesc item_from_union(const GemvArgs &a, int item)
+{
+    ItemDesc d;
+    d.item = item;
+    // all loads issued together (one round trip); slots past nt are unused
+    d.e = ld_shared_int(a.item_expert + item);
+    d.nt = ld_shared_int(a.item_ntok + item);
+#pragma unroll
+    for (int s = 0; s < MAX_SLOTS; ++s) d.tok[s] = ld_shared_int(a.item_tok + item * MAX_SLOTS + s);
+#pragma unroll
+    for (int s = 0; s < MAX_SLOTS; ++s) d.tok[s] = s < d.nt ? d.tok[s] : 0;
+    return d;
+}
+
+// The shared expert: item 0, slot t = token t (known before routing).
+__device__ __forceinline__ ItemDesc shared_item(const GemvArgs &a)
+{
+    ItemDesc d;
+    d.item = 0;
+    d.e = a.E;
+    d.nt = a.T;
+#pragma unroll
+    for (int s = 0; s < MAX_SLOTS; ++s) d.tok[s] = s;
+    return d;
+}
+
+template <int NT>
+struct GateUpShared {
+    double red[4][NT][64];
+};
+
+// Gate/up rows [rb*32, rb*32+32) of one item for its token slots, SwiGLU,
+// Q8(h); writes h, hq, hs of pairs item*8 + slot. All threads of the
+// workgroup must call it (blockDim = 64 * ceil(H/32/64), at most 256).
+// ONFLY: Q8(x) is computed here from x instead of read from xq. COHERENT
+// (single-launch path): hq/hs are handed on with device-coherent stores.
+template <int NT, int RC, bool ONFLY, bool COHERENT>
+__device__ __forceinline__ void gateup_rows(const GemvArgs &a, const ItemDesc &it, int rb, GateUpShared<NT> &sh)
+{
+    constexpr int NV = 2 * RC;                   // values per chunk: RC rows x (gate, up)
+    constexpr int NC = QK / RC;                  // chunks
+    const int nrb = a.I / QK;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int nblk = a.H / QK;
+    const int nw = (nblk + 63) >> 6;             // waves that own block columns
+    const long rowb = (long)(a.H / 2);
+    const long row0 = (long)it.e * a.I + (long)rb * QK;
+
+    if (wave < nw) {
+        const bool active = tid < nblk;
+        Blk8 act[NT];
+        double dsc[NT];
+#pragma unroll
+        for (int s = 0; s < NT; ++s) {
+            if (s < it.nt && active) {
+                const int t = it.tok[s];
+                if constexpr (ONFLY) {
+                    uint32_t o[8];
+                    float d;
+                    q8_block_regs(a.x + (long)t * a.H + tid * QK, o, d);
+#pragma unroll
+                    for (int k = 0; k < 8; ++k) act[s].v[k] = (int)o[k];
+                    dsc[s] = (double)d * 0.0625;
+                } else {
+                    act[s] = load_blk8(a.xq + (long)t * a.H + tid * QK);
+                    dsc[s] = (double)a.xs[(long)t * nblk + tid] * 0.0625;
+                }
+            } else {
+#pragma unroll
+                for (int k = 0; k < 8; ++k) act[s].v[k] = 0;
+                dsc[s] = 0.0;
+            }
+        }
+        // threads past the row's last block read block 0 and multiply it by zero
+        const int tb = active ? tid : 0;
+        const uint8_t *pg = a.q_a + row0 * rowb + tb * 16;
+        const uint8_t *pu = a.q_b + row0 * rowb + tb * 16;
+
+        uint4 wg[2][RC], wu[2][RC];
+#pragma unroll
+        for (int r = 0; r < RC; ++r) {
+            wg[0][r] = load_u4_stream(pg + (long)r * rowb);
+            wu[0][r] = load_u4_stream(pu + (long)r * rowb);
+        }
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            const int cur = c & 1;
+            if (c + 1 < NC) {
+#pragma unroll
+                for (int r = 0; r < RC; ++r) {
+                    wg[cur ^ 1][r] = load_u4_stream(pg + (long)((c + 1) * RC + r) * rowb);
+                    wu[cur ^ 1][r] = load_u4_stream(pu + (long)((c + 1) * RC + r) * rowb);
+                }
+            }
+            double v[NT][NV];
+#pragma unroll
+            for (int r = 0; r < RC; ++r) {
+                int lo[4], hi[4];
+                unpack_nibbles(wg[cur][r], lo, hi);
+#pragma unroll
+                for (int s = 0; s < NT; ++s) v[s][2 * r] = (double)dot_block16(lo, hi, act[s]) * dsc[s];
+                unpack_nibbles(wu[cur][r], lo, hi);
+#pragma unroll
+                for (int s = 0; s < NT; ++s) v[s][2 * r + 1] = (double)dot_block16(lo, hi, act[s]) * dsc[s];
+            }
+            const int vi = transpose_index<NV>(lane);
+#pragma unroll
+            for (int s = 0; s < NT; ++s) {
+                wave_transpose_reduce<NV>(v[s]);
+                if ((lane & (64 / NV - 1)) == 0) sh.red[wave][s][2 * c * RC + vi] = v[s][0];
+            }
+        }
+    }
+    __syncthreads();
+
+    for (int i = tid; i < NT * QK; i += blockDim.x) {
+        const int s = i / QK, r = i % QK;
+        if (s >= it.nt) continue;                // uniform over the 32 lanes of a slot
+        double g = sh.red[0][s][2 * r], u = sh.red[0][s][2 * r + 1];
+        for (int w = 1; w < nw; ++w) { g += sh.red[w][s][2 * r]; u += sh.red[w][s][2 * r + 1]; }
+        const long grow = row0 + r;
+        const float gf = (float)((double)a.s_a[grow] * g);
+        const float uf = (float)((double)a.s_b[grow] * u);
+        const float hv = (float)(silu_f64((double)gf) * (double)uf);
+        const float amax = wave_max(fabsf(hv), 32);
+        float d, id;
+        q8_scale(amax, d, id);
+        const int code = round_clamp(__fmul_rn(hv, id), -127.0f, 127.0f);
+        const long pair = (long)it.item * MAX_SLOTS + s;
+        a.h[pair * a.I + rb * QK + r] = hv;
+        if constexpr (COHERENT) {
+            // reordered dword 2g holds rows 8g+{0,2,4,6}, dword 2g+1 rows 8g+{1,3,5,7}
+            const int c0 = code & 0xFF;
+            const int c1 = __shfl_down(c0, 2, 32), c2 = __shfl_down(c0, 4, 32), c3 = __shfl_down(c0, 6, 32);
+            if ((r & 7) < 2) {
+                const int word = c0 | (c1 << 8) | (c2 << 16) | (c3 << 24);
+                st_dev(reinterpret_cast<int *>(a.hq + pair * a.I + rb * QK) + 2 * (r >> 3) + (r & 1), word);
+            }
+            if (r == 0) st_dev(a.hs + pair * nrb + rb, d);
+        } else {
+            a.hq[pair * a.I + rb * QK + (r & ~7) + perm8(r & 7)] = (int8_t)code;
+            if (r == 0) a.hs[pair * nrb + rb] = d;
+        }
+    }
+    __syncthreads();
+}
+
+// Down rows of one item for row group grp of 4*RPW rows (each wave RPW rows,
+// lane l owns block column l; chunks of RD rows with the next chunk's loads in
+// flight); writes ye of pairs item*8 + slot. blockDim = 256. COHERENT: hq/hs
+// are read and ye is written with device-coherent accesses.
+template <int NT, int RD, bool COHERENT, int RPW>
+__device__ __forceinline__ void down_rows(const GemvArgs &a, const ItemDesc &it, int grp)
+{
+    constexpr int NC = RPW / RD;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int nblk = a.I / QK;
+    const bool active = lane < nblk;
+    const long rowb = (long)(a.I / 2);
+    const long row0 = (long)grp * (4 * RPW) + wave * RPW;
+    const uint8_t *pd = a.q_a + ((long)it.e * a.H + row0) * rowb + (active ? lane : 0) * 16;
+
+    uint4 wd[2][RD];
+#pragma unroll
+    for (int r = 0; r < RD; ++r) wd[0][r] = load_u4_stream(pd + (long)r * rowb);
+
+    Blk8 act[NT];
+    double dsc[NT];
+#pragma unroll
+    for (int s = 0; s < NT; ++s) {
+        if (s < it.nt && active) {
+            const long pair = (long)it.item * MAX_SLOTS + s;
+            if constexpr (COHERENT) {
+                const int *src = reinterpret_cast<const int *>(a.hq + pair * a.I + lane * QK);
+#pragma unroll
+                for (int k = 0; k < 8; ++k) act[s].v[k] = ld_dev(src + k);
+                dsc[s] = (double)ld_dev(a.hs + pair * nblk + lane) * 0.0625;
+            } else {
+                act[s] = load_blk8(a.hq + pair * a.I + lane * QK);
+                dsc[s] = (double)a.hs[pair * nblk + lane] * 0.0625;
+            }
+        } else {
+#pragma unroll
+            for (int k = 0; k < 8; ++k) act[s].v[k] = 0;
+            dsc[s] = 0.0;
+        }
+    }
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+        const int cur = c & 1;
+        if (c + 1 < NC) {
+#pragma unroll
+            for (int r = 0; r < RD; ++r) wd[cur ^ 1][r] = load_u4_stream(pd + (long)((c + 1) * RD + r) * rowb);
+        }
+        double v[NT][RD];
+#pragma unroll
+        for (int r = 0; r < RD; ++r) {
+            int lo[4], hi[4];
+            unpack_nibbles(wd[cur][r], lo, hi);
+#pragma unroll
+            for (int s = 0; s < NT; ++s) v[s][r] = (double)dot_block16(lo, hi, act[s]) * dsc[s];
+        }
+        const int vi = transpose_index<RD>(lane);
+#pragma unroll
+        for (int s = 0; s < NT; ++s) {
+            wave_transpose_reduce<RD>(v[s]);
+            if (s < it.nt && (lane & (64 / RD - 1)) == 0) {
+                const long row = row0 + c * RD + vi;
+                const long pair = (long)it.item * MAX_SLOTS + s;
+                const float out = (float)((double)a.s_a[(long)it.e * a.H + row] * v[s][0]);
+                if constexpr (COHERENT) st_dev(a.ye + pair * a.H + row, out);
+                else a.ye[pair * a.H + row] = out;
+            }
+        }
+    }
+}
+
+// Gate/up chunking per token capacity: rows per chunk keep registers bounded.
+template <int NT> struct GemvTune;
+template <> struct GemvTune<1> { static constexpr int RC = 4, RD = 8; };
+template <> struct GemvTune<2> { static constexpr int RC = 4, RD = 8; };
+template <> struct GemvTune<4> { static constexpr int RC = 2, RD = 4; };
+template <> struct GemvTune<8> { static constexpr int RC = 2, RD = 2; };
+
+} // namespace coli

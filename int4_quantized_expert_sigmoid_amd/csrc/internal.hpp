@@ -22,7 +22,20 @@ struct WsLayout {
     size_t pair_of, shared_pair;
     size_t pair_tok, expert_off, tiles;          // grouped path buckets and tile list
     size_t h, hq, hs, ye;
+    size_t sync;                                 // FusedSync (GEMV path)
     size_t total;
+};
+
+// Counters of the fused decode kernel. Zero at rest: a zero-filled workspace
+// starts that way and every call leaves it that way. err is sticky.
+struct FusedSync {
+    unsigned exits_all, select_done, reserved0, reserved1, reserved2, err;
+    unsigned exits[8];
+    unsigned logits_done[8];
+    unsigned pad0[42];
+    unsigned gu_done[8 * COLI_MAX_TOPK + 1];
+    unsigned pad1[63];
+    unsigned dn_done[256];
 };
 
 WsLayout make_layout(const coli_moe_layer &L, int T, int path);
@@ -51,12 +64,25 @@ hipError_t launch_select(const coli_moe_layer &L, int T, const WsLayout &lay, ch
                          int32_t *idx_out, float *w_out, hipStream_t s);
 
 // ---- experts, GEMV path (kernels_gemv.hip)
-hipError_t launch_gateup_gemv(const coli_moe_layer &L, int T, const WsLayout &lay, char *ws, hipStream_t s);
-hipError_t launch_down_gemv(const coli_moe_layer &L, int T, const WsLayout &lay, char *ws, hipStream_t s);
+// Items item0.. of the union (item0 = 1 skips the shared expert, item 0).
+hipError_t launch_gateup_gemv(const coli_moe_layer &L, int T, const WsLayout &lay, char *ws, int item0,
+                              hipStream_t s);
+hipError_t launch_down_gemv(const coli_moe_layer &L, int T, const WsLayout &lay, char *ws, int item0,
+                            hipStream_t s);
+
+// ---- decode launches that also carry the shared expert (kernels_staged.hip), T <= 8:
+// router logits + Q8(x) + shared gate/up, then top-k/union + shared down.
+hipError_t launch_route_shared_gateup(const coli_moe_layer &L, const float *x, int T, const WsLayout &lay,
+                                      char *ws, hipStream_t s);
+hipError_t launch_select_shared_down(const coli_moe_layer &L, int T, const WsLayout &lay, char *ws, hipStream_t s);
 
 // ---- experts, grouped int8-MFMA path (kernels_grouped.hip)
 hipError_t launch_gateup_grouped(const coli_moe_layer &L, int T, const WsLayout &lay, char *ws, hipStream_t s);
 hipError_t launch_down_grouped(const coli_moe_layer &L, int T, const WsLayout &lay, char *ws, hipStream_t s);
+
+// ---- whole decode layer in one persistent launch (kernels_fused.hip), T <= 8
+hipError_t launch_decode_fused(const coli_moe_layer &L, const float *x, int T, const WsLayout &lay, char *ws,
+                               float *y, bool accumulate, hipStream_t s);
 
 // ---- combine (kernels_combine.hip)
 hipError_t launch_combine(const coli_moe_layer &L, int T, const WsLayout &lay, const char *ws,

@@ -82,6 +82,8 @@ def test_forward_argument_errors_before_launch():
     assert F(ctypes.byref(L), p, 1, p, 64, p, 1 << 30, None) == _lib.COLI_EINVAL         # unknown flag
     assert F(ctypes.byref(L), p, 1, p, 6, p, 1 << 30, None) == _lib.COLI_EINVAL          # two paths
     assert F(ctypes.byref(L), p, 9, p, 2, p, 1 << 30, None) == _lib.COLI_EINVAL          # GEMV needs T <= 8
+    assert F(ctypes.byref(L), p, 9, p, 8, p, 1 << 40, None) == _lib.COLI_EINVAL          # fused needs GEMV
+    assert F(ctypes.byref(L), p, 1, p, 12, p, 1 << 30, None) == _lib.COLI_EINVAL         # fused + grouped
     assert F(ctypes.byref(L), ctypes.c_void_p((1 << 20) + 4), 1, p, 0, p, 1 << 30, None) == _lib.COLI_EINVAL
     assert F(ctypes.byref(L), p, 1, p, 0, p, 100, None) == _lib.COLI_EWORKSPACE
     assert F(None, p, 1, p, 0, p, 1 << 30, None) == _lib.COLI_EINVAL
@@ -105,6 +107,8 @@ def test_workspace_layout_paths():
     assert out.path == 1 and out.n_pairs_max == 512 * 9
     assert lib().coli_moe_workspace_layout(ctypes.byref(L), 4, _lib.COLI_PATH_GROUPED, ctypes.byref(out)) == 0
     assert out.path == 1
+    assert lib().coli_moe_workspace_layout(ctypes.byref(L), 8, 0, ctypes.byref(out)) == 0
+    assert out.path == 0 and out.sync % 256 == 0 and out.sync > out.ye
     for f in ("xq", "xs", "idx", "w", "h", "hq", "hs", "ye"):
         assert getattr(out, f) % 256 == 0
 
