@@ -30,7 +30,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
-STAGES = ["route_shared_gateup", "select_shared_down", "gateup_gemv", "down_gemv", "combine"]
+STAGES = ["router_shared_gateup", "select_gateup", "down_combine"]   # the three decode launches
 
 
 def parse():
@@ -124,10 +124,11 @@ def main():
             routes.append(idx.cpu().numpy())
     union = [len(set(r.reshape(-1).tolist())) for r in routes]
     bytes_step = [(u + spec.has_shared) * spec.expert_bytes for u in union]
-    # the routed gate/up and down launches stream the U routed experts only
-    # (the shared expert's matrices ride along the two router launches)
+    # the routed gate/up launch streams the U routed experts' gate/up (the
+    # shared expert's ride along the router launch); the down launch streams
+    # every item's down matrix, the shared expert's included
     gateup_bytes = [u * 2 * spec.I * (spec.H // 2 + 4) for u in union]
-    down_bytes = [u * spec.H * (spec.I // 2 + 4) for u in union]
+    down_bytes = [(u + spec.has_shared) * spec.H * (spec.I // 2 + 4) for u in union]
 
     # ---------------- timed region: K steps (graph replays of G steps)
     K = max(G, (args.steps + G - 1) // G * G)
@@ -185,17 +186,18 @@ def main():
                                              ctypes.c_void_p(stream.cuda_stream), evs[i], 6)
         assert rc == 0, rc
     stream.synchronize()
-    stage_ms = np.zeros((KP, 5))
+    NS = len(STAGES)
+    stage_ms = np.zeros((KP, NS))
     for i in range(KP):
         hip.hipEventSynchronize(evs[i][5])
-        for k in range(5):
+        for k in range(NS):
             f = ctypes.c_float()
             hip.hipEventElapsedTime(ctypes.byref(f), evs[i][k], evs[i][k + 1])
             stage_ms[i, k] = f.value
     stage_avg = stage_ms.mean(axis=0)
     gu_bytes_avg = float(np.mean([gateup_bytes[i % G] for i in range(KP)]))
-    gu_gbs = gu_bytes_avg / (stage_avg[2] * 1e-3) / 1e9
-    dn_gbs = float(np.mean([down_bytes[i % G] for i in range(KP)])) / (stage_avg[3] * 1e-3) / 1e9
+    gu_gbs = gu_bytes_avg / (stage_avg[1] * 1e-3) / 1e9
+    dn_gbs = float(np.mean([down_bytes[i % G] for i in range(KP)])) / (stage_avg[2] * 1e-3) / 1e9
     step_gbs = float(np.mean(bytes_step)) / (ms_step * 1e-3) / 1e9
     log("bench: stage averages (ms): " + ", ".join(f"{n}={v:.4f}" for n, v in zip(STAGES, stage_avg)))
     log(f"bench: gate/up {gu_gbs:.0f} GB/s, down {dn_gbs:.0f} GB/s, whole step {step_gbs:.0f} GB/s "
@@ -225,10 +227,10 @@ def main():
                    "expert_bytes_per_step": float(np.mean(bytes_step)),
                    "step_hbm_gbs": round(step_gbs, 1),
                    "stage_ms": {n: round(float(v), 5) for n, v in zip(STAGES, stage_avg)}},
-        "roofline": {"bound": "hbm", "kernel": "k_gateup_gemv", "achieved": round(gu_gbs, 1),
+        "roofline": {"bound": "hbm", "kernel": "k_select_gateup", "achieved": round(gu_gbs, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gu_gbs / HBM_PEAK_GBS, 4),
                      "traffic": None,
-                     "bytes_per_launch": gu_bytes_avg, "avg_launch_ms": round(float(stage_avg[2]), 5)},
+                     "bytes_per_launch": gu_bytes_avg, "avg_launch_ms": round(float(stage_avg[1]), 5)},
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

@@ -9,7 +9,7 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libcoli_moe.so")
 SOURCES = ["abi.cpp", "kernels_quant.hip", "kernels_route.hip", "kernels_gemv.hip", "kernels_grouped.hip",
            "kernels_combine.hip", "kernels_fused.hip",
-           "kernels_staged.hip"]
+           "kernels_decode.hip"]
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-fno-fast-math", "-ffp-contract=fast-honor-pragmas", "-Wall", "-Wno-unused-function"]

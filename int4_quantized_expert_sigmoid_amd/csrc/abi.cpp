@@ -71,6 +71,7 @@ WsLayout make_layout(const coli_moe_layer &L, int T, int path)
     o.xq = p; p = up(p + t * H);
     o.xs = p; p = up(p + t * (H / 32) * 4);
     o.logits = p; p = up(p + t * E * 8);
+    o.keys = p; p = up(p + (path == 0 ? 2 * t * E * 8 : 0));
     o.idx = p; p = up(p + t * k * 4);
     o.w = p; p = up(p + t * k * 4);
     o.item_expert = p; p = up(p + (size_t)o.max_items * 4);
@@ -198,12 +199,25 @@ static int forward_impl(const coli_moe_layer *L, const float *x, int T, float *y
         return COLI_OK;
     }
     if (path == 0) {
-        // the shared expert rides along with the router launches
-        if (launch_route_shared_gateup(*L, x, T, lay, base, s) != hipSuccess) return COLI_EDEVICE;
+        // router (+ the shared expert's gate/up), routed gate/up, down + combine
+        if (launch_decode_router(*L, x, T, lay, base, s) != hipSuccess) return COLI_EDEVICE;
         if (record(ev, 1, s)) return COLI_EDEVICE;
-        if (launch_select_shared_down(*L, T, lay, base, s) != hipSuccess) return COLI_EDEVICE;
+        if (launch_decode_select_gateup(*L, T, lay, base, s) != hipSuccess) return COLI_EDEVICE;
         if (record(ev, 2, s)) return COLI_EDEVICE;
-        return run_experts(L, T, lay, base, y, flags, L->has_shared, s, ev);
+        if (T <= 2) {
+            if (launch_decode_down_combine(*L, T, lay, base, y, (flags & COLI_ACCUMULATE) != 0, s) != hipSuccess)
+                return COLI_EDEVICE;
+        } else {
+            // wider batches: item-major down projection (activations of all
+            // slots loaded once per 32 rows), then the combine
+            if (launch_down_gemv(*L, T, lay, base, 0, s) != hipSuccess) return COLI_EDEVICE;
+            if (launch_combine(*L, T, lay, base, reinterpret_cast<const float *>(base + lay.w), y,
+                               (flags & COLI_ACCUMULATE) != 0, s) != hipSuccess)
+                return COLI_EDEVICE;
+        }
+        for (int i = 3; i < COLI_PROFILE_EVENTS; ++i)
+            if (record(ev, i, s)) return COLI_EDEVICE;
+        return COLI_OK;
     }
     if (launch_logits(*L, x, T, reinterpret_cast<double *>(base + lay.logits),
                       reinterpret_cast<int8_t *>(base + lay.xq), reinterpret_cast<float *>(base + lay.xs),

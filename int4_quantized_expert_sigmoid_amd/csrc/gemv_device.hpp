@@ -78,23 +78,29 @@ struct GateUpShared {
 
 // Gate/up rows [rb*32, rb*32+32) of one item for its token slots, SwiGLU,
 // Q8(h); writes h, hq, hs of pairs item*8 + slot. All threads of the
-// workgroup must call it (blockDim = 64 * ceil(H/32/64), at most 256).
+// workgroup must call it (blockDim >= 64 * ceil(H/32/64) * RS; waves past
+// that idle until the epilogue). RS > 1 splits the 32 rows into RS sets of
+// waves, each streaming 32/RS rows, so fewer loads queue behind each other.
 // ONFLY: Q8(x) is computed here from x instead of read from xq. COHERENT
 // (single-launch path): hq/hs are handed on with device-coherent stores.
-template <int NT, int RC, bool ONFLY, bool COHERENT>
+template <int NT, int RC, bool ONFLY, bool COHERENT, int RS = 1>
 __device__ __forceinline__ void gateup_rows(const GemvArgs &a, const ItemDesc &it, int rb, GateUpShared<NT> &sh)
 {
     constexpr int NV = 2 * RC;                   // values per chunk: RC rows x (gate, up)
-    constexpr int NC = QK / RC;                  // chunks
+    constexpr int RPS = QK / RS;                 // rows per set
+    constexpr int NC = RPS / RC;                 // chunks per set
+    static_assert(RPS % RC == 0, "a set covers whole chunks");
     const int nrb = a.I / QK;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int nblk = a.H / QK;
     const int nw = (nblk + 63) >> 6;             // waves that own block columns
     const long rowb = (long)(a.H / 2);
     const long row0 = (long)it.e * a.I + (long)rb * QK;
+    const int set = wave / nw, wv = wave - set * nw;
+    const int col = wv * 64 + lane;              // this thread's block column
 
-    if (wave < nw) {
-        const bool active = tid < nblk;
+    if (set < RS) {
+        const bool active = col < nblk;
         Blk8 act[NT];
         double dsc[NT];
 #pragma unroll
@@ -104,13 +110,13 @@ __device__ __forceinline__ void gateup_rows(const GemvArgs &a, const ItemDesc &i
                 if constexpr (ONFLY) {
                     uint32_t o[8];
                     float d;
-                    q8_block_regs(a.x + (long)t * a.H + tid * QK, o, d);
+                    q8_block_regs(a.x + (long)t * a.H + col * QK, o, d);
 #pragma unroll
                     for (int k = 0; k < 8; ++k) act[s].v[k] = (int)o[k];
                     dsc[s] = (double)d * 0.0625;
                 } else {
-                    act[s] = load_blk8(a.xq + (long)t * a.H + tid * QK);
-                    dsc[s] = (double)a.xs[(long)t * nblk + tid] * 0.0625;
+                    act[s] = load_blk8(a.xq + (long)t * a.H + col * QK);
+                    dsc[s] = (double)a.xs[(long)t * nblk + col] * 0.0625;
                 }
             } else {
 #pragma unroll
@@ -119,9 +125,9 @@ __device__ __forceinline__ void gateup_rows(const GemvArgs &a, const ItemDesc &i
             }
         }
         // threads past the row's last block read block 0 and multiply it by zero
-        const int tb = active ? tid : 0;
-        const uint8_t *pg = a.q_a + row0 * rowb + tb * 16;
-        const uint8_t *pu = a.q_b + row0 * rowb + tb * 16;
+        const int tb = active ? col : 0;
+        const uint8_t *pg = a.q_a + (row0 + set * RPS) * rowb + tb * 16;
+        const uint8_t *pu = a.q_b + (row0 + set * RPS) * rowb + tb * 16;
 
         uint4 wg[2][RC], wu[2][RC];
 #pragma unroll
@@ -154,7 +160,7 @@ __device__ __forceinline__ void gateup_rows(const GemvArgs &a, const ItemDesc &i
 #pragma unroll
             for (int s = 0; s < NT; ++s) {
                 wave_transpose_reduce<NV>(v[s]);
-                if ((lane & (64 / NV - 1)) == 0) sh.red[wave][s][2 * c * RC + vi] = v[s][0];
+                if ((lane & (64 / NV - 1)) == 0) sh.red[wv][s][2 * (set * RPS + c * RC) + vi] = v[s][0];
             }
         }
     }

@@ -17,7 +17,7 @@ constexpr int MAX_SLOTS = 8;    // token slots of one expert item on the GEMV pa
 struct WsLayout {
     int path;            // 0 GEMV, 1 grouped
     int T, max_items, n_pairs;
-    size_t ctrl, xq, xs, logits, idx, w;
+    size_t ctrl, xq, xs, logits, keys, idx, w;   // keys: [2][T][E] f64 (key, sigmoid), GEMV path
     size_t item_expert, item_ntok, item_tok;     // GEMV path items
     size_t pair_of, shared_pair;
     size_t pair_tok, expert_off, tiles;          // grouped path buckets and tile list
@@ -70,12 +70,14 @@ hipError_t launch_gateup_gemv(const coli_moe_layer &L, int T, const WsLayout &la
 hipError_t launch_down_gemv(const coli_moe_layer &L, int T, const WsLayout &lay, char *ws, int item0,
                             hipStream_t s);
 
-// ---- decode launches that also carry the shared expert (kernels_staged.hip), T <= 8:
-// router logits + Q8(x) + shared gate/up, then top-k/union + shared down.
-hipError_t launch_route_shared_gateup(const coli_moe_layer &L, const float *x, int T, const WsLayout &lay,
-                                      char *ws, hipStream_t s);
-hipError_t launch_select_shared_down(const coli_moe_layer &L, int T, const WsLayout &lay, char *ws, hipStream_t s);
-
+// ---- decode / verify layer in three launches (kernels_decode.hip), T <= 8:
+// router logits + keys + Q8(x); shared gate/up beside per-workgroup
+// top-k/union + routed gate/up; down of every item + combine into y.
+hipError_t launch_decode_router(const coli_moe_layer &L, const float *x, int T, const WsLayout &lay, char *ws,
+                                hipStream_t s);
+hipError_t launch_decode_select_gateup(const coli_moe_layer &L, int T, const WsLayout &lay, char *ws, hipStream_t s);
+hipError_t launch_decode_down_combine(const coli_moe_layer &L, int T, const WsLayout &lay, char *ws, float *y,
+                                      bool accumulate, hipStream_t s);   // T <= 2
 // ---- experts, grouped int8-MFMA path (kernels_grouped.hip)
 hipError_t launch_gateup_grouped(const coli_moe_layer &L, int T, const WsLayout &lay, char *ws, hipStream_t s);
 hipError_t launch_down_grouped(const coli_moe_layer &L, int T, const WsLayout &lay, char *ws, hipStream_t s);

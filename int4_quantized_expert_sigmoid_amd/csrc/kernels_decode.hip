@@ -1,0 +1,394 @@
+// kernels_decode.hip — the decode / verify layer (T <= 8) in three launches.
+//
+//   1. k_router: router logits z = W_r x, the selection keys s + b and
+//      s = sigmoid(z), and Q8(x); one workgroup per expert.
+//   2. k_select_gateup: the first workgroups run the shared expert's gate/up
+//      + SwiGLU + Q8(h) (every token goes through it, so it needs no routing
+//      decision: colibri architecture overview, section 5) and stream while
+//      the others route. Each routed workgroup derives the top-k of every
+//      token and the batch union from the keys (the same deterministic
+//      computation in every workgroup), then runs the gate/up rows of its
+//      routed expert. The first routed workgroup also publishes the routing
+//      and the union for launch 3.
+//   3. k_down_combine: each workgroup owns a few output rows of the down
+//      projection for every item of the union (shared and routed; its waves
+//      take the items round-robin), keeps the per-pair results in LDS and
+//      combines them into y:
+//      y_t = sum_j w_tj * y_{t,e_j} + y_{t,shared}, f64, in slot order.
+//
+// Batch union (colibri README zh-TW, "how it works"): every distinct expert
+// of the batch is read once, for all of its tokens.
+#ifdef COLI_TRACE
+// selection phase marks of profiling builds: [workgroup][8] real-time stamps
+__device__ unsigned long long *coli_sel_marks;
+#define COLI_SEL_MARK(i)                                                                                        \
+    do {                                                                                                        \
+        if ((threadIdx.x & 63) == 0 && coli_sel_marks && blockIdx.x < 4096)                                     \
+            coli_sel_marks[blockIdx.x * 8 + (i)] = __builtin_amdgcn_s_memrealtime();                            \
+    } while (0)
+#endif
+#include "gemv_device.hpp"
+#include "route_device.hpp"
+#include "internal.hpp"
+
+namespace coli {
+
+#ifdef COLI_TRACE
+// Profiling builds only: per-workgroup timestamps [launch][workgroup][4] =
+// start, end of the first phase, end, XCC id (100 MHz real-time counter).
+static unsigned long long *g_dec_trace = nullptr;
+extern "C" void coli_trace_decode_set(void *p)
+{
+    g_dec_trace = static_cast<unsigned long long *>(p);
+    unsigned long long *m = p ? g_dec_trace + 3 * 4096 * 4 : nullptr;   // marks follow the three launches
+    (void)hipMemcpyToSymbol(HIP_SYMBOL(coli_sel_marks), &m, sizeof(m));
+}
+constexpr int TRACE_WG = 4096;
+__device__ __forceinline__ void trace_mark(unsigned long long *tr, int launch, int slot)
+{
+    if (tr && threadIdx.x == 0 && blockIdx.x < TRACE_WG) {
+        unsigned long long *p = tr + ((size_t)launch * TRACE_WG + blockIdx.x) * 4;
+        p[slot] = __builtin_amdgcn_s_memrealtime();
+        if (slot == 2) p[3] = __builtin_amdgcn_s_getreg((3 << 11) | 20);
+    }
+}
+#define TRACE(args, launch, slot) trace_mark((args).trace, launch, slot)
+#else
+#define TRACE(args, launch, slot) ((void)0)
+#endif
+
+namespace {
+
+// ------------------------------------------------------------ launch 1
+struct RouterArgs {
+    const float *W, *bias, *x;
+    int T, H, E;
+    double *z, *key, *sig;
+    int8_t *xq;
+    float *xs;
+#ifdef COLI_TRACE
+    unsigned long long *trace;
+#endif
+};
+
+template <int NT>
+__global__ void __launch_bounds__(512) k_router(RouterArgs r)
+{
+    __shared__ double red[8 * NT];
+    TRACE(r, 0, 0);
+    const long nb = (long)r.T * (r.H / QK);
+    for (long b = (long)blockIdx.x * blockDim.x + threadIdx.x; b < nb; b += (long)r.E * blockDim.x)
+        q8_block_reordered(r.x + b * QK, r.xq + b * QK, r.xs + b);
+    logits_expert<NT>(r.W, r.x, r.T, r.H, r.E, blockIdx.x, r.z, red, r.bias, r.key, r.sig);
+    TRACE(r, 0, 2);
+}
+
+// ------------------------------------------------------------ launch 2
+struct SelGuArgs {
+    const double *key, *sig;
+    int T, E, top_k, n_group, topk_group, has_shared;
+    float route_scale;
+    // published by workgroup 0
+    int32_t *idx;
+    float *w;
+    int *ctrl, *item_expert, *item_ntok, *item_tok, *pair_of, *shared_pair;
+#ifdef COLI_TRACE
+    unsigned long long *trace;
+#endif
+};
+
+struct SelGuShared {
+    DecUnion u;
+};
+
+template <int NT, int KPL>
+__global__ void __launch_bounds__(256) k_select_gateup(SelGuArgs a, GemvArgs g, int n_shared_wg)
+{
+    __shared__ GateUpShared<NT> sh;
+    __shared__ SelGuShared su;
+    TRACE(a, 1, 0);
+    if ((int)blockIdx.x < n_shared_wg) {         // the shared expert: no routing needed
+        gateup_rows<NT, GemvTune<NT>::RC, false, false>(g, shared_item(g), blockIdx.x, sh);
+        TRACE(a, 1, 2);
+        return;
+    }
+    const int b = (int)blockIdx.x - n_shared_wg;
+    DecUnion &u = su.u;
+    dec_route_union<KPL>(a.key, a.sig, a.T, a.E, a.top_k, a.n_group, a.topk_group, a.route_scale, a.has_shared,
+                         u);
+    TRACE(a, 1, 1);
+    const int nrb = g.I / QK;
+    const int item = a.has_shared + b / nrb, rb = b % nrb;
+    const int n_items = u.n_items;
+    if (b == 0) {
+        const int tid = threadIdx.x, np = a.T * a.top_k;
+        for (int i = tid; i < np; i += blockDim.x) {
+            a.idx[i] = u.sel_e[i];
+            a.w[i] = u.sel_w[i];
+            a.pair_of[i] = u.pair_of[i];
+        }
+        for (int i = tid; i < n_items; i += blockDim.x) {
+            a.item_expert[i] = u.item_e[i];
+            a.item_ntok[i] = u.item_nt[i];
+        }
+        for (int i = tid; i < n_items * MAX_SLOTS; i += blockDim.x) {
+            const int it = i / MAX_SLOTS, s = i % MAX_SLOTS;
+            a.item_tok[i] = s < u.item_nt[it] ? u.item_tok[i] : 0;
+        }
+        if (a.has_shared)
+            for (int t = tid; t < a.T; t += blockDim.x) a.shared_pair[t] = t;
+        if (tid == 0) a.ctrl[CTRL_N_ITEMS] = n_items;
+    }
+    if (item >= n_items) return;                 // uniform over the workgroup
+    ItemDesc it;
+    it.item = item;
+    it.e = u.item_e[item];
+    it.nt = u.item_nt[item];
+#pragma unroll
+    for (int s = 0; s < MAX_SLOTS; ++s) it.tok[s] = s < it.nt ? u.item_tok[item * MAX_SLOTS + s] : 0;
+    gateup_rows<NT, GemvTune<NT>::RC, false, false>(g, it, rb, sh);
+    TRACE(a, 1, 2);
+}
+
+// ------------------------------------------------------------ launch 3
+struct DnArgs {
+    const uint8_t *q;          // down_q [E+shared][H][I/2]
+    const float *s;            // down_s [E+shared][H]
+    int H, I, T, top_k, has_shared;
+    const int *ctrl, *item_expert, *item_ntok;
+    const int8_t *hq;          // [pairs][I] reordered
+    const float *hs;           // [pairs][I/32]
+    float *ye;                 // [pairs][H]
+    const int *pair_of, *shared_pair;
+    const float *w;
+    float *y;
+    int accumulate;
+#ifdef COLI_TRACE
+    unsigned long long *trace;
+#endif
+};
+
+// One item's slice: the workgroup's RPU rows of the item's down matrix (lane
+// l holds block column l of each row) and the activations of up to NT token
+// slots.
+template <int NT, int RPU>
+struct DnStage {
+    uint4 wd[RPU];
+    Blk8 act[NT];
+    double dsc[NT];
+    int e, nt;
+};
+
+template <int NT, int RPU>
+__device__ __forceinline__ void dn_load(const DnArgs &a, int item, long row0, int lane, const int *it_e,
+                                        const int *it_nt, DnStage<NT, RPU> &st)
+{
+    const int nblk = a.I / QK;
+    const bool active = lane < nblk;
+    const long rowb = (long)(a.I / 2);
+    st.e = it_e[item];
+    st.nt = it_nt[item];
+    const uint8_t *pd = a.q + ((long)st.e * a.H + row0) * rowb + (active ? lane : 0) * 16;
+#pragma unroll
+    for (int r = 0; r < RPU; ++r) st.wd[r] = load_u4_stream(pd + (long)r * rowb);
+#pragma unroll
+    for (int s = 0; s < NT; ++s) {
+        if (s < st.nt && active) {
+            const long pair = (long)item * MAX_SLOTS + s;
+            st.act[s] = load_blk8(a.hq + pair * a.I + lane * QK);
+            st.dsc[s] = (double)a.hs[pair * nblk + lane] * 0.0625;
+        } else {
+#pragma unroll
+            for (int k = 0; k < 8; ++k) st.act[s].v[k] = 0;
+            st.dsc[s] = 0.0;
+        }
+    }
+}
+
+template <int NT, int RPU>
+__device__ __forceinline__ void dn_compute(const DnArgs &a, int item, long row0, int lane,
+                                           const DnStage<NT, RPU> &st, float *ye_l)
+{
+    double v[NT][RPU];
+#pragma unroll
+    for (int r = 0; r < RPU; ++r) {
+        int lo[4], hi[4];
+        unpack_nibbles(st.wd[r], lo, hi);
+#pragma unroll
+        for (int s = 0; s < NT; ++s) v[s][r] = (double)dot_block16(lo, hi, st.act[s]) * st.dsc[s];
+    }
+    const int vi = transpose_index<RPU>(lane);
+#pragma unroll
+    for (int s = 0; s < NT; ++s) {
+        wave_transpose_reduce<RPU>(v[s]);
+        if (s < st.nt && (lane & (64 / RPU - 1)) == 0) {
+            const long row = row0 + vi;
+            const long pair = (long)item * MAX_SLOTS + s;
+            const float out = (float)((double)a.s[(long)st.e * a.H + row] * v[s][0]);
+            a.ye[pair * a.H + row] = out;
+            ye_l[pair * RPU + vi] = out;
+        }
+    }
+}
+
+// A workgroup owns RPU consecutive output rows. Its waves take the items of
+// the union round-robin (wave w: items w, w + 4, ...), each item's RPU rows
+// at once with the wave's next item already loading; then the per-pair row
+// values in LDS are combined into y.
+template <int NT, int RPU>
+__global__ void __launch_bounds__(256) k_down_combine(DnArgs a)
+{
+    extern __shared__ float ye_l[];              // [max pairs][RPU]
+    __shared__ int it_e[DEC_MAX_ITEMS], it_nt[DEC_MAX_ITEMS];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwave = blockDim.x >> 6;
+    const long row0 = (long)blockIdx.x * RPU;
+    TRACE(a, 2, 0);
+    // the whole item table up front, so no item's loads wait on a lookup
+    const int n_items = min(a.ctrl[CTRL_N_ITEMS], DEC_MAX_ITEMS);
+    for (int i = threadIdx.x; i < n_items; i += blockDim.x) {
+        it_e[i] = a.item_expert[i];
+        it_nt[i] = a.item_ntok[i];
+    }
+    __syncthreads();
+
+    DnStage<NT, RPU> A, B;
+    int i = wave;
+    if (i < n_items) dn_load(a, i, row0, lane, it_e, it_nt, A);
+    for (; i < n_items; i += 2 * nwave) {
+        if (i + nwave < n_items) dn_load(a, i + nwave, row0, lane, it_e, it_nt, B);
+        dn_compute(a, i, row0, lane, A, ye_l);
+        if (i + nwave < n_items) {
+            if (i + 2 * nwave < n_items) dn_load(a, i + 2 * nwave, row0, lane, it_e, it_nt, A);
+            dn_compute(a, i + nwave, row0, lane, B, ye_l);
+        }
+    }
+    __syncthreads();
+    TRACE(a, 2, 1);
+
+    const int k = a.top_k;
+    for (int j = threadIdx.x; j < a.T * RPU; j += blockDim.x) {
+        const int t = j / RPU, rl = j % RPU;
+        double acc = 0.0;
+        for (int q = 0; q < k; ++q)
+            acc += (double)a.w[t * k + q] * (double)ye_l[a.pair_of[t * k + q] * RPU + rl];
+        if (a.has_shared) acc += (double)ye_l[a.shared_pair[t] * RPU + rl];
+        const float out = (float)acc;
+        const long o = (long)t * a.H + row0 + rl;
+        a.y[o] = a.accumulate ? __fadd_rn(a.y[o], out) : out;
+    }
+    TRACE(a, 2, 2);
+}
+
+GemvArgs gemv_view(const coli_moe_layer &L, int T, const WsLayout &lay, char *ws)
+{
+    GemvArgs g;
+    g.H = L.H; g.I = L.I; g.E = L.E; g.T = T; g.item0 = 0; g.x = nullptr;
+    g.xq = reinterpret_cast<const int8_t *>(ws + lay.xq);
+    g.xs = reinterpret_cast<const float *>(ws + lay.xs);
+    g.ctrl = reinterpret_cast<const int *>(ws + lay.ctrl);
+    g.item_expert = reinterpret_cast<const int *>(ws + lay.item_expert);
+    g.item_ntok = reinterpret_cast<const int *>(ws + lay.item_ntok);
+    g.item_tok = reinterpret_cast<const int *>(ws + lay.item_tok);
+    g.h = reinterpret_cast<float *>(ws + lay.h);
+    g.hq = reinterpret_cast<int8_t *>(ws + lay.hq);
+    g.hs = reinterpret_cast<float *>(ws + lay.hs);
+    g.ye = reinterpret_cast<float *>(ws + lay.ye);
+    g.q_a = L.gate_q; g.s_a = L.gate_s; g.q_b = L.up_q; g.s_b = L.up_s;
+    return g;
+}
+
+// keys per lane of the selection: E <= 64 * KPL
+template <int NT>
+hipError_t launch_sel_nt(int E, dim3 grid, const SelGuArgs &a, const GemvArgs &g, int nsh, hipStream_t s)
+{
+    if (E <= 64) hipLaunchKernelGGL((k_select_gateup<NT, 1>), grid, dim3(256), 0, s, a, g, nsh);
+    else if (E <= 128) hipLaunchKernelGGL((k_select_gateup<NT, 2>), grid, dim3(256), 0, s, a, g, nsh);
+    else if (E <= 256) hipLaunchKernelGGL((k_select_gateup<NT, 4>), grid, dim3(256), 0, s, a, g, nsh);
+    else hipLaunchKernelGGL((k_select_gateup<NT, 8>), grid, dim3(256), 0, s, a, g, nsh);
+    return hipGetLastError();
+}
+
+template <int NT, int RPU>
+hipError_t launch_dn_nt(const coli_moe_layer &L, const WsLayout &lay, const DnArgs &a, hipStream_t s)
+{
+    const size_t lds = (size_t)lay.max_items * MAX_SLOTS * RPU * sizeof(float);
+    hipLaunchKernelGGL((k_down_combine<NT, RPU>), dim3((unsigned)(L.H / RPU)), dim3(256), lds, s, a);
+    return hipGetLastError();
+}
+
+} // namespace
+
+hipError_t launch_decode_router(const coli_moe_layer &L, const float *x, int T, const WsLayout &lay, char *ws,
+                                hipStream_t s)
+{
+    RouterArgs r;
+    r.W = L.router_w; r.bias = L.router_b; r.x = x;
+    r.T = T; r.H = L.H; r.E = L.E;
+    r.z = reinterpret_cast<double *>(ws + lay.logits);
+    r.key = reinterpret_cast<double *>(ws + lay.keys);
+    r.sig = r.key + (size_t)T * L.E;
+    r.xq = reinterpret_cast<int8_t *>(ws + lay.xq);
+    r.xs = reinterpret_cast<float *>(ws + lay.xs);
+#ifdef COLI_TRACE
+    r.trace = g_dec_trace;
+#endif
+    const dim3 grid((unsigned)L.E);
+    if (T <= 1) hipLaunchKernelGGL(k_router<1>, grid, dim3(512), 0, s, r);
+    else if (T <= 2) hipLaunchKernelGGL(k_router<2>, grid, dim3(512), 0, s, r);
+    else if (T <= 4) hipLaunchKernelGGL(k_router<4>, grid, dim3(512), 0, s, r);
+    else hipLaunchKernelGGL(k_router<8>, grid, dim3(512), 0, s, r);
+    return hipGetLastError();
+}
+
+hipError_t launch_decode_select_gateup(const coli_moe_layer &L, int T, const WsLayout &lay, char *ws, hipStream_t s)
+{
+    SelGuArgs a;
+    a.key = reinterpret_cast<const double *>(ws + lay.keys);
+    a.sig = a.key + (size_t)T * L.E;
+    a.T = T; a.E = L.E; a.top_k = L.top_k; a.n_group = L.n_group; a.topk_group = L.topk_group;
+    a.has_shared = L.has_shared; a.route_scale = L.route_scale;
+    a.idx = reinterpret_cast<int32_t *>(ws + lay.idx);
+    a.w = reinterpret_cast<float *>(ws + lay.w);
+    a.ctrl = reinterpret_cast<int *>(ws + lay.ctrl);
+    a.item_expert = reinterpret_cast<int *>(ws + lay.item_expert);
+    a.item_ntok = reinterpret_cast<int *>(ws + lay.item_ntok);
+    a.item_tok = reinterpret_cast<int *>(ws + lay.item_tok);
+    a.pair_of = reinterpret_cast<int *>(ws + lay.pair_of);
+    a.shared_pair = reinterpret_cast<int *>(ws + lay.shared_pair);
+#ifdef COLI_TRACE
+    a.trace = g_dec_trace;
+#endif
+    GemvArgs g = gemv_view(L, T, lay, ws);
+    const int nrb = L.I / QK, nsh = L.has_shared ? nrb : 0;
+    const dim3 grid((unsigned)(nsh + (lay.max_items - L.has_shared) * nrb));
+    if (T <= 1) return launch_sel_nt<1>(L.E, grid, a, g, nsh, s);
+    if (T <= 2) return launch_sel_nt<2>(L.E, grid, a, g, nsh, s);
+    if (T <= 4) return launch_sel_nt<4>(L.E, grid, a, g, nsh, s);
+    return launch_sel_nt<8>(L.E, grid, a, g, nsh, s);
+}
+
+hipError_t launch_decode_down_combine(const coli_moe_layer &L, int T, const WsLayout &lay, char *ws, float *y,
+                                      bool accumulate, hipStream_t s)
+{
+    DnArgs a;
+    a.q = L.down_q; a.s = L.down_s;
+    a.H = L.H; a.I = L.I; a.T = T; a.top_k = L.top_k; a.has_shared = L.has_shared;
+    a.ctrl = reinterpret_cast<const int *>(ws + lay.ctrl);
+    a.item_expert = reinterpret_cast<const int *>(ws + lay.item_expert);
+    a.item_ntok = reinterpret_cast<const int *>(ws + lay.item_ntok);
+    a.hq = reinterpret_cast<const int8_t *>(ws + lay.hq);
+    a.hs = reinterpret_cast<const float *>(ws + lay.hs);
+    a.ye = reinterpret_cast<float *>(ws + lay.ye);
+    a.pair_of = reinterpret_cast<const int *>(ws + lay.pair_of);
+    a.shared_pair = reinterpret_cast<const int *>(ws + lay.shared_pair);
+    a.w = reinterpret_cast<const float *>(ws + lay.w);
+    a.y = y;
+    a.accumulate = accumulate ? 1 : 0;
+#ifdef COLI_TRACE
+    a.trace = g_dec_trace;
+#endif
+    if (T <= 1) return launch_dn_nt<1, 8>(L, lay, a, s);
+    return launch_dn_nt<2, 4>(L, lay, a, s);
+}
+
+} // namespace coli

@@ -15,17 +15,25 @@
 #pragma once
 #include "device_common.hpp"
 
+// Optional timing hook of profiling builds (no-op otherwise).
+#ifndef COLI_SEL_MARK
+#define COLI_SEL_MARK(i) ((void)0)
+#endif
+
 namespace coli {
 
 constexpr int MAX_E = 512;
 constexpr int SEL_T = 8;            // tokens one selection workgroup handles
 
 // Logits of one expert for T <= NT tokens by the whole workgroup (blockDim a
-// multiple of 64, at most 256): float4 loads, f64 FMAs, wave sums, then the
-// waves in order. Writes z[t][e]. red must hold 4 * NT doubles of LDS.
+// multiple of 64): float4 loads, f64 FMAs, wave sums, then the waves in
+// order. Writes z[t][e] and, with key != nullptr, the selection key s + b and
+// s = sigmoid(z). red must hold (blockDim / 64) * NT doubles of LDS.
 template <int NT>
 __device__ __forceinline__ void logits_expert(const float *__restrict__ W, const float *__restrict__ x, int T,
-                                              int H, int E, int e, double *__restrict__ z, double *red)
+                                              int H, int E, int e, double *__restrict__ z, double *red,
+                                              const float *__restrict__ bias = nullptr,
+                                              double *__restrict__ key = nullptr, double *__restrict__ sig = nullptr)
 {
     typedef float f32x4 __attribute__((ext_vector_type(4)));
     const f32x4 *we = reinterpret_cast<const f32x4 *>(W + (long)e * H);
@@ -58,6 +66,12 @@ __device__ __forceinline__ void logits_expert(const float *__restrict__ W, const
         double v = red[t];
         for (int w = 1; w < (int)(blockDim.x >> 6); ++w) v += red[w * NT + t];
         st_dev(z + (long)t * E + e, v);
+        if (key) {
+            // the selection key of the sigmoid router: s = sigmoid(z), key = s + b
+            const double sg = 1.0 / (1.0 + exp(-v));
+            key[(long)t * E + e] = sg + (double)bias[e];
+            sig[(long)t * E + e] = sg;
+        }
     }
     __syncthreads();
 }
@@ -252,6 +266,308 @@ __device__ inline void build_union(const SelArgs &a, UnionShared &u)
 __device__ inline void routing_to_union(const SelArgs &a, const SelShared &sh, UnionShared &u)
 {
     for (int i = threadIdx.x; i < a.T * a.top_k; i += blockDim.x) u.idx[i] = sh.isel[i];
+}
+
+// ---------------------------------------------------------------------------
+// Selection and batch union inside one workgroup (decode, T <= 8). Every
+// workgroup of the routed gate/up launch derives the same routing from the
+// keys the router launch wrote, so no launch sits between the router and the
+// experts.
+
+constexpr int DEC_MAX_T = 8;
+constexpr int DEC_MAX_ITEMS = 1 + DEC_MAX_T * COLI_MAX_TOPK;
+constexpr int DEC_MAX_PAIRS = DEC_MAX_T * COLI_MAX_TOPK;
+
+// Order-preserving map of an f64 onto u64 (-0.0 is taken as +0.0, so equal
+// keys map to equal integers). A candidate of value 0 is never selected.
+__device__ __forceinline__ unsigned long long order_key(double v)
+{
+    const unsigned long long u = (unsigned long long)__double_as_longlong(v + 0.0);
+    return (u >> 63) ? ~u : (u | 0x8000000000000000ull);
+}
+
+// (key, expert) candidate of the wave argmax: larger key first, equal keys to
+// the lower expert index. A total order, so every lane ends with one winner.
+struct Cand {
+    unsigned lo, hi;
+    int e;
+};
+
+__device__ __forceinline__ bool cand_beats(const Cand &a, const Cand &b)
+{
+    const unsigned long long ka = ((unsigned long long)a.hi << 32) | a.lo;
+    const unsigned long long kb = ((unsigned long long)b.hi << 32) | b.lo;
+    return ka > kb || (ka == kb && a.e < b.e);
+}
+
+template <int CTRL>
+__device__ __forceinline__ void cand_dpp_step(Cand &c)
+{
+    Cand p;
+    p.lo = (unsigned)__builtin_amdgcn_mov_dpp((int)c.lo, CTRL, 0xF, 0xF, false);
+    p.hi = (unsigned)__builtin_amdgcn_mov_dpp((int)c.hi, CTRL, 0xF, 0xF, false);
+    p.e = __builtin_amdgcn_mov_dpp(c.e, CTRL, 0xF, 0xF, false);
+    if (cand_beats(p, c)) c = p;
+}
+
+// Both results of a permlane swap of a value with itself are {own, partner}
+// in some order; the better of the two is what the all-reduce keeps.
+template <bool W32>
+__device__ __forceinline__ void cand_swap_step(Cand &c)
+{
+    Cand a, b;
+    if constexpr (W32) {
+        const auto l = __builtin_amdgcn_permlane32_swap(c.lo, c.lo, false, false);
+        const auto h = __builtin_amdgcn_permlane32_swap(c.hi, c.hi, false, false);
+        const auto x = __builtin_amdgcn_permlane32_swap((unsigned)c.e, (unsigned)c.e, false, false);
+        a = Cand{l[0], h[0], (int)x[0]};
+        b = Cand{l[1], h[1], (int)x[1]};
+    } else {
+        const auto l = __builtin_amdgcn_permlane16_swap(c.lo, c.lo, false, false);
+        const auto h = __builtin_amdgcn_permlane16_swap(c.hi, c.hi, false, false);
+        const auto x = __builtin_amdgcn_permlane16_swap((unsigned)c.e, (unsigned)c.e, false, false);
+        a = Cand{l[0], h[0], (int)x[0]};
+        b = Cand{l[1], h[1], (int)x[1]};
+    }
+    c = cand_beats(b, a) ? b : a;
+}
+
+// Wave-wide best candidate, left in every lane: quad swaps, then row
+// rotations by 4 and 8 (each quad already uniform, so a rotation pairs whole
+// quads), then the 16- and 32-lane swaps.
+__device__ __forceinline__ Cand wave_best(Cand c)
+{
+    cand_dpp_step<DPP_XOR1>(c);
+    cand_dpp_step<DPP_XOR2>(c);
+    cand_dpp_step<0x124>(c);          // row_ror:4
+    cand_dpp_step<0x128>(c);          // row_ror:8
+    cand_swap_step<false>(c);
+    cand_swap_step<true>(c);
+    return c;
+}
+
+// Kept groups of group-limited routing for one token (one wave): a group's
+// score is the sum of its two largest keys (in index order, as a running
+// top-2), the topk_group best scores are kept, equal scores to the lower
+// group. Returns a bitmask over groups (all ones when n_group == 1).
+__device__ inline unsigned long long kept_groups(const double *__restrict__ key, int E, int n_group, int topk_group)
+{
+    if (n_group <= 1) return ~0ull;
+    const int lane = threadIdx.x & 63, gsize = E / n_group;
+    double gs = -INFINITY;
+    if (lane < n_group) {
+        double m1 = -INFINITY, m2 = -INFINITY;
+        for (int e = lane * gsize; e < (lane + 1) * gsize; ++e) {
+            const double v = key[e];
+            if (v > m1) { m2 = m1; m1 = v; }
+            else if (v > m2) { m2 = v; }
+        }
+        gs = gsize >= 2 ? m1 + m2 : m1;
+    }
+    int r = 0;
+    for (int g2 = 0; g2 < n_group; ++g2) {
+        const double o = __shfl(gs, g2);
+        r += (o > gs) || (o == gs && g2 < lane);
+    }
+    return __ballot(lane < n_group && r < topk_group);
+}
+
+// Wave-wide maximum of a u32, left in every lane.
+__device__ __forceinline__ unsigned wave_max_u32(unsigned v)
+{
+    v = max(v, (unsigned)__builtin_amdgcn_mov_dpp((int)v, DPP_XOR1, 0xF, 0xF, false));
+    v = max(v, (unsigned)__builtin_amdgcn_mov_dpp((int)v, DPP_XOR2, 0xF, 0xF, false));
+    v = max(v, (unsigned)__builtin_amdgcn_mov_dpp((int)v, 0x124, 0xF, 0xF, false));   // row_ror:4
+    v = max(v, (unsigned)__builtin_amdgcn_mov_dpp((int)v, 0x128, 0xF, 0xF, false));   // row_ror:8
+    const auto a = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    v = max(a[0], a[1]);
+    const auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return max(b[0], b[1]);
+}
+
+// Lane l's KPL keys (experts l, l+64, ...) as order keys, sorted by (key
+// desc, expert asc), and their sigmoids in expert order.
+template <int KPL>
+__device__ __forceinline__ void lane_keys(const double *__restrict__ key, const double *__restrict__ sig, int E,
+                                          int gsize, unsigned long long gm, unsigned long long (&ok)[KPL],
+                                          int (&oe)[KPL], double (&sv)[KPL])
+{
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int i = 0; i < KPL; ++i) {
+        const int e = lane + 64 * i;
+        const bool in = e < E;
+        const double kv = in ? key[e] : 0.0;
+        sv[i] = in ? sig[e] : 0.0;
+        ok[i] = (in && ((gm >> (e / gsize)) & 1ull)) ? order_key(kv) : 0ull;
+        oe[i] = e;
+    }
+    COLI_SEL_MARK(0);
+#pragma unroll
+    for (int i = 1; i < KPL; ++i) {                  // insertion sort
+#pragma unroll
+        for (int j = i; j > 0; --j) {
+            const bool sw = ok[j] > ok[j - 1] || (ok[j] == ok[j - 1] && oe[j] < oe[j - 1]);
+            const unsigned long long tk = ok[j];
+            const int te = oe[j];
+            ok[j] = sw ? ok[j - 1] : ok[j];
+            oe[j] = sw ? oe[j - 1] : oe[j];
+            ok[j - 1] = sw ? tk : ok[j - 1];
+            oe[j - 1] = sw ? te : oe[j - 1];
+        }
+    }
+}
+
+// The owning lane hands its best on: sel_e/sel_s of slot r, then shifts its
+// sorted list.
+template <int KPL>
+__device__ __forceinline__ void lane_pop(int r, unsigned long long (&ok)[KPL], int (&oe)[KPL],
+                                         const double (&sv)[KPL], int *sel_e, double *sel_s)
+{
+    const int lane = threadIdx.x & 63;
+    double s = 0.0;
+#pragma unroll
+    for (int i = 0; i < KPL; ++i) s = (oe[0] == lane + 64 * i) ? sv[i] : s;
+    sel_e[r] = oe[0];
+    sel_s[r] = s;
+#pragma unroll
+    for (int i = 0; i + 1 < KPL; ++i) { ok[i] = ok[i + 1]; oe[i] = oe[i + 1]; }
+    ok[KPL - 1] = 0ull;
+    oe[KPL - 1] = 0x7FFFFFFF;
+}
+
+// Top-k of one token (one wave; E <= 64 * KPL). Each of the k rounds takes
+// the wave maximum of the upper 32 bits of the lanes' current best keys;
+// when a single lane holds it, that lane's best is the next expert (every
+// other remaining key is smaller in its upper bits). If two lanes ever tie
+// there, the whole selection is taken again with the exact (key, expert)
+// order in every round. Writes the experts, largest key first, and
+// w_j = route_scale * s_j / sum_j s_j (s summed in slot order, f64) to LDS.
+template <int KPL>
+__device__ inline void wave_topk(const double *__restrict__ key, const double *__restrict__ sig, int E, int k,
+                                 int n_group, int topk_group, float route_scale, int *sel_e, float *sel_w,
+                                 double *sel_s)
+{
+    const int lane = threadIdx.x & 63;
+    const unsigned long long gm = kept_groups(key, E, n_group, topk_group);
+    const int gsize = E / n_group;
+    double sv[KPL];
+    unsigned long long ok[KPL];
+    int oe[KPL];
+    lane_keys<KPL>(key, sig, E, gsize, gm, ok, oe, sv);
+    COLI_SEL_MARK(1);
+    if (lane < k) { sel_e[lane] = 0; sel_s[lane] = 0.0; }   // kept only without enough finite keys
+    bool tie = false;
+    for (int r = 0; r < k; ++r) {
+        const unsigned hi = (unsigned)(ok[0] >> 32);
+        const unsigned long long m = __ballot(hi == wave_max_u32(hi));
+        tie |= (m & (m - 1ull)) != 0ull;
+        if (lane == __ffsll((long long)m) - 1 && ok[0] != 0ull) lane_pop<KPL>(r, ok, oe, sv, sel_e, sel_s);
+    }
+    if (tie) {                                       // exact order in every round
+        lane_keys<KPL>(key, sig, E, gsize, gm, ok, oe, sv);
+        if (lane < k) { sel_e[lane] = 0; sel_s[lane] = 0.0; }
+        for (int r = 0; r < k; ++r) {
+            Cand c{(unsigned)ok[0], (unsigned)(ok[0] >> 32), ok[0] != 0ull ? oe[0] : 0x7FFFFFFF};
+            c = wave_best(c);
+            if (oe[0] == c.e && ok[0] != 0ull) lane_pop<KPL>(r, ok, oe, sv, sel_e, sel_s);
+        }
+    }
+    COLI_SEL_MARK(2);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    if (lane < k) {
+        double ssum = 0.0;
+        for (int j = 0; j < k; ++j) ssum += sel_s[j];
+        sel_w[lane] = (float)((double)route_scale * sel_s[lane] / ssum);
+    }
+    COLI_SEL_MARK(3);
+}
+
+// Routing and batch union of T <= 8 tokens held in LDS by one workgroup.
+struct DecUnion {
+    int sel_e[DEC_MAX_PAIRS];        // [t][j] experts
+    float sel_w[DEC_MAX_PAIRS];      // [t][j] weights
+    double sel_s[DEC_MAX_PAIRS];     // [t][j] sigmoid of the chosen logits
+    int item_e[DEC_MAX_ITEMS];
+    int item_nt[DEC_MAX_ITEMS];
+    int item_tok[DEC_MAX_ITEMS * MAX_SLOTS];
+    int first_item[DEC_MAX_PAIRS];   // item of a pair that opens an item
+    int pair_of[DEC_MAX_PAIRS];      // item * 8 + slot
+    int n_items;
+};
+
+// Selection of all T tokens (wave w takes tokens w, w + waves, ...; E <=
+// 64 * KPL), then the
+// union: the shared expert is item 0 (slot t = token t), routed experts follow
+// in order of first use (token-major, then slot). All threads of the
+// workgroup call it; blockDim >= 64.
+template <int KPL>
+__device__ inline void dec_route_union(const double *__restrict__ key, const double *__restrict__ sig, int T, int E,
+                                       int k, int n_group, int topk_group, float route_scale, int has_shared,
+                                       DecUnion &u)
+{
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nwave = blockDim.x >> 6;
+    for (int t = wave; t < T; t += nwave) {
+        const double *kt = key + (long)t * E, *st = sig + (long)t * E;
+        int *se = u.sel_e + t * k;
+        float *sw = u.sel_w + t * k;
+        double *ss = u.sel_s + t * k;
+        wave_topk<KPL>(kt, st, E, k, n_group, topk_group, route_scale, se, sw, ss);
+    }
+    if (T == 1) {                                 // one token: item has_shared + j is its slot j
+        __syncthreads();
+        if (tid < k) {
+            const int it = has_shared + tid;
+            u.item_e[it] = u.sel_e[tid];
+            u.item_nt[it] = 1;
+            u.item_tok[it * MAX_SLOTS] = 0;
+            u.pair_of[tid] = it * MAX_SLOTS;
+        }
+        if (has_shared && tid == 0) { u.item_e[0] = E; u.item_nt[0] = 1; u.item_tok[0] = 0; }
+        if (tid == 0) u.n_items = has_shared + k;
+        COLI_SEL_MARK(4);
+        __syncthreads();
+        return;
+    }
+    const int n_items_max = has_shared + T * k;
+    for (int i = tid; i < n_items_max; i += blockDim.x) u.item_nt[i] = 0;
+    if (has_shared && tid == 0) { u.item_e[0] = E; u.item_nt[0] = T; }
+    if (has_shared && tid < T) u.item_tok[tid] = tid;
+    __syncthreads();
+    const int np = T * k;
+    int running = has_shared;                     // items so far (wave 0 keeps it)
+    for (int c = 0; c < np; c += 64) {
+        const int p = c + lane;
+        const bool valid = wave == 0 && p < np;
+        int e = -1, cnt = 0, qf = -1, my_item = -1;
+        if (wave == 0) {
+            if (valid) e = u.sel_e[p];
+            for (int q = 0; q < np; ++q) {                  // earlier pairs of the same expert
+                const bool eq = valid && q < p && u.sel_e[q] == e;
+                if (eq && qf < 0) qf = q;
+                cnt += eq ? 1 : 0;
+            }
+            const bool is_new = valid && cnt == 0;
+            const unsigned long long m = __ballot(is_new);
+            my_item = running + __popcll(m & ((1ull << lane) - 1ull));
+            if (is_new) { u.first_item[p] = my_item; u.item_e[my_item] = e; }
+            running += __popcll(m);
+        }
+        __syncthreads();
+        if (valid) {
+            const int it = cnt == 0 ? my_item : u.first_item[qf];
+            const int slot = cnt < MAX_SLOTS ? cnt : MAX_SLOTS - 1;   // repeats only from a caller's routing
+            u.pair_of[p] = it * MAX_SLOTS + slot;
+            u.item_tok[it * MAX_SLOTS + slot] = p / k;
+            atomicAdd(&u.item_nt[it], 1);
+        }
+        __syncthreads();
+    }
+    COLI_SEL_MARK(4);
+    if (tid == 0) u.n_items = running;
+    __syncthreads();
 }
 
 } // namespace coli
