@@ -28,6 +28,7 @@
 // leave (counted per group of workgroups, then overall) zeroes the counters.
 #include "gemv_device.hpp"
 #include "route_device.hpp"
+#include "sync_device.hpp"
 #include "internal.hpp"
 
 #include <algorithm>
@@ -35,7 +36,6 @@
 namespace coli {
 namespace {
 
-constexpr unsigned SPIN_LIMIT = 1u << 21;
 constexpr int LOGIT_EXPERTS = 1;        // experts per logits item
 constexpr int LOGIT_COUNTERS = 8;       // logits completions are counted on 8 words
 constexpr int EXIT_GROUPS = 8;
@@ -55,57 +55,6 @@ struct FusedArgs {
     unsigned long long *trace;          // [total][4]: workgroup, start, end, XCC (profiling builds only)
 #endif
 };
-
-__device__ __forceinline__ unsigned ld_counter(const unsigned *p)
-{
-    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// Thread 0 waits (bounded) until *p >= target; then the workgroup goes on.
-__device__ void wait_ge(const unsigned *p, unsigned target, unsigned *err)
-{
-    if (threadIdx.x == 0) {
-        unsigned spins = 0;
-        while (ld_counter(p) < target) {
-            if (++spins > SPIN_LIMIT) {
-                __hip_atomic_fetch_or(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                break;
-            }
-            __builtin_amdgcn_s_sleep(2);
-        }
-    }
-    __syncthreads();
-}
-
-// Lanes 0..n-1 of wave 0 each wait (bounded) for their own counter p[lane]
-// to reach target[lane]; then the workgroup goes on.
-__device__ void wait_all_ge(const unsigned *p, const unsigned *target, int n, unsigned *err)
-{
-    if (threadIdx.x < (unsigned)n) {
-        unsigned spins = 0;
-        const unsigned tgt = target[threadIdx.x];
-        while (ld_counter(p + threadIdx.x) < tgt) {
-            if (++spins > SPIN_LIMIT) {
-                __hip_atomic_fetch_or(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                break;
-            }
-            __builtin_amdgcn_s_sleep(2);
-        }
-    }
-    __syncthreads();
-}
-
-// After this workgroup's coherent stores have completed, add 1 to *p.
-// Returns the old value to thread 0 (other threads get 0).
-__device__ unsigned signal_add(unsigned *p)
-{
-    __builtin_amdgcn_s_waitcnt(0);
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-    __syncthreads();
-    unsigned old = 0;
-    if (threadIdx.x == 0) old = __hip_atomic_fetch_add(p, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    return old;
-}
 
 // y rows [g*dg, g*dg+dg) of every token: sum_j w_tj * ye[pair(t,j)] + ye[shared pair],
 // f64 in j order. Routing words are staged in LDS first so the ye loads of

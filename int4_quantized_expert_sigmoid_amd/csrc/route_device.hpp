@@ -69,8 +69,8 @@ __device__ __forceinline__ void logits_expert(const float *__restrict__ W, const
         if (key) {
             // the selection key of the sigmoid router: s = sigmoid(z), key = s + b
             const double sg = 1.0 / (1.0 + exp(-v));
-            key[(long)t * E + e] = sg + (double)bias[e];
-            sig[(long)t * E + e] = sg;
+            st_dev(key + (long)t * E + e, sg + (double)bias[e]);
+            st_dev(sig + (long)t * E + e, sg);
         }
     }
     __syncthreads();
@@ -358,7 +358,7 @@ __device__ inline unsigned long long kept_groups(const double *__restrict__ key,
     if (lane < n_group) {
         double m1 = -INFINITY, m2 = -INFINITY;
         for (int e = lane * gsize; e < (lane + 1) * gsize; ++e) {
-            const double v = key[e];
+            const double v = ld_dev(key + e);
             if (v > m1) { m2 = m1; m1 = v; }
             else if (v > m2) { m2 = v; }
         }
@@ -385,8 +385,9 @@ __device__ __forceinline__ unsigned wave_max_u32(unsigned v)
     return max(b[0], b[1]);
 }
 
-// Lane l's KPL keys (experts l, l+64, ...) as order keys, sorted by (key
-// desc, expert asc), and their sigmoids in expert order.
+// Lane l's KPL keys (experts l, l+64, ...) as order keys with their experts
+// and sigmoids, sorted by (key desc, expert asc). Coherent loads: the keys
+// may come from other workgroups of the same launch.
 template <int KPL>
 __device__ __forceinline__ void lane_keys(const double *__restrict__ key, const double *__restrict__ sig, int E,
                                           int gsize, unsigned long long gm, unsigned long long (&ok)[KPL],
@@ -397,8 +398,8 @@ __device__ __forceinline__ void lane_keys(const double *__restrict__ key, const 
     for (int i = 0; i < KPL; ++i) {
         const int e = lane + 64 * i;
         const bool in = e < E;
-        const double kv = in ? key[e] : 0.0;
-        sv[i] = in ? sig[e] : 0.0;
+        const double kv = in ? ld_dev(key + e) : 0.0;
+        sv[i] = in ? ld_dev(sig + e) : 0.0;
         ok[i] = (in && ((gm >> (e / gsize)) & 1ull)) ? order_key(kv) : 0ull;
         oe[i] = e;
     }
@@ -410,10 +411,13 @@ __device__ __forceinline__ void lane_keys(const double *__restrict__ key, const 
             const bool sw = ok[j] > ok[j - 1] || (ok[j] == ok[j - 1] && oe[j] < oe[j - 1]);
             const unsigned long long tk = ok[j];
             const int te = oe[j];
+            const double ts = sv[j];
             ok[j] = sw ? ok[j - 1] : ok[j];
             oe[j] = sw ? oe[j - 1] : oe[j];
+            sv[j] = sw ? sv[j - 1] : sv[j];
             ok[j - 1] = sw ? tk : ok[j - 1];
             oe[j - 1] = sw ? te : oe[j - 1];
+            sv[j - 1] = sw ? ts : sv[j - 1];
         }
     }
 }
@@ -421,19 +425,16 @@ __device__ __forceinline__ void lane_keys(const double *__restrict__ key, const 
 // The owning lane hands its best on: sel_e/sel_s of slot r, then shifts its
 // sorted list.
 template <int KPL>
-__device__ __forceinline__ void lane_pop(int r, unsigned long long (&ok)[KPL], int (&oe)[KPL],
-                                         const double (&sv)[KPL], int *sel_e, double *sel_s)
+__device__ __forceinline__ void lane_pop(int r, unsigned long long (&ok)[KPL], int (&oe)[KPL], double (&sv)[KPL],
+                                         int *sel_e, double *sel_s)
 {
-    const int lane = threadIdx.x & 63;
-    double s = 0.0;
-#pragma unroll
-    for (int i = 0; i < KPL; ++i) s = (oe[0] == lane + 64 * i) ? sv[i] : s;
     sel_e[r] = oe[0];
-    sel_s[r] = s;
+    sel_s[r] = sv[0];
 #pragma unroll
-    for (int i = 0; i + 1 < KPL; ++i) { ok[i] = ok[i + 1]; oe[i] = oe[i + 1]; }
+    for (int i = 0; i + 1 < KPL; ++i) { ok[i] = ok[i + 1]; oe[i] = oe[i + 1]; sv[i] = sv[i + 1]; }
     ok[KPL - 1] = 0ull;
     oe[KPL - 1] = 0x7FFFFFFF;
+    sv[KPL - 1] = 0.0;
 }
 
 // Top-k of one token (one wave; E <= 64 * KPL). Each of the k rounds takes
@@ -457,12 +458,23 @@ __device__ inline void wave_topk(const double *__restrict__ key, const double *_
     lane_keys<KPL>(key, sig, E, gsize, gm, ok, oe, sv);
     COLI_SEL_MARK(1);
     if (lane < k) { sel_e[lane] = 0; sel_s[lane] = 0.0; }   // kept only without enough finite keys
+    // fast rounds on the upper 32 bits only (a valid key's are never 0)
+    unsigned kh[KPL];
+    int fe[KPL];
+    double fs[KPL];
+#pragma unroll
+    for (int i = 0; i < KPL; ++i) { kh[i] = (unsigned)(ok[i] >> 32); fe[i] = oe[i]; fs[i] = sv[i]; }
     bool tie = false;
     for (int r = 0; r < k; ++r) {
-        const unsigned hi = (unsigned)(ok[0] >> 32);
-        const unsigned long long m = __ballot(hi == wave_max_u32(hi));
+        const unsigned long long m = __ballot(kh[0] == wave_max_u32(kh[0]));
         tie |= (m & (m - 1ull)) != 0ull;
-        if (lane == __ffsll((long long)m) - 1 && ok[0] != 0ull) lane_pop<KPL>(r, ok, oe, sv, sel_e, sel_s);
+        if (lane == __ffsll((long long)m) - 1 && kh[0] != 0u) {
+            sel_e[r] = fe[0];
+            sel_s[r] = fs[0];
+#pragma unroll
+            for (int i = 0; i + 1 < KPL; ++i) { kh[i] = kh[i + 1]; fe[i] = fe[i + 1]; fs[i] = fs[i + 1]; }
+            kh[KPL - 1] = 0u;
+        }
     }
     if (tie) {                                       // exact order in every round
         lane_keys<KPL>(key, sig, E, gsize, gm, ok, oe, sv);

@@ -1,8 +1,9 @@
-"""GPU checks of the single-launch (persistent) decode path (COLI_PATH_FUSED),
-through the C ABI: results bit-identical to the default multi-launch path and
-within the oracle bar,
-counters back at zero and the error word clear after every call, repeated
-calls and HIP-graph replays stable."""
+"""GPU checks of the decode paths that hand work between workgroups of one
+launch through counters in the workspace: the single-launch persistent path
+(COLI_PATH_FUSED) and the default path, whose first launch counts its router
+workgroups. Through the C ABI: results bit-identical between the paths and
+within the oracle bar, counters back at zero and the error word clear after
+every call, repeated calls and HIP-graph replays stable."""
 import numpy as np
 import pytest
 import torch
@@ -93,13 +94,25 @@ def test_fused_glm_T1_T4(glm):
         assert np.array_equal(yf, ys)
 
 
-def test_fused_graph_replays(glm):
+@pytest.mark.parametrize("T", [1, 2, 3, 8])
+def test_default_path_leaves_counters_clean(tiny, T):
+    L, ref = tiny
+    ws = api.workspace(L, T)
+    for rep in range(3):
+        x = S.tokens(S.TokenSpec(T=T, token_set=900 + 10 * T + rep), S.TINY.H, 0)
+        y = api.moe_forward(L, dev(x), ws).cpu().numpy()
+        check_clean(L, T, ws)
+        y_o, _, _ = O.moe_forward(ref, x)
+        assert rel_err(y, y_o).max() <= TOL
+
+
+@pytest.mark.parametrize("F", [COLI_PATH_FUSED, 0], ids=["fused", "default"])
+def test_graph_replays(glm, F):
     L = glm
     x = S.tokens(S.TokenSpec(T=1, token_set=700, outlier_channels=61), S.GLM52.H, 0)
     x2 = S.tokens(S.TokenSpec(T=1, token_set=701, outlier_channels=61), S.GLM52.H, 0)
     xd, xd2 = dev(x), dev(x2)
     ws = api.workspace(L, 1)
-    F = COLI_PATH_FUSED
     y_eager = api.moe_forward(L, xd, ws, flags=F).clone()
     y_eager2 = api.moe_forward(L, xd2, ws, flags=F).clone()
     ya = torch.empty_like(xd)
