@@ -30,6 +30,29 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_T1_glm52_traffic.json")
+KERNEL_SOURCES = ["kernels_decode.hip", "gemv_device.hpp", "route_device.hpp", "device_common.hpp"]
+
+
+def kernel_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for n in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "int4_quantized_expert_sigmoid_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload):
+    """HBM bytes per launch of the roofline kernel from the committed counter
+    runs, or None when they were taken on other kernel sources."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    with open(TRAFFIC_FILE) as f:
+        t = json.load(f)
+    if t.get("workload") != workload or t.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return t.get("traffic_bytes_per_launch")
 STAGES = ["router_shared_gateup", "select_gateup", "down_combine"]   # the three decode launches
 
 
@@ -42,6 +65,8 @@ def parse():
     p.add_argument("--instances", type=int, default=16, help="resident layer instances (MALL defeat)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-graph", action="store_true", help="launch every step eagerly")
+    p.add_argument("--copy-probe", action="store_true",
+                   help="after timing, copy a 1 GiB buffer once (a known-size kernel for HBM counter scaling)")
     return p.parse_args()
 
 
@@ -124,10 +149,9 @@ def main():
             routes.append(idx.cpu().numpy())
     union = [len(set(r.reshape(-1).tolist())) for r in routes]
     bytes_step = [(u + spec.has_shared) * spec.expert_bytes for u in union]
-    # the routed gate/up launch streams the U routed experts' gate/up (the
-    # shared expert's ride along the router launch); the down launch streams
-    # every item's down matrix, the shared expert's included
-    gateup_bytes = [u * 2 * spec.I * (spec.H // 2 + 4) for u in union]
+    # the gate/up launch streams the gate/up rows of the U routed experts and
+    # of the shared expert; the down launch streams every item's down matrix
+    gateup_bytes = [(u + spec.has_shared) * 2 * spec.I * (spec.H // 2 + 4) for u in union]
     down_bytes = [(u + spec.has_shared) * spec.H * (spec.I // 2 + 4) for u in union]
 
     # ---------------- timed region: K steps (graph replays of G steps)
@@ -203,6 +227,16 @@ def main():
     log(f"bench: gate/up {gu_gbs:.0f} GB/s, down {dn_gbs:.0f} GB/s, whole step {step_gbs:.0f} GB/s "
         f"on int4 expert bytes; {ms_step * 1e3:.2f} us/step (graph={use_graph}), wall {t_wall:.3f} s")
 
+    if args.copy_probe:
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"bench: copy probe {src.numel() * 4} B read, {dst.numel() * 4} B written; "
+            f"kernel source hash {kernel_source_hash()}")
+        del src, dst
+
     cpu = None
     if not args.no_cpu_baseline:
         log("bench: timing the oracle on a CPU sample")
@@ -229,7 +263,7 @@ def main():
                    "stage_ms": {n: round(float(v), 5) for n, v in zip(STAGES, stage_avg)}},
         "roofline": {"bound": "hbm", "kernel": "k_select_gateup", "achieved": round(gu_gbs, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gu_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": None,
+                     "traffic": measured_traffic(args.workload),
                      "bytes_per_launch": gu_bytes_avg, "avg_launch_ms": round(float(stage_avg[1]), 5)},
         "cpu_baseline": cpu,
     }
