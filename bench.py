@@ -3,15 +3,20 @@
 Default workload: the GLM-5.2-shaped MoE layer at decode, T = 1 token
 (H=6144, I=2048, 256 routed experts + 1 shared, sigmoid router top-8, int4
 experts, Q8_0-style activations). A step is one pass of the whole hot path
-for one token through one layer: Q8(x) + router logits, top-k + batch union,
-gate/up IDOT GEMV + SwiGLU + Q8(h), down IDOT GEMV, combine with the shared
-expert. Inputs (weights, tokens) are resident in HBM before timing starts.
+for one batch through one layer: router logits + Q8(x), top-k + batch union,
+gate/up IDOT + SwiGLU + Q8(h), down IDOT, combine with the shared expert.
+Inputs (weights, tokens) are resident in HBM before timing starts.
 
 The 256 MB Infinity Cache would hold one layer's 170 MB: steps therefore walk
 round-robin over 16 independently seeded layer instances of that exact shape
 (78 GB resident), so every step streams its experts from HBM as a real
 multi-layer decode does. The steps are captured once in a HIP graph (16
-steps, one per layer instance, 16 different tokens) and replayed.
+steps, one per layer instance, 16 different token batches) and replayed.
+
+Other workloads: glm52_mtp_verify_T4 (T=4), glm52_prefill_T512 (T=512, the
+grouped int8-MFMA path), glm52_chain16_T1 (one token through 16 layers:
+RMSNorm, then the layer with its output added to the residual stream; a step
+is the whole 16-layer stack, restarted from the same input token).
 
 Prints ONE JSON line (metric, value, roofline of the dominant kernel,
 cpu_baseline of the oracle on a bounded sample).
@@ -21,7 +26,6 @@ from __future__ import annotations
 import argparse
 import ctypes
 import json
-import math
 import os
 import sys
 import time
@@ -30,8 +34,13 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+INT8_MFMA_PEAK_TOPS = 5000.0   # MI355X dense int8 MFMA, published
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_T1_glm52_traffic.json")
 KERNEL_SOURCES = ["kernels_decode.hip", "gemv_device.hpp", "route_device.hpp", "device_common.hpp"]
+
+# launches of one layer call, between the profiled events
+STAGES_DECODE = ["router", "select_gateup", "down_combine"]
+STAGES_PREFILL = ["logits", "select_bucket", "gateup_mfma", "down_mfma", "combine"]
 
 
 def kernel_source_hash():
@@ -53,7 +62,6 @@ def measured_traffic(workload):
     if t.get("workload") != workload or t.get("kernel_source_hash") != kernel_source_hash():
         return None
     return t.get("traffic_bytes_per_launch")
-STAGES = ["router_shared_gateup", "select_gateup", "down_combine"]   # the three decode launches
 
 
 def parse():
@@ -76,7 +84,7 @@ def log(*a):
 
 def cpu_baseline(spec, tokens_np, n_tokens=3, reps=3):
     """The oracle (single thread, as it stands) on a bounded sample: n_tokens
-    decode tokens through layer instance 0, each timed reps times (median)."""
+    tokens through layer instance 0, each timed reps times (median)."""
     import numpy as np
     from oracle import layers as OL
     from synth import synth as S
@@ -94,7 +102,7 @@ def cpu_baseline(spec, tokens_np, n_tokens=3, reps=3):
         times.append(sorted(per)[len(per) // 2])
     sec_per_token = float(np.mean(times))
     return {"value": 1.0 / sec_per_token, "unit": "tokens*layers/s", "cores": 1, "kind": "oracle",
-            "sample": f"{n_tokens} decode tokens through one GLM-5.2-shaped layer, median of {reps} runs each "
+            "sample": f"{n_tokens} tokens through one layer of this shape, median of {reps} runs each "
                       f"({sec_per_token:.2f} s/token, single-threaded C oracle, -O2)"}
 
 
@@ -108,7 +116,7 @@ def main():
     import numpy as np
     import torch
 
-    from int4_quantized_expert_sigmoid_amd import api
+    from int4_quantized_expert_sigmoid_amd import api, COLI_ACCUMULATE
     from int4_quantized_expert_sigmoid_amd._lib import lib
     from int4_quantized_expert_sigmoid_amd.synthetic import device_layer
     from synth import synth as S
@@ -117,8 +125,11 @@ def main():
     torch.cuda.set_device(0)
     wl = S.WORKLOADS[args.workload]
     spec, T = wl.layer, wl.tokens.T
-    assert T <= 8, "this bench line covers the decode/verify workloads"
-    n_inst = args.instances
+    chain = wl.n_layers > 1
+    decode = T <= 8                              # token-GEMV path; larger batches take the MFMA path
+    STAGES = STAGES_DECODE if decode else STAGES_PREFILL
+    i_gu, i_dn = (1, 2) if decode else (2, 3)
+    n_inst = wl.n_layers if chain else args.instances
     log(f"bench: {args.workload} T={T}, building {n_inst} layer instances on device")
     t0 = time.time()
     scratch = torch.empty(spec.H * spec.I, dtype=torch.float32, device="cuda")
@@ -128,51 +139,70 @@ def main():
     log(f"bench: layers ready in {time.time() - t0:.1f} s "
         f"({n_inst * spec.n_experts_stored * spec.expert_bytes / 1e9:.1f} GB int4 resident)")
 
-    G = n_inst                                   # steps per captured graph: one per instance
-    from dataclasses import replace
-    toks = S.tokens(replace(wl.tokens, T=T * G), spec.H, wl.seed)
-    x_all = torch.from_numpy(toks).cuda().view(G, T, spec.H)
-    y_all = torch.empty_like(x_all)
     ws = [api.workspace(L, T) for L in layers]
     cls = [L.c() for L in layers]
     stream = torch.cuda.Stream()
+    from dataclasses import replace
 
-    def step(i, s):
-        j = i % G
-        api.moe_forward(layers[j], x_all[j], ws[j], y=y_all[j], stream=s, c_layer=cls[j])
+    if chain:
+        # one step = the token through all layers, restarted from the same input
+        G = 1
+        x0 = torch.from_numpy(S.tokens(wl.tokens, spec.H, wl.seed)).cuda()
+        xr = torch.empty_like(x0)                 # residual stream
+        xn = torch.empty_like(x0)                 # normalised layer input
+        gam = [torch.from_numpy(S.rms_gamma(spec.H, wl.seed, li)).cuda() for li in range(n_inst)]
+        toks = x0.cpu().numpy()
 
-    # algorithmic bytes: every distinct selected expert (+ shared) once per step
-    routes = []
-    with torch.cuda.stream(stream):
-        for j in range(G):
-            idx, _ = api.moe_route(layers[j], x_all[j], ws[j], stream=stream)
-            routes.append(idx.cpu().numpy())
-    union = [len(set(r.reshape(-1).tolist())) for r in routes]
-    bytes_step = [(u + spec.has_shared) * spec.expert_bytes for u in union]
-    # the gate/up launch streams the gate/up rows of the U routed experts and
-    # of the shared expert; the down launch streams every item's down matrix
-    gateup_bytes = [(u + spec.has_shared) * 2 * spec.I * (spec.H // 2 + 4) for u in union]
-    down_bytes = [(u + spec.has_shared) * spec.H * (spec.I // 2 + 4) for u in union]
+        def step(i, s):
+            with torch.cuda.stream(s):
+                xr.copy_(x0)
+            for l in range(n_inst):
+                api.rmsnorm(xr, gam[l], wl.rms_eps, out=xn, stream=s)
+                api.moe_forward(layers[l], xn, ws[l], y=xr, flags=COLI_ACCUMULATE, stream=s, c_layer=cls[l])
+        layer_calls = lambda i: [(l, xn, xr, COLI_ACCUMULATE) for l in range(n_inst)]
+    else:
+        G = n_inst                               # steps per captured graph: one per instance
+        toks = S.tokens(replace(wl.tokens, T=T * G), spec.H, wl.seed)
+        x_all = torch.from_numpy(toks).cuda().view(G, T, spec.H)
+        y_all = torch.empty_like(x_all)
 
-    # ---------------- timed region: K steps (graph replays of G steps)
-    K = max(G, (args.steps + G - 1) // G * G)
-    W = max(G, (args.warmup + G - 1) // G * G)
+        def step(i, s):
+            j = i % G
+            api.moe_forward(layers[j], x_all[j], ws[j], y=y_all[j], stream=s, c_layer=cls[j])
+        layer_calls = lambda i: [(i % G, x_all[i % G], y_all[i % G], 0)]
+
+    # the distinct experts each layer call reads (from the routing of one eager step)
+    for i in range(G):
+        step(i, stream)
+    stream.synchronize()
+    union = []
+    for j in range(n_inst):
+        lay = api.workspace_layout(layers[j], T)
+        idx = ws[j][lay.idx: lay.idx + 4 * T * spec.top_k].view(torch.int32).cpu().numpy()
+        union.append(len(set(idx.tolist())))
+    gu_row, dn_row = 2 * spec.I * (spec.H // 2 + 4), spec.H * (spec.I // 2 + 4)
+    bytes_call = [(u + spec.has_shared) * spec.expert_bytes for u in union]
+    gateup_bytes = [(u + spec.has_shared) * gu_row for u in union]
+    down_bytes = [(u + spec.has_shared) * dn_row for u in union]
+    calls_per_step = n_inst if chain else 1
+
+    # ---------------- timed region: K steps
+    if chain:
+        K, W = max(1, args.steps // n_inst), max(1, args.warmup // n_inst)
+    else:
+        K = max(G, (args.steps + G - 1) // G * G)
+        W = max(G, (args.warmup + G - 1) // G * G)
     use_graph = not args.no_graph
     if use_graph:
         g = torch.cuda.CUDAGraph()
-        with torch.cuda.stream(stream):
-            for i in range(G):                   # warm the code objects before capture
-                step(i, stream)
-        stream.synchronize()
         with torch.cuda.graph(g, stream=stream):
             for i in range(G):
                 step(i, torch.cuda.current_stream())
         run = lambda n: [g.replay() for _ in range(n // G)]
     else:
         def run(n):
-            with torch.cuda.stream(stream):
-                for i in range(n):
-                    step(i, stream)
+            for i in range(n):
+                step(i, stream)
     with torch.cuda.stream(stream):
         run(W)
     torch.cuda.synchronize()
@@ -186,44 +216,56 @@ def main():
     t_wall = time.perf_counter() - t_wall
     ms_total = ev0.elapsed_time(ev1)
     ms_step = ms_total / K
-    value = K * T / (ms_total / 1e3)
+    value = K * T * calls_per_step / (ms_total / 1e3)   # tokens x layers per second
 
-    # ---------------- per-stage durations with HIP events (eager, same steps)
+    # ---------------- per-launch durations with HIP events on the bench stream
+    # (eager layer calls on the same inputs; each span includes one launch gap)
     hip = ctypes.CDLL("libamdhip64.so")
     hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
     hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
     hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
-    KP = min(K, 256)
+    hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+    calls = []
+    for i in (range(8) if chain else range(min(K, 256))):
+        calls += layer_calls(i)
     evs = []
-    for _ in range(KP):
+    for _ in calls:
         arr = (ctypes.c_void_p * 6)()
         for k in range(6):
             e = ctypes.c_void_p()
             assert hip.hipEventCreate(ctypes.byref(e)) == 0
             arr[k] = e
         evs.append(arr)
-    for i in range(KP):
-        j = i % G
-        rc = lib().coli_moe_forward_profiled(ctypes.byref(cls[j]), ctypes.c_void_p(x_all[j].data_ptr()), T,
-                                             ctypes.c_void_p(y_all[j].data_ptr()), 0,
+    for (j, xin, yout, fl), arr in zip(calls, evs):
+        if chain:
+            api.rmsnorm(xr, gam[j], wl.rms_eps, out=xn, stream=stream)
+        rc = lib().coli_moe_forward_profiled(ctypes.byref(cls[j]), ctypes.c_void_p(xin.data_ptr()), T,
+                                             ctypes.c_void_p(yout.data_ptr()), fl,
                                              ctypes.c_void_p(ws[j].data_ptr()), ws[j].numel(),
-                                             ctypes.c_void_p(stream.cuda_stream), evs[i], 6)
+                                             ctypes.c_void_p(stream.cuda_stream), arr, 6)
         assert rc == 0, rc
     stream.synchronize()
     NS = len(STAGES)
-    stage_ms = np.zeros((KP, NS))
-    for i in range(KP):
-        hip.hipEventSynchronize(evs[i][5])
+    stage_ms = np.zeros((len(calls), NS))
+    for c, arr in enumerate(evs):
+        hip.hipEventSynchronize(arr[5])
         for k in range(NS):
             f = ctypes.c_float()
-            hip.hipEventElapsedTime(ctypes.byref(f), evs[i][k], evs[i][k + 1])
-            stage_ms[i, k] = f.value
+            hip.hipEventElapsedTime(ctypes.byref(f), arr[k], arr[k + 1])
+            stage_ms[c, k] = f.value
+        for k in range(6):
+            hip.hipEventDestroy(arr[k])
     stage_avg = stage_ms.mean(axis=0)
-    gu_bytes_avg = float(np.mean([gateup_bytes[i % G] for i in range(KP)]))
-    gu_gbs = gu_bytes_avg / (stage_avg[1] * 1e-3) / 1e9
-    dn_gbs = float(np.mean([down_bytes[i % G] for i in range(KP)])) / (stage_avg[2] * 1e-3) / 1e9
-    step_gbs = float(np.mean(bytes_step)) / (ms_step * 1e-3) / 1e9
-    log("bench: stage averages (ms): " + ", ".join(f"{n}={v:.4f}" for n, v in zip(STAGES, stage_avg)))
+    gu_bytes_avg = float(np.mean([gateup_bytes[j] for (j, _, _, _) in calls]))
+    dn_bytes_avg = float(np.mean([down_bytes[j] for (j, _, _, _) in calls]))
+    gu_gbs = gu_bytes_avg / (stage_avg[i_gu] * 1e-3) / 1e9
+    dn_gbs = dn_bytes_avg / (stage_avg[i_dn] * 1e-3) / 1e9
+    step_bytes = float(np.sum(bytes_call)) if chain else float(np.mean(bytes_call))
+    step_gbs = step_bytes / (ms_step * 1e-3) / 1e9
+    # int8 work of the gate/up launch: every (token, expert) pair, shared included
+    gu_ops = T * (spec.top_k + spec.has_shared) * 2 * 2 * spec.H * spec.I
+    gu_tops = gu_ops / (stage_avg[i_gu] * 1e-3) / 1e12
+    log("bench: launch averages (ms): " + ", ".join(f"{n}={v:.4f}" for n, v in zip(STAGES, stage_avg)))
     log(f"bench: gate/up {gu_gbs:.0f} GB/s, down {dn_gbs:.0f} GB/s, whole step {step_gbs:.0f} GB/s "
         f"on int4 expert bytes; {ms_step * 1e3:.2f} us/step (graph={use_graph}), wall {t_wall:.3f} s")
 
@@ -240,10 +282,20 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         log("bench: timing the oracle on a CPU sample")
-        cpu = cpu_baseline(spec, toks.reshape(G * T, spec.H))
+        cpu = cpu_baseline(spec, np.asarray(toks).reshape(-1, spec.H))
 
+    phase = "16-layer decode chain" if chain else ("decode" if decode else "prefill")
+    config = {"workload": args.workload, "H": spec.H, "I": spec.I, "E": spec.E, "top_k": spec.top_k,
+              "shared_experts": spec.has_shared, "T": T, "layers_per_step": calls_per_step,
+              "layer_instances": n_inst, "hip_graph": use_graph,
+              "mean_union_experts": float(np.mean(union)),
+              "expert_bytes_per_step": step_bytes,
+              "step_hbm_gbs": round(step_gbs, 1),
+              "launch_ms": {n: round(float(v), 5) for n, v in zip(STAGES, stage_avg)}}
+    if chain:
+        config["stack_tokens_per_s"] = round(K * T / (ms_total / 1e3), 1)
     out = {
-        "metric": "MoE-layer tokens*layers/s (GLM-5.2-shaped layer, int4 experts, decode)",
+        "metric": f"MoE-layer tokens*layers/s (GLM-5.2-shaped layer, int4 experts, {phase})",
         "value": round(value, 1),
         "unit": "tokens*layers/s",
         "n_gpus": 1,
@@ -255,16 +307,14 @@ def main():
         "vs_baseline": None,
         "dtype": "int4xint8->int32, f64 block sums",
         "data": "synthetic (seeded Philox weights and tokens, no trained checkpoint)",
-        "config": {"workload": args.workload, "H": spec.H, "I": spec.I, "E": spec.E, "top_k": spec.top_k,
-                   "shared_experts": spec.has_shared, "T": T, "layer_instances": n_inst,
-                   "hip_graph": use_graph, "mean_union_experts": float(np.mean(union)),
-                   "expert_bytes_per_step": float(np.mean(bytes_step)),
-                   "step_hbm_gbs": round(step_gbs, 1),
-                   "stage_ms": {n: round(float(v), 5) for n, v in zip(STAGES, stage_avg)}},
-        "roofline": {"bound": "hbm", "kernel": "k_select_gateup", "achieved": round(gu_gbs, 1),
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gu_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": measured_traffic(args.workload),
-                     "bytes_per_launch": gu_bytes_avg, "avg_launch_ms": round(float(stage_avg[1]), 5)},
+        "config": config,
+        "roofline": {"bound": "hbm", "kernel": "k_select_gateup" if decode else "k_gateup_mfma",
+                     "achieved": round(gu_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gu_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": None if chain else measured_traffic(args.workload),
+                     "bytes_per_launch": gu_bytes_avg, "avg_launch_ms": round(float(stage_avg[i_gu]), 5),
+                     "int8_tops": round(gu_tops, 1),
+                     "int8_mfma_frac": round(gu_tops / INT8_MFMA_PEAK_TOPS, 4)},
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
