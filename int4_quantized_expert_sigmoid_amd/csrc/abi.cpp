@@ -70,7 +70,7 @@ WsLayout make_layout(const coli_moe_layer &L, int T, int path)
     o.ctrl = p; p = up(p + CTRL_WORDS * 4);
     o.xq = p; p = up(p + t * H);
     o.xs = p; p = up(p + t * (H / 32) * 4);
-    o.logits = p; p = up(p + t * E * 8);
+    o.logits = p; p = up(p + t * E * 8 * (size_t)(path == 1 ? logits_splits(T, L.E, L.H) : 1));
     o.keys = p; p = up(p + (path == 0 ? 2 * t * E * 8 : 0));
     o.idx = p; p = up(p + t * k * 4);
     o.w = p; p = up(p + t * k * 4);
@@ -221,7 +221,7 @@ static int forward_impl(const coli_moe_layer *L, const float *x, int T, float *y
     }
     if (launch_logits(*L, x, T, reinterpret_cast<double *>(base + lay.logits),
                       reinterpret_cast<int8_t *>(base + lay.xq), reinterpret_cast<float *>(base + lay.xs),
-                      s) != hipSuccess)
+                      lay.path == 1, s) != hipSuccess)
         return COLI_EDEVICE;
     if (record(ev, 1, s)) return COLI_EDEVICE;
     if (launch_select(*L, T, lay, base, nullptr, nullptr, nullptr, nullptr, s) != hipSuccess) return COLI_EDEVICE;
@@ -239,7 +239,8 @@ int coli_moe_route(const coli_moe_layer *L, const float *x, int T, int32_t *idx,
     if (!al16(x) || !al4(idx) || !al4(w)) return COLI_EINVAL;
     hipStream_t s = (hipStream_t)stream;
     char *base = static_cast<char *>(ws);
-    if (launch_logits(*L, x, T, reinterpret_cast<double *>(base + lay.logits), nullptr, nullptr, s) != hipSuccess)
+    if (launch_logits(*L, x, T, reinterpret_cast<double *>(base + lay.logits), nullptr, nullptr, lay.path == 1,
+                      s) != hipSuccess)
         return COLI_EDEVICE;
     return status(launch_select(*L, T, lay, base, nullptr, nullptr, idx, w, s));
 }

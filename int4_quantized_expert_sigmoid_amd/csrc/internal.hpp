@@ -53,9 +53,13 @@ hipError_t launch_zero(void *p, size_t bytes, hipStream_t s);
 hipError_t launch_copy_f32(const float *src, float *dst, size_t n, hipStream_t s);
 
 // ---- router (kernels_route.hip)
-// Router logits z [T][E] (f64); with xq != nullptr also Q8(x) in the reordered layout.
+// Slices of H the large-batch logits are split into (their partial sums are
+// [slices][T][E] f64 at z and are added in order by the selection).
+int logits_splits(int T, int E, int H);
+// Router logits z [T][E] (f64; with split, as logits_splits() partial sums);
+// with xq != nullptr also Q8(x) in the reordered layout.
 hipError_t launch_logits(const coli_moe_layer &L, const float *x, int T, double *z, int8_t *xq, float *xs,
-                         hipStream_t s);
+                         bool split, hipStream_t s);   // split: the grouped-path layout (lay.path == 1)
 // Top-k of every token from logits (or, with given_idx, from the caller's
 // routing), then the batch union of experts (GEMV path) or the per-expert
 // buckets and tile lists (grouped path).

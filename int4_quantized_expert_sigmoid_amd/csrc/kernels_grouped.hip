@@ -43,6 +43,7 @@ struct GroupedArgs {
     int8_t *hq;
     float *hs;
     float *ye;
+    int ntiles_max;            // tiles the grid covers
 };
 
 __device__ __forceinline__ v4i unpack8(uint2 w)
@@ -58,11 +59,44 @@ __device__ __forceinline__ v4i unpack8(uint2 w)
 
 __device__ __forceinline__ int tile_row(int i, int half) { return 8 * (i >> 2) + 4 * half + (i & 3); }
 
+constexpr int PF = 4;          // 32-wide blocks loaded ahead of the MFMAs
+constexpr int N_XCD = 8;       // workgroups go round-robin over the 8 XCDs by index
+
+// Tile and row group of workgroup w. Tiles of one expert are consecutive in
+// the tile list and each re-reads that expert's rows; with nrg a multiple of
+// N_XCD, XCD x (w % 8 == x) owns row groups x, x + 8, ... and walks the
+// tiles in order for each, so the tiles that share rows run together behind
+// one L2 and the repeats hit there.
+__device__ __forceinline__ void tile_rg(int w, int nrg, int ntiles, int &tile, int &rg)
+{
+    if (nrg % N_XCD == 0) {
+        const int x = w % N_XCD, j = w / N_XCD;
+        rg = (j / ntiles) * N_XCD + x;
+        tile = j % ntiles;
+    } else {
+        tile = w / nrg;
+        rg = w % nrg;
+    }
+}
+
+static_assert(PF == 4, "activation scales are fetched four blocks at a time");
+
+struct GuStage {
+    uint2 wg, wu;              // this lane's 8 bytes (16 nibbles) of the gate and up rows
+    int4 xb;                   // its 16 activation codes
+};
+
+struct DnStageG {
+    uint2 wd;
+    int4 hb;
+};
+
 __global__ void __launch_bounds__(256) k_gateup_mfma(GroupedArgs a)
 {
     const int n_rt = a.I / QK;
     const int nrg = (n_rt + WAVES - 1) / WAVES;
-    const int tile = blockIdx.x / nrg, rg = blockIdx.x % nrg;
+    int tile, rg;
+    tile_rg(blockIdx.x, nrg, a.ntiles_max, tile, rg);
     if (tile >= a.ctrl[CTRL_N_TILES_GU]) return;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int rt = rg * WAVES + wave;
@@ -87,23 +121,46 @@ __global__ void __launch_bounds__(256) k_gateup_mfma(GroupedArgs a)
     for (int i = 0; i < 16; ++i) { acc_g[i] = 0.0; acc_u[i] = 0.0; }
     const v16i zero = {};
 
-    for (int b = 0; b < nblk; ++b) {
-        const uint2 wg = *reinterpret_cast<const uint2 *>(pg + 16 * b);
-        const uint2 wu = *reinterpret_cast<const uint2 *>(pu + 16 * b);
-        v4i B = {0, 0, 0, 0};
-        double d = 0.0;
-        if (valid) {
-            const int4 xb = *reinterpret_cast<const int4 *>(px + 32 * b);
-            B[0] = xb.x; B[1] = xb.y; B[2] = xb.z; B[3] = xb.w;
-            d = (double)ps[b] * 0.0625;
-        }
-        const v16i cg = __builtin_amdgcn_mfma_i32_32x32x32_i8(unpack8(wg), B, zero, 0, 0, 0);
-        const v16i cu = __builtin_amdgcn_mfma_i32_32x32x32_i8(unpack8(wu), B, zero, 0, 0, 0);
+    // PF blocks of weights and activations in flight ahead of the MFMAs; the
+    // activation scales of a group of PF blocks come as one 16-byte load
+    GuStage st[PF];
+    auto load = [&](GuStage &g, int b) {
+        g.wg = *reinterpret_cast<const uint2 *>(pg + 16 * b);
+        g.wu = *reinterpret_cast<const uint2 *>(pu + 16 * b);
+        g.xb = *reinterpret_cast<const int4 *>(px + 32 * b);   // padding lanes: token 0, scaled by zero
+    };
+    auto step = [&](const GuStage &g, float dsc) {
+        const v4i B = {g.xb.x, g.xb.y, g.xb.z, g.xb.w};
+        const double d = valid ? (double)dsc * 0.0625 : 0.0;
+        const v16i cg = __builtin_amdgcn_mfma_i32_32x32x32_i8(unpack8(g.wg), B, zero, 0, 0, 0);
+        const v16i cu = __builtin_amdgcn_mfma_i32_32x32x32_i8(unpack8(g.wu), B, zero, 0, 0, 0);
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             acc_g[i] = fma((double)cg[i], d, acc_g[i]);
             acc_u[i] = fma((double)cu[i], d, acc_u[i]);
         }
+    };
+    // whole groups of PF blocks: every load unconditional (past the end it
+    // re-reads the last group), so the waits count exactly the older loads
+    const int nfull = nblk - nblk % PF;
+    if (nfull > 0) {
+#pragma unroll
+        for (int q = 0; q < PF - 1; ++q) load(st[q], q);
+        float4 dcur = *reinterpret_cast<const float4 *>(ps);
+        for (int b0 = 0; b0 < nfull; b0 += PF) {
+            const float4 dnext = *reinterpret_cast<const float4 *>(ps + min(b0 + PF, nfull - PF));
+            const float dq[PF] = {dcur.x, dcur.y, dcur.z, dcur.w};
+#pragma unroll
+            for (int q = 0; q < PF; ++q) {
+                load(st[(q + PF - 1) % PF], min(b0 + q + PF - 1, nblk - 1));
+                step(st[q], dq[q]);
+            }
+            dcur = dnext;
+        }
+    }
+    for (int b = nfull; b < nblk; ++b) {
+        load(st[0], b);
+        step(st[0], ps[b]);
     }
     // epilogue: g, u, h = silu(g)*u, Q8 over the tile's 32 rows per pair
     float hv[16];
@@ -134,7 +191,8 @@ __global__ void __launch_bounds__(256) k_down_mfma(GroupedArgs a)
 {
     const int n_rt = a.H / QK;
     const int nrg = (n_rt + WAVES - 1) / WAVES;
-    const int tile = blockIdx.x / nrg, rg = blockIdx.x % nrg;
+    int tile, rg;
+    tile_rg(blockIdx.x, nrg, a.ntiles_max, tile, rg);
     if (tile >= a.ctrl[CTRL_N_TILES_GU]) return;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int rt = rg * WAVES + wave;
@@ -157,26 +215,45 @@ __global__ void __launch_bounds__(256) k_down_mfma(GroupedArgs a)
     for (int i = 0; i < 16; ++i) acc[i] = 0.0;
     const v16i zero = {};
 
-    for (int b = 0; b < nblk; ++b) {
-        const uint2 wd = *reinterpret_cast<const uint2 *>(pd + 16 * b);
-        v4i B = {0, 0, 0, 0};
-        double d = 0.0;
-        if (valid) {
-            const int4 hb = *reinterpret_cast<const int4 *>(ph + 32 * b);
-            B[0] = hb.x; B[1] = hb.y; B[2] = hb.z; B[3] = hb.w;
-            d = (double)ps[b] * 0.0625;
-        }
-        const v16i c = __builtin_amdgcn_mfma_i32_32x32x32_i8(unpack8(wd), B, zero, 0, 0, 0);
+    DnStageG st[PF];
+    auto load = [&](DnStageG &g, int b) {
+        g.wd = *reinterpret_cast<const uint2 *>(pd + 16 * b);
+        g.hb = *reinterpret_cast<const int4 *>(ph + 32 * b);   // padding lanes: pair p0, scaled by zero
+    };
+    auto step = [&](const DnStageG &g, float dsc) {
+        const v4i B = {g.hb.x, g.hb.y, g.hb.z, g.hb.w};
+        const double d = valid ? (double)dsc * 0.0625 : 0.0;
+        const v16i c = __builtin_amdgcn_mfma_i32_32x32x32_i8(unpack8(g.wd), B, zero, 0, 0, 0);
 #pragma unroll
         for (int i = 0; i < 16; ++i) acc[i] = fma((double)c[i], d, acc[i]);
+    };
+    const int nfull = nblk - nblk % PF;
+    if (nfull > 0) {
+#pragma unroll
+        for (int q = 0; q < PF - 1; ++q) load(st[q], q);
+        float4 dcur = *reinterpret_cast<const float4 *>(ps);
+        for (int b0 = 0; b0 < nfull; b0 += PF) {
+            const float4 dnext = *reinterpret_cast<const float4 *>(ps + min(b0 + PF, nfull - PF));
+            const float dq[PF] = {dcur.x, dcur.y, dcur.z, dcur.w};
+#pragma unroll
+            for (int q = 0; q < PF; ++q) {
+                load(st[(q + PF - 1) % PF], min(b0 + q + PF - 1, nblk - 1));
+                step(st[q], dq[q]);
+            }
+            dcur = dnext;
+        }
+    }
+    for (int b = nfull; b < nblk; ++b) {
+        load(st[0], b);
+        step(st[0], ps[b]);
     }
     if (!valid) return;
+    float rs[16];                                // row scales first: the stores below may not alias them
+#pragma unroll
+    for (int i = 0; i < 16; ++i) rs[i] = a.s_a[(long)e * a.H + (long)rt * QK + tile_row(i, half)];
     const long base = (long)pair * a.H + (long)rt * QK;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        const int r = tile_row(i, half);
-        a.ye[base + r] = (float)((double)a.s_a[(long)e * a.H + (long)rt * QK + r] * acc[i]);
-    }
+    for (int i = 0; i < 16; ++i) a.ye[base + tile_row(i, half)] = (float)((double)rs[i] * acc[i]);
 }
 
 GroupedArgs make_args(const WsLayout &lay, char *ws, const coli_moe_layer &L)
@@ -205,6 +282,7 @@ hipError_t launch_gateup_grouped(const coli_moe_layer &L, int T, const WsLayout 
 {
     (void)T;
     GroupedArgs a = make_args(lay, ws, L);
+    a.ntiles_max = max_tiles(lay, L);
     a.q_a = L.gate_q; a.s_a = L.gate_s; a.q_b = L.up_q; a.s_b = L.up_s;
     a.act = reinterpret_cast<const int8_t *>(ws + lay.xq);
     a.act_s = reinterpret_cast<const float *>(ws + lay.xs);
@@ -217,6 +295,7 @@ hipError_t launch_down_grouped(const coli_moe_layer &L, int T, const WsLayout &l
 {
     (void)T;
     GroupedArgs a = make_args(lay, ws, L);
+    a.ntiles_max = max_tiles(lay, L);
     a.q_a = L.down_q; a.s_a = L.down_s; a.q_b = nullptr; a.s_b = nullptr;
     a.act = reinterpret_cast<const int8_t *>(ws + lay.hq);
     a.act_s = reinterpret_cast<const float *>(ws + lay.hs);

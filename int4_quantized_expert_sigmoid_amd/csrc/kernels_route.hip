@@ -25,39 +25,73 @@ __global__ void __launch_bounds__(256) k_logits_small(const float *__restrict__ 
     logits_expert<NT>(W, x, T, H, E, blockIdx.x, z, red);
 }
 
-// 32 tokens x 32 experts per workgroup, 2x2 outputs per thread, f64 FMA.
-__global__ void __launch_bounds__(256) k_logits_tiled(const float *__restrict__ W, const float *__restrict__ x,
-                                                      int T, int H, int E, double *__restrict__ z)
+// Large batches: 64 tokens x 64 experts per workgroup over one slice of H
+// (blockIdx.z of n_split equal slices, each a whole number of 32-column
+// chunks), 4x4 outputs per thread. The f32 products are exact in f64 and are
+// summed in f64; slice s writes its partial sums to part[s][t][e] and the
+// selection adds the slices in order. The next chunk's loads are in flight
+// while the current one is multiplied.
+constexpr int LG_T = 64, LG_E = 64, LG_K = 32, LG_PAD = 36;
+
+__global__ void __launch_bounds__(256) k_logits_split(const float *__restrict__ W, const float *__restrict__ x,
+                                                      int T, int H, int E, int kspan, double *__restrict__ part)
 {
-    __shared__ float xs[32][33];
-    __shared__ float ws[32][33];
-    const int t0 = blockIdx.x * 32, e0 = blockIdx.y * 32;
-    const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
-    double acc[2][2] = {{0.0, 0.0}, {0.0, 0.0}};
-    for (int k0 = 0; k0 < H; k0 += 32) {
-        for (int i = threadIdx.x; i < 32 * 32; i += 256) {
-            const int r = i >> 5, c = i & 31;
-            xs[r][c] = (t0 + r < T) ? x[(long)(t0 + r) * H + k0 + c] : 0.0f;
-            ws[r][c] = (e0 + r < E) ? W[(long)(e0 + r) * H + k0 + c] : 0.0f;
+    __shared__ float xs[LG_T][LG_PAD];
+    __shared__ float wsm[LG_E][LG_PAD];
+    const int t0 = blockIdx.x * LG_T, e0 = blockIdx.y * LG_E, k0 = blockIdx.z * kspan;
+    const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
+    const int lr = tid >> 3, lc = (tid & 7) * 4;     // loader: rows lr and lr + 32, columns lc..lc+3
+    double acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = 0.0;
+    float4 rx[2], rw[2];
+    auto load = [&](int k) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int r = lr + 32 * h;
+            rx[h] = (t0 + r < T) ? *reinterpret_cast<const float4 *>(x + (long)(t0 + r) * H + k + lc)
+                                 : make_float4(0.f, 0.f, 0.f, 0.f);
+            rw[h] = (e0 + r < E) ? *reinterpret_cast<const float4 *>(W + (long)(e0 + r) * H + k + lc)
+                                 : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+    };
+    load(k0);
+    for (int kc = 0; kc < kspan; kc += LG_K) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            *reinterpret_cast<float4 *>(&xs[lr + 32 * h][lc]) = rx[h];
+            *reinterpret_cast<float4 *>(&wsm[lr + 32 * h][lc]) = rw[h];
         }
         __syncthreads();
-#pragma unroll 8
-        for (int k = 0; k < 32; ++k) {
-            const double a0 = xs[ty][k], a1 = xs[ty + 16][k];
-            const double b0 = ws[tx][k], b1 = ws[tx + 16][k];
-            acc[0][0] = fma(a0, b0, acc[0][0]);
-            acc[0][1] = fma(a0, b1, acc[0][1]);
-            acc[1][0] = fma(a1, b0, acc[1][0]);
-            acc[1][1] = fma(a1, b1, acc[1][1]);
+        if (kc + LG_K < kspan) load(k0 + kc + LG_K);
+#pragma unroll
+        for (int kk = 0; kk < LG_K; kk += 4) {
+            float4 a[4], b[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) a[i] = *reinterpret_cast<const float4 *>(&xs[ty + 16 * i][kk]);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) b[j] = *reinterpret_cast<const float4 *>(&wsm[tx + 16 * j][kk]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    acc[i][j] = fma((double)a[i].x, (double)b[j].x, acc[i][j]);
+                    acc[i][j] = fma((double)a[i].y, (double)b[j].y, acc[i][j]);
+                    acc[i][j] = fma((double)a[i].z, (double)b[j].z, acc[i][j]);
+                    acc[i][j] = fma((double)a[i].w, (double)b[j].w, acc[i][j]);
+                }
         }
         __syncthreads();
     }
+    double *out = part + (long)blockIdx.z * T * E;
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
+        for (int j = 0; j < 4; ++j) {
             const int t = t0 + ty + 16 * i, e = e0 + tx + 16 * j;
-            if (t < T && e < E) z[(long)t * E + e] = acc[i][j];
+            if (t < T && e < E) out[(long)t * E + e] = acc[i][j];
         }
 }
 
@@ -171,16 +205,26 @@ __global__ void __launch_bounds__(1024) k_bucket(BucketArgs a)
 
 } // namespace
 
-hipError_t launch_logits(const coli_moe_layer &L, const float *x, int T, double *z, int8_t *xq, float *xs,
-                         hipStream_t s)
+int logits_splits(int T, int E, int H)
 {
-    if (T > 8) {
+    const long tiles = (long)((T + LG_T - 1) / LG_T) * ((E + LG_E - 1) / LG_E);
+    const int nchunk = H / LG_K;
+    int ns = 1;
+    while (ns * 2 <= 16 && tiles * ns * 2 <= 1024 && nchunk % (ns * 2) == 0) ns *= 2;
+    return ns;
+}
+
+hipError_t launch_logits(const coli_moe_layer &L, const float *x, int T, double *z, int8_t *xq, float *xs,
+                         bool split, hipStream_t s)
+{
+    if (split) {
         if (xq) {
             hipError_t e = launch_quant_q8(x, T, L.H, xq, xs, true, s);
             if (e != hipSuccess) return e;
         }
-        hipLaunchKernelGGL(k_logits_tiled, dim3((T + 31) / 32, (L.E + 31) / 32), dim3(256), 0, s, L.router_w,
-                           x, T, L.H, L.E, z);
+        const int ns = logits_splits(T, L.E, L.H);
+        hipLaunchKernelGGL(k_logits_split, dim3((T + LG_T - 1) / LG_T, (L.E + LG_E - 1) / LG_E, ns), dim3(256), 0,
+                           s, L.router_w, x, T, L.H, L.E, L.H / ns, z);
     } else if (T <= 1) {
         hipLaunchKernelGGL(k_logits_small<1>, dim3(L.E), dim3(256), 0, s, L.router_w, x, T, L.H, L.E, z, xq, xs);
     } else if (T <= 2) {
@@ -199,6 +243,7 @@ hipError_t launch_select(const coli_moe_layer &L, int T, const WsLayout &lay, ch
 {
     SelArgs a;
     a.z = reinterpret_cast<const double *>(ws + lay.logits);
+    a.n_part = lay.path == 1 ? logits_splits(T, L.E, L.H) : 1;
     a.bias = L.router_b;
     a.T = T; a.E = L.E; a.top_k = L.top_k; a.n_group = L.n_group; a.topk_group = L.topk_group;
     a.has_shared = L.has_shared; a.route_scale = L.route_scale;

@@ -80,7 +80,8 @@ struct SelShared;
 struct UnionShared;
 
 struct SelArgs {
-    const double *z;
+    const double *z;           // [T][E] logits, or n_part partial sums [n_part][T][E] added in order
+    int n_part = 1;
     const float *bias;
     int T, E, top_k, n_group, topk_group, has_shared;
     float route_scale;
@@ -92,6 +93,17 @@ struct SelArgs {
     int *item_expert, *item_ntok, *item_tok;
     int *pair_of, *shared_pair;
 };
+
+// Logit z[t][e]: the partial sums over slices of H in slice order.
+__device__ __forceinline__ double sel_logit(const SelArgs &a, int t, int e)
+{
+    const double *p = a.z + (long)t * a.E + e;
+    if (a.n_part <= 1) return ld_dev(p);
+    const long stride = (long)a.T * a.E;
+    double v = 0.0;
+    for (int s = 0; s < a.n_part; ++s) v += ld_dev(p + s * stride);
+    return v;
+}
 
 // LDS of the selection for nt tokens, carved from dynamic shared memory.
 struct SelShared {
@@ -126,7 +138,7 @@ __device__ inline void select_tokens_block(const SelArgs &a, int t0, int nt, Sel
     const int tid = threadIdx.x, nth = blockDim.x;
     for (int i = tid; i < nt * E; i += nth) {
         const int t = i / E, e = i % E;
-        const double s = 1.0 / (1.0 + exp(-ld_dev(a.z + (long)(t0 + t) * E + e)));
+        const double s = 1.0 / (1.0 + exp(-sel_logit(a, t0 + t, e)));
         sh.key[t * E + e] = s + (double)a.bias[e];
     }
     __syncthreads();
@@ -168,7 +180,7 @@ __device__ inline void select_tokens_block(const SelArgs &a, int t0, int nt, Sel
         }
         if (r < k) {
             sh.isel[t * k + r] = e;
-            sh.ssel[t * k + r] = 1.0 / (1.0 + exp(-ld_dev(a.z + (long)(t0 + t) * E + e)));
+            sh.ssel[t * k + r] = 1.0 / (1.0 + exp(-sel_logit(a, t0 + t, e)));
         }
     }
     __syncthreads();
