@@ -114,8 +114,9 @@ __global__ void __launch_bounds__(256) k_select_gateup(SelGuArgs a, GemvArgs g, 
     }
     const int b = (int)blockIdx.x - n_shared_wg;
     DecUnion &u = su.u;
+    // only the publishing workgroup needs the routing weights
     dec_route_union<KPL>(a.key, a.sig, a.T, a.E, a.top_k, a.n_group, a.topk_group, a.route_scale, a.has_shared,
-                         u);
+                         u, b == 0);
     TRACE(a, 1, 1);
     const int nrb = g.I / QK;
     const int item = a.has_shared + b / nrb, rb = b % nrb;

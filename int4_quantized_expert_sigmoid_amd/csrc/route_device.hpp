@@ -459,7 +459,7 @@ __device__ __forceinline__ void lane_pop(int r, unsigned long long (&ok)[KPL], i
 template <int KPL>
 __device__ inline void wave_topk(const double *__restrict__ key, const double *__restrict__ sig, int E, int k,
                                  int n_group, int topk_group, float route_scale, int *sel_e, float *sel_w,
-                                 double *sel_s)
+                                 double *sel_s, bool weights)
 {
     const int lane = threadIdx.x & 63;
     const unsigned long long gm = kept_groups(key, E, n_group, topk_group);
@@ -498,6 +498,7 @@ __device__ inline void wave_topk(const double *__restrict__ key, const double *_
         }
     }
     COLI_SEL_MARK(2);
+    if (!weights) return;
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -530,7 +531,7 @@ struct DecUnion {
 template <int KPL>
 __device__ inline void dec_route_union(const double *__restrict__ key, const double *__restrict__ sig, int T, int E,
                                        int k, int n_group, int topk_group, float route_scale, int has_shared,
-                                       DecUnion &u)
+                                       DecUnion &u, bool weights = true)
 {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nwave = blockDim.x >> 6;
     for (int t = wave; t < T; t += nwave) {
@@ -538,7 +539,7 @@ __device__ inline void dec_route_union(const double *__restrict__ key, const dou
         int *se = u.sel_e + t * k;
         float *sw = u.sel_w + t * k;
         double *ss = u.sel_s + t * k;
-        wave_topk<KPL>(kt, st, E, k, n_group, topk_group, route_scale, se, sw, ss);
+        wave_topk<KPL>(kt, st, E, k, n_group, topk_group, route_scale, se, sw, ss, weights);
     }
     if (T == 1) {                                 // one token: item has_shared + j is its slot j
         __syncthreads();
