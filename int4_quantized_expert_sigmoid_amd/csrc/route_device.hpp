@@ -569,10 +569,19 @@ __device__ inline void dec_route_union(const double *__restrict__ key, const dou
         int e = -1, cnt = 0, qf = -1, my_item = -1;
         if (wave == 0) {
             if (valid) e = u.sel_e[p];
-            for (int q = 0; q < np; ++q) {                  // earlier pairs of the same expert
-                const bool eq = valid && q < p && u.sel_e[q] == e;
-                if (eq && qf < 0) qf = q;
-                cnt += eq ? 1 : 0;
+            if (np <= 64) {                                 // every pair in a lane: read them by readlane
+                for (int q = 0; q < np; ++q) {              // earlier pairs of the same expert
+                    const int eq_e = __builtin_amdgcn_readlane(e, q);
+                    const bool eq = valid && q < p && eq_e == e;
+                    if (eq && qf < 0) qf = q;
+                    cnt += eq ? 1 : 0;
+                }
+            } else {
+                for (int q = 0; q < np; ++q) {
+                    const bool eq = valid && q < p && u.sel_e[q] == e;
+                    if (eq && qf < 0) qf = q;
+                    cnt += eq ? 1 : 0;
+                }
             }
             const bool is_new = valid && cnt == 0;
             const unsigned long long m = __ballot(is_new);
