@@ -10,6 +10,9 @@ LIB = os.path.join(HERE, "libcoli_moe.so")
 SOURCES = ["abi.cpp", "kernels_quant.hip", "kernels_route.hip", "kernels_gemv.hip", "kernels_grouped.hip",
            "kernels_combine.hip", "kernels_fused.hip",
            "kernels_decode.hip"]
+# The grouped MFMA kernels read every MFMA result with VALU instructions; in
+# VGPR form the accumulator copies (one per result) disappear.
+SOURCE_FLAGS = {"kernels_grouped.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-fno-fast-math", "-ffp-contract=fast-honor-pragmas", "-Wall", "-Wno-unused-function"]
@@ -22,7 +25,7 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
     for src in SOURCES:
         obj = os.path.join(objdir, src + ".o")
         lang = ["-x", "hip"] if src.endswith(".cpp") else []
-        cmd = ["hipcc", *FLAGS, "-c", *lang, os.path.join(CSRC, src), "-o", obj]
+        cmd = ["hipcc", *FLAGS, *SOURCE_FLAGS.get(src, []), "-c", *lang, os.path.join(CSRC, src), "-o", obj]
         cmd = [c for c in cmd if c != "-shared"]
         if verbose:
             print(" ".join(cmd), flush=True)

@@ -79,16 +79,29 @@ __device__ __forceinline__ void tile_rg(int w, int nrg, int ntiles, int &tile, i
     }
 }
 
-static_assert(PF == 4, "activation scales are fetched four blocks at a time");
+static_assert(PF == 4, "two pairs of blocks per group: activation scales are fetched four blocks at a time");
+
+// A pair of blocks (b, b+1) per stage: lane half h loads the 16 bytes of
+// block b + h of its row (one contiguous load per row and block instead of
+// two 8-byte halves), and one permlane32 swap per dword hands each half its
+// 8 bytes of both blocks: afterwards A holds block b's bytes 8h..8h+7 and B
+// block b+1's, the layout one MFMA per block expects.
+__device__ __forceinline__ void split_pair(uint4 w, uint2 &A, uint2 &B)
+{
+    const auto s0 = __builtin_amdgcn_permlane32_swap(w.x, w.z, false, false);
+    const auto s1 = __builtin_amdgcn_permlane32_swap(w.y, w.w, false, false);
+    A = make_uint2(s0[0], s1[0]);
+    B = make_uint2(s0[1], s1[1]);
+}
 
 struct GuStage {
-    uint2 wg, wu;              // this lane's 8 bytes (16 nibbles) of the gate and up rows
-    int4 xb;                   // its 16 activation codes
+    uint4 wg, wu;              // 16 bytes of the gate and up rows: block b + half of the pair
+    int4 xb0, xb1;             // this lane's 16 activation codes of blocks b and b+1
 };
 
 struct DnStageG {
-    uint2 wd;
-    int4 hb;
+    uint4 wd;
+    int4 hb0, hb1;
 };
 
 __global__ void __launch_bounds__(256) k_gateup_mfma(GroupedArgs a)
@@ -111,8 +124,8 @@ __global__ void __launch_bounds__(256) k_gateup_mfma(GroupedArgs a)
     const int nblk = a.H / QK;
     const long rowb = a.H / 2;
     const long wrow = (long)e * a.I + (long)rt * QK + n;
-    const uint8_t *pg = a.q_a + wrow * rowb + 8 * half;
-    const uint8_t *pu = a.q_b + wrow * rowb + 8 * half;
+    const uint8_t *pg = a.q_a + wrow * rowb;
+    const uint8_t *pu = a.q_b + wrow * rowb;
     const int8_t *px = a.act + (long)tok * a.H + 16 * half;
     const float *ps = a.act_s + (long)tok * nblk;
 
@@ -121,46 +134,59 @@ __global__ void __launch_bounds__(256) k_gateup_mfma(GroupedArgs a)
     for (int i = 0; i < 16; ++i) { acc_g[i] = 0.0; acc_u[i] = 0.0; }
     const v16i zero = {};
 
-    // PF blocks of weights and activations in flight ahead of the MFMAs; the
-    // activation scales of a group of PF blocks come as one 16-byte load
-    GuStage st[PF];
-    auto load = [&](GuStage &g, int b) {
-        g.wg = *reinterpret_cast<const uint2 *>(pg + 16 * b);
-        g.wu = *reinterpret_cast<const uint2 *>(pu + 16 * b);
-        g.xb = *reinterpret_cast<const int4 *>(px + 32 * b);   // padding lanes: token 0, scaled by zero
-    };
-    auto step = [&](const GuStage &g, float dsc) {
-        const v4i B = {g.xb.x, g.xb.y, g.xb.z, g.xb.w};
+    auto mfma_block = [&](uint2 wg, uint2 wu, int4 xb, float dsc) {
+        const v4i B = {xb.x, xb.y, xb.z, xb.w};
         const double d = valid ? (double)dsc * 0.0625 : 0.0;
-        const v16i cg = __builtin_amdgcn_mfma_i32_32x32x32_i8(unpack8(g.wg), B, zero, 0, 0, 0);
-        const v16i cu = __builtin_amdgcn_mfma_i32_32x32x32_i8(unpack8(g.wu), B, zero, 0, 0, 0);
+        const v16i cg = __builtin_amdgcn_mfma_i32_32x32x32_i8(unpack8(wg), B, zero, 0, 0, 0);
+        const v16i cu = __builtin_amdgcn_mfma_i32_32x32x32_i8(unpack8(wu), B, zero, 0, 0, 0);
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             acc_g[i] = fma((double)cg[i], d, acc_g[i]);
             acc_u[i] = fma((double)cu[i], d, acc_u[i]);
         }
     };
-    // whole groups of PF blocks: every load unconditional (past the end it
-    // re-reads the last group), so the waits count exactly the older loads
-    const int nfull = nblk - nblk % PF;
+    // two pairs of blocks in flight ahead of the MFMAs; the activation
+    // scales of the four blocks of a group come as one 16-byte load
+    GuStage st[2];
+    auto load = [&](GuStage &g, int bp) {
+        const int b = 2 * bp;
+        g.wg = *reinterpret_cast<const uint4 *>(pg + 16 * (b + half));
+        g.wu = *reinterpret_cast<const uint4 *>(pu + 16 * (b + half));
+        g.xb0 = *reinterpret_cast<const int4 *>(px + 32 * b);   // padding lanes: token 0, scaled by zero
+        g.xb1 = *reinterpret_cast<const int4 *>(px + 32 * (b + 1));
+    };
+    auto step = [&](const GuStage &g, float d0, float d1) {
+        uint2 ga, gb, ua, ub;
+        split_pair(g.wg, ga, gb);
+        split_pair(g.wu, ua, ub);
+        mfma_block(ga, ua, g.xb0, d0);
+        mfma_block(gb, ub, g.xb1, d1);
+    };
+    // whole groups of two pairs: every load unconditional (past the end it
+    // re-reads the last pair), so the waits count exactly the older loads
+    const int npair = nblk / 2;
+    const int nfull = nblk % 4 == 0 ? npair - npair % 2 : 0;   // 16-byte scale loads need 4 | nblk
     if (nfull > 0) {
-#pragma unroll
-        for (int q = 0; q < PF - 1; ++q) load(st[q], q);
+        load(st[0], 0);
         float4 dcur = *reinterpret_cast<const float4 *>(ps);
-        for (int b0 = 0; b0 < nfull; b0 += PF) {
-            const float4 dnext = *reinterpret_cast<const float4 *>(ps + min(b0 + PF, nfull - PF));
-            const float dq[PF] = {dcur.x, dcur.y, dcur.z, dcur.w};
-#pragma unroll
-            for (int q = 0; q < PF; ++q) {
-                load(st[(q + PF - 1) % PF], min(b0 + q + PF - 1, nblk - 1));
-                step(st[q], dq[q]);
-            }
+        for (int p0 = 0; p0 < nfull; p0 += 2) {
+            const float4 dnext = *reinterpret_cast<const float4 *>(ps + 2 * min(p0 + 2, nfull - 2));
+            load(st[1], p0 + 1);
+            step(st[0], dcur.x, dcur.y);
+            load(st[0], min(p0 + 2, npair - 1));
+            step(st[1], dcur.z, dcur.w);
             dcur = dnext;
         }
     }
-    for (int b = nfull; b < nblk; ++b) {
-        load(st[0], b);
-        step(st[0], ps[b]);
+    for (int bp = nfull; bp < npair; ++bp) {
+        load(st[0], bp);
+        step(st[0], ps[2 * bp], ps[2 * bp + 1]);
+    }
+    if (nblk % 2) {                              // an odd last block: each half loads its own 8 bytes
+        const int b = nblk - 1;
+        mfma_block(*reinterpret_cast<const uint2 *>(pg + 16 * b + 8 * half),
+                   *reinterpret_cast<const uint2 *>(pu + 16 * b + 8 * half),
+                   *reinterpret_cast<const int4 *>(px + 32 * b), ps[b]);
     }
     // epilogue: g, u, h = silu(g)*u, Q8 over the tile's 32 rows per pair
     float hv[16];
@@ -206,7 +232,7 @@ __global__ void __launch_bounds__(256) k_down_mfma(GroupedArgs a)
     const int nblk = a.I / QK;
     const long rowb = a.I / 2;
     const long wrow = (long)e * a.H + (long)rt * QK + n;
-    const uint8_t *pd = a.q_a + wrow * rowb + 8 * half;
+    const uint8_t *pd = a.q_a + wrow * rowb;
     const int8_t *ph = a.act + (long)(valid ? pair : p0) * a.I + 16 * half;
     const float *ps = a.act_s + (long)(valid ? pair : p0) * nblk;
 
@@ -215,37 +241,48 @@ __global__ void __launch_bounds__(256) k_down_mfma(GroupedArgs a)
     for (int i = 0; i < 16; ++i) acc[i] = 0.0;
     const v16i zero = {};
 
-    DnStageG st[PF];
-    auto load = [&](DnStageG &g, int b) {
-        g.wd = *reinterpret_cast<const uint2 *>(pd + 16 * b);
-        g.hb = *reinterpret_cast<const int4 *>(ph + 32 * b);   // padding lanes: pair p0, scaled by zero
-    };
-    auto step = [&](const DnStageG &g, float dsc) {
-        const v4i B = {g.hb.x, g.hb.y, g.hb.z, g.hb.w};
+    auto mfma_block = [&](uint2 wd, int4 hb, float dsc) {
+        const v4i B = {hb.x, hb.y, hb.z, hb.w};
         const double d = valid ? (double)dsc * 0.0625 : 0.0;
-        const v16i c = __builtin_amdgcn_mfma_i32_32x32x32_i8(unpack8(g.wd), B, zero, 0, 0, 0);
+        const v16i c = __builtin_amdgcn_mfma_i32_32x32x32_i8(unpack8(wd), B, zero, 0, 0, 0);
 #pragma unroll
         for (int i = 0; i < 16; ++i) acc[i] = fma((double)c[i], d, acc[i]);
     };
-    const int nfull = nblk - nblk % PF;
+    DnStageG st[2];
+    auto load = [&](DnStageG &g, int bp) {
+        const int b = 2 * bp;
+        g.wd = *reinterpret_cast<const uint4 *>(pd + 16 * (b + half));
+        g.hb0 = *reinterpret_cast<const int4 *>(ph + 32 * b);   // padding lanes: pair p0, scaled by zero
+        g.hb1 = *reinterpret_cast<const int4 *>(ph + 32 * (b + 1));
+    };
+    auto step = [&](const DnStageG &g, float d0, float d1) {
+        uint2 wa, wb;
+        split_pair(g.wd, wa, wb);
+        mfma_block(wa, g.hb0, d0);
+        mfma_block(wb, g.hb1, d1);
+    };
+    const int npair = nblk / 2;
+    const int nfull = nblk % 4 == 0 ? npair - npair % 2 : 0;   // 16-byte scale loads need 4 | nblk
     if (nfull > 0) {
-#pragma unroll
-        for (int q = 0; q < PF - 1; ++q) load(st[q], q);
+        load(st[0], 0);
         float4 dcur = *reinterpret_cast<const float4 *>(ps);
-        for (int b0 = 0; b0 < nfull; b0 += PF) {
-            const float4 dnext = *reinterpret_cast<const float4 *>(ps + min(b0 + PF, nfull - PF));
-            const float dq[PF] = {dcur.x, dcur.y, dcur.z, dcur.w};
-#pragma unroll
-            for (int q = 0; q < PF; ++q) {
-                load(st[(q + PF - 1) % PF], min(b0 + q + PF - 1, nblk - 1));
-                step(st[q], dq[q]);
-            }
+        for (int p0 = 0; p0 < nfull; p0 += 2) {
+            const float4 dnext = *reinterpret_cast<const float4 *>(ps + 2 * min(p0 + 2, nfull - 2));
+            load(st[1], p0 + 1);
+            step(st[0], dcur.x, dcur.y);
+            load(st[0], min(p0 + 2, npair - 1));
+            step(st[1], dcur.z, dcur.w);
             dcur = dnext;
         }
     }
-    for (int b = nfull; b < nblk; ++b) {
-        load(st[0], b);
-        step(st[0], ps[b]);
+    for (int bp = nfull; bp < npair; ++bp) {
+        load(st[0], bp);
+        step(st[0], ps[2 * bp], ps[2 * bp + 1]);
+    }
+    if (nblk % 2) {
+        const int b = nblk - 1;
+        mfma_block(*reinterpret_cast<const uint2 *>(pd + 16 * b + 8 * half),
+                   *reinterpret_cast<const int4 *>(ph + 32 * b), ps[b]);
     }
     if (!valid) return;
     float rs[16];                                // row scales first: the stores below may not alias them
