@@ -35,31 +35,43 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 INT8_MFMA_PEAK_TOPS = 5000.0   # MI355X dense int8 MFMA, published
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_T1_glm52_traffic.json")
-KERNEL_SOURCES = ["kernels_decode.hip", "gemv_device.hpp", "route_device.hpp", "device_common.hpp"]
+# committed counter runs (HBM bytes per launch of the roofline kernel) and the
+# sources that kernel is built from: a reading counts only while they are unchanged
+TRAFFIC = {
+    "glm52_decode_T1": ("decode_T1_glm52_traffic.json",
+                        ["csrc/kernels_decode.hip", "csrc/gemv_device.hpp", "csrc/route_device.hpp",
+                         "csrc/device_common.hpp", "csrc/internal.hpp", "build.py"]),
+    "glm52_prefill_T512": ("prefill_T512_glm52_traffic.json",
+                           ["csrc/kernels_grouped.hip", "csrc/device_common.hpp", "csrc/internal.hpp",
+                            "build.py"]),
+}
 
 # launches of one layer call, between the profiled events
 STAGES_DECODE = ["router", "select_gateup", "down_combine"]
 STAGES_PREFILL = ["logits", "select_bucket", "gateup_mfma", "down_mfma", "combine"]
 
 
-def kernel_source_hash():
+def kernel_source_hash(workload):
     import hashlib
     h = hashlib.sha256()
-    for n in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "int4_quantized_expert_sigmoid_amd", "csrc", n), "rb") as f:
+    for n in TRAFFIC[workload][1]:
+        with open(os.path.join(ROOT, "int4_quantized_expert_sigmoid_amd", n), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
 def measured_traffic(workload):
     """HBM bytes per launch of the roofline kernel from the committed counter
-    runs, or None when they were taken on other kernel sources."""
-    if not os.path.exists(TRAFFIC_FILE):
+    runs, or None when there are none for this workload or they were taken on
+    other kernel sources."""
+    if workload not in TRAFFIC:
         return None
-    with open(TRAFFIC_FILE) as f:
+    path = os.path.join(ROOT, "profiles", TRAFFIC[workload][0])
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
         t = json.load(f)
-    if t.get("workload") != workload or t.get("kernel_source_hash") != kernel_source_hash():
+    if t.get("workload") != workload or t.get("kernel_source_hash") != kernel_source_hash(workload):
         return None
     return t.get("traffic_bytes_per_launch")
 
@@ -275,8 +287,8 @@ def main():
         torch.cuda.synchronize()
         dst.copy_(src)
         torch.cuda.synchronize()
-        log(f"bench: copy probe {src.numel() * 4} B read, {dst.numel() * 4} B written; "
-            f"kernel source hash {kernel_source_hash()}")
+        log(f"bench: copy probe {src.numel() * 4} B read, {dst.numel() * 4} B written"
+            + (f"; kernel source hash {kernel_source_hash(args.workload)}" if args.workload in TRAFFIC else ""))
         del src, dst
 
     cpu = None

@@ -59,7 +59,6 @@ __device__ __forceinline__ v4i unpack8(uint2 w)
 
 __device__ __forceinline__ int tile_row(int i, int half) { return 8 * (i >> 2) + 4 * half + (i & 3); }
 
-constexpr int PF = 4;          // 32-wide blocks loaded ahead of the MFMAs
 constexpr int N_XCD = 8;       // workgroups go round-robin over the 8 XCDs by index
 
 // Tile and row group of workgroup w. Tiles of one expert are consecutive in
@@ -79,13 +78,15 @@ __device__ __forceinline__ void tile_rg(int w, int nrg, int ntiles, int &tile, i
     }
 }
 
-static_assert(PF == 4, "two pairs of blocks per group: activation scales are fetched four blocks at a time");
+// Keeps the loads above it issued before the work below it: without it the
+// scheduler sinks a stage's loads to just before their use (to save
+// registers), and every stage then waits out a full memory latency.
+__device__ __forceinline__ void issue_fence() { __asm__ volatile("" ::: "memory"); }
 
-// A pair of blocks (b, b+1) per stage: lane half h loads the 16 bytes of
-// block b + h of its row (one contiguous load per row and block instead of
-// two 8-byte halves), and one permlane32 swap per dword hands each half its
-// 8 bytes of both blocks: afterwards A holds block b's bytes 8h..8h+7 and B
-// block b+1's, the layout one MFMA per block expects.
+// A pair of blocks (b, b+1): lane half h holds the 16 bytes of block b + h
+// of its row, and one permlane32 swap per dword hands each half its 8 bytes
+// of both blocks: afterwards A holds block b's bytes 8h..8h+7 and B block
+// b+1's, the layout one MFMA per block expects.
 __device__ __forceinline__ void split_pair(uint4 w, uint2 &A, uint2 &B)
 {
     const auto s0 = __builtin_amdgcn_permlane32_swap(w.x, w.z, false, false);
@@ -94,46 +95,126 @@ __device__ __forceinline__ void split_pair(uint4 w, uint2 &A, uint2 &B)
     B = make_uint2(s0[1], s1[1]);
 }
 
-struct GuStage {
-    uint4 wg, wu;              // 16 bytes of the gate and up rows: block b + half of the pair
-    int4 xb0, xb1;             // this lane's 16 activation codes of blocks b and b+1
+// Staging. The K loop runs in stages of KS = 8 blocks: one 128-byte line of
+// every weight row and 256 bytes of every pair's activation row. Global loads
+// read whole lines (8 lanes per weight row, 16 lanes per activation row) into
+// registers one stage ahead; after the current stage's MFMAs they go to LDS,
+// from where each lane reads the pieces its MFMA operands need. Row n's
+// 16-byte chunk c sits at chunk position c ^ (n & 7) (pair p's chunk c at
+// c ^ (p & 7)), so the 8 lanes of a 16-byte LDS access group touch 8
+// different bank groups both when storing lines and when reading columns.
+// The weight rows of a wave are its own (single buffer); the activation
+// rows are shared by the workgroup's waves (double buffer, one barrier per
+// stage).
+constexpr int KS = 8;
+constexpr int XC = 2 * KS;     // 16-byte activation chunks per pair and stage
+
+// Staged data is held in clang vector types: plain loads and stores (struct
+// copies of the HIP vector types become memcpys that keep the stage in
+// scratch memory).
+template <int NM>
+struct StageRegs {
+    v4i w[NM][4];              // NM weight matrices: 4 loads of 8 rows x 128 bytes
+    v4i x[2];                  // 2 loads of 4 pairs x 256 bytes (this wave's share of the tile)
+    float d[KS];               // this lane's pair: activation scales of the stage's blocks
 };
 
-struct DnStageG {
-    uint4 wd;
-    int4 hb0, hb1;
+template <int NM>
+struct StageLds {
+    v4i w[WAVES][NM][QK][KS];
+    v4i x[2][TILE_N][XC];
 };
+
+__device__ __forceinline__ uint4 as_u4(v4i v) { return make_uint4((uint32_t)v[0], (uint32_t)v[1], (uint32_t)v[2], (uint32_t)v[3]); }
+__device__ __forceinline__ int4 as_i4(v4i v) { return make_int4(v[0], v[1], v[2], v[3]); }
+
+// Loads stage s. Rows past the matrix end are never touched (waves without
+// rows skip the weight loads); blocks past nblk are clamped to the last
+// block (their products are never added).
+template <int NM>
+__device__ __forceinline__ void load_stage(StageRegs<NM> &r, int s, int nblk, bool rows_ok, const uint8_t *const (&wrow)[NM],
+                                           long rowb, const int8_t *const (&xrow)[2], const float *srow, bool vec_scales)
+{
+    const int lane = threadIdx.x & 63;
+    const int b0 = s * KS;
+    if (rows_ok) {
+        const int blk = min(b0 + (lane & 7), nblk - 1);
+#pragma unroll
+        for (int m = 0; m < NM; ++m)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                r.w[m][j] = *reinterpret_cast<const v4i *>(wrow[m] + (long)(8 * j) * rowb + 16 * blk);
+    }
+    const int c = lane & 15;
+    const int xb = min(b0 + (c >> 1), nblk - 1);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) r.x[i] = *reinterpret_cast<const v4i *>(xrow[i] + 32 * xb + 16 * (c & 1));
+    if (vec_scales) {                            // 4 | nblk: two 16-byte loads, the second clamped in bounds
+        const float4 d0 = *reinterpret_cast<const float4 *>(srow + b0);
+        const float4 d1 = *reinterpret_cast<const float4 *>(srow + min(b0 + 4, nblk - 4));
+        r.d[0] = d0.x; r.d[1] = d0.y; r.d[2] = d0.z; r.d[3] = d0.w;
+        r.d[4] = d1.x; r.d[5] = d1.y; r.d[6] = d1.z; r.d[7] = d1.w;
+    } else {
+#pragma unroll
+        for (int k = 0; k < KS; ++k) r.d[k] = srow[min(b0 + k, nblk - 1)];
+    }
+}
+
+template <int NM>
+__device__ __forceinline__ void store_stage(StageLds<NM> &sm, const StageRegs<NM> &r, int buf, bool rows_ok)
+{
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    if (rows_ok) {
+        const int r8 = lane >> 3, c8 = (lane & 7) ^ r8;
+#pragma unroll
+        for (int m = 0; m < NM; ++m)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) sm.w[wave][m][8 * j + r8][c8] = r.w[m][j];
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int p = 8 * wave + 4 * i + (lane >> 4);
+        sm.x[buf][p][(lane & 15) ^ (p & 7)] = r.x[i];
+    }
+}
+
+// Global row of this wave's share of the tile's activation loads (pair
+// 8*wave + 4*i + lane/16; pairs past np read the tile's first pair).
+__device__ __forceinline__ int stage_pair(int i, int np)
+{
+    const int p = 8 * (threadIdx.x >> 6) + 4 * i + ((threadIdx.x & 63) >> 4);
+    return p < np ? p : 0;
+}
 
 __global__ void __launch_bounds__(256) k_gateup_mfma(GroupedArgs a)
 {
+    __shared__ StageLds<2> sm;
     const int n_rt = a.I / QK;
     const int nrg = (n_rt + WAVES - 1) / WAVES;
     int tile, rg;
     tile_rg(blockIdx.x, nrg, a.ntiles_max, tile, rg);
-    if (tile >= a.ctrl[CTRL_N_TILES_GU]) return;
+    if (tile >= a.ctrl[CTRL_N_TILES_GU]) return;          // uniform over the workgroup
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int rt = rg * WAVES + wave;
-    if (rt >= n_rt) return;
+    const bool rows_ok = rt < n_rt;                       // waves past the last row tile only stage activations
     const int2 td = a.tiles[tile];
     const int e = td.x, p0 = td.y;
     const int np = min(TILE_N, a.expert_off[e + 1] - p0);
     const int n = lane & 31, half = lane >> 5;
     const bool valid = n < np;
-    const int pair = p0 + n;
-    const int tok = valid ? a.pair_tok[pair] : 0;
     const int nblk = a.H / QK;
     const long rowb = a.H / 2;
-    const long wrow = (long)e * a.I + (long)rt * QK + n;
-    const uint8_t *pg = a.q_a + wrow * rowb;
-    const uint8_t *pu = a.q_b + wrow * rowb;
-    const int8_t *px = a.act + (long)tok * a.H + 16 * half;
-    const float *ps = a.act_s + (long)tok * nblk;
+    const long wrow0 = (long)e * a.I + (long)min(rt, n_rt - 1) * QK + (lane >> 3);
+    const uint8_t *const wrow[2] = {a.q_a + wrow0 * rowb, a.q_b + wrow0 * rowb};
+    const int8_t *const xrow[2] = {a.act + (long)a.pair_tok[p0 + stage_pair(0, np)] * a.H,
+                                   a.act + (long)a.pair_tok[p0 + stage_pair(1, np)] * a.H};
+    const float *srow = a.act_s + (long)a.pair_tok[p0 + (valid ? n : 0)] * nblk;
+    const bool vec_scales = nblk % 4 == 0;
 
     double acc_g[16], acc_u[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) { acc_g[i] = 0.0; acc_u[i] = 0.0; }
     const v16i zero = {};
-
     auto mfma_block = [&](uint2 wg, uint2 wu, int4 xb, float dsc) {
         const v4i B = {xb.x, xb.y, xb.z, xb.w};
         const double d = valid ? (double)dsc * 0.0625 : 0.0;
@@ -145,49 +226,45 @@ __global__ void __launch_bounds__(256) k_gateup_mfma(GroupedArgs a)
             acc_u[i] = fma((double)cu[i], d, acc_u[i]);
         }
     };
-    // two pairs of blocks in flight ahead of the MFMAs; the activation
-    // scales of the four blocks of a group come as one 16-byte load
-    GuStage st[2];
-    auto load = [&](GuStage &g, int bp) {
-        const int b = 2 * bp;
-        g.wg = *reinterpret_cast<const uint4 *>(pg + 16 * (b + half));
-        g.wu = *reinterpret_cast<const uint4 *>(pu + 16 * (b + half));
-        g.xb0 = *reinterpret_cast<const int4 *>(px + 32 * b);   // padding lanes: token 0, scaled by zero
-        g.xb1 = *reinterpret_cast<const int4 *>(px + 32 * (b + 1));
-    };
-    auto step = [&](const GuStage &g, float d0, float d1) {
-        uint2 ga, gb, ua, ub;
-        split_pair(g.wg, ga, gb);
-        split_pair(g.wu, ua, ub);
-        mfma_block(ga, ua, g.xb0, d0);
-        mfma_block(gb, ub, g.xb1, d1);
-    };
-    // whole groups of two pairs: every load unconditional (past the end it
-    // re-reads the last pair), so the waits count exactly the older loads
-    const int npair = nblk / 2;
-    const int nfull = nblk % 4 == 0 ? npair - npair % 2 : 0;   // 16-byte scale loads need 4 | nblk
-    if (nfull > 0) {
-        load(st[0], 0);
-        float4 dcur = *reinterpret_cast<const float4 *>(ps);
-        for (int p0 = 0; p0 < nfull; p0 += 2) {
-            const float4 dnext = *reinterpret_cast<const float4 *>(ps + 2 * min(p0 + 2, nfull - 2));
-            load(st[1], p0 + 1);
-            step(st[0], dcur.x, dcur.y);
-            load(st[0], min(p0 + 2, npair - 1));
-            step(st[1], dcur.z, dcur.w);
-            dcur = dnext;
+
+    const int nst = (nblk + KS - 1) / KS;
+    StageRegs<2> st;
+    load_stage<2>(st, 0, nblk, rows_ok, wrow, rowb, xrow, srow, vec_scales);
+    store_stage<2>(sm, st, 0, rows_ok);
+    float dcur[KS];
+#pragma unroll
+    for (int k = 0; k < KS; ++k) dcur[k] = st.d[k];
+    __syncthreads();
+    for (int s = 0; s < nst; ++s) {
+        const bool more = s + 1 < nst;
+        if (more) load_stage<2>(st, s + 1, nblk, rows_ok, wrow, rowb, xrow, srow, vec_scales);
+        issue_fence();
+        if (rows_ok) {
+            const int buf = s & 1, b0 = s * KS;
+#pragma unroll
+            for (int j = 0; j < KS; j += 2) {
+                if (b0 + j >= nblk) break;               // uniform: the stage's valid blocks
+                const int sw = n & 7;
+                const uint4 wgp = as_u4(sm.w[wave][0][n][(j + half) ^ sw]);
+                const uint4 wup = as_u4(sm.w[wave][1][n][(j + half) ^ sw]);
+                const int4 x0 = as_i4(sm.x[buf][n][(2 * j + half) ^ sw]);
+                const int4 x1 = as_i4(sm.x[buf][n][(2 * j + 2 + half) ^ sw]);
+                uint2 ga, gb, ua, ub;
+                split_pair(wgp, ga, gb);
+                split_pair(wup, ua, ub);
+                mfma_block(ga, ua, x0, dcur[j]);
+                if (b0 + j + 1 < nblk) mfma_block(gb, ub, x1, dcur[j + 1]);
+            }
         }
+        issue_fence();
+        if (more) {
+            store_stage<2>(sm, st, (s + 1) & 1, rows_ok);
+#pragma unroll
+            for (int k = 0; k < KS; ++k) dcur[k] = st.d[k];
+        }
+        __syncthreads();
     }
-    for (int bp = nfull; bp < npair; ++bp) {
-        load(st[0], bp);
-        step(st[0], ps[2 * bp], ps[2 * bp + 1]);
-    }
-    if (nblk % 2) {                              // an odd last block: each half loads its own 8 bytes
-        const int b = nblk - 1;
-        mfma_block(*reinterpret_cast<const uint2 *>(pg + 16 * b + 8 * half),
-                   *reinterpret_cast<const uint2 *>(pu + 16 * b + 8 * half),
-                   *reinterpret_cast<const int4 *>(px + 32 * b), ps[b]);
-    }
+    if (!rows_ok) return;
     // epilogue: g, u, h = silu(g)*u, Q8 over the tile's 32 rows per pair
     float hv[16];
     float amax = 0.0f;
@@ -203,44 +280,45 @@ __global__ void __launch_bounds__(256) k_gateup_mfma(GroupedArgs a)
     if (!valid) return;
     float d, id;
     q8_scale(amax, d, id);
-    const long base = (long)pair * a.I + (long)rt * QK;
+    const long base = (long)(p0 + n) * a.I + (long)rt * QK;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
         const int r = tile_row(i, half);
         a.h[base + r] = hv[i];
         a.hq[base + (r & ~7) + perm8(r & 7)] = (int8_t)round_clamp(__fmul_rn(hv[i], id), -127.0f, 127.0f);
     }
-    if (half == 0) a.hs[(long)pair * n_rt + rt] = d;
+    if (half == 0) a.hs[(long)(p0 + n) * n_rt + rt] = d;
 }
 
 __global__ void __launch_bounds__(256) k_down_mfma(GroupedArgs a)
 {
+    __shared__ StageLds<1> sm;
     const int n_rt = a.H / QK;
     const int nrg = (n_rt + WAVES - 1) / WAVES;
     int tile, rg;
     tile_rg(blockIdx.x, nrg, a.ntiles_max, tile, rg);
-    if (tile >= a.ctrl[CTRL_N_TILES_GU]) return;
+    if (tile >= a.ctrl[CTRL_N_TILES_GU]) return;          // uniform over the workgroup
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int rt = rg * WAVES + wave;
-    if (rt >= n_rt) return;
+    const bool rows_ok = rt < n_rt;
     const int2 td = a.tiles[tile];
     const int e = td.x, p0 = td.y;
     const int np = min(TILE_N, a.expert_off[e + 1] - p0);
     const int n = lane & 31, half = lane >> 5;
     const bool valid = n < np;
-    const int pair = p0 + n;
     const int nblk = a.I / QK;
     const long rowb = a.I / 2;
-    const long wrow = (long)e * a.H + (long)rt * QK + n;
-    const uint8_t *pd = a.q_a + wrow * rowb;
-    const int8_t *ph = a.act + (long)(valid ? pair : p0) * a.I + 16 * half;
-    const float *ps = a.act_s + (long)(valid ? pair : p0) * nblk;
+    const long wrow0 = (long)e * a.H + (long)min(rt, n_rt - 1) * QK + (lane >> 3);
+    const uint8_t *const wrow[1] = {a.q_a + wrow0 * rowb};
+    const int8_t *const xrow[2] = {a.act + (long)(p0 + stage_pair(0, np)) * a.I,
+                                   a.act + (long)(p0 + stage_pair(1, np)) * a.I};
+    const float *srow = a.act_s + (long)(p0 + (valid ? n : 0)) * nblk;
+    const bool vec_scales = nblk % 4 == 0;
 
     double acc[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[i] = 0.0;
     const v16i zero = {};
-
     auto mfma_block = [&](uint2 wd, int4 hb, float dsc) {
         const v4i B = {hb.x, hb.y, hb.z, hb.w};
         const double d = valid ? (double)dsc * 0.0625 : 0.0;
@@ -248,47 +326,47 @@ __global__ void __launch_bounds__(256) k_down_mfma(GroupedArgs a)
 #pragma unroll
         for (int i = 0; i < 16; ++i) acc[i] = fma((double)c[i], d, acc[i]);
     };
-    DnStageG st[2];
-    auto load = [&](DnStageG &g, int bp) {
-        const int b = 2 * bp;
-        g.wd = *reinterpret_cast<const uint4 *>(pd + 16 * (b + half));
-        g.hb0 = *reinterpret_cast<const int4 *>(ph + 32 * b);   // padding lanes: pair p0, scaled by zero
-        g.hb1 = *reinterpret_cast<const int4 *>(ph + 32 * (b + 1));
-    };
-    auto step = [&](const DnStageG &g, float d0, float d1) {
-        uint2 wa, wb;
-        split_pair(g.wd, wa, wb);
-        mfma_block(wa, g.hb0, d0);
-        mfma_block(wb, g.hb1, d1);
-    };
-    const int npair = nblk / 2;
-    const int nfull = nblk % 4 == 0 ? npair - npair % 2 : 0;   // 16-byte scale loads need 4 | nblk
-    if (nfull > 0) {
-        load(st[0], 0);
-        float4 dcur = *reinterpret_cast<const float4 *>(ps);
-        for (int p0 = 0; p0 < nfull; p0 += 2) {
-            const float4 dnext = *reinterpret_cast<const float4 *>(ps + 2 * min(p0 + 2, nfull - 2));
-            load(st[1], p0 + 1);
-            step(st[0], dcur.x, dcur.y);
-            load(st[0], min(p0 + 2, npair - 1));
-            step(st[1], dcur.z, dcur.w);
-            dcur = dnext;
+
+    const int nst = (nblk + KS - 1) / KS;
+    StageRegs<1> st;
+    load_stage<1>(st, 0, nblk, rows_ok, wrow, rowb, xrow, srow, vec_scales);
+    store_stage<1>(sm, st, 0, rows_ok);
+    float dcur[KS];
+#pragma unroll
+    for (int k = 0; k < KS; ++k) dcur[k] = st.d[k];
+    __syncthreads();
+    for (int s = 0; s < nst; ++s) {
+        const bool more = s + 1 < nst;
+        if (more) load_stage<1>(st, s + 1, nblk, rows_ok, wrow, rowb, xrow, srow, vec_scales);
+        issue_fence();
+        if (rows_ok) {
+            const int buf = s & 1, b0 = s * KS;
+#pragma unroll
+            for (int j = 0; j < KS; j += 2) {
+                if (b0 + j >= nblk) break;
+                const int sw = n & 7;
+                const uint4 wdp = as_u4(sm.w[wave][0][n][(j + half) ^ sw]);
+                const int4 x0 = as_i4(sm.x[buf][n][(2 * j + half) ^ sw]);
+                const int4 x1 = as_i4(sm.x[buf][n][(2 * j + 2 + half) ^ sw]);
+                uint2 wa, wb;
+                split_pair(wdp, wa, wb);
+                mfma_block(wa, x0, dcur[j]);
+                if (b0 + j + 1 < nblk) mfma_block(wb, x1, dcur[j + 1]);
+            }
         }
+        issue_fence();
+        if (more) {
+            store_stage<1>(sm, st, (s + 1) & 1, rows_ok);
+#pragma unroll
+            for (int k = 0; k < KS; ++k) dcur[k] = st.d[k];
+        }
+        __syncthreads();
     }
-    for (int bp = nfull; bp < npair; ++bp) {
-        load(st[0], bp);
-        step(st[0], ps[2 * bp], ps[2 * bp + 1]);
-    }
-    if (nblk % 2) {
-        const int b = nblk - 1;
-        mfma_block(*reinterpret_cast<const uint2 *>(pd + 16 * b + 8 * half),
-                   *reinterpret_cast<const int4 *>(ph + 32 * b), ps[b]);
-    }
-    if (!valid) return;
+    if (!rows_ok || !valid) return;
     float rs[16];                                // row scales first: the stores below may not alias them
 #pragma unroll
     for (int i = 0; i < 16; ++i) rs[i] = a.s_a[(long)e * a.H + (long)rt * QK + tile_row(i, half)];
-    const long base = (long)pair * a.H + (long)rt * QK;
+    const long base = (long)(p0 + n) * a.H + (long)rt * QK;
 #pragma unroll
     for (int i = 0; i < 16; ++i) a.ye[base + tile_row(i, half)] = (float)((double)rs[i] * acc[i]);
 }
