@@ -109,16 +109,8 @@ __device__ __forceinline__ void split_pair(uint4 w, uint2 &A, uint2 &B)
 constexpr int KS = 8;
 constexpr int XC = 2 * KS;     // 16-byte activation chunks per pair and stage
 
-// Staged data is held in clang vector types: plain loads and stores (struct
-// copies of the HIP vector types become memcpys that keep the stage in
-// scratch memory).
-template <int NM>
-struct StageRegs {
-    v4i w[NM][4];              // NM weight matrices: 4 loads of 8 rows x 128 bytes
-    v4i x[2];                  // 2 loads of 4 pairs x 256 bytes (this wave's share of the tile)
-    float d[KS];               // this lane's pair: activation scales of the stage's blocks
-};
-
+// Staged data is held in clang vector types: plain loads and stores (copies
+// of the HIP vector structs become memcpys that keep a stage in scratch).
 template <int NM>
 struct StageLds {
     v4i w[WAVES][NM][QK][KS];
@@ -128,53 +120,51 @@ struct StageLds {
 __device__ __forceinline__ uint4 as_u4(v4i v) { return make_uint4((uint32_t)v[0], (uint32_t)v[1], (uint32_t)v[2], (uint32_t)v[3]); }
 __device__ __forceinline__ int4 as_i4(v4i v) { return make_int4(v[0], v[1], v[2], v[3]); }
 
-// Loads stage s. Rows past the matrix end are never touched (waves without
-// rows skip the weight loads); blocks past nblk are clamped to the last
-// block (their products are never added).
-template <int NM>
-__device__ __forceinline__ void load_stage(StageRegs<NM> &r, int s, int nblk, bool rows_ok, const uint8_t *const (&wrow)[NM],
-                                           long rowb, const int8_t *const (&xrow)[2], const float *srow, bool vec_scales)
+// Loads of stage s. Rows past the matrix end are never touched (waves
+// without rows skip the weight loads); blocks past nblk are clamped to the
+// last block (their products are never added).
+__device__ __forceinline__ void load_w(v4i (&w)[4], int s, int nblk, const uint8_t *wrow, long rowb)
 {
-    const int lane = threadIdx.x & 63;
-    const int b0 = s * KS;
-    if (rows_ok) {
-        const int blk = min(b0 + (lane & 7), nblk - 1);
+    const int blk = min(s * KS + (threadIdx.x & 7), nblk - 1);
 #pragma unroll
-        for (int m = 0; m < NM; ++m)
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                r.w[m][j] = *reinterpret_cast<const v4i *>(wrow[m] + (long)(8 * j) * rowb + 16 * blk);
-    }
-    const int c = lane & 15;
+    for (int j = 0; j < 4; ++j) w[j] = *reinterpret_cast<const v4i *>(wrow + (long)(8 * j) * rowb + 16 * blk);
+}
+
+__device__ __forceinline__ void load_xd(v4i (&x)[2], float (&d)[KS], int s, int nblk, const int8_t *const (&xrow)[2],
+                                        const float *srow, bool vec_scales)
+{
+    const int b0 = s * KS, c = threadIdx.x & 15;
     const int xb = min(b0 + (c >> 1), nblk - 1);
 #pragma unroll
-    for (int i = 0; i < 2; ++i) r.x[i] = *reinterpret_cast<const v4i *>(xrow[i] + 32 * xb + 16 * (c & 1));
+    for (int i = 0; i < 2; ++i) x[i] = *reinterpret_cast<const v4i *>(xrow[i] + 32 * xb + 16 * (c & 1));
     if (vec_scales) {                            // 4 | nblk: two 16-byte loads, the second clamped in bounds
         const float4 d0 = *reinterpret_cast<const float4 *>(srow + b0);
         const float4 d1 = *reinterpret_cast<const float4 *>(srow + min(b0 + 4, nblk - 4));
-        r.d[0] = d0.x; r.d[1] = d0.y; r.d[2] = d0.z; r.d[3] = d0.w;
-        r.d[4] = d1.x; r.d[5] = d1.y; r.d[6] = d1.z; r.d[7] = d1.w;
+        d[0] = d0.x; d[1] = d0.y; d[2] = d0.z; d[3] = d0.w;
+        d[4] = d1.x; d[5] = d1.y; d[6] = d1.z; d[7] = d1.w;
     } else {
 #pragma unroll
-        for (int k = 0; k < KS; ++k) r.d[k] = srow[min(b0 + k, nblk - 1)];
+        for (int k = 0; k < KS; ++k) d[k] = srow[min(b0 + k, nblk - 1)];
     }
 }
 
 template <int NM>
-__device__ __forceinline__ void store_stage(StageLds<NM> &sm, const StageRegs<NM> &r, int buf, bool rows_ok)
+__device__ __forceinline__ void store_w(StageLds<NM> &sm, int m, const v4i (&w)[4])
 {
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    if (rows_ok) {
-        const int r8 = lane >> 3, c8 = (lane & 7) ^ r8;
+    const int r8 = lane >> 3, c8 = (lane & 7) ^ r8;
 #pragma unroll
-        for (int m = 0; m < NM; ++m)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) sm.w[wave][m][8 * j + r8][c8] = r.w[m][j];
-    }
+    for (int j = 0; j < 4; ++j) sm.w[wave][m][8 * j + r8][c8] = w[j];
+}
+
+template <int NM>
+__device__ __forceinline__ void store_x(StageLds<NM> &sm, int buf, const v4i (&x)[2])
+{
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
         const int p = 8 * wave + 4 * i + (lane >> 4);
-        sm.x[buf][p][(lane & 15) ^ (p & 7)] = r.x[i];
+        sm.x[buf][p][(lane & 15) ^ (p & 7)] = x[i];
     }
 }
 
@@ -215,52 +205,64 @@ __global__ void __launch_bounds__(256) k_gateup_mfma(GroupedArgs a)
 #pragma unroll
     for (int i = 0; i < 16; ++i) { acc_g[i] = 0.0; acc_u[i] = 0.0; }
     const v16i zero = {};
-    auto mfma_block = [&](uint2 wg, uint2 wu, int4 xb, float dsc) {
+    auto mfma_block = [&](double (&acc)[16], uint2 w, int4 xb, float dsc) {
         const v4i B = {xb.x, xb.y, xb.z, xb.w};
         const double d = valid ? (double)dsc * 0.0625 : 0.0;
-        const v16i cg = __builtin_amdgcn_mfma_i32_32x32x32_i8(unpack8(wg), B, zero, 0, 0, 0);
-        const v16i cu = __builtin_amdgcn_mfma_i32_32x32x32_i8(unpack8(wu), B, zero, 0, 0, 0);
+        const v16i c = __builtin_amdgcn_mfma_i32_32x32x32_i8(unpack8(w), B, zero, 0, 0, 0);
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            acc_g[i] = fma((double)cg[i], d, acc_g[i]);
-            acc_u[i] = fma((double)cu[i], d, acc_u[i]);
+        for (int i = 0; i < 16; ++i) acc[i] = fma((double)c[i], d, acc[i]);
+    };
+    // one matrix over the stage's blocks (the activation chunks are read
+    // again for the second matrix: LDS has the bandwidth, registers are short)
+    auto pass = [&](int m, double (&acc)[16], int buf, int b0, const float (&dc)[KS]) {
+        const int sw = n & 7;
+#pragma unroll
+        for (int j = 0; j < KS; j += 2) {
+            if (b0 + j >= nblk) break;                   // uniform: the stage's valid blocks
+            const uint4 wp = as_u4(sm.w[wave][m][n][(j + half) ^ sw]);
+            const int4 x0 = as_i4(sm.x[buf][n][(2 * j + half) ^ sw]);
+            const int4 x1 = as_i4(sm.x[buf][n][(2 * j + 2 + half) ^ sw]);
+            uint2 wa, wb;
+            split_pair(wp, wa, wb);
+            mfma_block(acc, wa, x0, dc[j]);
+            if (b0 + j + 1 < nblk) mfma_block(acc, wb, x1, dc[j + 1]);
         }
     };
 
+    // Per stage: gate pass, then up pass. The next stage's gate rows and
+    // activations load during the gate pass, its up rows during the up pass,
+    // so only one matrix's stage is ever held in registers.
     const int nst = (nblk + KS - 1) / KS;
-    StageRegs<2> st;
-    load_stage<2>(st, 0, nblk, rows_ok, wrow, rowb, xrow, srow, vec_scales);
-    store_stage<2>(sm, st, 0, rows_ok);
-    float dcur[KS];
+    v4i wn[4], xn[2];
+    float dn[KS], dcur[KS];
+    load_xd(xn, dn, 0, nblk, xrow, srow, vec_scales);
+    if (rows_ok) { load_w(wn, 0, nblk, wrow[0], rowb); store_w<2>(sm, 0, wn); load_w(wn, 0, nblk, wrow[1], rowb); store_w<2>(sm, 1, wn); }
+    store_x<2>(sm, 0, xn);
 #pragma unroll
-    for (int k = 0; k < KS; ++k) dcur[k] = st.d[k];
+    for (int k = 0; k < KS; ++k) dcur[k] = dn[k];
     __syncthreads();
     for (int s = 0; s < nst; ++s) {
         const bool more = s + 1 < nst;
-        if (more) load_stage<2>(st, s + 1, nblk, rows_ok, wrow, rowb, xrow, srow, vec_scales);
-        issue_fence();
-        if (rows_ok) {
-            const int buf = s & 1, b0 = s * KS;
-#pragma unroll
-            for (int j = 0; j < KS; j += 2) {
-                if (b0 + j >= nblk) break;               // uniform: the stage's valid blocks
-                const int sw = n & 7;
-                const uint4 wgp = as_u4(sm.w[wave][0][n][(j + half) ^ sw]);
-                const uint4 wup = as_u4(sm.w[wave][1][n][(j + half) ^ sw]);
-                const int4 x0 = as_i4(sm.x[buf][n][(2 * j + half) ^ sw]);
-                const int4 x1 = as_i4(sm.x[buf][n][(2 * j + 2 + half) ^ sw]);
-                uint2 ga, gb, ua, ub;
-                split_pair(wgp, ga, gb);
-                split_pair(wup, ua, ub);
-                mfma_block(ga, ua, x0, dcur[j]);
-                if (b0 + j + 1 < nblk) mfma_block(gb, ub, x1, dcur[j + 1]);
-            }
+        const int buf = s & 1, b0 = s * KS;
+        if (more) {
+            load_xd(xn, dn, s + 1, nblk, xrow, srow, vec_scales);
+            if (rows_ok) load_w(wn, s + 1, nblk, wrow[0], rowb);
         }
         issue_fence();
+        if (rows_ok) pass(0, acc_g, buf, b0, dcur);
+        issue_fence();
+        if (more && rows_ok) {
+            store_w<2>(sm, 0, wn);
+            load_w(wn, s + 1, nblk, wrow[1], rowb);
+        }
+        issue_fence();
+        if (rows_ok) pass(1, acc_u, buf, b0, dcur);
+        issue_fence();
         if (more) {
-            store_stage<2>(sm, st, (s + 1) & 1, rows_ok);
+            if (rows_ok) store_w<2>(sm, 1, wn);
+            store_x<2>(sm, (s + 1) & 1, xn);
 #pragma unroll
-            for (int k = 0; k < KS; ++k) dcur[k] = st.d[k];
+            for (int k = 0; k < KS; ++k) dcur[k] = dn[k];
         }
         __syncthreads();
     }
@@ -290,7 +292,7 @@ __global__ void __launch_bounds__(256) k_gateup_mfma(GroupedArgs a)
     if (half == 0) a.hs[(long)(p0 + n) * n_rt + rt] = d;
 }
 
-__global__ void __launch_bounds__(256) k_down_mfma(GroupedArgs a)
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))) k_down_mfma(GroupedArgs a)
 {
     __shared__ StageLds<1> sm;
     const int n_rt = a.H / QK;
@@ -309,7 +311,7 @@ __global__ void __launch_bounds__(256) k_down_mfma(GroupedArgs a)
     const int nblk = a.I / QK;
     const long rowb = a.I / 2;
     const long wrow0 = (long)e * a.H + (long)min(rt, n_rt - 1) * QK + (lane >> 3);
-    const uint8_t *const wrow[1] = {a.q_a + wrow0 * rowb};
+    const uint8_t *wrow = a.q_a + wrow0 * rowb;
     const int8_t *const xrow[2] = {a.act + (long)(p0 + stage_pair(0, np)) * a.I,
                                    a.act + (long)(p0 + stage_pair(1, np)) * a.I};
     const float *srow = a.act_s + (long)(p0 + (valid ? n : 0)) * nblk;
@@ -328,23 +330,27 @@ __global__ void __launch_bounds__(256) k_down_mfma(GroupedArgs a)
     };
 
     const int nst = (nblk + KS - 1) / KS;
-    StageRegs<1> st;
-    load_stage<1>(st, 0, nblk, rows_ok, wrow, rowb, xrow, srow, vec_scales);
-    store_stage<1>(sm, st, 0, rows_ok);
-    float dcur[KS];
+    v4i wn[4], xn[2];
+    float dn[KS], dcur[KS];
+    load_xd(xn, dn, 0, nblk, xrow, srow, vec_scales);
+    if (rows_ok) { load_w(wn, 0, nblk, wrow, rowb); store_w<1>(sm, 0, wn); }
+    store_x<1>(sm, 0, xn);
 #pragma unroll
-    for (int k = 0; k < KS; ++k) dcur[k] = st.d[k];
+    for (int k = 0; k < KS; ++k) dcur[k] = dn[k];
     __syncthreads();
     for (int s = 0; s < nst; ++s) {
         const bool more = s + 1 < nst;
-        if (more) load_stage<1>(st, s + 1, nblk, rows_ok, wrow, rowb, xrow, srow, vec_scales);
+        if (more) {
+            load_xd(xn, dn, s + 1, nblk, xrow, srow, vec_scales);
+            if (rows_ok) load_w(wn, s + 1, nblk, wrow, rowb);
+        }
         issue_fence();
         if (rows_ok) {
             const int buf = s & 1, b0 = s * KS;
+            const int sw = n & 7;
 #pragma unroll
             for (int j = 0; j < KS; j += 2) {
                 if (b0 + j >= nblk) break;
-                const int sw = n & 7;
                 const uint4 wdp = as_u4(sm.w[wave][0][n][(j + half) ^ sw]);
                 const int4 x0 = as_i4(sm.x[buf][n][(2 * j + half) ^ sw]);
                 const int4 x1 = as_i4(sm.x[buf][n][(2 * j + 2 + half) ^ sw]);
@@ -356,9 +362,10 @@ __global__ void __launch_bounds__(256) k_down_mfma(GroupedArgs a)
         }
         issue_fence();
         if (more) {
-            store_stage<1>(sm, st, (s + 1) & 1, rows_ok);
+            if (rows_ok) store_w<1>(sm, 0, wn);
+            store_x<1>(sm, (s + 1) & 1, xn);
 #pragma unroll
-            for (int k = 0; k < KS; ++k) dcur[k] = st.d[k];
+            for (int k = 0; k < KS; ++k) dcur[k] = dn[k];
         }
         __syncthreads();
     }

@@ -54,6 +54,40 @@ def test_grouped_tiny_full_outputs(tiny, T):
             assert np.array_equal(v["hs"][p], eo.hs)
 
 
+# H = 320: 10 blocks per gate/up row (a part-filled last stage of 8 blocks,
+# scales loaded one by one); I = 96: 3 gate/up row tiles (a wave without
+# rows in the workgroup) and 3 down blocks (an odd last block).
+ODD = S.LayerSpec(H=320, I=96, E=16, top_k=4)
+
+
+@pytest.fixture(scope="module")
+def odd():
+    return device_layer(ODD, 0, 0), OL.full_layer(ODD, 0, 0)
+
+
+@pytest.mark.parametrize("T", [9, 40, 77])
+def test_grouped_odd_shape_full_outputs(odd, T):
+    L, ref = odd
+    x = S.tokens(S.TokenSpec(T=T, token_set=700 + T), ODD.H, 0)
+    ws = api.workspace(L, T)
+    say(f"grouped odd shape H={ODD.H} I={ODD.I} T={T}")
+    y = api.moe_forward(L, dev(x), ws).cpu().numpy()
+    v = ws_views(L, T, ws)
+    assert v["path"] == 1
+    y_o, idx_o, _ = O.moe_forward(ref, x)
+    assert np.array_equal(v["idx"], idx_o)
+    err = rel_err(y, y_o).max()
+    say(f"  max rel {err:.2e}, bit-identical {np.mean(y == y_o):.4f}")
+    assert err <= TOL
+    cache = OL.ExpertCache(ODD, 0, 0)
+    for t in range(0, T, max(1, T // 5)):
+        r = OL.forward_token(ODD, cache, ref.router_w, ref.router_b, x[t])
+        pairs = list(v["pair_of"][t]) + [v["shared_pair"][t]]
+        for p, eo in zip(pairs, r.experts):
+            assert np.array_equal(unreorder(v["hq"][p]), eo.hq)
+            assert np.array_equal(v["hs"][p], eo.hs)
+
+
 @pytest.mark.parametrize("T", [1, 4, 8])
 def test_path_invariance_tiny(tiny, T):
     L, _ = tiny
