@@ -99,22 +99,30 @@ __device__ __forceinline__ void split_pair(uint4 w, uint2 &A, uint2 &B)
 // every weight row and 256 bytes of every pair's activation row. Global loads
 // read whole lines (8 lanes per weight row, 16 lanes per activation row) into
 // registers one stage ahead; after the current stage's MFMAs they go to LDS,
-// from where each lane reads the pieces its MFMA operands need. Row n's
-// 16-byte chunk c sits at chunk position c ^ (n & 7) (pair p's chunk c at
-// c ^ (p & 7)), so the 8 lanes of a 16-byte LDS access group touch 8
-// different bank groups both when storing lines and when reading columns.
+// from where each lane reads the pieces its MFMA operands need. The LDS
+// serves a 16-byte access for 16 lanes per cycle across 64 banks (256
+// bytes): weight row n's 16-byte chunk c sits at chunk position
+// c ^ ((n >> 1) & 7) of its 128-byte row, pair p's chunk c at c ^ (p & 15)
+// of its 256-byte row, so the 16 lanes of an access touch 16 different
+// 16-byte bank groups both when storing lines and when reading columns.
 // The weight rows of a wave are its own (single buffer); the activation
 // rows are shared by the workgroup's waves (double buffer, one barrier per
 // stage).
 constexpr int KS = 8;
 constexpr int XC = 2 * KS;     // 16-byte activation chunks per pair and stage
 
+__device__ __forceinline__ int wsw(int n) { return (n >> 1) & 7; }
+__device__ __forceinline__ int xsw(int p) { return p & 15; }
+
 // Staged data is held in clang vector types: plain loads and stores (copies
 // of the HIP vector structs become memcpys that keep a stage in scratch).
+typedef float v4f __attribute__((ext_vector_type(4)));
+
 template <int NM>
 struct StageLds {
     v4i w[WAVES][NM][QK][KS];
     v4i x[2][TILE_N][XC];
+    float2 d[2][KS / 2][TILE_N];   // activation scales of the stage's block pairs, pair-minor
 };
 
 __device__ __forceinline__ uint4 as_u4(v4i v) { return make_uint4((uint32_t)v[0], (uint32_t)v[1], (uint32_t)v[2], (uint32_t)v[3]); }
@@ -130,31 +138,33 @@ __device__ __forceinline__ void load_w(v4i (&w)[4], int s, int nblk, const uint8
     for (int j = 0; j < 4; ++j) w[j] = *reinterpret_cast<const v4i *>(wrow + (long)(8 * j) * rowb + 16 * blk);
 }
 
-__device__ __forceinline__ void load_xd(v4i (&x)[2], float (&d)[KS], int s, int nblk, const int8_t *const (&xrow)[2],
-                                        const float *srow, bool vec_scales)
+__device__ __forceinline__ void load_x(v4i (&x)[2], int s, int nblk, const int8_t *const (&xrow)[2])
 {
-    const int b0 = s * KS, c = threadIdx.x & 15;
-    const int xb = min(b0 + (c >> 1), nblk - 1);
+    const int c = threadIdx.x & 15;
+    const int xb = min(s * KS + (c >> 1), nblk - 1);
 #pragma unroll
     for (int i = 0; i < 2; ++i) x[i] = *reinterpret_cast<const v4i *>(xrow[i] + 32 * xb + 16 * (c & 1));
-    if (vec_scales) {                            // 4 | nblk: two 16-byte loads, the second clamped in bounds
-        const float4 d0 = *reinterpret_cast<const float4 *>(srow + b0);
-        const float4 d1 = *reinterpret_cast<const float4 *>(srow + min(b0 + 4, nblk - 4));
-        d[0] = d0.x; d[1] = d0.y; d[2] = d0.z; d[3] = d0.w;
-        d[4] = d1.x; d[5] = d1.y; d[6] = d1.z; d[7] = d1.w;
-    } else {
+}
+
+// Wave 0 loads the tile's scales: lane l, pair l/2, blocks 4*(l&1).. of the
+// stage (a 16-byte load when 4 | nblk, clamped in bounds).
+__device__ __forceinline__ v4f load_d(int s, int nblk, const float *drow, bool vec_scales)
+{
+    const int b = s * KS + 4 * (threadIdx.x & 1);
+    if (vec_scales) return *reinterpret_cast<const v4f *>(drow + min(b, nblk - 4));
+    v4f d;
 #pragma unroll
-        for (int k = 0; k < KS; ++k) d[k] = srow[min(b0 + k, nblk - 1)];
-    }
+    for (int k = 0; k < 4; ++k) d[k] = drow[min(b + k, nblk - 1)];
+    return d;
 }
 
 template <int NM>
 __device__ __forceinline__ void store_w(StageLds<NM> &sm, int m, const v4i (&w)[4])
 {
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int r8 = lane >> 3, c8 = (lane & 7) ^ r8;
+    const int r8 = lane >> 3;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) sm.w[wave][m][8 * j + r8][c8] = w[j];
+    for (int j = 0; j < 4; ++j) sm.w[wave][m][8 * j + r8][(lane & 7) ^ wsw(8 * j + r8)] = w[j];
 }
 
 template <int NM>
@@ -164,8 +174,25 @@ __device__ __forceinline__ void store_x(StageLds<NM> &sm, int buf, const v4i (&x
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
         const int p = 8 * wave + 4 * i + (lane >> 4);
-        sm.x[buf][p][(lane & 15) ^ (p & 7)] = x[i];
+        sm.x[buf][p][(lane & 15) ^ xsw(p)] = x[i];
     }
+}
+
+// Scales are kept pair-minor: the 32 lanes reading one block pair's
+// scales read 256 contiguous bytes.
+template <int NM>
+__device__ __forceinline__ void store_d(StageLds<NM> &sm, int buf, v4f d)
+{
+    const int p = (threadIdx.x & 63) >> 1, jp = 2 * (threadIdx.x & 1);
+    sm.d[buf][jp][p] = make_float2(d[0], d[1]);
+    sm.d[buf][jp + 1][p] = make_float2(d[2], d[3]);
+}
+
+// Scales of blocks j and j+1 (j even) of the stage for pair n.
+template <int NM>
+__device__ __forceinline__ float2 read_d2(const StageLds<NM> &sm, int buf, int n, int j)
+{
+    return sm.d[buf][j >> 1][n];
 }
 
 // Global row of this wave's share of the tile's activation loads (pair
@@ -198,7 +225,8 @@ __global__ void __launch_bounds__(256) k_gateup_mfma(GroupedArgs a)
     const uint8_t *const wrow[2] = {a.q_a + wrow0 * rowb, a.q_b + wrow0 * rowb};
     const int8_t *const xrow[2] = {a.act + (long)a.pair_tok[p0 + stage_pair(0, np)] * a.H,
                                    a.act + (long)a.pair_tok[p0 + stage_pair(1, np)] * a.H};
-    const float *srow = a.act_s + (long)a.pair_tok[p0 + (valid ? n : 0)] * nblk;
+    const int pd = (lane >> 1) < np ? (lane >> 1) : 0;
+    const float *drow = a.act_s + (long)a.pair_tok[p0 + pd] * nblk;   // used by wave 0
     const bool vec_scales = nblk % 4 == 0;
 
     double acc_g[16], acc_u[16];
@@ -214,18 +242,19 @@ __global__ void __launch_bounds__(256) k_gateup_mfma(GroupedArgs a)
     };
     // one matrix over the stage's blocks (the activation chunks are read
     // again for the second matrix: LDS has the bandwidth, registers are short)
-    auto pass = [&](int m, double (&acc)[16], int buf, int b0, const float (&dc)[KS]) {
-        const int sw = n & 7;
+    auto pass = [&](int m, double (&acc)[16], int buf, int b0) {
+        const int sw = wsw(n), sx = xsw(n);
 #pragma unroll
         for (int j = 0; j < KS; j += 2) {
             if (b0 + j >= nblk) break;                   // uniform: the stage's valid blocks
             const uint4 wp = as_u4(sm.w[wave][m][n][(j + half) ^ sw]);
-            const int4 x0 = as_i4(sm.x[buf][n][(2 * j + half) ^ sw]);
-            const int4 x1 = as_i4(sm.x[buf][n][(2 * j + 2 + half) ^ sw]);
+            const int4 x0 = as_i4(sm.x[buf][n][(2 * j + half) ^ sx]);
+            const int4 x1 = as_i4(sm.x[buf][n][(2 * j + 2 + half) ^ sx]);
+            const float2 dd = read_d2<2>(sm, buf, n, j);
             uint2 wa, wb;
             split_pair(wp, wa, wb);
-            mfma_block(acc, wa, x0, dc[j]);
-            if (b0 + j + 1 < nblk) mfma_block(acc, wb, x1, dc[j + 1]);
+            mfma_block(acc, wa, x0, dd.x);
+            if (b0 + j + 1 < nblk) mfma_block(acc, wb, x1, dd.y);
         }
     };
 
@@ -234,35 +263,35 @@ __global__ void __launch_bounds__(256) k_gateup_mfma(GroupedArgs a)
     // so only one matrix's stage is ever held in registers.
     const int nst = (nblk + KS - 1) / KS;
     v4i wn[4], xn[2];
-    float dn[KS], dcur[KS];
-    load_xd(xn, dn, 0, nblk, xrow, srow, vec_scales);
+    v4f dn = {};
+    load_x(xn, 0, nblk, xrow);
+    if (wave == 0) dn = load_d(0, nblk, drow, vec_scales);
     if (rows_ok) { load_w(wn, 0, nblk, wrow[0], rowb); store_w<2>(sm, 0, wn); load_w(wn, 0, nblk, wrow[1], rowb); store_w<2>(sm, 1, wn); }
     store_x<2>(sm, 0, xn);
-#pragma unroll
-    for (int k = 0; k < KS; ++k) dcur[k] = dn[k];
+    if (wave == 0) store_d<2>(sm, 0, dn);
     __syncthreads();
     for (int s = 0; s < nst; ++s) {
         const bool more = s + 1 < nst;
         const int buf = s & 1, b0 = s * KS;
         if (more) {
-            load_xd(xn, dn, s + 1, nblk, xrow, srow, vec_scales);
+            load_x(xn, s + 1, nblk, xrow);
+            if (wave == 0) dn = load_d(s + 1, nblk, drow, vec_scales);
             if (rows_ok) load_w(wn, s + 1, nblk, wrow[0], rowb);
         }
         issue_fence();
-        if (rows_ok) pass(0, acc_g, buf, b0, dcur);
+        if (rows_ok) pass(0, acc_g, buf, b0);
         issue_fence();
         if (more && rows_ok) {
             store_w<2>(sm, 0, wn);
             load_w(wn, s + 1, nblk, wrow[1], rowb);
         }
         issue_fence();
-        if (rows_ok) pass(1, acc_u, buf, b0, dcur);
+        if (rows_ok) pass(1, acc_u, buf, b0);
         issue_fence();
         if (more) {
             if (rows_ok) store_w<2>(sm, 1, wn);
             store_x<2>(sm, (s + 1) & 1, xn);
-#pragma unroll
-            for (int k = 0; k < KS; ++k) dcur[k] = dn[k];
+            if (wave == 0) store_d<2>(sm, (s + 1) & 1, dn);
         }
         __syncthreads();
     }
@@ -292,7 +321,7 @@ __global__ void __launch_bounds__(256) k_gateup_mfma(GroupedArgs a)
     if (half == 0) a.hs[(long)(p0 + n) * n_rt + rt] = d;
 }
 
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))) k_down_mfma(GroupedArgs a)
+__global__ void __launch_bounds__(256) k_down_mfma(GroupedArgs a)
 {
     __shared__ StageLds<1> sm;
     const int n_rt = a.H / QK;
@@ -314,7 +343,8 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))
     const uint8_t *wrow = a.q_a + wrow0 * rowb;
     const int8_t *const xrow[2] = {a.act + (long)(p0 + stage_pair(0, np)) * a.I,
                                    a.act + (long)(p0 + stage_pair(1, np)) * a.I};
-    const float *srow = a.act_s + (long)(p0 + (valid ? n : 0)) * nblk;
+    const int pd = (lane >> 1) < np ? (lane >> 1) : 0;
+    const float *drow = a.act_s + (long)(p0 + pd) * nblk;             // used by wave 0
     const bool vec_scales = nblk % 4 == 0;
 
     double acc[16];
@@ -331,41 +361,42 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))
 
     const int nst = (nblk + KS - 1) / KS;
     v4i wn[4], xn[2];
-    float dn[KS], dcur[KS];
-    load_xd(xn, dn, 0, nblk, xrow, srow, vec_scales);
+    v4f dn = {};
+    load_x(xn, 0, nblk, xrow);
+    if (wave == 0) dn = load_d(0, nblk, drow, vec_scales);
     if (rows_ok) { load_w(wn, 0, nblk, wrow, rowb); store_w<1>(sm, 0, wn); }
     store_x<1>(sm, 0, xn);
-#pragma unroll
-    for (int k = 0; k < KS; ++k) dcur[k] = dn[k];
+    if (wave == 0) store_d<1>(sm, 0, dn);
     __syncthreads();
     for (int s = 0; s < nst; ++s) {
         const bool more = s + 1 < nst;
         if (more) {
-            load_xd(xn, dn, s + 1, nblk, xrow, srow, vec_scales);
+            load_x(xn, s + 1, nblk, xrow);
+            if (wave == 0) dn = load_d(s + 1, nblk, drow, vec_scales);
             if (rows_ok) load_w(wn, s + 1, nblk, wrow, rowb);
         }
         issue_fence();
         if (rows_ok) {
             const int buf = s & 1, b0 = s * KS;
-            const int sw = n & 7;
+            const int sw = wsw(n), sx = xsw(n);
 #pragma unroll
             for (int j = 0; j < KS; j += 2) {
                 if (b0 + j >= nblk) break;
                 const uint4 wdp = as_u4(sm.w[wave][0][n][(j + half) ^ sw]);
-                const int4 x0 = as_i4(sm.x[buf][n][(2 * j + half) ^ sw]);
-                const int4 x1 = as_i4(sm.x[buf][n][(2 * j + 2 + half) ^ sw]);
+                const int4 x0 = as_i4(sm.x[buf][n][(2 * j + half) ^ sx]);
+                const int4 x1 = as_i4(sm.x[buf][n][(2 * j + 2 + half) ^ sx]);
+                const float2 dd = read_d2<1>(sm, buf, n, j);
                 uint2 wa, wb;
                 split_pair(wdp, wa, wb);
-                mfma_block(wa, x0, dcur[j]);
-                if (b0 + j + 1 < nblk) mfma_block(wb, x1, dcur[j + 1]);
+                mfma_block(wa, x0, dd.x);
+                if (b0 + j + 1 < nblk) mfma_block(wb, x1, dd.y);
             }
         }
         issue_fence();
         if (more) {
             if (rows_ok) store_w<1>(sm, 0, wn);
             store_x<1>(sm, (s + 1) & 1, xn);
-#pragma unroll
-            for (int k = 0; k < KS; ++k) dcur[k] = dn[k];
+            if (wave == 0) store_d<1>(sm, (s + 1) & 1, dn);
         }
         __syncthreads();
     }
