@@ -59,6 +59,21 @@ __device__ __forceinline__ ItemDesc item_from_union(const GemvArgs &a, int item)
     return d;
 }
 
+// The same from tables an earlier launch wrote: plain loads, which the
+// launch boundary makes coherent (no device-scope loads from every thread).
+__device__ __forceinline__ ItemDesc item_from_table(const GemvArgs &a, int item)
+{
+    ItemDesc d;
+    d.item = item;
+    d.e = a.item_expert[item];
+    d.nt = a.item_ntok[item];
+#pragma unroll
+    for (int s = 0; s < MAX_SLOTS; ++s) d.tok[s] = a.item_tok[item * MAX_SLOTS + s];
+#pragma unroll
+    for (int s = 0; s < MAX_SLOTS; ++s) d.tok[s] = s < d.nt ? d.tok[s] : 0;
+    return d;
+}
+
 // The shared expert: item 0, slot t = token t (known before routing).
 __device__ __forceinline__ ItemDesc shared_item(const GemvArgs &a)
 {

@@ -13,8 +13,8 @@ __global__ void __launch_bounds__(256) k_gateup_gemv(GemvArgs a)
     __shared__ GateUpShared<NT> sh;
     const int nrb = a.I / QK;
     const int item = a.item0 + (int)blockIdx.x / nrb, rb = blockIdx.x % nrb;
-    if (item >= ld_shared_int(a.ctrl + CTRL_N_ITEMS)) return;
-    const ItemDesc it = item_from_union(a, item);
+    if (item >= a.ctrl[CTRL_N_ITEMS]) return;
+    const ItemDesc it = item_from_table(a, item);
     gateup_rows<NT, GemvTune<NT>::RC, false, false>(a, it, rb, sh);
 }
 
@@ -23,8 +23,8 @@ __global__ void __launch_bounds__(256) k_down_gemv(GemvArgs a)
 {
     const int ngrp = a.H / QK;
     const int item = a.item0 + (int)blockIdx.x / ngrp, grp = blockIdx.x % ngrp;
-    if (item >= ld_shared_int(a.ctrl + CTRL_N_ITEMS)) return;
-    const ItemDesc it = item_from_union(a, item);
+    if (item >= a.ctrl[CTRL_N_ITEMS]) return;
+    const ItemDesc it = item_from_table(a, item);
     down_rows<NT, GemvTune<NT>::RD, false, 8>(a, it, grp);
 }
 
