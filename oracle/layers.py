@@ -28,9 +28,10 @@ class PackedExpert:
 
 
 def packed_expert(spec: S.LayerSpec, seed: int, layer: int, e: int) -> PackedExpert:
+    pack = O.pack_int8_rows if spec.weight_bits == 8 else O.pack_int4_rows
     mats = []
     for m in (S.GATE, S.UP, S.DOWN):
-        mats.extend(O.pack_int4_rows(S.expert_matrix(spec, seed, layer, e, m)))
+        mats.extend(pack(S.expert_matrix(spec, seed, layer, e, m)))
     return PackedExpert(*mats)
 
 
@@ -66,6 +67,7 @@ class FullLayer:
     up_s: np.ndarray
     down_q: np.ndarray
     down_s: np.ndarray
+    weight_bits: int = 4
 
 
 def full_layer(spec: S.LayerSpec, seed: int = 0, layer: int = 0) -> FullLayer:
@@ -74,7 +76,7 @@ def full_layer(spec: S.LayerSpec, seed: int = 0, layer: int = 0) -> FullLayer:
     st = lambda name: np.stack([getattr(p, name) for p in ex])
     return FullLayer(spec.H, spec.I, spec.E, spec.top_k, spec.n_group, spec.topk_group,
                      spec.has_shared, spec.route_scale, W, b, st("gate_q"), st("gate_s"),
-                     st("up_q"), st("up_s"), st("down_q"), st("down_s"))
+                     st("up_q"), st("up_s"), st("down_q"), st("down_s"), spec.weight_bits)
 
 
 @dataclass

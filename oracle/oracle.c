@@ -107,6 +107,50 @@ void oracle_rowdot(const uint8_t *q4, const float *s4, const int8_t *q8, const f
     free(S);
 }
 
+/* ----------------------------------------------------------- O11 - O13 --- */
+void oracle_pack_int8_rows(const float *w, int rows, int cols, int8_t *q, float *s)
+{
+    for (int r = 0; r < rows; ++r) {
+        const float *row = w + (size_t)r * cols;
+        float amax = 0.0f;
+        for (int c = 0; c < cols; ++c) {
+            float a = fabsf(row[c]);
+            if (a > amax) amax = a;
+        }
+        float d = amax / 127.0f;
+        float id = (d != 0.0f) ? 1.0f / d : 0.0f;
+        s[r] = d;
+        for (int c = 0; c < cols; ++c)
+            q[(size_t)r * cols + c] = (int8_t)round_clamp(row[c] * id, -127.0f, 127.0f);
+    }
+}
+
+void oracle_block_dots_i8(const int8_t *qw, const int8_t *q8, int rows, int cols, int32_t *S)
+{
+    for (int r = 0; r < rows; ++r) {
+        const int8_t *row = qw + (size_t)r * cols;
+        for (int b = 0; b < cols / 32; ++b) {
+            int32_t acc = 0;
+            for (int k = 32 * b; k < 32 * b + 32; ++k) acc += (int32_t)row[k] * (int32_t)q8[k];
+            S[(size_t)r * (cols / 32) + b] = acc;
+        }
+    }
+}
+
+void oracle_rowdot_i8(const int8_t *qw, const float *sw, const int8_t *q8, const float *d8,
+                      int rows, int cols, float *out)
+{
+    const int nb = cols / 32;
+    int32_t *S = (int32_t *)malloc(sizeof(int32_t) * (size_t)nb);
+    for (int r = 0; r < rows; ++r) {
+        oracle_block_dots_i8(qw + (size_t)r * cols, q8, 1, cols, S);
+        double acc = 0.0;
+        for (int b = 0; b < nb; ++b) acc += (double)d8[b] * (double)S[b];
+        out[r] = (float)((double)sw[r] * acc);
+    }
+    free(S);
+}
+
 /* ------------------------------------------------------------------ O6 --- */
 int oracle_route(const float *W, const float *b, const float *x, int T, int H, int E, int top_k,
                  int n_group, int topk_group, float route_scale, int32_t *idx, float *w,
@@ -170,10 +214,18 @@ int oracle_route(const float *W, const float *b, const float *x, int T, int H, i
 }
 
 /* ------------------------------------------------------------------ O7 --- */
-void oracle_expert(const uint8_t *gate_q, const float *gate_s, const uint8_t *up_q, const float *up_s,
-                   const uint8_t *down_q, const float *down_s, int H, int I,
-                   const int8_t *xq, const float *xs, float *y,
-                   float *g_out, float *u_out, float *h_out, int8_t *hq_out, float *hs_out)
+/* The IDOT row product of either weight format (O5 for 4 bits, O13 for 8). */
+static void rowdot_w(int wbits, const void *q, const float *s, const int8_t *q8, const float *d8,
+                     int rows, int cols, float *out)
+{
+    if (wbits == 8) oracle_rowdot_i8((const int8_t *)q, s, q8, d8, rows, cols, out);
+    else oracle_rowdot((const uint8_t *)q, s, q8, d8, rows, cols, out);
+}
+
+void oracle_expert_w(int wbits, const void *gate_q, const float *gate_s, const void *up_q, const float *up_s,
+                     const void *down_q, const float *down_s, int H, int I,
+                     const int8_t *xq, const float *xs, float *y,
+                     float *g_out, float *u_out, float *h_out, int8_t *hq_out, float *hs_out)
 {
     float *g = (float *)malloc(sizeof(float) * (size_t)I);
     float *u = (float *)malloc(sizeof(float) * (size_t)I);
@@ -181,15 +233,15 @@ void oracle_expert(const uint8_t *gate_q, const float *gate_s, const uint8_t *up
     int8_t *hq = (int8_t *)malloc((size_t)I);
     float *hs = (float *)malloc(sizeof(float) * (size_t)(I / 32));
 
-    oracle_rowdot(gate_q, gate_s, xq, xs, I, H, g);
-    oracle_rowdot(up_q, up_s, xq, xs, I, H, u);
+    rowdot_w(wbits, gate_q, gate_s, xq, xs, I, H, g);
+    rowdot_w(wbits, up_q, up_s, xq, xs, I, H, u);
     for (int i = 0; i < I; ++i) {
         double gd = (double)g[i];
         double silu = gd / (1.0 + exp(-gd));
         h[i] = (float)(silu * (double)u[i]);
     }
     oracle_quant_q8(h, I, hq, hs);
-    oracle_rowdot(down_q, down_s, hq, hs, H, I, y);
+    rowdot_w(wbits, down_q, down_s, hq, hs, H, I, y);
 
     if (g_out) memcpy(g_out, g, sizeof(float) * (size_t)I);
     if (u_out) memcpy(u_out, u, sizeof(float) * (size_t)I);
@@ -197,6 +249,15 @@ void oracle_expert(const uint8_t *gate_q, const float *gate_s, const uint8_t *up
     if (hq_out) memcpy(hq_out, hq, (size_t)I);
     if (hs_out) memcpy(hs_out, hs, sizeof(float) * (size_t)(I / 32));
     free(g); free(u); free(h); free(hq); free(hs);
+}
+
+void oracle_expert(const uint8_t *gate_q, const float *gate_s, const uint8_t *up_q, const float *up_s,
+                   const uint8_t *down_q, const float *down_s, int H, int I,
+                   const int8_t *xq, const float *xs, float *y,
+                   float *g_out, float *u_out, float *h_out, int8_t *hq_out, float *hs_out)
+{
+    oracle_expert_w(4, gate_q, gate_s, up_q, up_s, down_q, down_s, H, I, xq, xs, y,
+                    g_out, u_out, h_out, hq_out, hs_out);
 }
 
 /* ------------------------------------------------------------------ O8 --- */
@@ -250,12 +311,35 @@ void oracle_expert_dense(const uint8_t *gate_q, const float *gate_s, const uint8
     free(h);
 }
 
+/* ----------------------------------------------------------------- O14 --- */
+void oracle_expert_dense_i8(const int8_t *gate_q, const float *gate_s, const int8_t *up_q,
+                            const float *up_s, const int8_t *down_q, const float *down_s, int H, int I,
+                            const float *x, double *y)
+{
+    double *h = (double *)malloc(sizeof(double) * (size_t)I);
+    for (int i = 0; i < I; ++i) {
+        double g = 0.0, u = 0.0;
+        for (int c = 0; c < H; ++c) {
+            g += (double)gate_s[i] * (double)gate_q[(size_t)i * H + c] * (double)x[c];
+            u += (double)up_s[i] * (double)up_q[(size_t)i * H + c] * (double)x[c];
+        }
+        h[i] = g / (1.0 + exp(-g)) * u;
+    }
+    for (int r = 0; r < H; ++r) {
+        double acc = 0.0;
+        for (int i = 0; i < I; ++i) acc += (double)down_s[r] * (double)down_q[(size_t)r * I + i] * h[i];
+        y[r] = acc;
+    }
+    free(h);
+}
+
 /* --------------------------------------------------------- whole layer --- */
 int oracle_moe_forward(const oracle_layer *L, const float *x, int T, float *y, int32_t *idx_out,
                        float *w_out)
 {
     const int H = L->H, I = L->I, E = L->E, k = L->top_k;
     if (H <= 0 || I <= 0 || H % 32 || I % 32 || T < 0) return -1;
+    if (L->weight_bits != 0 && L->weight_bits != 4 && L->weight_bits != 8) return -1;
     int32_t *idx = (int32_t *)malloc(sizeof(int32_t) * (size_t)(T * k + 1));
     float *w = (float *)malloc(sizeof(float) * (size_t)(T * k + 1));
     if (oracle_route(L->router_w, L->router_b, x, T, H, E, k, L->n_group, L->topk_group,
@@ -267,20 +351,23 @@ int oracle_moe_forward(const oracle_layer *L, const float *x, int T, float *y, i
     float *xs = (float *)malloc(sizeof(float) * (size_t)(H / 32));
     float *yr = (float *)malloc(sizeof(float) * (size_t)k * H);
     float *ysh = (float *)malloc(sizeof(float) * (size_t)H);
-    const size_t gq = (size_t)I * (H / 2), dq = (size_t)H * (I / 2);
+    const int wb = L->weight_bits == 8 ? 8 : 4;
+    /* bytes per expert matrix: a byte holds two 4-bit codes or one 8-bit code */
+    const size_t gq = wb == 8 ? (size_t)I * H : (size_t)I * (H / 2);
+    const size_t dq = wb == 8 ? (size_t)H * I : (size_t)H * (I / 2);
     for (int t = 0; t < T; ++t) {
         oracle_quant_q8(x + (size_t)t * H, H, xq, xs);
         for (int j = 0; j < k; ++j) {
             int e = idx[t * k + j];
-            oracle_expert(L->gate_q + e * gq, L->gate_s + (size_t)e * I, L->up_q + e * gq,
-                          L->up_s + (size_t)e * I, L->down_q + e * dq, L->down_s + (size_t)e * H,
-                          H, I, xq, xs, yr + (size_t)j * H, NULL, NULL, NULL, NULL, NULL);
+            oracle_expert_w(wb, L->gate_q + e * gq, L->gate_s + (size_t)e * I, L->up_q + e * gq,
+                            L->up_s + (size_t)e * I, L->down_q + e * dq, L->down_s + (size_t)e * H,
+                            H, I, xq, xs, yr + (size_t)j * H, NULL, NULL, NULL, NULL, NULL);
         }
         if (L->has_shared) {
             int e = E;
-            oracle_expert(L->gate_q + e * gq, L->gate_s + (size_t)e * I, L->up_q + e * gq,
-                          L->up_s + (size_t)e * I, L->down_q + e * dq, L->down_s + (size_t)e * H,
-                          H, I, xq, xs, ysh, NULL, NULL, NULL, NULL, NULL);
+            oracle_expert_w(wb, L->gate_q + e * gq, L->gate_s + (size_t)e * I, L->up_q + e * gq,
+                            L->up_s + (size_t)e * I, L->down_q + e * dq, L->down_s + (size_t)e * H,
+                            H, I, xq, xs, ysh, NULL, NULL, NULL, NULL, NULL);
         }
         oracle_combine(yr, w + (size_t)t * k, k, L->has_shared ? ysh : NULL, H, y + (size_t)t * H);
     }

@@ -63,6 +63,22 @@ void oracle_block_dots(const uint8_t *q4, const int8_t *q8, int rows, int cols, 
 void oracle_rowdot(const uint8_t *q4, const float *s4, const int8_t *q8, const float *d8,
                    int rows, int cols, float *out);
 
+/* O11 [P1 s3.1, quantize_rows] int8 weights, one byte per value. The pages
+ * give no scale rule for them; the reading taken is the symmetric one of
+ * the Q8 activations, per row: d = absmax/127 (f32), id = 1/d (0 if d == 0),
+ * code = clamp(rint(w*id), -127, 127), same rounding and NaN rule as O1.
+ * Natural element order. q: [rows][cols], s: [rows]. */
+void oracle_pack_int8_rows(const float *w, int rows, int cols, int8_t *q, float *s);
+
+/* O12 [P1 s3.1, dot_i8i8] exact int32 block dots of int8 weight rows with
+ * Q8 activations: S[r][b] = sum_{k in block b} qw[r][k] * q8[k]. */
+void oracle_block_dots_i8(const int8_t *qw, const int8_t *q8, int rows, int cols, int32_t *S);
+
+/* O13 [P1 s3.1] IDOT row product of int8 rows: out[r] = (float)(sw[r] * sum_b d8[b]*S[r][b]),
+ * the block sum in double in block order (O5 with O12's block dots). */
+void oracle_rowdot_i8(const int8_t *qw, const float *sw, const int8_t *q8, const float *d8,
+                      int rows, int cols, float *out);
+
 /* O6 [P3 impl, P1 s5] DeepSeek-V3-style sigmoid router for T tokens:
  * z = W x (double), s = 1/(1+exp(-z)), key = s + b (bias used for selection
  * only). With n_group > 1, E is split into n_group equal groups, a group's
@@ -85,6 +101,13 @@ void oracle_expert(const uint8_t *gate_q, const float *gate_s, const uint8_t *up
                    const int8_t *xq, const float *xs, float *y,
                    float *g, float *u, float *h, int8_t *hq, float *hs);
 
+/* O7 for either weight format: wbits = 4 (O5 row products on int4 rows) or
+ * 8 (O13 on int8 rows: gate/up [I][H] int8, down [H][I] int8). */
+void oracle_expert_w(int wbits, const void *gate_q, const float *gate_s, const void *up_q, const float *up_s,
+                     const void *down_q, const float *down_s, int H, int I,
+                     const int8_t *xq, const float *xs, float *y,
+                     float *g, float *u, float *h, int8_t *hq, float *hs);
+
 /* O8 [P1 s5, P3 impl] combine for one token: y = (float)(sum_j w_j*y_j + y_shared),
  * summed in double in j order, the shared expert (weight 1) last; y_shared may
  * be NULL (no shared expert). y_routed: [k][H]. */
@@ -102,14 +125,21 @@ void oracle_expert_dense(const uint8_t *gate_q, const float *gate_s, const uint8
                          const float *up_s, const uint8_t *down_q, const float *down_s, int H, int I,
                          const float *x, double *y);
 
+/* O14 [P1 s3.1] O10 for int8 weight rows (dequantised in double). */
+void oracle_expert_dense_i8(const int8_t *gate_q, const float *gate_s, const int8_t *up_q,
+                            const float *up_s, const int8_t *down_q, const float *down_s, int H, int I,
+                            const float *x, double *y);
+
 /* A whole layer, every expert in host memory. Expert e's matrices start at
- * gate_q + e*I*H/2 (etc.); the shared expert is index E when has_shared. */
+ * gate_q + e*I*H/2 (int4) or gate_q + e*I*H (int8), etc.; the shared expert
+ * is index E when has_shared. */
 typedef struct oracle_layer {
     int H, I, E, top_k, n_group, topk_group, has_shared;
     float route_scale;
     const float *router_w, *router_b;
-    const uint8_t *gate_q, *up_q, *down_q;
+    const uint8_t *gate_q, *up_q, *down_q;   /* int8 rows when weight_bits == 8 */
     const float *gate_s, *up_s, *down_s;
+    int weight_bits;                         /* 4 (or 0) or 8 */
 } oracle_layer;
 
 /* O6 -> O3 -> O7 per selected expert (+ shared) -> O8, for T tokens.

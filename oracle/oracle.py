@@ -41,6 +41,11 @@ def _lib():
         L.oracle_expert_dense.argtypes = [P, P, P, P, P, P, i, i, P, P]
         L.oracle_moe_forward.argtypes = [P, P, i, P, P, P]
         L.oracle_moe_forward.restype = i
+        L.oracle_pack_int8_rows.argtypes = [P, i, i, P, P]
+        L.oracle_block_dots_i8.argtypes = [P, P, i, i, P]
+        L.oracle_rowdot_i8.argtypes = [P, P, P, P, i, i, P]
+        L.oracle_expert_w.argtypes = [i, P, P, P, P, P, P, i, i, P, P, P, P, P, P, P, P]
+        L.oracle_expert_dense_i8.argtypes = [P, P, P, P, P, P, i, i, P, P]
         _L = L
     return _L
 
@@ -105,6 +110,35 @@ def rowdot(q4, s4, q8, d8) -> np.ndarray:
     return out
 
 
+# ---------------------------------------------------------------- O11 - O13
+def pack_int8_rows(w: np.ndarray):
+    """int8 weight rows (natural element order) and their f32 scales."""
+    w = _c(w, np.float32)
+    rows, cols = w.shape
+    q = np.empty((rows, cols), dtype=np.int8)
+    s = np.empty(rows, dtype=np.float32)
+    _lib().oracle_pack_int8_rows(_p(w), rows, cols, _p(q), _p(s))
+    return q, s
+
+
+def block_dots_i8(qw: np.ndarray, q8: np.ndarray) -> np.ndarray:
+    qw = _c(qw, np.int8)
+    q8 = _c(q8, np.int8)
+    rows, cols = qw.shape
+    S = np.empty((rows, cols // 32), dtype=np.int32)
+    _lib().oracle_block_dots_i8(_p(qw), _p(q8), rows, cols, _p(S))
+    return S
+
+
+def rowdot_i8(qw, sw, q8, d8) -> np.ndarray:
+    qw = _c(qw, np.int8)
+    rows, cols = qw.shape
+    out = np.empty(rows, dtype=np.float32)
+    _lib().oracle_rowdot_i8(_p(qw), _p(_c(sw, np.float32)), _p(_c(q8, np.int8)), _p(_c(d8, np.float32)),
+                            rows, cols, _p(out))
+    return out
+
+
 # ----------------------------------------------------------------------- O6
 def route(W, b, x, top_k: int, n_group: int = 1, topk_group: int = 1, route_scale: float = 1.0,
           want_keys: bool = False):
@@ -134,27 +168,38 @@ class ExpertOut:
     hs: np.ndarray
 
 
+def _wbits(q) -> int:
+    """Weight format from the packed array's dtype: int8 rows, or uint8 bytes of int4 pairs."""
+    return 8 if np.asarray(q).dtype == np.int8 else 4
+
+
 def expert(gate_q, gate_s, up_q, up_s, down_q, down_s, xq, xs) -> ExpertOut:
-    gate_q = _c(gate_q, np.uint8)
-    I, Hh = gate_q.shape
-    H = 2 * Hh
+    """O7 (int4 rows, uint8 [I][H/2]) or its int8 form (int8 rows [I][H])."""
+    wb = _wbits(gate_q)
+    dt = np.int8 if wb == 8 else np.uint8
+    gate_q = _c(gate_q, dt)
+    I, Hc = gate_q.shape
+    H = Hc if wb == 8 else 2 * Hc
     o = ExpertOut(y=np.empty(H, np.float32), g=np.empty(I, np.float32), u=np.empty(I, np.float32),
                   h=np.empty(I, np.float32), hq=np.empty(I, np.int8), hs=np.empty(I // 32, np.float32))
-    _lib().oracle_expert(_p(gate_q), _p(_c(gate_s, np.float32)), _p(_c(up_q, np.uint8)),
-                         _p(_c(up_s, np.float32)), _p(_c(down_q, np.uint8)), _p(_c(down_s, np.float32)),
-                         H, I, _p(_c(xq, np.int8)), _p(_c(xs, np.float32)), _p(o.y), _p(o.g), _p(o.u),
-                         _p(o.h), _p(o.hq), _p(o.hs))
+    _lib().oracle_expert_w(wb, _p(gate_q), _p(_c(gate_s, np.float32)), _p(_c(up_q, dt)),
+                           _p(_c(up_s, np.float32)), _p(_c(down_q, dt)), _p(_c(down_s, np.float32)),
+                           H, I, _p(_c(xq, np.int8)), _p(_c(xs, np.float32)), _p(o.y), _p(o.g), _p(o.u),
+                           _p(o.h), _p(o.hq), _p(o.hs))
     return o
 
 
 def expert_dense(gate_q, gate_s, up_q, up_s, down_q, down_s, x) -> np.ndarray:
-    gate_q = _c(gate_q, np.uint8)
-    I, Hh = gate_q.shape
-    H = 2 * Hh
+    """O10 / O14: dequantised weights, unquantised x and h, in double."""
+    wb = _wbits(gate_q)
+    dt = np.int8 if wb == 8 else np.uint8
+    gate_q = _c(gate_q, dt)
+    I, Hc = gate_q.shape
+    H = Hc if wb == 8 else 2 * Hc
     y = np.empty(H, np.float64)
-    _lib().oracle_expert_dense(_p(gate_q), _p(_c(gate_s, np.float32)), _p(_c(up_q, np.uint8)),
-                               _p(_c(up_s, np.float32)), _p(_c(down_q, np.uint8)),
-                               _p(_c(down_s, np.float32)), H, I, _p(_c(x, np.float32)), _p(y))
+    fn = _lib().oracle_expert_dense_i8 if wb == 8 else _lib().oracle_expert_dense
+    fn(_p(gate_q), _p(_c(gate_s, np.float32)), _p(_c(up_q, dt)), _p(_c(up_s, np.float32)),
+       _p(_c(down_q, dt)), _p(_c(down_s, np.float32)), H, I, _p(_c(x, np.float32)), _p(y))
     return y
 
 
@@ -183,22 +228,27 @@ class _CLayer(ctypes.Structure):
         ("route_scale", ctypes.c_float),
         ("router_w", ctypes.c_void_p), ("router_b", ctypes.c_void_p),
         ("gate_q", ctypes.c_void_p), ("up_q", ctypes.c_void_p), ("down_q", ctypes.c_void_p),
-        ("gate_s", ctypes.c_void_p), ("up_s", ctypes.c_void_p), ("down_s", ctypes.c_void_p)]
+        ("gate_s", ctypes.c_void_p), ("up_s", ctypes.c_void_p), ("down_s", ctypes.c_void_p),
+        ("weight_bits", ctypes.c_int)]
 
 
 def moe_forward(layer, x):
-    """layer: object with H, I, E, top_k, n_group, topk_group, has_shared, route_scale and
-    numpy arrays router_w [E][H], router_b [E], gate_q/up_q [E+s][I][H/2], down_q [E+s][H][I/2],
-    gate_s/up_s [E+s][I], down_s [E+s][H]. Returns y [T][H], idx [T][k], w [T][k]."""
+    """layer: object with H, I, E, top_k, n_group, topk_group, has_shared, route_scale,
+    weight_bits (4 if absent) and numpy arrays router_w [E][H], router_b [E],
+    gate_q/up_q [E+s][I][H/2] uint8, down_q [E+s][H][I/2] uint8 (int4) or
+    gate_q/up_q [E+s][I][H], down_q [E+s][H][I] int8 (int8), gate_s/up_s [E+s][I],
+    down_s [E+s][H]. Returns y [T][H], idx [T][k], w [T][k]."""
     x = _c(np.atleast_2d(x), np.float32)
     T = x.shape[0]
+    wb = getattr(layer, "weight_bits", 4)
+    qt = np.int8 if wb == 8 else np.uint8
     arrs = {n: _c(getattr(layer, n), dt) for n, dt in (
-        ("router_w", np.float32), ("router_b", np.float32), ("gate_q", np.uint8), ("up_q", np.uint8),
-        ("down_q", np.uint8), ("gate_s", np.float32), ("up_s", np.float32), ("down_s", np.float32))}
+        ("router_w", np.float32), ("router_b", np.float32), ("gate_q", qt), ("up_q", qt),
+        ("down_q", qt), ("gate_s", np.float32), ("up_s", np.float32), ("down_s", np.float32))}
     cl = _CLayer(layer.H, layer.I, layer.E, layer.top_k, layer.n_group, layer.topk_group,
                  layer.has_shared, layer.route_scale,
                  *[arrs[n].ctypes.data for n in ("router_w", "router_b", "gate_q", "up_q", "down_q",
-                                                 "gate_s", "up_s", "down_s")])
+                                                 "gate_s", "up_s", "down_s")], wb)
     y = np.empty((T, layer.H), np.float32)
     idx = np.empty((T, layer.top_k), np.int32)
     w = np.empty((T, layer.top_k), np.float32)

@@ -148,6 +148,7 @@ class LayerSpec:
     bias_sigma: float = 0.01         # router bias ~ N(0, bias_sigma)
     zipf_s: float = 0.0              # > 0: bias -= zipf_alpha * zipf_s * ln(rank)
     zipf_alpha: float = 0.02
+    weight_bits: int = 4             # packed expert format: 4 (two codes per byte) or 8
 
     @property
     def router_sigma(self) -> float:
@@ -159,8 +160,9 @@ class LayerSpec:
 
     @property
     def expert_bytes(self) -> int:
-        """Packed int4 bytes + f32 row scales of one expert (gate, up, down)."""
-        return 3 * self.H * self.I // 2 + 4 * (2 * self.I + self.H)
+        """Packed bytes (int4: two codes per byte; int8: one) + f32 row scales of one
+        expert (gate, up, down)."""
+        return 3 * self.H * self.I * self.weight_bits // 8 + 4 * (2 * self.I + self.H)
 
 
 @dataclass(frozen=True)
