@@ -18,8 +18,8 @@ COLI_GEMV_MAX_T, COLI_MAX_T, COLI_MAX_TOPK, COLI_PROFILE_EVENTS = 8, 65536, 16, 
 
 EXPORTS = ("coli_quant_act_q8", "coli_moe_workspace_bytes", "coli_moe_workspace_init",
            "coli_moe_route", "coli_moe_forward", "coli_moe_forward_profiled", "coli_moe_experts", "coli_moe_workspace_layout",
-           "coli_rmsnorm", "coli_pack_int4_rows", "coli_pack_int4_rows_dev", "coli_debug_block_dots",
-           "coli_version")
+           "coli_rmsnorm", "coli_pack_int4_rows", "coli_pack_int4_rows_dev", "coli_pack_int8_rows",
+           "coli_pack_int8_rows_dev", "coli_debug_block_dots", "coli_version")
 
 
 class ColiError(RuntimeError):
@@ -37,7 +37,8 @@ class CLayer(ctypes.Structure):
                 ("has_shared", ctypes.c_int32), ("route_scale", ctypes.c_float),
                 ("router_w", ctypes.c_void_p), ("router_b", ctypes.c_void_p),
                 ("gate_q", ctypes.c_void_p), ("up_q", ctypes.c_void_p), ("down_q", ctypes.c_void_p),
-                ("gate_s", ctypes.c_void_p), ("up_s", ctypes.c_void_p), ("down_s", ctypes.c_void_p)]
+                ("gate_s", ctypes.c_void_p), ("up_s", ctypes.c_void_p), ("down_s", ctypes.c_void_p),
+                ("weight_bits", ctypes.c_int32)]
 
 
 class CWsLayout(ctypes.Structure):
@@ -70,6 +71,8 @@ def lib():
             "coli_rmsnorm": ([P, P, i, i, f, P, P], i),
             "coli_pack_int4_rows": ([P, i, i, P, P], i),
             "coli_pack_int4_rows_dev": ([P, i, i, P, P, P], i),
+            "coli_pack_int8_rows": ([P, i, i, P, P], i),
+            "coli_pack_int8_rows_dev": ([P, i, i, P, P, P], i),
             "coli_debug_block_dots": ([P, P, i, i, P, P], i),
             "coli_version": ([], ctypes.c_char_p),
         }

@@ -45,34 +45,37 @@ class MoELayer:
     route_scale: float
     router_w: torch.Tensor   # [E][H] f32
     router_b: torch.Tensor   # [E] f32
-    gate_q: torch.Tensor     # [E+s][I][H/2] u8
+    gate_q: torch.Tensor     # [E+s][I][H/2] u8 (int4) or [E+s][I][H] i8 (int8)
     up_q: torch.Tensor
-    down_q: torch.Tensor     # [E+s][H][I/2] u8
+    down_q: torch.Tensor     # [E+s][H][I/2] u8 (int4) or [E+s][H][I] i8 (int8)
     gate_s: torch.Tensor     # [E+s][I] f32
     up_s: torch.Tensor
     down_s: torch.Tensor     # [E+s][H] f32
+    weight_bits: int = 4
 
     @classmethod
-    def empty(cls, H, I, E, top_k, has_shared=1, n_group=1, topk_group=1, route_scale=1.0, device="cuda"):
+    def empty(cls, H, I, E, top_k, has_shared=1, n_group=1, topk_group=1, route_scale=1.0, device="cuda",
+              weight_bits=4):
         n = E + has_shared
-        u8, f32 = torch.uint8, torch.float32
+        f32 = torch.float32
+        qt, div = (torch.int8, 1) if weight_bits == 8 else (torch.uint8, 2)
         return cls(H, I, E, top_k, has_shared, n_group, topk_group, route_scale,
                    torch.empty((E, H), dtype=f32, device=device), torch.empty(E, dtype=f32, device=device),
-                   torch.empty((n, I, H // 2), dtype=u8, device=device),
-                   torch.empty((n, I, H // 2), dtype=u8, device=device),
-                   torch.empty((n, H, I // 2), dtype=u8, device=device),
+                   torch.empty((n, I, H // div), dtype=qt, device=device),
+                   torch.empty((n, I, H // div), dtype=qt, device=device),
+                   torch.empty((n, H, I // div), dtype=qt, device=device),
                    torch.empty((n, I), dtype=f32, device=device), torch.empty((n, I), dtype=f32, device=device),
-                   torch.empty((n, H), dtype=f32, device=device))
+                   torch.empty((n, H), dtype=f32, device=device), weight_bits)
 
     def c(self) -> CLayer:
         return CLayer(self.H, self.I, self.E, self.top_k, self.n_group, self.topk_group, self.has_shared,
                       self.route_scale, *(t.data_ptr() for t in (
                           self.router_w, self.router_b, self.gate_q, self.up_q, self.down_q,
-                          self.gate_s, self.up_s, self.down_s)))
+                          self.gate_s, self.up_s, self.down_s)), self.weight_bits)
 
     @property
     def expert_bytes(self) -> int:
-        return 3 * self.H * self.I // 2 + 4 * (2 * self.I + self.H)
+        return 3 * self.H * self.I * self.weight_bits // 8 + 4 * (2 * self.I + self.H)
 
 
 def version() -> str:
@@ -171,6 +174,25 @@ def pack_int4_rows_dev(w: torch.Tensor, q: torch.Tensor, s: torch.Tensor, stream
     _dev(w, torch.float32, "w")
     rows, cols = w.shape
     check("coli_pack_int4_rows_dev", lib().coli_pack_int4_rows_dev(_ptr(w), rows, cols, _ptr(q), _ptr(s),
+                                                                   _stream(stream)))
+
+
+def pack_int8_rows(w: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+    """Host int8 packer (synchronous, host memory); the library's int8 layout."""
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    rows, cols = w.shape
+    q = np.empty((rows, cols), dtype=np.int8)
+    s = np.empty(rows, dtype=np.float32)
+    check("coli_pack_int8_rows", lib().coli_pack_int8_rows(ctypes.c_void_p(w.ctypes.data), rows, cols,
+                                                           ctypes.c_void_p(q.ctypes.data),
+                                                           ctypes.c_void_p(s.ctypes.data)))
+    return q, s
+
+
+def pack_int8_rows_dev(w: torch.Tensor, q: torch.Tensor, s: torch.Tensor, stream=None) -> None:
+    _dev(w, torch.float32, "w")
+    rows, cols = w.shape
+    check("coli_pack_int8_rows_dev", lib().coli_pack_int8_rows_dev(_ptr(w), rows, cols, _ptr(q), _ptr(s),
                                                                    _stream(stream)))
 
 

@@ -28,6 +28,7 @@ bool layer_ok(const coli_moe_layer *L)
     if (L->n_group > 1 && L->top_k > L->topk_group * (L->E / L->n_group)) return false;
     if (L->has_shared != 0 && L->has_shared != 1) return false;
     if (!std::isfinite(L->route_scale)) return false;
+    if (L->weight_bits != 0 && L->weight_bits != 4 && L->weight_bits != 8) return false;
     if (!al4(L->router_w) || !al4(L->router_b)) return false;
     if (!al16(L->gate_q) || !al16(L->up_q) || !al16(L->down_q)) return false;
     if (!al4(L->gate_s) || !al4(L->up_s) || !al4(L->down_s)) return false;
@@ -46,6 +47,13 @@ int choose_path(const coli_moe_layer &L, int T, int flags)
 }
 
 int status(hipError_t e) { return e == hipSuccess ? COLI_OK : COLI_EDEVICE; }
+
+// int8 experts run on the token-GEMV path only (not grouped, not fused).
+int format_ok(const coli_moe_layer &L, int path, int flags)
+{
+    if (L.weight_bits == 8 && (path != 0 || (flags & COLI_PATH_FUSED))) return COLI_EUNSUPPORTED;
+    return COLI_OK;
+}
 
 } // namespace
 
@@ -187,6 +195,7 @@ static int forward_impl(const coli_moe_layer *L, const float *x, int T, float *y
     WsLayout lay;
     int rc = check_common(L, T, flags, ws, ws_bytes, path, lay);
     if (rc != COLI_OK) return rc;
+    if ((rc = format_ok(*L, path, flags)) != COLI_OK) return rc;
     if (!al16(x) || !al16(y)) return COLI_EINVAL;
     hipStream_t s = (hipStream_t)stream;
     char *base = static_cast<char *>(ws);
@@ -267,6 +276,7 @@ int coli_moe_experts(const coli_moe_layer *L, const int8_t *xq, const float *xs,
     WsLayout lay;
     int rc = check_common(L, T, flags, ws, ws_bytes, path, lay);
     if (rc != COLI_OK) return rc;
+    if ((rc = format_ok(*L, path, flags)) != COLI_OK) return rc;
     if (!al16(xq) || !al4(xs) || !al4(idx) || !al4(w) || !al16(y)) return COLI_EINVAL;
     hipStream_t s = (hipStream_t)stream;
     char *base = static_cast<char *>(ws);
@@ -314,6 +324,34 @@ int coli_pack_int4_rows_dev(const float *w, int rows, int cols, uint8_t *q, floa
 {
     if (!al4(w) || !q || !al4(s) || rows < 1 || cols < 2 || (cols & 1)) return COLI_EINVAL;
     return status(launch_pack_int4(w, rows, cols, q, s, (hipStream_t)stream));
+}
+
+int coli_pack_int8_rows(const float *w, int rows, int cols, int8_t *q, float *s)
+{
+    if (!w || !q || !s || rows < 1 || cols < 8 || (cols % 8)) return COLI_EINVAL;
+    for (int r = 0; r < rows; ++r) {
+        const float *src = w + (size_t)r * cols;
+        float amax = 0.0f;
+        for (int c = 0; c < cols; ++c) amax = std::fmax(amax, std::fabs(src[c]));
+        const float d = amax / 127.0f;
+        const float id = (d != 0.0f) ? 1.0f / d : 0.0f;
+        s[r] = d;
+        int8_t *dst = q + (size_t)r * cols;
+        for (int c = 0; c < cols; ++c) {
+            const float v = src[c] * id;
+            float rv = std::isnan(v) ? 0.0f : std::rint(v);
+            rv = rv < -127.0f ? -127.0f : (rv > 127.0f ? 127.0f : rv);
+            const int j = c & 7;                 // byte of column j in its group of 8
+            dst[(c & ~7) + ((j & 1) ? 4 + (j >> 1) : (j >> 1))] = (int8_t)rv;
+        }
+    }
+    return COLI_OK;
+}
+
+int coli_pack_int8_rows_dev(const float *w, int rows, int cols, int8_t *q, float *s, void *stream)
+{
+    if (!al4(w) || !al16(q) || !al4(s) || rows < 1 || cols < 32 || cols % 32) return COLI_EINVAL;
+    return status(launch_pack_int8(w, rows, cols, q, s, (hipStream_t)stream));
 }
 
 int coli_debug_block_dots(const uint8_t *q4, const int8_t *q8, int rows, int cols, int32_t *S, void *stream)

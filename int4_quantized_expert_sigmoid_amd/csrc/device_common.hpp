@@ -49,6 +49,43 @@ __device__ __forceinline__ int dot_block16(const int (&lo)[4], const int (&hi)[4
     return s;
 }
 
+// int8 weight block (32 codes in the activations' reordered byte order, as
+// the int8 packer stores them) against a reordered activation block: 16·S_b
+// is not needed here, the dot is S_b itself.
+__device__ __forceinline__ int dot_block_i8(const uint4 w0, const uint4 w1, const Blk8 &a)
+{
+    int s = 0;
+    s = __builtin_amdgcn_sdot4((int)w0.x, a.v[0], s, false);
+    s = __builtin_amdgcn_sdot4((int)w0.y, a.v[1], s, false);
+    s = __builtin_amdgcn_sdot4((int)w0.z, a.v[2], s, false);
+    s = __builtin_amdgcn_sdot4((int)w0.w, a.v[3], s, false);
+    s = __builtin_amdgcn_sdot4((int)w1.x, a.v[4], s, false);
+    s = __builtin_amdgcn_sdot4((int)w1.y, a.v[5], s, false);
+    s = __builtin_amdgcn_sdot4((int)w1.z, a.v[6], s, false);
+    s = __builtin_amdgcn_sdot4((int)w1.w, a.v[7], s, false);
+    return s;
+}
+
+// Weight formats of the token-GEMV path: bytes of one row's 32-wide block and
+// the factor that turns a block dot into S_b (int4 dots come out x16).
+template <int WB> struct WFmt;
+template <> struct WFmt<4> { static constexpr int BLK_BYTES = 16; static constexpr double KSCALE = 0.0625; };
+template <> struct WFmt<8> { static constexpr int BLK_BYTES = 32; static constexpr double KSCALE = 1.0; };
+
+// One block of one weight row times one activation block: S_b scaled by the
+// format's factor applies later; w holds BLK_BYTES/16 16-byte pieces.
+template <int WB>
+__device__ __forceinline__ int dot_block_w(const uint4 (&w)[WFmt<WB>::BLK_BYTES / 16], const Blk8 &a)
+{
+    if constexpr (WB == 8) {
+        return dot_block_i8(w[0], w[1], a);
+    } else {
+        int lo[4], hi[4];
+        unpack_nibbles(w[0], lo, hi);
+        return dot_block16(lo, hi, a);
+    }
+}
+
 __device__ __forceinline__ Blk8 load_blk8(const int8_t *p)
 {
     const int4 a = *reinterpret_cast<const int4 *>(p);

@@ -98,9 +98,11 @@ struct GateUpShared {
 // waves, each streaming 32/RS rows, so fewer loads queue behind each other.
 // ONFLY: Q8(x) is computed here from x instead of read from xq. COHERENT
 // (single-launch path): hq/hs are handed on with device-coherent stores.
-template <int NT, int RC, bool ONFLY, bool COHERENT, int RS = 1>
+template <int NT, int RC, bool ONFLY, bool COHERENT, int RS = 1, int WB = 4>
 __device__ __forceinline__ void gateup_rows(const GemvArgs &a, const ItemDesc &it, int rb, GateUpShared<NT> &sh)
 {
+    constexpr int NP = WFmt<WB>::BLK_BYTES / 16;     // 16-byte pieces per row block
+    constexpr double KS = WFmt<WB>::KSCALE;
     constexpr int NV = 2 * RC;                   // values per chunk: RC rows x (gate, up)
     constexpr int RPS = QK / RS;                 // rows per set
     constexpr int NC = RPS / RC;                 // chunks per set
@@ -109,7 +111,7 @@ __device__ __forceinline__ void gateup_rows(const GemvArgs &a, const ItemDesc &i
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int nblk = a.H / QK;
     const int nw = (nblk + 63) >> 6;             // waves that own block columns
-    const long rowb = (long)(a.H / 2);
+    const long rowb = (long)a.H * WB / 8;
     const long row0 = (long)it.e * a.I + (long)rb * QK;
     const int set = wave / nw, wv = wave - set * nw;
     const int col = wv * 64 + lane;              // this thread's block column
@@ -128,10 +130,10 @@ __device__ __forceinline__ void gateup_rows(const GemvArgs &a, const ItemDesc &i
                     q8_block_regs(a.x + (long)t * a.H + col * QK, o, d);
 #pragma unroll
                     for (int k = 0; k < 8; ++k) act[s].v[k] = (int)o[k];
-                    dsc[s] = (double)d * 0.0625;
+                    dsc[s] = (double)d * KS;
                 } else {
                     act[s] = load_blk8(a.xq + (long)t * a.H + col * QK);
-                    dsc[s] = (double)a.xs[(long)t * nblk + col] * 0.0625;
+                    dsc[s] = (double)a.xs[(long)t * nblk + col] * KS;
                 }
             } else {
 #pragma unroll
@@ -141,35 +143,36 @@ __device__ __forceinline__ void gateup_rows(const GemvArgs &a, const ItemDesc &i
         }
         // threads past the row's last block read block 0 and multiply it by zero
         const int tb = active ? col : 0;
-        const uint8_t *pg = a.q_a + (row0 + set * RPS) * rowb + tb * 16;
-        const uint8_t *pu = a.q_b + (row0 + set * RPS) * rowb + tb * 16;
+        const uint8_t *pg = a.q_a + (row0 + set * RPS) * rowb + tb * WFmt<WB>::BLK_BYTES;
+        const uint8_t *pu = a.q_b + (row0 + set * RPS) * rowb + tb * WFmt<WB>::BLK_BYTES;
 
-        uint4 wg[2][RC], wu[2][RC];
+        uint4 wg[2][RC][NP], wu[2][RC][NP];
 #pragma unroll
-        for (int r = 0; r < RC; ++r) {
-            wg[0][r] = load_u4_stream(pg + (long)r * rowb);
-            wu[0][r] = load_u4_stream(pu + (long)r * rowb);
-        }
+        for (int r = 0; r < RC; ++r)
+#pragma unroll
+            for (int q = 0; q < NP; ++q) {
+                wg[0][r][q] = load_u4_stream(pg + (long)r * rowb + 16 * q);
+                wu[0][r][q] = load_u4_stream(pu + (long)r * rowb + 16 * q);
+            }
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
             const int cur = c & 1;
             if (c + 1 < NC) {
 #pragma unroll
-                for (int r = 0; r < RC; ++r) {
-                    wg[cur ^ 1][r] = load_u4_stream(pg + (long)((c + 1) * RC + r) * rowb);
-                    wu[cur ^ 1][r] = load_u4_stream(pu + (long)((c + 1) * RC + r) * rowb);
-                }
+                for (int r = 0; r < RC; ++r)
+#pragma unroll
+                    for (int q = 0; q < NP; ++q) {
+                        wg[cur ^ 1][r][q] = load_u4_stream(pg + (long)((c + 1) * RC + r) * rowb + 16 * q);
+                        wu[cur ^ 1][r][q] = load_u4_stream(pu + (long)((c + 1) * RC + r) * rowb + 16 * q);
+                    }
             }
             double v[NT][NV];
 #pragma unroll
             for (int r = 0; r < RC; ++r) {
-                int lo[4], hi[4];
-                unpack_nibbles(wg[cur][r], lo, hi);
 #pragma unroll
-                for (int s = 0; s < NT; ++s) v[s][2 * r] = (double)dot_block16(lo, hi, act[s]) * dsc[s];
-                unpack_nibbles(wu[cur][r], lo, hi);
+                for (int s = 0; s < NT; ++s) v[s][2 * r] = (double)dot_block_w<WB>(wg[cur][r], act[s]) * dsc[s];
 #pragma unroll
-                for (int s = 0; s < NT; ++s) v[s][2 * r + 1] = (double)dot_block16(lo, hi, act[s]) * dsc[s];
+                for (int s = 0; s < NT; ++s) v[s][2 * r + 1] = (double)dot_block_w<WB>(wu[cur][r], act[s]) * dsc[s];
             }
             const int vi = transpose_index<NV>(lane);
 #pragma unroll
@@ -217,20 +220,24 @@ __device__ __forceinline__ void gateup_rows(const GemvArgs &a, const ItemDesc &i
 // lane l owns block column l; chunks of RD rows with the next chunk's loads in
 // flight); writes ye of pairs item*8 + slot. blockDim = 256. COHERENT: hq/hs
 // are read and ye is written with device-coherent accesses.
-template <int NT, int RD, bool COHERENT, int RPW>
+template <int NT, int RD, bool COHERENT, int RPW, int WB = 4>
 __device__ __forceinline__ void down_rows(const GemvArgs &a, const ItemDesc &it, int grp)
 {
+    constexpr int NP = WFmt<WB>::BLK_BYTES / 16;
+    constexpr double KS = WFmt<WB>::KSCALE;
     constexpr int NC = RPW / RD;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int nblk = a.I / QK;
     const bool active = lane < nblk;
-    const long rowb = (long)(a.I / 2);
+    const long rowb = (long)a.I * WB / 8;
     const long row0 = (long)grp * (4 * RPW) + wave * RPW;
-    const uint8_t *pd = a.q_a + ((long)it.e * a.H + row0) * rowb + (active ? lane : 0) * 16;
+    const uint8_t *pd = a.q_a + ((long)it.e * a.H + row0) * rowb + (active ? lane : 0) * WFmt<WB>::BLK_BYTES;
 
-    uint4 wd[2][RD];
+    uint4 wd[2][RD][NP];
 #pragma unroll
-    for (int r = 0; r < RD; ++r) wd[0][r] = load_u4_stream(pd + (long)r * rowb);
+    for (int r = 0; r < RD; ++r)
+#pragma unroll
+        for (int q = 0; q < NP; ++q) wd[0][r][q] = load_u4_stream(pd + (long)r * rowb + 16 * q);
 
     Blk8 act[NT];
     double dsc[NT];
@@ -242,10 +249,10 @@ __device__ __forceinline__ void down_rows(const GemvArgs &a, const ItemDesc &it,
                 const int *src = reinterpret_cast<const int *>(a.hq + pair * a.I + lane * QK);
 #pragma unroll
                 for (int k = 0; k < 8; ++k) act[s].v[k] = ld_dev(src + k);
-                dsc[s] = (double)ld_dev(a.hs + pair * nblk + lane) * 0.0625;
+                dsc[s] = (double)ld_dev(a.hs + pair * nblk + lane) * KS;
             } else {
                 act[s] = load_blk8(a.hq + pair * a.I + lane * QK);
-                dsc[s] = (double)a.hs[pair * nblk + lane] * 0.0625;
+                dsc[s] = (double)a.hs[pair * nblk + lane] * KS;
             }
         } else {
 #pragma unroll
@@ -258,15 +265,16 @@ __device__ __forceinline__ void down_rows(const GemvArgs &a, const ItemDesc &it,
         const int cur = c & 1;
         if (c + 1 < NC) {
 #pragma unroll
-            for (int r = 0; r < RD; ++r) wd[cur ^ 1][r] = load_u4_stream(pd + (long)((c + 1) * RD + r) * rowb);
+            for (int r = 0; r < RD; ++r)
+#pragma unroll
+                for (int q = 0; q < NP; ++q)
+                    wd[cur ^ 1][r][q] = load_u4_stream(pd + (long)((c + 1) * RD + r) * rowb + 16 * q);
         }
         double v[NT][RD];
 #pragma unroll
         for (int r = 0; r < RD; ++r) {
-            int lo[4], hi[4];
-            unpack_nibbles(wd[cur][r], lo, hi);
 #pragma unroll
-            for (int s = 0; s < NT; ++s) v[s][r] = (double)dot_block16(lo, hi, act[s]) * dsc[s];
+            for (int s = 0; s < NT; ++s) v[s][r] = (double)dot_block_w<WB>(wd[cur][r], act[s]) * dsc[s];
         }
         const int vi = transpose_index<RD>(lane);
 #pragma unroll
@@ -289,5 +297,12 @@ template <> struct GemvTune<1> { static constexpr int RC = 4, RD = 8; };
 template <> struct GemvTune<2> { static constexpr int RC = 4, RD = 8; };
 template <> struct GemvTune<4> { static constexpr int RC = 2, RD = 4; };
 template <> struct GemvTune<8> { static constexpr int RC = 2, RD = 2; };
+
+// The same per weight format: an int8 row block is twice the bytes, so a
+// chunk holds half the rows (at least one).
+template <int NT, int WB> struct GemvTuneW {
+    static constexpr int RC = WB == 8 ? (GemvTune<NT>::RC > 1 ? GemvTune<NT>::RC / 2 : 1) : GemvTune<NT>::RC;
+    static constexpr int RD = WB == 8 ? (GemvTune<NT>::RD > 1 ? GemvTune<NT>::RD / 2 : 1) : GemvTune<NT>::RD;
+};
 
 } // namespace coli

@@ -47,6 +47,7 @@ enum CtrlWord { CTRL_N_ITEMS = 0, CTRL_N_TILES_GU = 1, CTRL_N_TILES_DN = 2, CTRL
 hipError_t launch_quant_q8(const float *x, int T, int H, int8_t *xq, float *xs, bool reorder, hipStream_t s);
 hipError_t launch_reorder_q8(const int8_t *xq_nat, int n, int8_t *xq_perm, hipStream_t s);
 hipError_t launch_pack_int4(const float *w, int rows, int cols, uint8_t *q, float *sc, hipStream_t s);
+hipError_t launch_pack_int8(const float *w, int rows, int cols, int8_t *q, float *sc, hipStream_t s);
 hipError_t launch_rmsnorm(const float *x, const float *g, int T, int H, float eps, float *out, hipStream_t s);
 hipError_t launch_block_dots(const uint8_t *q4, const int8_t *q8, int rows, int cols, int32_t *S, hipStream_t s);
 hipError_t launch_zero(void *p, size_t bytes, hipStream_t s);

@@ -101,14 +101,14 @@ struct SelGuShared {
     DecUnion u;
 };
 
-template <int NT, int KPL>
+template <int NT, int KPL, int WB>
 __global__ void __launch_bounds__(256) k_select_gateup(SelGuArgs a, GemvArgs g, int n_shared_wg)
 {
     __shared__ GateUpShared<NT> sh;
     __shared__ SelGuShared su;
     TRACE(a, 1, 0);
     if ((int)blockIdx.x < n_shared_wg) {         // the shared expert: no routing needed
-        gateup_rows<NT, GemvTune<NT>::RC, false, false>(g, shared_item(g), blockIdx.x, sh);
+        gateup_rows<NT, GemvTuneW<NT, WB>::RC, false, false, 1, WB>(g, shared_item(g), blockIdx.x, sh);
         TRACE(a, 1, 2);
         return;
     }
@@ -147,13 +147,13 @@ __global__ void __launch_bounds__(256) k_select_gateup(SelGuArgs a, GemvArgs g, 
     it.nt = u.item_nt[item];
 #pragma unroll
     for (int s = 0; s < MAX_SLOTS; ++s) it.tok[s] = s < it.nt ? u.item_tok[item * MAX_SLOTS + s] : 0;
-    gateup_rows<NT, GemvTune<NT>::RC, false, false>(g, it, rb, sh);
+    gateup_rows<NT, GemvTuneW<NT, WB>::RC, false, false, 1, WB>(g, it, rb, sh);
     TRACE(a, 1, 2);
 }
 
 // ------------------------------------------------------------ launch 3
 struct DnArgs {
-    const uint8_t *q;          // down_q [E+shared][H][I/2]
+    const uint8_t *q;          // down_q [E+shared][H][I/2] (int4) or [E+shared][H][I] (int8)
     const float *s;            // down_s [E+shared][H]
     int H, I, T, top_k, has_shared;
     const int *ctrl, *item_expert, *item_ntok;
@@ -172,32 +172,35 @@ struct DnArgs {
 // One item's slice: the workgroup's RPU rows of the item's down matrix (lane
 // l holds block column l of each row) and the activations of up to NT token
 // slots.
-template <int NT, int RPU>
+template <int NT, int RPU, int WB>
 struct DnStage {
-    uint4 wd[RPU];
+    uint4 wd[RPU][WFmt<WB>::BLK_BYTES / 16];
     Blk8 act[NT];
     double dsc[NT];
     int e, nt;
 };
 
-template <int NT, int RPU>
+template <int NT, int RPU, int WB>
 __device__ __forceinline__ void dn_load(const DnArgs &a, int item, long row0, int lane, const int *it_e,
-                                        const int *it_nt, DnStage<NT, RPU> &st)
+                                        const int *it_nt, DnStage<NT, RPU, WB> &st)
 {
+    constexpr int NP = WFmt<WB>::BLK_BYTES / 16;
     const int nblk = a.I / QK;
     const bool active = lane < nblk;
-    const long rowb = (long)(a.I / 2);
+    const long rowb = (long)a.I * WB / 8;
     st.e = it_e[item];
     st.nt = it_nt[item];
-    const uint8_t *pd = a.q + ((long)st.e * a.H + row0) * rowb + (active ? lane : 0) * 16;
+    const uint8_t *pd = a.q + ((long)st.e * a.H + row0) * rowb + (active ? lane : 0) * WFmt<WB>::BLK_BYTES;
 #pragma unroll
-    for (int r = 0; r < RPU; ++r) st.wd[r] = load_u4_stream(pd + (long)r * rowb);
+    for (int r = 0; r < RPU; ++r)
+#pragma unroll
+        for (int q = 0; q < NP; ++q) st.wd[r][q] = load_u4_stream(pd + (long)r * rowb + 16 * q);
 #pragma unroll
     for (int s = 0; s < NT; ++s) {
         if (s < st.nt && active) {
             const long pair = (long)item * MAX_SLOTS + s;
             st.act[s] = load_blk8(a.hq + pair * a.I + lane * QK);
-            st.dsc[s] = (double)a.hs[pair * nblk + lane] * 0.0625;
+            st.dsc[s] = (double)a.hs[pair * nblk + lane] * WFmt<WB>::KSCALE;
         } else {
 #pragma unroll
             for (int k = 0; k < 8; ++k) st.act[s].v[k] = 0;
@@ -206,17 +209,15 @@ __device__ __forceinline__ void dn_load(const DnArgs &a, int item, long row0, in
     }
 }
 
-template <int NT, int RPU>
+template <int NT, int RPU, int WB>
 __device__ __forceinline__ void dn_compute(const DnArgs &a, int item, long row0, int lane,
-                                           const DnStage<NT, RPU> &st, float *ye_l)
+                                           const DnStage<NT, RPU, WB> &st, float *ye_l)
 {
     double v[NT][RPU];
 #pragma unroll
     for (int r = 0; r < RPU; ++r) {
-        int lo[4], hi[4];
-        unpack_nibbles(st.wd[r], lo, hi);
 #pragma unroll
-        for (int s = 0; s < NT; ++s) v[s][r] = (double)dot_block16(lo, hi, st.act[s]) * st.dsc[s];
+        for (int s = 0; s < NT; ++s) v[s][r] = (double)dot_block_w<WB>(st.wd[r], st.act[s]) * st.dsc[s];
     }
     const int vi = transpose_index<RPU>(lane);
 #pragma unroll
@@ -236,7 +237,7 @@ __device__ __forceinline__ void dn_compute(const DnArgs &a, int item, long row0,
 // the union round-robin (wave w: items w, w + 4, ...), each item's RPU rows
 // at once with the wave's next item already loading; then the per-pair row
 // values in LDS are combined into y.
-template <int NT, int RPU>
+template <int NT, int RPU, int WB>
 __global__ void __launch_bounds__(256) k_down_combine(DnArgs a)
 {
     extern __shared__ float ye_l[];              // [max pairs][RPU]
@@ -252,7 +253,7 @@ __global__ void __launch_bounds__(256) k_down_combine(DnArgs a)
     }
     __syncthreads();
 
-    DnStage<NT, RPU> A, B;
+    DnStage<NT, RPU, WB> A, B;
     int i = wave;
     if (i < n_items) dn_load(a, i, row0, lane, it_e, it_nt, A);
     for (; i < n_items; i += 2 * nwave) {
@@ -299,21 +300,29 @@ GemvArgs gemv_view(const coli_moe_layer &L, int T, const WsLayout &lay, char *ws
 }
 
 // keys per lane of the selection: E <= 64 * KPL
-template <int NT>
+template <int NT, int WB>
 hipError_t launch_sel_nt(int E, dim3 grid, const SelGuArgs &a, const GemvArgs &g, int nsh, hipStream_t s)
 {
-    if (E <= 64) hipLaunchKernelGGL((k_select_gateup<NT, 1>), grid, dim3(256), 0, s, a, g, nsh);
-    else if (E <= 128) hipLaunchKernelGGL((k_select_gateup<NT, 2>), grid, dim3(256), 0, s, a, g, nsh);
-    else if (E <= 256) hipLaunchKernelGGL((k_select_gateup<NT, 4>), grid, dim3(256), 0, s, a, g, nsh);
-    else hipLaunchKernelGGL((k_select_gateup<NT, 8>), grid, dim3(256), 0, s, a, g, nsh);
+    if (E <= 64) hipLaunchKernelGGL((k_select_gateup<NT, 1, WB>), grid, dim3(256), 0, s, a, g, nsh);
+    else if (E <= 128) hipLaunchKernelGGL((k_select_gateup<NT, 2, WB>), grid, dim3(256), 0, s, a, g, nsh);
+    else if (E <= 256) hipLaunchKernelGGL((k_select_gateup<NT, 4, WB>), grid, dim3(256), 0, s, a, g, nsh);
+    else hipLaunchKernelGGL((k_select_gateup<NT, 8, WB>), grid, dim3(256), 0, s, a, g, nsh);
     return hipGetLastError();
 }
 
-template <int NT, int RPU>
+template <int NT>
+hipError_t launch_sel_wb(const coli_moe_layer &L, dim3 grid, const SelGuArgs &a, const GemvArgs &g, int nsh,
+                         hipStream_t s)
+{
+    return L.weight_bits == 8 ? launch_sel_nt<NT, 8>(L.E, grid, a, g, nsh, s)
+                              : launch_sel_nt<NT, 4>(L.E, grid, a, g, nsh, s);
+}
+
+template <int NT, int RPU, int WB>
 hipError_t launch_dn_nt(const coli_moe_layer &L, const WsLayout &lay, const DnArgs &a, hipStream_t s)
 {
     const size_t lds = (size_t)lay.max_items * MAX_SLOTS * RPU * sizeof(float);
-    hipLaunchKernelGGL((k_down_combine<NT, RPU>), dim3((unsigned)(L.H / RPU)), dim3(256), lds, s, a);
+    hipLaunchKernelGGL((k_down_combine<NT, RPU, WB>), dim3((unsigned)(L.H / RPU)), dim3(256), lds, s, a);
     return hipGetLastError();
 }
 
@@ -362,10 +371,10 @@ hipError_t launch_decode_select_gateup(const coli_moe_layer &L, int T, const WsL
     GemvArgs g = gemv_view(L, T, lay, ws);
     const int nrb = L.I / QK, nsh = L.has_shared ? nrb : 0;
     const dim3 grid((unsigned)(nsh + (lay.max_items - L.has_shared) * nrb));
-    if (T <= 1) return launch_sel_nt<1>(L.E, grid, a, g, nsh, s);
-    if (T <= 2) return launch_sel_nt<2>(L.E, grid, a, g, nsh, s);
-    if (T <= 4) return launch_sel_nt<4>(L.E, grid, a, g, nsh, s);
-    return launch_sel_nt<8>(L.E, grid, a, g, nsh, s);
+    if (T <= 1) return launch_sel_wb<1>(L, grid, a, g, nsh, s);
+    if (T <= 2) return launch_sel_wb<2>(L, grid, a, g, nsh, s);
+    if (T <= 4) return launch_sel_wb<4>(L, grid, a, g, nsh, s);
+    return launch_sel_wb<8>(L, grid, a, g, nsh, s);
 }
 
 hipError_t launch_decode_down_combine(const coli_moe_layer &L, int T, const WsLayout &lay, char *ws, float *y,
@@ -388,8 +397,13 @@ hipError_t launch_decode_down_combine(const coli_moe_layer &L, int T, const WsLa
 #ifdef COLI_TRACE
     a.trace = g_dec_trace;
 #endif
-    if (T <= 1) return launch_dn_nt<1, 8>(L, lay, a, s);
-    return launch_dn_nt<2, 4>(L, lay, a, s);
+    // int8 rows are twice the bytes: half the rows per workgroup
+    if (L.weight_bits == 8) {
+        if (T <= 1) return launch_dn_nt<1, 4, 8>(L, lay, a, s);
+        return launch_dn_nt<2, 2, 8>(L, lay, a, s);
+    }
+    if (T <= 1) return launch_dn_nt<1, 8, 4>(L, lay, a, s);
+    return launch_dn_nt<2, 4, 4>(L, lay, a, s);
 }
 
 } // namespace coli

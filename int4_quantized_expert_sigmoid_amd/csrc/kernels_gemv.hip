@@ -7,7 +7,7 @@
 namespace coli {
 namespace {
 
-template <int NT>
+template <int NT, int WB>
 __global__ void __launch_bounds__(256) k_gateup_gemv(GemvArgs a)
 {
     __shared__ GateUpShared<NT> sh;
@@ -15,17 +15,35 @@ __global__ void __launch_bounds__(256) k_gateup_gemv(GemvArgs a)
     const int item = a.item0 + (int)blockIdx.x / nrb, rb = blockIdx.x % nrb;
     if (item >= a.ctrl[CTRL_N_ITEMS]) return;
     const ItemDesc it = item_from_table(a, item);
-    gateup_rows<NT, GemvTune<NT>::RC, false, false>(a, it, rb, sh);
+    gateup_rows<NT, GemvTuneW<NT, WB>::RC, false, false, 1, WB>(a, it, rb, sh);
 }
 
-template <int NT>
+template <int NT, int WB>
 __global__ void __launch_bounds__(256) k_down_gemv(GemvArgs a)
 {
     const int ngrp = a.H / QK;
     const int item = a.item0 + (int)blockIdx.x / ngrp, grp = blockIdx.x % ngrp;
     if (item >= a.ctrl[CTRL_N_ITEMS]) return;
     const ItemDesc it = item_from_table(a, item);
-    down_rows<NT, GemvTune<NT>::RD, false, 8>(a, it, grp);
+    down_rows<NT, GemvTuneW<NT, WB>::RD, false, 8, WB>(a, it, grp);
+}
+
+template <int WB>
+void launch_gateup_wb(int T, dim3 grid, dim3 block, const GemvArgs &a, hipStream_t s)
+{
+    if (T <= 1) hipLaunchKernelGGL((k_gateup_gemv<1, WB>), grid, block, 0, s, a);
+    else if (T <= 2) hipLaunchKernelGGL((k_gateup_gemv<2, WB>), grid, block, 0, s, a);
+    else if (T <= 4) hipLaunchKernelGGL((k_gateup_gemv<4, WB>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((k_gateup_gemv<8, WB>), grid, block, 0, s, a);
+}
+
+template <int WB>
+void launch_down_wb(int T, dim3 grid, const GemvArgs &a, hipStream_t s)
+{
+    if (T <= 1) hipLaunchKernelGGL((k_down_gemv<1, WB>), grid, dim3(256), 0, s, a);
+    else if (T <= 2) hipLaunchKernelGGL((k_down_gemv<2, WB>), grid, dim3(256), 0, s, a);
+    else if (T <= 4) hipLaunchKernelGGL((k_down_gemv<4, WB>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((k_down_gemv<8, WB>), grid, dim3(256), 0, s, a);
 }
 
 GemvArgs make_args(const coli_moe_layer &L, const WsLayout &lay, char *ws)
@@ -56,14 +74,8 @@ hipError_t launch_gateup_gemv(const coli_moe_layer &L, int T, const WsLayout &la
     const int nblk = L.H / QK;
     const int threads = ((nblk + 63) / 64) * 64;
     const dim3 grid((unsigned)((lay.max_items - item0) * (L.I / QK)));
-    if (T <= 1)
-        hipLaunchKernelGGL((k_gateup_gemv<1>), grid, dim3(threads), 0, s, a);
-    else if (T <= 2)
-        hipLaunchKernelGGL((k_gateup_gemv<2>), grid, dim3(threads), 0, s, a);
-    else if (T <= 4)
-        hipLaunchKernelGGL((k_gateup_gemv<4>), grid, dim3(threads), 0, s, a);
-    else
-        hipLaunchKernelGGL((k_gateup_gemv<8>), grid, dim3(threads), 0, s, a);
+    if (L.weight_bits == 8) launch_gateup_wb<8>(T, grid, dim3(threads), a, s);
+    else launch_gateup_wb<4>(T, grid, dim3(threads), a, s);
     return hipGetLastError();
 }
 
@@ -74,14 +86,8 @@ hipError_t launch_down_gemv(const coli_moe_layer &L, int T, const WsLayout &lay,
     a.item0 = item0;
     a.q_a = L.down_q; a.s_a = L.down_s; a.q_b = nullptr; a.s_b = nullptr;
     const dim3 grid((unsigned)((lay.max_items - item0) * (L.H / QK)));
-    if (T <= 1)
-        hipLaunchKernelGGL((k_down_gemv<1>), grid, dim3(256), 0, s, a);
-    else if (T <= 2)
-        hipLaunchKernelGGL((k_down_gemv<2>), grid, dim3(256), 0, s, a);
-    else if (T <= 4)
-        hipLaunchKernelGGL((k_down_gemv<4>), grid, dim3(256), 0, s, a);
-    else
-        hipLaunchKernelGGL((k_down_gemv<8>), grid, dim3(256), 0, s, a);
+    if (L.weight_bits == 8) launch_down_wb<8>(T, grid, a, s);
+    else launch_down_wb<4>(T, grid, a, s);
     return hipGetLastError();
 }
 

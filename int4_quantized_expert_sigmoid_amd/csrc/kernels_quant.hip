@@ -95,6 +95,29 @@ __global__ void __launch_bounds__(256) k_pack_int4(const float *__restrict__ w, 
     if (threadIdx.x == 0) sc[row] = d;
 }
 
+// int8 rows: d = absmax/127, codes clamp(rint(w/d), -127, 127); within each
+// group of 8 columns column c goes to byte perm8(c) (0,2,4,6 then 1,3,5,7).
+__global__ void __launch_bounds__(256) k_pack_int8(const float *__restrict__ w, int cols,
+                                                   int8_t *__restrict__ q, float *__restrict__ sc)
+{
+    __shared__ float red[4];
+    const long row = blockIdx.x;
+    const float *src = w + row * (long)cols;
+    float amax = 0.0f;
+    for (int c = threadIdx.x; c < cols; c += blockDim.x) amax = fmaxf(amax, fabsf(src[c]));
+    amax = wave_max(amax);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = amax;
+    __syncthreads();
+    amax = red[0];
+    for (int i = 1; i < (int)(blockDim.x >> 6); ++i) amax = fmaxf(amax, red[i]);
+    const float d = __fdiv_rn(amax, 127.0f);
+    const float id = (d != 0.0f) ? __fdiv_rn(1.0f, d) : 0.0f;
+    int8_t *dst = q + row * (long)cols;
+    for (int c = threadIdx.x; c < cols; c += blockDim.x)
+        dst[(c & ~7) + perm8(c & 7)] = (int8_t)round_clamp(__fmul_rn(src[c], id), -127.0f, 127.0f);
+    if (threadIdx.x == 0) sc[row] = d;
+}
+
 // One workgroup per token; mean of squares in f64.
 // One workgroup per token. With 16-byte aligned x, gamma and out, H a
 // multiple of 4 and at most 4 float4 per thread, x and gamma are loaded once, all at the start, and kept in
@@ -215,6 +238,12 @@ hipError_t launch_reorder_q8(const int8_t *xq_nat, int n, int8_t *xq_perm, hipSt
 hipError_t launch_pack_int4(const float *w, int rows, int cols, uint8_t *q, float *sc, hipStream_t s)
 {
     hipLaunchKernelGGL(k_pack_int4, dim3(rows), dim3(256), 0, s, w, cols, q, sc);
+    return hipGetLastError();
+}
+
+hipError_t launch_pack_int8(const float *w, int rows, int cols, int8_t *q, float *sc, hipStream_t s)
+{
+    hipLaunchKernelGGL(k_pack_int8, dim3(rows), dim3(256), 0, s, w, cols, q, sc);
     return hipGetLastError();
 }
 

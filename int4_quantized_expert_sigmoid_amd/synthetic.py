@@ -2,7 +2,8 @@
 
 Weights come from the seeded generator (synth/, counter-addressed, its device
 twin writes f32 rows straight into HBM) and are packed to int4 on the GPU by
-the library's own packer (coli_pack_int4_rows_dev). Router weights, bias,
+the library's own packer (coli_pack_int4_rows_dev, or coli_pack_int8_rows_dev
+for int8 experts). Router weights, bias,
 tokens and RMSNorm gains are small and generated on the host.
 """
 from __future__ import annotations
@@ -12,13 +13,14 @@ import torch
 
 from synth import synth as S
 
-from .api import MoELayer, pack_int4_rows_dev
+from .api import MoELayer, pack_int4_rows_dev, pack_int8_rows_dev
 
 
 def device_layer(spec: S.LayerSpec, seed: int = 0, layer: int = 0, device: str = "cuda",
                  scratch: torch.Tensor = None) -> MoELayer:
     L = MoELayer.empty(spec.H, spec.I, spec.E, spec.top_k, spec.has_shared, spec.n_group, spec.topk_group,
-                       spec.route_scale, device=device)
+                       spec.route_scale, device=device, weight_bits=spec.weight_bits)
+    pack = pack_int8_rows_dev if spec.weight_bits == 8 else pack_int4_rows_dev
     W, b = S.router(spec, seed, layer)
     L.router_w.copy_(torch.from_numpy(W))
     L.router_b.copy_(torch.from_numpy(b))
@@ -32,7 +34,7 @@ def device_layer(spec: S.LayerSpec, seed: int = 0, layer: int = 0, device: str =
                                (S.DOWN, L.down_q, L.down_s, (spec.H, spec.I))):
             buf = scratch[:n].view(shape)
             S.dev_expert_matrix(buf.data_ptr(), spec, seed, layer, e, m, hip_stream=stream)
-            pack_int4_rows_dev(buf, q[e], s[e])
+            pack(buf, q[e], s[e])
     return L
 
 

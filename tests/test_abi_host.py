@@ -41,8 +41,10 @@ def fake_layer(H=6144, I=2048, E=256, k=8, **kw):
     p = 1 << 20     # aligned dummy address: never dereferenced by the checks below
     args = dict(H=H, I=I, E=E, top_k=k, n_group=1, topk_group=1, has_shared=1, route_scale=1.0)
     args.update(kw)
-    return CLayer(args["H"], args["I"], args["E"], args["top_k"], args["n_group"], args["topk_group"],
-                  args["has_shared"], args["route_scale"], p, p, p, p, p, p, p, p)
+    L = CLayer(args["H"], args["I"], args["E"], args["top_k"], args["n_group"], args["topk_group"],
+               args["has_shared"], args["route_scale"], p, p, p, p, p, p, p, p)
+    L.weight_bits = args.get("weight_bits", 4)
+    return L
 
 
 def ws_bytes(layer, T):
@@ -63,7 +65,7 @@ def test_workspace_sizes():
 @pytest.mark.parametrize("bad", [
     dict(H=48), dict(I=40), dict(E=0), dict(E=600), dict(top_k=0), dict(top_k=17), dict(top_k=9, E=8),
     dict(n_group=3), dict(n_group=8, topk_group=9), dict(n_group=8, topk_group=1, top_k=33),
-    dict(has_shared=2), dict(route_scale=float("nan")),
+    dict(has_shared=2), dict(route_scale=float("nan")), dict(weight_bits=5), dict(weight_bits=16),
 ])
 def test_invalid_layers_rejected(bad):
     L = fake_layer(**bad)
@@ -135,3 +137,42 @@ def test_host_packer_matches_oracle_packer():
     q, s = host_pack(edge)
     qo, so = O.pack_int4_rows(edge)
     assert np.array_equal(q, qo) and np.array_equal(s, so)
+
+
+def test_int8_experts_only_on_the_gemv_path():
+    """int8 experts run on the token-GEMV path; larger batches and the fused
+    path are refused before any launch (COLI_EUNSUPPORTED), routing is not."""
+    L = fake_layer(weight_bits=8)
+    p = ctypes.c_void_p(1 << 20)
+    F = lib().coli_moe_forward
+    assert ws_bytes(L, 4) > 0
+    assert F(ctypes.byref(L), p, 9, p, 0, p, 1 << 40, None) == _lib.COLI_EUNSUPPORTED      # grouped batch
+    assert F(ctypes.byref(L), p, 4, p, 4, p, 1 << 40, None) == _lib.COLI_EUNSUPPORTED      # forced grouped
+    assert F(ctypes.byref(L), p, 1, p, 8, p, 1 << 40, None) == _lib.COLI_EUNSUPPORTED      # fused
+    X = lib().coli_moe_experts
+    assert X(ctypes.byref(L), p, p, p, p, 9, p, 0, p, 1 << 40, None) == _lib.COLI_EUNSUPPORTED
+
+
+def _perm8(j):
+    return 4 + (j >> 1) if j & 1 else j >> 1
+
+
+def test_host_int8_packer_matches_oracle_in_library_layout():
+    w = S.expert_matrix(S.LayerSpec(H=256, I=128, E=4, top_k=1), 0, 0, 1, S.GATE)
+    edge = np.zeros((4, 64), np.float32)
+    edge[1, :] = 1e-40                      # subnormal row: 1/d overflows
+    edge[2, 5] = -3.5                       # single nonzero
+    edge[3, :] = np.linspace(-127, 127, 64) # ties at .5 after scaling
+    for m in (w, edge):
+        rows, cols = m.shape
+        q = np.empty((rows, cols), np.int8)
+        s = np.empty(rows, np.float32)
+        assert lib().coli_pack_int8_rows(ctypes.c_void_p(m.ctypes.data), rows, cols, ctypes.c_void_p(q.ctypes.data),
+                                         ctypes.c_void_p(s.ctypes.data)) == 0
+        qo, so = O.pack_int8_rows(m)
+        pos = np.array([(c & ~7) + _perm8(c & 7) for c in range(cols)])
+        assert np.array_equal(s, so)
+        assert np.array_equal(q[:, pos], qo)       # column c of the oracle sits at byte pos[c]
+    bad = np.zeros((2, 12), np.float32)
+    assert lib().coli_pack_int8_rows(ctypes.c_void_p(bad.ctypes.data), 2, 12, ctypes.c_void_p(bad.ctypes.data),
+                                     ctypes.c_void_p(bad.ctypes.data)) == _lib.COLI_EINVAL
