@@ -115,6 +115,8 @@ __device__ __forceinline__ void gateup_rows(const GemvArgs &a, const ItemDesc &i
     const long row0 = (long)it.e * a.I + (long)rb * QK;
     const int set = wave / nw, wv = wave - set * nw;
     const int col = wv * 64 + lane;              // this thread's block column
+    // token slots in use, as a scalar: slots past it cost no dot products
+    const int ntu = __builtin_amdgcn_readfirstlane(it.nt);
 
     if (set < RS) {
         const bool active = col < nblk;
@@ -170,13 +172,16 @@ __device__ __forceinline__ void gateup_rows(const GemvArgs &a, const ItemDesc &i
 #pragma unroll
             for (int r = 0; r < RC; ++r) {
 #pragma unroll
-                for (int s = 0; s < NT; ++s) v[s][2 * r] = (double)dot_block_w<WB>(wg[cur][r], act[s]) * dsc[s];
-#pragma unroll
-                for (int s = 0; s < NT; ++s) v[s][2 * r + 1] = (double)dot_block_w<WB>(wu[cur][r], act[s]) * dsc[s];
+                for (int s = 0; s < NT; ++s) {
+                    if (s > 0 && s >= ntu) break;    // slot 0 is always in use
+                    v[s][2 * r] = (double)dot_block_w<WB>(wg[cur][r], act[s]) * dsc[s];
+                    v[s][2 * r + 1] = (double)dot_block_w<WB>(wu[cur][r], act[s]) * dsc[s];
+                }
             }
             const int vi = transpose_index<NV>(lane);
 #pragma unroll
             for (int s = 0; s < NT; ++s) {
+                if (s > 0 && s >= ntu) break;
                 wave_transpose_reduce<NV>(v[s]);
                 if ((lane & (64 / NV - 1)) == 0) sh.red[wv][s][2 * (set * RPS + c * RC) + vi] = v[s][0];
             }
@@ -231,6 +236,7 @@ __device__ __forceinline__ void down_rows(const GemvArgs &a, const ItemDesc &it,
     const bool active = lane < nblk;
     const long rowb = (long)a.I * WB / 8;
     const long row0 = (long)grp * (4 * RPW) + wave * RPW;
+    const int ntu = __builtin_amdgcn_readfirstlane(it.nt);
     const uint8_t *pd = a.q_a + ((long)it.e * a.H + row0) * rowb + (active ? lane : 0) * WFmt<WB>::BLK_BYTES;
 
     uint4 wd[2][RD][NP];
@@ -274,13 +280,17 @@ __device__ __forceinline__ void down_rows(const GemvArgs &a, const ItemDesc &it,
 #pragma unroll
         for (int r = 0; r < RD; ++r) {
 #pragma unroll
-            for (int s = 0; s < NT; ++s) v[s][r] = (double)dot_block_w<WB>(wd[cur][r], act[s]) * dsc[s];
+            for (int s = 0; s < NT; ++s) {
+                if (s > 0 && s >= ntu) break;        // slot 0 is always in use
+                v[s][r] = (double)dot_block_w<WB>(wd[cur][r], act[s]) * dsc[s];
+            }
         }
         const int vi = transpose_index<RD>(lane);
 #pragma unroll
         for (int s = 0; s < NT; ++s) {
+            if (s > 0 && s >= ntu) break;
             wave_transpose_reduce<RD>(v[s]);
-            if (s < it.nt && (lane & (64 / RD - 1)) == 0) {
+            if ((lane & (64 / RD - 1)) == 0) {
                 const long row = row0 + c * RD + vi;
                 const long pair = (long)it.item * MAX_SLOTS + s;
                 const float out = (float)((double)a.s_a[(long)it.e * a.H + row] * v[s][0]);

@@ -156,6 +156,7 @@ struct DnArgs {
     const uint8_t *q;          // down_q [E+shared][H][I/2] (int4) or [E+shared][H][I] (int8)
     const float *s;            // down_s [E+shared][H]
     int H, I, T, top_k, has_shared;
+    int max_items;             // entries of the item tables (<= DEC_MAX_ITEMS)
     const int *ctrl, *item_expert, *item_ntok;
     const int8_t *hq;          // [pairs][I] reordered
     const float *hs;           // [pairs][I/32]
@@ -213,17 +214,22 @@ template <int NT, int RPU, int WB>
 __device__ __forceinline__ void dn_compute(const DnArgs &a, int item, long row0, int lane,
                                            const DnStage<NT, RPU, WB> &st, float *ye_l)
 {
+    const int ntu = __builtin_amdgcn_readfirstlane(st.nt);   // slots past it cost no dot products
     double v[NT][RPU];
 #pragma unroll
     for (int r = 0; r < RPU; ++r) {
 #pragma unroll
-        for (int s = 0; s < NT; ++s) v[s][r] = (double)dot_block_w<WB>(st.wd[r], st.act[s]) * st.dsc[s];
+        for (int s = 0; s < NT; ++s) {
+            if (s > 0 && s >= ntu) break;            // slot 0 is always in use
+            v[s][r] = (double)dot_block_w<WB>(st.wd[r], st.act[s]) * st.dsc[s];
+        }
     }
     const int vi = transpose_index<RPU>(lane);
 #pragma unroll
     for (int s = 0; s < NT; ++s) {
+        if (s > 0 && s >= ntu) break;
         wave_transpose_reduce<RPU>(v[s]);
-        if (s < st.nt && (lane & (64 / RPU - 1)) == 0) {
+        if ((lane & (64 / RPU - 1)) == 0) {
             const long row = row0 + vi;
             const long pair = (long)item * MAX_SLOTS + s;
             const float out = (float)((double)a.s[(long)st.e * a.H + row] * v[s][0]);
@@ -245,9 +251,11 @@ __global__ void __launch_bounds__(256) k_down_combine(DnArgs a)
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwave = blockDim.x >> 6;
     const long row0 = (long)blockIdx.x * RPU;
     TRACE(a, 2, 0);
-    // the whole item table up front, so no item's loads wait on a lookup
-    const int n_items = min(a.ctrl[CTRL_N_ITEMS], DEC_MAX_ITEMS);
-    for (int i = threadIdx.x; i < n_items; i += blockDim.x) {
+    // the whole item table up front, so no item's loads wait on a lookup;
+    // every entry a union of this batch can have is read together with the
+    // item count (one round trip; entries past the count go unused)
+    const int n_items = min(a.ctrl[CTRL_N_ITEMS], a.max_items);
+    for (int i = threadIdx.x; i < a.max_items; i += blockDim.x) {
         it_e[i] = a.item_expert[i];
         it_nt[i] = a.item_ntok[i];
     }
@@ -383,6 +391,7 @@ hipError_t launch_decode_down_combine(const coli_moe_layer &L, int T, const WsLa
     DnArgs a;
     a.q = L.down_q; a.s = L.down_s;
     a.H = L.H; a.I = L.I; a.T = T; a.top_k = L.top_k; a.has_shared = L.has_shared;
+    a.max_items = lay.max_items < DEC_MAX_ITEMS ? lay.max_items : DEC_MAX_ITEMS;
     a.ctrl = reinterpret_cast<const int *>(ws + lay.ctrl);
     a.item_expert = reinterpret_cast<const int *>(ws + lay.item_expert);
     a.item_ntok = reinterpret_cast<const int *>(ws + lay.item_ntok);

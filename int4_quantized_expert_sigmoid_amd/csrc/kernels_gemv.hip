@@ -13,8 +13,14 @@ __global__ void __launch_bounds__(256) k_gateup_gemv(GemvArgs a)
     __shared__ GateUpShared<NT> sh;
     const int nrb = a.I / QK;
     const int item = a.item0 + (int)blockIdx.x / nrb, rb = blockIdx.x % nrb;
-    if (item >= a.ctrl[CTRL_N_ITEMS]) return;
+    // the grid covers every item a union can have, so the table entry is in
+    // bounds: read it together with the item count (one round trip; the
+    // empty asm keeps the compiler from sinking the entry's loads past the
+    // exit test)
+    const int n_items = a.ctrl[CTRL_N_ITEMS];
     const ItemDesc it = item_from_table(a, item);
+    asm volatile("" ::"s"(n_items), "s"(it.e), "s"(it.nt));
+    if (item >= n_items) return;
     gateup_rows<NT, GemvTuneW<NT, WB>::RC, false, false, 1, WB>(a, it, rb, sh);
 }
 
@@ -23,8 +29,10 @@ __global__ void __launch_bounds__(256) k_down_gemv(GemvArgs a)
 {
     const int ngrp = a.H / QK;
     const int item = a.item0 + (int)blockIdx.x / ngrp, grp = blockIdx.x % ngrp;
-    if (item >= a.ctrl[CTRL_N_ITEMS]) return;
+    const int n_items = a.ctrl[CTRL_N_ITEMS];   // with the entry in one round trip, as above
     const ItemDesc it = item_from_table(a, item);
+    asm volatile("" ::"s"(n_items), "s"(it.e), "s"(it.nt));
+    if (item >= n_items) return;
     down_rows<NT, GemvTuneW<NT, WB>::RD, false, 8, WB>(a, it, grp);
 }
 

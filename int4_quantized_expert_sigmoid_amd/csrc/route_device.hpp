@@ -370,7 +370,7 @@ __device__ inline unsigned long long kept_groups(const double *__restrict__ key,
     if (lane < n_group) {
         double m1 = -INFINITY, m2 = -INFINITY;
         for (int e = lane * gsize; e < (lane + 1) * gsize; ++e) {
-            const double v = ld_dev(key + e);
+            const double v = key[e];
             if (v > m1) { m2 = m1; m1 = v; }
             else if (v > m2) { m2 = v; }
         }
@@ -398,8 +398,9 @@ __device__ __forceinline__ unsigned wave_max_u32(unsigned v)
 }
 
 // Lane l's KPL keys (experts l, l+64, ...) as order keys with their experts
-// and sigmoids, sorted by (key desc, expert asc). Coherent loads: the keys
-// may come from other workgroups of the same launch.
+// and sigmoids, sorted by (key desc, expert asc). The keys come from an
+// earlier launch: plain loads, so the workgroups on one XCD share its L2
+// copy instead of each reading the same lines from memory.
 template <int KPL>
 __device__ __forceinline__ void lane_keys(const double *__restrict__ key, const double *__restrict__ sig, int E,
                                           int gsize, unsigned long long gm, unsigned long long (&ok)[KPL],
@@ -410,8 +411,8 @@ __device__ __forceinline__ void lane_keys(const double *__restrict__ key, const 
     for (int i = 0; i < KPL; ++i) {
         const int e = lane + 64 * i;
         const bool in = e < E;
-        const double kv = in ? ld_dev(key + e) : 0.0;
-        sv[i] = in ? ld_dev(sig + e) : 0.0;
+        const double kv = in ? key[e] : 0.0;
+        sv[i] = in ? sig[e] : 0.0;
         ok[i] = (in && ((gm >> (e / gsize)) & 1ull)) ? order_key(kv) : 0ull;
         oe[i] = e;
     }
