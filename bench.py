@@ -16,7 +16,9 @@ steps, one per layer instance, 16 different token batches) and replayed.
 Other workloads: glm52_mtp_verify_T4 (T=4), glm52_prefill_T512 (T=512, the
 grouped int8-MFMA path), glm52_chain16_T1 (one token through 16 layers:
 RMSNorm, then the layer with its output added to the residual stream; a step
-is the whole 16-layer stack, restarted from the same input token).
+is the whole 16-layer stack, restarted from the same input token), and
+glm52_int8_mtp_T1 / glm52_int8_T4 (the same layer with int8 experts, the
+MTP head's format, at T=1 and T=4).
 
 Prints ONE JSON line (metric, value, roofline of the dominant kernel,
 cpu_baseline of the oracle on a bounded sample).
@@ -149,7 +151,7 @@ def main():
     del scratch
     torch.cuda.synchronize()
     log(f"bench: layers ready in {time.time() - t0:.1f} s "
-        f"({n_inst * spec.n_experts_stored * spec.expert_bytes / 1e9:.1f} GB int4 resident)")
+        f"({n_inst * spec.n_experts_stored * spec.expert_bytes / 1e9:.1f} GB of int{spec.weight_bits} experts resident)")
 
     ws = [api.workspace(L, T) for L in layers]
     cls = [L.c() for L in layers]
@@ -192,7 +194,8 @@ def main():
         lay = api.workspace_layout(layers[j], T)
         idx = ws[j][lay.idx: lay.idx + 4 * T * spec.top_k].view(torch.int32).cpu().numpy()
         union.append(len(set(idx.tolist())))
-    gu_row, dn_row = 2 * spec.I * (spec.H // 2 + 4), spec.H * (spec.I // 2 + 4)
+    wb = spec.weight_bits                        # 4: two codes per byte; 8: one
+    gu_row, dn_row = 2 * spec.I * (spec.H * wb // 8 + 4), spec.H * (spec.I * wb // 8 + 4)
     bytes_call = [(u + spec.has_shared) * spec.expert_bytes for u in union]
     gateup_bytes = [(u + spec.has_shared) * gu_row for u in union]
     down_bytes = [(u + spec.has_shared) * dn_row for u in union]
@@ -279,7 +282,7 @@ def main():
     gu_tops = gu_ops / (stage_avg[i_gu] * 1e-3) / 1e12
     log("bench: launch averages (ms): " + ", ".join(f"{n}={v:.4f}" for n, v in zip(STAGES, stage_avg)))
     log(f"bench: gate/up {gu_gbs:.0f} GB/s, down {dn_gbs:.0f} GB/s, whole step {step_gbs:.0f} GB/s "
-        f"on int4 expert bytes; {ms_step * 1e3:.2f} us/step (graph={use_graph}), wall {t_wall:.3f} s")
+        f"on int{wb} expert bytes; {ms_step * 1e3:.2f} us/step (graph={use_graph}), wall {t_wall:.3f} s")
 
     if args.copy_probe:
         src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
@@ -307,7 +310,7 @@ def main():
     if chain:
         config["stack_tokens_per_s"] = round(K * T / (ms_total / 1e3), 1)
     out = {
-        "metric": f"MoE-layer tokens*layers/s (GLM-5.2-shaped layer, int4 experts, {phase})",
+        "metric": f"MoE-layer tokens*layers/s (GLM-5.2-shaped layer, int{wb} experts, {phase})",
         "value": round(value, 1),
         "unit": "tokens*layers/s",
         "n_gpus": 1,
@@ -317,7 +320,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "int4xint8->int32, f64 block sums",
+        "dtype": f"int{wb}xint8->int32, f64 block sums",
         "data": "synthetic (seeded Philox weights and tokens, no trained checkpoint)",
         "config": config,
         "roofline": {"bound": "hbm", "kernel": "k_select_gateup" if decode else "k_gateup_mfma",

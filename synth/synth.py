@@ -197,6 +197,12 @@ WORKLOADS = {
                                    TokenSpec(T=512, outlier_channels=61)),
     "glm52_chain16_T1": Workload("glm52_chain16_T1", GLM52, TokenSpec(T=1, outlier_channels=61),
                                  n_layers=16),
+    # the same layer with int8 experts (one byte per weight), the format the
+    # pages keep for the MTP head: its draft step (T=1) and a verify-sized batch
+    "glm52_int8_mtp_T1": Workload("glm52_int8_mtp_T1", replace(GLM52, weight_bits=8),
+                                  TokenSpec(T=1, outlier_channels=61)),
+    "glm52_int8_T4": Workload("glm52_int8_T4", replace(GLM52, weight_bits=8),
+                              TokenSpec(T=4, rho=0.8, outlier_channels=61)),
 }
 
 
