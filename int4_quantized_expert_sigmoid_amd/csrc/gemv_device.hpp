@@ -25,6 +25,7 @@ struct GemvArgs {
     const uint8_t *q_a, *q_b;      // gate, up (gate/up) or down (down)
     const float *s_a, *s_b;
     int H, I, E, T;
+    int has_shared;                // item 0 is the shared expert (expert E, slot t = token t)
     int item0;                     // first item of a launch that covers items item0.. only
     const float *x;                // [T][H] layer input (coherent mode quantises it on the fly)
     const int8_t *xq;              // [T][H] reordered Q8(x)

@@ -155,7 +155,7 @@ __global__ void __launch_bounds__(256) k_select_gateup(SelGuArgs a, GemvArgs g, 
 struct DnArgs {
     const uint8_t *q;          // down_q [E+shared][H][I/2] (int4) or [E+shared][H][I] (int8)
     const float *s;            // down_s [E+shared][H]
-    int H, I, T, top_k, has_shared;
+    int H, I, E, T, top_k, has_shared;
     int max_items;             // entries of the item tables (<= DEC_MAX_ITEMS)
     const int *ctrl, *item_expert, *item_ntok;
     const int8_t *hq;          // [pairs][I] reordered
@@ -177,20 +177,20 @@ template <int NT, int RPU, int WB>
 struct DnStage {
     uint4 wd[RPU][WFmt<WB>::BLK_BYTES / 16];
     Blk8 act[NT];
-    double dsc[NT];
+    float ds[NT];              // block scales as loaded (turned to f64 where used, so a load is never waited for early)
     int e, nt;
 };
 
 template <int NT, int RPU, int WB>
-__device__ __forceinline__ void dn_load(const DnArgs &a, int item, long row0, int lane, const int *it_e,
-                                        const int *it_nt, DnStage<NT, RPU, WB> &st)
+__device__ __forceinline__ void dn_load_e(const DnArgs &a, int item, long row0, int lane, int e, int nt,
+                                          DnStage<NT, RPU, WB> &st)
 {
     constexpr int NP = WFmt<WB>::BLK_BYTES / 16;
     const int nblk = a.I / QK;
     const bool active = lane < nblk;
     const long rowb = (long)a.I * WB / 8;
-    st.e = it_e[item];
-    st.nt = it_nt[item];
+    st.e = e;
+    st.nt = nt;
     const uint8_t *pd = a.q + ((long)st.e * a.H + row0) * rowb + (active ? lane : 0) * WFmt<WB>::BLK_BYTES;
 #pragma unroll
     for (int r = 0; r < RPU; ++r)
@@ -201,13 +201,22 @@ __device__ __forceinline__ void dn_load(const DnArgs &a, int item, long row0, in
         if (s < st.nt && active) {
             const long pair = (long)item * MAX_SLOTS + s;
             st.act[s] = load_blk8(a.hq + pair * a.I + lane * QK);
-            st.dsc[s] = (double)a.hs[pair * nblk + lane] * WFmt<WB>::KSCALE;
+            st.ds[s] = a.hs[pair * nblk + lane];
         } else {
 #pragma unroll
             for (int k = 0; k < 8; ++k) st.act[s].v[k] = 0;
-            st.dsc[s] = 0.0;
+            st.ds[s] = 0.0f;
         }
     }
+}
+
+// The same for an item of the union, its expert and token count from the
+// table in LDS.
+template <int NT, int RPU, int WB>
+__device__ __forceinline__ void dn_load(const DnArgs &a, int item, long row0, int lane, const int *it_e,
+                                        const int *it_nt, DnStage<NT, RPU, WB> &st)
+{
+    dn_load_e(a, item, row0, lane, it_e[item], it_nt[item], st);
 }
 
 template <int NT, int RPU, int WB>
@@ -221,7 +230,7 @@ __device__ __forceinline__ void dn_compute(const DnArgs &a, int item, long row0,
 #pragma unroll
         for (int s = 0; s < NT; ++s) {
             if (s > 0 && s >= ntu) break;            // slot 0 is always in use
-            v[s][r] = (double)dot_block_w<WB>(st.wd[r], st.act[s]) * st.dsc[s];
+            v[s][r] = (double)dot_block_w<WB>(st.wd[r], st.act[s]) * ((double)st.ds[s] * WFmt<WB>::KSCALE);
         }
     }
     const int vi = transpose_index<RPU>(lane);
@@ -241,8 +250,9 @@ __device__ __forceinline__ void dn_compute(const DnArgs &a, int item, long row0,
 
 // A workgroup owns RPU consecutive output rows. Its waves take the items of
 // the union round-robin (wave w: items w, w + 4, ...), each item's RPU rows
-// at once with the wave's next item already loading; then the per-pair row
-// values in LDS are combined into y.
+// at once with the wave's next item already loading (wave 0 starts on the
+// shared expert at once); then the per-pair row values in LDS are combined
+// into y.
 template <int NT, int RPU, int WB>
 __global__ void __launch_bounds__(256) k_down_combine(DnArgs a)
 {
@@ -251,6 +261,11 @@ __global__ void __launch_bounds__(256) k_down_combine(DnArgs a)
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwave = blockDim.x >> 6;
     const long row0 = (long)blockIdx.x * RPU;
     TRACE(a, 2, 0);
+    DnStage<NT, RPU, WB> A, B;
+    // the shared expert is item 0 with T token slots whatever the routing:
+    // wave 0 starts loading it before the item table arrives
+    const bool early = a.has_shared && wave == 0;
+    if (early) dn_load_e(a, 0, row0, lane, a.E, a.T, A);
     // the whole item table up front, so no item's loads wait on a lookup;
     // every entry a union of this batch can have is read together with the
     // item count (one round trip; entries past the count go unused)
@@ -261,9 +276,8 @@ __global__ void __launch_bounds__(256) k_down_combine(DnArgs a)
     }
     __syncthreads();
 
-    DnStage<NT, RPU, WB> A, B;
     int i = wave;
-    if (i < n_items) dn_load(a, i, row0, lane, it_e, it_nt, A);
+    if (i < n_items && !early) dn_load(a, i, row0, lane, it_e, it_nt, A);
     for (; i < n_items; i += 2 * nwave) {
         if (i + nwave < n_items) dn_load(a, i + nwave, row0, lane, it_e, it_nt, B);
         dn_compute(a, i, row0, lane, A, ye_l);
@@ -292,7 +306,7 @@ __global__ void __launch_bounds__(256) k_down_combine(DnArgs a)
 GemvArgs gemv_view(const coli_moe_layer &L, int T, const WsLayout &lay, char *ws)
 {
     GemvArgs g;
-    g.H = L.H; g.I = L.I; g.E = L.E; g.T = T; g.item0 = 0; g.x = nullptr;
+    g.H = L.H; g.I = L.I; g.E = L.E; g.T = T; g.has_shared = L.has_shared; g.item0 = 0; g.x = nullptr;
     g.xq = reinterpret_cast<const int8_t *>(ws + lay.xq);
     g.xs = reinterpret_cast<const float *>(ws + lay.xs);
     g.ctrl = reinterpret_cast<const int *>(ws + lay.ctrl);
@@ -390,7 +404,7 @@ hipError_t launch_decode_down_combine(const coli_moe_layer &L, int T, const WsLa
 {
     DnArgs a;
     a.q = L.down_q; a.s = L.down_s;
-    a.H = L.H; a.I = L.I; a.T = T; a.top_k = L.top_k; a.has_shared = L.has_shared;
+    a.H = L.H; a.I = L.I; a.E = L.E; a.T = T; a.top_k = L.top_k; a.has_shared = L.has_shared;
     a.max_items = lay.max_items < DEC_MAX_ITEMS ? lay.max_items : DEC_MAX_ITEMS;
     a.ctrl = reinterpret_cast<const int *>(ws + lay.ctrl);
     a.item_expert = reinterpret_cast<const int *>(ws + lay.item_expert);

@@ -29,6 +29,10 @@ __global__ void __launch_bounds__(256) k_down_gemv(GemvArgs a)
 {
     const int ngrp = a.H / QK;
     const int item = a.item0 + (int)blockIdx.x / ngrp, grp = blockIdx.x % ngrp;
+    if (a.has_shared && item == 0) {            // the shared expert exists whatever the routing:
+        down_rows<NT, GemvTuneW<NT, WB>::RD, false, 8, WB>(a, shared_item(a), grp);   // no table wait
+        return;
+    }
     const int n_items = a.ctrl[CTRL_N_ITEMS];   // with the entry in one round trip, as above
     const ItemDesc it = item_from_table(a, item);
     asm volatile("" ::"s"(n_items), "s"(it.e), "s"(it.nt));
@@ -57,7 +61,7 @@ void launch_down_wb(int T, dim3 grid, const GemvArgs &a, hipStream_t s)
 GemvArgs make_args(const coli_moe_layer &L, const WsLayout &lay, char *ws)
 {
     GemvArgs a;
-    a.H = L.H; a.I = L.I; a.E = L.E; a.T = lay.T; a.x = nullptr; a.item0 = 0;
+    a.H = L.H; a.I = L.I; a.E = L.E; a.T = lay.T; a.has_shared = L.has_shared; a.x = nullptr; a.item0 = 0;
     a.xq = reinterpret_cast<const int8_t *>(ws + lay.xq);
     a.xs = reinterpret_cast<const float *>(ws + lay.xs);
     a.ctrl = reinterpret_cast<const int *>(ws + lay.ctrl);
