@@ -48,9 +48,6 @@ TRAFFIC = {
                             "build.py"]),
 }
 
-# launches of one layer call, between the profiled events
-STAGES_DECODE = ["router", "select_gateup", "down_combine"]
-STAGES_PREFILL = ["logits", "select_bucket", "gateup_mfma", "down_mfma", "combine"]
 
 
 def kernel_source_hash(workload):
@@ -141,8 +138,6 @@ def main():
     spec, T = wl.layer, wl.tokens.T
     chain = wl.n_layers > 1
     decode = T <= 8                              # token-GEMV path; larger batches take the MFMA path
-    STAGES = STAGES_DECODE if decode else STAGES_PREFILL
-    i_gu, i_dn = (1, 2) if decode else (2, 3)
     n_inst = wl.n_layers if chain else args.instances
     log(f"bench: {args.workload} T={T}, building {n_inst} layer instances on device")
     t0 = time.time()
@@ -233,44 +228,28 @@ def main():
     ms_step = ms_total / K
     value = K * T * calls_per_step / (ms_total / 1e3)   # tokens x layers per second
 
-    # ---------------- per-launch durations with HIP events on the bench stream
-    # (eager layer calls on the same inputs; each span includes one launch gap)
-    hip = ctypes.CDLL("libamdhip64.so")
-    hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
-    hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
-    hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
-    hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+    # ---------------- per-kernel durations: eager layer calls on the same
+    # inputs through coli_moe_forward_timed, every launch recording its own
+    # start and stop (the kernel's timestamps, as a kernel-trace profiler
+    # reads them), on the bench stream
     calls = []
     for i in (range(8) if chain else range(min(K, 256))):
         calls += layer_calls(i)
-    evs = []
-    for _ in calls:
-        arr = (ctypes.c_void_p * 6)()
-        for k in range(6):
-            e = ctypes.c_void_p()
-            assert hip.hipEventCreate(ctypes.byref(e)) == 0
-            arr[k] = e
-        evs.append(arr)
-    for (j, xin, yout, fl), arr in zip(calls, evs):
+    evs = [api.KernelEvents(16) for _ in calls]
+    for (j, xin, yout, fl), ev in zip(calls, evs):
         if chain:
             api.rmsnorm(xr, gam[j], wl.rms_eps, out=xn, stream=stream)
-        rc = lib().coli_moe_forward_profiled(ctypes.byref(cls[j]), ctypes.c_void_p(xin.data_ptr()), T,
-                                             ctypes.c_void_p(yout.data_ptr()), fl,
-                                             ctypes.c_void_p(ws[j].data_ptr()), ws[j].numel(),
-                                             ctypes.c_void_p(stream.cuda_stream), arr, 6)
-        assert rc == 0, rc
+        api.moe_forward_timed(layers[j], xin, ws[j], ev, y=yout, flags=fl, stream=stream, c_layer=cls[j])
     stream.synchronize()
-    NS = len(STAGES)
-    stage_ms = np.zeros((len(calls), NS))
-    for c, arr in enumerate(evs):
-        hip.hipEventSynchronize(arr[5])
-        for k in range(NS):
-            f = ctypes.c_float()
-            hip.hipEventElapsedTime(ctypes.byref(f), arr[k], arr[k + 1])
-            stage_ms[c, k] = f.value
-        for k in range(6):
-            hip.hipEventDestroy(arr[k])
-    stage_avg = stage_ms.mean(axis=0)
+    per_call = [ev.durations_ms() for ev in evs]
+    label = lambda n: n.strip("()").split("<")[0]
+    names = [label(n) for n, _ in per_call[0]]
+    assert all([label(n) for n, _ in d] == names for d in per_call), "launch sequence varies between calls"
+    stage_avg = np.array([[ms for _, ms in d] for d in per_call]).mean(axis=0)
+    del evs
+    STAGES = names
+    i_gu = next(i for i, n in enumerate(names) if n in ("k_select_gateup", "k_gateup_mfma"))
+    i_dn = next(i for i, n in enumerate(names) if n in ("k_down_combine", "k_down_gemv", "k_down_mfma"))
     gu_bytes_avg = float(np.mean([gateup_bytes[j] for (j, _, _, _) in calls]))
     dn_bytes_avg = float(np.mean([down_bytes[j] for (j, _, _, _) in calls]))
     gu_gbs = gu_bytes_avg / (stage_avg[i_gu] * 1e-3) / 1e9
@@ -280,7 +259,7 @@ def main():
     # int8 work of the gate/up launch: every (token, expert) pair, shared included
     gu_ops = T * (spec.top_k + spec.has_shared) * 2 * 2 * spec.H * spec.I
     gu_tops = gu_ops / (stage_avg[i_gu] * 1e-3) / 1e12
-    log("bench: launch averages (ms): " + ", ".join(f"{n}={v:.4f}" for n, v in zip(STAGES, stage_avg)))
+    log("bench: kernel averages (ms): " + ", ".join(f"{n}={v:.4f}" for n, v in zip(STAGES, stage_avg)))
     log(f"bench: gate/up {gu_gbs:.0f} GB/s, down {dn_gbs:.0f} GB/s, whole step {step_gbs:.0f} GB/s "
         f"on int{wb} expert bytes; {ms_step * 1e3:.2f} us/step (graph={use_graph}), wall {t_wall:.3f} s")
 
@@ -306,7 +285,7 @@ def main():
               "mean_union_experts": float(np.mean(union)),
               "expert_bytes_per_step": step_bytes,
               "step_hbm_gbs": round(step_gbs, 1),
-              "launch_ms": {n: round(float(v), 5) for n, v in zip(STAGES, stage_avg)}}
+              "kernel_ms": [[n, round(float(v), 5)] for n, v in zip(STAGES, stage_avg)]}
     if chain:
         config["stack_tokens_per_s"] = round(K * T / (ms_total / 1e3), 1)
     out = {
@@ -323,7 +302,7 @@ def main():
         "dtype": f"int{wb}xint8->int32, f64 block sums",
         "data": "synthetic (seeded Philox weights and tokens, no trained checkpoint)",
         "config": config,
-        "roofline": {"bound": "hbm", "kernel": "k_select_gateup" if decode else "k_gateup_mfma",
+        "roofline": {"bound": "hbm", "kernel": STAGES[i_gu],
                      "achieved": round(gu_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gu_gbs / HBM_PEAK_GBS, 4),
                      "traffic": None if chain else measured_traffic(args.workload),

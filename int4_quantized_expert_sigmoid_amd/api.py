@@ -135,6 +135,65 @@ def moe_forward(layer: MoELayer, x: torch.Tensor, ws: torch.Tensor, y: Optional[
     return y
 
 
+class KernelEvents:
+    """Start/stop event pairs (HIP events with timing) for coli_moe_forward_timed."""
+
+    def __init__(self, n: int = 16):
+        self._hip = ctypes.CDLL("libamdhip64.so")
+        self._hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self._hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self._hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self._hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.n = n
+        self.start = (ctypes.c_void_p * n)()
+        self.stop = (ctypes.c_void_p * n)()
+        for arr in (self.start, self.stop):
+            for i in range(n):
+                e = ctypes.c_void_p()
+                if self._hip.hipEventCreate(ctypes.byref(e)) != 0:
+                    raise RuntimeError("hipEventCreate failed")
+                arr[i] = e
+        self.names = (ctypes.c_char_p * n)()
+        self.count = ctypes.c_int(0)
+
+    def durations_ms(self):
+        """(kernel name, ms) of each timed launch of the last call (waits for them)."""
+        out = []
+        for i in range(min(self.n, self.count.value)):
+            self._hip.hipEventSynchronize(self.stop[i])
+            f = ctypes.c_float()
+            if self._hip.hipEventElapsedTime(ctypes.byref(f), self.start[i], self.stop[i]) != 0:
+                raise RuntimeError("hipEventElapsedTime failed")
+            out.append((self.names[i].decode(), f.value))
+        return out
+
+    def __del__(self):
+        try:
+            for arr in (self.start, self.stop):
+                for e in arr:
+                    if e:
+                        self._hip.hipEventDestroy(e)
+        except Exception:
+            pass
+
+
+def moe_forward_timed(layer: MoELayer, x: torch.Tensor, ws: torch.Tensor, events: KernelEvents,
+                      y: Optional[torch.Tensor] = None, flags: int = 0, stream=None,
+                      c_layer: Optional[CLayer] = None) -> torch.Tensor:
+    """moe_forward with every launch's own start/stop in `events`
+    (events.durations_ms() reads them after the stream has run)."""
+    _dev(x, torch.float32, "x")
+    T = x.shape[0]
+    if y is None:
+        y = torch.empty_like(x)
+    cl = c_layer if c_layer is not None else layer.c()
+    check("coli_moe_forward_timed",
+          lib().coli_moe_forward_timed(ctypes.byref(cl), _ptr(x), T, _ptr(y), flags, _ptr(ws), ws.numel(),
+                                       _stream(stream), events.start, events.stop, events.n,
+                                       ctypes.byref(events.count), events.names))
+    return y
+
+
 def moe_experts(layer: MoELayer, xq: torch.Tensor, xs: torch.Tensor, idx: torch.Tensor, w: torch.Tensor,
                 ws: torch.Tensor, y: Optional[torch.Tensor] = None, flags: int = 0, stream=None) -> torch.Tensor:
     _dev(xq, torch.int8, "xq"); _dev(xs, torch.float32, "xs")

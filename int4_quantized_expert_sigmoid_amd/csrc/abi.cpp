@@ -10,6 +10,13 @@
 #include "internal.hpp"
 
 namespace coli {
+
+KernelTimer *&kernel_timer()
+{
+    static thread_local KernelTimer *t = nullptr;
+    return t;
+}
+
 namespace {
 
 constexpr size_t ALIGN = 256;
@@ -267,6 +274,24 @@ int coli_moe_forward_profiled(const coli_moe_layer *L, const float *x, int T, fl
     for (int i = 0; i < COLI_PROFILE_EVENTS; ++i)
         if (!events[i]) return COLI_EINVAL;
     return forward_impl(L, x, T, y, flags, ws, ws_bytes, stream, events);
+}
+
+int coli_moe_forward_timed(const coli_moe_layer *L, const float *x, int T, float *y, int flags, void *ws,
+                           size_t ws_bytes, void *stream, void *const *start, void *const *stop, int n_pairs,
+                           int *n_launches, const char **names)
+{
+    if (!n_launches || n_pairs < 0 || (n_pairs > 0 && (!start || !stop))) return COLI_EINVAL;
+    for (int i = 0; i < n_pairs; ++i)
+        if (!start[i] || !stop[i]) return COLI_EINVAL;
+    KernelTimer kt{reinterpret_cast<const hipEvent_t *>(start), reinterpret_cast<const hipEvent_t *>(stop), names,
+                   n_pairs, 0};
+    KernelTimer *&slot = kernel_timer();
+    KernelTimer *const prev = slot;
+    slot = &kt;
+    const int rc = forward_impl(L, x, T, y, flags, ws, ws_bytes, stream, nullptr);
+    slot = prev;
+    *n_launches = kt.next;
+    return rc;
 }
 
 int coli_moe_experts(const coli_moe_layer *L, const int8_t *xq, const float *xs, const int32_t *idx,

@@ -2,6 +2,7 @@
 // Host-side declarations only; every launcher enqueues on `s` and returns
 // the HIP status of its launch.
 #pragma once
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -9,6 +10,29 @@
 #include "../../include/coli_moe.h"
 
 namespace coli {
+
+// Kernel-exact timing of one layer call (coli_moe_forward_timed): while a
+// timer is installed on the calling thread, every launch records its own
+// start and stop (the kernel packet's timestamps) in the next event pair.
+struct KernelTimer {
+    const hipEvent_t *start, *stop;
+    const char **names;          // optional: the kernel expression of each launch
+    int n, next;                 // event pairs; launches so far (past n: untimed)
+};
+KernelTimer *&kernel_timer();    // this thread's timer, nullptr outside a timed call
+
+#define COLI_LAUNCH(kernel, grid, block, shmem, stream, ...)                                               \
+    do {                                                                                                    \
+        ::coli::KernelTimer *kt_ = ::coli::kernel_timer();                                                  \
+        const int i_ = kt_ ? kt_->next++ : 0;                                                               \
+        if (kt_ && i_ < kt_->n) {                                                                           \
+            if (kt_->names) kt_->names[i_] = #kernel;                                                       \
+            hipExtLaunchKernelGGL(kernel, grid, block, shmem, stream, kt_->start[i_], kt_->stop[i_], 0,     \
+                                  __VA_ARGS__);                                                             \
+        } else {                                                                                            \
+            hipLaunchKernelGGL(kernel, grid, block, shmem, stream, __VA_ARGS__);                            \
+        }                                                                                                   \
+    } while (0)
 
 constexpr int QK = 32;          // activation block width (Q8_0-style)
 constexpr int MAX_SLOTS = 8;    // token slots of one expert item on the GEMV path

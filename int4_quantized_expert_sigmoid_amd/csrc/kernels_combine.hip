@@ -32,7 +32,7 @@ hipError_t launch_combine(const coli_moe_layer &L, int T, const WsLayout &lay, c
                           float *y, bool accumulate, hipStream_t s)
 {
     const long n = (long)T * L.H;
-    hipLaunchKernelGGL(k_combine, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
+    COLI_LAUNCH(k_combine, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
                        reinterpret_cast<const float *>(ws + lay.ye), reinterpret_cast<const int *>(ws + lay.pair_of),
                        reinterpret_cast<const int *>(ws + lay.shared_pair), w, T, L.H, L.top_k, L.has_shared, y,
                        accumulate ? 1 : 0);

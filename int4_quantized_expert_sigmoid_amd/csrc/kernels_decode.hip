@@ -325,10 +325,10 @@ GemvArgs gemv_view(const coli_moe_layer &L, int T, const WsLayout &lay, char *ws
 template <int NT, int WB>
 hipError_t launch_sel_nt(int E, dim3 grid, const SelGuArgs &a, const GemvArgs &g, int nsh, hipStream_t s)
 {
-    if (E <= 64) hipLaunchKernelGGL((k_select_gateup<NT, 1, WB>), grid, dim3(256), 0, s, a, g, nsh);
-    else if (E <= 128) hipLaunchKernelGGL((k_select_gateup<NT, 2, WB>), grid, dim3(256), 0, s, a, g, nsh);
-    else if (E <= 256) hipLaunchKernelGGL((k_select_gateup<NT, 4, WB>), grid, dim3(256), 0, s, a, g, nsh);
-    else hipLaunchKernelGGL((k_select_gateup<NT, 8, WB>), grid, dim3(256), 0, s, a, g, nsh);
+    if (E <= 64) COLI_LAUNCH((k_select_gateup<NT, 1, WB>), grid, dim3(256), 0, s, a, g, nsh);
+    else if (E <= 128) COLI_LAUNCH((k_select_gateup<NT, 2, WB>), grid, dim3(256), 0, s, a, g, nsh);
+    else if (E <= 256) COLI_LAUNCH((k_select_gateup<NT, 4, WB>), grid, dim3(256), 0, s, a, g, nsh);
+    else COLI_LAUNCH((k_select_gateup<NT, 8, WB>), grid, dim3(256), 0, s, a, g, nsh);
     return hipGetLastError();
 }
 
@@ -344,7 +344,7 @@ template <int NT, int RPU, int WB>
 hipError_t launch_dn_nt(const coli_moe_layer &L, const WsLayout &lay, const DnArgs &a, hipStream_t s)
 {
     const size_t lds = (size_t)lay.max_items * MAX_SLOTS * RPU * sizeof(float);
-    hipLaunchKernelGGL((k_down_combine<NT, RPU, WB>), dim3((unsigned)(L.H / RPU)), dim3(256), lds, s, a);
+    COLI_LAUNCH((k_down_combine<NT, RPU, WB>), dim3((unsigned)(L.H / RPU)), dim3(256), lds, s, a);
     return hipGetLastError();
 }
 
@@ -365,10 +365,10 @@ hipError_t launch_decode_router(const coli_moe_layer &L, const float *x, int T, 
     r.trace = g_dec_trace;
 #endif
     const dim3 grid((unsigned)L.E);
-    if (T <= 1) hipLaunchKernelGGL(k_router<1>, grid, dim3(512), 0, s, r);
-    else if (T <= 2) hipLaunchKernelGGL(k_router<2>, grid, dim3(512), 0, s, r);
-    else if (T <= 4) hipLaunchKernelGGL(k_router<4>, grid, dim3(512), 0, s, r);
-    else hipLaunchKernelGGL(k_router<8>, grid, dim3(512), 0, s, r);
+    if (T <= 1) COLI_LAUNCH(k_router<1>, grid, dim3(512), 0, s, r);
+    else if (T <= 2) COLI_LAUNCH(k_router<2>, grid, dim3(512), 0, s, r);
+    else if (T <= 4) COLI_LAUNCH(k_router<4>, grid, dim3(512), 0, s, r);
+    else COLI_LAUNCH(k_router<8>, grid, dim3(512), 0, s, r);
     return hipGetLastError();
 }
 

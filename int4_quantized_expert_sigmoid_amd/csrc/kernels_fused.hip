@@ -298,16 +298,16 @@ hipError_t launch_decode_fused(const coli_moe_layer &L, const float *x, int T, c
     lds = std::max(lds, (size_t)T * (L.top_k + 1) * 4 + (size_t)T * L.top_k * 4);   // combine
     lds = (lds + 15) & ~(size_t)15;
     if (T <= 1) {
-        hipLaunchKernelGGL(k_decode_fused<1>, dim3(grid_size((const void *)k_decode_fused<1>, 0, total, lds)),
+        COLI_LAUNCH(k_decode_fused<1>, dim3(grid_size((const void *)k_decode_fused<1>, 0, total, lds)),
                            dim3(256), lds, s, a);
     } else if (T <= 2) {
-        hipLaunchKernelGGL(k_decode_fused<2>, dim3(grid_size((const void *)k_decode_fused<2>, 1, total, lds)),
+        COLI_LAUNCH(k_decode_fused<2>, dim3(grid_size((const void *)k_decode_fused<2>, 1, total, lds)),
                            dim3(256), lds, s, a);
     } else if (T <= 4) {
-        hipLaunchKernelGGL(k_decode_fused<4>, dim3(grid_size((const void *)k_decode_fused<4>, 2, total, lds)),
+        COLI_LAUNCH(k_decode_fused<4>, dim3(grid_size((const void *)k_decode_fused<4>, 2, total, lds)),
                            dim3(256), lds, s, a);
     } else {
-        hipLaunchKernelGGL(k_decode_fused<8>, dim3(grid_size((const void *)k_decode_fused<8>, 3, total, lds)),
+        COLI_LAUNCH(k_decode_fused<8>, dim3(grid_size((const void *)k_decode_fused<8>, 3, total, lds)),
                            dim3(256), lds, s, a);
     }
     return hipGetLastError();

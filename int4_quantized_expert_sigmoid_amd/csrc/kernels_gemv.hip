@@ -43,19 +43,19 @@ __global__ void __launch_bounds__(256) k_down_gemv(GemvArgs a)
 template <int WB>
 void launch_gateup_wb(int T, dim3 grid, dim3 block, const GemvArgs &a, hipStream_t s)
 {
-    if (T <= 1) hipLaunchKernelGGL((k_gateup_gemv<1, WB>), grid, block, 0, s, a);
-    else if (T <= 2) hipLaunchKernelGGL((k_gateup_gemv<2, WB>), grid, block, 0, s, a);
-    else if (T <= 4) hipLaunchKernelGGL((k_gateup_gemv<4, WB>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((k_gateup_gemv<8, WB>), grid, block, 0, s, a);
+    if (T <= 1) COLI_LAUNCH((k_gateup_gemv<1, WB>), grid, block, 0, s, a);
+    else if (T <= 2) COLI_LAUNCH((k_gateup_gemv<2, WB>), grid, block, 0, s, a);
+    else if (T <= 4) COLI_LAUNCH((k_gateup_gemv<4, WB>), grid, block, 0, s, a);
+    else COLI_LAUNCH((k_gateup_gemv<8, WB>), grid, block, 0, s, a);
 }
 
 template <int WB>
 void launch_down_wb(int T, dim3 grid, const GemvArgs &a, hipStream_t s)
 {
-    if (T <= 1) hipLaunchKernelGGL((k_down_gemv<1, WB>), grid, dim3(256), 0, s, a);
-    else if (T <= 2) hipLaunchKernelGGL((k_down_gemv<2, WB>), grid, dim3(256), 0, s, a);
-    else if (T <= 4) hipLaunchKernelGGL((k_down_gemv<4, WB>), grid, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((k_down_gemv<8, WB>), grid, dim3(256), 0, s, a);
+    if (T <= 1) COLI_LAUNCH((k_down_gemv<1, WB>), grid, dim3(256), 0, s, a);
+    else if (T <= 2) COLI_LAUNCH((k_down_gemv<2, WB>), grid, dim3(256), 0, s, a);
+    else if (T <= 4) COLI_LAUNCH((k_down_gemv<4, WB>), grid, dim3(256), 0, s, a);
+    else COLI_LAUNCH((k_down_gemv<8, WB>), grid, dim3(256), 0, s, a);
 }
 
 GemvArgs make_args(const coli_moe_layer &L, const WsLayout &lay, char *ws)

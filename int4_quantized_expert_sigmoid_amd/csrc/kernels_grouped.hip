@@ -446,8 +446,8 @@ hipError_t launch_gateup_grouped(const coli_moe_layer &L, int T, const WsLayout 
     a.act_s = reinterpret_cast<const float *>(ws + lay.xs);
     const int nrg = (L.I / QK + WAVES - 1) / WAVES;
     const dim3 grid((unsigned)(max_tiles(lay, L) * nrg));
-    if ((L.H / QK) % KS == 0) hipLaunchKernelGGL(k_gateup_mfma<true>, grid, dim3(64 * WAVES), 0, s, a);
-    else hipLaunchKernelGGL(k_gateup_mfma<false>, grid, dim3(64 * WAVES), 0, s, a);
+    if ((L.H / QK) % KS == 0) COLI_LAUNCH(k_gateup_mfma<true>, grid, dim3(64 * WAVES), 0, s, a);
+    else COLI_LAUNCH(k_gateup_mfma<false>, grid, dim3(64 * WAVES), 0, s, a);
     return hipGetLastError();
 }
 
@@ -460,7 +460,7 @@ hipError_t launch_down_grouped(const coli_moe_layer &L, int T, const WsLayout &l
     a.act = reinterpret_cast<const int8_t *>(ws + lay.hq);
     a.act_s = reinterpret_cast<const float *>(ws + lay.hs);
     const int nrg = (L.H / QK + WAVES - 1) / WAVES;
-    hipLaunchKernelGGL(k_down_mfma, dim3((unsigned)(max_tiles(lay, L) * nrg)), dim3(64 * WAVES), 0, s, a);
+    COLI_LAUNCH(k_down_mfma, dim3((unsigned)(max_tiles(lay, L) * nrg)), dim3(64 * WAVES), 0, s, a);
     return hipGetLastError();
 }
 

@@ -224,26 +224,26 @@ inline unsigned grid_for(long n, int bs) { return (unsigned)((n + bs - 1) / bs);
 hipError_t launch_quant_q8(const float *x, int T, int H, int8_t *xq, float *xs, bool reorder, hipStream_t s)
 {
     const long nb = (long)T * (H / QK);
-    hipLaunchKernelGGL(k_quant_q8, dim3(grid_for(nb, 256)), dim3(256), 0, s, x, nb, xq, xs, reorder ? 1 : 0);
+    COLI_LAUNCH(k_quant_q8, dim3(grid_for(nb, 256)), dim3(256), 0, s, x, nb, xq, xs, reorder ? 1 : 0);
     return hipGetLastError();
 }
 
 hipError_t launch_reorder_q8(const int8_t *xq_nat, int n, int8_t *xq_perm, hipStream_t s)
 {
     const long ng = n / 8;
-    hipLaunchKernelGGL(k_reorder_q8, dim3(grid_for(ng, 256)), dim3(256), 0, s, xq_nat, ng, xq_perm);
+    COLI_LAUNCH(k_reorder_q8, dim3(grid_for(ng, 256)), dim3(256), 0, s, xq_nat, ng, xq_perm);
     return hipGetLastError();
 }
 
 hipError_t launch_pack_int4(const float *w, int rows, int cols, uint8_t *q, float *sc, hipStream_t s)
 {
-    hipLaunchKernelGGL(k_pack_int4, dim3(rows), dim3(256), 0, s, w, cols, q, sc);
+    COLI_LAUNCH(k_pack_int4, dim3(rows), dim3(256), 0, s, w, cols, q, sc);
     return hipGetLastError();
 }
 
 hipError_t launch_pack_int8(const float *w, int rows, int cols, int8_t *q, float *sc, hipStream_t s)
 {
-    hipLaunchKernelGGL(k_pack_int8, dim3(rows), dim3(256), 0, s, w, cols, q, sc);
+    COLI_LAUNCH(k_pack_int8, dim3(rows), dim3(256), 0, s, w, cols, q, sc);
     return hipGetLastError();
 }
 
@@ -254,14 +254,14 @@ hipError_t launch_rmsnorm(const float *x, const float *g, int T, int H, float ep
     threads = threads < 256 ? 256 : (threads > RMS_THREADS ? RMS_THREADS : threads);
     const auto a16 = [](const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; };
     const int aligned16 = a16(x) && a16(g) && a16(out) ? 1 : 0;
-    hipLaunchKernelGGL(k_rmsnorm, dim3(T), dim3(threads), 0, s, x, g, H, eps, out, aligned16);
+    COLI_LAUNCH(k_rmsnorm, dim3(T), dim3(threads), 0, s, x, g, H, eps, out, aligned16);
     return hipGetLastError();
 }
 
 hipError_t launch_block_dots(const uint8_t *q4, const int8_t *q8, int rows, int cols, int32_t *S, hipStream_t s)
 {
     const long n = (long)rows * (cols / QK);
-    hipLaunchKernelGGL(k_block_dots, dim3(grid_for(n, 256)), dim3(256), 0, s, q4, q8, rows, cols, S);
+    COLI_LAUNCH(k_block_dots, dim3(grid_for(n, 256)), dim3(256), 0, s, q4, q8, rows, cols, S);
     return hipGetLastError();
 }
 
@@ -271,7 +271,7 @@ hipError_t launch_zero(void *p, size_t bytes, hipStream_t s)
     size_t blocks = (n16 + 255) / 256;
     if (blocks == 0) blocks = 1;
     if (blocks > 4096) blocks = 4096;
-    hipLaunchKernelGGL(k_zero, dim3((unsigned)blocks), dim3(256), 0, s, reinterpret_cast<uint4 *>(p), n16,
+    COLI_LAUNCH(k_zero, dim3((unsigned)blocks), dim3(256), 0, s, reinterpret_cast<uint4 *>(p), n16,
                        reinterpret_cast<uint8_t *>(p) + n16 * 16, ntail);
     return hipGetLastError();
 }
@@ -281,7 +281,7 @@ hipError_t launch_copy_f32(const float *src, float *dst, size_t n, hipStream_t s
     size_t blocks = (n + 255) / 256;
     if (blocks == 0) return hipSuccess;
     if (blocks > 4096) blocks = 4096;
-    hipLaunchKernelGGL(k_copy_f32, dim3((unsigned)blocks), dim3(256), 0, s, src, dst, n);
+    COLI_LAUNCH(k_copy_f32, dim3((unsigned)blocks), dim3(256), 0, s, src, dst, n);
     return hipGetLastError();
 }
 

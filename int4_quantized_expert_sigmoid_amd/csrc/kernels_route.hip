@@ -223,16 +223,16 @@ hipError_t launch_logits(const coli_moe_layer &L, const float *x, int T, double 
             if (e != hipSuccess) return e;
         }
         const int ns = logits_splits(T, L.E, L.H);
-        hipLaunchKernelGGL(k_logits_split, dim3((T + LG_T - 1) / LG_T, (L.E + LG_E - 1) / LG_E, ns), dim3(256), 0,
+        COLI_LAUNCH(k_logits_split, dim3((T + LG_T - 1) / LG_T, (L.E + LG_E - 1) / LG_E, ns), dim3(256), 0,
                            s, L.router_w, x, T, L.H, L.E, L.H / ns, z);
     } else if (T <= 1) {
-        hipLaunchKernelGGL(k_logits_small<1>, dim3(L.E), dim3(256), 0, s, L.router_w, x, T, L.H, L.E, z, xq, xs);
+        COLI_LAUNCH(k_logits_small<1>, dim3(L.E), dim3(256), 0, s, L.router_w, x, T, L.H, L.E, z, xq, xs);
     } else if (T <= 2) {
-        hipLaunchKernelGGL(k_logits_small<2>, dim3(L.E), dim3(256), 0, s, L.router_w, x, T, L.H, L.E, z, xq, xs);
+        COLI_LAUNCH(k_logits_small<2>, dim3(L.E), dim3(256), 0, s, L.router_w, x, T, L.H, L.E, z, xq, xs);
     } else if (T <= 4) {
-        hipLaunchKernelGGL(k_logits_small<4>, dim3(L.E), dim3(256), 0, s, L.router_w, x, T, L.H, L.E, z, xq, xs);
+        COLI_LAUNCH(k_logits_small<4>, dim3(L.E), dim3(256), 0, s, L.router_w, x, T, L.H, L.E, z, xq, xs);
     } else {
-        hipLaunchKernelGGL(k_logits_small<8>, dim3(L.E), dim3(256), 0, s, L.router_w, x, T, L.H, L.E, z, xq, xs);
+        COLI_LAUNCH(k_logits_small<8>, dim3(L.E), dim3(256), 0, s, L.router_w, x, T, L.H, L.E, z, xq, xs);
     }
     return hipGetLastError();
 }
@@ -259,10 +259,10 @@ hipError_t launch_select(const coli_moe_layer &L, int T, const WsLayout &lay, ch
     a.shared_pair = reinterpret_cast<int *>(ws + lay.shared_pair);
     if (lay.path == 0) {
         const size_t lds = sel_lds_bytes(T, L.E, L.top_k, L.n_group) + union_lds_bytes(T, L.E, L.top_k);
-        hipLaunchKernelGGL(k_select_union, dim3(1), dim3(1024), lds, s, a);
+        COLI_LAUNCH(k_select_union, dim3(1), dim3(1024), lds, s, a);
         return hipGetLastError();
     }
-    hipLaunchKernelGGL(k_select_tokens, dim3(T), dim3(256), sel_lds_bytes(1, L.E, L.top_k, L.n_group), s, a);
+    COLI_LAUNCH(k_select_tokens, dim3(T), dim3(256), sel_lds_bytes(1, L.E, L.top_k, L.n_group), s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     BucketArgs b;
@@ -271,7 +271,7 @@ hipError_t launch_select(const coli_moe_layer &L, int T, const WsLayout &lay, ch
     b.pair_tok = reinterpret_cast<int *>(ws + lay.pair_tok);
     b.pair_of = a.pair_of; b.shared_pair = a.shared_pair;
     b.tiles = reinterpret_cast<int2 *>(ws + lay.tiles);
-    hipLaunchKernelGGL(k_bucket, dim3(1), dim3(1024), 0, s, b);
+    COLI_LAUNCH(k_bucket, dim3(1), dim3(1024), 0, s, b);
     return hipGetLastError();
 }
 
