@@ -148,6 +148,8 @@ class LayerSpec:
     bias_sigma: float = 0.01         # router bias ~ N(0, bias_sigma)
     zipf_s: float = 0.0              # > 0: bias -= zipf_alpha * zipf_s * ln(rank)
     zipf_alpha: float = 0.02
+    hot_experts: int = 0             # > 0: that many seeded experts get hot_bias added (chosen by every token)
+    hot_bias: float = 2.0
     weight_bits: int = 4             # packed expert format: 4 (two codes per byte) or 8
 
     @property
@@ -197,6 +199,11 @@ WORKLOADS = {
                                    TokenSpec(T=512, outlier_channels=61)),
     "glm52_chain16_T1": Workload("glm52_chain16_T1", GLM52, TokenSpec(T=1, outlier_channels=61),
                                  n_layers=16),
+    # every token on the same 8 experts (router bias +2 on a seeded set): 9
+    # experts x 512 pairs, a compute-bound grouped GEMM (about 2,000 int8
+    # ops per weight byte), where the matrix-core rate is the measure
+    "glm52_hot8_T512": Workload("glm52_hot8_T512", replace(GLM52, hot_experts=8),
+                                TokenSpec(T=512, outlier_channels=61)),
     # the same layer with int8 experts (one byte per weight), the format the
     # pages keep for the MTP head: its draft step (T=1) and a verify-sized batch
     "glm52_int8_mtp_T1": Workload("glm52_int8_mtp_T1", replace(GLM52, weight_bits=8),
@@ -227,6 +234,10 @@ def router(spec: LayerSpec, seed: int, layer: int):
     if spec.zipf_s > 0:
         rank = permutation(seed, stream_layer(layer, 3), spec.E).astype(np.float64) + 1.0
         b = (b.astype(np.float64) - spec.zipf_alpha * spec.zipf_s * np.log(rank)).astype(np.float32)
+    if spec.hot_experts > 0:
+        hot = permutation(seed, stream_layer(layer, 4), spec.E)[:spec.hot_experts]
+        b = b.copy()
+        b[hot] += np.float32(spec.hot_bias)
     return W, b
 
 

@@ -54,6 +54,27 @@ def test_grouped_tiny_full_outputs(tiny, T):
             assert np.array_equal(v["hs"][p], eo.hs)
 
 
+def test_grouped_hot_experts_full_tiles():
+    """Every token on the same experts: each expert's bucket holds all T
+    tokens (several full 32-pair tiles of one expert), the compute-bound
+    regime of the grouped GEMM."""
+    spec = S.LayerSpec(H=256, I=128, E=16, top_k=2, hot_experts=2)
+    L, ref = device_layer(spec, 0, 0), OL.full_layer(spec, 0, 0)
+    T = 100
+    x = S.tokens(S.TokenSpec(T=T, token_set=7), spec.H, 0)
+    ws = api.workspace(L, T)
+    say(f"grouped hot experts T={T}")
+    y = api.moe_forward(L, dev(x), ws).cpu().numpy()
+    y_o, idx_o, _ = O.moe_forward(ref, x)
+    assert len(np.unique(idx_o)) == 2                 # the two hot experts, for every token
+    v = ws_views(L, T, ws)
+    assert v["path"] == 1
+    assert np.array_equal(np.sort(v["idx"], axis=1), np.sort(idx_o, axis=1))
+    err = rel_err(y, y_o).max()
+    say(f"  max rel {err:.2e}, bit-identical {np.mean(y == y_o):.4f}")
+    assert err <= TOL
+
+
 # H = 320: 10 blocks per gate/up row (a part-filled last stage of 8 blocks,
 # scales loaded one by one); I = 96: 3 gate/up row tiles (a wave without
 # rows in the workgroup) and 3 down blocks (an odd last block).
