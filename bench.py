@@ -160,17 +160,16 @@ def main():
         G = 1
         x0 = torch.from_numpy(S.tokens(wl.tokens, spec.H, wl.seed)).cuda()
         xr = torch.empty_like(x0)                 # residual stream
-        xn = torch.empty_like(x0)                 # normalised layer input
         gam = [torch.from_numpy(S.rms_gamma(spec.H, wl.seed, li)).cuda() for li in range(n_inst)]
         toks = x0.cpu().numpy()
 
         def step(i, s):
             with torch.cuda.stream(s):
                 xr.copy_(x0)
-            for l in range(n_inst):
-                api.rmsnorm(xr, gam[l], wl.rms_eps, out=xn, stream=s)
-                api.moe_forward(layers[l], xn, ws[l], y=xr, flags=COLI_ACCUMULATE, stream=s, c_layer=cls[l])
-        layer_calls = lambda i: [(l, xn, xr, COLI_ACCUMULATE) for l in range(n_inst)]
+            for l in range(n_inst):      # x <- x + MoE(RMSNorm(x) * gamma): the router launch takes the norm
+                api.moe_forward_rms(layers[l], xr, gam[l], wl.rms_eps, ws[l], y=xr, flags=COLI_ACCUMULATE,
+                                    stream=s, c_layer=cls[l])
+        layer_calls = lambda i: [(l, xr, xr, COLI_ACCUMULATE) for l in range(n_inst)]
     else:
         G = n_inst                               # steps per captured graph: one per instance
         toks = S.tokens(replace(wl.tokens, T=T * G), spec.H, wl.seed)
@@ -239,9 +238,8 @@ def main():
         calls += layer_calls(i)
     evs = [api.KernelEvents(16) for _ in calls]
     for (j, xin, yout, fl), ev in zip(calls, evs):
-        if chain:
-            api.rmsnorm(xr, gam[j], wl.rms_eps, out=xn, stream=stream)
-        api.moe_forward_timed(layers[j], xin, ws[j], ev, y=yout, flags=fl, stream=stream, c_layer=cls[j])
+        api.moe_forward_timed(layers[j], xin, ws[j], ev, y=yout, flags=fl, stream=stream, c_layer=cls[j],
+                              gamma=gam[j] if chain else None, eps=wl.rms_eps)
     stream.synchronize()
     per_call = [ev.durations_ms() for ev in evs]
     label = lambda n: n.strip("()").split("<")[0]

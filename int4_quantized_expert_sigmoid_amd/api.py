@@ -135,6 +135,21 @@ def moe_forward(layer: MoELayer, x: torch.Tensor, ws: torch.Tensor, y: Optional[
     return y
 
 
+def moe_forward_rms(layer: MoELayer, x: torch.Tensor, gamma: torch.Tensor, eps: float, ws: torch.Tensor,
+                    y: Optional[torch.Tensor] = None, flags: int = 0, stream=None,
+                    c_layer: Optional[CLayer] = None) -> torch.Tensor:
+    """y (+)= MoE(RMSNorm(x) * gamma) in one call (y may be x: the residual add in place)."""
+    _dev(x, torch.float32, "x"); _dev(gamma, torch.float32, "gamma")
+    T = x.shape[0]
+    if y is None:
+        y = torch.empty_like(x)
+    cl = c_layer if c_layer is not None else layer.c()
+    check("coli_moe_forward_rms", lib().coli_moe_forward_rms(ctypes.byref(cl), _ptr(x), _ptr(gamma), eps, T,
+                                                             _ptr(y), flags, _ptr(ws), ws.numel(),
+                                                             _stream(stream)))
+    return y
+
+
 class KernelEvents:
     """Start/stop event pairs (HIP events with timing) for coli_moe_forward_timed."""
 
@@ -179,16 +194,21 @@ class KernelEvents:
 
 def moe_forward_timed(layer: MoELayer, x: torch.Tensor, ws: torch.Tensor, events: KernelEvents,
                       y: Optional[torch.Tensor] = None, flags: int = 0, stream=None,
-                      c_layer: Optional[CLayer] = None) -> torch.Tensor:
-    """moe_forward with every launch's own start/stop in `events`
-    (events.durations_ms() reads them after the stream has run)."""
+                      c_layer: Optional[CLayer] = None, gamma: Optional[torch.Tensor] = None,
+                      eps: float = 1e-6) -> torch.Tensor:
+    """moe_forward (or moe_forward_rms with gamma) with every launch's own
+    start/stop in `events` (events.durations_ms() reads them after the stream
+    has run)."""
     _dev(x, torch.float32, "x")
+    if gamma is not None:
+        _dev(gamma, torch.float32, "gamma")
     T = x.shape[0]
     if y is None:
         y = torch.empty_like(x)
     cl = c_layer if c_layer is not None else layer.c()
     check("coli_moe_forward_timed",
-          lib().coli_moe_forward_timed(ctypes.byref(cl), _ptr(x), T, _ptr(y), flags, _ptr(ws), ws.numel(),
+          lib().coli_moe_forward_timed(ctypes.byref(cl), _ptr(x), _ptr(gamma), eps, T, _ptr(y), flags, _ptr(ws),
+                                       ws.numel(),
                                        _stream(stream), events.start, events.stop, events.n,
                                        ctypes.byref(events.count), events.names))
     return y

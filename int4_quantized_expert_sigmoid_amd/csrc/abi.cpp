@@ -101,6 +101,7 @@ WsLayout make_layout(const coli_moe_layer &L, int T, int path)
     o.hq = p; p = up(p + n_pairs * I);
     o.hs = p; p = up(p + n_pairs * (I / 32) * 4);
     o.ye = p; p = up(p + n_pairs * H * 4);
+    o.xn = p; p = up(p + t * H * 4);
     o.sync = p; p = up(p + (path == 0 ? sizeof(FusedSync) : 0));
     o.total = p;
     return o;
@@ -195,8 +196,13 @@ static int run_experts(const coli_moe_layer *L, int T, const WsLayout &lay, char
     return record(ev, 5, s);
 }
 
+// gamma != nullptr: x holds raw rows, and the layer's input is their
+// RMSNorm with gains gamma and eps. The decode launches take it inside the
+// router launch; the other paths run coli_rmsnorm's kernel into the
+// workspace first.
 static int forward_impl(const coli_moe_layer *L, const float *x, int T, float *y, int flags, void *ws,
-                        size_t ws_bytes, void *stream, void *const *ev)
+                        size_t ws_bytes, void *stream, void *const *ev, const float *gamma = nullptr,
+                        float eps = 0.0f)
 {
     int path;
     WsLayout lay;
@@ -204,9 +210,16 @@ static int forward_impl(const coli_moe_layer *L, const float *x, int T, float *y
     if (rc != COLI_OK) return rc;
     if ((rc = format_ok(*L, path, flags)) != COLI_OK) return rc;
     if (!al16(x) || !al16(y)) return COLI_EINVAL;
+    if (gamma && (!al16(gamma) || !(eps >= 0.0f) || !std::isfinite(eps))) return COLI_EINVAL;
     hipStream_t s = (hipStream_t)stream;
     char *base = static_cast<char *>(ws);
     if (record(ev, 0, s)) return COLI_EDEVICE;
+    const bool norm_in_router = gamma && path == 0 && !(flags & COLI_PATH_FUSED);
+    if (gamma && !norm_in_router) {
+        float *xn = reinterpret_cast<float *>(base + lay.xn);
+        if (launch_rmsnorm(x, gamma, T, L->H, eps, xn, s) != hipSuccess) return COLI_EDEVICE;
+        x = xn;
+    }
     if (path == 0 && (flags & COLI_PATH_FUSED)) {
         if (launch_decode_fused(*L, x, T, lay, base, y, (flags & COLI_ACCUMULATE) != 0, s) != hipSuccess)
             return COLI_EDEVICE;
@@ -216,7 +229,8 @@ static int forward_impl(const coli_moe_layer *L, const float *x, int T, float *y
     }
     if (path == 0) {
         // router (+ the shared expert's gate/up), routed gate/up, down + combine
-        if (launch_decode_router(*L, x, T, lay, base, s) != hipSuccess) return COLI_EDEVICE;
+        if (launch_decode_router(*L, x, T, lay, base, norm_in_router ? gamma : nullptr, eps, s) != hipSuccess)
+            return COLI_EDEVICE;
         if (record(ev, 1, s)) return COLI_EDEVICE;
         if (launch_decode_select_gateup(*L, T, lay, base, s) != hipSuccess) return COLI_EDEVICE;
         if (record(ev, 2, s)) return COLI_EDEVICE;
@@ -267,6 +281,13 @@ int coli_moe_forward(const coli_moe_layer *L, const float *x, int T, float *y, i
     return forward_impl(L, x, T, y, flags, ws, ws_bytes, stream, nullptr);
 }
 
+int coli_moe_forward_rms(const coli_moe_layer *L, const float *x, const float *gamma, float eps, int T, float *y,
+                         int flags, void *ws, size_t ws_bytes, void *stream)
+{
+    if (!gamma) return COLI_EINVAL;
+    return forward_impl(L, x, T, y, flags, ws, ws_bytes, stream, nullptr, gamma, eps);
+}
+
 int coli_moe_forward_profiled(const coli_moe_layer *L, const float *x, int T, float *y, int flags, void *ws,
                               size_t ws_bytes, void *stream, void *const *events, int n_events)
 {
@@ -276,9 +297,9 @@ int coli_moe_forward_profiled(const coli_moe_layer *L, const float *x, int T, fl
     return forward_impl(L, x, T, y, flags, ws, ws_bytes, stream, events);
 }
 
-int coli_moe_forward_timed(const coli_moe_layer *L, const float *x, int T, float *y, int flags, void *ws,
-                           size_t ws_bytes, void *stream, void *const *start, void *const *stop, int n_pairs,
-                           int *n_launches, const char **names)
+int coli_moe_forward_timed(const coli_moe_layer *L, const float *x, const float *gamma, float eps, int T, float *y,
+                           int flags, void *ws, size_t ws_bytes, void *stream, void *const *start,
+                           void *const *stop, int n_pairs, int *n_launches, const char **names)
 {
     if (!n_launches || n_pairs < 0 || (n_pairs > 0 && (!start || !stop))) return COLI_EINVAL;
     for (int i = 0; i < n_pairs; ++i)
@@ -288,7 +309,7 @@ int coli_moe_forward_timed(const coli_moe_layer *L, const float *x, int T, float
     KernelTimer *&slot = kernel_timer();
     KernelTimer *const prev = slot;
     slot = &kt;
-    const int rc = forward_impl(L, x, T, y, flags, ws, ws_bytes, stream, nullptr);
+    const int rc = forward_impl(L, x, T, y, flags, ws, ws_bytes, stream, nullptr, gamma, eps);
     slot = prev;
     *n_launches = kt.next;
     return rc;

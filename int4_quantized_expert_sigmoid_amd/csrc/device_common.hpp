@@ -162,14 +162,8 @@ __device__ __forceinline__ void q8_scale(float amax, float &d, float &id)
 
 // Q8 of one 32-wide activation block into registers in the reordered layout:
 // the Q8_0-style rule d = absmax/127, codes rint(x * (1/d)) clamped to +-127.
-__device__ __forceinline__ void q8_block_regs(const float *__restrict__ src, uint32_t (&o)[8], float &dsc)
+__device__ __forceinline__ void q8_block_vals(const float (&v)[QK], uint32_t (&o)[8], float &dsc)
 {
-    float v[QK];
-#pragma unroll
-    for (int i = 0; i < QK / 4; ++i) {
-        const float4 f = reinterpret_cast<const float4 *>(src)[i];
-        v[4 * i] = f.x; v[4 * i + 1] = f.y; v[4 * i + 2] = f.z; v[4 * i + 3] = f.w;
-    }
     float amax = 0.0f;
 #pragma unroll
     for (int i = 0; i < QK; ++i) amax = fmaxf(amax, fabsf(v[i]));
@@ -184,6 +178,18 @@ __device__ __forceinline__ void q8_block_regs(const float *__restrict__ src, uin
         o[2 * m + 1] = (uint32_t)(c[8 * m + 1] | (c[8 * m + 3] << 8) | (c[8 * m + 5] << 16) | (c[8 * m + 7] << 24));
     }
     dsc = d;
+}
+
+// The same from memory (16-byte aligned block).
+__device__ __forceinline__ void q8_block_regs(const float *__restrict__ src, uint32_t (&o)[8], float &dsc)
+{
+    float v[QK];
+#pragma unroll
+    for (int i = 0; i < QK / 4; ++i) {
+        const float4 f = reinterpret_cast<const float4 *>(src)[i];
+        v[4 * i] = f.x; v[4 * i + 1] = f.y; v[4 * i + 2] = f.z; v[4 * i + 3] = f.w;
+    }
+    q8_block_vals(v, o, dsc);
 }
 
 __device__ __forceinline__ void q8_block_reordered(const float *__restrict__ src, int8_t *__restrict__ dst,
@@ -309,5 +315,59 @@ __device__ __forceinline__ int transpose_index(int lane) { return (lane >> (6 - 
 
 // Sigmoid-weighted linear unit on f64 inputs: silu(g) = g / (1 + exp(-g)).
 __device__ __forceinline__ double silu_f64(double g) { return g / (1.0 + exp(-g)); }
+
+// RMSNorm scales of T <= NT token rows (the chain's glue: colibri
+// architecture overview, section 4, rmsnorm among the kernels). Every
+// workgroup that needs a row's scale takes it in this one order, so all of
+// them agree bit for bit: RMS_BLOCK threads, thread j summing the f64 squares
+// of its float4s j, j + RMS_BLOCK, ... (components x, y, z, w), or of its
+// elements j, j + RMS_BLOCK, ... when !vec; a wave sum; the wave sums in wave
+// order. scale = 1 / sqrt(sum / H + eps) in f64, and a normalised element is
+// (float)((double)x * scale * (double)gamma). vec: x 16-byte aligned and
+// H % 4 == 0. All RMS_BLOCK threads call it; red holds 8 * NT doubles.
+constexpr int RMS_BLOCK = 512;
+
+template <int NT>
+__device__ __forceinline__ void rms_scales(const float *__restrict__ x, int T, int H, float eps, bool vec,
+                                           double *red, double (&scale)[NT])
+{
+    double ss[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+        ss[t] = 0.0;
+        if (t < T) {
+            const float *xt = x + (long)t * H;
+            if (vec) {
+                for (int i = threadIdx.x; i < H / 4; i += RMS_BLOCK) {
+                    const float4 v = reinterpret_cast<const float4 *>(xt)[i];
+                    ss[t] += (double)v.x * (double)v.x;
+                    ss[t] += (double)v.y * (double)v.y;
+                    ss[t] += (double)v.z * (double)v.z;
+                    ss[t] += (double)v.w * (double)v.w;
+                }
+            } else {
+                for (int i = threadIdx.x; i < H; i += RMS_BLOCK) ss[t] += (double)xt[i] * (double)xt[i];
+            }
+        }
+    }
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+        const double v = wave_sum(ss[t]);
+        if ((threadIdx.x & 63) == 0) red[(threadIdx.x >> 6) * NT + t] = v;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+        double v = red[t];
+        for (int w = 1; w < RMS_BLOCK / 64; ++w) v += red[w * NT + t];
+        scale[t] = 1.0 / sqrt(v / (double)H + (double)eps);
+    }
+    __syncthreads();
+}
+
+__device__ __forceinline__ float rms_apply(float x, double scale, float g)
+{
+    return (float)((double)x * scale * (double)g);
+}
 
 } // namespace coli

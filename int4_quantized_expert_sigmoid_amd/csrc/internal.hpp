@@ -46,6 +46,7 @@ struct WsLayout {
     size_t pair_of, shared_pair;
     size_t pair_tok, expert_off, tiles;          // grouped path buckets and tile list
     size_t h, hq, hs, ye;
+    size_t xn;                                   // [T][H] f32: the RMSNorm of raw rows (coli_moe_forward_rms off the decode launches)
     size_t sync;                                 // FusedSync (GEMV path)
     size_t total;
 };
@@ -73,6 +74,9 @@ hipError_t launch_reorder_q8(const int8_t *xq_nat, int n, int8_t *xq_perm, hipSt
 hipError_t launch_pack_int4(const float *w, int rows, int cols, uint8_t *q, float *sc, hipStream_t s);
 hipError_t launch_pack_int8(const float *w, int rows, int cols, int8_t *q, float *sc, hipStream_t s);
 hipError_t launch_rmsnorm(const float *x, const float *g, int T, int H, float eps, float *out, hipStream_t s);
+// The float4 order of the RMSNorm sums (x 16-byte aligned, H % 4 == 0): the
+// same rule wherever a row's scale is taken.
+inline bool rms_vec(const float *x, int H) { return (reinterpret_cast<uintptr_t>(x) & 15u) == 0 && H % 4 == 0; }
 hipError_t launch_block_dots(const uint8_t *q4, const int8_t *q8, int rows, int cols, int32_t *S, hipStream_t s);
 hipError_t launch_zero(void *p, size_t bytes, hipStream_t s);
 hipError_t launch_copy_f32(const float *src, float *dst, size_t n, hipStream_t s);
@@ -102,8 +106,10 @@ hipError_t launch_down_gemv(const coli_moe_layer &L, int T, const WsLayout &lay,
 // ---- decode / verify layer in three launches (kernels_decode.hip), T <= 8:
 // router logits + keys + Q8(x); shared gate/up beside per-workgroup
 // top-k/union + routed gate/up; down of every item + combine into y.
+// gamma != nullptr: x holds raw rows and the launch takes their RMSNorm
+// (gains gamma, eps) first (H <= 8192).
 hipError_t launch_decode_router(const coli_moe_layer &L, const float *x, int T, const WsLayout &lay, char *ws,
-                                hipStream_t s);
+                                const float *gamma, float eps, hipStream_t s);
 hipError_t launch_decode_select_gateup(const coli_moe_layer &L, int T, const WsLayout &lay, char *ws, hipStream_t s);
 hipError_t launch_decode_down_combine(const coli_moe_layer &L, int T, const WsLayout &lay, char *ws, float *y,
                                       bool accumulate, hipStream_t s);   // T <= 2

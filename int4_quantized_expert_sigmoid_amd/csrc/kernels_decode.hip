@@ -62,6 +62,9 @@ namespace {
 // ------------------------------------------------------------ launch 1
 struct RouterArgs {
     const float *W, *bias, *x;
+    const float *gamma;        // RMSNorm gains of the norm-fused router (x is then the raw residual row)
+    float eps;
+    int vec;                   // rms_vec(x, H)
     int T, H, E;
     double *z, *key, *sig;
     int8_t *xq;
@@ -80,6 +83,76 @@ __global__ void __launch_bounds__(512) k_router(RouterArgs r)
     for (long b = (long)blockIdx.x * blockDim.x + threadIdx.x; b < nb; b += (long)r.E * blockDim.x)
         q8_block_reordered(r.x + b * QK, r.xq + b * QK, r.xs + b);
     logits_expert<NT>(r.W, r.x, r.T, r.H, r.E, blockIdx.x, r.z, red, r.bias, r.key, r.sig);
+    TRACE(r, 0, 2);
+}
+
+// Launch 1 with the chain's RMSNorm folded in: every workgroup takes the
+// scales of the T raw rows itself (rms_scales, the order k_rmsnorm uses, so
+// the normalised rows are the ones coli_rmsnorm writes), then the logits of
+// its expert and its share of Q8 from the normalised rows. The workgroup's
+// router row is loaded before the scales are taken, so the two loads
+// overlap. Needs H <= 4 * RMS_BLOCK * 4.
+constexpr int RN_PRE = 4;      // float4 of the router row per thread
+
+template <int NT>
+__global__ void __launch_bounds__(RMS_BLOCK) k_router_norm(RouterArgs r)
+{
+    typedef float f32x4 __attribute__((ext_vector_type(4)));
+    __shared__ double red[8 * NT];
+    const int e = blockIdx.x, tid = threadIdx.x;
+    TRACE(r, 0, 0);
+    const int H4 = r.H / 4;
+    const f32x4 *we = reinterpret_cast<const f32x4 *>(r.W + (long)e * r.H);
+    f32x4 wp[RN_PRE];
+#pragma unroll
+    for (int j = 0; j < RN_PRE; ++j) {
+        const int i = tid + j * RMS_BLOCK;
+        wp[j] = i < H4 ? __builtin_nontemporal_load(&we[i]) : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    double sc[NT];
+    rms_scales<NT>(r.x, r.T, r.H, r.eps, r.vec != 0, red, sc);
+
+    // Q8 of the normalised rows, the workgroups sharing the blocks
+    const int nblk = r.H / QK;
+    const long nb = (long)r.T * nblk;
+    for (long b = (long)e * RMS_BLOCK + tid; b < nb; b += (long)r.E * RMS_BLOCK) {
+        const int t = (int)(b / nblk), c0 = (int)(b % nblk) * QK;
+        float v[QK];
+        double st = sc[0];
+#pragma unroll
+        for (int k = 1; k < NT; ++k) st = t == k ? sc[k] : st;
+#pragma unroll
+        for (int i = 0; i < QK; ++i) v[i] = rms_apply(r.x[(long)t * r.H + c0 + i], st, r.gamma[c0 + i]);
+        uint32_t o[8];
+        float d;
+        q8_block_vals(v, o, d);
+        reinterpret_cast<uint4 *>(r.xq + b * QK)[0] = make_uint4(o[0], o[1], o[2], o[3]);
+        reinterpret_cast<uint4 *>(r.xq + b * QK)[1] = make_uint4(o[4], o[5], o[6], o[7]);
+        r.xs[b] = d;
+    }
+
+    // logits of expert e from the normalised rows, summed in logits_expert's order
+    double acc[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[t] = 0.0;
+#pragma unroll
+    for (int j = 0; j < RN_PRE; ++j) {
+        const int h = tid + j * RMS_BLOCK;
+        if (h < H4) {
+            const float4 g = reinterpret_cast<const float4 *>(r.gamma)[h];
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                if (t < r.T) {
+                    const float4 xv = reinterpret_cast<const float4 *>(r.x + (long)t * r.H)[h];
+                    acc[t] = fma((double)wp[j].x, (double)rms_apply(xv.x, sc[t], g.x), acc[t]);
+                    acc[t] = fma((double)wp[j].y, (double)rms_apply(xv.y, sc[t], g.y), acc[t]);
+                    acc[t] = fma((double)wp[j].z, (double)rms_apply(xv.z, sc[t], g.z), acc[t]);
+                    acc[t] = fma((double)wp[j].w, (double)rms_apply(xv.w, sc[t], g.w), acc[t]);
+                }
+            }
+        }
+    }
+    logits_finish<NT>(acc, r.T, r.E, e, r.z, red, r.bias, r.key, r.sig);
     TRACE(r, 0, 2);
 }
 
@@ -351,10 +424,11 @@ hipError_t launch_dn_nt(const coli_moe_layer &L, const WsLayout &lay, const DnAr
 } // namespace
 
 hipError_t launch_decode_router(const coli_moe_layer &L, const float *x, int T, const WsLayout &lay, char *ws,
-                                hipStream_t s)
+                                const float *gamma, float eps, hipStream_t s)
 {
     RouterArgs r;
     r.W = L.router_w; r.bias = L.router_b; r.x = x;
+    r.gamma = gamma; r.eps = eps; r.vec = rms_vec(x, L.H) ? 1 : 0;
     r.T = T; r.H = L.H; r.E = L.E;
     r.z = reinterpret_cast<double *>(ws + lay.logits);
     r.key = reinterpret_cast<double *>(ws + lay.keys);
@@ -365,6 +439,13 @@ hipError_t launch_decode_router(const coli_moe_layer &L, const float *x, int T, 
     r.trace = g_dec_trace;
 #endif
     const dim3 grid((unsigned)L.E);
+    if (gamma) {
+        if (T <= 1) COLI_LAUNCH(k_router_norm<1>, grid, dim3(RMS_BLOCK), 0, s, r);
+        else if (T <= 2) COLI_LAUNCH(k_router_norm<2>, grid, dim3(RMS_BLOCK), 0, s, r);
+        else if (T <= 4) COLI_LAUNCH(k_router_norm<4>, grid, dim3(RMS_BLOCK), 0, s, r);
+        else COLI_LAUNCH(k_router_norm<8>, grid, dim3(RMS_BLOCK), 0, s, r);
+        return hipGetLastError();
+    }
     if (T <= 1) COLI_LAUNCH(k_router<1>, grid, dim3(512), 0, s, r);
     else if (T <= 2) COLI_LAUNCH(k_router<2>, grid, dim3(512), 0, s, r);
     else if (T <= 4) COLI_LAUNCH(k_router<4>, grid, dim3(512), 0, s, r);

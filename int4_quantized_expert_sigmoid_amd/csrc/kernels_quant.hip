@@ -118,65 +118,19 @@ __global__ void __launch_bounds__(256) k_pack_int8(const float *__restrict__ w, 
     if (threadIdx.x == 0) sc[row] = d;
 }
 
-// One workgroup per token; mean of squares in f64.
-// One workgroup per token. With 16-byte aligned x, gamma and out, H a
-// multiple of 4 and at most 4 float4 per thread, x and gamma are loaded once, all at the start, and kept in
-// registers between the sum of squares and the scaling; otherwise the
-// element loops run twice.
-constexpr int RMS_THREADS = 1024, RMS_V4 = 4;
-
-__global__ void __launch_bounds__(RMS_THREADS) k_rmsnorm(const float *__restrict__ x, const float *__restrict__ g,
-                                                         int H, float eps, float *__restrict__ out, int aligned16)
+// One workgroup of RMS_BLOCK threads per token: the row's scale as
+// rms_scales takes it (so a router launch that normalises its own input
+// agrees with this kernel bit for bit), then the scaled row.
+__global__ void __launch_bounds__(RMS_BLOCK) k_rmsnorm(const float *__restrict__ x, const float *__restrict__ g,
+                                                       int H, float eps, float *__restrict__ out, int vec)
 {
-    __shared__ double red[RMS_THREADS / 64];
+    __shared__ double red[RMS_BLOCK / 64];
     const long t = blockIdx.x;
     const float *xt = x + t * (long)H;
     float *ot = out + t * (long)H;
-    const bool vec = aligned16 && (H % 4 == 0) && H <= 4 * RMS_V4 * (int)blockDim.x;
-    float4 xv[RMS_V4], gv[RMS_V4];
-    double ss = 0.0;
-    if (vec) {
-        const int n4 = H / 4;
-#pragma unroll
-        for (int j = 0; j < RMS_V4; ++j) {
-            const int i = threadIdx.x + j * blockDim.x;
-            xv[j] = i < n4 ? reinterpret_cast<const float4 *>(xt)[i] : make_float4(0.f, 0.f, 0.f, 0.f);
-            gv[j] = i < n4 ? reinterpret_cast<const float4 *>(g)[i] : make_float4(0.f, 0.f, 0.f, 0.f);
-        }
-#pragma unroll
-        for (int j = 0; j < RMS_V4; ++j) {
-            ss += (double)xv[j].x * (double)xv[j].x;
-            ss += (double)xv[j].y * (double)xv[j].y;
-            ss += (double)xv[j].z * (double)xv[j].z;
-            ss += (double)xv[j].w * (double)xv[j].w;
-        }
-    } else {
-        for (int i = threadIdx.x; i < H; i += blockDim.x) ss += (double)xt[i] * (double)xt[i];
-    }
-    ss = wave_sum(ss);
-    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
-    __syncthreads();
-    ss = red[0];
-    for (int i = 1; i < (int)(blockDim.x >> 6); ++i) ss += red[i];
-    const double r = 1.0 / sqrt(ss / (double)H + (double)eps);
-    __syncthreads();   // every thread has read x and red[] before out may overwrite x
-    if (vec) {
-        const int n4 = H / 4;
-#pragma unroll
-        for (int j = 0; j < RMS_V4; ++j) {
-            const int i = threadIdx.x + j * blockDim.x;
-            if (i < n4) {
-                float4 o;
-                o.x = (float)((double)xv[j].x * r * (double)gv[j].x);
-                o.y = (float)((double)xv[j].y * r * (double)gv[j].y);
-                o.z = (float)((double)xv[j].z * r * (double)gv[j].z);
-                o.w = (float)((double)xv[j].w * r * (double)gv[j].w);
-                reinterpret_cast<float4 *>(ot)[i] = o;
-            }
-        }
-    } else {
-        for (int i = threadIdx.x; i < H; i += blockDim.x) ot[i] = (float)((double)xt[i] * r * (double)g[i]);
-    }
+    double sc[1];
+    rms_scales<1>(xt, 1, H, eps, vec != 0, red, sc);   // ends with a barrier: x is read before out is written
+    for (int i = threadIdx.x; i < H; i += RMS_BLOCK) ot[i] = rms_apply(xt[i], sc[0], g[i]);
 }
 
 // S[r][b] for one (row, block) per thread with the layer's block-dot function.
@@ -249,12 +203,7 @@ hipError_t launch_pack_int8(const float *w, int rows, int cols, int8_t *q, float
 
 hipError_t launch_rmsnorm(const float *x, const float *g, int T, int H, float eps, float *out, hipStream_t s)
 {
-    // enough threads that each holds at most one float4 of a 6144-wide row
-    int threads = ((H / 4 + 63) / 64) * 64;
-    threads = threads < 256 ? 256 : (threads > RMS_THREADS ? RMS_THREADS : threads);
-    const auto a16 = [](const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; };
-    const int aligned16 = a16(x) && a16(g) && a16(out) ? 1 : 0;
-    COLI_LAUNCH(k_rmsnorm, dim3(T), dim3(threads), 0, s, x, g, H, eps, out, aligned16);
+    COLI_LAUNCH(k_rmsnorm, dim3(T), dim3(RMS_BLOCK), 0, s, x, g, H, eps, out, rms_vec(x, H) ? 1 : 0);
     return hipGetLastError();
 }
 

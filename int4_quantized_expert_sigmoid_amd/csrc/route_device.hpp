@@ -25,6 +25,35 @@ namespace coli {
 constexpr int MAX_E = 512;
 constexpr int SEL_T = 8;            // tokens one selection workgroup handles
 
+// The workgroup's per-thread logit partials of expert e summed: wave sums,
+// then the waves in order; z (and the selection key s + b and s = sigmoid(z))
+// written for each token.
+template <int NT>
+__device__ __forceinline__ void logits_finish(const double (&acc)[NT], int T, int E, int e, double *__restrict__ z,
+                                              double *red, const float *__restrict__ bias,
+                                              double *__restrict__ key, double *__restrict__ sig)
+{
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+        const double v = wave_sum(acc[t]);
+        if ((threadIdx.x & 63) == 0) red[(threadIdx.x >> 6) * NT + t] = v;
+    }
+    __syncthreads();
+    if (threadIdx.x < (unsigned)T && threadIdx.x < NT) {
+        const int t = threadIdx.x;
+        double v = red[t];
+        for (int w = 1; w < (int)(blockDim.x >> 6); ++w) v += red[w * NT + t];
+        st_dev(z + (long)t * E + e, v);
+        if (key) {
+            // the selection key of the sigmoid router: s = sigmoid(z), key = s + b
+            const double sg = 1.0 / (1.0 + exp(-v));
+            st_dev(key + (long)t * E + e, sg + (double)bias[e]);
+            st_dev(sig + (long)t * E + e, sg);
+        }
+    }
+    __syncthreads();
+}
+
 // Logits of one expert for T <= NT tokens by the whole workgroup (blockDim a
 // multiple of 64): float4 loads, f64 FMAs, wave sums, then the waves in
 // order. Writes z[t][e] and, with key != nullptr, the selection key s + b and
@@ -55,25 +84,7 @@ __device__ __forceinline__ void logits_expert(const float *__restrict__ W, const
             }
         }
     }
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-        const double v = wave_sum(acc[t]);
-        if ((threadIdx.x & 63) == 0) red[(threadIdx.x >> 6) * NT + t] = v;
-    }
-    __syncthreads();
-    if (threadIdx.x < (unsigned)T && threadIdx.x < NT) {
-        const int t = threadIdx.x;
-        double v = red[t];
-        for (int w = 1; w < (int)(blockDim.x >> 6); ++w) v += red[w * NT + t];
-        st_dev(z + (long)t * E + e, v);
-        if (key) {
-            // the selection key of the sigmoid router: s = sigmoid(z), key = s + b
-            const double sg = 1.0 / (1.0 + exp(-v));
-            st_dev(key + (long)t * E + e, sg + (double)bias[e]);
-            st_dev(sig + (long)t * E + e, sg);
-        }
-    }
-    __syncthreads();
+    logits_finish<NT>(acc, T, E, e, z, red, bias, key, sig);
 }
 
 struct SelShared;

@@ -100,6 +100,20 @@ def test_forward_argument_errors_before_launch():
     assert D(p, p, 4, 48, p, None) == _lib.COLI_EINVAL
 
 
+def test_rms_forward_argument_errors_before_launch():
+    L = fake_layer()
+    p = ctypes.c_void_p(1 << 20)
+    R = lib().coli_moe_forward_rms
+    f = ctypes.c_float
+    assert R(ctypes.byref(L), p, None, f(1e-6), 1, p, 0, p, 1 << 30, None) == _lib.COLI_EINVAL      # no gamma
+    assert R(ctypes.byref(L), p, ctypes.c_void_p((1 << 20) + 4), f(1e-6), 1, p, 0, p, 1 << 30, None) \
+        == _lib.COLI_EINVAL                                                                      # misaligned gamma
+    assert R(ctypes.byref(L), p, p, f(-1.0), 1, p, 0, p, 1 << 30, None) == _lib.COLI_EINVAL         # eps < 0
+    assert R(ctypes.byref(L), p, p, f(float("nan")), 1, p, 0, p, 1 << 30, None) == _lib.COLI_EINVAL
+    assert R(ctypes.byref(L), p, p, f(1e-6), 0, p, 0, p, 1 << 30, None) == _lib.COLI_EINVAL         # T = 0
+    assert R(ctypes.byref(L), p, p, f(1e-6), 1, p, 0, p, 100, None) == _lib.COLI_EWORKSPACE
+
+
 def test_timed_forward_argument_errors_before_launch():
     L = fake_layer()
     p = ctypes.c_void_p(1 << 20)
@@ -107,14 +121,14 @@ def test_timed_forward_argument_errors_before_launch():
     ev = (ctypes.c_void_p * 4)(*([1 << 20] * 4))           # non-null stand-ins: nothing is launched
     nul = (ctypes.c_void_p * 4)(1 << 20, None, 1 << 20, 1 << 20)
     n = ctypes.c_int(-7)
-    assert TM(ctypes.byref(L), p, 1, p, 0, p, 1 << 30, None, ev, ev, 4, None, None) == _lib.COLI_EINVAL
-    assert TM(ctypes.byref(L), p, 1, p, 0, p, 1 << 30, None, ev, ev, -1, ctypes.byref(n), None) == _lib.COLI_EINVAL
-    assert TM(ctypes.byref(L), p, 1, p, 0, p, 1 << 30, None, ev, nul, 4, ctypes.byref(n), None) == _lib.COLI_EINVAL
-    assert TM(ctypes.byref(L), p, 1, p, 0, p, 1 << 30, None, None, None, 2, ctypes.byref(n), None) == _lib.COLI_EINVAL
+    assert TM(ctypes.byref(L), p, None, ctypes.c_float(0.0), 1, p, 0, p, 1 << 30, None, ev, ev, 4, None, None) == _lib.COLI_EINVAL
+    assert TM(ctypes.byref(L), p, None, ctypes.c_float(0.0), 1, p, 0, p, 1 << 30, None, ev, ev, -1, ctypes.byref(n), None) == _lib.COLI_EINVAL
+    assert TM(ctypes.byref(L), p, None, ctypes.c_float(0.0), 1, p, 0, p, 1 << 30, None, ev, nul, 4, ctypes.byref(n), None) == _lib.COLI_EINVAL
+    assert TM(ctypes.byref(L), p, None, ctypes.c_float(0.0), 1, p, 0, p, 1 << 30, None, None, None, 2, ctypes.byref(n), None) == _lib.COLI_EINVAL
     # a layer call rejected before launching: no launch counted
-    assert TM(ctypes.byref(L), p, 0, p, 0, p, 1 << 30, None, ev, ev, 4, ctypes.byref(n), None) == _lib.COLI_EINVAL
+    assert TM(ctypes.byref(L), p, None, ctypes.c_float(0.0), 0, p, 0, p, 1 << 30, None, ev, ev, 4, ctypes.byref(n), None) == _lib.COLI_EINVAL
     assert n.value == 0
-    assert TM(ctypes.byref(L), p, 1, p, 0, p, 100, None, ev, ev, 4, ctypes.byref(n), None) == _lib.COLI_EWORKSPACE
+    assert TM(ctypes.byref(L), p, None, ctypes.c_float(0.0), 1, p, 0, p, 100, None, ev, ev, 4, ctypes.byref(n), None) == _lib.COLI_EWORKSPACE
     assert n.value == 0
 
 

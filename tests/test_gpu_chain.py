@@ -31,7 +31,8 @@ def gpu():
     torch.cuda.set_device(0)
 
 
-def test_sixteen_layer_chain_free_running():
+@pytest.mark.parametrize("one_call", [False, True], ids=["norm_then_forward", "forward_rms"])
+def test_sixteen_layer_chain_free_running(one_call):
     spec = S.GLM52
     wl = S.WORKLOADS["glm52_chain16_T1"]
     x0 = S.tokens(wl.tokens, spec.H, wl.seed)                # [1, H]
@@ -43,8 +44,11 @@ def test_sixteen_layer_chain_free_running():
         L = device_layer(spec, wl.seed, li)
         g = S.rms_gamma(spec.H, wl.seed, li)
         ws = api.workspace(L, 1)
-        xn = api.rmsnorm(xd, dev(g), wl.rms_eps)
-        api.moe_forward(L, xn, ws, y=xd, flags=COLI_ACCUMULATE)
+        if one_call:                                      # the router launch takes the norm itself
+            api.moe_forward_rms(L, xd, dev(g), wl.rms_eps, ws, y=xd, flags=COLI_ACCUMULATE)
+        else:
+            xn = api.rmsnorm(xd, dev(g), wl.rms_eps)
+            api.moe_forward(L, xn, ws, y=xd, flags=COLI_ACCUMULATE)
         v = ws_views(L, 1, ws)
         x_gpu = xd.cpu().numpy()[0]
 
