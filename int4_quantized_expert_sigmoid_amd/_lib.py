@@ -17,7 +17,8 @@ COLI_ACCUMULATE, COLI_PATH_GEMV, COLI_PATH_GROUPED, COLI_PATH_FUSED = 1, 2, 4, 8
 COLI_GEMV_MAX_T, COLI_MAX_T, COLI_MAX_TOPK, COLI_PROFILE_EVENTS = 8, 65536, 16, 6
 
 EXPORTS = ("coli_quant_act_q8", "coli_moe_workspace_bytes", "coli_moe_workspace_init",
-           "coli_moe_route", "coli_moe_forward", "coli_moe_forward_profiled", "coli_moe_forward_timed", "coli_moe_forward_rms", "coli_moe_experts", "coli_moe_workspace_layout",
+           "coli_moe_route", "coli_moe_forward", "coli_moe_forward_profiled", "coli_moe_forward_timed", "coli_moe_forward_rms",
+           "coli_dense_workspace_bytes", "coli_dense_forward", "coli_moe_experts", "coli_moe_workspace_layout",
            "coli_rmsnorm", "coli_pack_int4_rows", "coli_pack_int4_rows_dev", "coli_pack_int8_rows",
            "coli_pack_int8_rows_dev", "coli_debug_block_dots", "coli_version")
 
@@ -39,6 +40,13 @@ class CLayer(ctypes.Structure):
                 ("gate_q", ctypes.c_void_p), ("up_q", ctypes.c_void_p), ("down_q", ctypes.c_void_p),
                 ("gate_s", ctypes.c_void_p), ("up_s", ctypes.c_void_p), ("down_s", ctypes.c_void_p),
                 ("weight_bits", ctypes.c_int32)]
+
+
+class CDense(ctypes.Structure):
+    """Mirror of struct coli_dense_mlp."""
+    _fields_ = [("H", ctypes.c_int32), ("I", ctypes.c_int32), ("weight_bits", ctypes.c_int32),
+                ("gate_q", ctypes.c_void_p), ("up_q", ctypes.c_void_p), ("down_q", ctypes.c_void_p),
+                ("gate_s", ctypes.c_void_p), ("up_s", ctypes.c_void_p), ("down_s", ctypes.c_void_p)]
 
 
 class CWsLayout(ctypes.Structure):
@@ -67,6 +75,8 @@ def lib():
             "coli_moe_forward": ([LP, P, i, P, i, P, sz, P], i),
             "coli_moe_forward_profiled": ([LP, P, i, P, i, P, sz, P, ctypes.POINTER(P), i], i),
             "coli_moe_forward_rms": ([LP, P, P, f, i, P, i, P, sz, P], i),
+            "coli_dense_workspace_bytes": ([ctypes.POINTER(CDense), i], sz),
+            "coli_dense_forward": ([ctypes.POINTER(CDense), P, P, f, i, P, i, P, sz, P], i),
             "coli_moe_forward_timed": ([LP, P, P, f, i, P, i, P, sz, P, ctypes.POINTER(P), ctypes.POINTER(P), i,
                                         ctypes.POINTER(i), ctypes.POINTER(ctypes.c_char_p)], i),
             "coli_moe_experts": ([LP, P, P, P, P, i, P, i, P, sz, P], i),

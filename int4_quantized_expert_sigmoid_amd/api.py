@@ -13,7 +13,8 @@ from typing import Optional, Tuple
 import numpy as np
 import torch
 
-from ._lib import (CLayer, CWsLayout, COLI_ACCUMULATE, COLI_PATH_GEMV, COLI_PATH_GROUPED, ColiError,
+from . import _lib
+from ._lib import (CDense, CLayer, CWsLayout, COLI_ACCUMULATE, COLI_PATH_GEMV, COLI_PATH_GROUPED, ColiError,
                    check, lib)
 
 
@@ -76,6 +77,64 @@ class MoELayer:
     @property
     def expert_bytes(self) -> int:
         return 3 * self.H * self.I * self.weight_bits // 8 + 4 * (2 * self.I + self.H)
+
+
+@dataclass
+class DenseMLP:
+    """Device tensors of one dense SwiGLU MLP plus the C struct that points at them."""
+    H: int
+    I: int
+    gate_q: torch.Tensor     # [I][H/2] u8 (int4) or [I][H] i8 (int8)
+    up_q: torch.Tensor
+    down_q: torch.Tensor     # [H][I/2] u8 (int4) or [H][I] i8 (int8)
+    gate_s: torch.Tensor     # [I] f32
+    up_s: torch.Tensor
+    down_s: torch.Tensor     # [H] f32
+    weight_bits: int = 4
+
+    @classmethod
+    def empty(cls, H, I, device="cuda", weight_bits=4):
+        f32 = torch.float32
+        qt, div = (torch.int8, 1) if weight_bits == 8 else (torch.uint8, 2)
+        return cls(H, I, torch.empty((I, H // div), dtype=qt, device=device),
+                   torch.empty((I, H // div), dtype=qt, device=device),
+                   torch.empty((H, I // div), dtype=qt, device=device),
+                   torch.empty(I, dtype=f32, device=device), torch.empty(I, dtype=f32, device=device),
+                   torch.empty(H, dtype=f32, device=device), weight_bits)
+
+    def c(self) -> CDense:
+        return CDense(self.H, self.I, self.weight_bits, *(t.data_ptr() for t in (
+            self.gate_q, self.up_q, self.down_q, self.gate_s, self.up_s, self.down_s)))
+
+    @property
+    def nbytes(self) -> int:
+        return 3 * self.H * self.I * self.weight_bits // 8 + 4 * (2 * self.I + self.H)
+
+
+def dense_workspace(mlp: DenseMLP, T: int, stream=None) -> torch.Tensor:
+    cm = mlp.c()
+    n = lib().coli_dense_workspace_bytes(ctypes.byref(cm), T)
+    if n == 0:
+        raise ColiError("coli_dense_workspace_bytes", _lib.COLI_EINVAL)
+    ws = torch.empty(n, dtype=torch.uint8, device=mlp.gate_q.device)
+    check("coli_moe_workspace_init", lib().coli_moe_workspace_init(_ptr(ws), n, _stream(stream)))
+    return ws
+
+
+def dense_forward(mlp: DenseMLP, x: torch.Tensor, ws: torch.Tensor, y: Optional[torch.Tensor] = None,
+                  flags: int = 0, gamma: Optional[torch.Tensor] = None, eps: float = 1e-6, stream=None,
+                  c_mlp: Optional[CDense] = None) -> torch.Tensor:
+    """y (+)= MLP(x), or MLP(RMSNorm(x) * gamma) when gamma is given (y may be x)."""
+    _dev(x, torch.float32, "x")
+    if gamma is not None:
+        _dev(gamma, torch.float32, "gamma")
+    T = x.shape[0]
+    if y is None:
+        y = torch.empty_like(x)
+    cm = c_mlp if c_mlp is not None else mlp.c()
+    check("coli_dense_forward", lib().coli_dense_forward(ctypes.byref(cm), _ptr(x), _ptr(gamma), eps, T, _ptr(y),
+                                                         flags, _ptr(ws), ws.numel(), _stream(stream)))
+    return y
 
 
 def version() -> str:

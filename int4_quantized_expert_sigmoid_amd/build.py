@@ -9,7 +9,7 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libcoli_moe.so")
 SOURCES = ["abi.cpp", "kernels_quant.hip", "kernels_route.hip", "kernels_gemv.hip", "kernels_grouped.hip",
            "kernels_combine.hip", "kernels_fused.hip",
-           "kernels_decode.hip"]
+           "kernels_decode.hip", "kernels_dense.hip"]
 # The grouped MFMA kernels read every MFMA result with VALU instructions; in
 # VGPR form the accumulator copies (one per result) disappear.
 SOURCE_FLAGS = {"kernels_grouped.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}

@@ -44,6 +44,16 @@ bool layer_ok(const coli_moe_layer *L)
 
 bool gemv_shape_ok(const coli_moe_layer &L) { return L.H <= 8192 && L.I <= 2048; }
 
+bool dense_ok(const coli_dense_mlp *M)
+{
+    if (!M) return false;
+    if (M->H <= 0 || M->I <= 0 || M->H % 32 || M->I % 32 || M->H > 8192 || M->I > 16384) return false;
+    if (M->weight_bits != 0 && M->weight_bits != 4 && M->weight_bits != 8) return false;
+    if (!al16(M->gate_q) || !al16(M->up_q) || !al16(M->down_q)) return false;
+    if (!al4(M->gate_s) || !al4(M->up_s) || !al4(M->down_s)) return false;
+    return true;
+}
+
 constexpr int KNOWN_FLAGS = COLI_ACCUMULATE | COLI_PATH_GEMV | COLI_PATH_GROUPED | COLI_PATH_FUSED;
 
 int choose_path(const coli_moe_layer &L, int T, int flags)
@@ -103,6 +113,31 @@ WsLayout make_layout(const coli_moe_layer &L, int T, int path)
     o.ye = p; p = up(p + n_pairs * H * 4);
     o.xn = p; p = up(p + t * H * 4);
     o.sync = p; p = up(p + (path == 0 ? sizeof(FusedSync) : 0));
+    o.total = p;
+    return o;
+}
+
+WsLayout make_dense_layout(const coli_dense_mlp &M, int T)
+{
+    WsLayout o;
+    std::memset(&o, 0, sizeof(o));
+    const size_t H = (size_t)M.H, I = (size_t)M.I, t = (size_t)T;
+    o.path = T <= COLI_GEMV_MAX_T ? 0 : 1;
+    o.T = T;
+    o.n_pairs = T;
+    const size_t pairs = t < MAX_SLOTS ? MAX_SLOTS : t;   // the GEMV body indexes item 0's slots
+    size_t p = 0;
+    o.ctrl = p; p = up(p + CTRL_WORDS * 4);
+    o.xn = p; p = up(p + t * H * 4);
+    o.xq = p; p = up(p + t * H);
+    o.xs = p; p = up(p + t * (H / 32) * 4);
+    o.h = p; p = up(p + pairs * I * 4);
+    o.hq = p; p = up(p + pairs * I);
+    o.hs = p; p = up(p + pairs * (I / 32) * 4);
+    o.ye = p; p = up(p + t * H * 4);
+    o.tiles = p; p = up(p + ((t + 31) / 32) * 8);
+    o.expert_off = p; p = up(p + 2 * 4);
+    o.pair_tok = p; p = up(p + t * 4);
     o.total = p;
     return o;
 }
@@ -286,6 +321,52 @@ int coli_moe_forward_rms(const coli_moe_layer *L, const float *x, const float *g
 {
     if (!gamma) return COLI_EINVAL;
     return forward_impl(L, x, T, y, flags, ws, ws_bytes, stream, nullptr, gamma, eps);
+}
+
+size_t coli_dense_workspace_bytes(const coli_dense_mlp *M, int T)
+{
+    if (!dense_ok(M) || T < 1 || T > COLI_MAX_T) return 0;
+    return make_dense_layout(*M, T).total;
+}
+
+int coli_dense_forward(const coli_dense_mlp *M, const float *x, const float *gamma, float eps, int T, float *y,
+                       int flags, void *ws, size_t ws_bytes, void *stream)
+{
+    if (!dense_ok(M) || T < 1 || T > COLI_MAX_T) return COLI_EINVAL;
+    if (flags & ~(COLI_ACCUMULATE | COLI_PATH_GEMV | COLI_PATH_GROUPED)) return COLI_EINVAL;
+    if ((flags & COLI_PATH_GEMV) && (flags & COLI_PATH_GROUPED)) return COLI_EINVAL;
+    if ((flags & COLI_PATH_GEMV) && T > COLI_GEMV_MAX_T) return COLI_EINVAL;
+    if (!al16(x) || !al16(y) || !al16(ws)) return COLI_EINVAL;
+    if (gamma && (!al16(gamma) || !(eps >= 0.0f) || !std::isfinite(eps))) return COLI_EINVAL;
+    const WsLayout lay = make_dense_layout(*M, T);
+    if (ws_bytes < lay.total) return COLI_EWORKSPACE;
+    const bool grouped = (flags & COLI_PATH_GROUPED) || (!(flags & COLI_PATH_GEMV) && T > COLI_GEMV_MAX_T);
+    if (grouped && M->weight_bits == 8) return COLI_EUNSUPPORTED;
+    hipStream_t s = (hipStream_t)stream;
+    char *base = static_cast<char *>(ws);
+    const bool acc = (flags & COLI_ACCUMULATE) != 0;
+    if (gamma) {
+        float *xn = reinterpret_cast<float *>(base + lay.xn);
+        if (launch_rmsnorm(x, gamma, T, M->H, eps, xn, s) != hipSuccess) return COLI_EDEVICE;
+        x = xn;
+    }
+    if (launch_quant_q8(x, T, M->H, reinterpret_cast<int8_t *>(base + lay.xq), reinterpret_cast<float *>(base + lay.xs),
+                        true, s) != hipSuccess)
+        return COLI_EDEVICE;
+    if (!grouped) return status(launch_dense_gemv(*M, T, lay, base, y, acc, s));
+    // one expert holding every token on the grouped kernels of the expert path
+    coli_moe_layer L;
+    std::memset(&L, 0, sizeof(L));
+    L.H = M->H; L.I = M->I; L.E = 1; L.top_k = 1; L.n_group = 1; L.topk_group = 1; L.has_shared = 0;
+    L.route_scale = 1.0f; L.weight_bits = 4;
+    L.gate_q = M->gate_q; L.up_q = M->up_q; L.down_q = M->down_q;
+    L.gate_s = M->gate_s; L.up_s = M->up_s; L.down_s = M->down_s;
+    WsLayout gl = lay;
+    gl.path = 1;
+    if (launch_dense_setup(T, lay, base, s) != hipSuccess) return COLI_EDEVICE;
+    if (launch_gateup_grouped(L, T, gl, base, s) != hipSuccess) return COLI_EDEVICE;
+    if (launch_down_grouped(L, T, gl, base, s) != hipSuccess) return COLI_EDEVICE;
+    return status(launch_dense_out(T, M->H, lay, base, y, acc, s));
 }
 
 int coli_moe_forward_profiled(const coli_moe_layer *L, const float *x, int T, float *y, int flags, void *ws,

@@ -121,6 +121,17 @@ hipError_t launch_down_grouped(const coli_moe_layer &L, int T, const WsLayout &l
 hipError_t launch_decode_fused(const coli_moe_layer &L, const float *x, int T, const WsLayout &lay, char *ws,
                                float *y, bool accumulate, hipStream_t s);
 
+// ---- dense MLP (kernels_dense.hip); its workspace uses the WsLayout fields
+// ctrl, xq, xs, h, hq, hs, ye, xn, tiles, expert_off, pair_tok (pair p = token p)
+typedef coli_dense_mlp DenseLayer;
+typedef WsLayout DenseLayout;
+WsLayout make_dense_layout(const coli_dense_mlp &M, int T);
+hipError_t launch_dense_gemv(const DenseLayer &M, int T, const DenseLayout &lay, char *ws, float *y, bool accumulate,
+                             hipStream_t s);
+hipError_t launch_dense_setup(int T, const DenseLayout &lay, char *ws, hipStream_t s);
+hipError_t launch_dense_out(int T, int H, const DenseLayout &lay, const char *ws, float *y, bool accumulate,
+                            hipStream_t s);
+
 // ---- combine (kernels_combine.hip)
 hipError_t launch_combine(const coli_moe_layer &L, int T, const WsLayout &lay, const char *ws,
                           const float *w, float *y, bool accumulate, hipStream_t s);

@@ -13,7 +13,7 @@ import torch
 
 from synth import synth as S
 
-from .api import MoELayer, pack_int4_rows_dev, pack_int8_rows_dev
+from .api import DenseMLP, MoELayer, pack_int4_rows_dev, pack_int8_rows_dev
 
 
 def device_layer(spec: S.LayerSpec, seed: int = 0, layer: int = 0, device: str = "cuda",
@@ -40,3 +40,20 @@ def device_layer(spec: S.LayerSpec, seed: int = 0, layer: int = 0, device: str =
 
 def host_tokens(tspec: S.TokenSpec, H: int, seed: int = 0) -> np.ndarray:
     return S.tokens(tspec, H, seed)
+
+
+def device_dense(spec: S.DenseSpec, seed: int = 0, layer: int = 0, device: str = "cuda",
+                 scratch: torch.Tensor = None) -> DenseMLP:
+    """A dense MLP's weights from the seeded generator, packed on the GPU."""
+    M = DenseMLP.empty(spec.H, spec.I, device=device, weight_bits=spec.weight_bits)
+    pack = pack_int8_rows_dev if spec.weight_bits == 8 else pack_int4_rows_dev
+    n = spec.H * spec.I
+    if scratch is None or scratch.numel() < n:
+        scratch = torch.empty(n, dtype=torch.float32, device=device)
+    stream = torch.cuda.current_stream().cuda_stream
+    for m, q, s, shape in ((S.GATE, M.gate_q, M.gate_s, (spec.I, spec.H)), (S.UP, M.up_q, M.up_s, (spec.I, spec.H)),
+                           (S.DOWN, M.down_q, M.down_s, (spec.H, spec.I))):
+        buf = scratch[:n].view(shape)
+        S.dev_dense_matrix(buf.data_ptr(), spec, seed, layer, m, hip_stream=stream)
+        pack(buf, q, s)
+    return M

@@ -203,6 +203,21 @@ def expert_dense(gate_q, gate_s, up_q, up_s, down_q, down_s, x) -> np.ndarray:
     return y
 
 
+# ---------------------------------------------------------------------- O15
+def dense_forward(gate_q, gate_s, up_q, up_s, down_q, down_s, x, gamma=None, eps: float = 1e-6) -> np.ndarray:
+    """O15 [P1 s4: dense_mlp, the first layers] the dense SwiGLU MLP with the
+    experts' numerics, every token, no routing: y_t = O7(weights, O3(x_t)).y,
+    with x first replaced by O9's RMSNorm(x) * gamma when gamma is given."""
+    x = np.atleast_2d(np.asarray(x, np.float32))
+    if gamma is not None:
+        x = rmsnorm(x, gamma, eps)
+    y = np.empty_like(x)
+    for t in range(x.shape[0]):
+        xq, xs = quant_q8(x[t])
+        y[t] = expert(gate_q, gate_s, up_q, up_s, down_q, down_s, xq, xs).y
+    return y
+
+
 # ----------------------------------------------------------------------- O8
 def combine(y_routed, w, y_shared=None) -> np.ndarray:
     y_routed = _c(np.atleast_2d(y_routed), np.float32)

@@ -213,6 +213,55 @@ WORKLOADS = {
 }
 
 
+# ------------------------------------------------ dense MLP (the first layers)
+DENSE_EXPERT = 4095   # stream id of a layer's dense MLP weights, past every routed and shared expert
+
+
+@dataclass(frozen=True)
+class DenseSpec:
+    """Shape and weight distribution of one dense SwiGLU MLP."""
+    H: int
+    I: int
+    w_sigma: float = 0.02
+    w_outlier_rate: float = 0.0
+    w_outlier_mult: float = 10.0
+    weight_bits: int = 8             # the dense layers' format on the pages
+
+    @property
+    def nbytes(self) -> int:
+        return 3 * self.H * self.I * self.weight_bits // 8 + 4 * (2 * self.I + self.H)
+
+
+@dataclass(frozen=True)
+class DenseWorkload:
+    name: str
+    dense: DenseSpec
+    tokens: TokenSpec
+    seed: int = 0
+    rms_eps: float = 1e-6
+
+
+# intermediate size 12288 = 2H: the pages do not give it (a stated reading)
+GLM52_DENSE = DenseSpec(H=6144, I=12288, w_outlier_rate=0.001)
+DENSE_WORKLOADS = {
+    "glm52_dense_T1": DenseWorkload("glm52_dense_T1", GLM52_DENSE, TokenSpec(T=1, outlier_channels=61)),
+    "glm52_dense_T4": DenseWorkload("glm52_dense_T4", GLM52_DENSE, TokenSpec(T=4, rho=0.8, outlier_channels=61)),
+}
+
+
+def dense_matrix(spec: DenseSpec, seed: int, layer: int, matrix: int) -> np.ndarray:
+    """f32 weights of one dense MLP matrix: gate/up are [I][H], down is [H][I]."""
+    rows, cols = (spec.I, spec.H) if matrix in (GATE, UP) else (spec.H, spec.I)
+    return fill_matrix(seed, stream_expert(layer, DENSE_EXPERT, matrix), rows, cols, spec.w_sigma,
+                       spec.w_outlier_rate, spec.w_outlier_mult)
+
+
+def dev_dense_matrix(ptr: int, spec: DenseSpec, seed: int, layer: int, matrix: int, hip_stream: int = 0) -> None:
+    rows, cols = (spec.I, spec.H) if matrix in (GATE, UP) else (spec.H, spec.I)
+    dev_fill_matrix(ptr, seed, stream_expert(layer, DENSE_EXPERT, matrix), rows, cols, spec.w_sigma,
+                    spec.w_outlier_rate, spec.w_outlier_mult, hip_stream=hip_stream)
+
+
 def expert_matrix(spec: LayerSpec, seed: int, layer: int, expert: int, matrix: int) -> np.ndarray:
     """f32 weights of one expert matrix: gate/up are [I][H], down is [H][I]."""
     rows, cols = (spec.I, spec.H) if matrix in (GATE, UP) else (spec.H, spec.I)

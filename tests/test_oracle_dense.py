@@ -1,0 +1,94 @@
+"""CPU pins of the oracle's dense MLP (O15; colibri architecture overview,
+section 4: dense_mlp ahead of the MoE layers), and host checks of its C ABI.
+
+O15 is O3 + O7 per token (plus O9 with gamma), each pinned elsewhere. The
+pins below tie the composition to something other than itself: a MoE layer
+with one routed expert, top-1 and no shared expert routes every token to
+that expert with weight s/s = 1 exactly, so its output must equal the dense
+MLP's bit for bit; the RMSNorm variant must equal the norm applied first;
+and the IDOT error against the dequantised f64 reference stays at the order
+the experts show."""
+import ctypes
+
+import numpy as np
+import pytest
+
+from int4_quantized_expert_sigmoid_amd import _lib
+from int4_quantized_expert_sigmoid_amd._lib import CDense, lib
+from oracle import layers as OL
+from oracle import oracle as O
+from synth import synth as S
+
+SPEC = S.DenseSpec(H=128, I=352, w_outlier_rate=0.01)
+
+
+def packed(spec, bits, seed=0, layer=0):
+    pack = O.pack_int8_rows if bits == 8 else O.pack_int4_rows
+    out = []
+    for m in (S.GATE, S.UP, S.DOWN):
+        out.extend(pack(S.dense_matrix(spec, seed, layer, m)))
+    return out
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+def test_dense_equals_single_expert_moe_layer(bits):
+    gq, gs, uq, us, dq, ds = packed(SPEC, bits)
+    x = S.tokens(S.TokenSpec(T=5, outlier_channels=2), SPEC.H, 0)
+    y = O.dense_forward(gq, gs, uq, us, dq, ds, x)
+    W = np.zeros((1, SPEC.H), np.float32)
+    L = OL.FullLayer(SPEC.H, SPEC.I, 1, 1, 1, 1, 0, 1.0, W, np.zeros(1, np.float32),
+                     gq[None], gs[None], uq[None], us[None], dq[None], ds[None], bits)
+    y_moe, idx, w = O.moe_forward(L, x)
+    assert np.all(idx == 0) and np.all(w == 1.0)
+    assert np.array_equal(y, y_moe)
+
+
+def test_dense_rmsnorm_input():
+    gq, gs, uq, us, dq, ds = packed(SPEC, 8)
+    x = S.tokens(S.TokenSpec(T=3, token_set=4), SPEC.H, 0) * 3.0
+    g = S.rms_gamma(SPEC.H, 0, 2)
+    a = O.dense_forward(gq, gs, uq, us, dq, ds, x, gamma=g, eps=1e-6)
+    b = O.dense_forward(gq, gs, uq, us, dq, ds, O.rmsnorm(x, g, 1e-6))
+    assert np.array_equal(a, b)
+    assert not np.array_equal(a, O.dense_forward(gq, gs, uq, us, dq, ds, x))
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+def test_dense_idot_error_against_dequantised_reference(bits):
+    """Against the dequantised weights with unquantised x and h, only the two
+    Q8 steps differ: about 0.5% RMS each for N(0,1)-like inputs (the closed
+    form pinned for one projection), about 1% through gate/up and down."""
+    gq, gs, uq, us, dq, ds = packed(SPEC, bits)
+    x = S.tokens(S.TokenSpec(T=8, token_set=9), SPEC.H, 0)
+    y = O.dense_forward(gq, gs, uq, us, dq, ds, x)
+    ref = np.stack([O.expert_dense(gq, gs, uq, us, dq, ds, x[t]) for t in range(8)])
+    rel = np.sqrt(((y - ref) ** 2).mean()) / np.sqrt((ref ** 2).mean())
+    assert 0.003 < rel < 0.02, rel
+
+
+def fake_dense(H=6144, I=12288, bits=8):
+    p = 1 << 20
+    return CDense(H, I, bits, p, p, p, p, p, p)
+
+
+def test_dense_workspace_and_argument_errors():
+    L = lib()
+    M = fake_dense()
+    n1 = L.coli_dense_workspace_bytes(ctypes.byref(M), 1)
+    assert n1 >= 6144 * 4 + 6144 + 8 * 12288 * 5
+    assert L.coli_dense_workspace_bytes(ctypes.byref(M), 0) == 0
+    for bad in (fake_dense(H=100), fake_dense(I=16416), fake_dense(H=8224), fake_dense(bits=2)):
+        assert L.coli_dense_workspace_bytes(ctypes.byref(bad), 1) == 0
+    p = ctypes.c_void_p(1 << 20)
+    F = L.coli_dense_forward
+    f = ctypes.c_float
+    big = 1 << 34
+    assert F(ctypes.byref(M), p, None, f(0), 0, p, 0, p, big, None) == _lib.COLI_EINVAL           # T = 0
+    assert F(ctypes.byref(M), p, None, f(0), 1, p, 16, p, big, None) == _lib.COLI_EINVAL          # unknown flag
+    assert F(ctypes.byref(M), p, None, f(0), 9, p, _lib.COLI_PATH_GEMV, p, big, None) == _lib.COLI_EINVAL
+    assert F(ctypes.byref(M), p, None, f(0), 1, p, 6, p, big, None) == _lib.COLI_EINVAL           # two paths
+    assert F(ctypes.byref(M), p, p, f(-1), 1, p, 0, p, big, None) == _lib.COLI_EINVAL             # eps < 0
+    assert F(ctypes.byref(M), ctypes.c_void_p((1 << 20) + 8), None, f(0), 1, p, 0, p, big, None) == _lib.COLI_EINVAL
+    assert F(ctypes.byref(M), p, None, f(0), 1, p, 0, p, 100, None) == _lib.COLI_EWORKSPACE
+    assert F(ctypes.byref(M), p, None, f(0), 16, p, 0, p, big, None) == _lib.COLI_EUNSUPPORTED    # int8 grouped
+    assert F(None, p, None, f(0), 1, p, 0, p, big, None) == _lib.COLI_EINVAL
