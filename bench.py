@@ -18,9 +18,10 @@ grouped int8-MFMA path), glm52_chain16_T1 (one token through 16 layers:
 RMSNorm, then the layer with its output added to the residual stream; a step
 is the whole 16-layer stack, restarted from the same input token), and
 glm52_int8_mtp_T1 / glm52_int8_T4 (the same layer with int8 experts, the
-MTP head's format, at T=1 and T=4), and glm52_hot8_T512 (prefill with every
+MTP head's format, at T=1 and T=4), glm52_hot8_T512 (prefill with every
 token on the same 8 experts: a compute-bound grouped GEMM, whose roofline
-field is the int8 matrix-core rate).
+field is the int8 matrix-core rate), and glm52_dense_T1 / glm52_dense_T4
+(the dense SwiGLU MLP of the first layers, int8, H 6144, I 12288).
 
 Prints ONE JSON line (metric, value, roofline of the dominant kernel,
 cpu_baseline of the oracle on a bounded sample).
@@ -125,6 +126,9 @@ def main():
         print("bench.py measures one GPU: this build has no multi-GPU path "
               "(sharding is described in DESIGN.md); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
+    from synth import synth as S0
+    if args.workload in S0.DENSE_WORKLOADS:
+        return bench_dense(args)
 
     import numpy as np
     import torch
@@ -317,6 +321,120 @@ def main():
         "data": "synthetic (seeded Philox weights and tokens, no trained checkpoint)",
         "config": config,
         "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def bench_dense(args):
+    """A dense layer of the first ones (the dense SwiGLU MLP) at decode: a step
+    is one call of coli_dense_forward on one batch, walking resident
+    instances round-robin as the MoE workloads do."""
+    import numpy as np
+    import torch
+
+    from int4_quantized_expert_sigmoid_amd import api
+    from int4_quantized_expert_sigmoid_amd.synthetic import device_dense
+    from synth import synth as S
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    wl = S.DENSE_WORKLOADS[args.workload]
+    spec, T = wl.dense, wl.tokens.T
+    G = args.instances
+    log(f"bench: {args.workload} T={T}, building {G} dense MLP instances on device")
+    scratch = torch.empty(spec.H * spec.I, dtype=torch.float32, device="cuda")
+    mlps = [device_dense(spec, wl.seed, li, scratch=scratch) for li in range(G)]
+    del scratch
+    wss = [api.dense_workspace(M, T) for M in mlps]
+    cms = [M.c() for M in mlps]
+    from dataclasses import replace
+    toks = S.tokens(replace(wl.tokens, T=T * G), spec.H, wl.seed)
+    x_all = torch.from_numpy(toks).cuda().view(G, T, spec.H)
+    y_all = torch.empty_like(x_all)
+    stream = torch.cuda.Stream()
+
+    def step(i, s):
+        j = i % G
+        api.dense_forward(mlps[j], x_all[j], wss[j], y=y_all[j], stream=s, c_mlp=cms[j])
+
+    K = max(G, (args.steps + G - 1) // G * G)
+    W = max(G, (args.warmup + G - 1) // G * G)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for i in range(G):
+            step(i, torch.cuda.current_stream())
+    with torch.cuda.stream(stream):
+        for _ in range(W // G):
+            g.replay()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        ev0.record(stream)
+        for _ in range(K // G):
+            g.replay()
+        ev1.record(stream)
+    torch.cuda.synchronize()
+    ms_total = ev0.elapsed_time(ev1)
+    ms_step = ms_total / K
+    value = K * T / (ms_total / 1e3)
+
+    # kernel-exact durations of 256 eager calls
+    per_call = []
+    for i in range(min(K, 256)):
+        ev = api.KernelEvents(8)
+        with api.kernel_timer(ev):
+            step(i, stream)
+        per_call.append(ev)
+    stream.synchronize()
+    durs = [ev.durations_ms() for ev in per_call]
+    label = lambda n: n.strip("()").split("<")[0]
+    names = [label(n) for n, _ in durs[0]]
+    kms = np.array([[ms for _, ms in d] for d in durs]).mean(axis=0)
+    del per_call
+    i_gu = names.index("k_dense_gateup")
+    i_dn = names.index("k_dense_down")
+    wb = spec.weight_bits
+    gu_bytes = 2 * spec.I * (spec.H * wb // 8 + 4)
+    dn_bytes = spec.H * (spec.I * wb // 8 + 4)
+    gu_gbs = gu_bytes / (kms[i_gu] * 1e-3) / 1e9
+    dn_gbs = dn_bytes / (kms[i_dn] * 1e-3) / 1e9
+    step_gbs = spec.nbytes / (ms_step * 1e-3) / 1e9
+    log("bench: kernel averages (ms): " + ", ".join(f"{n}={v:.4f}" for n, v in zip(names, kms)))
+    log(f"bench: gate/up {gu_gbs:.0f} GB/s, down {dn_gbs:.0f} GB/s, whole step {step_gbs:.0f} GB/s; "
+        f"{ms_step * 1e3:.2f} us/step")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        from oracle import oracle as O
+        log("bench: timing the oracle on a CPU sample")
+        pack = O.pack_int8_rows if wb == 8 else O.pack_int4_rows
+        w = []
+        for m in (S.GATE, S.UP, S.DOWN):
+            w.extend(pack(S.dense_matrix(spec, wl.seed, 0, m)))
+        x = np.asarray(toks).reshape(-1, spec.H)[:3]
+        times = []
+        for t in range(3):
+            t0 = time.perf_counter()
+            O.dense_forward(*w, x[t:t + 1])
+            times.append(time.perf_counter() - t0)
+        sec = float(np.median(times))
+        cpu = {"value": 1.0 / sec, "unit": "tokens*layers/s", "cores": 1, "kind": "oracle",
+               "sample": f"3 tokens through one dense MLP of this shape, median ({sec:.2f} s/token, "
+                         f"single-threaded C oracle, -O2; weight generation and packing untimed)"}
+    out = {
+        "metric": f"dense-MLP tokens*layers/s (GLM-5.2-shaped first-layer MLP, int{wb} weights, decode)",
+        "value": round(value, 1), "unit": "tokens*layers/s", "n_gpus": 1, "steps": K, "warmup": W,
+        "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": f"int{wb}xint8->int32, f64 block sums",
+        "data": "synthetic (seeded Philox weights and tokens, no trained checkpoint)",
+        "config": {"workload": args.workload, "H": spec.H, "I": spec.I, "T": T, "layer_instances": G,
+                   "hip_graph": True, "weight_bytes_per_step": spec.nbytes, "step_hbm_gbs": round(step_gbs, 1),
+                   "kernel_ms": [[n, round(float(v), 5)] for n, v in zip(names, kms)]},
+        "roofline": {"bound": "hbm", "kernel": "k_dense_gateup", "achieved": round(gu_gbs, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(gu_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "bytes_per_launch": gu_bytes, "avg_launch_ms": round(float(kms[i_gu]), 5),
+                     "down_gbs": round(dn_gbs, 1)},
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

@@ -18,7 +18,7 @@ COLI_GEMV_MAX_T, COLI_MAX_T, COLI_MAX_TOPK, COLI_PROFILE_EVENTS = 8, 65536, 16, 
 
 EXPORTS = ("coli_quant_act_q8", "coli_moe_workspace_bytes", "coli_moe_workspace_init",
            "coli_moe_route", "coli_moe_forward", "coli_moe_forward_profiled", "coli_moe_forward_timed", "coli_moe_forward_rms",
-           "coli_dense_workspace_bytes", "coli_dense_forward", "coli_moe_experts", "coli_moe_workspace_layout",
+           "coli_dense_workspace_bytes", "coli_dense_forward", "coli_timer_begin", "coli_timer_end", "coli_moe_experts", "coli_moe_workspace_layout",
            "coli_rmsnorm", "coli_pack_int4_rows", "coli_pack_int4_rows_dev", "coli_pack_int8_rows",
            "coli_pack_int8_rows_dev", "coli_debug_block_dots", "coli_version")
 
@@ -76,6 +76,8 @@ def lib():
             "coli_moe_forward_profiled": ([LP, P, i, P, i, P, sz, P, ctypes.POINTER(P), i], i),
             "coli_moe_forward_rms": ([LP, P, P, f, i, P, i, P, sz, P], i),
             "coli_dense_workspace_bytes": ([ctypes.POINTER(CDense), i], sz),
+            "coli_timer_begin": ([ctypes.POINTER(P), ctypes.POINTER(P), i, ctypes.POINTER(ctypes.c_char_p)], i),
+            "coli_timer_end": ([ctypes.POINTER(i)], i),
             "coli_dense_forward": ([ctypes.POINTER(CDense), P, P, f, i, P, i, P, sz, P], i),
             "coli_moe_forward_timed": ([LP, P, P, f, i, P, i, P, sz, P, ctypes.POINTER(P), ctypes.POINTER(P), i,
                                         ctypes.POINTER(i), ctypes.POINTER(ctypes.c_char_p)], i),

@@ -251,6 +251,23 @@ class KernelEvents:
             pass
 
 
+class kernel_timer:
+    """Context manager: every library launch inside the block records its own
+    start/stop in `events` (coli_timer_begin / coli_timer_end)."""
+
+    def __init__(self, events: KernelEvents):
+        self.events = events
+
+    def __enter__(self):
+        check("coli_timer_begin", lib().coli_timer_begin(self.events.start, self.events.stop, self.events.n,
+                                                         self.events.names))
+        return self.events
+
+    def __exit__(self, *exc):
+        check("coli_timer_end", lib().coli_timer_end(ctypes.byref(self.events.count)))
+        return False
+
+
 def moe_forward_timed(layer: MoELayer, x: torch.Tensor, ws: torch.Tensor, events: KernelEvents,
                       y: Optional[torch.Tensor] = None, flags: int = 0, stream=None,
                       c_layer: Optional[CLayer] = None, gamma: Optional[torch.Tensor] = None,

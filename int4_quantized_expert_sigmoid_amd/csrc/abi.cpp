@@ -323,6 +323,29 @@ int coli_moe_forward_rms(const coli_moe_layer *L, const float *x, const float *g
     return forward_impl(L, x, T, y, flags, ws, ws_bytes, stream, nullptr, gamma, eps);
 }
 
+int coli_timer_begin(void *const *start, void *const *stop, int n_pairs, const char **names)
+{
+    if (n_pairs < 1 || !start || !stop) return COLI_EINVAL;
+    for (int i = 0; i < n_pairs; ++i)
+        if (!start[i] || !stop[i]) return COLI_EINVAL;
+    KernelTimer *&slot = kernel_timer();
+    if (slot) return COLI_EINVAL;                // one open scope per thread
+    static thread_local KernelTimer scope;
+    scope = KernelTimer{reinterpret_cast<const hipEvent_t *>(start), reinterpret_cast<const hipEvent_t *>(stop),
+                        names, n_pairs, 0};
+    slot = &scope;
+    return COLI_OK;
+}
+
+int coli_timer_end(int *n_launches)
+{
+    KernelTimer *&slot = kernel_timer();
+    if (!slot || !n_launches) return COLI_EINVAL;
+    *n_launches = slot->next;
+    slot = nullptr;
+    return COLI_OK;
+}
+
 size_t coli_dense_workspace_bytes(const coli_dense_mlp *M, int T)
 {
     if (!dense_ok(M) || T < 1 || T > COLI_MAX_T) return 0;
@@ -388,6 +411,7 @@ int coli_moe_forward_timed(const coli_moe_layer *L, const float *x, const float 
     KernelTimer kt{reinterpret_cast<const hipEvent_t *>(start), reinterpret_cast<const hipEvent_t *>(stop), names,
                    n_pairs, 0};
     KernelTimer *&slot = kernel_timer();
+    if (slot) return COLI_EINVAL;                // inside an open coli_timer_begin scope
     KernelTimer *const prev = slot;
     slot = &kt;
     const int rc = forward_impl(L, x, T, y, flags, ws, ws_bytes, stream, nullptr, gamma, eps);

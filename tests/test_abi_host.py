@@ -114,6 +114,23 @@ def test_rms_forward_argument_errors_before_launch():
     assert R(ctypes.byref(L), p, p, f(1e-6), 1, p, 0, p, 100, None) == _lib.COLI_EWORKSPACE
 
 
+def test_timer_scope_errors():
+    L = lib()
+    ev = (ctypes.c_void_p * 2)(1 << 20, 1 << 20)     # stand-ins: nothing is launched in the scope
+    nul = (ctypes.c_void_p * 2)(1 << 20, None)
+    n = ctypes.c_int(-1)
+    assert L.coli_timer_end(ctypes.byref(n)) == _lib.COLI_EINVAL             # no open scope
+    assert L.coli_timer_begin(ev, ev, 0, None) == _lib.COLI_EINVAL
+    assert L.coli_timer_begin(ev, nul, 2, None) == _lib.COLI_EINVAL
+    assert L.coli_timer_begin(None, ev, 2, None) == _lib.COLI_EINVAL
+    assert L.coli_timer_begin(ev, ev, 2, None) == _lib.COLI_OK
+    assert L.coli_timer_begin(ev, ev, 2, None) == _lib.COLI_EINVAL           # one scope at a time
+    assert L.coli_timer_end(None) == _lib.COLI_EINVAL
+    assert L.coli_timer_end(ctypes.byref(n)) == _lib.COLI_OK
+    assert n.value == 0
+    assert L.coli_timer_end(ctypes.byref(n)) == _lib.COLI_EINVAL
+
+
 def test_timed_forward_argument_errors_before_launch():
     L = fake_layer()
     p = ctypes.c_void_p(1 << 20)
