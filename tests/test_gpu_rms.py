@@ -62,6 +62,12 @@ def test_rms_forward_equals_norm_then_forward_glm():
         say(f"rms forward GLM T={T}")
         a, b = _both(L, x, g, 0)
         assert np.array_equal(a, b)
+        # the chain layer as a decode step captures it: residual added in place
+        x0, xr, gd = dev(x), dev(x), dev(g)
+        ws = api.workspace(L, T)
+        say(f"rms forward GLM T={T} graph replays")
+        _replay(lambda st: api.moe_forward_rms(L, xr, gd, EPS, ws, y=xr, flags=COLI_ACCUMULATE, stream=st),
+                [torch.from_numpy(a).cuda()], [xr], reset=lambda: xr.copy_(x0))
     del L
     torch.cuda.empty_cache()
 
@@ -73,3 +79,49 @@ def test_rms_forward_not_accumulating(tiny):
     xn = api.rmsnorm(dev(x), dev(g), EPS)
     y2 = api.moe_forward(tiny, xn, api.workspace(tiny, 2)).cpu().numpy()
     assert np.array_equal(y1, y2)
+
+
+def _replay(capture, eager, outs, n=4, reset=None):
+    """Capture `capture` in a HIP graph, replay it n times with eager work in
+    between, and compare every replay with the eager results. `reset` restores
+    the outputs' starting values before each replay (default: zeros)."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        capture(torch.cuda.current_stream())
+    for rep in range(n):
+        if reset is None:
+            for o in outs:
+                o.zero_()
+        else:
+            reset()
+        g.replay()
+        torch.cuda.synchronize()
+        for o, e in zip(outs, eager):
+            assert torch.equal(o, e), f"replay {rep}"
+        capture(torch.cuda.current_stream())       # the same work eagerly between replays
+        torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("T", [1, 4, 20])
+def test_rms_forward_graph_replays(tiny, T):
+    x = dev(S.tokens(S.TokenSpec(T=T, token_set=97 + T), S.TINY.H, 0))
+    g = dev(S.rms_gamma(S.TINY.H, 0, 7))
+    ws = api.workspace(tiny, T)
+    eager = [api.moe_forward_rms(tiny, x, g, EPS, ws).clone()]
+    y = torch.empty_like(x)
+    _replay(lambda st: api.moe_forward_rms(tiny, x, g, EPS, ws, y=y, stream=st), eager, [y])
+
+
+@pytest.mark.parametrize("T", [1, 3, 12])
+def test_dense_forward_graph_replays(T):
+    from int4_quantized_expert_sigmoid_amd.synthetic import device_dense
+    spec = S.DenseSpec(H=256, I=512, weight_bits=4)
+    M = device_dense(spec, 0, 0)
+    x = dev(S.tokens(S.TokenSpec(T=T, token_set=98 + T), spec.H, 0))
+    g = dev(S.rms_gamma(spec.H, 0, 8))
+    ws = api.dense_workspace(M, T)
+    eager = [api.dense_forward(M, x, ws, gamma=g).clone()]
+    y = torch.empty_like(x)
+    _replay(lambda st: api.dense_forward(M, x, ws, y=y, gamma=g, stream=st), eager, [y])
