@@ -28,7 +28,10 @@ class PackedExpert:
 
 
 def packed_expert(spec: S.LayerSpec, seed: int, layer: int, e: int) -> PackedExpert:
-    pack = O.pack_int8_rows if spec.weight_bits == 8 else O.pack_int4_rows
+    if spec.group_size:
+        pack = lambda w: O.pack_int4_groups(w, spec.group_size)
+    else:
+        pack = O.pack_int8_rows if spec.weight_bits == 8 else O.pack_int4_rows
     mats = []
     for m in (S.GATE, S.UP, S.DOWN):
         mats.extend(pack(S.expert_matrix(spec, seed, layer, e, m)))
@@ -68,6 +71,7 @@ class FullLayer:
     down_q: np.ndarray
     down_s: np.ndarray
     weight_bits: int = 4
+    group_size: int = 0
 
 
 def full_layer(spec: S.LayerSpec, seed: int = 0, layer: int = 0) -> FullLayer:
@@ -76,7 +80,7 @@ def full_layer(spec: S.LayerSpec, seed: int = 0, layer: int = 0) -> FullLayer:
     st = lambda name: np.stack([getattr(p, name) for p in ex])
     return FullLayer(spec.H, spec.I, spec.E, spec.top_k, spec.n_group, spec.topk_group,
                      spec.has_shared, spec.route_scale, W, b, st("gate_q"), st("gate_s"),
-                     st("up_q"), st("up_s"), st("down_q"), st("down_s"), spec.weight_bits)
+                     st("up_q"), st("up_s"), st("down_q"), st("down_s"), spec.weight_bits, spec.group_size)
 
 
 @dataclass
@@ -94,7 +98,7 @@ def forward_token(spec: S.LayerSpec, cache: ExpertCache, W: np.ndarray, b: np.nd
     """One token through the layer (O6 -> O3 -> O7 -> O8), regenerating experts."""
     idx, w = O.route(W, b, x[None, :], spec.top_k, spec.n_group, spec.topk_group, spec.route_scale)
     xq, xs = O.quant_q8(x)
-    outs = [O.expert(*cache[int(e)].args(), xq, xs) for e in idx[0]]
-    sh = O.expert(*cache[spec.E].args(), xq, xs) if spec.has_shared else None
+    outs = [O.expert(*cache[int(e)].args(), xq, xs, group=spec.group_size) for e in idx[0]]
+    sh = O.expert(*cache[spec.E].args(), xq, xs, group=spec.group_size) if spec.has_shared else None
     y = O.combine(np.stack([o.y for o in outs]), w[0], None if sh is None else sh.y)
     return TokenResult(idx[0], w[0], xq, xs, tuple(outs) + ((sh,) if sh else ()), y)

@@ -107,6 +107,60 @@ void oracle_rowdot(const uint8_t *q4, const float *s4, const int8_t *q8, const f
     free(S);
 }
 
+/* ----------------------------------------------------------- O16 / O17 --- */
+void oracle_pack_int4_groups(const float *w, int rows, int cols, int group, uint8_t *q, float *s)
+{
+    const int ng = cols / group;
+    for (int r = 0; r < rows; ++r) {
+        const float *row = w + (size_t)r * cols;
+        uint8_t *dst = q + (size_t)r * (cols / 2);
+        for (int g = 0; g < ng; ++g) {
+            const float *grp = row + (size_t)g * group;
+            float amax = 0.0f;
+            for (int c = 0; c < group; ++c) {
+                float a = fabsf(grp[c]);
+                if (a > amax) amax = a;
+            }
+            float d = amax / 7.0f;
+            float id = (d != 0.0f) ? 1.0f / d : 0.0f;
+            s[(size_t)r * ng + g] = d;
+            for (int j = 0; j < group / 2; ++j) {
+                int lo = round_clamp(grp[2 * j] * id, -8.0f, 7.0f);
+                int hi = round_clamp(grp[2 * j + 1] * id, -8.0f, 7.0f);
+                dst[(size_t)g * (group / 2) + j] = (uint8_t)((lo & 0xF) | ((hi & 0xF) << 4));
+            }
+        }
+    }
+}
+
+void oracle_unpack_int4_groups(const uint8_t *q, const float *s, int rows, int cols, int group, double *w)
+{
+    const int ng = cols / group;
+    for (int r = 0; r < rows; ++r) {
+        for (int c = 0; c < cols; ++c) {
+            uint8_t byte = q[(size_t)r * (cols / 2) + c / 2];
+            w[(size_t)r * cols + c] = (double)s[(size_t)r * ng + c / group] * (double)oracle_nibble(byte, c & 1);
+        }
+    }
+}
+
+void oracle_rowdot_groups(const uint8_t *q4, const float *s4, int group, const int8_t *q8, const float *d8,
+                          int rows, int cols, float *out)
+{
+    const int nb = cols / 32, ng = cols / group;
+    int32_t *S = (int32_t *)malloc(sizeof(int32_t) * (size_t)nb);
+    for (int r = 0; r < rows; ++r) {
+        oracle_block_dots(q4 + (size_t)r * (cols / 2), q8, 1, cols, S);
+        double acc = 0.0;
+        for (int b = 0; b < nb; ++b) {
+            double sg = (double)s4[(size_t)r * ng + (32 * b) / group];
+            acc += sg * ((double)d8[b] * (double)S[b]);
+        }
+        out[r] = (float)acc;
+    }
+    free(S);
+}
+
 /* ----------------------------------------------------------- O11 - O13 --- */
 void oracle_pack_int8_rows(const float *w, int rows, int cols, int8_t *q, float *s)
 {
@@ -215,17 +269,19 @@ int oracle_route(const float *W, const float *b, const float *x, int T, int H, i
 
 /* ------------------------------------------------------------------ O7 --- */
 /* The IDOT row product of either weight format (O5 for 4 bits, O13 for 8). */
-static void rowdot_w(int wbits, const void *q, const float *s, const int8_t *q8, const float *d8,
+/* group > 0: int4 rows with one scale per group of that many columns (O17). */
+static void rowdot_w(int wbits, int group, const void *q, const float *s, const int8_t *q8, const float *d8,
                      int rows, int cols, float *out)
 {
     if (wbits == 8) oracle_rowdot_i8((const int8_t *)q, s, q8, d8, rows, cols, out);
+    else if (group > 0) oracle_rowdot_groups((const uint8_t *)q, s, group, q8, d8, rows, cols, out);
     else oracle_rowdot((const uint8_t *)q, s, q8, d8, rows, cols, out);
 }
 
-void oracle_expert_w(int wbits, const void *gate_q, const float *gate_s, const void *up_q, const float *up_s,
-                     const void *down_q, const float *down_s, int H, int I,
-                     const int8_t *xq, const float *xs, float *y,
-                     float *g_out, float *u_out, float *h_out, int8_t *hq_out, float *hs_out)
+static void expert_impl(int wbits, int group, const void *gate_q, const float *gate_s, const void *up_q,
+                        const float *up_s, const void *down_q, const float *down_s, int H, int I,
+                        const int8_t *xq, const float *xs, float *y,
+                        float *g_out, float *u_out, float *h_out, int8_t *hq_out, float *hs_out)
 {
     float *g = (float *)malloc(sizeof(float) * (size_t)I);
     float *u = (float *)malloc(sizeof(float) * (size_t)I);
@@ -233,15 +289,15 @@ void oracle_expert_w(int wbits, const void *gate_q, const float *gate_s, const v
     int8_t *hq = (int8_t *)malloc((size_t)I);
     float *hs = (float *)malloc(sizeof(float) * (size_t)(I / 32));
 
-    rowdot_w(wbits, gate_q, gate_s, xq, xs, I, H, g);
-    rowdot_w(wbits, up_q, up_s, xq, xs, I, H, u);
+    rowdot_w(wbits, group, gate_q, gate_s, xq, xs, I, H, g);
+    rowdot_w(wbits, group, up_q, up_s, xq, xs, I, H, u);
     for (int i = 0; i < I; ++i) {
         double gd = (double)g[i];
         double silu = gd / (1.0 + exp(-gd));
         h[i] = (float)(silu * (double)u[i]);
     }
     oracle_quant_q8(h, I, hq, hs);
-    rowdot_w(wbits, down_q, down_s, hq, hs, H, I, y);
+    rowdot_w(wbits, group, down_q, down_s, hq, hs, H, I, y);
 
     if (g_out) memcpy(g_out, g, sizeof(float) * (size_t)I);
     if (u_out) memcpy(u_out, u, sizeof(float) * (size_t)I);
@@ -249,6 +305,24 @@ void oracle_expert_w(int wbits, const void *gate_q, const float *gate_s, const v
     if (hq_out) memcpy(hq_out, hq, (size_t)I);
     if (hs_out) memcpy(hs_out, hs, sizeof(float) * (size_t)(I / 32));
     free(g); free(u); free(h); free(hq); free(hs);
+}
+
+void oracle_expert_w(int wbits, const void *gate_q, const float *gate_s, const void *up_q, const float *up_s,
+                     const void *down_q, const float *down_s, int H, int I,
+                     const int8_t *xq, const float *xs, float *y,
+                     float *g_out, float *u_out, float *h_out, int8_t *hq_out, float *hs_out)
+{
+    expert_impl(wbits, 0, gate_q, gate_s, up_q, up_s, down_q, down_s, H, I, xq, xs, y, g_out, u_out, h_out,
+                hq_out, hs_out);
+}
+
+void oracle_expert_groups(int group, const uint8_t *gate_q, const float *gate_s, const uint8_t *up_q,
+                          const float *up_s, const uint8_t *down_q, const float *down_s, int H, int I,
+                          const int8_t *xq, const float *xs, float *y,
+                          float *g_out, float *u_out, float *h_out, int8_t *hq_out, float *hs_out)
+{
+    expert_impl(4, group, gate_q, gate_s, up_q, up_s, down_q, down_s, H, I, xq, xs, y, g_out, u_out, h_out,
+                hq_out, hs_out);
 }
 
 void oracle_expert(const uint8_t *gate_q, const float *gate_s, const uint8_t *up_q, const float *up_s,
@@ -340,6 +414,8 @@ int oracle_moe_forward(const oracle_layer *L, const float *x, int T, float *y, i
     const int H = L->H, I = L->I, E = L->E, k = L->top_k;
     if (H <= 0 || I <= 0 || H % 32 || I % 32 || T < 0) return -1;
     if (L->weight_bits != 0 && L->weight_bits != 4 && L->weight_bits != 8) return -1;
+    const int G = L->group_size;
+    if (G < 0 || (G > 0 && (L->weight_bits == 8 || G % 32 || H % G || I % G))) return -1;
     int32_t *idx = (int32_t *)malloc(sizeof(int32_t) * (size_t)(T * k + 1));
     float *w = (float *)malloc(sizeof(float) * (size_t)(T * k + 1));
     if (oracle_route(L->router_w, L->router_b, x, T, H, E, k, L->n_group, L->topk_group,
@@ -355,19 +431,21 @@ int oracle_moe_forward(const oracle_layer *L, const float *x, int T, float *y, i
     /* bytes per expert matrix: a byte holds two 4-bit codes or one 8-bit code */
     const size_t gq = wb == 8 ? (size_t)I * H : (size_t)I * (H / 2);
     const size_t dq = wb == 8 ? (size_t)H * I : (size_t)H * (I / 2);
+    /* scales per expert matrix: one per row, or one per group of G columns */
+    const size_t gs = G > 0 ? (size_t)I * (H / G) : (size_t)I;
+    const size_t ds = G > 0 ? (size_t)H * (I / G) : (size_t)H;
     for (int t = 0; t < T; ++t) {
         oracle_quant_q8(x + (size_t)t * H, H, xq, xs);
         for (int j = 0; j < k; ++j) {
             int e = idx[t * k + j];
-            oracle_expert_w(wb, L->gate_q + e * gq, L->gate_s + (size_t)e * I, L->up_q + e * gq,
-                            L->up_s + (size_t)e * I, L->down_q + e * dq, L->down_s + (size_t)e * H,
-                            H, I, xq, xs, yr + (size_t)j * H, NULL, NULL, NULL, NULL, NULL);
+            expert_impl(wb, G, L->gate_q + e * gq, L->gate_s + e * gs, L->up_q + e * gq, L->up_s + e * gs,
+                        L->down_q + e * dq, L->down_s + e * ds, H, I, xq, xs, yr + (size_t)j * H,
+                        NULL, NULL, NULL, NULL, NULL);
         }
         if (L->has_shared) {
             int e = E;
-            oracle_expert_w(wb, L->gate_q + e * gq, L->gate_s + (size_t)e * I, L->up_q + e * gq,
-                            L->up_s + (size_t)e * I, L->down_q + e * dq, L->down_s + (size_t)e * H,
-                            H, I, xq, xs, ysh, NULL, NULL, NULL, NULL, NULL);
+            expert_impl(wb, G, L->gate_q + e * gq, L->gate_s + e * gs, L->up_q + e * gq, L->up_s + e * gs,
+                        L->down_q + e * dq, L->down_s + e * ds, H, I, xq, xs, ysh, NULL, NULL, NULL, NULL, NULL);
         }
         oracle_combine(yr, w + (size_t)t * k, k, L->has_shared ? ysh : NULL, H, y + (size_t)t * H);
     }

@@ -17,6 +17,8 @@
  *              gate/up/SiLU/down expert matmuls on the IDOT path, shared expert.
  *   [P2 how]   README (zh-TW), "how it works": a batch reads each distinct expert
  *              once (batch union); placement never changes routing or precision.
+ *   [P2 results] same README, "actual results": quality is measured, including
+ *              the int4 container's cost and scale-granularity ablations.
  *   [P3 impl]  ai4coding.ru summary, "what is implemented": DeepSeek-V3-style
  *              sigmoid router, shared expert, Q8_0-style int8 activations.
  * Where the pages leave a step open, the reading taken is stated at the
@@ -63,6 +65,25 @@ void oracle_block_dots(const uint8_t *q4, const int8_t *q8, int rows, int cols, 
 void oracle_rowdot(const uint8_t *q4, const float *s4, const int8_t *q8, const float *d8,
                    int rows, int cols, float *out);
 
+/* O16 [P1 s3.1 int4 format; P2 results: the quality measurements include
+ * scale-granularity ablations] int4 with one scale per group of `group`
+ * consecutive columns of a row instead of one per row. The pages name the
+ * ablation but not the group format; the reading taken is O1 applied to
+ * every group as if it were a row: d_g = absmax_g/7 (f32), the same codes,
+ * rounding, clamp and nibble order. q: [rows][cols/2] as O1,
+ * s: [rows][cols/group]. group must be even and divide cols. */
+void oracle_pack_int4_groups(const float *w, int rows, int cols, int group, uint8_t *q, float *s);
+
+/* O16 dequantise on use: w~[r][c] = s[r][c/group] * code[r][c] (double). */
+void oracle_unpack_int4_groups(const uint8_t *q, const float *s, int rows, int cols, int group, double *w);
+
+/* O17 [P1 s3.1, dot_i4i8 with O16 scales] IDOT row product with group scales
+ * (group a multiple of 32, so a group is whole activation blocks):
+ * out[r] = (float)(sum_b s[r][g(b)] * (d8[b] * S[r][b])), g(b) = 32b/group,
+ * every term in double, summed in block order. With group = cols it is O5. */
+void oracle_rowdot_groups(const uint8_t *q4, const float *s4, int group, const int8_t *q8, const float *d8,
+                          int rows, int cols, float *out);
+
 /* O11 [P1 s3.1, quantize_rows] int8 weights, one byte per value. The pages
  * give no scale rule for them; the reading taken is the symmetric one of
  * the Q8 activations, per row: d = absmax/127 (f32), id = 1/d (0 if d == 0),
@@ -108,6 +129,13 @@ void oracle_expert_w(int wbits, const void *gate_q, const float *gate_s, const v
                      const int8_t *xq, const float *xs, float *y,
                      float *g, float *u, float *h, int8_t *hq, float *hs);
 
+/* O7 with O16 weights: every row product is O17 with the given group.
+ * gate/up scales [I][H/group], down scales [H][I/group]. */
+void oracle_expert_groups(int group, const uint8_t *gate_q, const float *gate_s, const uint8_t *up_q,
+                          const float *up_s, const uint8_t *down_q, const float *down_s, int H, int I,
+                          const int8_t *xq, const float *xs, float *y,
+                          float *g_out, float *u_out, float *h_out, int8_t *hq_out, float *hs_out);
+
 /* O8 [P1 s5, P3 impl] combine for one token: y = (float)(sum_j w_j*y_j + y_shared),
  * summed in double in j order, the shared expert (weight 1) last; y_shared may
  * be NULL (no shared expert). y_routed: [k][H]. */
@@ -140,6 +168,8 @@ typedef struct oracle_layer {
     const uint8_t *gate_q, *up_q, *down_q;   /* int8 rows when weight_bits == 8 */
     const float *gate_s, *up_s, *down_s;
     int weight_bits;                         /* 4 (or 0) or 8 */
+    int group_size;                          /* 0: one scale per row; else int4 with O16 group scales,
+                                                gate_s/up_s [E'][I][H/G], down_s [E'][H][I/G] */
 } oracle_layer;
 
 /* O6 -> O3 -> O7 per selected expert (+ shared) -> O8, for T tokens.

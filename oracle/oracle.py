@@ -46,6 +46,10 @@ def _lib():
         L.oracle_rowdot_i8.argtypes = [P, P, P, P, i, i, P]
         L.oracle_expert_w.argtypes = [i, P, P, P, P, P, P, i, i, P, P, P, P, P, P, P, P]
         L.oracle_expert_dense_i8.argtypes = [P, P, P, P, P, P, i, i, P, P]
+        L.oracle_pack_int4_groups.argtypes = [P, i, i, i, P, P]
+        L.oracle_unpack_int4_groups.argtypes = [P, P, i, i, i, P]
+        L.oracle_rowdot_groups.argtypes = [P, P, i, P, P, i, i, P]
+        L.oracle_expert_groups.argtypes = [i, P, P, P, P, P, P, i, i, P, P, P, P, P, P, P, P]
         _L = L
     return _L
 
@@ -107,6 +111,39 @@ def rowdot(q4, s4, q8, d8) -> np.ndarray:
     out = np.empty(rows, dtype=np.float32)
     _lib().oracle_rowdot(_p(q4), _p(_c(s4, np.float32)), _p(_c(q8, np.int8)), _p(_c(d8, np.float32)),
                          rows, 2 * half, _p(out))
+    return out
+
+
+# ---------------------------------------------------------------- O16 / O17
+def pack_int4_groups(w: np.ndarray, group: int):
+    """int4 codes (O1's byte layout) and one f32 scale per group of `group` columns."""
+    w = _c(w, np.float32)
+    rows, cols = w.shape
+    if group < 2 or group % 2 or cols % group:
+        raise ValueError("group must be even and divide the row length")
+    q = np.empty((rows, cols // 2), dtype=np.uint8)
+    s = np.empty((rows, cols // group), dtype=np.float32)
+    _lib().oracle_pack_int4_groups(_p(w), rows, cols, group, _p(q), _p(s))
+    return q, s
+
+
+def unpack_int4_groups(q: np.ndarray, s: np.ndarray, group: int) -> np.ndarray:
+    q = _c(q, np.uint8)
+    s = _c(s, np.float32)
+    rows, half = q.shape
+    out = np.empty((rows, 2 * half), dtype=np.float64)
+    _lib().oracle_unpack_int4_groups(_p(q), _p(s), rows, 2 * half, group, _p(out))
+    return out
+
+
+def rowdot_groups(q4, s4, group: int, q8, d8) -> np.ndarray:
+    q4 = _c(q4, np.uint8)
+    rows, half = q4.shape
+    if group % 32 or (2 * half) % group:
+        raise ValueError("group must be a multiple of 32 that divides the row length")
+    out = np.empty(rows, dtype=np.float32)
+    _lib().oracle_rowdot_groups(_p(q4), _p(_c(s4, np.float32)), group, _p(_c(q8, np.int8)),
+                                _p(_c(d8, np.float32)), rows, 2 * half, _p(out))
     return out
 
 
@@ -173,8 +210,9 @@ def _wbits(q) -> int:
     return 8 if np.asarray(q).dtype == np.int8 else 4
 
 
-def expert(gate_q, gate_s, up_q, up_s, down_q, down_s, xq, xs) -> ExpertOut:
-    """O7 (int4 rows, uint8 [I][H/2]) or its int8 form (int8 rows [I][H])."""
+def expert(gate_q, gate_s, up_q, up_s, down_q, down_s, xq, xs, group: int = 0) -> ExpertOut:
+    """O7 (int4 rows, uint8 [I][H/2]) or its int8 form (int8 rows [I][H]); with
+    group > 0, int4 rows with O16 group scales (gate/up [I][H/group], down [H][I/group])."""
     wb = _wbits(gate_q)
     dt = np.int8 if wb == 8 else np.uint8
     gate_q = _c(gate_q, dt)
@@ -182,10 +220,16 @@ def expert(gate_q, gate_s, up_q, up_s, down_q, down_s, xq, xs) -> ExpertOut:
     H = Hc if wb == 8 else 2 * Hc
     o = ExpertOut(y=np.empty(H, np.float32), g=np.empty(I, np.float32), u=np.empty(I, np.float32),
                   h=np.empty(I, np.float32), hq=np.empty(I, np.int8), hs=np.empty(I // 32, np.float32))
-    _lib().oracle_expert_w(wb, _p(gate_q), _p(_c(gate_s, np.float32)), _p(_c(up_q, dt)),
-                           _p(_c(up_s, np.float32)), _p(_c(down_q, dt)), _p(_c(down_s, np.float32)),
-                           H, I, _p(_c(xq, np.int8)), _p(_c(xs, np.float32)), _p(o.y), _p(o.g), _p(o.u),
-                           _p(o.h), _p(o.hq), _p(o.hs))
+    tail = (H, I, _p(_c(xq, np.int8)), _p(_c(xs, np.float32)), _p(o.y), _p(o.g), _p(o.u), _p(o.h), _p(o.hq),
+            _p(o.hs))
+    heads = (_p(gate_q), _p(_c(gate_s, np.float32)), _p(_c(up_q, dt)), _p(_c(up_s, np.float32)), _p(_c(down_q, dt)),
+             _p(_c(down_s, np.float32)))
+    if group:
+        if wb != 4:
+            raise ValueError("group scales are an int4 format")
+        _lib().oracle_expert_groups(group, *heads, *tail)
+    else:
+        _lib().oracle_expert_w(wb, *heads, *tail)
     return o
 
 
@@ -244,7 +288,7 @@ class _CLayer(ctypes.Structure):
         ("router_w", ctypes.c_void_p), ("router_b", ctypes.c_void_p),
         ("gate_q", ctypes.c_void_p), ("up_q", ctypes.c_void_p), ("down_q", ctypes.c_void_p),
         ("gate_s", ctypes.c_void_p), ("up_s", ctypes.c_void_p), ("down_s", ctypes.c_void_p),
-        ("weight_bits", ctypes.c_int)]
+        ("weight_bits", ctypes.c_int), ("group_size", ctypes.c_int)]
 
 
 def moe_forward(layer, x):
@@ -252,7 +296,9 @@ def moe_forward(layer, x):
     weight_bits (4 if absent) and numpy arrays router_w [E][H], router_b [E],
     gate_q/up_q [E+s][I][H/2] uint8, down_q [E+s][H][I/2] uint8 (int4) or
     gate_q/up_q [E+s][I][H], down_q [E+s][H][I] int8 (int8), gate_s/up_s [E+s][I],
-    down_s [E+s][H]. Returns y [T][H], idx [T][k], w [T][k]."""
+    down_s [E+s][H]; with group_size G > 0 (int4 only) the scales are per group
+    of G columns: gate_s/up_s [E+s][I][H/G], down_s [E+s][H][I/G].
+    Returns y [T][H], idx [T][k], w [T][k]."""
     x = _c(np.atleast_2d(x), np.float32)
     T = x.shape[0]
     wb = getattr(layer, "weight_bits", 4)
@@ -263,7 +309,8 @@ def moe_forward(layer, x):
     cl = _CLayer(layer.H, layer.I, layer.E, layer.top_k, layer.n_group, layer.topk_group,
                  layer.has_shared, layer.route_scale,
                  *[arrs[n].ctypes.data for n in ("router_w", "router_b", "gate_q", "up_q", "down_q",
-                                                 "gate_s", "up_s", "down_s")], wb)
+                                                 "gate_s", "up_s", "down_s")], wb,
+                 getattr(layer, "group_size", 0))
     y = np.empty((T, layer.H), np.float32)
     idx = np.empty((T, layer.top_k), np.int32)
     w = np.empty((T, layer.top_k), np.float32)

@@ -151,6 +151,7 @@ class LayerSpec:
     hot_experts: int = 0             # > 0: that many seeded experts get hot_bias added (chosen by every token)
     hot_bias: float = 2.0
     weight_bits: int = 4             # packed expert format: 4 (two codes per byte) or 8
+    group_size: int = 0              # int4 only: > 0 gives one scale per group of that many columns
 
     @property
     def router_sigma(self) -> float:
@@ -162,9 +163,12 @@ class LayerSpec:
 
     @property
     def expert_bytes(self) -> int:
-        """Packed bytes (int4: two codes per byte; int8: one) + f32 row scales of one
-        expert (gate, up, down)."""
-        return 3 * self.H * self.I * self.weight_bits // 8 + 4 * (2 * self.I + self.H)
+        """Packed bytes (int4: two codes per byte; int8: one) + f32 scales of one
+        expert (gate, up, down): one per row, or one per group of columns."""
+        codes = 3 * self.H * self.I * self.weight_bits // 8
+        if self.group_size:
+            return codes + 4 * 3 * self.H * self.I // self.group_size
+        return codes + 4 * (2 * self.I + self.H)
 
 
 @dataclass(frozen=True)
