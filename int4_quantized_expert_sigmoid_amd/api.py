@@ -49,17 +49,30 @@ class MoELayer:
     gate_q: torch.Tensor     # [E+s][I][H/2] u8 (int4) or [E+s][I][H] i8 (int8)
     up_q: torch.Tensor
     down_q: torch.Tensor     # [E+s][H][I/2] u8 (int4) or [E+s][H][I] i8 (int8)
-    gate_s: torch.Tensor     # [E+s][I] f32
+    gate_s: torch.Tensor     # [E+s][I] f32 ([E+s][I][H/G] with group scales)
     up_s: torch.Tensor
-    down_s: torch.Tensor     # [E+s][H] f32
+    down_s: torch.Tensor     # [E+s][H] f32 ([E+s][H][I/G])
     weight_bits: int = 4
+    group_size: int = 0      # int4 only: > 0 gives one scale per group of that many columns
 
     @classmethod
     def empty(cls, H, I, E, top_k, has_shared=1, n_group=1, topk_group=1, route_scale=1.0, device="cuda",
-              weight_bits=4):
+              weight_bits=4, group_size=0):
         n = E + has_shared
         f32 = torch.float32
         qt, div = (torch.int8, 1) if weight_bits == 8 else (torch.uint8, 2)
+        if group_size:
+            if weight_bits == 8:
+                raise ValueError("group scales are an int4 format")
+            G = group_size
+            return cls(H, I, E, top_k, has_shared, n_group, topk_group, route_scale,
+                       torch.empty((E, H), dtype=f32, device=device), torch.empty(E, dtype=f32, device=device),
+                       torch.empty((n, I, H // 2), dtype=qt, device=device),
+                       torch.empty((n, I, H // 2), dtype=qt, device=device),
+                       torch.empty((n, H, I // 2), dtype=qt, device=device),
+                       torch.empty((n, I, H // G), dtype=f32, device=device),
+                       torch.empty((n, I, H // G), dtype=f32, device=device),
+                       torch.empty((n, H, I // G), dtype=f32, device=device), weight_bits, group_size)
         return cls(H, I, E, top_k, has_shared, n_group, topk_group, route_scale,
                    torch.empty((E, H), dtype=f32, device=device), torch.empty(E, dtype=f32, device=device),
                    torch.empty((n, I, H // div), dtype=qt, device=device),
@@ -72,11 +85,14 @@ class MoELayer:
         return CLayer(self.H, self.I, self.E, self.top_k, self.n_group, self.topk_group, self.has_shared,
                       self.route_scale, *(t.data_ptr() for t in (
                           self.router_w, self.router_b, self.gate_q, self.up_q, self.down_q,
-                          self.gate_s, self.up_s, self.down_s)), self.weight_bits)
+                          self.gate_s, self.up_s, self.down_s)), self.weight_bits, self.group_size)
 
     @property
     def expert_bytes(self) -> int:
-        return 3 * self.H * self.I * self.weight_bits // 8 + 4 * (2 * self.I + self.H)
+        codes = 3 * self.H * self.I * self.weight_bits // 8
+        if self.group_size:
+            return codes + 4 * 3 * self.H * self.I // self.group_size
+        return codes + 4 * (2 * self.I + self.H)
 
 
 @dataclass
@@ -330,6 +346,14 @@ def pack_int4_rows_dev(w: torch.Tensor, q: torch.Tensor, s: torch.Tensor, stream
     rows, cols = w.shape
     check("coli_pack_int4_rows_dev", lib().coli_pack_int4_rows_dev(_ptr(w), rows, cols, _ptr(q), _ptr(s),
                                                                    _stream(stream)))
+
+
+def pack_int4_groups_dev(w: torch.Tensor, group: int, q: torch.Tensor, s: torch.Tensor, stream=None) -> None:
+    """int4 codes and one f32 scale per group of `group` columns of each row (device)."""
+    _dev(w, torch.float32, "w")
+    rows, cols = w.shape
+    check("coli_pack_int4_groups_dev", lib().coli_pack_int4_groups_dev(_ptr(w), rows, cols, group, _ptr(q), _ptr(s),
+                                                                       _stream(stream)))
 
 
 def pack_int8_rows(w: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:

@@ -24,6 +24,16 @@ inline size_t up(size_t v) { return (v + ALIGN - 1) / ALIGN * ALIGN; }
 inline bool al16(const void *p) { return p != nullptr && (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 inline bool al4(const void *p) { return p != nullptr && (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 
+// Group scales: int4 only; the group is whole 32-wide blocks, a power of two
+// of them, and divides both row lengths.
+bool group_ok(int G, int H, int I, int wbits)
+{
+    if (wbits == 8 || G < QK || G > 4096 || G % QK) return false;
+    const int nb = G / QK;
+    if (nb & (nb - 1)) return false;
+    return H % G == 0 && I % G == 0;
+}
+
 bool layer_ok(const coli_moe_layer *L)
 {
     if (!L) return false;
@@ -36,6 +46,7 @@ bool layer_ok(const coli_moe_layer *L)
     if (L->has_shared != 0 && L->has_shared != 1) return false;
     if (!std::isfinite(L->route_scale)) return false;
     if (L->weight_bits != 0 && L->weight_bits != 4 && L->weight_bits != 8) return false;
+    if (L->group_size != 0 && !group_ok(L->group_size, L->H, L->I, L->weight_bits)) return false;
     if (!al4(L->router_w) || !al4(L->router_b)) return false;
     if (!al16(L->gate_q) || !al16(L->up_q) || !al16(L->down_q)) return false;
     if (!al4(L->gate_s) || !al4(L->up_s) || !al4(L->down_s)) return false;
@@ -65,10 +76,12 @@ int choose_path(const coli_moe_layer &L, int T, int flags)
 
 int status(hipError_t e) { return e == hipSuccess ? COLI_OK : COLI_EDEVICE; }
 
-// int8 experts run on the token-GEMV path only (not grouped, not fused).
+// int8 experts and group scales run on the token-GEMV path only (not
+// grouped, not fused).
 int format_ok(const coli_moe_layer &L, int path, int flags)
 {
-    if (L.weight_bits == 8 && (path != 0 || (flags & COLI_PATH_FUSED))) return COLI_EUNSUPPORTED;
+    if ((L.weight_bits == 8 || L.group_size != 0) && (path != 0 || (flags & COLI_PATH_FUSED)))
+        return COLI_EUNSUPPORTED;
     return COLI_OK;
 }
 
@@ -475,6 +488,14 @@ int coli_pack_int4_rows_dev(const float *w, int rows, int cols, uint8_t *q, floa
 {
     if (!al4(w) || !q || !al4(s) || rows < 1 || cols < 2 || (cols & 1)) return COLI_EINVAL;
     return status(launch_pack_int4(w, rows, cols, q, s, (hipStream_t)stream));
+}
+
+int coli_pack_int4_groups_dev(const float *w, int rows, int cols, int group, uint8_t *q, float *s, void *stream)
+{
+    if (!al4(w) || !q || !al4(s) || rows < 1 || group < 2 || group > 4096 || (group & 1) || cols < group ||
+        cols % group)
+        return COLI_EINVAL;
+    return status(launch_pack_int4_groups(w, rows, cols, group, q, s, (hipStream_t)stream));
 }
 
 int coli_pack_int8_rows(const float *w, int rows, int cols, int8_t *q, float *s)

@@ -26,6 +26,7 @@ struct GemvArgs {
     const float *s_a, *s_b;
     int H, I, E, T;
     int has_shared;                // item 0 is the shared expert (expert E, slot t = token t)
+    int gsh;                       // group scales: log2(group / 32) (kernels instantiated with GS)
     int item0;                     // first item of a launch that covers items item0.. only
     const float *x;                // [T][H] layer input (coherent mode quantises it on the fly)
     const int8_t *xq;              // [T][H] reordered Q8(x)
@@ -99,9 +100,13 @@ struct GateUpShared {
 // waves, each streaming 32/RS rows, so fewer loads queue behind each other.
 // ONFLY: Q8(x) is computed here from x instead of read from xq. COHERENT
 // (single-launch path): hq/hs are handed on with device-coherent stores.
-template <int NT, int RC, bool ONFLY, bool COHERENT, int RS = 1, int WB = 4>
+// GS: int4 rows with one scale per group of 32 << gsh columns; each block's
+// term is (S_b * d_b) * s_group, so no row scale is applied at the end.
+template <int NT, int RC, bool ONFLY, bool COHERENT, int RS = 1, int WB = 4, bool GS = false>
 __device__ __forceinline__ void gateup_rows(const GemvArgs &a, const ItemDesc &it, int rb, GateUpShared<NT> &sh)
 {
+    static_assert(!GS || WB == 4, "group scales are an int4 format");
+    constexpr int RG = GS ? RC : 1;              // group scales held per chunk
     constexpr int NP = WFmt<WB>::BLK_BYTES / 16;     // 16-byte pieces per row block
     constexpr double KS = WFmt<WB>::KSCALE;
     constexpr int NV = 2 * RC;                   // values per chunk: RC rows x (gate, up)
@@ -148,26 +153,41 @@ __device__ __forceinline__ void gateup_rows(const GemvArgs &a, const ItemDesc &i
         const int tb = active ? col : 0;
         const uint8_t *pg = a.q_a + (row0 + set * RPS) * rowb + tb * WFmt<WB>::BLK_BYTES;
         const uint8_t *pu = a.q_b + (row0 + set * RPS) * rowb + tb * WFmt<WB>::BLK_BYTES;
+        // group scales of this thread's block column: row stride H / group
+        const long gstr = GS ? (long)(nblk >> a.gsh) : 0;
+        const float *psg = GS ? a.s_a + (row0 + set * RPS) * gstr + (tb >> a.gsh) : nullptr;
+        const float *psu = GS ? a.s_b + (row0 + set * RPS) * gstr + (tb >> a.gsh) : nullptr;
 
         uint4 wg[2][RC][NP], wu[2][RC][NP];
+        float sg[2][RG], su[2][RG];
 #pragma unroll
-        for (int r = 0; r < RC; ++r)
+        for (int r = 0; r < RC; ++r) {
 #pragma unroll
             for (int q = 0; q < NP; ++q) {
                 wg[0][r][q] = load_u4_stream(pg + (long)r * rowb + 16 * q);
                 wu[0][r][q] = load_u4_stream(pu + (long)r * rowb + 16 * q);
             }
+            if constexpr (GS) {
+                sg[0][r] = psg[(long)r * gstr];
+                su[0][r] = psu[(long)r * gstr];
+            }
+        }
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
             const int cur = c & 1;
             if (c + 1 < NC) {
 #pragma unroll
-                for (int r = 0; r < RC; ++r)
+                for (int r = 0; r < RC; ++r) {
 #pragma unroll
                     for (int q = 0; q < NP; ++q) {
                         wg[cur ^ 1][r][q] = load_u4_stream(pg + (long)((c + 1) * RC + r) * rowb + 16 * q);
                         wu[cur ^ 1][r][q] = load_u4_stream(pu + (long)((c + 1) * RC + r) * rowb + 16 * q);
                     }
+                    if constexpr (GS) {
+                        sg[cur ^ 1][r] = psg[(long)((c + 1) * RC + r) * gstr];
+                        su[cur ^ 1][r] = psu[(long)((c + 1) * RC + r) * gstr];
+                    }
+                }
             }
             double v[NT][NV];
 #pragma unroll
@@ -177,6 +197,10 @@ __device__ __forceinline__ void gateup_rows(const GemvArgs &a, const ItemDesc &i
                     if (s > 0 && s >= ntu) break;    // slot 0 is always in use
                     v[s][2 * r] = (double)dot_block_w<WB>(wg[cur][r], act[s]) * dsc[s];
                     v[s][2 * r + 1] = (double)dot_block_w<WB>(wu[cur][r], act[s]) * dsc[s];
+                    if constexpr (GS) {
+                        v[s][2 * r] *= (double)sg[cur][r];
+                        v[s][2 * r + 1] *= (double)su[cur][r];
+                    }
                 }
             }
             const int vi = transpose_index<NV>(lane);
@@ -196,8 +220,8 @@ __device__ __forceinline__ void gateup_rows(const GemvArgs &a, const ItemDesc &i
         double g = sh.red[0][s][2 * r], u = sh.red[0][s][2 * r + 1];
         for (int w = 1; w < nw; ++w) { g += sh.red[w][s][2 * r]; u += sh.red[w][s][2 * r + 1]; }
         const long grow = row0 + r;
-        const float gf = (float)((double)a.s_a[grow] * g);
-        const float uf = (float)((double)a.s_b[grow] * u);
+        const float gf = GS ? (float)g : (float)((double)a.s_a[grow] * g);
+        const float uf = GS ? (float)u : (float)((double)a.s_b[grow] * u);
         const float hv = (float)(silu_f64((double)gf) * (double)uf);
         const float amax = wave_max(fabsf(hv), 32);
         float d, id;
@@ -225,10 +249,13 @@ __device__ __forceinline__ void gateup_rows(const GemvArgs &a, const ItemDesc &i
 // Down rows of one item for row group grp of 4*RPW rows (each wave RPW rows,
 // lane l owns block column l; chunks of RD rows with the next chunk's loads in
 // flight); writes ye of pairs item*8 + slot. blockDim = 256. COHERENT: hq/hs
-// are read and ye is written with device-coherent accesses.
-template <int NT, int RD, bool COHERENT, int RPW, int WB = 4>
+// are read and ye is written with device-coherent accesses. GS: group
+// scales, as gateup_rows.
+template <int NT, int RD, bool COHERENT, int RPW, int WB = 4, bool GS = false>
 __device__ __forceinline__ void down_rows(const GemvArgs &a, const ItemDesc &it, int grp)
 {
+    static_assert(!GS || WB == 4, "group scales are an int4 format");
+    constexpr int RG = GS ? RD : 1;
     constexpr int NP = WFmt<WB>::BLK_BYTES / 16;
     constexpr double KS = WFmt<WB>::KSCALE;
     constexpr int NC = RPW / RD;
@@ -239,12 +266,17 @@ __device__ __forceinline__ void down_rows(const GemvArgs &a, const ItemDesc &it,
     const long row0 = (long)grp * (4 * RPW) + wave * RPW;
     const int ntu = __builtin_amdgcn_readfirstlane(it.nt);
     const uint8_t *pd = a.q_a + ((long)it.e * a.H + row0) * rowb + (active ? lane : 0) * WFmt<WB>::BLK_BYTES;
+    const long gstr = GS ? (long)(nblk >> a.gsh) : 0;     // group scales per row: I / group
+    const float *psd = GS ? a.s_a + ((long)it.e * a.H + row0) * gstr + ((active ? lane : 0) >> a.gsh) : nullptr;
 
     uint4 wd[2][RD][NP];
+    float sd[2][RG];
 #pragma unroll
-    for (int r = 0; r < RD; ++r)
+    for (int r = 0; r < RD; ++r) {
 #pragma unroll
         for (int q = 0; q < NP; ++q) wd[0][r][q] = load_u4_stream(pd + (long)r * rowb + 16 * q);
+        if constexpr (GS) sd[0][r] = psd[(long)r * gstr];
+    }
 
     Blk8 act[NT];
     double dsc[NT];
@@ -272,10 +304,12 @@ __device__ __forceinline__ void down_rows(const GemvArgs &a, const ItemDesc &it,
         const int cur = c & 1;
         if (c + 1 < NC) {
 #pragma unroll
-            for (int r = 0; r < RD; ++r)
+            for (int r = 0; r < RD; ++r) {
 #pragma unroll
                 for (int q = 0; q < NP; ++q)
                     wd[cur ^ 1][r][q] = load_u4_stream(pd + (long)((c + 1) * RD + r) * rowb + 16 * q);
+                if constexpr (GS) sd[cur ^ 1][r] = psd[(long)((c + 1) * RD + r) * gstr];
+            }
         }
         double v[NT][RD];
 #pragma unroll
@@ -284,6 +318,7 @@ __device__ __forceinline__ void down_rows(const GemvArgs &a, const ItemDesc &it,
             for (int s = 0; s < NT; ++s) {
                 if (s > 0 && s >= ntu) break;        // slot 0 is always in use
                 v[s][r] = (double)dot_block_w<WB>(wd[cur][r], act[s]) * dsc[s];
+                if constexpr (GS) v[s][r] *= (double)sd[cur][r];
             }
         }
         const int vi = transpose_index<RD>(lane);
@@ -294,7 +329,7 @@ __device__ __forceinline__ void down_rows(const GemvArgs &a, const ItemDesc &it,
             if ((lane & (64 / RD - 1)) == 0) {
                 const long row = row0 + c * RD + vi;
                 const long pair = (long)it.item * MAX_SLOTS + s;
-                const float out = (float)((double)a.s_a[(long)it.e * a.H + row] * v[s][0]);
+                const float out = GS ? (float)v[s][0] : (float)((double)a.s_a[(long)it.e * a.H + row] * v[s][0]);
                 if constexpr (COHERENT) st_dev(a.ye + pair * a.H + row, out);
                 else a.ye[pair * a.H + row] = out;
             }

@@ -71,8 +71,17 @@ enum CtrlWord { CTRL_N_ITEMS = 0, CTRL_N_TILES_GU = 1, CTRL_N_TILES_DN = 2, CTRL
 // ---- quantisation, packing, norms (kernels_quant.hip)
 hipError_t launch_quant_q8(const float *x, int T, int H, int8_t *xq, float *xs, bool reorder, hipStream_t s);
 hipError_t launch_reorder_q8(const int8_t *xq_nat, int n, int8_t *xq_perm, hipStream_t s);
+// log2(group / 32) of a layer with group scales (0 without them).
+inline int group_shift(const coli_moe_layer &L)
+{
+    int sh = 0;
+    while (L.group_size > 0 && (QK << sh) < L.group_size) ++sh;
+    return sh;
+}
+
 hipError_t launch_pack_int4(const float *w, int rows, int cols, uint8_t *q, float *sc, hipStream_t s);
 hipError_t launch_pack_int8(const float *w, int rows, int cols, int8_t *q, float *sc, hipStream_t s);
+hipError_t launch_pack_int4_groups(const float *w, int rows, int cols, int group, uint8_t *q, float *sc, hipStream_t s);
 hipError_t launch_rmsnorm(const float *x, const float *g, int T, int H, float eps, float *out, hipStream_t s);
 // The float4 order of the RMSNorm sums (x 16-byte aligned, H % 4 == 0): the
 // same rule wherever a row's scale is taken.

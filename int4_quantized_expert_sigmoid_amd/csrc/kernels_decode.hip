@@ -174,14 +174,14 @@ struct SelGuShared {
     DecUnion u;
 };
 
-template <int NT, int KPL, int WB>
+template <int NT, int KPL, int WB, bool GS>
 __global__ void __launch_bounds__(256) k_select_gateup(SelGuArgs a, GemvArgs g, int n_shared_wg)
 {
     __shared__ GateUpShared<NT> sh;
     __shared__ SelGuShared su;
     TRACE(a, 1, 0);
     if ((int)blockIdx.x < n_shared_wg) {         // the shared expert: no routing needed
-        gateup_rows<NT, GemvTuneW<NT, WB>::RC, false, false, 1, WB>(g, shared_item(g), blockIdx.x, sh);
+        gateup_rows<NT, GemvTuneW<NT, WB>::RC, false, false, 1, WB, GS>(g, shared_item(g), blockIdx.x, sh);
         TRACE(a, 1, 2);
         return;
     }
@@ -220,15 +220,16 @@ __global__ void __launch_bounds__(256) k_select_gateup(SelGuArgs a, GemvArgs g, 
     it.nt = u.item_nt[item];
 #pragma unroll
     for (int s = 0; s < MAX_SLOTS; ++s) it.tok[s] = s < it.nt ? u.item_tok[item * MAX_SLOTS + s] : 0;
-    gateup_rows<NT, GemvTuneW<NT, WB>::RC, false, false, 1, WB>(g, it, rb, sh);
+    gateup_rows<NT, GemvTuneW<NT, WB>::RC, false, false, 1, WB, GS>(g, it, rb, sh);
     TRACE(a, 1, 2);
 }
 
 // ------------------------------------------------------------ launch 3
 struct DnArgs {
     const uint8_t *q;          // down_q [E+shared][H][I/2] (int4) or [E+shared][H][I] (int8)
-    const float *s;            // down_s [E+shared][H]
+    const float *s;            // down_s [E+shared][H], or [E+shared][H][I/group] with group scales
     int H, I, E, T, top_k, has_shared;
+    int gsh;                   // group scales: log2(group / 32)
     int max_items;             // entries of the item tables (<= DEC_MAX_ITEMS)
     const int *ctrl, *item_expert, *item_ntok;
     const int8_t *hq;          // [pairs][I] reordered
@@ -245,18 +246,19 @@ struct DnArgs {
 
 // One item's slice: the workgroup's RPU rows of the item's down matrix (lane
 // l holds block column l of each row) and the activations of up to NT token
-// slots.
-template <int NT, int RPU, int WB>
+// slots; with group scales (GS) also the scale of each row's group.
+template <int NT, int RPU, int WB, bool GS>
 struct DnStage {
     uint4 wd[RPU][WFmt<WB>::BLK_BYTES / 16];
+    float sw[GS ? RPU : 1];
     Blk8 act[NT];
     float ds[NT];              // block scales as loaded (turned to f64 where used, so a load is never waited for early)
     int e, nt;
 };
 
-template <int NT, int RPU, int WB>
+template <int NT, int RPU, int WB, bool GS>
 __device__ __forceinline__ void dn_load_e(const DnArgs &a, int item, long row0, int lane, int e, int nt,
-                                          DnStage<NT, RPU, WB> &st)
+                                          DnStage<NT, RPU, WB, GS> &st)
 {
     constexpr int NP = WFmt<WB>::BLK_BYTES / 16;
     const int nblk = a.I / QK;
@@ -269,6 +271,12 @@ __device__ __forceinline__ void dn_load_e(const DnArgs &a, int item, long row0, 
     for (int r = 0; r < RPU; ++r)
 #pragma unroll
         for (int q = 0; q < NP; ++q) st.wd[r][q] = load_u4_stream(pd + (long)r * rowb + 16 * q);
+    if constexpr (GS) {
+        const long gstr = nblk >> a.gsh;         // group scales per row: I / group
+        const float *ps = a.s + ((long)st.e * a.H + row0) * gstr + ((active ? lane : 0) >> a.gsh);
+#pragma unroll
+        for (int r = 0; r < RPU; ++r) st.sw[r] = ps[(long)r * gstr];
+    }
 #pragma unroll
     for (int s = 0; s < NT; ++s) {
         if (s < st.nt && active) {
@@ -285,16 +293,16 @@ __device__ __forceinline__ void dn_load_e(const DnArgs &a, int item, long row0, 
 
 // The same for an item of the union, its expert and token count from the
 // table in LDS.
-template <int NT, int RPU, int WB>
+template <int NT, int RPU, int WB, bool GS>
 __device__ __forceinline__ void dn_load(const DnArgs &a, int item, long row0, int lane, const int *it_e,
-                                        const int *it_nt, DnStage<NT, RPU, WB> &st)
+                                        const int *it_nt, DnStage<NT, RPU, WB, GS> &st)
 {
     dn_load_e(a, item, row0, lane, it_e[item], it_nt[item], st);
 }
 
-template <int NT, int RPU, int WB>
+template <int NT, int RPU, int WB, bool GS>
 __device__ __forceinline__ void dn_compute(const DnArgs &a, int item, long row0, int lane,
-                                           const DnStage<NT, RPU, WB> &st, float *ye_l)
+                                           const DnStage<NT, RPU, WB, GS> &st, float *ye_l)
 {
     const int ntu = __builtin_amdgcn_readfirstlane(st.nt);   // slots past it cost no dot products
     double v[NT][RPU];
@@ -304,6 +312,7 @@ __device__ __forceinline__ void dn_compute(const DnArgs &a, int item, long row0,
         for (int s = 0; s < NT; ++s) {
             if (s > 0 && s >= ntu) break;            // slot 0 is always in use
             v[s][r] = (double)dot_block_w<WB>(st.wd[r], st.act[s]) * ((double)st.ds[s] * WFmt<WB>::KSCALE);
+            if constexpr (GS) v[s][r] *= (double)st.sw[r];
         }
     }
     const int vi = transpose_index<RPU>(lane);
@@ -314,7 +323,7 @@ __device__ __forceinline__ void dn_compute(const DnArgs &a, int item, long row0,
         if ((lane & (64 / RPU - 1)) == 0) {
             const long row = row0 + vi;
             const long pair = (long)item * MAX_SLOTS + s;
-            const float out = (float)((double)a.s[(long)st.e * a.H + row] * v[s][0]);
+            const float out = GS ? (float)v[s][0] : (float)((double)a.s[(long)st.e * a.H + row] * v[s][0]);
             a.ye[pair * a.H + row] = out;
             ye_l[pair * RPU + vi] = out;
         }
@@ -326,7 +335,7 @@ __device__ __forceinline__ void dn_compute(const DnArgs &a, int item, long row0,
 // at once with the wave's next item already loading (wave 0 starts on the
 // shared expert at once); then the per-pair row values in LDS are combined
 // into y.
-template <int NT, int RPU, int WB>
+template <int NT, int RPU, int WB, bool GS>
 __global__ void __launch_bounds__(256) k_down_combine(DnArgs a)
 {
     extern __shared__ float ye_l[];              // [max pairs][RPU]
@@ -334,7 +343,7 @@ __global__ void __launch_bounds__(256) k_down_combine(DnArgs a)
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwave = blockDim.x >> 6;
     const long row0 = (long)blockIdx.x * RPU;
     TRACE(a, 2, 0);
-    DnStage<NT, RPU, WB> A, B;
+    DnStage<NT, RPU, WB, GS> A, B;
     // the shared expert is item 0 with T token slots whatever the routing:
     // wave 0 starts loading it before the item table arrives
     const bool early = a.has_shared && wave == 0;
@@ -391,17 +400,18 @@ GemvArgs gemv_view(const coli_moe_layer &L, int T, const WsLayout &lay, char *ws
     g.hs = reinterpret_cast<float *>(ws + lay.hs);
     g.ye = reinterpret_cast<float *>(ws + lay.ye);
     g.q_a = L.gate_q; g.s_a = L.gate_s; g.q_b = L.up_q; g.s_b = L.up_s;
+    g.gsh = group_shift(L);
     return g;
 }
 
 // keys per lane of the selection: E <= 64 * KPL
-template <int NT, int WB>
+template <int NT, int WB, bool GS = false>
 hipError_t launch_sel_nt(int E, dim3 grid, const SelGuArgs &a, const GemvArgs &g, int nsh, hipStream_t s)
 {
-    if (E <= 64) COLI_LAUNCH((k_select_gateup<NT, 1, WB>), grid, dim3(256), 0, s, a, g, nsh);
-    else if (E <= 128) COLI_LAUNCH((k_select_gateup<NT, 2, WB>), grid, dim3(256), 0, s, a, g, nsh);
-    else if (E <= 256) COLI_LAUNCH((k_select_gateup<NT, 4, WB>), grid, dim3(256), 0, s, a, g, nsh);
-    else COLI_LAUNCH((k_select_gateup<NT, 8, WB>), grid, dim3(256), 0, s, a, g, nsh);
+    if (E <= 64) COLI_LAUNCH((k_select_gateup<NT, 1, WB, GS>), grid, dim3(256), 0, s, a, g, nsh);
+    else if (E <= 128) COLI_LAUNCH((k_select_gateup<NT, 2, WB, GS>), grid, dim3(256), 0, s, a, g, nsh);
+    else if (E <= 256) COLI_LAUNCH((k_select_gateup<NT, 4, WB, GS>), grid, dim3(256), 0, s, a, g, nsh);
+    else COLI_LAUNCH((k_select_gateup<NT, 8, WB, GS>), grid, dim3(256), 0, s, a, g, nsh);
     return hipGetLastError();
 }
 
@@ -409,15 +419,16 @@ template <int NT>
 hipError_t launch_sel_wb(const coli_moe_layer &L, dim3 grid, const SelGuArgs &a, const GemvArgs &g, int nsh,
                          hipStream_t s)
 {
+    if (L.group_size) return launch_sel_nt<NT, 4, true>(L.E, grid, a, g, nsh, s);
     return L.weight_bits == 8 ? launch_sel_nt<NT, 8>(L.E, grid, a, g, nsh, s)
                               : launch_sel_nt<NT, 4>(L.E, grid, a, g, nsh, s);
 }
 
-template <int NT, int RPU, int WB>
+template <int NT, int RPU, int WB, bool GS = false>
 hipError_t launch_dn_nt(const coli_moe_layer &L, const WsLayout &lay, const DnArgs &a, hipStream_t s)
 {
     const size_t lds = (size_t)lay.max_items * MAX_SLOTS * RPU * sizeof(float);
-    COLI_LAUNCH((k_down_combine<NT, RPU, WB>), dim3((unsigned)(L.H / RPU)), dim3(256), lds, s, a);
+    COLI_LAUNCH((k_down_combine<NT, RPU, WB, GS>), dim3((unsigned)(L.H / RPU)), dim3(256), lds, s, a);
     return hipGetLastError();
 }
 
@@ -486,6 +497,7 @@ hipError_t launch_decode_down_combine(const coli_moe_layer &L, int T, const WsLa
     DnArgs a;
     a.q = L.down_q; a.s = L.down_s;
     a.H = L.H; a.I = L.I; a.E = L.E; a.T = T; a.top_k = L.top_k; a.has_shared = L.has_shared;
+    a.gsh = group_shift(L);
     a.max_items = lay.max_items < DEC_MAX_ITEMS ? lay.max_items : DEC_MAX_ITEMS;
     a.ctrl = reinterpret_cast<const int *>(ws + lay.ctrl);
     a.item_expert = reinterpret_cast<const int *>(ws + lay.item_expert);
@@ -505,6 +517,10 @@ hipError_t launch_decode_down_combine(const coli_moe_layer &L, int T, const WsLa
     if (L.weight_bits == 8) {
         if (T <= 1) return launch_dn_nt<1, 4, 8>(L, lay, a, s);
         return launch_dn_nt<2, 2, 8>(L, lay, a, s);
+    }
+    if (L.group_size) {
+        if (T <= 1) return launch_dn_nt<1, 8, 4, true>(L, lay, a, s);
+        return launch_dn_nt<2, 4, 4, true>(L, lay, a, s);
     }
     if (T <= 1) return launch_dn_nt<1, 8, 4>(L, lay, a, s);
     return launch_dn_nt<2, 4, 4>(L, lay, a, s);

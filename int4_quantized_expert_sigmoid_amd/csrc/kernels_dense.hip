@@ -186,7 +186,7 @@ hipError_t launch_dense_gemv(const DenseLayer &M, int T, const DenseLayout &lay,
 {
     GemvArgs g;
     g.q_a = M.gate_q; g.s_a = M.gate_s; g.q_b = M.up_q; g.s_b = M.up_s;
-    g.H = M.H; g.I = M.I; g.E = 0; g.T = T; g.has_shared = 0; g.item0 = 0; g.x = nullptr;
+    g.H = M.H; g.I = M.I; g.E = 0; g.T = T; g.has_shared = 0; g.gsh = 0; g.item0 = 0; g.x = nullptr;
     g.xq = reinterpret_cast<const int8_t *>(ws + lay.xq);
     g.xs = reinterpret_cast<const float *>(ws + lay.xs);
     g.ctrl = nullptr; g.item_expert = nullptr; g.item_ntok = nullptr; g.item_tok = nullptr;

@@ -246,7 +246,7 @@ hipError_t launch_decode_fused(const coli_moe_layer &L, const float *x, int T, c
     FusedArgs a;
     // gate/up and down views of the GEMV arguments
     GemvArgs g;
-    g.H = L.H; g.I = L.I; g.E = L.E; g.T = T; g.has_shared = L.has_shared; g.item0 = 0;
+    g.H = L.H; g.I = L.I; g.E = L.E; g.T = T; g.has_shared = L.has_shared; g.gsh = 0; g.item0 = 0;
     g.xq = reinterpret_cast<const int8_t *>(ws + lay.xq);
     g.xs = reinterpret_cast<const float *>(ws + lay.xs);
     g.ctrl = reinterpret_cast<const int *>(ws + lay.ctrl);

@@ -95,6 +95,29 @@ __global__ void __launch_bounds__(256) k_pack_int4(const float *__restrict__ w, 
     if (threadIdx.x == 0) sc[row] = d;
 }
 
+// Group scales: one workgroup per row, one thread per group of G columns,
+// each group packed as k_pack_int4 packs a row.
+__global__ void __launch_bounds__(256) k_pack_int4_groups(const float *__restrict__ w, int cols, int G,
+                                                          uint8_t *__restrict__ q, float *__restrict__ sc)
+{
+    const long row = blockIdx.x;
+    const int ng = cols / G;
+    for (int g = threadIdx.x; g < ng; g += blockDim.x) {
+        const float *src = w + row * (long)cols + (long)g * G;
+        float amax = 0.0f;
+        for (int c = 0; c < G; ++c) amax = fmaxf(amax, fabsf(src[c]));
+        const float d = __fdiv_rn(amax, 7.0f);
+        const float id = (d != 0.0f) ? __fdiv_rn(1.0f, d) : 0.0f;
+        uint8_t *dst = q + row * (long)(cols / 2) + (long)g * (G / 2);
+        for (int j = 0; j < G / 2; ++j) {
+            const int lo = round_clamp(__fmul_rn(src[2 * j], id), -8.0f, 7.0f);
+            const int hi = round_clamp(__fmul_rn(src[2 * j + 1], id), -8.0f, 7.0f);
+            dst[j] = (uint8_t)((lo & 0xF) | ((hi & 0xF) << 4));
+        }
+        sc[row * ng + g] = d;
+    }
+}
+
 // int8 rows: d = absmax/127, codes clamp(rint(w/d), -127, 127); within each
 // group of 8 columns column c goes to byte perm8(c) (0,2,4,6 then 1,3,5,7).
 __global__ void __launch_bounds__(256) k_pack_int8(const float *__restrict__ w, int cols,
@@ -192,6 +215,12 @@ hipError_t launch_reorder_q8(const int8_t *xq_nat, int n, int8_t *xq_perm, hipSt
 hipError_t launch_pack_int4(const float *w, int rows, int cols, uint8_t *q, float *sc, hipStream_t s)
 {
     COLI_LAUNCH(k_pack_int4, dim3(rows), dim3(256), 0, s, w, cols, q, sc);
+    return hipGetLastError();
+}
+
+hipError_t launch_pack_int4_groups(const float *w, int rows, int cols, int group, uint8_t *q, float *sc, hipStream_t s)
+{
+    COLI_LAUNCH(k_pack_int4_groups, dim3(rows), dim3(256), 0, s, w, cols, group, q, sc);
     return hipGetLastError();
 }
 

@@ -3,7 +3,7 @@
 Weights come from the seeded generator (synth/, counter-addressed, its device
 twin writes f32 rows straight into HBM) and are packed to int4 on the GPU by
 the library's own packer (coli_pack_int4_rows_dev, or coli_pack_int8_rows_dev
-for int8 experts). Router weights, bias,
+for int8 experts, coli_pack_int4_groups_dev for group scales). Router weights, bias,
 tokens and RMSNorm gains are small and generated on the host.
 """
 from __future__ import annotations
@@ -13,14 +13,17 @@ import torch
 
 from synth import synth as S
 
-from .api import DenseMLP, MoELayer, pack_int4_rows_dev, pack_int8_rows_dev
+from .api import DenseMLP, MoELayer, pack_int4_groups_dev, pack_int4_rows_dev, pack_int8_rows_dev
 
 
 def device_layer(spec: S.LayerSpec, seed: int = 0, layer: int = 0, device: str = "cuda",
                  scratch: torch.Tensor = None) -> MoELayer:
     L = MoELayer.empty(spec.H, spec.I, spec.E, spec.top_k, spec.has_shared, spec.n_group, spec.topk_group,
-                       spec.route_scale, device=device, weight_bits=spec.weight_bits)
-    pack = pack_int8_rows_dev if spec.weight_bits == 8 else pack_int4_rows_dev
+                       spec.route_scale, device=device, weight_bits=spec.weight_bits, group_size=spec.group_size)
+    if spec.group_size:
+        pack = lambda w, q, s: pack_int4_groups_dev(w, spec.group_size, q, s)
+    else:
+        pack = pack_int8_rows_dev if spec.weight_bits == 8 else pack_int4_rows_dev
     W, b = S.router(spec, seed, layer)
     L.router_w.copy_(torch.from_numpy(W))
     L.router_b.copy_(torch.from_numpy(b))

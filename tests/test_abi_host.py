@@ -44,6 +44,7 @@ def fake_layer(H=6144, I=2048, E=256, k=8, **kw):
     L = CLayer(args["H"], args["I"], args["E"], args["top_k"], args["n_group"], args["topk_group"],
                args["has_shared"], args["route_scale"], p, p, p, p, p, p, p, p)
     L.weight_bits = args.get("weight_bits", 4)
+    L.group_size = args.get("group_size", 0)
     return L
 
 
@@ -66,6 +67,8 @@ def test_workspace_sizes():
     dict(H=48), dict(I=40), dict(E=0), dict(E=600), dict(top_k=0), dict(top_k=17), dict(top_k=9, E=8),
     dict(n_group=3), dict(n_group=8, topk_group=9), dict(n_group=8, topk_group=1, top_k=33),
     dict(has_shared=2), dict(route_scale=float("nan")), dict(weight_bits=5), dict(weight_bits=16),
+    dict(group_size=16), dict(group_size=48), dict(group_size=96), dict(group_size=-32),
+    dict(group_size=4096), dict(group_size=32, weight_bits=8), dict(group_size=64, I=2080),
 ])
 def test_invalid_layers_rejected(bad):
     L = fake_layer(**bad)
@@ -200,6 +203,29 @@ def test_int8_experts_only_on_the_gemv_path():
     assert F(ctypes.byref(L), p, 1, p, 8, p, 1 << 40, None) == _lib.COLI_EUNSUPPORTED      # fused
     X = lib().coli_moe_experts
     assert X(ctypes.byref(L), p, p, p, p, 9, p, 0, p, 1 << 40, None) == _lib.COLI_EUNSUPPORTED
+
+
+def test_group_scales_only_on_the_gemv_path():
+    """Group-scaled int4 experts: valid groups are accepted (workspace sized),
+    and like int8 they run on the token-GEMV path only."""
+    for G in (32, 64, 128, 256, 2048):
+        assert ws_bytes(fake_layer(group_size=G), 4) > 0, G
+    L = fake_layer(group_size=32)
+    p = ctypes.c_void_p(1 << 20)
+    F = lib().coli_moe_forward
+    assert F(ctypes.byref(L), p, 9, p, 0, p, 1 << 40, None) == _lib.COLI_EUNSUPPORTED      # grouped batch
+    assert F(ctypes.byref(L), p, 4, p, 4, p, 1 << 40, None) == _lib.COLI_EUNSUPPORTED      # forced grouped
+    assert F(ctypes.byref(L), p, 1, p, 8, p, 1 << 40, None) == _lib.COLI_EUNSUPPORTED      # fused
+    X = lib().coli_moe_experts
+    assert X(ctypes.byref(L), p, p, p, p, 9, p, 0, p, 1 << 40, None) == _lib.COLI_EUNSUPPORTED
+
+
+def test_group_packer_argument_errors():
+    P = lib().coli_pack_int4_groups_dev
+    p = ctypes.c_void_p(1 << 20)
+    for rows, cols, G in ((0, 64, 32), (4, 64, 3), (4, 64, 0), (4, 96, 64), (4, 32, 64), (4, 8192, 8192)):
+        assert P(p, rows, cols, G, p, p, None) == _lib.COLI_EINVAL, (rows, cols, G)
+    assert P(None, 4, 64, 32, p, p, None) == _lib.COLI_EINVAL
 
 
 def _perm8(j):

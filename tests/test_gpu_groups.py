@@ -1,0 +1,183 @@
+"""GPU parity of the group-scaled int4 experts (one f32 scale per group of
+columns, the scale-granularity variant) through the C ABI: the device packer
+bit-exact against the oracle's packer, whole layers against the oracle on
+the token-GEMV path (tiny and GLM-5.2-shaped, groups of 32, 64 and 128),
+the expert stage fed the oracle's routing, and the refusals off that path.
+
+Every block term s_g * (d_b * S_b) is computed exactly as the oracle
+computes it, but the f64 block sums run in another order, so a row product
+can land one f32 ulp away from the oracle's (rarely: the f64 sums differ in
+their last bits only). Routing is bit-exact; h is within 2 ulp; a Q8(h) code
+may then move by one where h * (1/d) sits on a rounding boundary; the
+outputs are within the floating-point bar TOL."""
+import numpy as np
+import pytest
+import torch
+from dataclasses import replace
+
+from int4_quantized_expert_sigmoid_amd import api, COLI_ACCUMULATE
+from int4_quantized_expert_sigmoid_amd._lib import ColiError, COLI_EUNSUPPORTED, COLI_PATH_FUSED, COLI_PATH_GROUPED
+from int4_quantized_expert_sigmoid_amd.synthetic import device_layer
+from oracle import layers as OL
+from oracle import oracle as O
+from synth import synth as S
+
+from gpu_common import dev, rel_err, unreorder, ws_views
+
+pytestmark = pytest.mark.gpu
+TOL = 1e-4
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    torch.cuda.set_device(0)
+
+
+@pytest.mark.parametrize("G", [32, 64, 128])
+def test_pack_groups_dev_matches_oracle(G):
+    r = np.random.default_rng(G)
+    mats = [S.expert_matrix(replace(S.GLM52, group_size=G), 0, 0, 5, S.DOWN),
+            (r.standard_normal((64, 512)) * 0.02).astype(np.float32)]
+    for w in mats:
+        w = np.ascontiguousarray(w, np.float32)
+        w[0, :] = 0.0                                   # zero row
+        w[1, 3] = 1e30                                  # one huge element in group 0
+        w[2, G:2 * G] = 0.0                             # one zero group
+        q_o, s_o = O.pack_int4_groups(w, G)
+        q_d = torch.empty((w.shape[0], w.shape[1] // 2), dtype=torch.uint8, device="cuda")
+        s_d = torch.empty((w.shape[0], w.shape[1] // G), dtype=torch.float32, device="cuda")
+        api.pack_int4_groups_dev(dev(w), G, q_d, s_d)
+        torch.cuda.synchronize()
+        assert np.array_equal(q_d.cpu().numpy(), q_o)
+        assert np.array_equal(s_d.cpu().numpy(), s_o)
+
+
+def _ulps(a, b):
+    a = a.astype(np.float32); b = b.astype(np.float32)
+    return np.abs(a.astype(np.float64) - b.astype(np.float64)) / np.spacing(np.maximum(np.abs(a), np.abs(b)))
+
+
+def _check(L, ref_tokens, T, ws, y):
+    v = ws_views(L, T, ws)
+    assert v["path"] == 0
+    n_codes = n_moved = 0
+    for t, r in enumerate(ref_tokens):
+        assert np.array_equal(v["idx"][t], r.idx)
+        pairs = list(v["pair_of"][t]) + [v["shared_pair"][t]]
+        for p, eo in zip(pairs, r.experts):
+            assert _ulps(v["h"][p], eo.h).max() <= 2, f"h token {t} pair {p}"
+            hq = unreorder(v["hq"][p]).astype(np.int32)
+            d = np.abs(hq - eo.hq.astype(np.int32))
+            assert d.max() <= 1
+            n_codes += d.size
+            n_moved += int((d > 0).sum())
+            assert _ulps(v["hs"][p], eo.hs).max() <= 2
+    y_o = np.stack([r.y for r in ref_tokens])
+    err = rel_err(y, y_o).max()
+    say(f"  max rel {err:.2e}, bit-identical {np.mean(y == y_o):.4f}, Q8(h) codes moved {n_moved}/{n_codes}")
+    assert n_moved <= max(2, n_codes // 10000)
+    assert err <= TOL
+
+
+@pytest.fixture(scope="module", params=[32, 64, 128])
+def tiny_g(request):
+    spec = replace(S.TINY, group_size=request.param)
+    return spec, device_layer(spec, 0, 0), OL.full_layer(spec, 0, 0)
+
+
+@pytest.mark.parametrize("T", [1, 2, 3, 5, 8])
+def test_forward_tiny_groups(tiny_g, T):
+    spec, L, ref = tiny_g
+    x = S.tokens(S.TokenSpec(T=T, token_set=400 + T, outlier_channels=2), spec.H, 0)
+    ws = api.workspace(L, T)
+    say(f"forward tiny groups G={spec.group_size} T={T}")
+    y = api.moe_forward(L, dev(x), ws).cpu().numpy()
+    cache = OL.ExpertCache(spec, 0, 0)
+    toks = [OL.forward_token(spec, cache, ref.router_w, ref.router_b, x[t]) for t in range(T)]
+    _check(L, toks, T, ws, y)
+    y_o, _, _ = O.moe_forward(ref, x)
+    assert rel_err(y, y_o).max() <= TOL
+    # accumulate into a nonzero y
+    y0 = np.full((T, spec.H), 0.5, np.float32)
+    yd = dev(y0)
+    api.moe_forward(L, dev(x), ws, y=yd, flags=COLI_ACCUMULATE)
+    assert rel_err(yd.cpu().numpy(), (np.float32(0.5) + y_o).astype(np.float32)).max() <= TOL
+
+
+def test_groups_spanning_the_row_equal_the_row_format():
+    """H = I = G: one group per row, the same codes and scales as the row
+    format. The group kernels scale every block term and the row kernels the
+    block sum, so the two agree to the last bits of f64 sums: within the
+    bar, nearly every output bit for bit."""
+    sp = replace(S.TINY, H=128, I=128, E=8, top_k=2)
+    La = device_layer(sp, 0, 0)
+    Lb = device_layer(replace(sp, group_size=128), 0, 0)
+    for name in ("gate_q", "up_q", "down_q"):
+        assert torch.equal(getattr(La, name), getattr(Lb, name))
+    for name in ("gate_s", "up_s", "down_s"):
+        assert torch.equal(getattr(La, name).flatten(), getattr(Lb, name).flatten())
+    for T in (1, 2, 4, 8):
+        x = S.tokens(S.TokenSpec(T=T, token_set=500 + T), sp.H, 0)
+        ya = api.moe_forward(La, dev(x), api.workspace(La, T)).cpu().numpy()
+        yb = api.moe_forward(Lb, dev(x), api.workspace(Lb, T)).cpu().numpy()
+        say(f"groups spanning the row T={T}: max rel {rel_err(yb, ya).max():.2e}, identical {np.mean(ya == yb):.4f}")
+        assert rel_err(yb, ya).max() <= TOL
+        assert np.mean(ya == yb) >= 0.99
+
+
+def test_groups_refused_off_the_gemv_path():
+    spec = replace(S.TINY, group_size=32)
+    L = device_layer(spec, 0, 0)
+    x = S.tokens(S.TokenSpec(T=9, token_set=1), spec.H, 0)
+    with pytest.raises(ColiError) as e:
+        api.moe_forward(L, dev(x), api.workspace(L, 9))
+    assert e.value.code == COLI_EUNSUPPORTED
+    ws1 = api.workspace(L, 1)
+    for flags in (COLI_PATH_FUSED, COLI_PATH_GROUPED):
+        with pytest.raises(ColiError) as e:
+            api.moe_forward(L, dev(x[:1]), ws1, flags=flags)
+        assert e.value.code == COLI_EUNSUPPORTED
+
+
+@pytest.fixture(scope="module")
+def glm_g32():
+    spec = replace(S.GLM52, group_size=32)
+    say("building the GLM-5.2-shaped layer with groups of 32 on the GPU")
+    L = device_layer(spec, 0, 0)
+    W, b = S.router(spec, 0, 0)
+    yield spec, L, OL.ExpertCache(spec, 0, 0), W, b
+    del L
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("T", [1, 4])
+def test_forward_glm_groups(glm_g32, T):
+    spec, L, cache, W, b = glm_g32
+    x = S.tokens(S.TokenSpec(T=T, token_set=60 + T, outlier_channels=61), spec.H, 0)
+    ws = api.workspace(L, T)
+    say(f"forward GLM groups of 32 T={T}")
+    y = api.moe_forward(L, dev(x), ws).cpu().numpy()
+    toks = [OL.forward_token(spec, cache, W, b, x[t]) for t in range(T)]
+    _check(L, toks, T, ws, y)
+
+
+def test_experts_teacher_forced_glm_groups(glm_g32):
+    """The expert stage (coli_moe_experts) fed the GPU's Q8(x) and the
+    oracle's routing, T = 3 (the item-major down launch)."""
+    spec, L, cache, W, b = glm_g32
+    x = S.tokens(S.TokenSpec(T=3, token_set=8, outlier_channels=61), spec.H, 0)
+    xq, xs = api.quant_act_q8(dev(x))
+    idx_o, w_o = O.route(W, b, x, spec.top_k)
+    ws = api.workspace(L, 3)
+    y = api.moe_experts(L, xq, xs, dev(idx_o), dev(w_o), ws).cpu().numpy()
+    xq_h, xs_h = xq.cpu().numpy(), xs.cpu().numpy()
+    for t in range(3):
+        outs = [O.expert(*cache[int(e)].args(), xq_h[t], xs_h[t], group=32) for e in idx_o[t]]
+        sh = O.expert(*cache[spec.E].args(), xq_h[t], xs_h[t], group=32)
+        y_o = O.combine(np.stack([o.y for o in outs]), w_o[t], sh.y)
+        assert rel_err(y[t][None], y_o[None]).max() <= TOL
