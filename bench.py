@@ -195,7 +195,10 @@ def main():
         idx = ws[j][lay.idx: lay.idx + 4 * T * spec.top_k].view(torch.int32).cpu().numpy()
         union.append(len(set(idx.tolist())))
     wb = spec.weight_bits                        # 4: two codes per byte; 8: one
-    gu_row, dn_row = 2 * spec.I * (spec.H * wb // 8 + 4), spec.H * (spec.I * wb // 8 + 4)
+    # codes + f32 scales per row: one per row, or one per group of columns
+    ns_gu = spec.H // spec.group_size if spec.group_size else 1
+    ns_dn = spec.I // spec.group_size if spec.group_size else 1
+    gu_row, dn_row = 2 * spec.I * (spec.H * wb // 8 + 4 * ns_gu), spec.H * (spec.I * wb // 8 + 4 * ns_dn)
     bytes_call = [(u + spec.has_shared) * spec.expert_bytes for u in union]
     gateup_bytes = [(u + spec.has_shared) * gu_row for u in union]
     down_bytes = [(u + spec.has_shared) * dn_row for u in union]

@@ -214,6 +214,14 @@ WORKLOADS = {
                                   TokenSpec(T=1, outlier_channels=61)),
     "glm52_int8_T4": Workload("glm52_int8_T4", replace(GLM52, weight_bits=8),
                               TokenSpec(T=4, rho=0.8, outlier_channels=61)),
+    # the scale-granularity variant: int4 codes with one f32 scale per group of
+    # 32 (or 128) columns instead of one per row (scale bytes +25% / +6%)
+    "glm52_g32_decode_T1": Workload("glm52_g32_decode_T1", replace(GLM52, group_size=32),
+                                    TokenSpec(T=1, outlier_channels=61)),
+    "glm52_g128_decode_T1": Workload("glm52_g128_decode_T1", replace(GLM52, group_size=128),
+                                     TokenSpec(T=1, outlier_channels=61)),
+    "glm52_g32_verify_T4": Workload("glm52_g32_verify_T4", replace(GLM52, group_size=32),
+                                    TokenSpec(T=4, rho=0.8, outlier_channels=61)),
 }
 
 
