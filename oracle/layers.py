@@ -30,6 +30,8 @@ class PackedExpert:
 def packed_expert(spec: S.LayerSpec, seed: int, layer: int, e: int) -> PackedExpert:
     if spec.group_size:
         pack = lambda w: O.pack_int4_groups(w, spec.group_size)
+    elif spec.weight_bits == 2:
+        pack = O.pack_int2_rows
     else:
         pack = O.pack_int8_rows if spec.weight_bits == 8 else O.pack_int4_rows
     mats = []

@@ -161,6 +161,69 @@ void oracle_rowdot_groups(const uint8_t *q4, const float *s4, int group, const i
     free(S);
 }
 
+/* ----------------------------------------------------------- O18 / O19 --- */
+void oracle_pack_int2_rows(const float *w, int rows, int cols, uint8_t *q, float *s)
+{
+    for (int r = 0; r < rows; ++r) {
+        const float *row = w + (size_t)r * cols;
+        float amax = 0.0f;
+        for (int c = 0; c < cols; ++c) {
+            float a = fabsf(row[c]);
+            if (a > amax) amax = a;
+        }
+        float d = amax / 1.0f;
+        float id = (d != 0.0f) ? 1.0f / d : 0.0f;
+        s[r] = d;
+        uint8_t *dst = q + (size_t)r * (cols / 4);
+        for (int j = 0; j < cols / 4; ++j) {
+            int byte = 0;
+            for (int i = 0; i < 4; ++i)
+                byte |= (round_clamp(row[4 * j + i] * id, -2.0f, 1.0f) & 0x3) << (2 * i);
+            dst[j] = (uint8_t)byte;
+        }
+    }
+}
+
+int oracle_crumb(uint8_t byte, int i)
+{
+    int v = (byte >> (2 * i)) & 0x3;
+    return v >= 2 ? v - 4 : v;    /* 2-bit two's complement */
+}
+
+void oracle_unpack_int2_rows(const uint8_t *q, const float *s, int rows, int cols, double *w)
+{
+    for (int r = 0; r < rows; ++r)
+        for (int c = 0; c < cols; ++c)
+            w[(size_t)r * cols + c] = (double)s[r] * (double)oracle_crumb(q[(size_t)r * (cols / 4) + c / 4], c & 3);
+}
+
+void oracle_block_dots_i2(const uint8_t *q2, const int8_t *q8, int rows, int cols, int32_t *S)
+{
+    for (int r = 0; r < rows; ++r) {
+        const uint8_t *row = q2 + (size_t)r * (cols / 4);
+        for (int b = 0; b < cols / 32; ++b) {
+            int32_t acc = 0;
+            for (int k = 32 * b; k < 32 * b + 32; ++k)
+                acc += oracle_crumb(row[k / 4], k & 3) * (int32_t)q8[k];
+            S[(size_t)r * (cols / 32) + b] = acc;
+        }
+    }
+}
+
+void oracle_rowdot_i2(const uint8_t *q2, const float *s2, const int8_t *q8, const float *d8,
+                      int rows, int cols, float *out)
+{
+    const int nb = cols / 32;
+    int32_t *S = (int32_t *)malloc(sizeof(int32_t) * (size_t)nb);
+    for (int r = 0; r < rows; ++r) {
+        oracle_block_dots_i2(q2 + (size_t)r * (cols / 4), q8, 1, cols, S);
+        double acc = 0.0;
+        for (int b = 0; b < nb; ++b) acc += (double)d8[b] * (double)S[b];
+        out[r] = (float)((double)s2[r] * acc);
+    }
+    free(S);
+}
+
 /* ----------------------------------------------------------- O11 - O13 --- */
 void oracle_pack_int8_rows(const float *w, int rows, int cols, int8_t *q, float *s)
 {
@@ -274,6 +337,7 @@ static void rowdot_w(int wbits, int group, const void *q, const float *s, const 
                      int rows, int cols, float *out)
 {
     if (wbits == 8) oracle_rowdot_i8((const int8_t *)q, s, q8, d8, rows, cols, out);
+    else if (wbits == 2) oracle_rowdot_i2((const uint8_t *)q, s, q8, d8, rows, cols, out);
     else if (group > 0) oracle_rowdot_groups((const uint8_t *)q, s, group, q8, d8, rows, cols, out);
     else oracle_rowdot((const uint8_t *)q, s, q8, d8, rows, cols, out);
 }
@@ -413,9 +477,9 @@ int oracle_moe_forward(const oracle_layer *L, const float *x, int T, float *y, i
 {
     const int H = L->H, I = L->I, E = L->E, k = L->top_k;
     if (H <= 0 || I <= 0 || H % 32 || I % 32 || T < 0) return -1;
-    if (L->weight_bits != 0 && L->weight_bits != 4 && L->weight_bits != 8) return -1;
+    if (L->weight_bits != 0 && L->weight_bits != 2 && L->weight_bits != 4 && L->weight_bits != 8) return -1;
     const int G = L->group_size;
-    if (G < 0 || (G > 0 && (L->weight_bits == 8 || G % 32 || H % G || I % G))) return -1;
+    if (G < 0 || (G > 0 && (L->weight_bits == 8 || L->weight_bits == 2 || G % 32 || H % G || I % G))) return -1;
     int32_t *idx = (int32_t *)malloc(sizeof(int32_t) * (size_t)(T * k + 1));
     float *w = (float *)malloc(sizeof(float) * (size_t)(T * k + 1));
     if (oracle_route(L->router_w, L->router_b, x, T, H, E, k, L->n_group, L->topk_group,
@@ -427,10 +491,10 @@ int oracle_moe_forward(const oracle_layer *L, const float *x, int T, float *y, i
     float *xs = (float *)malloc(sizeof(float) * (size_t)(H / 32));
     float *yr = (float *)malloc(sizeof(float) * (size_t)k * H);
     float *ysh = (float *)malloc(sizeof(float) * (size_t)H);
-    const int wb = L->weight_bits == 8 ? 8 : 4;
-    /* bytes per expert matrix: a byte holds two 4-bit codes or one 8-bit code */
-    const size_t gq = wb == 8 ? (size_t)I * H : (size_t)I * (H / 2);
-    const size_t dq = wb == 8 ? (size_t)H * I : (size_t)H * (I / 2);
+    const int wb = L->weight_bits == 0 ? 4 : L->weight_bits;
+    /* bytes per expert matrix: a byte holds one 8-bit, two 4-bit or four 2-bit codes */
+    const size_t gq = (size_t)I * H * wb / 8;
+    const size_t dq = (size_t)H * I * wb / 8;
     /* scales per expert matrix: one per row, or one per group of G columns */
     const size_t gs = G > 0 ? (size_t)I * (H / G) : (size_t)I;
     const size_t ds = G > 0 ? (size_t)H * (I / G) : (size_t)H;

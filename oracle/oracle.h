@@ -84,6 +84,31 @@ void oracle_unpack_int4_groups(const uint8_t *q, const float *s, int rows, int c
 void oracle_rowdot_groups(const uint8_t *q4, const float *s4, int group, const int8_t *q8, const float *d8,
                           int rows, int cols, float *out);
 
+/* O18 [P1 s3.1: int2 packed, experimental, four 2-bit values per byte; the
+ * kernel layer's matmul_i2] int2 pack, per row. The pages give no scale
+ * rule; the reading taken is O1's with the 2-bit range: d = absmax/1 (the
+ * largest positive code is 1, as 7 is for int4), id = 1/d (0 if d == 0),
+ * code = clamp(rint(w*id), -2, 1) with O1's rounding and NaN rule, so the
+ * codes in use are -1, 0, 1. Byte j of a row holds elements 4j..4j+3 in bits
+ * 0-1, 2-3, 4-5, 6-7, as 2-bit two's complement. q: [rows][cols/4], s: [rows].
+ * cols a multiple of 4. */
+void oracle_pack_int2_rows(const float *w, int rows, int cols, uint8_t *q, float *s);
+
+/* O18 decode one 2-bit field i (0..3) of a byte. */
+int oracle_crumb(uint8_t byte, int i);
+
+/* O18 dequantise on use: w~[r][c] = s[r] * code[r][c] (double). */
+void oracle_unpack_int2_rows(const uint8_t *q, const float *s, int rows, int cols, double *w);
+
+/* O19 [P1 s3.1, the IDOT path with int2 rows] exact int32 block dots
+ * S[r][b] = sum_{k in block b} code2[r][k] * q8[k]. */
+void oracle_block_dots_i2(const uint8_t *q2, const int8_t *q8, int rows, int cols, int32_t *S);
+
+/* O19 row product: out[r] = (float)(s2[r] * sum_b d8[b]*S[r][b]), the block
+ * sum in double in block order (O5 with O19's block dots). */
+void oracle_rowdot_i2(const uint8_t *q2, const float *s2, const int8_t *q8, const float *d8,
+                      int rows, int cols, float *out);
+
 /* O11 [P1 s3.1, quantize_rows] int8 weights, one byte per value. The pages
  * give no scale rule for them; the reading taken is the symmetric one of
  * the Q8 activations, per row: d = absmax/127 (f32), id = 1/d (0 if d == 0),
@@ -122,8 +147,9 @@ void oracle_expert(const uint8_t *gate_q, const float *gate_s, const uint8_t *up
                    const int8_t *xq, const float *xs, float *y,
                    float *g, float *u, float *h, int8_t *hq, float *hs);
 
-/* O7 for either weight format: wbits = 4 (O5 row products on int4 rows) or
- * 8 (O13 on int8 rows: gate/up [I][H] int8, down [H][I] int8). */
+/* O7 for any weight format: wbits = 4 (O5 row products on int4 rows), 8
+ * (O13 on int8 rows: gate/up [I][H] int8, down [H][I] int8) or 2 (O19 on
+ * int2 rows: gate/up [I][H/4], down [H][I/4]). */
 void oracle_expert_w(int wbits, const void *gate_q, const float *gate_s, const void *up_q, const float *up_s,
                      const void *down_q, const float *down_s, int H, int I,
                      const int8_t *xq, const float *xs, float *y,
@@ -165,9 +191,9 @@ typedef struct oracle_layer {
     int H, I, E, top_k, n_group, topk_group, has_shared;
     float route_scale;
     const float *router_w, *router_b;
-    const uint8_t *gate_q, *up_q, *down_q;   /* int8 rows when weight_bits == 8 */
+    const uint8_t *gate_q, *up_q, *down_q;   /* int8 rows when weight_bits == 8, int2 when 2 */
     const float *gate_s, *up_s, *down_s;
-    int weight_bits;                         /* 4 (or 0) or 8 */
+    int weight_bits;                         /* 4 (or 0), 8 or 2 */
     int group_size;                          /* 0: one scale per row; else int4 with O16 group scales,
                                                 gate_s/up_s [E'][I][H/G], down_s [E'][H][I/G] */
 } oracle_layer;

@@ -47,6 +47,12 @@ def _lib():
         L.oracle_expert_w.argtypes = [i, P, P, P, P, P, P, i, i, P, P, P, P, P, P, P, P]
         L.oracle_expert_dense_i8.argtypes = [P, P, P, P, P, P, i, i, P, P]
         L.oracle_pack_int4_groups.argtypes = [P, i, i, i, P, P]
+        L.oracle_pack_int2_rows.argtypes = [P, i, i, P, P]
+        L.oracle_crumb.argtypes = [ctypes.c_uint8, i]
+        L.oracle_crumb.restype = i
+        L.oracle_unpack_int2_rows.argtypes = [P, P, i, i, P]
+        L.oracle_block_dots_i2.argtypes = [P, P, i, i, P]
+        L.oracle_rowdot_i2.argtypes = [P, P, P, P, i, i, P]
         L.oracle_unpack_int4_groups.argtypes = [P, P, i, i, i, P]
         L.oracle_rowdot_groups.argtypes = [P, P, i, P, P, i, i, P]
         L.oracle_expert_groups.argtypes = [i, P, P, P, P, P, P, i, i, P, P, P, P, P, P, P, P]
@@ -147,6 +153,52 @@ def rowdot_groups(q4, s4, group: int, q8, d8) -> np.ndarray:
     return out
 
 
+# ---------------------------------------------------------------- O18 / O19
+class Int2Rows(np.ndarray):
+    """uint8 [rows][cols/4] holding int2 codes (tags the format for expert())."""
+
+
+def pack_int2_rows(w: np.ndarray):
+    """int2 codes, four per byte (element 4j+i in bits 2i..2i+1 of byte j), and f32 row scales."""
+    w = _c(w, np.float32)
+    rows, cols = w.shape
+    if cols % 4:
+        raise ValueError("cols must be a multiple of 4")
+    q = np.empty((rows, cols // 4), dtype=np.uint8)
+    s = np.empty(rows, dtype=np.float32)
+    _lib().oracle_pack_int2_rows(_p(w), rows, cols, _p(q), _p(s))
+    return q.view(Int2Rows), s
+
+
+def crumb(byte: int, i: int) -> int:
+    return int(_lib().oracle_crumb(byte, i))
+
+
+def unpack_int2_rows(q: np.ndarray, s: np.ndarray) -> np.ndarray:
+    q = _c(q, np.uint8)
+    rows, quarter = q.shape
+    out = np.empty((rows, 4 * quarter), dtype=np.float64)
+    _lib().oracle_unpack_int2_rows(_p(q), _p(_c(s, np.float32)), rows, 4 * quarter, _p(out))
+    return out
+
+
+def block_dots_i2(q2: np.ndarray, q8: np.ndarray) -> np.ndarray:
+    q2 = _c(q2, np.uint8)
+    rows, quarter = q2.shape
+    S = np.empty((rows, 4 * quarter // 32), dtype=np.int32)
+    _lib().oracle_block_dots_i2(_p(q2), _p(_c(q8, np.int8)), rows, 4 * quarter, _p(S))
+    return S
+
+
+def rowdot_i2(q2, s2, q8, d8) -> np.ndarray:
+    q2 = _c(q2, np.uint8)
+    rows, quarter = q2.shape
+    out = np.empty(rows, dtype=np.float32)
+    _lib().oracle_rowdot_i2(_p(q2), _p(_c(s2, np.float32)), _p(_c(q8, np.int8)), _p(_c(d8, np.float32)),
+                            rows, 4 * quarter, _p(out))
+    return out
+
+
 # ---------------------------------------------------------------- O11 - O13
 def pack_int8_rows(w: np.ndarray):
     """int8 weight rows (natural element order) and their f32 scales."""
@@ -206,18 +258,22 @@ class ExpertOut:
 
 
 def _wbits(q) -> int:
-    """Weight format from the packed array's dtype: int8 rows, or uint8 bytes of int4 pairs."""
+    """Weight format from the packed array: int8 rows, int2 rows (the Int2Rows
+    tag pack_int2_rows returns), or uint8 bytes of int4 pairs."""
+    if isinstance(q, Int2Rows):
+        return 2
     return 8 if np.asarray(q).dtype == np.int8 else 4
 
 
-def expert(gate_q, gate_s, up_q, up_s, down_q, down_s, xq, xs, group: int = 0) -> ExpertOut:
-    """O7 (int4 rows, uint8 [I][H/2]) or its int8 form (int8 rows [I][H]); with
-    group > 0, int4 rows with O16 group scales (gate/up [I][H/group], down [H][I/group])."""
-    wb = _wbits(gate_q)
+def expert(gate_q, gate_s, up_q, up_s, down_q, down_s, xq, xs, group: int = 0, wbits: int = 0) -> ExpertOut:
+    """O7 (int4 rows, uint8 [I][H/2]), its int8 form (int8 rows [I][H]) or its
+    int2 form (wbits=2 or Int2Rows arrays, uint8 [I][H/4]); with group > 0,
+    int4 rows with O16 group scales (gate/up [I][H/group], down [H][I/group])."""
+    wb = wbits or _wbits(gate_q)
     dt = np.int8 if wb == 8 else np.uint8
     gate_q = _c(gate_q, dt)
     I, Hc = gate_q.shape
-    H = Hc if wb == 8 else 2 * Hc
+    H = Hc * 8 // wb
     o = ExpertOut(y=np.empty(H, np.float32), g=np.empty(I, np.float32), u=np.empty(I, np.float32),
                   h=np.empty(I, np.float32), hq=np.empty(I, np.int8), hs=np.empty(I // 32, np.float32))
     tail = (H, I, _p(_c(xq, np.int8)), _p(_c(xs, np.float32)), _p(o.y), _p(o.g), _p(o.u), _p(o.h), _p(o.hq),
@@ -292,6 +348,7 @@ class _CLayer(ctypes.Structure):
 
 
 def moe_forward(layer, x):
+    # weight_bits 2: gate_q/up_q [E+s][I][H/4], down_q [E+s][H][I/4] uint8 (four codes per byte)
     """layer: object with H, I, E, top_k, n_group, topk_group, has_shared, route_scale,
     weight_bits (4 if absent) and numpy arrays router_w [E][H], router_b [E],
     gate_q/up_q [E+s][I][H/2] uint8, down_q [E+s][H][I/2] uint8 (int4) or
@@ -301,7 +358,7 @@ def moe_forward(layer, x):
     Returns y [T][H], idx [T][k], w [T][k]."""
     x = _c(np.atleast_2d(x), np.float32)
     T = x.shape[0]
-    wb = getattr(layer, "weight_bits", 4)
+    wb = getattr(layer, "weight_bits", 4) or 4
     qt = np.int8 if wb == 8 else np.uint8
     arrs = {n: _c(getattr(layer, n), dt) for n, dt in (
         ("router_w", np.float32), ("router_b", np.float32), ("gate_q", qt), ("up_q", qt),
