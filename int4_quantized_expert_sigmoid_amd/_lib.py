@@ -19,7 +19,7 @@ COLI_GEMV_MAX_T, COLI_MAX_T, COLI_MAX_TOPK, COLI_PROFILE_EVENTS = 8, 65536, 16, 
 EXPORTS = ("coli_quant_act_q8", "coli_moe_workspace_bytes", "coli_moe_workspace_init",
            "coli_moe_route", "coli_moe_forward", "coli_moe_forward_profiled", "coli_moe_forward_timed", "coli_moe_forward_rms",
            "coli_dense_workspace_bytes", "coli_dense_forward", "coli_timer_begin", "coli_timer_end", "coli_moe_experts", "coli_moe_workspace_layout",
-           "coli_rmsnorm", "coli_pack_int4_rows", "coli_pack_int4_rows_dev", "coli_pack_int4_groups_dev", "coli_pack_int8_rows",
+           "coli_rmsnorm", "coli_pack_int4_rows", "coli_pack_int4_rows_dev", "coli_pack_int4_groups_dev", "coli_pack_int2_rows_dev", "coli_pack_int8_rows",
            "coli_pack_int8_rows_dev", "coli_debug_block_dots", "coli_version")
 
 
@@ -87,6 +87,7 @@ def lib():
             "coli_pack_int4_rows": ([P, i, i, P, P], i),
             "coli_pack_int4_rows_dev": ([P, i, i, P, P, P], i),
             "coli_pack_int4_groups_dev": ([P, i, i, i, P, P, P], i),
+            "coli_pack_int2_rows_dev": ([P, i, i, P, P, P], i),
             "coli_pack_int8_rows": ([P, i, i, P, P], i),
             "coli_pack_int8_rows_dev": ([P, i, i, P, P, P], i),
             "coli_debug_block_dots": ([P, P, i, i, P, P], i),

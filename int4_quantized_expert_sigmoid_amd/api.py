@@ -46,9 +46,9 @@ class MoELayer:
     route_scale: float
     router_w: torch.Tensor   # [E][H] f32
     router_b: torch.Tensor   # [E] f32
-    gate_q: torch.Tensor     # [E+s][I][H/2] u8 (int4) or [E+s][I][H] i8 (int8)
+    gate_q: torch.Tensor     # [E+s][I][H/2] u8 (int4), [E+s][I][H] i8 (int8) or [E+s][I][H/4] u8 (int2)
     up_q: torch.Tensor
-    down_q: torch.Tensor     # [E+s][H][I/2] u8 (int4) or [E+s][H][I] i8 (int8)
+    down_q: torch.Tensor     # [E+s][H][I/2] u8 (int4), [E+s][H][I] i8 (int8) or [E+s][H][I/4] u8 (int2)
     gate_s: torch.Tensor     # [E+s][I] f32 ([E+s][I][H/G] with group scales)
     up_s: torch.Tensor
     down_s: torch.Tensor     # [E+s][H] f32 ([E+s][H][I/G])
@@ -60,7 +60,7 @@ class MoELayer:
               weight_bits=4, group_size=0):
         n = E + has_shared
         f32 = torch.float32
-        qt, div = (torch.int8, 1) if weight_bits == 8 else (torch.uint8, 2)
+        qt, div = {8: (torch.int8, 1), 2: (torch.uint8, 4)}.get(weight_bits, (torch.uint8, 2))
         if group_size:
             if weight_bits == 8:
                 raise ValueError("group scales are an int4 format")
@@ -345,6 +345,14 @@ def pack_int4_rows_dev(w: torch.Tensor, q: torch.Tensor, s: torch.Tensor, stream
     _dev(w, torch.float32, "w")
     rows, cols = w.shape
     check("coli_pack_int4_rows_dev", lib().coli_pack_int4_rows_dev(_ptr(w), rows, cols, _ptr(q), _ptr(s),
+                                                                   _stream(stream)))
+
+
+def pack_int2_rows_dev(w: torch.Tensor, q: torch.Tensor, s: torch.Tensor, stream=None) -> None:
+    """int2 codes (the library's column order, four per byte) and f32 row scales (device)."""
+    _dev(w, torch.float32, "w")
+    rows, cols = w.shape
+    check("coli_pack_int2_rows_dev", lib().coli_pack_int2_rows_dev(_ptr(w), rows, cols, _ptr(q), _ptr(s),
                                                                    _stream(stream)))
 
 

@@ -28,7 +28,7 @@ inline bool al4(const void *p) { return p != nullptr && (reinterpret_cast<uintpt
 // of them, and divides both row lengths.
 bool group_ok(int G, int H, int I, int wbits)
 {
-    if (wbits == 8 || G < QK || G > 4096 || G % QK) return false;
+    if (wbits == 8 || wbits == 2 || G < QK || G > 4096 || G % QK) return false;
     const int nb = G / QK;
     if (nb & (nb - 1)) return false;
     return H % G == 0 && I % G == 0;
@@ -45,7 +45,7 @@ bool layer_ok(const coli_moe_layer *L)
     if (L->n_group > 1 && L->top_k > L->topk_group * (L->E / L->n_group)) return false;
     if (L->has_shared != 0 && L->has_shared != 1) return false;
     if (!std::isfinite(L->route_scale)) return false;
-    if (L->weight_bits != 0 && L->weight_bits != 4 && L->weight_bits != 8) return false;
+    if (L->weight_bits != 0 && L->weight_bits != 2 && L->weight_bits != 4 && L->weight_bits != 8) return false;
     if (L->group_size != 0 && !group_ok(L->group_size, L->H, L->I, L->weight_bits)) return false;
     if (!al4(L->router_w) || !al4(L->router_b)) return false;
     if (!al16(L->gate_q) || !al16(L->up_q) || !al16(L->down_q)) return false;
@@ -76,11 +76,11 @@ int choose_path(const coli_moe_layer &L, int T, int flags)
 
 int status(hipError_t e) { return e == hipSuccess ? COLI_OK : COLI_EDEVICE; }
 
-// int8 experts and group scales run on the token-GEMV path only (not
-// grouped, not fused).
+// int8 and int2 experts and group scales run on the token-GEMV path only
+// (not grouped, not fused).
 int format_ok(const coli_moe_layer &L, int path, int flags)
 {
-    if ((L.weight_bits == 8 || L.group_size != 0) && (path != 0 || (flags & COLI_PATH_FUSED)))
+    if ((L.weight_bits == 8 || L.weight_bits == 2 || L.group_size != 0) && (path != 0 || (flags & COLI_PATH_FUSED)))
         return COLI_EUNSUPPORTED;
     return COLI_OK;
 }
@@ -488,6 +488,12 @@ int coli_pack_int4_rows_dev(const float *w, int rows, int cols, uint8_t *q, floa
 {
     if (!al4(w) || !q || !al4(s) || rows < 1 || cols < 2 || (cols & 1)) return COLI_EINVAL;
     return status(launch_pack_int4(w, rows, cols, q, s, (hipStream_t)stream));
+}
+
+int coli_pack_int2_rows_dev(const float *w, int rows, int cols, uint8_t *q, float *s, void *stream)
+{
+    if (!al4(w) || !al16(q) || !al4(s) || rows < 1 || cols < 32 || cols % 32) return COLI_EINVAL;
+    return status(launch_pack_int2(w, rows, cols, q, s, (hipStream_t)stream));
 }
 
 int coli_pack_int4_groups_dev(const float *w, int rows, int cols, int group, uint8_t *q, float *s, void *stream)

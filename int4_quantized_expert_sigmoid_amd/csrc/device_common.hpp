@@ -66,19 +66,43 @@ __device__ __forceinline__ int dot_block_i8(const uint4 w0, const uint4 w1, cons
     return s;
 }
 
-// Weight formats of the token-GEMV path: bytes of one row's 32-wide block and
-// the factor that turns a block dot into S_b (int4 dots come out x16).
+// Weight formats of the token-GEMV path: bytes of one row's 32-wide block,
+// the register pieces (16 bytes each; an int2 block fills half of one) and
+// the factor that turns a block dot into S_b (int4 dots come out x16, int2
+// dots x64).
 template <int WB> struct WFmt;
-template <> struct WFmt<4> { static constexpr int BLK_BYTES = 16; static constexpr double KSCALE = 0.0625; };
-template <> struct WFmt<8> { static constexpr int BLK_BYTES = 32; static constexpr double KSCALE = 1.0; };
+template <> struct WFmt<2> { static constexpr int BLK_BYTES = 8, NP = 1; static constexpr double KSCALE = 1.0 / 64; };
+template <> struct WFmt<4> { static constexpr int BLK_BYTES = 16, NP = 1; static constexpr double KSCALE = 0.0625; };
+template <> struct WFmt<8> { static constexpr int BLK_BYTES = 32, NP = 2; static constexpr double KSCALE = 1.0; };
+
+// int2 rows, in the order the activation blocks are read: in every aligned
+// group of 16 columns, byte k holds columns 2k, 2k+1, 2k+8, 2k+9 in its 2-bit
+// fields 0..3. Field i of the four bytes, moved to the top of each byte, is
+// then the x64 code of the columns activation dword i of the group holds
+// (8-groups stored as 0,2,4,6 then 1,3,5,7).
+__device__ __forceinline__ int dot_block_i2(uint32_t w0, uint32_t w1, const Blk8 &a)
+{
+    int s = 0;
+    s = __builtin_amdgcn_sdot4((int)((w0 << 6) & 0xC0C0C0C0u), a.v[0], s, false);
+    s = __builtin_amdgcn_sdot4((int)((w0 << 4) & 0xC0C0C0C0u), a.v[1], s, false);
+    s = __builtin_amdgcn_sdot4((int)((w0 << 2) & 0xC0C0C0C0u), a.v[2], s, false);
+    s = __builtin_amdgcn_sdot4((int)(w0 & 0xC0C0C0C0u), a.v[3], s, false);
+    s = __builtin_amdgcn_sdot4((int)((w1 << 6) & 0xC0C0C0C0u), a.v[4], s, false);
+    s = __builtin_amdgcn_sdot4((int)((w1 << 4) & 0xC0C0C0C0u), a.v[5], s, false);
+    s = __builtin_amdgcn_sdot4((int)((w1 << 2) & 0xC0C0C0C0u), a.v[6], s, false);
+    s = __builtin_amdgcn_sdot4((int)(w1 & 0xC0C0C0C0u), a.v[7], s, false);
+    return s;
+}
 
 // One block of one weight row times one activation block: S_b scaled by the
-// format's factor applies later; w holds BLK_BYTES/16 16-byte pieces.
+// format's factor applies later; w holds the block's NP pieces.
 template <int WB>
-__device__ __forceinline__ int dot_block_w(const uint4 (&w)[WFmt<WB>::BLK_BYTES / 16], const Blk8 &a)
+__device__ __forceinline__ int dot_block_w(const uint4 (&w)[WFmt<WB>::NP], const Blk8 &a)
 {
     if constexpr (WB == 8) {
         return dot_block_i8(w[0], w[1], a);
+    } else if constexpr (WB == 2) {
+        return dot_block_i2(w[0].x, w[0].y, a);
     } else {
         int lo[4], hi[4];
         unpack_nibbles(w[0], lo, hi);
@@ -108,6 +132,21 @@ __device__ __forceinline__ uint4 load_u4_stream(const uint8_t *p)
 {
     const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
     return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+// One register piece of a weight row block: 16 bytes, or the 8 bytes of an
+// int2 block (the upper half unused).
+template <int WB>
+__device__ __forceinline__ uint4 load_w_stream(const uint8_t *p)
+{
+    if constexpr (WB == 2) {
+        const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(p));
+        return make_uint4(v.x, v.y, 0u, 0u);
+    } else {
+        return load_u4_stream(p);
+    }
 }
 
 // Device-coherent relaxed accesses for data one workgroup hands to another in

@@ -107,7 +107,7 @@ __device__ __forceinline__ void gateup_rows(const GemvArgs &a, const ItemDesc &i
 {
     static_assert(!GS || WB == 4, "group scales are an int4 format");
     constexpr int RG = GS ? RC : 1;              // group scales held per chunk
-    constexpr int NP = WFmt<WB>::BLK_BYTES / 16;     // 16-byte pieces per row block
+    constexpr int NP = WFmt<WB>::NP;     // 16-byte pieces per row block
     constexpr double KS = WFmt<WB>::KSCALE;
     constexpr int NV = 2 * RC;                   // values per chunk: RC rows x (gate, up)
     constexpr int RPS = QK / RS;                 // rows per set
@@ -164,8 +164,8 @@ __device__ __forceinline__ void gateup_rows(const GemvArgs &a, const ItemDesc &i
         for (int r = 0; r < RC; ++r) {
 #pragma unroll
             for (int q = 0; q < NP; ++q) {
-                wg[0][r][q] = load_u4_stream(pg + (long)r * rowb + 16 * q);
-                wu[0][r][q] = load_u4_stream(pu + (long)r * rowb + 16 * q);
+                wg[0][r][q] = load_w_stream<WB>(pg + (long)r * rowb + 16 * q);
+                wu[0][r][q] = load_w_stream<WB>(pu + (long)r * rowb + 16 * q);
             }
             if constexpr (GS) {
                 sg[0][r] = psg[(long)r * gstr];
@@ -180,8 +180,8 @@ __device__ __forceinline__ void gateup_rows(const GemvArgs &a, const ItemDesc &i
                 for (int r = 0; r < RC; ++r) {
 #pragma unroll
                     for (int q = 0; q < NP; ++q) {
-                        wg[cur ^ 1][r][q] = load_u4_stream(pg + (long)((c + 1) * RC + r) * rowb + 16 * q);
-                        wu[cur ^ 1][r][q] = load_u4_stream(pu + (long)((c + 1) * RC + r) * rowb + 16 * q);
+                        wg[cur ^ 1][r][q] = load_w_stream<WB>(pg + (long)((c + 1) * RC + r) * rowb + 16 * q);
+                        wu[cur ^ 1][r][q] = load_w_stream<WB>(pu + (long)((c + 1) * RC + r) * rowb + 16 * q);
                     }
                     if constexpr (GS) {
                         sg[cur ^ 1][r] = psg[(long)((c + 1) * RC + r) * gstr];
@@ -256,7 +256,7 @@ __device__ __forceinline__ void down_rows(const GemvArgs &a, const ItemDesc &it,
 {
     static_assert(!GS || WB == 4, "group scales are an int4 format");
     constexpr int RG = GS ? RD : 1;
-    constexpr int NP = WFmt<WB>::BLK_BYTES / 16;
+    constexpr int NP = WFmt<WB>::NP;
     constexpr double KS = WFmt<WB>::KSCALE;
     constexpr int NC = RPW / RD;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -274,7 +274,7 @@ __device__ __forceinline__ void down_rows(const GemvArgs &a, const ItemDesc &it,
 #pragma unroll
     for (int r = 0; r < RD; ++r) {
 #pragma unroll
-        for (int q = 0; q < NP; ++q) wd[0][r][q] = load_u4_stream(pd + (long)r * rowb + 16 * q);
+        for (int q = 0; q < NP; ++q) wd[0][r][q] = load_w_stream<WB>(pd + (long)r * rowb + 16 * q);
         if constexpr (GS) sd[0][r] = psd[(long)r * gstr];
     }
 
@@ -307,7 +307,7 @@ __device__ __forceinline__ void down_rows(const GemvArgs &a, const ItemDesc &it,
             for (int r = 0; r < RD; ++r) {
 #pragma unroll
                 for (int q = 0; q < NP; ++q)
-                    wd[cur ^ 1][r][q] = load_u4_stream(pd + (long)((c + 1) * RD + r) * rowb + 16 * q);
+                    wd[cur ^ 1][r][q] = load_w_stream<WB>(pd + (long)((c + 1) * RD + r) * rowb + 16 * q);
                 if constexpr (GS) sd[cur ^ 1][r] = psd[(long)((c + 1) * RD + r) * gstr];
             }
         }

@@ -81,6 +81,7 @@ inline int group_shift(const coli_moe_layer &L)
 
 hipError_t launch_pack_int4(const float *w, int rows, int cols, uint8_t *q, float *sc, hipStream_t s);
 hipError_t launch_pack_int8(const float *w, int rows, int cols, int8_t *q, float *sc, hipStream_t s);
+hipError_t launch_pack_int2(const float *w, int rows, int cols, uint8_t *q, float *sc, hipStream_t s);
 hipError_t launch_pack_int4_groups(const float *w, int rows, int cols, int group, uint8_t *q, float *sc, hipStream_t s);
 hipError_t launch_rmsnorm(const float *x, const float *g, int T, int H, float eps, float *out, hipStream_t s);
 // The float4 order of the RMSNorm sums (x 16-byte aligned, H % 4 == 0): the

@@ -226,7 +226,7 @@ __global__ void __launch_bounds__(256) k_select_gateup(SelGuArgs a, GemvArgs g, 
 
 // ------------------------------------------------------------ launch 3
 struct DnArgs {
-    const uint8_t *q;          // down_q [E+shared][H][I/2] (int4) or [E+shared][H][I] (int8)
+    const uint8_t *q;          // down_q [E+shared][H][I/2] (int4), [E+shared][H][I] (int8) or [E+shared][H][I/4] (int2)
     const float *s;            // down_s [E+shared][H], or [E+shared][H][I/group] with group scales
     int H, I, E, T, top_k, has_shared;
     int gsh;                   // group scales: log2(group / 32)
@@ -249,7 +249,7 @@ struct DnArgs {
 // slots; with group scales (GS) also the scale of each row's group.
 template <int NT, int RPU, int WB, bool GS>
 struct DnStage {
-    uint4 wd[RPU][WFmt<WB>::BLK_BYTES / 16];
+    uint4 wd[RPU][WFmt<WB>::NP];
     float sw[GS ? RPU : 1];
     Blk8 act[NT];
     float ds[NT];              // block scales as loaded (turned to f64 where used, so a load is never waited for early)
@@ -260,7 +260,7 @@ template <int NT, int RPU, int WB, bool GS>
 __device__ __forceinline__ void dn_load_e(const DnArgs &a, int item, long row0, int lane, int e, int nt,
                                           DnStage<NT, RPU, WB, GS> &st)
 {
-    constexpr int NP = WFmt<WB>::BLK_BYTES / 16;
+    constexpr int NP = WFmt<WB>::NP;
     const int nblk = a.I / QK;
     const bool active = lane < nblk;
     const long rowb = (long)a.I * WB / 8;
@@ -270,7 +270,7 @@ __device__ __forceinline__ void dn_load_e(const DnArgs &a, int item, long row0, 
 #pragma unroll
     for (int r = 0; r < RPU; ++r)
 #pragma unroll
-        for (int q = 0; q < NP; ++q) st.wd[r][q] = load_u4_stream(pd + (long)r * rowb + 16 * q);
+        for (int q = 0; q < NP; ++q) st.wd[r][q] = load_w_stream<WB>(pd + (long)r * rowb + 16 * q);
     if constexpr (GS) {
         const long gstr = nblk >> a.gsh;         // group scales per row: I / group
         const float *ps = a.s + ((long)st.e * a.H + row0) * gstr + ((active ? lane : 0) >> a.gsh);
@@ -420,6 +420,7 @@ hipError_t launch_sel_wb(const coli_moe_layer &L, dim3 grid, const SelGuArgs &a,
                          hipStream_t s)
 {
     if (L.group_size) return launch_sel_nt<NT, 4, true>(L.E, grid, a, g, nsh, s);
+    if (L.weight_bits == 2) return launch_sel_nt<NT, 2>(L.E, grid, a, g, nsh, s);
     return L.weight_bits == 8 ? launch_sel_nt<NT, 8>(L.E, grid, a, g, nsh, s)
                               : launch_sel_nt<NT, 4>(L.E, grid, a, g, nsh, s);
 }
@@ -517,6 +518,10 @@ hipError_t launch_decode_down_combine(const coli_moe_layer &L, int T, const WsLa
     if (L.weight_bits == 8) {
         if (T <= 1) return launch_dn_nt<1, 4, 8>(L, lay, a, s);
         return launch_dn_nt<2, 2, 8>(L, lay, a, s);
+    }
+    if (L.weight_bits == 2) {
+        if (T <= 1) return launch_dn_nt<1, 8, 2>(L, lay, a, s);
+        return launch_dn_nt<2, 4, 2>(L, lay, a, s);
     }
     if (L.group_size) {
         if (T <= 1) return launch_dn_nt<1, 8, 4, true>(L, lay, a, s);

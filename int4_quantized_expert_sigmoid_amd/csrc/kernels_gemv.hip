@@ -88,6 +88,7 @@ hipError_t launch_gateup_gemv(const coli_moe_layer &L, int T, const WsLayout &la
     const int threads = ((nblk + 63) / 64) * 64;
     const dim3 grid((unsigned)((lay.max_items - item0) * (L.I / QK)));
     if (L.group_size) launch_gateup_wb<4, true>(T, grid, dim3(threads), a, s);
+    else if (L.weight_bits == 2) launch_gateup_wb<2>(T, grid, dim3(threads), a, s);
     else if (L.weight_bits == 8) launch_gateup_wb<8>(T, grid, dim3(threads), a, s);
     else launch_gateup_wb<4>(T, grid, dim3(threads), a, s);
     return hipGetLastError();
@@ -101,6 +102,7 @@ hipError_t launch_down_gemv(const coli_moe_layer &L, int T, const WsLayout &lay,
     a.q_a = L.down_q; a.s_a = L.down_s; a.q_b = nullptr; a.s_b = nullptr;
     const dim3 grid((unsigned)((lay.max_items - item0) * (L.H / QK)));
     if (L.group_size) launch_down_wb<4, true>(T, grid, a, s);
+    else if (L.weight_bits == 2) launch_down_wb<2>(T, grid, a, s);
     else if (L.weight_bits == 8) launch_down_wb<8>(T, grid, a, s);
     else launch_down_wb<4>(T, grid, a, s);
     return hipGetLastError();

@@ -118,6 +118,37 @@ __global__ void __launch_bounds__(256) k_pack_int4_groups(const float *__restric
     }
 }
 
+// int2 rows: d = absmax/1, codes clamp(rint(w/d), -2, 1); in every aligned
+// group of 16 columns byte k holds columns 2k, 2k+1, 2k+8, 2k+9 in its 2-bit
+// fields 0..3 (the order the kernels read activation blocks in). One thread
+// per output byte.
+__global__ void __launch_bounds__(256) k_pack_int2(const float *__restrict__ w, int cols,
+                                                   uint8_t *__restrict__ q, float *__restrict__ sc)
+{
+    __shared__ float red[4];
+    const long row = blockIdx.x;
+    const float *src = w + row * (long)cols;
+    float amax = 0.0f;
+    for (int c = threadIdx.x; c < cols; c += blockDim.x) amax = fmaxf(amax, fabsf(src[c]));
+    amax = wave_max(amax);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = amax;
+    __syncthreads();
+    amax = red[0];
+    for (int i = 1; i < (int)(blockDim.x >> 6); ++i) amax = fmaxf(amax, red[i]);
+    const float d = __fdiv_rn(amax, 1.0f);
+    const float id = (d != 0.0f) ? __fdiv_rn(1.0f, d) : 0.0f;
+    uint8_t *dst = q + row * (long)(cols / 4);
+    for (int j = threadIdx.x; j < cols / 4; j += blockDim.x) {
+        const int c0 = (j >> 2) * 16 + 2 * (j & 3);
+        const int cs[4] = {c0, c0 + 1, c0 + 8, c0 + 9};
+        int byte = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) byte |= (round_clamp(__fmul_rn(src[cs[i]], id), -2.0f, 1.0f) & 3) << (2 * i);
+        dst[j] = (uint8_t)byte;
+    }
+    if (threadIdx.x == 0) sc[row] = d;
+}
+
 // int8 rows: d = absmax/127, codes clamp(rint(w/d), -127, 127); within each
 // group of 8 columns column c goes to byte perm8(c) (0,2,4,6 then 1,3,5,7).
 __global__ void __launch_bounds__(256) k_pack_int8(const float *__restrict__ w, int cols,
@@ -221,6 +252,12 @@ hipError_t launch_pack_int4(const float *w, int rows, int cols, uint8_t *q, floa
 hipError_t launch_pack_int4_groups(const float *w, int rows, int cols, int group, uint8_t *q, float *sc, hipStream_t s)
 {
     COLI_LAUNCH(k_pack_int4_groups, dim3(rows), dim3(256), 0, s, w, cols, group, q, sc);
+    return hipGetLastError();
+}
+
+hipError_t launch_pack_int2(const float *w, int rows, int cols, uint8_t *q, float *sc, hipStream_t s)
+{
+    COLI_LAUNCH(k_pack_int2, dim3(rows), dim3(256), 0, s, w, cols, q, sc);
     return hipGetLastError();
 }
 

@@ -13,7 +13,8 @@ import torch
 
 from synth import synth as S
 
-from .api import DenseMLP, MoELayer, pack_int4_groups_dev, pack_int4_rows_dev, pack_int8_rows_dev
+from .api import (DenseMLP, MoELayer, pack_int2_rows_dev, pack_int4_groups_dev, pack_int4_rows_dev,
+                  pack_int8_rows_dev)
 
 
 def device_layer(spec: S.LayerSpec, seed: int = 0, layer: int = 0, device: str = "cuda",
@@ -22,6 +23,8 @@ def device_layer(spec: S.LayerSpec, seed: int = 0, layer: int = 0, device: str =
                        spec.route_scale, device=device, weight_bits=spec.weight_bits, group_size=spec.group_size)
     if spec.group_size:
         pack = lambda w, q, s: pack_int4_groups_dev(w, spec.group_size, q, s)
+    elif spec.weight_bits == 2:
+        pack = pack_int2_rows_dev
     else:
         pack = pack_int8_rows_dev if spec.weight_bits == 8 else pack_int4_rows_dev
     W, b = S.router(spec, seed, layer)

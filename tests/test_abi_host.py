@@ -69,6 +69,7 @@ def test_workspace_sizes():
     dict(has_shared=2), dict(route_scale=float("nan")), dict(weight_bits=5), dict(weight_bits=16),
     dict(group_size=16), dict(group_size=48), dict(group_size=96), dict(group_size=-32),
     dict(group_size=4096), dict(group_size=32, weight_bits=8), dict(group_size=64, I=2080),
+    dict(group_size=32, weight_bits=2), dict(weight_bits=1), dict(weight_bits=3),
 ])
 def test_invalid_layers_rejected(bad):
     L = fake_layer(**bad)
@@ -218,6 +219,20 @@ def test_group_scales_only_on_the_gemv_path():
     assert F(ctypes.byref(L), p, 1, p, 8, p, 1 << 40, None) == _lib.COLI_EUNSUPPORTED      # fused
     X = lib().coli_moe_experts
     assert X(ctypes.byref(L), p, p, p, p, 9, p, 0, p, 1 << 40, None) == _lib.COLI_EUNSUPPORTED
+
+
+def test_int2_experts_only_on_the_gemv_path():
+    L = fake_layer(weight_bits=2)
+    p = ctypes.c_void_p(1 << 20)
+    F = lib().coli_moe_forward
+    assert ws_bytes(L, 4) > 0
+    assert F(ctypes.byref(L), p, 9, p, 0, p, 1 << 40, None) == _lib.COLI_EUNSUPPORTED      # grouped batch
+    assert F(ctypes.byref(L), p, 4, p, 4, p, 1 << 40, None) == _lib.COLI_EUNSUPPORTED      # forced grouped
+    assert F(ctypes.byref(L), p, 1, p, 8, p, 1 << 40, None) == _lib.COLI_EUNSUPPORTED      # fused
+    P = lib().coli_pack_int2_rows_dev
+    for rows, cols in ((0, 64), (4, 48), (4, 16)):
+        assert P(p, rows, cols, p, p, None) == _lib.COLI_EINVAL
+    assert P(p, 4, 64, ctypes.c_void_p((1 << 20) + 8), p, None) == _lib.COLI_EINVAL      # q not 16-byte aligned
 
 
 def test_group_packer_argument_errors():
