@@ -99,3 +99,35 @@ def test_decode_routing_ties(layers, name, T):
     finally:
         L.router_w.copy_(w_save)
         L.router_b.copy_(b_save)
+
+
+@pytest.mark.parametrize("name", ["tiny", "wide"])
+def test_decode_routing_ties_inside_topk(layers, name):
+    """Keys equal in their upper 32 bits, or exactly equal, inside the top-k
+    but not across its last place: the selection is decided by the upper
+    bits and the chosen keys must still be ranked by the exact (key desc,
+    expert asc) order. Pairs of experts hold biases one f32 ulp apart or
+    equal; every other bias is far lower."""
+    L, ref = layers[name]
+    rng = np.random.default_rng(11)
+    k, E = L.top_k, L.E
+    w_save, b_save = L.router_w.clone(), L.router_b.clone()
+    try:
+        for rep in range(3):
+            b = np.full(E, -0.5, np.float32) + rng.random(E).astype(np.float32) * 0.01
+            top = rng.choice(E, size=k, replace=False)
+            levels = np.float32(0.1) * (1 + np.arange((k + 1) // 2, dtype=np.float32))
+            for j in range(0, k, 2):
+                b[top[j]] = levels[j // 2]
+                if j + 1 < k:   # the partner: equal, or one ulp above
+                    b[top[j + 1]] = levels[j // 2] if rep == 1 else np.nextafter(levels[j // 2], np.float32(1))
+            L.router_w.zero_()
+            L.router_b.copy_(torch.from_numpy(b))
+            ref_t = replace(ref, router_w=np.zeros_like(ref.router_w), router_b=b)
+            x = S.tokens(S.TokenSpec(T=2, token_set=90 + rep), L.H, 0)
+            say(f"decode routing ties inside the top-k {name} rep={rep}")
+            idx = _run(L, ref_t, x)
+            assert set(idx[0].tolist()) == set(top.tolist())
+    finally:
+        L.router_w.copy_(w_save)
+        L.router_b.copy_(b_save)
