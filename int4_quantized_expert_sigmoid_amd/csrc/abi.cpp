@@ -506,7 +506,7 @@ int coli_pack_int4_groups_dev(const float *w, int rows, int cols, int group, uin
 
 int coli_pack_int8_rows(const float *w, int rows, int cols, int8_t *q, float *s)
 {
-    if (!w || !q || !s || rows < 1 || cols < 8 || (cols % 8)) return COLI_EINVAL;
+    if (!w || !q || !s || rows < 1 || cols < 32 || (cols % 32)) return COLI_EINVAL;
     for (int r = 0; r < rows; ++r) {
         const float *src = w + (size_t)r * cols;
         float amax = 0.0f;
@@ -520,7 +520,8 @@ int coli_pack_int8_rows(const float *w, int rows, int cols, int8_t *q, float *s)
             float rv = std::isnan(v) ? 0.0f : std::rint(v);
             rv = rv < -127.0f ? -127.0f : (rv > 127.0f ? 127.0f : rv);
             const int j = c & 7;                 // byte of column j in its group of 8
-            dst[(c & ~7) + ((j & 1) ? 4 + (j >> 1) : (j >> 1))] = (int8_t)rv;
+            const int p = (c & 31 & ~7) + ((j & 1) ? 4 + (j >> 1) : (j >> 1));   // byte in its block
+            dst[(p >> 4) * 16 * (cols / 32) + (c >> 5) * 16 + (p & 15)] = (int8_t)rv;
         }
     }
     return COLI_OK;

@@ -94,6 +94,22 @@ __device__ __forceinline__ int dot_block_i2(uint32_t w0, uint32_t w1, const Blk8
     return s;
 }
 
+// Where a row's pieces sit: block b's piece q starts at blk_off(b) +
+// piece_off(q). int8 rows keep the first 16 bytes of every block, then the
+// second 16 bytes of every block (nblk blocks per row), so each piece's
+// load by a wave's 64 lanes reads 1 KB contiguous; int4 and int2 blocks are
+// one piece each.
+template <int WB>
+__device__ __forceinline__ long blk_off(int b)
+{
+    return WB == 8 ? 16L * b : (long)b * WFmt<WB>::BLK_BYTES;
+}
+template <int WB>
+__device__ __forceinline__ long piece_off(int q, int nblk)
+{
+    return WB == 8 ? 16L * q * nblk : 16L * q;
+}
+
 // One block of one weight row times one activation block: S_b scaled by the
 // format's factor applies later; w holds the block's NP pieces.
 template <int WB>

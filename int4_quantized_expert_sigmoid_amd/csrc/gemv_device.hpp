@@ -151,8 +151,8 @@ __device__ __forceinline__ void gateup_rows(const GemvArgs &a, const ItemDesc &i
         }
         // threads past the row's last block read block 0 and multiply it by zero
         const int tb = active ? col : 0;
-        const uint8_t *pg = a.q_a + (row0 + set * RPS) * rowb + tb * WFmt<WB>::BLK_BYTES;
-        const uint8_t *pu = a.q_b + (row0 + set * RPS) * rowb + tb * WFmt<WB>::BLK_BYTES;
+        const uint8_t *pg = a.q_a + (row0 + set * RPS) * rowb + blk_off<WB>(tb);
+        const uint8_t *pu = a.q_b + (row0 + set * RPS) * rowb + blk_off<WB>(tb);
         // group scales of this thread's block column: row stride H / group
         const long gstr = GS ? (long)(nblk >> a.gsh) : 0;
         const float *psg = GS ? a.s_a + (row0 + set * RPS) * gstr + (tb >> a.gsh) : nullptr;
@@ -164,8 +164,8 @@ __device__ __forceinline__ void gateup_rows(const GemvArgs &a, const ItemDesc &i
         for (int r = 0; r < RC; ++r) {
 #pragma unroll
             for (int q = 0; q < NP; ++q) {
-                wg[0][r][q] = load_w_stream<WB>(pg + (long)r * rowb + 16 * q);
-                wu[0][r][q] = load_w_stream<WB>(pu + (long)r * rowb + 16 * q);
+                wg[0][r][q] = load_w_stream<WB>(pg + (long)r * rowb + piece_off<WB>(q, nblk));
+                wu[0][r][q] = load_w_stream<WB>(pu + (long)r * rowb + piece_off<WB>(q, nblk));
             }
             if constexpr (GS) {
                 sg[0][r] = psg[(long)r * gstr];
@@ -180,8 +180,8 @@ __device__ __forceinline__ void gateup_rows(const GemvArgs &a, const ItemDesc &i
                 for (int r = 0; r < RC; ++r) {
 #pragma unroll
                     for (int q = 0; q < NP; ++q) {
-                        wg[cur ^ 1][r][q] = load_w_stream<WB>(pg + (long)((c + 1) * RC + r) * rowb + 16 * q);
-                        wu[cur ^ 1][r][q] = load_w_stream<WB>(pu + (long)((c + 1) * RC + r) * rowb + 16 * q);
+                        wg[cur ^ 1][r][q] = load_w_stream<WB>(pg + (long)((c + 1) * RC + r) * rowb + piece_off<WB>(q, nblk));
+                        wu[cur ^ 1][r][q] = load_w_stream<WB>(pu + (long)((c + 1) * RC + r) * rowb + piece_off<WB>(q, nblk));
                     }
                     if constexpr (GS) {
                         sg[cur ^ 1][r] = psg[(long)((c + 1) * RC + r) * gstr];
@@ -265,7 +265,7 @@ __device__ __forceinline__ void down_rows(const GemvArgs &a, const ItemDesc &it,
     const long rowb = (long)a.I * WB / 8;
     const long row0 = (long)grp * (4 * RPW) + wave * RPW;
     const int ntu = __builtin_amdgcn_readfirstlane(it.nt);
-    const uint8_t *pd = a.q_a + ((long)it.e * a.H + row0) * rowb + (active ? lane : 0) * WFmt<WB>::BLK_BYTES;
+    const uint8_t *pd = a.q_a + ((long)it.e * a.H + row0) * rowb + blk_off<WB>(active ? lane : 0);
     const long gstr = GS ? (long)(nblk >> a.gsh) : 0;     // group scales per row: I / group
     const float *psd = GS ? a.s_a + ((long)it.e * a.H + row0) * gstr + ((active ? lane : 0) >> a.gsh) : nullptr;
 
@@ -274,7 +274,7 @@ __device__ __forceinline__ void down_rows(const GemvArgs &a, const ItemDesc &it,
 #pragma unroll
     for (int r = 0; r < RD; ++r) {
 #pragma unroll
-        for (int q = 0; q < NP; ++q) wd[0][r][q] = load_w_stream<WB>(pd + (long)r * rowb + 16 * q);
+        for (int q = 0; q < NP; ++q) wd[0][r][q] = load_w_stream<WB>(pd + (long)r * rowb + piece_off<WB>(q, nblk));
         if constexpr (GS) sd[0][r] = psd[(long)r * gstr];
     }
 
@@ -307,7 +307,7 @@ __device__ __forceinline__ void down_rows(const GemvArgs &a, const ItemDesc &it,
             for (int r = 0; r < RD; ++r) {
 #pragma unroll
                 for (int q = 0; q < NP; ++q)
-                    wd[cur ^ 1][r][q] = load_w_stream<WB>(pd + (long)((c + 1) * RD + r) * rowb + 16 * q);
+                    wd[cur ^ 1][r][q] = load_w_stream<WB>(pd + (long)((c + 1) * RD + r) * rowb + piece_off<WB>(q, nblk));
                 if constexpr (GS) sd[cur ^ 1][r] = psd[(long)((c + 1) * RD + r) * gstr];
             }
         }

@@ -266,11 +266,11 @@ __device__ __forceinline__ void dn_load_e(const DnArgs &a, int item, long row0, 
     const long rowb = (long)a.I * WB / 8;
     st.e = e;
     st.nt = nt;
-    const uint8_t *pd = a.q + ((long)st.e * a.H + row0) * rowb + (active ? lane : 0) * WFmt<WB>::BLK_BYTES;
+    const uint8_t *pd = a.q + ((long)st.e * a.H + row0) * rowb + blk_off<WB>(active ? lane : 0);
 #pragma unroll
     for (int r = 0; r < RPU; ++r)
 #pragma unroll
-        for (int q = 0; q < NP; ++q) st.wd[r][q] = load_w_stream<WB>(pd + (long)r * rowb + 16 * q);
+        for (int q = 0; q < NP; ++q) st.wd[r][q] = load_w_stream<WB>(pd + (long)r * rowb + piece_off<WB>(q, nblk));
     if constexpr (GS) {
         const long gstr = nblk >> a.gsh;         // group scales per row: I / group
         const float *ps = a.s + ((long)st.e * a.H + row0) * gstr + ((active ? lane : 0) >> a.gsh);

@@ -68,7 +68,7 @@ __global__ void __launch_bounds__(256) k_dense_down(DenseDnArgs a)
     for (int k = 0; k < CPT; ++k) {
         const int col = tid + 256 * k;
         active[k] = col < nblk;
-        pw[k] = a.q + row0 * rowb + (active[k] ? col : 0) * WFmt<WB>::BLK_BYTES;
+        pw[k] = a.q + row0 * rowb + blk_off<WB>(active[k] ? col : 0);
 #pragma unroll
         for (int s = 0; s < NT; ++s) {
             if (s < a.T && active[k]) {
@@ -87,7 +87,7 @@ __global__ void __launch_bounds__(256) k_dense_down(DenseDnArgs a)
 #pragma unroll
         for (int k = 0; k < CPT; ++k)
 #pragma unroll
-            for (int q = 0; q < NP; ++q) w[0][r][k][q] = load_u4_stream(pw[k] + (long)r * rowb + 16 * q);
+            for (int q = 0; q < NP; ++q) w[0][r][k][q] = load_u4_stream(pw[k] + (long)r * rowb + piece_off<WB>(q, nblk));
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
         const int cur = c & 1;
@@ -98,7 +98,7 @@ __global__ void __launch_bounds__(256) k_dense_down(DenseDnArgs a)
                 for (int k = 0; k < CPT; ++k)
 #pragma unroll
                     for (int q = 0; q < NP; ++q)
-                        w[cur ^ 1][r][k][q] = load_u4_stream(pw[k] + (long)((c + 1) * RC + r) * rowb + 16 * q);
+                        w[cur ^ 1][r][k][q] = load_u4_stream(pw[k] + (long)((c + 1) * RC + r) * rowb + piece_off<WB>(q, nblk));
         }
         double v[NT][RC];
 #pragma unroll

@@ -150,7 +150,9 @@ __global__ void __launch_bounds__(256) k_pack_int2(const float *__restrict__ w, 
 }
 
 // int8 rows: d = absmax/127, codes clamp(rint(w/d), -127, 127); within each
-// group of 8 columns column c goes to byte perm8(c) (0,2,4,6 then 1,3,5,7).
+// group of 8 columns column c goes to byte perm8(c) (0,2,4,6 then 1,3,5,7) of
+// its block, and a row holds the first 16 bytes of every block, then the
+// second 16 bytes of every block.
 __global__ void __launch_bounds__(256) k_pack_int8(const float *__restrict__ w, int cols,
                                                    int8_t *__restrict__ q, float *__restrict__ sc)
 {
@@ -167,8 +169,12 @@ __global__ void __launch_bounds__(256) k_pack_int8(const float *__restrict__ w, 
     const float d = __fdiv_rn(amax, 127.0f);
     const float id = (d != 0.0f) ? __fdiv_rn(1.0f, d) : 0.0f;
     int8_t *dst = q + row * (long)cols;
-    for (int c = threadIdx.x; c < cols; c += blockDim.x)
-        dst[(c & ~7) + perm8(c & 7)] = (int8_t)round_clamp(__fmul_rn(src[c], id), -127.0f, 127.0f);
+    const int nblk = cols / 32;
+    for (int c = threadIdx.x; c < cols; c += blockDim.x) {
+        const int p = (c & 31 & ~7) + perm8(c & 7);          // byte of column c in its block
+        dst[(p >> 4) * 16 * nblk + (c >> 5) * 16 + (p & 15)] =
+            (int8_t)round_clamp(__fmul_rn(src[c], id), -127.0f, 127.0f);
+    }
     if (threadIdx.x == 0) sc[row] = d;
 }
 

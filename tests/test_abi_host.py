@@ -247,12 +247,21 @@ def _perm8(j):
     return 4 + (j >> 1) if j & 1 else j >> 1
 
 
+def int8_positions(cols):
+    """Byte of column c in a library int8 row: the 8-group order 0,2,4,6,1,3,5,7
+    inside its block, then the block halves split (all first halves, then all
+    second halves)."""
+    p = np.array([(c & 31 & ~7) + _perm8(c & 7) for c in range(cols)])
+    b = np.arange(cols) >> 5
+    return (p >> 4) * 16 * (cols // 32) + b * 16 + (p & 15)
+
+
 def test_host_int8_packer_matches_oracle_in_library_layout():
     w = S.expert_matrix(S.LayerSpec(H=256, I=128, E=4, top_k=1), 0, 0, 1, S.GATE)
-    edge = np.zeros((4, 64), np.float32)
+    edge = np.zeros((4, 96), np.float32)
     edge[1, :] = 1e-40                      # subnormal row: 1/d overflows
     edge[2, 5] = -3.5                       # single nonzero
-    edge[3, :] = np.linspace(-127, 127, 64) # ties at .5 after scaling
+    edge[3, :] = np.linspace(-127, 127, 96) # ties at .5 after scaling
     for m in (w, edge):
         rows, cols = m.shape
         q = np.empty((rows, cols), np.int8)
@@ -260,9 +269,11 @@ def test_host_int8_packer_matches_oracle_in_library_layout():
         assert lib().coli_pack_int8_rows(ctypes.c_void_p(m.ctypes.data), rows, cols, ctypes.c_void_p(q.ctypes.data),
                                          ctypes.c_void_p(s.ctypes.data)) == 0
         qo, so = O.pack_int8_rows(m)
-        pos = np.array([(c & ~7) + _perm8(c & 7) for c in range(cols)])
+        pos = int8_positions(cols)
+        assert sorted(pos.tolist()) == list(range(cols))
         assert np.array_equal(s, so)
         assert np.array_equal(q[:, pos], qo)       # column c of the oracle sits at byte pos[c]
-    bad = np.zeros((2, 12), np.float32)
-    assert lib().coli_pack_int8_rows(ctypes.c_void_p(bad.ctypes.data), 2, 12, ctypes.c_void_p(bad.ctypes.data),
-                                     ctypes.c_void_p(bad.ctypes.data)) == _lib.COLI_EINVAL
+    bad = np.zeros((2, 48), np.float32)
+    for cols in (12, 48):
+        assert lib().coli_pack_int8_rows(ctypes.c_void_p(bad.ctypes.data), 2, cols, ctypes.c_void_p(bad.ctypes.data),
+                                         ctypes.c_void_p(bad.ctypes.data)) == _lib.COLI_EINVAL

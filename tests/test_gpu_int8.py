@@ -122,7 +122,8 @@ def test_int8_device_layer_equals_int4_on_shared_codes():
         n = codes.shape[-1]
         stored = np.empty_like(codes)
         i = np.arange(n)
-        stored[..., (i & ~7) + np.where(i & 1, 4 + ((i & 7) >> 1), (i & 7) >> 1)] = codes
+        p = (i & 31 & ~7) + np.where(i & 1, 4 + ((i & 7) >> 1), (i & 7) >> 1)     # byte in its block
+        stored[..., (p >> 4) * 16 * (n // 32) + (i >> 5) * 16 + (p & 15)] = codes
         getattr(L8, name).copy_(torch.from_numpy(stored))
     for T in (1, 4, 8):
         x = S.tokens(S.TokenSpec(T=T, token_set=300 + T), sp4.H, 0)
