@@ -377,7 +377,9 @@ int coli_dense_forward(const coli_dense_mlp *M, const float *x, const float *gam
     const WsLayout lay = make_dense_layout(*M, T);
     if (ws_bytes < lay.total) return COLI_EWORKSPACE;
     const bool grouped = (flags & COLI_PATH_GROUPED) || (!(flags & COLI_PATH_GEMV) && T > COLI_GEMV_MAX_T);
-    if (grouped && M->weight_bits == 8) return COLI_EUNSUPPORTED;
+    // int8 weights have no grouped kernels: larger batches take the token-GEMV
+    // kernels in chunks of 8 tokens (each chunk reads the weights once)
+    if ((flags & COLI_PATH_GROUPED) && M->weight_bits == 8) return COLI_EUNSUPPORTED;
     hipStream_t s = (hipStream_t)stream;
     char *base = static_cast<char *>(ws);
     const bool acc = (flags & COLI_ACCUMULATE) != 0;
@@ -389,7 +391,14 @@ int coli_dense_forward(const coli_dense_mlp *M, const float *x, const float *gam
     if (launch_quant_q8(x, T, M->H, reinterpret_cast<int8_t *>(base + lay.xq), reinterpret_cast<float *>(base + lay.xs),
                         true, s) != hipSuccess)
         return COLI_EDEVICE;
-    if (!grouped) return status(launch_dense_gemv(*M, T, lay, base, y, acc, s));
+    if (!grouped) return status(launch_dense_gemv(*M, T, 0, lay, base, y, acc, s));
+    if (M->weight_bits == 8) {
+        for (int t0 = 0; t0 < T; t0 += COLI_GEMV_MAX_T) {
+            const int tc = T - t0 < COLI_GEMV_MAX_T ? T - t0 : COLI_GEMV_MAX_T;
+            if (launch_dense_gemv(*M, tc, t0, lay, base, y, acc, s) != hipSuccess) return COLI_EDEVICE;
+        }
+        return COLI_OK;
+    }
     // one expert holding every token on the grouped kernels of the expert path
     coli_moe_layer L;
     std::memset(&L, 0, sizeof(L));

@@ -136,7 +136,8 @@ hipError_t launch_decode_fused(const coli_moe_layer &L, const float *x, int T, c
 typedef coli_dense_mlp DenseLayer;
 typedef WsLayout DenseLayout;
 WsLayout make_dense_layout(const coli_dense_mlp &M, int T);
-hipError_t launch_dense_gemv(const DenseLayer &M, int T, const DenseLayout &lay, char *ws, float *y, bool accumulate,
+// T <= 8 tokens from token t0 on (their Q8(x), h, hq, hs and y rows)
+hipError_t launch_dense_gemv(const DenseLayer &M, int T, int t0, const DenseLayout &lay, char *ws, float *y, bool accumulate,
                              hipStream_t s);
 hipError_t launch_dense_setup(int T, const DenseLayout &lay, char *ws, hipStream_t s);
 hipError_t launch_dense_out(int T, int H, const DenseLayout &lay, const char *ws, float *y, bool accumulate,

@@ -181,22 +181,23 @@ void launch_dense_gemv_wb(const DenseLayer &M, int T, const GemvArgs &g, const D
 
 } // namespace
 
-hipError_t launch_dense_gemv(const DenseLayer &M, int T, const DenseLayout &lay, char *ws, float *y, bool accumulate,
-                             hipStream_t s)
+hipError_t launch_dense_gemv(const DenseLayer &M, int T, int t0, const DenseLayout &lay, char *ws, float *y,
+                             bool accumulate, hipStream_t s)
 {
+    const long t = t0;
     GemvArgs g;
     g.q_a = M.gate_q; g.s_a = M.gate_s; g.q_b = M.up_q; g.s_b = M.up_s;
     g.H = M.H; g.I = M.I; g.E = 0; g.T = T; g.has_shared = 0; g.gsh = 0; g.item0 = 0; g.x = nullptr;
-    g.xq = reinterpret_cast<const int8_t *>(ws + lay.xq);
-    g.xs = reinterpret_cast<const float *>(ws + lay.xs);
+    g.xq = reinterpret_cast<const int8_t *>(ws + lay.xq) + t * M.H;
+    g.xs = reinterpret_cast<const float *>(ws + lay.xs) + t * (M.H / QK);
     g.ctrl = nullptr; g.item_expert = nullptr; g.item_ntok = nullptr; g.item_tok = nullptr;
-    g.h = reinterpret_cast<float *>(ws + lay.h);
-    g.hq = reinterpret_cast<int8_t *>(ws + lay.hq);
-    g.hs = reinterpret_cast<float *>(ws + lay.hs);
+    g.h = reinterpret_cast<float *>(ws + lay.h) + t * M.I;
+    g.hq = reinterpret_cast<int8_t *>(ws + lay.hq) + t * M.I;
+    g.hs = reinterpret_cast<float *>(ws + lay.hs) + t * (M.I / QK);
     g.ye = nullptr;
     DenseDnArgs d;
     d.q = M.down_q; d.s = M.down_s;
-    d.hq = g.hq; d.hs = g.hs; d.y = y;
+    d.hq = g.hq; d.hs = g.hs; d.y = y + t * M.H;
     d.H = M.H; d.I = M.I; d.T = T; d.accumulate = accumulate ? 1 : 0;
     if (M.weight_bits == 8) launch_dense_gemv_wb<8>(M, T, g, d, s);
     else launch_dense_gemv_wb<4>(M, T, g, d, s);

@@ -263,6 +263,8 @@ GLM52_DENSE = DenseSpec(H=6144, I=12288, w_outlier_rate=0.001)
 DENSE_WORKLOADS = {
     "glm52_dense_T1": DenseWorkload("glm52_dense_T1", GLM52_DENSE, TokenSpec(T=1, outlier_channels=61)),
     "glm52_dense_T4": DenseWorkload("glm52_dense_T4", GLM52_DENSE, TokenSpec(T=4, rho=0.8, outlier_channels=61)),
+    # a 64-token prefill chunk through an int8 dense layer: eight 8-token GEMV passes
+    "glm52_dense_T64": DenseWorkload("glm52_dense_T64", GLM52_DENSE, TokenSpec(T=64, outlier_channels=61)),
 }
 
 

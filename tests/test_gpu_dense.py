@@ -1,5 +1,6 @@
 """GPU parity of the dense MLP (coli_dense_forward) through the C ABI against
-the oracle's O15, on both paths (token-GEMV for T <= 8, grouped MFMA above),
+the oracle's O15, on both paths (token-GEMV for T <= 8, grouped MFMA above;
+int8 above 8 tokens on the token-GEMV kernels in chunks of 8),
 both weight formats, intermediate sizes below and above 256 blocks (one and
 two block columns per thread in the down kernel), with the RMSNorm input and
 the residual added in place."""
@@ -73,6 +74,22 @@ def test_dense_grouped_small(T, flags):
     check(SMALL, T, flags, token_set=20 + T)
 
 
+@pytest.mark.parametrize("T", [9, 16, 21])
+def test_dense_int8_chunked(T):
+    """int8 weights past 8 tokens: the token-GEMV kernels over chunks of 8
+    (a full chunk, full chunks only, a ragged last chunk), bit for bit the
+    oracle's O15 per token; an explicit grouped request is refused."""
+    from dataclasses import replace
+    from int4_quantized_expert_sigmoid_amd._lib import ColiError, COLI_EUNSUPPORTED
+    spec = replace(SMALL, weight_bits=8)
+    y = check(spec, T, token_set=70 + T, accumulate=(T == 21))
+    M = device_dense(spec, 0, 0)
+    x = dev(S.tokens(S.TokenSpec(T=T, token_set=80 + T), spec.H, 0))
+    with pytest.raises(ColiError) as e:
+        api.dense_forward(M, x, api.dense_workspace(M, T), flags=COLI_PATH_GROUPED)
+    assert e.value.code == COLI_EUNSUPPORTED
+
+
 def test_dense_paths_agree():
     """The same tokens through both paths: identical outputs (same integer
     block dots, f64 sums)."""
@@ -97,7 +114,7 @@ def test_dense_rmsnorm_and_residual_in_place():
     check(S.DenseSpec(H=256, I=512, weight_bits=4), 20, gamma=True, accumulate=True, token_set=53)
 
 
-@pytest.mark.parametrize("bits,T", [(8, 1), (4, 2)])
+@pytest.mark.parametrize("bits,T", [(8, 1), (4, 2), (8, 12)])
 def test_dense_glm_shape(bits, T):
     """H = 6144, I = 12288: the dense layers' shape read for GLM-5.2."""
     from dataclasses import replace
