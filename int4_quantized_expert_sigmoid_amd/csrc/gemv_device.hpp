@@ -172,9 +172,10 @@ __device__ __forceinline__ void gateup_rows(const GemvArgs &a, const ItemDesc &i
                 su[0][r] = psu[(long)r * gstr];
             }
         }
-#pragma unroll
-        for (int c = 0; c < NC; ++c) {
-            const int cur = c & 1;
+        // chunk c computes from buffer cur (= c % 2) while chunk c + 1 loads
+        // into the other; cur must fold to a constant at every call, or the
+        // buffers go to scratch memory
+        auto chunk = [&](int c, int cur) {
             if (c + 1 < NC) {
 #pragma unroll
                 for (int r = 0; r < RC; ++r) {
@@ -210,6 +211,18 @@ __device__ __forceinline__ void gateup_rows(const GemvArgs &a, const ItemDesc &i
                 wave_transpose_reduce<NV>(v[s]);
                 if ((lane & (64 / NV - 1)) == 0) sh.red[wv][s][2 * (set * RPS + c * RC) + vi] = v[s][0];
             }
+        };
+        if constexpr (NT >= 8) {
+            // 8 slots: the unrolled loop would cost more registers than
+            // its loads in flight are worth, so it runs in pairs
+#pragma unroll 1
+            for (int c = 0; c < NC; c += 2) {
+                chunk(c, 0);
+                if (c + 1 < NC) chunk(c + 1, 1);
+            }
+        } else {
+#pragma unroll
+            for (int c = 0; c < NC; ++c) chunk(c, c & 1);
         }
     }
     __syncthreads();
