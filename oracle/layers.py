@@ -100,7 +100,8 @@ def forward_token(spec: S.LayerSpec, cache: ExpertCache, W: np.ndarray, b: np.nd
     """One token through the layer (O6 -> O3 -> O7 -> O8), regenerating experts."""
     idx, w = O.route(W, b, x[None, :], spec.top_k, spec.n_group, spec.topk_group, spec.route_scale)
     xq, xs = O.quant_q8(x)
-    outs = [O.expert(*cache[int(e)].args(), xq, xs, group=spec.group_size) for e in idx[0]]
-    sh = O.expert(*cache[spec.E].args(), xq, xs, group=spec.group_size) if spec.has_shared else None
+    kw = dict(group=spec.group_size, wbits=spec.weight_bits)
+    outs = [O.expert(*cache[int(e)].args(), xq, xs, **kw) for e in idx[0]]
+    sh = O.expert(*cache[spec.E].args(), xq, xs, **kw) if spec.has_shared else None
     y = O.combine(np.stack([o.y for o in outs]), w[0], None if sh is None else sh.y)
     return TokenResult(idx[0], w[0], xq, xs, tuple(outs) + ((sh,) if sh else ()), y)

@@ -154,10 +154,6 @@ def rowdot_groups(q4, s4, group: int, q8, d8) -> np.ndarray:
 
 
 # ---------------------------------------------------------------- O18 / O19
-class Int2Rows(np.ndarray):
-    """uint8 [rows][cols/4] holding int2 codes (tags the format for expert())."""
-
-
 def pack_int2_rows(w: np.ndarray):
     """int2 codes, four per byte (element 4j+i in bits 2i..2i+1 of byte j), and f32 row scales."""
     w = _c(w, np.float32)
@@ -167,7 +163,7 @@ def pack_int2_rows(w: np.ndarray):
     q = np.empty((rows, cols // 4), dtype=np.uint8)
     s = np.empty(rows, dtype=np.float32)
     _lib().oracle_pack_int2_rows(_p(w), rows, cols, _p(q), _p(s))
-    return q.view(Int2Rows), s
+    return q, s
 
 
 def crumb(byte: int, i: int) -> int:
@@ -258,16 +254,14 @@ class ExpertOut:
 
 
 def _wbits(q) -> int:
-    """Weight format from the packed array: int8 rows, int2 rows (the Int2Rows
-    tag pack_int2_rows returns), or uint8 bytes of int4 pairs."""
-    if isinstance(q, Int2Rows):
-        return 2
+    """Weight format from the packed array's dtype: int8 rows, or uint8 bytes
+    of int4 pairs (int2 bytes are uint8 too: callers name them, wbits=2)."""
     return 8 if np.asarray(q).dtype == np.int8 else 4
 
 
 def expert(gate_q, gate_s, up_q, up_s, down_q, down_s, xq, xs, group: int = 0, wbits: int = 0) -> ExpertOut:
     """O7 (int4 rows, uint8 [I][H/2]), its int8 form (int8 rows [I][H]) or its
-    int2 form (wbits=2 or Int2Rows arrays, uint8 [I][H/4]); with group > 0,
+    int2 form (wbits=2, uint8 [I][H/4]); with group > 0,
     int4 rows with O16 group scales (gate/up [I][H/group], down [H][I/group])."""
     wb = wbits or _wbits(gate_q)
     dt = np.int8 if wb == 8 else np.uint8

@@ -109,7 +109,7 @@ def test_expert_int2_equals_int4_on_the_same_codes():
     p2 = OL.packed_expert(spec, 0, 0, 3)
     x = S.tokens(S.TokenSpec(T=1, outlier_channels=2), spec.H, 0)[0]
     xq, xs = O.quant_q8(x)
-    a = O.expert(*p2.args(), xq, xs)
+    a = O.expert(*p2.args(), xq, xs, wbits=2)
     b = O.expert(_as_int4(p2.gate_q), p2.gate_s, _as_int4(p2.up_q), p2.up_s, _as_int4(p2.down_q), p2.down_s, xq, xs)
     for f in ("y", "g", "u", "h", "hq", "hs"):
         assert np.array_equal(getattr(a, f), getattr(b, f)), f
