@@ -165,3 +165,21 @@ def test_forward_glm_int2(glm2, T):
     y = api.moe_forward(L, dev(x), ws).cpu().numpy()
     toks = [OL.forward_token(GLM2, cache, W, b, x[t]) for t in range(T)]
     _check(L, toks, T, ws, y)
+
+
+@pytest.mark.parametrize("T", [1, 3, 8])
+def test_experts_teacher_forced_tiny_int2(tiny2, T):
+    """The expert stage alone (coli_moe_experts: the standalone GEMV gate/up
+    and down kernels) fed the GPU's Q8(x) and the oracle's routing."""
+    L, ref = tiny2
+    x = S.tokens(S.TokenSpec(T=T, token_set=630 + T), TINY2.H, 0)
+    xq, xs = api.quant_act_q8(dev(x))
+    idx_o, w_o = O.route(ref.router_w, ref.router_b, x, TINY2.top_k)
+    y = api.moe_experts(L, xq, xs, dev(idx_o), dev(w_o), api.workspace(L, T)).cpu().numpy()
+    xq_h, xs_h = xq.cpu().numpy(), xs.cpu().numpy()
+    cache = OL.ExpertCache(TINY2, 0, 0)
+    for t in range(T):
+        outs = [O.expert(*cache[int(e)].args(), xq_h[t], xs_h[t], wbits=2) for e in idx_o[t]]
+        sh = O.expert(*cache[TINY2.E].args(), xq_h[t], xs_h[t], wbits=2)
+        y_o = O.combine(np.stack([o.y for o in outs]), w_o[t], sh.y)
+        assert np.array_equal(y[t], y_o), f"token {t}"
