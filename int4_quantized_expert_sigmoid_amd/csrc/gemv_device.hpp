@@ -358,11 +358,12 @@ template <> struct GemvTune<4> { static constexpr int RC = 2, RD = 4; };
 template <> struct GemvTune<8> { static constexpr int RC = 2, RD = 2; };
 
 // The same per weight format: an int8 row block is twice the bytes, so a
-// chunk holds half the rows, except with 8 slots, where one int8 row per
-// chunk leaves too few bytes in flight for the long dot-product work of a
-// chunk (two rows: 68 -> 51 us per 151 MB gate/up pass).
+// chunk holds half the rows, except with 4 or more slots, where one int8
+// row per chunk leaves too few bytes in flight for the long dot-product
+// work of a chunk (two rows: 68 -> 51 us per 151 MB gate/up pass at 8
+// slots, dense T=4 59 -> 56 us).
 template <int NT, int WB> struct GemvTuneW {
-    static constexpr int RC = WB == 8 ? (NT >= 8 ? 2 : (GemvTune<NT>::RC > 1 ? GemvTune<NT>::RC / 2 : 1))
+    static constexpr int RC = WB == 8 ? (NT >= 4 ? 2 : (GemvTune<NT>::RC > 1 ? GemvTune<NT>::RC / 2 : 1))
                                       : GemvTune<NT>::RC;
     static constexpr int RD = WB == 8 ? (GemvTune<NT>::RD > 1 ? GemvTune<NT>::RD / 2 : 1) : GemvTune<NT>::RD;
 };
