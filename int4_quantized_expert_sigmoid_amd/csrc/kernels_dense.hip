@@ -7,8 +7,8 @@
 //
 // T <= 8: the token-GEMV gate/up body of the expert path (one item, the T
 // tokens as its slots) and k_dense_down, a GEMV over the H down rows whose
-// threads own block columns of every row (the intermediate size can exceed
-// one wave's 64 columns). T > 8: the grouped MFMA kernels of the expert path
+// threads own one (or, at one slot, two) block columns of every row (up to
+// 8 waves: the intermediate size can exceed one wave's 64 columns). T > 8: the grouped MFMA kernels of the expert path
 // over one "expert" holding all T tokens, then k_dense_out.
 #include "gemv_device.hpp"
 #include "internal.hpp"
@@ -40,20 +40,21 @@ struct DenseDnArgs {
 };
 
 constexpr int DD_ROWS = 8;     // down rows per workgroup
+constexpr int DD_WAVES = 8;    // at most: I/32 <= 512 block columns
 
-// Down rows [blockIdx*8, +8). Thread c owns block columns c, c + 256, ...
-// (CPT of them) of every row, with the activations of those columns for the
-// T slots in registers; rows stream in chunks of RC with the next chunk's
-// loads in flight. Per-row partials: a transposing wave reduction, then the
-// waves in order through LDS.
+// Down rows [blockIdx*8, +8). Thread c owns block columns c, c + blockDim,
+// ... (CPT of them) of every row, with the activations of those columns for
+// the T slots in registers; rows stream in chunks of RC with the next
+// chunk's loads in flight. Per-row partials: a transposing wave reduction,
+// then the waves in order through LDS.
 template <int NT, int WB, int CPT, int RC>
-__global__ void __launch_bounds__(256) k_dense_down(DenseDnArgs a)
+__global__ void __launch_bounds__(64 * DD_WAVES) k_dense_down(DenseDnArgs a)
 {
     constexpr int NP = WFmt<WB>::BLK_BYTES / 16;
     constexpr double KS = WFmt<WB>::KSCALE;
     constexpr int NC = DD_ROWS / RC;
     static_assert(DD_ROWS % RC == 0, "whole chunks");
-    __shared__ double red[4][NT][DD_ROWS];
+    __shared__ double red[DD_WAVES][NT][DD_ROWS];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int nblk = a.I / QK;
     const long rowb = (long)a.I * WB / 8;
@@ -66,7 +67,7 @@ __global__ void __launch_bounds__(256) k_dense_down(DenseDnArgs a)
     const uint8_t *pw[CPT];
 #pragma unroll
     for (int k = 0; k < CPT; ++k) {
-        const int col = tid + 256 * k;
+        const int col = tid + (int)blockDim.x * k;
         active[k] = col < nblk;
         pw[k] = a.q + row0 * rowb + blk_off<WB>(active[k] ? col : 0);
 #pragma unroll
@@ -122,7 +123,7 @@ __global__ void __launch_bounds__(256) k_dense_down(DenseDnArgs a)
         }
     }
     __syncthreads();
-    const int nw = (nblk + 63) >> 6 < 4 ? (nblk + 63) >> 6 : 4;   // waves that own columns
+    const int nw = (int)(blockDim.x >> 6);      // every wave owns columns
     for (int i = tid; i < NT * DD_ROWS; i += blockDim.x) {
         const int s = i / DD_ROWS, r = i % DD_ROWS;
         if (s >= a.T) continue;
@@ -163,10 +164,18 @@ template <int NT, int WB>
 void launch_dense_down_nt(const DenseDnArgs &d, hipStream_t s)
 {
     const dim3 grid((unsigned)(d.H / DD_ROWS));
-    const bool two = d.I / QK > 256;             // two block columns per thread (I <= 16384)
+    const int nblk = d.I / QK;                   // <= 512 (I <= 16384)
     constexpr int RC = NT <= 2 ? 4 : (NT <= 4 ? 2 : 1);
-    if (two) COLI_LAUNCH((k_dense_down<NT, WB, 2, RC>), grid, dim3(256), 0, s, d);
-    else COLI_LAUNCH((k_dense_down<NT, WB, 1, RC>), grid, dim3(256), 0, s, d);
+    // one slot: four waves with a second column for the blocks past 256
+    // (measured a little faster there); more slots: one column per thread,
+    // as many waves as the blocks need (fewer registers per thread)
+    if constexpr (NT == 1) {
+        if (nblk > 256) {
+            COLI_LAUNCH((k_dense_down<NT, WB, 2, RC>), grid, dim3(256), 0, s, d);
+            return;
+        }
+    }
+    COLI_LAUNCH((k_dense_down<NT, WB, 1, RC>), grid, dim3((unsigned)(64 * ((nblk + 63) / 64))), 0, s, d);
 }
 
 template <int WB>

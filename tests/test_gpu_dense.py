@@ -102,7 +102,7 @@ def test_dense_paths_agree():
 
 @pytest.mark.parametrize("bits", [4, 8])
 def test_dense_two_columns_per_thread(bits):
-    """I = 8448: 264 blocks per down row, past one block column per thread."""
+    """I = 8448: 264 blocks per down row, a fifth wave in the down kernel with 8 of its lanes in use."""
     spec = S.DenseSpec(H=256, I=8448, w_outlier_rate=0.01, weight_bits=bits)
     check(spec, 3, token_set=41)
 
