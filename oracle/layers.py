@@ -2,11 +2,14 @@
 oracle's own packer. TEST INFRASTRUCTURE ONLY (tests, smoke, CPU baseline).
 
 For the GLM-5.2-shaped layers the oracle never holds all 257 experts: it
-regenerates only the experts a token selects (ExpertCache)."""
+regenerates only the experts a token selects (ExpertCache), or, for a whole
+batch (forward_batch), takes the experts one at a time from a source the
+caller gives (the f32 weights may come from the generator's device twin,
+which writes the same values; the packing is always the oracle's own)."""
 from __future__ import annotations
 
 from dataclasses import dataclass
-from typing import Dict, Tuple
+from typing import Callable, Dict, Tuple
 
 import numpy as np
 
@@ -27,7 +30,8 @@ class PackedExpert:
         return (self.gate_q, self.gate_s, self.up_q, self.up_s, self.down_q, self.down_s)
 
 
-def packed_expert(spec: S.LayerSpec, seed: int, layer: int, e: int) -> PackedExpert:
+def pack_matrices(spec: S.LayerSpec, gate_w: np.ndarray, up_w: np.ndarray, down_w: np.ndarray) -> PackedExpert:
+    """One expert's f32 matrices packed in the spec's format by the oracle."""
     if spec.group_size:
         pack = lambda w: O.pack_int4_groups(w, spec.group_size)
     elif spec.weight_bits == 2:
@@ -35,9 +39,13 @@ def packed_expert(spec: S.LayerSpec, seed: int, layer: int, e: int) -> PackedExp
     else:
         pack = O.pack_int8_rows if spec.weight_bits == 8 else O.pack_int4_rows
     mats = []
-    for m in (S.GATE, S.UP, S.DOWN):
-        mats.extend(pack(S.expert_matrix(spec, seed, layer, e, m)))
+    for w in (gate_w, up_w, down_w):
+        mats.extend(pack(w))
     return PackedExpert(*mats)
+
+
+def packed_expert(spec: S.LayerSpec, seed: int, layer: int, e: int) -> PackedExpert:
+    return pack_matrices(spec, *[S.expert_matrix(spec, seed, layer, e, m) for m in (S.GATE, S.UP, S.DOWN)])
 
 
 class ExpertCache:
@@ -105,3 +113,52 @@ def forward_token(spec: S.LayerSpec, cache: ExpertCache, W: np.ndarray, b: np.nd
     sh = O.expert(*cache[spec.E].args(), xq, xs, **kw) if spec.has_shared else None
     y = O.combine(np.stack([o.y for o in outs]), w[0], None if sh is None else sh.y)
     return TokenResult(idx[0], w[0], xq, xs, tuple(outs) + ((sh,) if sh else ()), y)
+
+
+@dataclass
+class BatchResult:
+    """A batch through the layer. Per (token, slot): slots 0..k-1 are the
+    routed experts in routing order, slot k the shared expert."""
+    idx: np.ndarray      # [T][k]
+    w: np.ndarray        # [T][k]
+    xq: np.ndarray       # [T][H]
+    xs: np.ndarray       # [T][H/32]
+    h: np.ndarray        # [T][k+s][I]
+    hq: np.ndarray       # [T][k+s][I]
+    hs: np.ndarray       # [T][k+s][I/32]
+    ye: np.ndarray       # [T][k+s][H]
+    y: np.ndarray        # [T][H]
+
+
+def forward_batch(spec: S.LayerSpec, W: np.ndarray, b: np.ndarray, x: np.ndarray,
+                  expert_of: Callable[[int], PackedExpert], log: Callable[[str], None] = None) -> BatchResult:
+    """O6 (routing of every token) -> O3 (Q8 of every token) -> O7 for every
+    (token, expert) pair -> O8 for every token: the same arithmetic as
+    forward_token, token by token, with each expert taken once (from
+    expert_of) for all of its tokens."""
+    x = np.ascontiguousarray(np.atleast_2d(x), np.float32)
+    T, H = x.shape
+    k, I, E = spec.top_k, spec.I, spec.E
+    idx, w = O.route(W, b, x, k, spec.n_group, spec.topk_group, spec.route_scale)
+    xq, xs = O.quant_q8(x)
+    ns = k + spec.has_shared
+    r = BatchResult(idx, w, xq, xs, np.zeros((T, ns, I), np.float32), np.zeros((T, ns, I), np.int8),
+                    np.zeros((T, ns, I // 32), np.float32), np.zeros((T, ns, H), np.float32),
+                    np.empty((T, H), np.float32))
+    experts = sorted(set(int(e) for e in idx.reshape(-1)))
+    if spec.has_shared:
+        experts.append(E)
+    kw = dict(group=spec.group_size, wbits=spec.weight_bits)
+    for n, e in enumerate(experts):
+        if e == E and spec.has_shared:
+            toks, slots = np.arange(T), np.full(T, k)
+        else:
+            toks, slots = np.nonzero(idx == e)
+        P = expert_of(e)
+        o = O.expert_tokens(*P.args(), xq[toks], xs[toks], **kw)
+        r.ye[toks, slots], r.h[toks, slots], r.hq[toks, slots], r.hs[toks, slots] = o.y, o.h, o.hq, o.hs
+        if log and (n + 1) % 32 == 0:
+            log(f"oracle: {n + 1} of {len(experts)} experts")
+    for t in range(T):
+        r.y[t] = O.combine(r.ye[t, :k], w[t], r.ye[t, k] if spec.has_shared else None)
+    return r

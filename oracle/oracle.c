@@ -11,6 +11,18 @@
 #include <math.h>
 #include <stdlib.h>
 #include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+int oracle_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
 
 /* Shared rounding rule of both quantisers: round half to even, clamp to
  * [lo, hi]; a NaN product (0 * inf) gives 0. */
@@ -26,6 +38,7 @@ static int round_clamp(float v, float lo, float hi)
 /* ------------------------------------------------------------ O1 / O2 ---- */
 void oracle_pack_int4_rows(const float *w, int rows, int cols, uint8_t *q, float *s)
 {
+#pragma omp parallel for schedule(static)
     for (int r = 0; r < rows; ++r) {
         const float *row = w + (size_t)r * cols;
         float amax = 0.0f;
@@ -80,16 +93,22 @@ void oracle_quant_q8(const float *x, int n, int8_t *q, float *d)
 }
 
 /* ------------------------------------------------------------- O4 / O5 --- */
+/* S_b of one packed row: the exact int32 dot of block b's 32 int4 codes with
+ * the 32 Q8 codes of the same block. */
+static int32_t block_dot_i4(const uint8_t *row, const int8_t *q8, int b)
+{
+    int32_t acc = 0;
+    for (int k = 32 * b; k < 32 * b + 32; ++k)
+        acc += oracle_nibble(row[k / 2], k & 1) * (int32_t)q8[k];
+    return acc;
+}
+
 void oracle_block_dots(const uint8_t *q4, const int8_t *q8, int rows, int cols, int32_t *S)
 {
     for (int r = 0; r < rows; ++r) {
         const uint8_t *row = q4 + (size_t)r * (cols / 2);
-        for (int b = 0; b < cols / 32; ++b) {
-            int32_t acc = 0;
-            for (int k = 32 * b; k < 32 * b + 32; ++k)
-                acc += oracle_nibble(row[k / 2], k & 1) * (int32_t)q8[k];
-            S[(size_t)r * (cols / 32) + b] = acc;
-        }
+        for (int b = 0; b < cols / 32; ++b)
+            S[(size_t)r * (cols / 32) + b] = block_dot_i4(row, q8, b);
     }
 }
 
@@ -97,20 +116,20 @@ void oracle_rowdot(const uint8_t *q4, const float *s4, const int8_t *q8, const f
                    int rows, int cols, float *out)
 {
     const int nb = cols / 32;
-    int32_t *S = (int32_t *)malloc(sizeof(int32_t) * (size_t)nb);
+#pragma omp parallel for schedule(static)
     for (int r = 0; r < rows; ++r) {
-        oracle_block_dots(q4 + (size_t)r * (cols / 2), q8, 1, cols, S);
+        const uint8_t *row = q4 + (size_t)r * (cols / 2);
         double acc = 0.0;
-        for (int b = 0; b < nb; ++b) acc += (double)d8[b] * (double)S[b];
+        for (int b = 0; b < nb; ++b) acc += (double)d8[b] * (double)block_dot_i4(row, q8, b);
         out[r] = (float)((double)s4[r] * acc);
     }
-    free(S);
 }
 
 /* ----------------------------------------------------------- O16 / O17 --- */
 void oracle_pack_int4_groups(const float *w, int rows, int cols, int group, uint8_t *q, float *s)
 {
     const int ng = cols / group;
+#pragma omp parallel for schedule(static)
     for (int r = 0; r < rows; ++r) {
         const float *row = w + (size_t)r * cols;
         uint8_t *dst = q + (size_t)r * (cols / 2);
@@ -148,22 +167,22 @@ void oracle_rowdot_groups(const uint8_t *q4, const float *s4, int group, const i
                           int rows, int cols, float *out)
 {
     const int nb = cols / 32, ng = cols / group;
-    int32_t *S = (int32_t *)malloc(sizeof(int32_t) * (size_t)nb);
+#pragma omp parallel for schedule(static)
     for (int r = 0; r < rows; ++r) {
-        oracle_block_dots(q4 + (size_t)r * (cols / 2), q8, 1, cols, S);
+        const uint8_t *row = q4 + (size_t)r * (cols / 2);
         double acc = 0.0;
         for (int b = 0; b < nb; ++b) {
             double sg = (double)s4[(size_t)r * ng + (32 * b) / group];
-            acc += sg * ((double)d8[b] * (double)S[b]);
+            acc += sg * ((double)d8[b] * (double)block_dot_i4(row, q8, b));
         }
         out[r] = (float)acc;
     }
-    free(S);
 }
 
 /* ----------------------------------------------------------- O18 / O19 --- */
 void oracle_pack_int2_rows(const float *w, int rows, int cols, uint8_t *q, float *s)
 {
+#pragma omp parallel for schedule(static)
     for (int r = 0; r < rows; ++r) {
         const float *row = w + (size_t)r * cols;
         float amax = 0.0f;
@@ -197,16 +216,22 @@ void oracle_unpack_int2_rows(const uint8_t *q, const float *s, int rows, int col
             w[(size_t)r * cols + c] = (double)s[r] * (double)oracle_crumb(q[(size_t)r * (cols / 4) + c / 4], c & 3);
 }
 
+/* S_b of one int2 row: the exact int32 dot of block b's 32 two-bit codes with
+ * the block's 32 Q8 codes. */
+static int32_t block_dot_i2(const uint8_t *row, const int8_t *q8, int b)
+{
+    int32_t acc = 0;
+    for (int k = 32 * b; k < 32 * b + 32; ++k)
+        acc += oracle_crumb(row[k / 4], k & 3) * (int32_t)q8[k];
+    return acc;
+}
+
 void oracle_block_dots_i2(const uint8_t *q2, const int8_t *q8, int rows, int cols, int32_t *S)
 {
     for (int r = 0; r < rows; ++r) {
         const uint8_t *row = q2 + (size_t)r * (cols / 4);
-        for (int b = 0; b < cols / 32; ++b) {
-            int32_t acc = 0;
-            for (int k = 32 * b; k < 32 * b + 32; ++k)
-                acc += oracle_crumb(row[k / 4], k & 3) * (int32_t)q8[k];
-            S[(size_t)r * (cols / 32) + b] = acc;
-        }
+        for (int b = 0; b < cols / 32; ++b)
+            S[(size_t)r * (cols / 32) + b] = block_dot_i2(row, q8, b);
     }
 }
 
@@ -214,19 +239,19 @@ void oracle_rowdot_i2(const uint8_t *q2, const float *s2, const int8_t *q8, cons
                       int rows, int cols, float *out)
 {
     const int nb = cols / 32;
-    int32_t *S = (int32_t *)malloc(sizeof(int32_t) * (size_t)nb);
+#pragma omp parallel for schedule(static)
     for (int r = 0; r < rows; ++r) {
-        oracle_block_dots_i2(q2 + (size_t)r * (cols / 4), q8, 1, cols, S);
+        const uint8_t *row = q2 + (size_t)r * (cols / 4);
         double acc = 0.0;
-        for (int b = 0; b < nb; ++b) acc += (double)d8[b] * (double)S[b];
+        for (int b = 0; b < nb; ++b) acc += (double)d8[b] * (double)block_dot_i2(row, q8, b);
         out[r] = (float)((double)s2[r] * acc);
     }
-    free(S);
 }
 
 /* ----------------------------------------------------------- O11 - O13 --- */
 void oracle_pack_int8_rows(const float *w, int rows, int cols, int8_t *q, float *s)
 {
+#pragma omp parallel for schedule(static)
     for (int r = 0; r < rows; ++r) {
         const float *row = w + (size_t)r * cols;
         float amax = 0.0f;
@@ -242,15 +267,20 @@ void oracle_pack_int8_rows(const float *w, int rows, int cols, int8_t *q, float 
     }
 }
 
+/* S_b of one int8 row: the exact int32 dot of block b's 32 weight codes with
+ * the block's 32 Q8 codes. */
+static int32_t block_dot_i8(const int8_t *row, const int8_t *q8, int b)
+{
+    int32_t acc = 0;
+    for (int k = 32 * b; k < 32 * b + 32; ++k) acc += (int32_t)row[k] * (int32_t)q8[k];
+    return acc;
+}
+
 void oracle_block_dots_i8(const int8_t *qw, const int8_t *q8, int rows, int cols, int32_t *S)
 {
     for (int r = 0; r < rows; ++r) {
         const int8_t *row = qw + (size_t)r * cols;
-        for (int b = 0; b < cols / 32; ++b) {
-            int32_t acc = 0;
-            for (int k = 32 * b; k < 32 * b + 32; ++k) acc += (int32_t)row[k] * (int32_t)q8[k];
-            S[(size_t)r * (cols / 32) + b] = acc;
-        }
+        for (int b = 0; b < cols / 32; ++b) S[(size_t)r * (cols / 32) + b] = block_dot_i8(row, q8, b);
     }
 }
 
@@ -258,14 +288,13 @@ void oracle_rowdot_i8(const int8_t *qw, const float *sw, const int8_t *q8, const
                       int rows, int cols, float *out)
 {
     const int nb = cols / 32;
-    int32_t *S = (int32_t *)malloc(sizeof(int32_t) * (size_t)nb);
+#pragma omp parallel for schedule(static)
     for (int r = 0; r < rows; ++r) {
-        oracle_block_dots_i8(qw + (size_t)r * cols, q8, 1, cols, S);
+        const int8_t *row = qw + (size_t)r * cols;
         double acc = 0.0;
-        for (int b = 0; b < nb; ++b) acc += (double)d8[b] * (double)S[b];
+        for (int b = 0; b < nb; ++b) acc += (double)d8[b] * (double)block_dot_i8(row, q8, b);
         out[r] = (float)((double)sw[r] * acc);
     }
-    free(S);
 }
 
 /* ------------------------------------------------------------------ O6 --- */
@@ -396,6 +425,27 @@ void oracle_expert(const uint8_t *gate_q, const float *gate_s, const uint8_t *up
 {
     oracle_expert_w(4, gate_q, gate_s, up_q, up_s, down_q, down_s, H, I, xq, xs, y,
                     g_out, u_out, h_out, hq_out, hs_out);
+}
+
+/* O7 for n tokens of one expert (the rows of xq/xs and of every output are
+ * the tokens): each token is oracle_expert_w on its own row; the OpenMP
+ * build spreads the tokens over threads. Outputs as oracle_expert_w, one row
+ * per token (y [n][H]; g, u, h [n][I]; hq [n][I]; hs [n][I/32]; any may be
+ * NULL except y). group > 0: int4 rows with O16 group scales (as
+ * oracle_expert_groups). */
+void oracle_expert_tokens(int wbits, int group, const void *gate_q, const float *gate_s, const void *up_q,
+                          const float *up_s, const void *down_q, const float *down_s, int H, int I, int n,
+                          const int8_t *xq, const float *xs, float *y,
+                          float *g_out, float *u_out, float *h_out, int8_t *hq_out, float *hs_out)
+{
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int t = 0; t < n; ++t) {
+        const size_t ti = (size_t)t * I;
+        expert_impl(wbits, group, gate_q, gate_s, up_q, up_s, down_q, down_s, H, I, xq + (size_t)t * H,
+                    xs + (size_t)t * (H / 32), y + (size_t)t * H, g_out ? g_out + ti : NULL,
+                    u_out ? u_out + ti : NULL, h_out ? h_out + ti : NULL, hq_out ? hq_out + ti : NULL,
+                    hs_out ? hs_out + (size_t)t * (I / 32) : NULL);
+    }
 }
 
 /* ------------------------------------------------------------------ O8 --- */

@@ -1,9 +1,11 @@
 /*
- * oracle.h — plain, slow, single-threaded CPU reference of one MoE layer's
+ * oracle.h — plain, slow CPU reference of one MoE layer's
  * routed-expert FFN with int4 experts and Q8_0-style int8 activations.
  *
  * TEST INFRASTRUCTURE ONLY. Only the tests, the smoke check and the CPU
- * baseline leg of the benchmark may load or call this library. The GPU
+ * baseline leg of the benchmark may load or call this library (either
+ * build: liboracle.so, or liboracle_omp.so with the independent row loops
+ * spread over OpenMP threads, bit for bit the same results). The GPU
  * library never calls it, includes it or shares code with it.
  *
  * Sources (the pages on the colibri engine):
@@ -162,6 +164,15 @@ void oracle_expert_groups(int group, const uint8_t *gate_q, const float *gate_s,
                           const int8_t *xq, const float *xs, float *y,
                           float *g_out, float *u_out, float *h_out, int8_t *hq_out, float *hs_out);
 
+/* O7 for n tokens of one expert: token t is oracle_expert_w (wbits, or
+ * oracle_expert_groups when group > 0) on row t of xq [n][H] / xs [n][H/32],
+ * its outputs in row t of y [n][H], g/u/h [n][I], hq [n][I], hs [n][I/32]
+ * (g..hs may be NULL). The OpenMP build takes the tokens in parallel. */
+void oracle_expert_tokens(int wbits, int group, const void *gate_q, const float *gate_s, const void *up_q,
+                          const float *up_s, const void *down_q, const float *down_s, int H, int I, int n,
+                          const int8_t *xq, const float *xs, float *y,
+                          float *g, float *u, float *h, int8_t *hq, float *hs);
+
 /* O8 [P1 s5, P3 impl] combine for one token: y = (float)(sum_j w_j*y_j + y_shared),
  * summed in double in j order, the shared expert (weight 1) last; y_shared may
  * be NULL (no shared expert). y_routed: [k][H]. */
@@ -183,6 +194,10 @@ void oracle_expert_dense(const uint8_t *gate_q, const float *gate_s, const uint8
 void oracle_expert_dense_i8(const int8_t *gate_q, const float *gate_s, const int8_t *up_q,
                             const float *up_s, const int8_t *down_q, const float *down_s, int H, int I,
                             const float *x, double *y);
+
+/* Threads the row loops use: the OpenMP build's thread count, 1 in the
+ * plain build. */
+int oracle_threads(void);
 
 /* A whole layer, every expert in host memory. Expert e's matrices start at
  * gate_q + e*I*H/2 (int4) or gate_q + e*I*H (int8), etc.; the shared expert

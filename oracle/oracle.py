@@ -14,13 +14,27 @@ from typing import Optional
 import numpy as np
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-_L = None
+_LIBS = {}
+_THREADED = False
+
+
+def use_threads(on: bool = True) -> None:
+    """Route every call through liboracle_omp.so (the same source with the
+    loops over independent matrix rows spread over OpenMP threads; bit for
+    bit the results of the plain build) or back to liboracle.so."""
+    global _THREADED
+    _THREADED = bool(on)
+
+
+def threads() -> int:
+    """Threads the selected build's row loops use (1 for the plain build)."""
+    return int(_lib().oracle_threads())
 
 
 def _lib():
-    global _L
-    if _L is None:
-        path = os.path.join(HERE, "liboracle.so")
+    name = "liboracle_omp.so" if _THREADED else "liboracle.so"
+    if name not in _LIBS:
+        path = os.path.join(HERE, name)
         if not os.path.exists(path):
             raise RuntimeError(f"{path} is not built; run __graft_entry__.build()")
         L = ctypes.CDLL(path)
@@ -56,8 +70,10 @@ def _lib():
         L.oracle_unpack_int4_groups.argtypes = [P, P, i, i, i, P]
         L.oracle_rowdot_groups.argtypes = [P, P, i, P, P, i, i, P]
         L.oracle_expert_groups.argtypes = [i, P, P, P, P, P, P, i, i, P, P, P, P, P, P, P, P]
-        _L = L
-    return _L
+        L.oracle_threads.restype = i
+        L.oracle_expert_tokens.argtypes = [i, i, P, P, P, P, P, P, i, i, i, P, P, P, P, P, P, P, P]
+        _LIBS[name] = L
+    return _LIBS[name]
 
 
 def _p(a: Optional[np.ndarray]):
@@ -280,6 +296,38 @@ def expert(gate_q, gate_s, up_q, up_s, down_q, down_s, xq, xs, group: int = 0, w
         _lib().oracle_expert_groups(group, *heads, *tail)
     else:
         _lib().oracle_expert_w(wb, *heads, *tail)
+    return o
+
+
+def expert_tokens(gate_q, gate_s, up_q, up_s, down_q, down_s, xq, xs, group: int = 0,
+                  wbits: int = 0) -> ExpertOut:
+    """O7 of one expert for n tokens: row t of every output is expert() on
+    row t of xq [n][H] / xs [n][H/32]. With the threaded build the tokens
+    run in parallel when there are enough of them, else each token's row
+    loops do; either way every token's arithmetic is expert()'s."""
+    wb = wbits or _wbits(gate_q)
+    if group and wb != 4:
+        raise ValueError("group scales are an int4 format")
+    dt = np.int8 if wb == 8 else np.uint8
+    gate_q = _c(gate_q, dt)
+    I, Hc = gate_q.shape
+    H = Hc * 8 // wb
+    xq = _c(np.atleast_2d(xq), np.int8)
+    xs = _c(np.atleast_2d(xs), np.float32)
+    n = xq.shape[0]
+    if xq.shape[1] != H or xs.shape != (n, H // 32):
+        raise ValueError("xq must be [n][H] and xs [n][H/32]")
+    o = ExpertOut(y=np.empty((n, H), np.float32), g=np.empty((n, I), np.float32), u=np.empty((n, I), np.float32),
+                  h=np.empty((n, I), np.float32), hq=np.empty((n, I), np.int8), hs=np.empty((n, I // 32), np.float32))
+    heads = [_c(gate_q, dt), _c(gate_s, np.float32), _c(up_q, dt), _c(up_s, np.float32), _c(down_q, dt),
+             _c(down_s, np.float32)]
+    if _THREADED and n < threads():
+        for t in range(n):
+            r = expert(*heads, xq[t], xs[t], group=group, wbits=wb)
+            o.y[t], o.g[t], o.u[t], o.h[t], o.hq[t], o.hs[t] = r.y, r.g, r.u, r.h, r.hq, r.hs
+        return o
+    _lib().oracle_expert_tokens(wb, group, *[_p(a) for a in heads], H, I, n, _p(xq), _p(xs), _p(o.y), _p(o.g),
+                                _p(o.u), _p(o.h), _p(o.hq), _p(o.hs))
     return o
 
 

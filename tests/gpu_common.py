@@ -50,3 +50,27 @@ def ws_views(layer, T, ws: torch.Tensor, flags=0):
 
 def dev(a: np.ndarray) -> torch.Tensor:
     return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+class DeviceGenExperts:
+    """The oracle's packed experts of one layer, from f32 weights the
+    generator's device twin writes (the same values as the host generator,
+    checked bit for bit by test_device_generator_matches_host), copied to
+    the host and packed by the oracle's own packer. expert_of(e) for
+    oracle.layers.forward_batch; the f32 generation on the GPU is what makes
+    a whole GLM-shaped layer affordable on the host."""
+
+    def __init__(self, spec, seed: int = 0, layer: int = 0):
+        self.spec, self.seed, self.layer = spec, seed, layer
+        self.buf = torch.empty(spec.H * spec.I, dtype=torch.float32, device="cuda")
+
+    def __call__(self, e: int):
+        from oracle import layers as OL
+        sp = self.spec
+        n = sp.H * sp.I
+        stream = torch.cuda.current_stream().cuda_stream
+        mats = []
+        for m, shape in ((S.GATE, (sp.I, sp.H)), (S.UP, (sp.I, sp.H)), (S.DOWN, (sp.H, sp.I))):
+            S.dev_expert_matrix(self.buf.data_ptr(), sp, self.seed, self.layer, e, m, hip_stream=stream)
+            mats.append(self.buf[:n].view(shape).cpu().numpy())
+        return OL.pack_matrices(sp, *mats)

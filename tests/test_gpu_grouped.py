@@ -10,7 +10,8 @@ from oracle import layers as OL
 from oracle import oracle as O
 from synth import synth as S
 
-from gpu_common import dev, rel_err, unreorder, ws_views
+import parity as PR
+from gpu_common import DeviceGenExperts, dev, rel_err, unreorder, ws_views
 
 pytestmark = pytest.mark.gpu
 TOL = 1e-4
@@ -31,6 +32,19 @@ def tiny():
     return device_layer(S.TINY, 0, 0), OL.full_layer(S.TINY, 0, 0)
 
 
+def _tiny_batch_check(spec, L, ref, x, ws, y, label):
+    """Every token and pair of a small batch against the oracle's whole batch."""
+    v = ws_views(L, x.shape[0], ws)
+    assert v["path"] == 1
+    cache = OL.ExpertCache(spec, 0, 0)
+    o = OL.forward_batch(spec, ref.router_w, ref.router_b, x, lambda e: cache[e])
+    y_o, _, _ = O.moe_forward(ref, x)
+    assert np.array_equal(o.y, y_o)              # the batch driver is the per-token oracle
+    st = PR.check_free_running(spec, PR.gpu_pairs(v, spec.has_shared, y), PR.batch_pairs(o),
+                               lambda e: cache[e], say)
+    say(f"  {label}: max rel {st['worst_y']:.2e}, bit-identical {st['y_bit_identical']:.4f}")
+
+
 @pytest.mark.parametrize("T", [9, 64, 200])
 def test_grouped_tiny_full_outputs(tiny, T):
     L, ref = tiny
@@ -38,20 +52,7 @@ def test_grouped_tiny_full_outputs(tiny, T):
     ws = api.workspace(L, T)
     say(f"grouped tiny T={T}")
     y = api.moe_forward(L, dev(x), ws).cpu().numpy()
-    assert ws_views(L, T, ws)["path"] == 1
-    y_o, idx_o, _ = O.moe_forward(ref, x)
-    err = rel_err(y, y_o).max()
-    say(f"  max rel {err:.2e}, bit-identical {np.mean(y == y_o):.4f}")
-    assert err <= TOL
-    # intermediates of every pair bit-exact
-    v = ws_views(L, T, ws)
-    cache = OL.ExpertCache(S.TINY, 0, 0)
-    for t in range(0, T, max(1, T // 7)):
-        r = OL.forward_token(S.TINY, cache, ref.router_w, ref.router_b, x[t])
-        pairs = list(v["pair_of"][t]) + [v["shared_pair"][t]]
-        for p, eo in zip(pairs, r.experts):
-            assert np.array_equal(unreorder(v["hq"][p]), eo.hq)
-            assert np.array_equal(v["hs"][p], eo.hs)
+    _tiny_batch_check(S.TINY, L, ref, x, ws, y, f"tiny T={T}")
 
 
 def test_grouped_hot_experts_full_tiles():
@@ -70,9 +71,7 @@ def test_grouped_hot_experts_full_tiles():
     v = ws_views(L, T, ws)
     assert v["path"] == 1
     assert np.array_equal(np.sort(v["idx"], axis=1), np.sort(idx_o, axis=1))
-    err = rel_err(y, y_o).max()
-    say(f"  max rel {err:.2e}, bit-identical {np.mean(y == y_o):.4f}")
-    assert err <= TOL
+    _tiny_batch_check(spec, L, ref, x, ws, y, f"hot experts T={T}")
 
 
 # H = 320: 10 blocks per gate/up row (a part-filled last stage of 8 blocks,
@@ -93,20 +92,7 @@ def test_grouped_odd_shape_full_outputs(odd, T):
     ws = api.workspace(L, T)
     say(f"grouped odd shape H={ODD.H} I={ODD.I} T={T}")
     y = api.moe_forward(L, dev(x), ws).cpu().numpy()
-    v = ws_views(L, T, ws)
-    assert v["path"] == 1
-    y_o, idx_o, _ = O.moe_forward(ref, x)
-    assert np.array_equal(v["idx"], idx_o)
-    err = rel_err(y, y_o).max()
-    say(f"  max rel {err:.2e}, bit-identical {np.mean(y == y_o):.4f}")
-    assert err <= TOL
-    cache = OL.ExpertCache(ODD, 0, 0)
-    for t in range(0, T, max(1, T // 5)):
-        r = OL.forward_token(ODD, cache, ref.router_w, ref.router_b, x[t])
-        pairs = list(v["pair_of"][t]) + [v["shared_pair"][t]]
-        for p, eo in zip(pairs, r.experts):
-            assert np.array_equal(unreorder(v["hq"][p]), eo.hq)
-            assert np.array_equal(v["hs"][p], eo.hs)
+    _tiny_batch_check(ODD, L, ref, x, ws, y, f"odd T={T}")
 
 
 @pytest.mark.parametrize("T", [1, 4, 8])
@@ -137,29 +123,54 @@ def glm_prefill():
     return wl, L, W, b
 
 
-def test_grouped_glm_prefill_T512(glm_prefill):
-    wl, L, W, b = glm_prefill
-    spec = wl.layer
+def _full_layer_check(wl, L, W, b, label):
+    """Every token and every (token, expert) pair of a GLM-shaped batch on
+    the grouped path against the oracle's whole batch (the threaded build,
+    bit for bit the plain one), free-running with flip accounting."""
+    spec, T = wl.layer, wl.tokens.T
     x = S.tokens(wl.tokens, spec.H, 0)
-    ws = api.workspace(L, 512)
-    xd = dev(x)
-    y = api.moe_forward(L, xd, ws).cpu().numpy()
-    v = ws_views(L, 512, ws)
-    idx_o, w_o = O.route(W, b, x, spec.top_k)
-    assert np.array_equal(v["idx"], idx_o)
-    load = np.bincount(idx_o.reshape(-1), minlength=spec.E)
-    say(f"prefill T=512: {int((load > 0).sum())} experts touched, top load {load.max()}, median {np.median(load[load > 0])}")
-    cache = OL.ExpertCache(spec, 0, 0)
-    hot = int(np.argmax(load))
-    sample = [0, 511] + [int(np.nonzero((idx_o == hot).any(axis=1))[0][0])]
-    for t in sample:
-        r = OL.forward_token(spec, cache, W, b, x[t])
-        err = rel_err(y[t][None], r.y[None]).max()
-        pairs = list(v["pair_of"][t]) + [v["shared_pair"][t]]
-        for p, eo in zip(pairs, r.experts):
-            assert np.array_equal(unreorder(v["hq"][p]), eo.hq)
-        say(f"  token {t}: max rel {err:.2e}, bit-identical {np.mean(y[t] == r.y):.4f}")
-        assert err <= TOL
+    ws = api.workspace(L, T)
+    say(f"{label}: GPU forward T={T}")
+    y = api.moe_forward(L, dev(x), ws).cpu().numpy()
+    v = ws_views(L, T, ws)
+    assert v["path"] == 1
+    experts = DeviceGenExperts(spec, 0, 0)
+    O.use_threads(True)
+    try:
+        say(f"{label}: oracle batch on {O.threads()} threads")
+        ref = OL.forward_batch(spec, W, b, x, experts, log=say)
+    finally:
+        O.use_threads(False)
+    load = np.bincount(ref.idx.reshape(-1), minlength=spec.E)
+    say(f"{label}: {int((load > 0).sum())} experts touched, top load {load.max()}, "
+        f"median {np.median(load[load > 0])}, {T * (spec.top_k + spec.has_shared)} pairs compared")
+    return PR.check_free_running(spec, PR.gpu_pairs(v, spec.has_shared, y), PR.batch_pairs(ref), experts, say), load
+
+
+@pytest.mark.timeout(900)
+def test_grouped_glm_prefill_T512(glm_prefill):
+    """All 512 tokens and all 4,608 pairs of the Zipf-routed prefill batch."""
+    wl, L, W, b = glm_prefill
+    st, load = _full_layer_check(wl, L, W, b, "prefill T=512")
+    assert (load > 0).sum() > 100                 # the skewed load spreads over most experts
+
+
+@pytest.fixture(scope="module")
+def glm_hot8():
+    wl = S.WORKLOADS["glm52_hot8_T512"]
+    say("building GLM-5.2-shaped layer with 8 hot experts on device")
+    L = device_layer(wl.layer, 0, 0)
+    W, b = S.router(wl.layer, 0, 0)
+    return wl, L, W, b
+
+
+@pytest.mark.timeout(900)
+def test_grouped_glm_hot8_T512(glm_hot8):
+    """Every token on the same 8 experts: 9 experts x 512 pairs in full
+    32-pair tiles at H = 6144, I = 2048 (the XCD-aware tile order runs)."""
+    wl, L, W, b = glm_hot8
+    st, load = _full_layer_check(wl, L, W, b, "hot8 T=512")
+    assert (load > 0).sum() == 8 and load.max() == 512
 
 
 def test_path_invariance_glm_T4(glm_prefill):

@@ -1,10 +1,14 @@
 """GPU parity of the HIP path against the CPU oracle, through the C ABI.
 
-Bar: bit-exact for integer/byte/index results (Q8 codes, int4 bytes, int32
-block dots, expert indices, hq codes); fp32 outputs within
-max_i |y_i - o_i| / max(|o_i|, rms(o)) <= 1e-4. The kernels sum block terms
-in f64 like the oracle, so most fp32 outputs come out bit-identical; the
-tests report how many.
+Bar: bit-exact for integer/byte/index results (Q8 codes of x, int4 bytes,
+int32 block dots, expert indices); fp32 outputs within
+max_i |y_i - o_i| / max(|o_i|, rms(o)) <= 1e-4. Whole layers run free: the
+GPU and the oracle each quantise their own h, so a Q8(h) code may move by
+one where h * (1/d) sits on a rounding boundary; every such move is logged
+and accounted for (tests/parity.py). The teacher-forced stage test feeds the
+oracle the GPU's own Q8(x) and Q8(h) and holds every code bit for bit. The
+kernels sum block terms in f64 like the oracle, so most fp32 outputs come out
+bit-identical; the tests report how many.
 """
 import numpy as np
 import pytest
@@ -16,6 +20,7 @@ from oracle import layers as OL
 from oracle import oracle as O
 from synth import synth as S
 
+import parity as PR
 from gpu_common import dev, rel_err, unreorder, ws_views
 
 pytestmark = pytest.mark.gpu
@@ -150,23 +155,13 @@ def test_route_group_limited_and_scale(tiny_layer):
 
 
 # ------------------------------------------------------------ whole layer
-def _check_pairs(L, T, ws, tok_results, flags=0):
-    """Intermediates per (token, slot) pair against the oracle's: h and hq
-    bit-exact, per-expert outputs within tolerance."""
-    v = ws_views(L, T, ws, flags)
-    n_h_exact = n_h = 0
-    worst = 0.0
-    for t, r in enumerate(tok_results):
-        pairs = list(v["pair_of"][t]) + ([v["shared_pair"][t]] if L.has_shared else [])
-        for p, eo in zip(pairs, r.experts):
-            hq = unreorder(v["hq"][p])
-            assert np.array_equal(hq, eo.hq), f"hq differs token {t} pair {p}"
-            assert np.array_equal(v["hs"][p], eo.hs)
-            n_h_exact += int(np.sum(v["h"][p] == eo.h))
-            n_h += eo.h.size
-            worst = max(worst, float(rel_err(v["ye"][p][None], eo.y[None]).max()))
-    assert worst <= TOL, worst
-    return n_h_exact / max(n_h, 1)
+def _check_pairs(spec, L, T, ws, y, tok_results, cache, flags=0):
+    """Free-running against the oracle's tokens (tests/parity.py): routing
+    bit for bit, every moved Q8(h) code shown to sit on a rounding boundary
+    and to account for the outputs it moves, everything else within the bar.
+    Returns the fraction of h values bit-identical to the oracle's."""
+    st = PR.check_tokens(spec, L, T, ws, y, tok_results, lambda e: cache[e], say, flags=flags)
+    return st["h_bit_identical"]
 
 
 @pytest.mark.parametrize("T", [1, 3, 5, 8])
@@ -179,7 +174,7 @@ def test_forward_tiny(tiny_layer, T):
     y_o, idx_o, w_o = O.moe_forward(ref, x)
     cache = OL.ExpertCache(S.TINY, 0, 0)
     toks = [OL.forward_token(S.TINY, cache, ref.router_w, ref.router_b, x[t]) for t in range(T)]
-    frac = _check_pairs(L, T, ws, toks)
+    frac = _check_pairs(S.TINY, L, T, ws, y, toks, cache)
     err = rel_err(y, y_o).max()
     say(f"  max rel {err:.2e}, outputs bit-identical {np.mean(y == y_o):.4f}, h bit-identical {frac:.4f}")
     assert err <= TOL
@@ -210,7 +205,7 @@ def test_forward_glm_decode_T1(glm_layer):
     say("forward GLM decode T=1")
     y = api.moe_forward(L, dev(x), ws).cpu().numpy()
     toks = _glm_oracle_tokens(cache, W, b, x)
-    frac = _check_pairs(L, 1, ws, toks)
+    frac = _check_pairs(S.GLM52, L, 1, ws, y, toks, cache)
     y_o = np.stack([t.y for t in toks])
     err = rel_err(y, y_o).max()
     say(f"  experts {toks[0].idx.tolist()} max rel {err:.2e} bit-identical {np.mean(y == y_o):.4f} h {frac:.4f}")
@@ -226,7 +221,7 @@ def test_forward_glm_mtp_verify_T4_and_batch_invariance(glm_layer):
     y = api.moe_forward(L, dev(x), ws).cpu().numpy()
     toks = _glm_oracle_tokens(cache, W, b, x)
     union = len({int(e) for t in toks for e in t.idx})
-    frac = _check_pairs(L, 4, ws, toks)
+    frac = _check_pairs(S.GLM52, L, 4, ws, y, toks, cache)
     y_o = np.stack([t.y for t in toks])
     err = rel_err(y, y_o).max()
     say(f"  union {union} of 32 picks, max rel {err:.2e}, bit-identical {np.mean(y == y_o):.4f}, h {frac:.4f}")
@@ -246,12 +241,22 @@ def test_experts_teacher_forced_glm(glm_layer):
     idx_o, w_o = O.route(W, b, x, 8)
     ws = api.workspace(L, 2)
     y = api.moe_experts(L, xq, xs, dev(idx_o), dev(w_o), ws).cpu().numpy()
+    v = ws_views(L, 2, ws)
     xq_h, xs_h = xq.cpu().numpy(), xs.cpu().numpy()
     for t in range(2):
         outs = [O.expert(*cache[int(e)].args(), xq_h[t], xs_h[t]) for e in idx_o[t]]
         sh = O.expert(*cache[S.GLM52.E].args(), xq_h[t], xs_h[t])
         y_o = O.combine(np.stack([o.y for o in outs]), w_o[t], sh.y)
         assert rel_err(y[t][None], y_o[None]).max() <= TOL
+        # the gate/up stage from the same Q8(x): h and its Q8 codes bit for
+        # bit; the down stage fed the GPU's own Q8(h): outputs bit for bit
+        pairs = list(v["pair_of"][t]) + [v["shared_pair"][t]]
+        experts = list(idx_o[t]) + [S.GLM52.E]
+        for p, e, eo in zip(pairs, experts, outs + [sh]):
+            assert np.array_equal(v["h"][p], eo.h) and np.array_equal(unreorder(v["hq"][p]), eo.hq)
+            assert np.array_equal(v["hs"][p], eo.hs)
+            ye_o = PR.down_rowdot(S.GLM52, cache[int(e)], unreorder(v["hq"][p]), v["hs"][p])
+            assert np.array_equal(v["ye"][p], ye_o), f"token {t} expert {e}: down stage differs"
 
 
 def test_rmsnorm_and_two_layer_chain(glm_layer):

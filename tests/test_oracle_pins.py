@@ -43,6 +43,18 @@ def test_pack_exact_codes_even_index_in_low_nibble():
     assert np.array_equal(O.unpack_int4_rows(q, s), codes.astype(np.float64))
 
 
+def test_pack_int4_rounds_half_to_even():
+    # amax = 7 gives d = 1 exactly, so w * (1/d) == w: every k.5 is a tie,
+    # and round-half-to-even gives the even neighbour (half away from zero
+    # would give 1, 2, 3, 4, 5, 6, 7)
+    ties = np.array([0.5, 1.5, 2.5, 3.5, 4.5, 5.5, 6.5], np.float32)
+    w = np.concatenate([ties, -ties, [7.0, 0.0]]).astype(np.float32).reshape(1, -1)
+    q, s = O.pack_int4_rows(w)
+    assert s[0] == 1.0
+    codes = O.unpack_int4_rows(q, s)[0]
+    assert codes.tolist() == [0, 2, 2, 4, 4, 6, 6, 0, -2, -2, -4, -4, -6, -6, 7, 0]
+
+
 # ------------------------------------------------------------- P2 invariants
 @pytest.mark.parametrize("cols", [32, 256, 6144])
 def test_int4_invariants(cols):
@@ -229,6 +241,30 @@ def test_expert_idot_close_to_dense_reference():
     hq, hs = O.quant_q8(o.h)
     assert np.array_equal(hq, o.hq) and np.array_equal(hs, o.hs)
     assert np.array_equal(o.y, O.rowdot(ex.down_q, ex.down_s, o.hq, o.hs))
+
+
+def test_expert_dense_exact_case_is_f64_matmul():
+    """O10 with exactly representable weights (codes * 2^-6) and integer
+    activations: g and u are exact, so they equal the integer matmul; h and
+    y then follow the f64 formula, which a numpy matmul reproduces to
+    rounding (a transposed operand, a dropped term or a wrong sign would be
+    off by far more)."""
+    codes_g, wg, xi, x = _exact_case(32, 64, 16)
+    codes_u, wu, _, _ = _exact_case(32, 64, 17)
+    codes_d, wd, _, _ = _exact_case(64, 32, 18)
+    gq, gs = O.pack_int4_rows(wg)
+    uq, us = O.pack_int4_rows(wu)
+    dq, ds = O.pack_int4_rows(wd)
+    y = O.expert_dense(gq, gs, uq, us, dq, ds, x)
+    g = (codes_g.astype(np.int64) @ xi.astype(np.int64)) * 2.0 ** -6       # exact
+    u = (codes_u.astype(np.int64) @ xi.astype(np.int64)) * 2.0 ** -6
+    h = g / (1.0 + np.exp(-g)) * u
+    y_ref = (codes_d.astype(np.float64) * 2.0 ** -6) @ h
+    assert np.allclose(y, y_ref, rtol=1e-12, atol=1e-12 * np.abs(y_ref).max())
+    # the same weights with x quantised losslessly (d_b = 1): O7's g and u are O10's
+    xq, xs = O.quant_q8(x)
+    o = O.expert(gq, gs, uq, us, dq, ds, xq, xs)
+    assert np.array_equal(o.g.astype(np.float64), g) and np.array_equal(o.u.astype(np.float64), u)
 
 
 def test_expert_swiglu_exact_case():
