@@ -96,28 +96,61 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def host_cpu():
+    """The host's CPU model and logical core count."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return model, os.cpu_count()
+
+
 def cpu_baseline(spec, tokens_np, n_tokens=3, reps=3):
-    """The oracle (single thread, as it stands) on a bounded sample: n_tokens
-    tokens through layer instance 0, each timed reps times (median)."""
+    """The oracle as it stands on a bounded sample, in both builds: n_tokens
+    tokens through layer instance 0, each timed reps times (median), first on
+    one thread (liboracle.so), then with its row loops on every host core
+    (liboracle_omp.so, the same arithmetic). The threaded figure is the
+    headline value; both are reported."""
     import numpy as np
     from oracle import layers as OL
+    from oracle import oracle as O
     from synth import synth as S
 
     W, b = S.router(spec, 0, 0)
     cache = OL.ExpertCache(spec, 0, 0)
-    times = []
     for t in range(n_tokens):
         OL.forward_token(spec, cache, W, b, tokens_np[t])          # regenerate experts (untimed)
-        per = []
-        for _ in range(reps):
-            t0 = time.perf_counter()
-            OL.forward_token(spec, cache, W, b, tokens_np[t])
-            per.append(time.perf_counter() - t0)
-        times.append(sorted(per)[len(per) // 2])
-    sec_per_token = float(np.mean(times))
-    return {"value": 1.0 / sec_per_token, "unit": "tokens*layers/s", "cores": 1, "kind": "oracle",
-            "sample": f"{n_tokens} tokens through one layer of this shape, median of {reps} runs each "
-                      f"({sec_per_token:.2f} s/token, single-threaded C oracle, -O2)"}
+
+    def leg(threaded):
+        O.use_threads(threaded)
+        try:
+            times = []
+            for t in range(n_tokens):
+                per = []
+                for _ in range(reps):
+                    t0 = time.perf_counter()
+                    OL.forward_token(spec, cache, W, b, tokens_np[t])
+                    per.append(time.perf_counter() - t0)
+                times.append(sorted(per)[len(per) // 2])
+            return float(np.mean(times)), O.threads()
+        finally:
+            O.use_threads(False)
+
+    s1, _ = leg(False)
+    sN, nthr = leg(True)
+    model, nproc = host_cpu()
+    sample = (f"{n_tokens} tokens through one layer of this shape, median of {reps} runs each; "
+              f"C oracle, -O2; expert generation and packing untimed")
+    return {"value": 1.0 / sN, "unit": "tokens*layers/s", "cores": nthr, "kind": "oracle",
+            "sample": sample + f"; OpenMP build, {nthr} threads ({sN:.3f} s/token)",
+            "single_thread": {"value": 1.0 / s1, "unit": "tokens*layers/s", "cores": 1,
+                              "sample": sample + f"; plain build, one thread ({s1:.3f} s/token)"},
+            "nproc": nproc, "cpu_model": model}
 
 
 def main():
@@ -204,19 +237,31 @@ def main():
     down_bytes = [(u + spec.has_shared) * dn_row for u in union]
     calls_per_step = n_inst if chain else 1
 
-    # ---------------- timed region: K steps
-    if chain:
-        K, W = max(1, args.steps // n_inst), max(1, args.warmup // n_inst)
-    else:
-        K = max(G, (args.steps + G - 1) // G * G)
-        W = max(G, (args.warmup + G - 1) // G * G)
+    # ---------------- timed region: exactly K steps after exactly W
+    K, W = max(1, args.steps), max(0, args.warmup)
     use_graph = not args.no_graph
     if use_graph:
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g, stream=stream):
-            for i in range(G):
-                step(i, torch.cuda.current_stream())
-        run = lambda n: [g.replay() for _ in range(n // G)]
+        # one graph of G steps (one per layer instance), replayed; a count
+        # that is not a multiple of G ends with a graph of its first steps
+        graphs = {}
+
+        def graph_of(n):
+            if n not in graphs:
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=stream):
+                    for i in range(n):
+                        step(i, torch.cuda.current_stream())
+                graphs[n] = g
+            return graphs[n]
+
+        for n in {G, K % G, W % G} - {0}:
+            graph_of(n)
+
+        def run(n):
+            for _ in range(n // G):
+                graphs[G].replay()
+            if n % G:
+                graphs[n % G].replay()
     else:
         def run(n):
             for i in range(n):
@@ -361,21 +406,28 @@ def bench_dense(args):
         j = i % G
         api.dense_forward(mlps[j], x_all[j], wss[j], y=y_all[j], stream=s, c_mlp=cms[j])
 
-    K = max(G, (args.steps + G - 1) // G * G)
-    W = max(G, (args.warmup + G - 1) // G * G)
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g, stream=stream):
-        for i in range(G):
-            step(i, torch.cuda.current_stream())
+    K, W = max(1, args.steps), max(0, args.warmup)
+    graphs = {}
+    for n in {G, K % G, W % G} - {0}:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for i in range(n):
+                step(i, torch.cuda.current_stream())
+        graphs[n] = g
+
+    def run(n):                                   # exactly n steps
+        for _ in range(n // G):
+            graphs[G].replay()
+        if n % G:
+            graphs[n % G].replay()
+
     with torch.cuda.stream(stream):
-        for _ in range(W // G):
-            g.replay()
+        run(W)
     torch.cuda.synchronize()
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     with torch.cuda.stream(stream):
         ev0.record(stream)
-        for _ in range(K // G):
-            g.replay()
+        run(K)
         ev1.record(stream)
     torch.cuda.synchronize()
     ms_total = ev0.elapsed_time(ev1)
@@ -422,15 +474,29 @@ def bench_dense(args):
         for m in (S.GATE, S.UP, S.DOWN):
             w.extend(pack(S.dense_matrix(spec, wl.seed, 0, m)))
         x = np.asarray(toks).reshape(-1, spec.H)[:3]
-        times = []
-        for t in range(3):
-            t0 = time.perf_counter()
-            O.dense_forward(*w, x[t:t + 1])
-            times.append(time.perf_counter() - t0)
-        sec = float(np.median(times))
-        cpu = {"value": 1.0 / sec, "unit": "tokens*layers/s", "cores": 1, "kind": "oracle",
-               "sample": f"3 tokens through one dense MLP of this shape, median ({sec:.2f} s/token, "
-                         f"single-threaded C oracle, -O2; weight generation and packing untimed)"}
+
+        def leg(threaded):
+            O.use_threads(threaded)
+            try:
+                times = []
+                for t in range(3):
+                    t0 = time.perf_counter()
+                    O.dense_forward(*w, x[t:t + 1])
+                    times.append(time.perf_counter() - t0)
+                return float(np.median(times)), O.threads()
+            finally:
+                O.use_threads(False)
+
+        s1, _ = leg(False)
+        sN, nthr = leg(True)
+        model, nproc = host_cpu()
+        sample = ("3 tokens through one dense MLP of this shape, median; C oracle, -O2; "
+                  "weight generation and packing untimed")
+        cpu = {"value": 1.0 / sN, "unit": "tokens*layers/s", "cores": nthr, "kind": "oracle",
+               "sample": sample + f"; OpenMP build, {nthr} threads ({sN:.3f} s/token)",
+               "single_thread": {"value": 1.0 / s1, "unit": "tokens*layers/s", "cores": 1,
+                                 "sample": sample + f"; plain build, one thread ({s1:.3f} s/token)"},
+               "nproc": nproc, "cpu_model": model}
     out = {
         "metric": f"dense-MLP tokens*layers/s (GLM-5.2-shaped first-layer MLP, int{wb} weights, "
                   f"{'decode' if T <= 8 else 'prefill chunk'})",
