@@ -15,9 +15,10 @@ LIB_PATH = os.path.join(HERE, "libcoli_moe.so")
 COLI_OK, COLI_EINVAL, COLI_EWORKSPACE, COLI_EDEVICE, COLI_EUNSUPPORTED = 0, -1, -2, -3, -4
 COLI_ACCUMULATE, COLI_PATH_GEMV, COLI_PATH_GROUPED, COLI_PATH_FUSED = 1, 2, 4, 8
 COLI_GEMV_MAX_T, COLI_MAX_T, COLI_MAX_TOPK, COLI_PROFILE_EVENTS = 8, 65536, 16, 6
+COLI_NOALLOC_MAX_BYTES = 32 << 20
 
 EXPORTS = ("coli_quant_act_q8", "coli_moe_workspace_bytes", "coli_moe_workspace_init",
-           "coli_moe_route", "coli_moe_forward", "coli_moe_forward_profiled", "coli_moe_forward_timed", "coli_moe_forward_rms",
+           "coli_moe_route", "coli_moe_forward", "coli_moe_forward_noalloc", "coli_moe_forward_profiled", "coli_moe_forward_timed", "coli_moe_forward_rms",
            "coli_dense_workspace_bytes", "coli_dense_forward", "coli_timer_begin", "coli_timer_end", "coli_moe_experts", "coli_moe_workspace_layout",
            "coli_rmsnorm", "coli_pack_int4_rows", "coli_pack_int4_rows_dev", "coli_pack_int4_groups_dev", "coli_pack_int2_rows_dev", "coli_pack_int8_rows",
            "coli_pack_int8_rows_dev", "coli_debug_block_dots", "coli_version")
@@ -73,6 +74,7 @@ def lib():
             "coli_moe_workspace_init": ([P, sz, P], i),
             "coli_moe_route": ([LP, P, i, P, P, P, sz, P], i),
             "coli_moe_forward": ([LP, P, i, P, i, P, sz, P], i),
+            "coli_moe_forward_noalloc": ([LP, P, i, P, i, P], i),
             "coli_moe_forward_profiled": ([LP, P, i, P, i, P, sz, P, ctypes.POINTER(P), i], i),
             "coli_moe_forward_rms": ([LP, P, P, f, i, P, i, P, sz, P], i),
             "coli_dense_workspace_bytes": ([ctypes.POINTER(CDense), i], sz),

@@ -210,6 +210,17 @@ def moe_forward(layer: MoELayer, x: torch.Tensor, ws: torch.Tensor, y: Optional[
     return y
 
 
+def moe_forward_noalloc(layer: MoELayer, x: torch.Tensor, y: torch.Tensor, flags: int = 0, stream=None,
+                        c_layer: Optional[CLayer] = None) -> torch.Tensor:
+    """coli_moe_forward on the library's own device scratch (no workspace, no
+    allocation: the caller passes the output y)."""
+    _dev(x, torch.float32, "x"); _dev(y, torch.float32, "y")
+    cl = c_layer if c_layer is not None else layer.c()
+    check("coli_moe_forward_noalloc", lib().coli_moe_forward_noalloc(ctypes.byref(cl), _ptr(x), x.shape[0], _ptr(y),
+                                                                     flags, _stream(stream)))
+    return y
+
+
 def moe_forward_rms(layer: MoELayer, x: torch.Tensor, gamma: torch.Tensor, eps: float, ws: torch.Tensor,
                     y: Optional[torch.Tensor] = None, flags: int = 0, stream=None,
                     c_layer: Optional[CLayer] = None) -> torch.Tensor:

@@ -6,6 +6,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 
 #include "internal.hpp"
 
@@ -334,6 +335,65 @@ int coli_moe_forward_rms(const coli_moe_layer *L, const float *x, const float *g
 {
     if (!gamma) return COLI_EINVAL;
     return forward_impl(L, x, T, y, flags, ws, ws_bytes, stream, nullptr, gamma, eps);
+}
+
+// ---- coli_moe_forward_noalloc: the library's own device scratch in place
+// of a caller workspace, for callers that cannot allocate. One copy of the
+// array per GPU, alive until the process ends. Host code never passes the
+// array's name to a kernel (on the host it is only a stand-in for the
+// symbol): it uses the device address hipGetSymbolAddress returns, taken
+// once per device with that device current.
+static __device__ __align__(256) unsigned char scratch[COLI_NOALLOC_MAX_BYTES];
+
+namespace {
+constexpr int SCRATCH_MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[SCRATCH_MAX_DEVICES];     // device address of `scratch` on each device
+bool g_scratch_zeroed[SCRATCH_MAX_DEVICES];   // zero-filled, and no call failed since
+
+// The current device's scratch address (taken on its first call), or null
+// when the runtime cannot give it.
+void *scratch_of_current_device(int &dev)
+{
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= SCRATCH_MAX_DEVICES) return nullptr;
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+        g_scratch_ptr[dev] = p;
+        g_scratch_zeroed[dev] = false;
+    }
+    return g_scratch_ptr[dev];
+}
+} // namespace
+
+int coli_moe_forward_noalloc(const coli_moe_layer *L, const float *x, int T, float *y, int flags, void *stream)
+{
+    int path;
+    WsLayout lay;
+    int dev = -1;
+    // the size check needs no device: a call past the limit is refused first
+    int rc = check_common(L, T, flags, reinterpret_cast<void *>(ALIGN), COLI_NOALLOC_MAX_BYTES, path, lay);
+    if (rc != COLI_OK) return rc;
+    void *ws = scratch_of_current_device(dev);
+    if (!ws) return COLI_EDEVICE;
+    hipStream_t s = (hipStream_t)stream;
+    bool zeroed;
+    {
+        std::lock_guard<std::mutex> lk(g_scratch_mu);
+        zeroed = g_scratch_zeroed[dev];
+    }
+    // the workspace contract: zero-filled before the first use and after a
+    // failed call (a fill kernel, not a memset)
+    if (!zeroed) {
+        if (launch_zero(ws, COLI_NOALLOC_MAX_BYTES, s) != hipSuccess) return COLI_EDEVICE;
+    }
+    rc = forward_impl(L, x, T, y, flags, ws, COLI_NOALLOC_MAX_BYTES, stream, nullptr);
+    {
+        std::lock_guard<std::mutex> lk(g_scratch_mu);
+        g_scratch_zeroed[dev] = rc == COLI_OK || (rc != COLI_EDEVICE && zeroed);
+    }
+    return rc;
 }
 
 int coli_timer_begin(void *const *start, void *const *stop, int n_pairs, const char **names)
