@@ -13,7 +13,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libcoli_moe.so")
 
 COLI_OK, COLI_EINVAL, COLI_EWORKSPACE, COLI_EDEVICE, COLI_EUNSUPPORTED = 0, -1, -2, -3, -4
-COLI_ACCUMULATE, COLI_PATH_GEMV, COLI_PATH_GROUPED, COLI_PATH_FUSED = 1, 2, 4, 8
+COLI_ACCUMULATE, COLI_PATH_GEMV, COLI_PATH_GROUPED = 1, 2, 4
 COLI_GEMV_MAX_T, COLI_MAX_T, COLI_MAX_TOPK, COLI_PROFILE_EVENTS = 8, 65536, 16, 6
 COLI_NOALLOC_MAX_BYTES = 32 << 20
 
@@ -53,7 +53,7 @@ class CDense(ctypes.Structure):
 class CWsLayout(ctypes.Structure):
     """Mirror of struct coli_moe_ws_layout."""
     _fields_ = [(n, ctypes.c_size_t) for n in ("xq", "xs", "idx", "w", "pair_of", "shared_pair", "h", "hq",
-                                                "hs", "ye", "n_pairs_max", "sync")] + [("path", ctypes.c_int32)]
+                                                "hs", "ye", "n_pairs_max")] + [("path", ctypes.c_int32)]
 
 
 _lib = None

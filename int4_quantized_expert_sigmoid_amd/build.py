@@ -8,7 +8,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libcoli_moe.so")
 SOURCES = ["abi.cpp", "kernels_quant.hip", "kernels_route.hip", "kernels_gemv.hip", "kernels_grouped.hip",
-           "kernels_combine.hip", "kernels_fused.hip",
+           "kernels_combine.hip",
            "kernels_decode.hip", "kernels_dense.hip"]
 # The grouped MFMA kernels read every MFMA result with VALU instructions; in
 # VGPR form the accumulator copies (one per result) disappear.

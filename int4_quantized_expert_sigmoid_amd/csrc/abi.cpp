@@ -66,7 +66,7 @@ bool dense_ok(const coli_dense_mlp *M)
     return true;
 }
 
-constexpr int KNOWN_FLAGS = COLI_ACCUMULATE | COLI_PATH_GEMV | COLI_PATH_GROUPED | COLI_PATH_FUSED;
+constexpr int KNOWN_FLAGS = COLI_ACCUMULATE | COLI_PATH_GEMV | COLI_PATH_GROUPED;
 
 int choose_path(const coli_moe_layer &L, int T, int flags)
 {
@@ -78,10 +78,10 @@ int choose_path(const coli_moe_layer &L, int T, int flags)
 int status(hipError_t e) { return e == hipSuccess ? COLI_OK : COLI_EDEVICE; }
 
 // int8 and int2 experts and group scales run on the token-GEMV path only
-// (not grouped, not fused).
-int format_ok(const coli_moe_layer &L, int path, int flags)
+// (not grouped).
+int format_ok(const coli_moe_layer &L, int path)
 {
-    if ((L.weight_bits == 8 || L.weight_bits == 2 || L.group_size != 0) && (path != 0 || (flags & COLI_PATH_FUSED)))
+    if ((L.weight_bits == 8 || L.weight_bits == 2 || L.group_size != 0) && path != 0)
         return COLI_EUNSUPPORTED;
     return COLI_OK;
 }
@@ -126,7 +126,6 @@ WsLayout make_layout(const coli_moe_layer &L, int T, int path)
     o.hs = p; p = up(p + n_pairs * (I / 32) * 4);
     o.ye = p; p = up(p + n_pairs * H * 4);
     o.xn = p; p = up(p + t * H * 4);
-    o.sync = p; p = up(p + (path == 0 ? sizeof(FusedSync) : 0));
     o.total = p;
     return o;
 }
@@ -197,7 +196,6 @@ int coli_moe_workspace_layout(const coli_moe_layer *L, int T, int flags, coli_mo
     out->pair_of = l.pair_of; out->shared_pair = l.shared_pair;
     out->h = l.h; out->hq = l.hq; out->hs = l.hs; out->ye = l.ye;
     out->n_pairs_max = (size_t)l.n_pairs;
-    out->sync = l.sync;
     out->path = path;
     return COLI_OK;
 }
@@ -211,7 +209,6 @@ static int check_common(const coli_moe_layer *L, int T, int flags, void *ws, siz
     if ((flags & COLI_PATH_GEMV) && (T > COLI_GEMV_MAX_T || !gemv_shape_ok(*L))) return COLI_EINVAL;
     if (!al16(ws)) return COLI_EINVAL;
     path = choose_path(*L, T, flags);
-    if ((flags & COLI_PATH_FUSED) && path != 0) return COLI_EINVAL;
     lay = make_layout(*L, T, path);
     if (ws_bytes < lay.total) return COLI_EWORKSPACE;
     return COLI_OK;
@@ -257,24 +254,17 @@ static int forward_impl(const coli_moe_layer *L, const float *x, int T, float *y
     WsLayout lay;
     int rc = check_common(L, T, flags, ws, ws_bytes, path, lay);
     if (rc != COLI_OK) return rc;
-    if ((rc = format_ok(*L, path, flags)) != COLI_OK) return rc;
+    if ((rc = format_ok(*L, path)) != COLI_OK) return rc;
     if (!al16(x) || !al16(y)) return COLI_EINVAL;
     if (gamma && (!al16(gamma) || !(eps >= 0.0f) || !std::isfinite(eps))) return COLI_EINVAL;
     hipStream_t s = (hipStream_t)stream;
     char *base = static_cast<char *>(ws);
     if (record(ev, 0, s)) return COLI_EDEVICE;
-    const bool norm_in_router = gamma && path == 0 && !(flags & COLI_PATH_FUSED);
+    const bool norm_in_router = gamma && path == 0;
     if (gamma && !norm_in_router) {
         float *xn = reinterpret_cast<float *>(base + lay.xn);
         if (launch_rmsnorm(x, gamma, T, L->H, eps, xn, s) != hipSuccess) return COLI_EDEVICE;
         x = xn;
-    }
-    if (path == 0 && (flags & COLI_PATH_FUSED)) {
-        if (launch_decode_fused(*L, x, T, lay, base, y, (flags & COLI_ACCUMULATE) != 0, s) != hipSuccess)
-            return COLI_EDEVICE;
-        for (int i = 1; i < COLI_PROFILE_EVENTS; ++i)
-            if (record(ev, i, s)) return COLI_EDEVICE;
-        return COLI_OK;
     }
     if (path == 0) {
         // router (+ the shared expert's gate/up), routed gate/up, down + combine
@@ -509,7 +499,7 @@ int coli_moe_experts(const coli_moe_layer *L, const int8_t *xq, const float *xs,
     WsLayout lay;
     int rc = check_common(L, T, flags, ws, ws_bytes, path, lay);
     if (rc != COLI_OK) return rc;
-    if ((rc = format_ok(*L, path, flags)) != COLI_OK) return rc;
+    if ((rc = format_ok(*L, path)) != COLI_OK) return rc;
     if (!al16(xq) || !al4(xs) || !al4(idx) || !al4(w) || !al16(y)) return COLI_EINVAL;
     hipStream_t s = (hipStream_t)stream;
     char *base = static_cast<char *>(ws);

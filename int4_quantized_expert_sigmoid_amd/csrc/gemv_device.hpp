@@ -1,5 +1,5 @@
 // gemv_device.hpp — device bodies of the token-GEMV expert path (T <= 8),
-// shared by the standalone GEMV kernels and the fused decode kernel.
+// shared by the standalone GEMV kernels, the decode launches and the dense MLP.
 //
 // What is computed (colibri architecture overview, sections 3.1 and 5; the
 // IDOT path dot_i4i8): for every item (a distinct expert of the batch, read
@@ -28,7 +28,6 @@ struct GemvArgs {
     int has_shared;                // item 0 is the shared expert (expert E, slot t = token t)
     int gsh;                       // group scales: log2(group / 32) (kernels instantiated with GS)
     int item0;                     // first item of a launch that covers items item0.. only
-    const float *x;                // [T][H] layer input (coherent mode quantises it on the fly)
     const int8_t *xq;              // [T][H] reordered Q8(x)
     const float *xs;               // [T][H/32]
     const int *ctrl, *item_expert, *item_ntok, *item_tok;
@@ -43,26 +42,8 @@ struct ItemDesc {
     int tok[MAX_SLOTS];
 };
 
-// A value another workgroup of the same launch may have written.
-__device__ __forceinline__ int ld_shared_int(const int *p) { return ld_dev(p); }
-
-// The item's expert and token slots from the union lists.
-__device__ __forceinline__ ItemDesc item_from_union(const GemvArgs &a, int item)
-{
-    ItemDesc d;
-    d.item = item;
-    // all loads issued together (one round trip); slots past nt are unused
-    d.e = ld_shared_int(a.item_expert + item);
-    d.nt = ld_shared_int(a.item_ntok + item);
-#pragma unroll
-    for (int s = 0; s < MAX_SLOTS; ++s) d.tok[s] = ld_shared_int(a.item_tok + item * MAX_SLOTS + s);
-#pragma unroll
-    for (int s = 0; s < MAX_SLOTS; ++s) d.tok[s] = s < d.nt ? d.tok[s] : 0;
-    return d;
-}
-
-// The same from tables an earlier launch wrote: plain loads, which the
-// launch boundary makes coherent (no device-scope loads from every thread).
+// An item's expert and token slots from the union tables an earlier launch
+// wrote: plain loads, which the launch boundary makes coherent.
 __device__ __forceinline__ ItemDesc item_from_table(const GemvArgs &a, int item)
 {
     ItemDesc d;
@@ -98,11 +79,9 @@ struct GateUpShared {
 // workgroup must call it (blockDim >= 64 * ceil(H/32/64) * RS; waves past
 // that idle until the epilogue). RS > 1 splits the 32 rows into RS sets of
 // waves, each streaming 32/RS rows, so fewer loads queue behind each other.
-// ONFLY: Q8(x) is computed here from x instead of read from xq. COHERENT
-// (single-launch path): hq/hs are handed on with device-coherent stores.
 // GS: int4 rows with one scale per group of 32 << gsh columns; each block's
 // term is (S_b * d_b) * s_group, so no row scale is applied at the end.
-template <int NT, int RC, bool ONFLY, bool COHERENT, int RS = 1, int WB = 4, bool GS = false>
+template <int NT, int RC, int RS = 1, int WB = 4, bool GS = false>
 __device__ __forceinline__ void gateup_rows(const GemvArgs &a, const ItemDesc &it, int rb, GateUpShared<NT> &sh)
 {
     static_assert(!GS || WB == 4, "group scales are an int4 format");
@@ -132,17 +111,8 @@ __device__ __forceinline__ void gateup_rows(const GemvArgs &a, const ItemDesc &i
         for (int s = 0; s < NT; ++s) {
             if (s < it.nt && active) {
                 const int t = it.tok[s];
-                if constexpr (ONFLY) {
-                    uint32_t o[8];
-                    float d;
-                    q8_block_regs(a.x + (long)t * a.H + col * QK, o, d);
-#pragma unroll
-                    for (int k = 0; k < 8; ++k) act[s].v[k] = (int)o[k];
-                    dsc[s] = (double)d * KS;
-                } else {
-                    act[s] = load_blk8(a.xq + (long)t * a.H + col * QK);
-                    dsc[s] = (double)a.xs[(long)t * nblk + col] * KS;
-                }
+                act[s] = load_blk8(a.xq + (long)t * a.H + col * QK);
+                dsc[s] = (double)a.xs[(long)t * nblk + col] * KS;
             } else {
 #pragma unroll
                 for (int k = 0; k < 8; ++k) act[s].v[k] = 0;
@@ -242,29 +212,17 @@ __device__ __forceinline__ void gateup_rows(const GemvArgs &a, const ItemDesc &i
         const int code = round_clamp(__fmul_rn(hv, id), -127.0f, 127.0f);
         const long pair = (long)it.item * MAX_SLOTS + s;
         a.h[pair * a.I + rb * QK + r] = hv;
-        if constexpr (COHERENT) {
-            // reordered dword 2g holds rows 8g+{0,2,4,6}, dword 2g+1 rows 8g+{1,3,5,7}
-            const int c0 = code & 0xFF;
-            const int c1 = __shfl_down(c0, 2, 32), c2 = __shfl_down(c0, 4, 32), c3 = __shfl_down(c0, 6, 32);
-            if ((r & 7) < 2) {
-                const int word = c0 | (c1 << 8) | (c2 << 16) | (c3 << 24);
-                st_dev(reinterpret_cast<int *>(a.hq + pair * a.I + rb * QK) + 2 * (r >> 3) + (r & 1), word);
-            }
-            if (r == 0) st_dev(a.hs + pair * nrb + rb, d);
-        } else {
-            a.hq[pair * a.I + rb * QK + (r & ~7) + perm8(r & 7)] = (int8_t)code;
-            if (r == 0) a.hs[pair * nrb + rb] = d;
-        }
+        a.hq[pair * a.I + rb * QK + (r & ~7) + perm8(r & 7)] = (int8_t)code;
+        if (r == 0) a.hs[pair * nrb + rb] = d;
     }
     __syncthreads();
 }
 
 // Down rows of one item for row group grp of 4*RPW rows (each wave RPW rows,
 // lane l owns block column l; chunks of RD rows with the next chunk's loads in
-// flight); writes ye of pairs item*8 + slot. blockDim = 256. COHERENT: hq/hs
-// are read and ye is written with device-coherent accesses. GS: group
+// flight); writes ye of pairs item*8 + slot. blockDim = 256. GS: group
 // scales, as gateup_rows.
-template <int NT, int RD, bool COHERENT, int RPW, int WB = 4, bool GS = false>
+template <int NT, int RD, int RPW, int WB = 4, bool GS = false>
 __device__ __forceinline__ void down_rows(const GemvArgs &a, const ItemDesc &it, int grp)
 {
     static_assert(!GS || WB == 4, "group scales are an int4 format");
@@ -297,15 +255,8 @@ __device__ __forceinline__ void down_rows(const GemvArgs &a, const ItemDesc &it,
     for (int s = 0; s < NT; ++s) {
         if (s < it.nt && active) {
             const long pair = (long)it.item * MAX_SLOTS + s;
-            if constexpr (COHERENT) {
-                const int *src = reinterpret_cast<const int *>(a.hq + pair * a.I + lane * QK);
-#pragma unroll
-                for (int k = 0; k < 8; ++k) act[s].v[k] = ld_dev(src + k);
-                dsc[s] = (double)ld_dev(a.hs + pair * nblk + lane) * KS;
-            } else {
-                act[s] = load_blk8(a.hq + pair * a.I + lane * QK);
-                dsc[s] = (double)a.hs[pair * nblk + lane] * KS;
-            }
+            act[s] = load_blk8(a.hq + pair * a.I + lane * QK);
+            dsc[s] = (double)a.hs[pair * nblk + lane] * KS;
         } else {
 #pragma unroll
             for (int k = 0; k < 8; ++k) act[s].v[k] = 0;
@@ -343,8 +294,7 @@ __device__ __forceinline__ void down_rows(const GemvArgs &a, const ItemDesc &it,
                 const long row = row0 + c * RD + vi;
                 const long pair = (long)it.item * MAX_SLOTS + s;
                 const float out = GS ? (float)v[s][0] : (float)((double)a.s_a[(long)it.e * a.H + row] * v[s][0]);
-                if constexpr (COHERENT) st_dev(a.ye + pair * a.H + row, out);
-                else a.ye[pair * a.H + row] = out;
+                a.ye[pair * a.H + row] = out;
             }
         }
     }

@@ -47,20 +47,7 @@ struct WsLayout {
     size_t pair_tok, expert_off, tiles;          // grouped path buckets and tile list
     size_t h, hq, hs, ye;
     size_t xn;                                   // [T][H] f32: the RMSNorm of raw rows (coli_moe_forward_rms off the decode launches)
-    size_t sync;                                 // FusedSync (GEMV path)
     size_t total;
-};
-
-// Counters of the fused decode kernel. Zero at rest: a zero-filled workspace
-// starts that way and every call leaves it that way. err is sticky.
-struct FusedSync {
-    unsigned exits_all, select_done, reserved0, reserved1, reserved2, err;
-    unsigned exits[8];
-    unsigned logits_done[8];
-    unsigned pad0[42];
-    unsigned gu_done[8 * COLI_MAX_TOPK + 1];
-    unsigned pad1[63];
-    unsigned dn_done[256];
 };
 
 WsLayout make_layout(const coli_moe_layer &L, int T, int path);
@@ -126,10 +113,6 @@ hipError_t launch_decode_down_combine(const coli_moe_layer &L, int T, const WsLa
 // ---- experts, grouped int8-MFMA path (kernels_grouped.hip)
 hipError_t launch_gateup_grouped(const coli_moe_layer &L, int T, const WsLayout &lay, char *ws, hipStream_t s);
 hipError_t launch_down_grouped(const coli_moe_layer &L, int T, const WsLayout &lay, char *ws, hipStream_t s);
-
-// ---- whole decode layer in one persistent launch (kernels_fused.hip), T <= 8
-hipError_t launch_decode_fused(const coli_moe_layer &L, const float *x, int T, const WsLayout &lay, char *ws,
-                               float *y, bool accumulate, hipStream_t s);
 
 // ---- dense MLP (kernels_dense.hip); its workspace uses the WsLayout fields
 // ctrl, xq, xs, h, hq, hs, ye, xn, tiles, expert_off, pair_tok (pair p = token p)

@@ -181,7 +181,7 @@ __global__ void __launch_bounds__(256) k_select_gateup(SelGuArgs a, GemvArgs g, 
     __shared__ SelGuShared su;
     TRACE(a, 1, 0);
     if ((int)blockIdx.x < n_shared_wg) {         // the shared expert: no routing needed
-        gateup_rows<NT, GemvTuneW<NT, WB>::RC, false, false, 1, WB, GS>(g, shared_item(g), blockIdx.x, sh);
+        gateup_rows<NT, GemvTuneW<NT, WB>::RC, 1, WB, GS>(g, shared_item(g), blockIdx.x, sh);
         TRACE(a, 1, 2);
         return;
     }
@@ -220,7 +220,7 @@ __global__ void __launch_bounds__(256) k_select_gateup(SelGuArgs a, GemvArgs g, 
     it.nt = u.item_nt[item];
 #pragma unroll
     for (int s = 0; s < MAX_SLOTS; ++s) it.tok[s] = s < it.nt ? u.item_tok[item * MAX_SLOTS + s] : 0;
-    gateup_rows<NT, GemvTuneW<NT, WB>::RC, false, false, 1, WB, GS>(g, it, rb, sh);
+    gateup_rows<NT, GemvTuneW<NT, WB>::RC, 1, WB, GS>(g, it, rb, sh);
     TRACE(a, 1, 2);
 }
 
@@ -388,7 +388,7 @@ __global__ void __launch_bounds__(256) k_down_combine(DnArgs a)
 GemvArgs gemv_view(const coli_moe_layer &L, int T, const WsLayout &lay, char *ws)
 {
     GemvArgs g;
-    g.H = L.H; g.I = L.I; g.E = L.E; g.T = T; g.has_shared = L.has_shared; g.item0 = 0; g.x = nullptr;
+    g.H = L.H; g.I = L.I; g.E = L.E; g.T = T; g.has_shared = L.has_shared; g.item0 = 0;
     g.xq = reinterpret_cast<const int8_t *>(ws + lay.xq);
     g.xs = reinterpret_cast<const float *>(ws + lay.xs);
     g.ctrl = reinterpret_cast<const int *>(ws + lay.ctrl);

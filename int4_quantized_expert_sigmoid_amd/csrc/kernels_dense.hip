@@ -27,7 +27,7 @@ __global__ void __launch_bounds__(256) k_dense_gateup(GemvArgs a)
     it.nt = a.T;
 #pragma unroll
     for (int s = 0; s < MAX_SLOTS; ++s) it.tok[s] = s;
-    gateup_rows<NT, GemvTuneW<NT, WB>::RC, false, false, 1, WB>(a, it, blockIdx.x, sh);
+    gateup_rows<NT, GemvTuneW<NT, WB>::RC, 1, WB>(a, it, blockIdx.x, sh);
 }
 
 struct DenseDnArgs {
@@ -196,7 +196,7 @@ hipError_t launch_dense_gemv(const DenseLayer &M, int T, int t0, const DenseLayo
     const long t = t0;
     GemvArgs g;
     g.q_a = M.gate_q; g.s_a = M.gate_s; g.q_b = M.up_q; g.s_b = M.up_s;
-    g.H = M.H; g.I = M.I; g.E = 0; g.T = T; g.has_shared = 0; g.gsh = 0; g.item0 = 0; g.x = nullptr;
+    g.H = M.H; g.I = M.I; g.E = 0; g.T = T; g.has_shared = 0; g.gsh = 0; g.item0 = 0;
     g.xq = reinterpret_cast<const int8_t *>(ws + lay.xq) + t * M.H;
     g.xs = reinterpret_cast<const float *>(ws + lay.xs) + t * (M.H / QK);
     g.ctrl = nullptr; g.item_expert = nullptr; g.item_ntok = nullptr; g.item_tok = nullptr;

@@ -21,7 +21,7 @@ __global__ void __launch_bounds__(256) k_gateup_gemv(GemvArgs a)
     const ItemDesc it = item_from_table(a, item);
     asm volatile("" ::"s"(n_items), "s"(it.e), "s"(it.nt));
     if (item >= n_items) return;
-    gateup_rows<NT, GemvTuneW<NT, WB>::RC, false, false, 1, WB, GS>(a, it, rb, sh);
+    gateup_rows<NT, GemvTuneW<NT, WB>::RC, 1, WB, GS>(a, it, rb, sh);
 }
 
 template <int NT, int WB, bool GS>
@@ -30,14 +30,14 @@ __global__ void __launch_bounds__(256) k_down_gemv(GemvArgs a)
     const int ngrp = a.H / QK;
     const int item = a.item0 + (int)blockIdx.x / ngrp, grp = blockIdx.x % ngrp;
     if (a.has_shared && item == 0) {            // the shared expert exists whatever the routing:
-        down_rows<NT, GemvTuneW<NT, WB>::RD, false, 8, WB, GS>(a, shared_item(a), grp);   // no table wait
+        down_rows<NT, GemvTuneW<NT, WB>::RD, 8, WB, GS>(a, shared_item(a), grp);   // no table wait
         return;
     }
     const int n_items = a.ctrl[CTRL_N_ITEMS];   // with the entry in one round trip, as above
     const ItemDesc it = item_from_table(a, item);
     asm volatile("" ::"s"(n_items), "s"(it.e), "s"(it.nt));
     if (item >= n_items) return;
-    down_rows<NT, GemvTuneW<NT, WB>::RD, false, 8, WB, GS>(a, it, grp);
+    down_rows<NT, GemvTuneW<NT, WB>::RD, 8, WB, GS>(a, it, grp);
 }
 
 template <int WB, bool GS = false>
@@ -61,7 +61,7 @@ void launch_down_wb(int T, dim3 grid, const GemvArgs &a, hipStream_t s)
 GemvArgs make_args(const coli_moe_layer &L, const WsLayout &lay, char *ws)
 {
     GemvArgs a;
-    a.H = L.H; a.I = L.I; a.E = L.E; a.T = lay.T; a.has_shared = L.has_shared; a.x = nullptr; a.item0 = 0;
+    a.H = L.H; a.I = L.I; a.E = L.E; a.T = lay.T; a.has_shared = L.has_shared; a.item0 = 0;
     a.gsh = group_shift(L);
     a.xq = reinterpret_cast<const int8_t *>(ws + lay.xq);
     a.xs = reinterpret_cast<const float *>(ws + lay.xs);

@@ -1,5 +1,5 @@
 // route_device.hpp — device bodies of the router and the batch bookkeeping,
-// shared by the standalone router kernels and the fused decode kernel.
+// shared by the standalone router kernels and the decode launches.
 //
 // Router (ai4coding.ru summary, "what is implemented"; colibri architecture
 // overview, section 5): logits z = W_r x with f64 sums, s = sigmoid(z),

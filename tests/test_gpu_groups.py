@@ -18,7 +18,7 @@ import torch
 from dataclasses import replace
 
 from int4_quantized_expert_sigmoid_amd import api, COLI_ACCUMULATE
-from int4_quantized_expert_sigmoid_amd._lib import ColiError, COLI_EUNSUPPORTED, COLI_PATH_FUSED, COLI_PATH_GROUPED
+from int4_quantized_expert_sigmoid_amd._lib import ColiError, COLI_EUNSUPPORTED, COLI_PATH_GROUPED
 from int4_quantized_expert_sigmoid_amd.synthetic import device_layer
 from oracle import layers as OL
 from oracle import oracle as O
@@ -121,10 +121,9 @@ def test_groups_refused_off_the_gemv_path():
         api.moe_forward(L, dev(x), api.workspace(L, 9))
     assert e.value.code == COLI_EUNSUPPORTED
     ws1 = api.workspace(L, 1)
-    for flags in (COLI_PATH_FUSED, COLI_PATH_GROUPED):
-        with pytest.raises(ColiError) as e:
-            api.moe_forward(L, dev(x[:1]), ws1, flags=flags)
-        assert e.value.code == COLI_EUNSUPPORTED
+    with pytest.raises(ColiError) as e:
+        api.moe_forward(L, dev(x[:1]), ws1, flags=COLI_PATH_GROUPED)
+    assert e.value.code == COLI_EUNSUPPORTED
 
 
 @pytest.fixture(scope="module")

@@ -12,7 +12,7 @@ import pytest
 import torch
 
 from int4_quantized_expert_sigmoid_amd import api, COLI_ACCUMULATE
-from int4_quantized_expert_sigmoid_amd._lib import ColiError, COLI_EUNSUPPORTED, COLI_PATH_FUSED
+from int4_quantized_expert_sigmoid_amd._lib import ColiError, COLI_EUNSUPPORTED, COLI_PATH_GROUPED
 from int4_quantized_expert_sigmoid_amd.synthetic import device_layer
 from oracle import layers as OL
 from oracle import oracle as O
@@ -91,7 +91,7 @@ def test_int8_refused_off_the_gemv_path(tiny8):
     assert e.value.code == COLI_EUNSUPPORTED
     ws1 = api.workspace(L, 1)
     with pytest.raises(ColiError) as e:
-        api.moe_forward(L, dev(x[:1]), ws1, flags=COLI_PATH_FUSED)
+        api.moe_forward(L, dev(x[:1]), ws1, flags=COLI_PATH_GROUPED)
     assert e.value.code == COLI_EUNSUPPORTED
 
 

@@ -6,7 +6,7 @@ import numpy as np
 import pytest
 import torch
 
-from int4_quantized_expert_sigmoid_amd import api, COLI_ACCUMULATE, COLI_PATH_FUSED, COLI_PATH_GROUPED
+from int4_quantized_expert_sigmoid_amd import api, COLI_ACCUMULATE, COLI_PATH_GEMV, COLI_PATH_GROUPED
 from int4_quantized_expert_sigmoid_amd.synthetic import device_layer
 from synth import synth as S
 
@@ -42,7 +42,7 @@ def _both(L, x, g, flags):
     return xa.cpu().numpy(), xb.cpu().numpy()
 
 
-@pytest.mark.parametrize("T,flags", [(1, 0), (2, 0), (4, 0), (8, 0), (3, COLI_PATH_FUSED), (40, 0),
+@pytest.mark.parametrize("T,flags", [(1, 0), (2, 0), (4, 0), (8, 0), (3, COLI_PATH_GEMV), (40, 0),
                                      (5, COLI_PATH_GROUPED)])
 def test_rms_forward_equals_norm_then_forward(tiny, T, flags):
     x = S.tokens(S.TokenSpec(T=T, token_set=90 + T, outlier_channels=3), S.TINY.H, 0)
