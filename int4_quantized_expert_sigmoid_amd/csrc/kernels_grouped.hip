@@ -78,6 +78,22 @@ __device__ __forceinline__ void tile_rg(int w, int nrg, int ntiles, int &tile, i
     }
 }
 
+// Tile-major order: with nrg a multiple of N_XCD, XCD x walks its row
+// groups x, x + 8, ... for one tile before the next tile, so a tile's
+// activation rows are read from memory once per XCD (then from its L2),
+// and the tiles of one expert still follow each other.
+__device__ __forceinline__ void tile_rg_tm(int w, int nrg, int ntiles, int &tile, int &rg)
+{
+    if (nrg % N_XCD == 0) {
+        const int x = w % N_XCD, j = w / N_XCD, per = nrg / N_XCD;
+        tile = j / per;
+        rg = (j % per) * N_XCD + x;
+    } else {
+        tile = w / nrg;
+        rg = w % nrg;
+    }
+}
+
 // Keeps the loads above it issued before the work below it: without it the
 // scheduler sinks a stage's loads to just before their use (to save
 // registers), and every stage then waits out a full memory latency.
@@ -118,11 +134,13 @@ __device__ __forceinline__ int xsw(int p) { return p & 15; }
 // of the HIP vector structs become memcpys that keep a stage in scratch).
 typedef float v4f __attribute__((ext_vector_type(4)));
 
+typedef double v2d __attribute__((ext_vector_type(2)));
+
 template <int NM>
 struct StageLds {
     v4i w[WAVES][NM][QK][KS];
     v4i x[2][TILE_N][XC];
-    float2 d[2][KS / 2][TILE_N];   // activation scales of the stage's block pairs, pair-minor
+    v2d d[2][KS / 2][TILE_N];      // f64 factors d_b/16 of the stage's block pairs (0 past the tile's pairs), pair-minor
 };
 
 __device__ __forceinline__ uint4 as_u4(v4i v) { return make_uint4((uint32_t)v[0], (uint32_t)v[1], (uint32_t)v[2], (uint32_t)v[3]); }
@@ -178,19 +196,22 @@ __device__ __forceinline__ void store_x(StageLds<NM> &sm, int buf, const v4i (&x
     }
 }
 
-// Scales are kept pair-minor: the 32 lanes reading one block pair's
-// scales read 256 contiguous bytes.
+// Scales are staged as the f64 factors the rescale multiplies by, d_b/16
+// (the nibble trick's x16 undone, exact), and 0 for pairs past the tile's
+// np, so the MFMA loops do no conversions. Kept pair-minor: the lanes
+// reading one block pair's factors read contiguous bytes.
 template <int NM>
-__device__ __forceinline__ void store_d(StageLds<NM> &sm, int buf, v4f d)
+__device__ __forceinline__ void store_d(StageLds<NM> &sm, int buf, v4f d, int np)
 {
     const int p = (threadIdx.x & 63) >> 1, jp = 2 * (threadIdx.x & 1);
-    sm.d[buf][jp][p] = make_float2(d[0], d[1]);
-    sm.d[buf][jp + 1][p] = make_float2(d[2], d[3]);
+    const double v = p < np ? 0.0625 : 0.0;
+    sm.d[buf][jp][p] = v2d{(double)d[0] * v, (double)d[1] * v};
+    sm.d[buf][jp + 1][p] = v2d{(double)d[2] * v, (double)d[3] * v};
 }
 
-// Scales of blocks j and j+1 (j even) of the stage for pair n.
+// Factors of blocks j and j+1 (j even) of the stage for pair n.
 template <int NM>
-__device__ __forceinline__ float2 read_d2(const StageLds<NM> &sm, int buf, int n, int j)
+__device__ __forceinline__ v2d read_d2(const StageLds<NM> &sm, int buf, int n, int j)
 {
     return sm.d[buf][j >> 1][n];
 }
@@ -203,27 +224,113 @@ __device__ __forceinline__ int stage_pair(int i, int np)
     return p < np ? p : 0;
 }
 
+// Narrow tiles. A tile holding at most 16 pairs (the last tile of an expert
+// with n % 32 <= 16 pairs, which at prefill is most experts) runs
+// v_mfma_i32_16x16x32_i8 twice per block instead of the 32x32 MFMA: rows
+// 0-15 and 16-31 of the wave's 32 against the tile's 16 pairs. Lane l then
+// holds pair l%16 and the 8 k of quarter q = l/16 of the block (8-group q:
+// weight bytes 4q..4q+3, activation bytes 8q..8q+7 of the reordered block,
+// the same k for both operands), and gets rows 4q..4q+3 of each MFMA's
+// 16x16 result. Each lane rescales 8 elements per block instead of 16, so
+// a narrow tile costs about half the vector work of a 32-pair one.
+template <bool NARROW> struct TileShape;
+template <> struct TileShape<false> { static constexpr int NACC = 16, NPAIR = 32; };
+template <> struct TileShape<true> { static constexpr int NACC = 8, NPAIR = 16; };
+
+// Row of accumulator i of this lane within the wave's 32 rows.
+template <bool NARROW>
+__device__ __forceinline__ int acc_row(int i, int lane)
+{
+    if constexpr (NARROW) return 16 * (i >> 2) + 4 * (lane >> 4) + (i & 3);
+    else return tile_row(i, lane >> 5);
+}
+
+// Pair of this lane's accumulators within the tile.
+template <bool NARROW>
+__device__ __forceinline__ int acc_pair(int lane) { return NARROW ? (lane & 15) : (lane & 31); }
+
+// Both unpacked nibble dwords of one packed dword (elements of one 8-group,
+// x16, in the reordered order) as the 8-byte operand of the 16x16x32 MFMA.
+__device__ __forceinline__ long unpack4(uint32_t w)
+{
+    const uint32_t m = 0xF0F0F0F0u;
+    return (long)(((unsigned long long)(w & m) << 32) | (unsigned long long)((w << 4) & m));
+}
+
+// One matrix over the stage's blocks, adding every block's int32 results
+// times d_b/16 (f64) into acc. m: the matrix's LDS slot; buf: the stage's
+// activation buffer; b0: its first block.
+template <bool FULL, bool NARROW, int NM>
+__device__ __forceinline__ void stage_pass(const StageLds<NM> &sm, int m, double (&acc)[TileShape<NARROW>::NACC], int buf,
+                                           int b0, int nblk)
+{
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    if constexpr (!NARROW) {
+        const v16i zero = {};
+        const int n = lane & 31, half = lane >> 5;
+        const int sw = wsw(n), sx = xsw(n);
+        auto mfma_block = [&](uint2 w, int4 xb, double d) {
+            const v4i B = {xb.x, xb.y, xb.z, xb.w};
+            const v16i c = __builtin_amdgcn_mfma_i32_32x32x32_i8(unpack8(w), B, zero, 0, 0, 0);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[i] = fma((double)c[i], d, acc[i]);
+        };
+#pragma unroll
+        for (int j = 0; j < KS; j += 2) {
+            if (!FULL && b0 + j >= nblk) break;          // uniform: the stage's valid blocks
+            const uint4 wp = as_u4(sm.w[wave][m][n][(j + half) ^ sw]);
+            const int4 x0 = as_i4(sm.x[buf][n][(2 * j + half) ^ sx]);
+            const int4 x1 = as_i4(sm.x[buf][n][(2 * j + 2 + half) ^ sx]);
+            const v2d dd = read_d2<NM>(sm, buf, n, j);
+            uint2 wa, wb;
+            split_pair(wp, wa, wb);
+            mfma_block(wa, x0, dd[0]);
+            if (FULL || b0 + j + 1 < nblk) mfma_block(wb, x1, dd[1]);
+        }
+    } else {
+        const v4i zero = {};
+        const int pr = lane & 15, q = lane >> 4;
+        const int sx = xsw(pr);
+        const int r0 = pr, r1 = pr + 16;                 // the lane's weight rows of the two MFMAs
+        const int sw0 = wsw(r0), sw1 = wsw(r1);
+#pragma unroll
+        for (int j = 0; j < KS; j += 2) {
+            if (!FULL && b0 + j >= nblk) break;
+            const v2d dd = read_d2<NM>(sm, buf, pr, j);
+#pragma unroll
+            for (int jj = 0; jj < 2; ++jj) {
+                const int blk = j + jj;
+                if (!FULL && jj == 1 && b0 + blk >= nblk) break;
+                const char *xr = reinterpret_cast<const char *>(&sm.x[buf][pr][(2 * blk + (q >> 1)) ^ sx]);
+                const long B = *reinterpret_cast<const long *>(xr + 8 * (q & 1));
+                const uint32_t w0 = *reinterpret_cast<const uint32_t *>(
+                    reinterpret_cast<const char *>(&sm.w[wave][m][r0][blk ^ sw0]) + 4 * q);
+                const uint32_t w1 = *reinterpret_cast<const uint32_t *>(
+                    reinterpret_cast<const char *>(&sm.w[wave][m][r1][blk ^ sw1]) + 4 * q);
+                const double d = dd[jj];
+                const v4i c0 = __builtin_amdgcn_mfma_i32_16x16x32_i8(unpack4(w0), B, zero, 0, 0, 0);
+                const v4i c1 = __builtin_amdgcn_mfma_i32_16x16x32_i8(unpack4(w1), B, zero, 0, 0, 0);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    acc[i] = fma((double)c0[i], d, acc[i]);
+                    acc[4 + i] = fma((double)c1[i], d, acc[4 + i]);
+                }
+            }
+        }
+    }
+}
+
 // FULL: the K blocks fill whole stages (nblk % KS == 0), so a stage's blocks
 // need no bounds tests and the scheduler sees a stage as straight-line code
 // (held to 3 waves per SIMD, the occupancy of the general form: about 2%
 // faster at the GLM prefill shape).
-template <bool FULL>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) k_gateup_mfma(GroupedArgs a)
+template <bool FULL, bool NARROW>
+__device__ __forceinline__ void gateup_tile(const GroupedArgs &a, StageLds<2> &sm, int e, int p0, int np, int rt,
+                                            bool rows_ok)
 {
-    __shared__ StageLds<2> sm;
+    constexpr int NACC = TileShape<NARROW>::NACC;
     const int n_rt = a.I / QK;
-    const int nrg = (n_rt + WAVES - 1) / WAVES;
-    int tile, rg;
-    tile_rg(blockIdx.x, nrg, a.ntiles_max, tile, rg);
-    if (tile >= a.ctrl[CTRL_N_TILES_GU]) return;          // uniform over the workgroup
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int rt = rg * WAVES + wave;
-    const bool rows_ok = rt < n_rt;                       // waves past the last row tile only stage activations
-    const int2 td = a.tiles[tile];
-    const int e = td.x, p0 = td.y;
-    const int np = min(TILE_N, a.expert_off[e + 1] - p0);
-    const int n = lane & 31, half = lane >> 5;
-    const bool valid = n < np;
     const int nblk = a.H / QK;
     const long rowb = a.H / 2;
     const long wrow0 = (long)e * a.I + (long)min(rt, n_rt - 1) * QK + (lane >> 3);
@@ -234,34 +341,9 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) k
     const float *drow = a.act_s + (long)a.pair_tok[p0 + pd] * nblk;   // used by wave 0
     const bool vec_scales = nblk % 4 == 0;
 
-    double acc_g[16], acc_u[16];
+    double acc_g[NACC], acc_u[NACC];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) { acc_g[i] = 0.0; acc_u[i] = 0.0; }
-    const v16i zero = {};
-    auto mfma_block = [&](double (&acc)[16], uint2 w, int4 xb, float dsc) {
-        const v4i B = {xb.x, xb.y, xb.z, xb.w};
-        const double d = valid ? (double)dsc * 0.0625 : 0.0;
-        const v16i c = __builtin_amdgcn_mfma_i32_32x32x32_i8(unpack8(w), B, zero, 0, 0, 0);
-#pragma unroll
-        for (int i = 0; i < 16; ++i) acc[i] = fma((double)c[i], d, acc[i]);
-    };
-    // one matrix over the stage's blocks (the activation chunks are read
-    // again for the second matrix: LDS has the bandwidth, registers are short)
-    auto pass = [&](int m, double (&acc)[16], int buf, int b0) {
-        const int sw = wsw(n), sx = xsw(n);
-#pragma unroll
-        for (int j = 0; j < KS; j += 2) {
-            if (!FULL && b0 + j >= nblk) break;          // uniform: the stage's valid blocks
-            const uint4 wp = as_u4(sm.w[wave][m][n][(j + half) ^ sw]);
-            const int4 x0 = as_i4(sm.x[buf][n][(2 * j + half) ^ sx]);
-            const int4 x1 = as_i4(sm.x[buf][n][(2 * j + 2 + half) ^ sx]);
-            const float2 dd = read_d2<2>(sm, buf, n, j);
-            uint2 wa, wb;
-            split_pair(wp, wa, wb);
-            mfma_block(acc, wa, x0, dd.x);
-            if (FULL || b0 + j + 1 < nblk) mfma_block(acc, wb, x1, dd.y);
-        }
-    };
+    for (int i = 0; i < NACC; ++i) { acc_g[i] = 0.0; acc_u[i] = 0.0; }
 
     // Per stage: gate pass, then up pass. The next stage's gate rows and
     // activations load during the gate pass, its up rows during the up pass,
@@ -273,7 +355,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) k
     if (wave == 0) dn = load_d(0, nblk, drow, vec_scales);
     if (rows_ok) { load_w(wn, 0, nblk, wrow[0], rowb); store_w<2>(sm, 0, wn); load_w(wn, 0, nblk, wrow[1], rowb); store_w<2>(sm, 1, wn); }
     store_x<2>(sm, 0, xn);
-    if (wave == 0) store_d<2>(sm, 0, dn);
+    if (wave == 0) store_d<2>(sm, 0, dn, np);
     __syncthreads();
     for (int s = 0; s < nst; ++s) {
         const bool more = s + 1 < nst;
@@ -284,64 +366,77 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) k
             if (rows_ok) load_w(wn, s + 1, nblk, wrow[0], rowb);
         }
         issue_fence();
-        if (rows_ok) pass(0, acc_g, buf, b0);
+        if (rows_ok) stage_pass<FULL, NARROW, 2>(sm, 0, acc_g, buf, b0, nblk);
         issue_fence();
         if (more && rows_ok) {
             store_w<2>(sm, 0, wn);
             load_w(wn, s + 1, nblk, wrow[1], rowb);
         }
         issue_fence();
-        if (rows_ok) pass(1, acc_u, buf, b0);
+        if (rows_ok) stage_pass<FULL, NARROW, 2>(sm, 1, acc_u, buf, b0, nblk);
         issue_fence();
         if (more) {
             if (rows_ok) store_w<2>(sm, 1, wn);
             store_x<2>(sm, (s + 1) & 1, xn);
-            if (wave == 0) store_d<2>(sm, (s + 1) & 1, dn);
+            if (wave == 0) store_d<2>(sm, (s + 1) & 1, dn, np);
         }
         __syncthreads();
     }
     if (!rows_ok) return;
     // epilogue: g, u, h = silu(g)*u, Q8 over the tile's 32 rows per pair
-    float hv[16];
+    // (held by 2 lanes of a 32-pair tile, 4 lanes of a narrow one)
+    float hv[NACC];
     float amax = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        const long grow = (long)e * a.I + (long)rt * QK + tile_row(i, half);
+    for (int i = 0; i < NACC; ++i) {
+        const long grow = (long)e * a.I + (long)rt * QK + acc_row<NARROW>(i, lane);
         const float gf = (float)((double)a.s_a[grow] * acc_g[i]);
         const float uf = (float)((double)a.s_b[grow] * acc_u[i]);
         hv[i] = (float)(silu_f64((double)gf) * (double)uf);
         amax = fmaxf(amax, fabsf(hv[i]));
     }
     amax = fmaxf(amax, __shfl_xor(amax, 32));
-    if (!valid) return;
+    if constexpr (NARROW) amax = fmaxf(amax, __shfl_xor(amax, 16));
+    const int n = acc_pair<NARROW>(lane);
+    if (n >= np) return;
     float d, id;
     q8_scale(amax, d, id);
     const long base = (long)(p0 + n) * a.I + (long)rt * QK;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        const int r = tile_row(i, half);
+    for (int i = 0; i < NACC; ++i) {
+        const int r = acc_row<NARROW>(i, lane);
         a.h[base + r] = hv[i];
         a.hq[base + (r & ~7) + perm8(r & 7)] = (int8_t)round_clamp(__fmul_rn(hv[i], id), -127.0f, 127.0f);
     }
-    if (half == 0) a.hs[(long)(p0 + n) * n_rt + rt] = d;
+    if (lane < TileShape<NARROW>::NPAIR) a.hs[(long)(p0 + n) * n_rt + rt] = d;
 }
 
-__global__ void __launch_bounds__(256) k_down_mfma(GroupedArgs a)
+template <bool FULL>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) k_gateup_mfma(GroupedArgs a)
 {
-    __shared__ StageLds<1> sm;
-    const int n_rt = a.H / QK;
+    __shared__ StageLds<2> sm;
+    const int n_rt = a.I / QK;
     const int nrg = (n_rt + WAVES - 1) / WAVES;
     int tile, rg;
     tile_rg(blockIdx.x, nrg, a.ntiles_max, tile, rg);
     if (tile >= a.ctrl[CTRL_N_TILES_GU]) return;          // uniform over the workgroup
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
     const int rt = rg * WAVES + wave;
-    const bool rows_ok = rt < n_rt;
+    const bool rows_ok = rt < n_rt;                       // waves past the last row tile only stage activations
     const int2 td = a.tiles[tile];
     const int e = td.x, p0 = td.y;
     const int np = min(TILE_N, a.expert_off[e + 1] - p0);
-    const int n = lane & 31, half = lane >> 5;
-    const bool valid = n < np;
+    if (np <= 16) gateup_tile<FULL, true>(a, sm, e, p0, np, rt, rows_ok);
+    else gateup_tile<FULL, false>(a, sm, e, p0, np, rt, rows_ok);
+}
+
+template <bool NARROW>
+__device__ __forceinline__ void down_tile(const GroupedArgs &a, StageLds<1> &sm, int e, int p0, int np, int rt,
+                                          bool rows_ok)
+{
+    constexpr int NACC = TileShape<NARROW>::NACC;
+    const int n_rt = a.H / QK;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int nblk = a.I / QK;
     const long rowb = a.I / 2;
     const long wrow0 = (long)e * a.H + (long)min(rt, n_rt - 1) * QK + (lane >> 3);
@@ -352,17 +447,9 @@ __global__ void __launch_bounds__(256) k_down_mfma(GroupedArgs a)
     const float *drow = a.act_s + (long)(p0 + pd) * nblk;             // used by wave 0
     const bool vec_scales = nblk % 4 == 0;
 
-    double acc[16];
+    double acc[NACC];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) acc[i] = 0.0;
-    const v16i zero = {};
-    auto mfma_block = [&](uint2 wd, int4 hb, float dsc) {
-        const v4i B = {hb.x, hb.y, hb.z, hb.w};
-        const double d = valid ? (double)dsc * 0.0625 : 0.0;
-        const v16i c = __builtin_amdgcn_mfma_i32_32x32x32_i8(unpack8(wd), B, zero, 0, 0, 0);
-#pragma unroll
-        for (int i = 0; i < 16; ++i) acc[i] = fma((double)c[i], d, acc[i]);
-    };
+    for (int i = 0; i < NACC; ++i) acc[i] = 0.0;
 
     const int nst = (nblk + KS - 1) / KS;
     v4i wn[4], xn[2];
@@ -371,7 +458,7 @@ __global__ void __launch_bounds__(256) k_down_mfma(GroupedArgs a)
     if (wave == 0) dn = load_d(0, nblk, drow, vec_scales);
     if (rows_ok) { load_w(wn, 0, nblk, wrow, rowb); store_w<1>(sm, 0, wn); }
     store_x<1>(sm, 0, xn);
-    if (wave == 0) store_d<1>(sm, 0, dn);
+    if (wave == 0) store_d<1>(sm, 0, dn, np);
     __syncthreads();
     for (int s = 0; s < nst; ++s) {
         const bool more = s + 1 < nst;
@@ -381,37 +468,41 @@ __global__ void __launch_bounds__(256) k_down_mfma(GroupedArgs a)
             if (rows_ok) load_w(wn, s + 1, nblk, wrow, rowb);
         }
         issue_fence();
-        if (rows_ok) {
-            const int buf = s & 1, b0 = s * KS;
-            const int sw = wsw(n), sx = xsw(n);
-#pragma unroll
-            for (int j = 0; j < KS; j += 2) {
-                if (b0 + j >= nblk) break;
-                const uint4 wdp = as_u4(sm.w[wave][0][n][(j + half) ^ sw]);
-                const int4 x0 = as_i4(sm.x[buf][n][(2 * j + half) ^ sx]);
-                const int4 x1 = as_i4(sm.x[buf][n][(2 * j + 2 + half) ^ sx]);
-                const float2 dd = read_d2<1>(sm, buf, n, j);
-                uint2 wa, wb;
-                split_pair(wdp, wa, wb);
-                mfma_block(wa, x0, dd.x);
-                if (b0 + j + 1 < nblk) mfma_block(wb, x1, dd.y);
-            }
-        }
+        if (rows_ok) stage_pass<false, NARROW, 1>(sm, 0, acc, s & 1, s * KS, nblk);
         issue_fence();
         if (more) {
             if (rows_ok) store_w<1>(sm, 0, wn);
             store_x<1>(sm, (s + 1) & 1, xn);
-            if (wave == 0) store_d<1>(sm, (s + 1) & 1, dn);
+            if (wave == 0) store_d<1>(sm, (s + 1) & 1, dn, np);
         }
         __syncthreads();
     }
-    if (!rows_ok || !valid) return;
-    float rs[16];                                // row scales first: the stores below may not alias them
+    const int n = acc_pair<NARROW>(lane);
+    if (!rows_ok || n >= np) return;
+    float rs[NACC];                              // row scales first: the stores below may not alias them
 #pragma unroll
-    for (int i = 0; i < 16; ++i) rs[i] = a.s_a[(long)e * a.H + (long)rt * QK + tile_row(i, half)];
+    for (int i = 0; i < NACC; ++i) rs[i] = a.s_a[(long)e * a.H + (long)rt * QK + acc_row<NARROW>(i, lane)];
     const long base = (long)(p0 + n) * a.H + (long)rt * QK;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) a.ye[base + tile_row(i, half)] = (float)((double)rs[i] * acc[i]);
+    for (int i = 0; i < NACC; ++i) a.ye[base + acc_row<NARROW>(i, lane)] = (float)((double)rs[i] * acc[i]);
+}
+
+__global__ void __launch_bounds__(256) k_down_mfma(GroupedArgs a)
+{
+    __shared__ StageLds<1> sm;
+    const int n_rt = a.H / QK;
+    const int nrg = (n_rt + WAVES - 1) / WAVES;
+    int tile, rg;
+    tile_rg_tm(blockIdx.x, nrg, a.ntiles_max, tile, rg);
+    if (tile >= a.ctrl[CTRL_N_TILES_GU]) return;          // uniform over the workgroup
+    const int wave = threadIdx.x >> 6;
+    const int rt = rg * WAVES + wave;
+    const bool rows_ok = rt < n_rt;
+    const int2 td = a.tiles[tile];
+    const int e = td.x, p0 = td.y;
+    const int np = min(TILE_N, a.expert_off[e + 1] - p0);
+    if (np <= 16) down_tile<true>(a, sm, e, p0, np, rt, rows_ok);
+    else down_tile<false>(a, sm, e, p0, np, rt, rows_ok);
 }
 
 GroupedArgs make_args(const WsLayout &lay, char *ws, const coli_moe_layer &L)
