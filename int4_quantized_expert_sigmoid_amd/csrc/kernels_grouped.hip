@@ -269,23 +269,29 @@ __device__ __forceinline__ void stage_pass(const StageLds<NM> &sm, int m, double
         const v16i zero = {};
         const int n = lane & 31, half = lane >> 5;
         const int sw = wsw(n), sx = xsw(n);
-        auto mfma_block = [&](uint2 w, int4 xb, double d) {
-            const v4i B = {xb.x, xb.y, xb.z, xb.w};
-            const v16i c = __builtin_amdgcn_mfma_i32_32x32x32_i8(unpack8(w), B, zero, 0, 0, 0);
-#pragma unroll
-            for (int i = 0; i < 16; ++i) acc[i] = fma((double)c[i], d, acc[i]);
-        };
+        // Both MFMAs of a block pair are issued before either result is
+        // rescaled: the second runs on the matrix core while the vector
+        // unit converts and accumulates the first.
 #pragma unroll
         for (int j = 0; j < KS; j += 2) {
             if (!FULL && b0 + j >= nblk) break;          // uniform: the stage's valid blocks
+            const bool two = FULL || b0 + j + 1 < nblk;
             const uint4 wp = as_u4(sm.w[wave][m][n][(j + half) ^ sw]);
             const int4 x0 = as_i4(sm.x[buf][n][(2 * j + half) ^ sx]);
             const int4 x1 = as_i4(sm.x[buf][n][(2 * j + 2 + half) ^ sx]);
             const v2d dd = read_d2<NM>(sm, buf, n, j);
             uint2 wa, wb;
             split_pair(wp, wa, wb);
-            mfma_block(wa, x0, dd[0]);
-            if (FULL || b0 + j + 1 < nblk) mfma_block(wb, x1, dd[1]);
+            const v4i ua = unpack8(wa), ub = unpack8(wb);
+            const v16i ca = __builtin_amdgcn_mfma_i32_32x32x32_i8(ua, v4i{x0.x, x0.y, x0.z, x0.w}, zero, 0, 0, 0);
+            const v16i cb = two ? __builtin_amdgcn_mfma_i32_32x32x32_i8(ub, v4i{x1.x, x1.y, x1.z, x1.w}, zero, 0, 0, 0)
+                                : zero;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[i] = fma((double)ca[i], dd[0], acc[i]);
+            if (two) {
+#pragma unroll
+                for (int i = 0; i < 16; ++i) acc[i] = fma((double)cb[i], dd[1], acc[i]);
+            }
         }
     } else {
         const v4i zero = {};
@@ -293,27 +299,38 @@ __device__ __forceinline__ void stage_pass(const StageLds<NM> &sm, int m, double
         const int sx = xsw(pr);
         const int r0 = pr, r1 = pr + 16;                 // the lane's weight rows of the two MFMAs
         const int sw0 = wsw(r0), sw1 = wsw(r1);
+        // the four MFMAs of a block pair are issued before any result is
+        // rescaled (see the 32-pair form)
 #pragma unroll
         for (int j = 0; j < KS; j += 2) {
             if (!FULL && b0 + j >= nblk) break;
+            const bool two = FULL || b0 + j + 1 < nblk;
             const v2d dd = read_d2<NM>(sm, buf, pr, j);
+            v4i c[2][2];
 #pragma unroll
             for (int jj = 0; jj < 2; ++jj) {
                 const int blk = j + jj;
-                if (!FULL && jj == 1 && b0 + blk >= nblk) break;
+                if (jj == 1 && !two) {
+                    c[1][0] = zero;
+                    c[1][1] = zero;
+                    break;
+                }
                 const char *xr = reinterpret_cast<const char *>(&sm.x[buf][pr][(2 * blk + (q >> 1)) ^ sx]);
                 const long B = *reinterpret_cast<const long *>(xr + 8 * (q & 1));
                 const uint32_t w0 = *reinterpret_cast<const uint32_t *>(
                     reinterpret_cast<const char *>(&sm.w[wave][m][r0][blk ^ sw0]) + 4 * q);
                 const uint32_t w1 = *reinterpret_cast<const uint32_t *>(
                     reinterpret_cast<const char *>(&sm.w[wave][m][r1][blk ^ sw1]) + 4 * q);
-                const double d = dd[jj];
-                const v4i c0 = __builtin_amdgcn_mfma_i32_16x16x32_i8(unpack4(w0), B, zero, 0, 0, 0);
-                const v4i c1 = __builtin_amdgcn_mfma_i32_16x16x32_i8(unpack4(w1), B, zero, 0, 0, 0);
+                c[jj][0] = __builtin_amdgcn_mfma_i32_16x16x32_i8(unpack4(w0), B, zero, 0, 0, 0);
+                c[jj][1] = __builtin_amdgcn_mfma_i32_16x16x32_i8(unpack4(w1), B, zero, 0, 0, 0);
+            }
+#pragma unroll
+            for (int jj = 0; jj < 2; ++jj) {
+                if (jj == 1 && !two) break;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    acc[i] = fma((double)c0[i], d, acc[i]);
-                    acc[4 + i] = fma((double)c1[i], d, acc[4 + i]);
+                    acc[i] = fma((double)c[jj][0][i], dd[jj], acc[i]);
+                    acc[4 + i] = fma((double)c[jj][1][i], dd[jj], acc[4 + i]);
                 }
             }
         }
