@@ -12,7 +12,8 @@ SOURCES = ["abi.cpp", "kernels_quant.hip", "kernels_route.hip", "kernels_gemv.hi
            "kernels_decode.hip", "kernels_dense.hip"]
 # The grouped MFMA kernels read every MFMA result with VALU instructions; in
 # VGPR form the accumulator copies (one per result) disappear.
-SOURCE_FLAGS = {"kernels_grouped.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+SOURCE_FLAGS = {"kernels_grouped.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+                "kernels_route.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-fno-fast-math", "-ffp-contract=fast-honor-pragmas", "-Wall", "-Wno-unused-function"]

@@ -170,15 +170,17 @@ struct SelGuArgs {
 #endif
 };
 
+template <int KPL>
 struct SelGuShared {
     DecUnion u;
+    double kw[4][64 * KPL];    // each wave's copy of a token's keys (group scores)
 };
 
 template <int NT, int KPL, int WB, bool GS>
 __global__ void __launch_bounds__(256) k_select_gateup(SelGuArgs a, GemvArgs g, int n_shared_wg)
 {
     __shared__ GateUpShared<NT> sh;
-    __shared__ SelGuShared su;
+    __shared__ SelGuShared<KPL> su;
     TRACE(a, 1, 0);
     if ((int)blockIdx.x < n_shared_wg) {         // the shared expert: no routing needed
         gateup_rows<NT, GemvTuneW<NT, WB>::RC, 1, WB, GS>(g, shared_item(g), blockIdx.x, sh);
@@ -189,7 +191,7 @@ __global__ void __launch_bounds__(256) k_select_gateup(SelGuArgs a, GemvArgs g, 
     DecUnion &u = su.u;
     // only the publishing workgroup needs the routing weights
     dec_route_union<KPL>(a.key, a.sig, a.T, a.E, a.top_k, a.n_group, a.topk_group, a.route_scale, a.has_shared,
-                         u, b == 0);
+                         u, &su.kw[0][0], b == 0);
     TRACE(a, 1, 1);
     const int nrb = g.I / QK;
     const int item = a.has_shared + b / nrb, rb = b % nrb;

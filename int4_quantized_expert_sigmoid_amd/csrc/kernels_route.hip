@@ -27,72 +27,98 @@ __global__ void __launch_bounds__(256) k_logits_small(const float *__restrict__ 
 
 // Large batches: 64 tokens x 64 experts per workgroup over one slice of H
 // (blockIdx.z of n_split equal slices, each a whole number of 32-column
-// chunks), 4x4 outputs per thread. The f32 products are exact in f64 and are
-// summed in f64; slice s writes its partial sums to part[s][t][e] and the
-// selection adds the slices in order. The next chunk's loads are in flight
-// while the current one is multiplied.
-constexpr int LG_T = 64, LG_E = 64, LG_K = 32, LG_PAD = 36;
+// chunks), on the f64 matrix cores: wave w owns the 32 x 32 quarter
+// (w >> 1, w & 1) as 2 x 2 tiles of v_mfma_f64_16x16x4f64. The f32 inputs and
+// their products are exact in f64; the sums are f64. Within a chunk the
+// MFMA's k index q (lane / 16) takes columns 8q .. 8q+7 in turn, so a lane's
+// values of a row are two float4 loads and nothing is staged in LDS. The
+// next chunk's loads are in flight while the current one is multiplied.
+// Slice s writes its partial sums to part[s][t][e] and the selection adds
+// the slices in order.
+constexpr int LG_T = 64, LG_E = 64, LG_K = 32;
+typedef double f64x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float f4_at(const float4 &v, int i)
+{
+    return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
+}
 
 __global__ void __launch_bounds__(256) k_logits_split(const float *__restrict__ W, const float *__restrict__ x,
                                                       int T, int H, int E, int kspan, double *__restrict__ part)
 {
-    __shared__ float xs[LG_T][LG_PAD];
-    __shared__ float wsm[LG_E][LG_PAD];
-    const int t0 = blockIdx.x * LG_T, e0 = blockIdx.y * LG_E, k0 = blockIdx.z * kspan;
-    const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
-    const int lr = tid >> 3, lc = (tid & 7) * 4;     // loader: rows lr and lr + 32, columns lc..lc+3
-    double acc[4][4];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int r = lane & 15, q = lane >> 4;
+    const int t0 = blockIdx.x * LG_T + (wave >> 1) * 32, e0 = blockIdx.y * LG_E + (wave & 1) * 32;
+    const long k0 = (long)blockIdx.z * kspan + 8 * q;
+    // the lane's rows: tokens t0 + r and t0 + 16 + r, experts e0 + r and e0 + 16 + r.
+    // A row past T (or E) reads row 0 instead: it only feeds output rows (or
+    // columns) that are never stored, so every load is unconditional.
+    const float *px[2], *pw[2];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 2; ++i) {
+        const int t = t0 + 16 * i + r, e = e0 + 16 * i + r;
+        px[i] = x + (long)(t < T ? t : 0) * H + k0;
+        pw[i] = W + (long)(e < E ? e : 0) * H + k0;
+    }
+    float4 ax[2][2], aw[2][2], bx[2][2], bw[2][2];   // two chunks: [row block][half of the lane's 8 columns]
+    auto load = [&](int kc, float4 (&lx)[2][2], float4 (&lw)[2][2]) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = 0.0;
-    float4 rx[2], rw[2];
-    auto load = [&](int k) {
+        for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const int r = lr + 32 * h;
-            rx[h] = (t0 + r < T) ? *reinterpret_cast<const float4 *>(x + (long)(t0 + r) * H + k + lc)
-                                 : make_float4(0.f, 0.f, 0.f, 0.f);
-            rw[h] = (e0 + r < E) ? *reinterpret_cast<const float4 *>(W + (long)(e0 + r) * H + k + lc)
-                                 : make_float4(0.f, 0.f, 0.f, 0.f);
+            for (int h = 0; h < 2; ++h) {
+                lx[i][h] = *reinterpret_cast<const float4 *>(px[i] + kc + 4 * h);
+                lw[i][h] = *reinterpret_cast<const float4 *>(pw[i] + kc + 4 * h);
+            }
+    };
+    f64x4 acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = f64x4{0.0, 0.0, 0.0, 0.0};
+    auto mult = [&](const float4 (&lx)[2][2], const float4 (&lw)[2][2]) {
+#pragma unroll
+        for (int st = 0; st < 8; ++st) {
+            double a[2], b[2];
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                a[i] = (double)f4_at(lx[i][st >> 2], st & 3);
+                b[i] = (double)f4_at(lw[i][st >> 2], st & 3);
+            }
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[i], b[j], acc[i][j], 0, 0, 0);
         }
     };
-    load(k0);
-    for (int kc = 0; kc < kspan; kc += LG_K) {
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            *reinterpret_cast<float4 *>(&xs[lr + 32 * h][lc]) = rx[h];
-            *reinterpret_cast<float4 *>(&wsm[lr + 32 * h][lc]) = rw[h];
-        }
-        __syncthreads();
-        if (kc + LG_K < kspan) load(k0 + kc + LG_K);
-#pragma unroll
-        for (int kk = 0; kk < LG_K; kk += 4) {
-            float4 a[4], b[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) a[i] = *reinterpret_cast<const float4 *>(&xs[ty + 16 * i][kk]);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) b[j] = *reinterpret_cast<const float4 *>(&wsm[tx + 16 * j][kk]);
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    acc[i][j] = fma((double)a[i].x, (double)b[j].x, acc[i][j]);
-                    acc[i][j] = fma((double)a[i].y, (double)b[j].y, acc[i][j]);
-                    acc[i][j] = fma((double)a[i].z, (double)b[j].z, acc[i][j]);
-                    acc[i][j] = fma((double)a[i].w, (double)b[j].w, acc[i][j]);
-                }
-        }
-        __syncthreads();
+    // chunks alternate between the two buffers, the next one loading while
+    // the current one is multiplied. The loop body is one straight block
+    // (two chunks, no exits) and every load in it is issued (past the
+    // slice's end it reads the last chunk again, unused), so each wait is for
+    // the current chunk only; the scheduling barriers keep the loads ahead of
+    // the products instead of next to their uses.
+    const int nch = kspan / LG_K, last = kspan - LG_K;
+    load(0, ax, aw);
+    int c = 0;
+    for (; c + 2 <= nch; c += 2) {
+        load((c + 1) * LG_K, bx, bw);
+        __builtin_amdgcn_sched_barrier(0);
+        mult(ax, aw);
+        load(min((c + 2) * LG_K, last), ax, aw);
+        __builtin_amdgcn_sched_barrier(0);
+        mult(bx, bw);
     }
+    if (c < nch) mult(ax, aw);                       // an odd last chunk
+    // lane (r, q) holds rows q, q + 4, q + 8, q + 12 (tokens) of column r (expert) of each tile
     double *out = part + (long)blockIdx.z * T * E;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int t = t0 + ty + 16 * i, e = e0 + tx + 16 * j;
-            if (t < T && e < E) out[(long)t * E + e] = acc[i][j];
-        }
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                const int t = t0 + 16 * i + 4 * m + q, e = e0 + 16 * j + r;
+                if (t < T && e < E) out[(long)t * E + e] = acc[i][j][m];
+            }
 }
 
 // T <= 8: top-k of every token, then the batch union.
@@ -171,17 +197,27 @@ __global__ void __launch_bounds__(1024) k_bucket(BucketArgs a)
     }
     if (threadIdx.x == 0 && a.has_shared) cnt[a.E] = a.T;
     __syncthreads();
-    if (threadIdx.x == 0) {
-        int acc = 0, tacc = 0;
-        for (int e = 0; e < nb; ++e) {
-            off[e] = acc; toff[e] = tacc;
-            acc += cnt[e];
-            tacc += (cnt[e] + TILE_M - 1) / TILE_M;
+    {
+        // exclusive scans of the pair and tile counts over buckets 0..nb
+        // (thread e holds bucket e; entry nb, of count 0, gets the totals):
+        // wave scans, then the wave totals, then both added together
+        __shared__ int wsum[2][16];
+        const int e = threadIdx.x, lane = e & 63, wave = e >> 6;
+        const int c = e < nb ? cnt[e] : 0, tc = (c + TILE_M - 1) / TILE_M;
+        int ic = c, it = tc;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const int oc = __shfl_up(ic, d), ot = __shfl_up(it, d);
+            if (lane >= d) { ic += oc; it += ot; }
         }
-        off[nb] = acc; toff[nb] = tacc;
-        a.ctrl[CTRL_N_TILES_GU] = tacc;
+        if (lane == 63) { wsum[0][wave] = ic; wsum[1][wave] = it; }
+        __syncthreads();
+        int bc = 0, bt = 0;
+        for (int w = 0; w < wave; ++w) { bc += wsum[0][w]; bt += wsum[1][w]; }
+        if (e <= nb) { off[e] = bc + ic - c; toff[e] = bt + it - tc; }
+        __syncthreads();
+        if (e == 0) a.ctrl[CTRL_N_TILES_GU] = toff[nb];
     }
-    __syncthreads();
     for (int e = threadIdx.x; e <= nb; e += blockDim.x) a.expert_off[e] = off[e];
     for (int e = threadIdx.x; e < nb; e += blockDim.x) {
         for (int tt = 0; tt < toff[e + 1] - toff[e]; ++tt)
@@ -210,7 +246,7 @@ int logits_splits(int T, int E, int H)
     const long tiles = (long)((T + LG_T - 1) / LG_T) * ((E + LG_E - 1) / LG_E);
     const int nchunk = H / LG_K;
     int ns = 1;
-    while (ns * 2 <= 16 && tiles * ns * 2 <= 1024 && nchunk % (ns * 2) == 0) ns *= 2;
+    while (ns * 2 <= MAX_SPLIT && tiles * ns * 2 <= 1024 && nchunk % (ns * 2) == 0) ns *= 2;
     return ns;
 }
 

@@ -105,15 +105,24 @@ struct SelArgs {
     int *pair_of, *shared_pair;
 };
 
-// Logit z[t][e]: the partial sums over slices of H in slice order.
+constexpr int MAX_SPLIT = 16;       // slices of H the large-batch logits are split into, at most
+
+// Logit z[t][e]: the partial sums over slices of H in slice order. The
+// partials come from an earlier launch: every load is issued before the
+// first is added, so the sum waits on one round trip, not n_part.
 __device__ __forceinline__ double sel_logit(const SelArgs &a, int t, int e)
 {
     const double *p = a.z + (long)t * a.E + e;
-    if (a.n_part <= 1) return ld_dev(p);
+    if (a.n_part <= 1) return *p;
     const long stride = (long)a.T * a.E;
-    double v = 0.0;
-    for (int s = 0; s < a.n_part; ++s) v += ld_dev(p + s * stride);
-    return v;
+    double v[MAX_SPLIT];
+#pragma unroll
+    for (int s = 0; s < MAX_SPLIT; ++s) v[s] = s < a.n_part ? p[s * stride] : 0.0;
+    double acc = 0.0;
+#pragma unroll
+    for (int s = 0; s < MAX_SPLIT; ++s)
+        if (s < a.n_part) acc += v[s];
+    return acc;
 }
 
 // LDS of the selection for nt tokens, carved from dynamic shared memory.
@@ -139,6 +148,32 @@ __device__ inline SelShared sel_view(char *base, int nt, int E, int k, int ng)
     return v;
 }
 
+// Score of one group of group-limited routing: the sum of its two largest
+// keys (a running top-2 in index order; the group's single key when it has
+// one). The keys are read eight at a time, so the reads of a chunk are in
+// flight together.
+__device__ inline double group_score(const double *g, int gsize)
+{
+    double m1 = -INFINITY, m2 = -INFINITY;
+    int j = 0;
+    for (; j + 8 <= gsize; j += 8) {
+        double v[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = g[j + i];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            if (v[i] > m1) { m2 = m1; m1 = v[i]; }
+            else if (v[i] > m2) { m2 = v[i]; }
+        }
+    }
+    for (; j < gsize; ++j) {
+        const double v = g[j];
+        if (v > m1) { m2 = m1; m1 = v; }
+        else if (v > m2) { m2 = v; }
+    }
+    return gsize >= 2 ? m1 + m2 : m1;
+}
+
 // Top-k of nt tokens (t0 ..) by rank: expert e is chosen at position
 // rank(e) = #{e' : key_e' > key_e, or key_e' == key_e and e' < e} when that
 // rank is below top_k. This is the largest-first order with ties to the lower
@@ -157,13 +192,7 @@ __device__ inline void select_tokens_block(const SelArgs &a, int t0, int nt, Sel
         const int gsize = E / a.n_group;
         for (int i = tid; i < nt * a.n_group; i += nth) {
             const int t = i / a.n_group, g = i % a.n_group;
-            double m1 = -INFINITY, m2 = -INFINITY;       // two largest keys, in index order
-            for (int e = g * gsize; e < (g + 1) * gsize; ++e) {
-                const double v = sh.key[t * E + e];
-                if (v > m1) { m2 = m1; m1 = v; }
-                else if (v > m2) { m2 = v; }
-            }
-            sh.gscore[t * a.n_group + g] = gsize >= 2 ? m1 + m2 : m1;
+            sh.gscore[t * a.n_group + g] = group_score(sh.key + (size_t)t * E + g * gsize, gsize);
         }
         __syncthreads();
         for (int i = tid; i < nt * E; i += nth) {
@@ -370,23 +399,16 @@ __device__ __forceinline__ Cand wave_best(Cand c)
 }
 
 // Kept groups of group-limited routing for one token (one wave): a group's
-// score is the sum of its two largest keys (in index order, as a running
-// top-2), the topk_group best scores are kept, equal scores to the lower
-// group. Returns a bitmask over groups (all ones when n_group == 1).
-__device__ inline unsigned long long kept_groups(const double *__restrict__ key, int E, int n_group, int topk_group)
+// score is the sum of its two largest keys (group_score), the topk_group best
+// scores are kept, equal scores to the lower group. kw holds the token's E
+// keys (this wave's LDS copy); lane g scores group g. Returns a bitmask over
+// groups (all ones when n_group == 1).
+__device__ inline unsigned long long kept_groups(const double *kw, int E, int n_group, int topk_group)
 {
     if (n_group <= 1) return ~0ull;
     const int lane = threadIdx.x & 63, gsize = E / n_group;
     double gs = -INFINITY;
-    if (lane < n_group) {
-        double m1 = -INFINITY, m2 = -INFINITY;
-        for (int e = lane * gsize; e < (lane + 1) * gsize; ++e) {
-            const double v = key[e];
-            if (v > m1) { m2 = m1; m1 = v; }
-            else if (v > m2) { m2 = v; }
-        }
-        gs = gsize >= 2 ? m1 + m2 : m1;
-    }
+    if (lane < n_group) gs = group_score(kw + lane * gsize, gsize);
     int r = 0;
     for (int g2 = 0; g2 < n_group; ++g2) {
         const double o = __shfl(gs, g2);
@@ -408,23 +430,33 @@ __device__ __forceinline__ unsigned wave_max_u32(unsigned v)
     return max(b[0], b[1]);
 }
 
-// Lane l's KPL keys (experts l, l+64, ...) as order keys with their experts
-// and sigmoids, sorted by (key desc, expert asc). The keys come from an
-// earlier launch: plain loads, so the workgroups on one XCD share its L2
-// copy instead of each reading the same lines from memory.
+// Lane l's KPL keys and sigmoids (experts l, l+64, ...), read together. The
+// keys come from an earlier launch: plain loads, so the workgroups on one
+// XCD share its L2 copy instead of each reading the same lines from memory.
 template <int KPL>
-__device__ __forceinline__ void lane_keys(const double *__restrict__ key, const double *__restrict__ sig, int E,
-                                          int gsize, unsigned long long gm, unsigned long long (&ok)[KPL],
-                                          int (&oe)[KPL], double (&sv)[KPL])
+__device__ __forceinline__ void lane_load(const double *__restrict__ key, const double *__restrict__ sig, int E,
+                                          double (&kv)[KPL], double (&sv)[KPL])
 {
     const int lane = threadIdx.x & 63;
 #pragma unroll
     for (int i = 0; i < KPL; ++i) {
         const int e = lane + 64 * i;
-        const bool in = e < E;
-        const double kv = in ? key[e] : 0.0;
-        sv[i] = in ? sig[e] : 0.0;
-        ok[i] = (in && ((gm >> (e / gsize)) & 1ull)) ? order_key(kv) : 0ull;
+        kv[i] = e < E ? key[e] : 0.0;
+        sv[i] = e < E ? sig[e] : 0.0;
+    }
+}
+
+// The lane's keys as order keys (0 for experts outside the kept groups gm)
+// with their experts and sigmoids, sorted by (key desc, expert asc).
+template <int KPL>
+__device__ __forceinline__ void lane_order(const double (&kv)[KPL], int E, int gsize, unsigned long long gm,
+                                           unsigned long long (&ok)[KPL], int (&oe)[KPL], double (&sv)[KPL])
+{
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int i = 0; i < KPL; ++i) {
+        const int e = lane + 64 * i;
+        ok[i] = (e < E && ((gm >> (e / gsize)) & 1ull)) ? order_key(kv[i]) : 0ull;
         oe[i] = e;
     }
     COLI_SEL_MARK(0);
@@ -471,15 +503,28 @@ __device__ __forceinline__ void lane_pop(int r, unsigned long long (&ok)[KPL], i
 template <int KPL>
 __device__ inline void wave_topk(const double *__restrict__ key, const double *__restrict__ sig, int E, int k,
                                  int n_group, int topk_group, float route_scale, int *sel_e, float *sel_w,
-                                 double *sel_s, bool weights)
+                                 double *sel_s, bool weights, double *kw)
 {
     const int lane = threadIdx.x & 63;
-    const unsigned long long gm = kept_groups(key, E, n_group, topk_group);
     const int gsize = E / n_group;
-    double sv[KPL];
+    double kv[KPL], sv[KPL];
+    lane_load<KPL>(key, sig, E, kv, sv);             // one round trip for all keys and sigmoids
+    unsigned long long gm = ~0ull;
+    if (n_group > 1) {                               // group scores from this wave's LDS copy of the keys
+#pragma unroll
+        for (int i = 0; i < KPL; ++i)
+            if (lane + 64 * i < E) kw[lane + 64 * i] = kv[i];
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        gm = kept_groups(kw, E, n_group, topk_group);
+    }
     unsigned long long ok[KPL];
     int oe[KPL];
-    lane_keys<KPL>(key, sig, E, gsize, gm, ok, oe, sv);
+    double ss[KPL];
+#pragma unroll
+    for (int i = 0; i < KPL; ++i) ss[i] = sv[i];
+    lane_order<KPL>(kv, E, gsize, gm, ok, oe, ss);
     COLI_SEL_MARK(1);
     if (lane < k) { sel_e[lane] = 0; sel_s[lane] = 0.0; }   // kept only without enough finite keys
     // fast rounds on the upper 32 bits only (a valid key's are never 0)
@@ -487,7 +532,7 @@ __device__ inline void wave_topk(const double *__restrict__ key, const double *_
     int fe[KPL];
     double fs[KPL];
 #pragma unroll
-    for (int i = 0; i < KPL; ++i) { kh[i] = (unsigned)(ok[i] >> 32); fe[i] = oe[i]; fs[i] = sv[i]; }
+    for (int i = 0; i < KPL; ++i) { kh[i] = (unsigned)(ok[i] >> 32); fe[i] = oe[i]; fs[i] = ss[i]; }
     bool tie = false;
     for (int r = 0; r < k; ++r) {
         const unsigned long long m = __ballot(kh[0] == wave_max_u32(kh[0]));
@@ -501,7 +546,7 @@ __device__ inline void wave_topk(const double *__restrict__ key, const double *_
         }
     }
     if (tie) {                                       // exact order in every round
-        lane_keys<KPL>(key, sig, E, gsize, gm, ok, oe, sv);
+        lane_order<KPL>(kv, E, gsize, gm, ok, oe, sv);
         if (lane < k) { sel_e[lane] = 0; sel_s[lane] = 0.0; }
         for (int r = 0; r < k; ++r) {
             Cand c{(unsigned)ok[0], (unsigned)(ok[0] >> 32), ok[0] != 0ull ? oe[0] : 0x7FFFFFFF};
@@ -539,11 +584,12 @@ struct DecUnion {
 // 64 * KPL), then the
 // union: the shared expert is item 0 (slot t = token t), routed experts follow
 // in order of first use (token-major, then slot). All threads of the
-// workgroup call it; blockDim >= 64.
+// workgroup call it; blockDim >= 64. kw: LDS of 64 * KPL doubles per wave
+// (the wave's copy of a token's keys while its groups are scored).
 template <int KPL>
 __device__ inline void dec_route_union(const double *__restrict__ key, const double *__restrict__ sig, int T, int E,
                                        int k, int n_group, int topk_group, float route_scale, int has_shared,
-                                       DecUnion &u, bool weights = true)
+                                       DecUnion &u, double *kw, bool weights = true)
 {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nwave = blockDim.x >> 6;
     for (int t = wave; t < T; t += nwave) {
@@ -551,7 +597,7 @@ __device__ inline void dec_route_union(const double *__restrict__ key, const dou
         int *se = u.sel_e + t * k;
         float *sw = u.sel_w + t * k;
         double *ss = u.sel_s + t * k;
-        wave_topk<KPL>(kt, st, E, k, n_group, topk_group, route_scale, se, sw, ss, weights);
+        wave_topk<KPL>(kt, st, E, k, n_group, topk_group, route_scale, se, sw, ss, weights, kw + wave * 64 * KPL);
     }
     if (T == 1) {                                 // one token: item has_shared + j is its slot j
         __syncthreads();
