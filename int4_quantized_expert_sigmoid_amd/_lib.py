@@ -10,7 +10,9 @@ import ctypes
 import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libcoli_moe.so")
+# COLI_LIB_VARIANT=asan selects the host-sanitizer build of the CPU test suite
+# (host code only, no device code: see tests/run_sanitized.py)
+LIB_PATH = os.path.join(HERE, "_asan" if os.environ.get("COLI_LIB_VARIANT") == "asan" else "", "libcoli_moe.so")
 
 COLI_OK, COLI_EINVAL, COLI_EWORKSPACE, COLI_EDEVICE, COLI_EUNSUPPORTED = 0, -1, -2, -3, -4
 COLI_ACCUMULATE, COLI_PATH_GEMV, COLI_PATH_GROUPED = 1, 2, 4

@@ -34,7 +34,8 @@ def threads() -> int:
 def _lib():
     name = "liboracle_omp.so" if _THREADED else "liboracle.so"
     if name not in _LIBS:
-        path = os.path.join(HERE, name)
+        # COLI_LIB_VARIANT=asan: the sanitizer build of the CPU test suite
+        path = os.path.join(HERE, "_asan" if os.environ.get("COLI_LIB_VARIANT") == "asan" else "", name)
         if not os.path.exists(path):
             raise RuntimeError(f"{path} is not built; run __graft_entry__.build()")
         L = ctypes.CDLL(path)

@@ -27,7 +27,8 @@ GATE, UP, DOWN = 0, 1, 2
 def _lib():
     global _host
     if _host is None:
-        path = os.path.join(HERE, "libsynth.so")
+        # COLI_LIB_VARIANT=asan: the sanitizer build of the CPU test suite
+        path = os.path.join(HERE, "_asan" if os.environ.get("COLI_LIB_VARIANT") == "asan" else "", "libsynth.so")
         if not os.path.exists(path):
             raise RuntimeError(f"{path} is not built; run __graft_entry__.build()")
         L = ctypes.CDLL(path)

@@ -1,9 +1,10 @@
 """GPU parity of the dense MLP (coli_dense_forward) through the C ABI against
 the oracle's O15, on both paths (token-GEMV for T <= 8, grouped MFMA above;
 int8 above 8 tokens on the token-GEMV kernels in chunks of 8),
-both weight formats, intermediate sizes below and above 256 blocks (one and
-two block columns per thread in the down kernel), with the RMSNorm input and
-the residual added in place."""
+both weight formats, intermediate sizes below and above 256 blocks (for one
+token slot the down kernel then gives each thread a second block column, for
+more slots it adds waves), with the RMSNorm input and the residual added in
+place."""
 import numpy as np
 import pytest
 import torch
@@ -101,10 +102,14 @@ def test_dense_paths_agree():
 
 
 @pytest.mark.parametrize("bits", [4, 8])
-def test_dense_two_columns_per_thread(bits):
-    """I = 8448: 264 blocks per down row, a fifth wave in the down kernel with 8 of its lanes in use."""
+@pytest.mark.parametrize("T", [1, 3])
+def test_dense_down_past_256_blocks(bits, T):
+    """I = 8448: 264 blocks per down row. One token slot (T = 1) takes the
+    four-wave form with a second block column per thread for the blocks past
+    256; more slots (T = 3) take one column per thread with a fifth wave, 8
+    of its lanes in use."""
     spec = S.DenseSpec(H=256, I=8448, w_outlier_rate=0.01, weight_bits=bits)
-    check(spec, 3, token_set=41)
+    check(spec, T, token_set=41 + T)
 
 
 def test_dense_rmsnorm_and_residual_in_place():
