@@ -448,11 +448,14 @@ def bench_dense(args):
     kms = np.array([[ms for _, ms in d] for d in durs]).mean(axis=0)
     del per_call
     wb = spec.weight_bits
-    # every launch of a kernel reads its whole matrices: int8 batches past 8
-    # tokens run the GEMV kernels once per 8-token chunk
-    ms_gu = float(np.mean([v for n, v in zip(names, kms) if n == "k_dense_gateup"]))
-    ms_dn = float(np.mean([v for n, v in zip(names, kms) if n == "k_dense_down"]))
-    passes = sum(1 for n in names if n == "k_dense_gateup")
+    # every launch of a gate/up or down kernel reads its whole matrices: the
+    # token-GEMV kernels (T <= 8) or the grouped MFMA kernels (larger T, one
+    # expert holding every token)
+    GU, DN = ("k_dense_gateup", "k_gateup_mfma"), ("k_dense_down", "k_down_mfma")
+    k_gu = next(n for n in names if n in GU)
+    ms_gu = float(np.mean([v for n, v in zip(names, kms) if n in GU]))
+    ms_dn = float(np.mean([v for n, v in zip(names, kms) if n in DN]))
+    passes = sum(1 for n in names if n in GU)
     gu_bytes = 2 * spec.I * (spec.H * wb // 8 + 4)
     dn_bytes = spec.H * (spec.I * wb // 8 + 4)
     gu_gbs = gu_bytes / (ms_gu * 1e-3) / 1e9
@@ -461,7 +464,7 @@ def bench_dense(args):
     step_gbs = step_bytes / (ms_step * 1e-3) / 1e9
     log("bench: kernel averages (ms): " + ", ".join(f"{n}={v:.4f}" for n, v in zip(names, kms)))
     if passes > 1:
-        log(f"bench: {passes} GEMV passes of 8 tokens per step")
+        log(f"bench: {passes} gate/up passes per step")
     log(f"bench: gate/up {gu_gbs:.0f} GB/s, down {dn_gbs:.0f} GB/s, whole step {step_gbs:.0f} GB/s; "
         f"{ms_step * 1e3:.2f} us/step")
 
@@ -508,7 +511,7 @@ def bench_dense(args):
                    "hip_graph": True, "weight_bytes_per_step": step_bytes, "gemv_passes": passes,
                    "step_hbm_gbs": round(step_gbs, 1),
                    "kernel_ms": [[n, round(float(v), 5)] for n, v in zip(names, kms)]},
-        "roofline": {"bound": "hbm", "kernel": "k_dense_gateup", "achieved": round(gu_gbs, 1), "peak": HBM_PEAK_GBS,
+        "roofline": {"bound": "hbm", "kernel": k_gu, "achieved": round(gu_gbs, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(gu_gbs / HBM_PEAK_GBS, 4), "traffic": None,
                      "bytes_per_launch": gu_bytes, "avg_launch_ms": round(ms_gu, 5),
                      "down_gbs": round(dn_gbs, 1)},

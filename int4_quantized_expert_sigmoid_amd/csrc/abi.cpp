@@ -81,7 +81,7 @@ int status(hipError_t e) { return e == hipSuccess ? COLI_OK : COLI_EDEVICE; }
 // (not grouped).
 int format_ok(const coli_moe_layer &L, int path)
 {
-    if ((L.weight_bits == 8 || L.weight_bits == 2 || L.group_size != 0) && path != 0)
+    if ((L.weight_bits == 2 || L.group_size != 0) && path != 0)   // int4 and int8 have grouped kernels
         return COLI_EUNSUPPORTED;
     return COLI_OK;
 }
@@ -427,9 +427,6 @@ int coli_dense_forward(const coli_dense_mlp *M, const float *x, const float *gam
     const WsLayout lay = make_dense_layout(*M, T);
     if (ws_bytes < lay.total) return COLI_EWORKSPACE;
     const bool grouped = (flags & COLI_PATH_GROUPED) || (!(flags & COLI_PATH_GEMV) && T > COLI_GEMV_MAX_T);
-    // int8 weights have no grouped kernels: larger batches take the token-GEMV
-    // kernels in chunks of 8 tokens (each chunk reads the weights once)
-    if ((flags & COLI_PATH_GROUPED) && M->weight_bits == 8) return COLI_EUNSUPPORTED;
     hipStream_t s = (hipStream_t)stream;
     char *base = static_cast<char *>(ws);
     const bool acc = (flags & COLI_ACCUMULATE) != 0;
@@ -442,18 +439,11 @@ int coli_dense_forward(const coli_dense_mlp *M, const float *x, const float *gam
                         true, s) != hipSuccess)
         return COLI_EDEVICE;
     if (!grouped) return status(launch_dense_gemv(*M, T, 0, lay, base, y, acc, s));
-    if (M->weight_bits == 8) {
-        for (int t0 = 0; t0 < T; t0 += COLI_GEMV_MAX_T) {
-            const int tc = T - t0 < COLI_GEMV_MAX_T ? T - t0 : COLI_GEMV_MAX_T;
-            if (launch_dense_gemv(*M, tc, t0, lay, base, y, acc, s) != hipSuccess) return COLI_EDEVICE;
-        }
-        return COLI_OK;
-    }
     // one expert holding every token on the grouped kernels of the expert path
     coli_moe_layer L;
     std::memset(&L, 0, sizeof(L));
     L.H = M->H; L.I = M->I; L.E = 1; L.top_k = 1; L.n_group = 1; L.topk_group = 1; L.has_shared = 0;
-    L.route_scale = 1.0f; L.weight_bits = 4;
+    L.route_scale = 1.0f; L.weight_bits = M->weight_bits == 8 ? 8 : 4;
     L.gate_q = M->gate_q; L.up_q = M->up_q; L.down_q = M->down_q;
     L.gate_s = M->gate_s; L.up_s = M->up_s; L.down_s = M->down_s;
     WsLayout gl = lay;

@@ -124,11 +124,24 @@ __device__ __forceinline__ void split_pair(uint4 w, uint2 &A, uint2 &B)
 // The weight rows of a wave are its own (single buffer); the activation
 // rows are shared by the workgroup's waves (double buffer, one barrier per
 // stage).
-constexpr int KS = 8;
-constexpr int XC = 2 * KS;     // 16-byte activation chunks per pair and stage
+//
+// int8 weights (WB = 8) store every block as two 16-byte halves, all first
+// halves of a row and then all second halves (the activations' reordered
+// 8-groups 0-1 and 2-3), and need no unpack. Their stages hold KS = 4
+// blocks: a row's 8 LDS chunks are the 4 first halves, then the 4 second
+// halves (two 64-byte runs of the row), and a pair's activations are 128
+// bytes, whose chunk c sits at c ^ ((p >> 1) & 7) so that 16 pairs' reads of
+// one column still touch 16 different bank groups.
+template <int WB> struct Stage;
+template <> struct Stage<4> { static constexpr int KS = 8; };
+template <> struct Stage<8> { static constexpr int KS = 4; };
+constexpr int WCH = 8;         // 16-byte weight chunks per row and stage (both formats)
+
+template <int WB> constexpr int stage_blocks() { return Stage<WB>::KS; }
+template <int WB> constexpr int stage_xc() { return 2 * Stage<WB>::KS; }   // 16-byte activation chunks per pair and stage
 
 __device__ __forceinline__ int wsw(int n) { return (n >> 1) & 7; }
-__device__ __forceinline__ int xsw(int p) { return p & 15; }
+template <int WB> __device__ __forceinline__ int xsw(int p) { return WB == 4 ? (p & 15) : ((p >> 1) & 7); }
 
 // Staged data is held in clang vector types: plain loads and stores (copies
 // of the HIP vector structs become memcpys that keep a stage in scratch).
@@ -136,11 +149,11 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 
 typedef double v2d __attribute__((ext_vector_type(2)));
 
-template <int NM>
+template <int NM, int WB>
 struct StageLds {
-    v4i w[WAVES][NM][QK][KS];
-    v4i x[2][TILE_N][XC];
-    v2d d[2][KS / 2][TILE_N];      // f64 factors d_b/16 of the stage's block pairs (0 past the tile's pairs), pair-minor
+    v4i w[WAVES][NM][QK][WCH];
+    v4i x[2][TILE_N][stage_xc<WB>()];
+    v2d d[2][stage_blocks<WB>() / 2][TILE_N];   // f64 block factors of the stage's block pairs (0 past the tile's pairs), pair-minor
 };
 
 __device__ __forceinline__ uint4 as_u4(v4i v) { return make_uint4((uint32_t)v[0], (uint32_t)v[1], (uint32_t)v[2], (uint32_t)v[3]); }
@@ -148,27 +161,42 @@ __device__ __forceinline__ int4 as_i4(v4i v) { return make_int4(v[0], v[1], v[2]
 
 // Loads of stage s. Rows past the matrix end are never touched (waves
 // without rows skip the weight loads); blocks past nblk are clamped to the
-// last block (their products are never added).
+// last block (their products are never added). Lane l loads chunk l % 8 of
+// rows l/8, l/8 + 8, ...: int4, block l % 8 of the stage; int8, half
+// (l % 8) / 4 of block l % 4 (rowb: bytes per row).
+template <int WB>
 __device__ __forceinline__ void load_w(v4i (&w)[4], int s, int nblk, const uint8_t *wrow, long rowb)
 {
-    const int blk = min(s * KS + (threadIdx.x & 7), nblk - 1);
+    constexpr int KS = stage_blocks<WB>();
+    const int c = threadIdx.x & 7;
+    const int blk = min(s * KS + (WB == 4 ? c : (c & 3)), nblk - 1);
+    const long off = WB == 4 ? 16 * blk : (c >> 2) * (rowb / 2) + 16 * blk;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) w[j] = *reinterpret_cast<const v4i *>(wrow + (long)(8 * j) * rowb + 16 * blk);
+    for (int j = 0; j < 4; ++j) w[j] = *reinterpret_cast<const v4i *>(wrow + (long)(8 * j) * rowb + off);
 }
 
-__device__ __forceinline__ void load_x(v4i (&x)[2], int s, int nblk, const int8_t *const (&xrow)[2])
+// Activation loads: 2 * KS lanes per pair row (16-byte chunk c of the
+// stage: block c/2, half c%2), 64 / (2 * KS) pairs per load instruction.
+template <int WB> constexpr int x_loads() { return stage_xc<WB>() / 8; }   // per wave and stage: 2 (int4), 1 (int8)
+
+template <int WB>
+__device__ __forceinline__ void load_x(v4i (&x)[x_loads<WB>()], int s, int nblk, const int8_t *const (&xrow)[x_loads<WB>()])
 {
-    const int c = threadIdx.x & 15;
+    constexpr int KS = stage_blocks<WB>(), XC = stage_xc<WB>();
+    const int c = threadIdx.x & (XC - 1);
     const int xb = min(s * KS + (c >> 1), nblk - 1);
 #pragma unroll
-    for (int i = 0; i < 2; ++i) x[i] = *reinterpret_cast<const v4i *>(xrow[i] + 32 * xb + 16 * (c & 1));
+    for (int i = 0; i < x_loads<WB>(); ++i) x[i] = *reinterpret_cast<const v4i *>(xrow[i] + 32 * xb + 16 * (c & 1));
 }
 
-// Wave 0 loads the tile's scales: lane l, pair l/2, blocks 4*(l&1).. of the
-// stage (a 16-byte load when 4 | nblk, clamped in bounds).
+// Wave 0 loads the tile's scales, 4 blocks per lane: int4, pair l/2 and
+// blocks 4*(l&1).. of the stage; int8, pair l (lanes 0-31). A 16-byte load
+// when 4 | nblk, clamped in bounds.
+template <int WB>
 __device__ __forceinline__ v4f load_d(int s, int nblk, const float *drow, bool vec_scales)
 {
-    const int b = s * KS + 4 * (threadIdx.x & 1);
+    constexpr int KS = stage_blocks<WB>();
+    const int b = s * KS + (WB == 4 ? 4 * (threadIdx.x & 1) : 0);
     if (vec_scales) return *reinterpret_cast<const v4f *>(drow + min(b, nblk - 4));
     v4f d;
 #pragma unroll
@@ -176,8 +204,8 @@ __device__ __forceinline__ v4f load_d(int s, int nblk, const float *drow, bool v
     return d;
 }
 
-template <int NM>
-__device__ __forceinline__ void store_w(StageLds<NM> &sm, int m, const v4i (&w)[4])
+template <int NM, int WB>
+__device__ __forceinline__ void store_w(StageLds<NM, WB> &sm, int m, const v4i (&w)[4])
 {
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int r8 = lane >> 3;
@@ -185,42 +213,51 @@ __device__ __forceinline__ void store_w(StageLds<NM> &sm, int m, const v4i (&w)[
     for (int j = 0; j < 4; ++j) sm.w[wave][m][8 * j + r8][(lane & 7) ^ wsw(8 * j + r8)] = w[j];
 }
 
-template <int NM>
-__device__ __forceinline__ void store_x(StageLds<NM> &sm, int buf, const v4i (&x)[2])
+template <int NM, int WB>
+__device__ __forceinline__ void store_x(StageLds<NM, WB> &sm, int buf, const v4i (&x)[x_loads<WB>()])
 {
+    constexpr int XC = stage_xc<WB>();
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int p = 8 * wave + 4 * i + (lane >> 4);
-        sm.x[buf][p][(lane & 15) ^ xsw(p)] = x[i];
+    for (int i = 0; i < x_loads<WB>(); ++i) {
+        const int p = 8 * wave + (64 / XC) * i + lane / XC;
+        sm.x[buf][p][(lane & (XC - 1)) ^ xsw<WB>(p)] = x[i];
     }
 }
 
-// Scales are staged as the f64 factors the rescale multiplies by, d_b/16
-// (the nibble trick's x16 undone, exact), and 0 for pairs past the tile's
-// np, so the MFMA loops do no conversions. Kept pair-minor: the lanes
-// reading one block pair's factors read contiguous bytes.
-template <int NM>
-__device__ __forceinline__ void store_d(StageLds<NM> &sm, int buf, v4f d, int np)
+// Scales are staged as the f64 factors the rescale multiplies by: d_b/16
+// for int4 (the nibble trick's x16 undone, exact), d_b for int8, and 0 for
+// pairs past the tile's np, so the MFMA loops do no conversions. Kept
+// pair-minor: the lanes reading one block pair's factors read contiguous
+// bytes.
+template <int WB>
+__device__ __forceinline__ int d_pair(int lane) { return WB == 4 ? (lane >> 1) : lane; }
+
+template <int NM, int WB>
+__device__ __forceinline__ void store_d(StageLds<NM, WB> &sm, int buf, v4f d, int np)
 {
-    const int p = (threadIdx.x & 63) >> 1, jp = 2 * (threadIdx.x & 1);
-    const double v = p < np ? 0.0625 : 0.0;
+    const int lane = threadIdx.x & 63;
+    const int p = d_pair<WB>(lane), jp = WB == 4 ? 2 * (lane & 1) : 0;
+    if (p >= TILE_N) return;                     // int8: lanes 32-63 stage nothing
+    const double v = p < np ? (WB == 4 ? 0.0625 : 1.0) : 0.0;
     sm.d[buf][jp][p] = v2d{(double)d[0] * v, (double)d[1] * v};
     sm.d[buf][jp + 1][p] = v2d{(double)d[2] * v, (double)d[3] * v};
 }
 
 // Factors of blocks j and j+1 (j even) of the stage for pair n.
-template <int NM>
-__device__ __forceinline__ v2d read_d2(const StageLds<NM> &sm, int buf, int n, int j)
+template <int NM, int WB>
+__device__ __forceinline__ v2d read_d2(const StageLds<NM, WB> &sm, int buf, int n, int j)
 {
     return sm.d[buf][j >> 1][n];
 }
 
 // Global row of this wave's share of the tile's activation loads (pair
-// 8*wave + 4*i + lane/16; pairs past np read the tile's first pair).
+// 8*wave + (64/XC)*i + lane/XC; pairs past np read the tile's first pair).
+template <int WB>
 __device__ __forceinline__ int stage_pair(int i, int np)
 {
-    const int p = 8 * (threadIdx.x >> 6) + 4 * i + ((threadIdx.x & 63) >> 4);
+    constexpr int XC = stage_xc<WB>();
+    const int p = 8 * (threadIdx.x >> 6) + (64 / XC) * i + (threadIdx.x & 63) / XC;
     return p < np ? p : 0;
 }
 
@@ -257,18 +294,53 @@ __device__ __forceinline__ long unpack4(uint32_t w)
     return (long)(((unsigned long long)(w & m) << 32) | (unsigned long long)((w << 4) & m));
 }
 
-// One matrix over the stage's blocks, adding every block's int32 results
-// times d_b/16 (f64) into acc. m: the matrix's LDS slot; buf: the stage's
-// activation buffer; b0: its first block.
-template <bool FULL, bool NARROW, int NM>
-__device__ __forceinline__ void stage_pass(const StageLds<NM> &sm, int m, double (&acc)[TileShape<NARROW>::NACC], int buf,
-                                           int b0, int nblk)
+// The 16 bytes of block j (of the stage) that lane half `half` multiplies,
+// as the 32x32x32 MFMA's operand, for blocks j and j+1: int4 chunks hold a
+// whole block (one permlane swap hands each half its 8 packed bytes of both,
+// then the nibbles are unpacked x16); int8 chunks hold one half of a block.
+template <int NM, int WB>
+__device__ __forceinline__ void w_pair(const StageLds<NM, WB> &sm, int wave, int m, int n, int half, int sw, int j,
+                                       v4i &a, v4i &b)
 {
+    if constexpr (WB == 4) {
+        const uint4 wp = as_u4(sm.w[wave][m][n][(j + half) ^ sw]);
+        uint2 wa, wb;
+        split_pair(wp, wa, wb);
+        a = unpack8(wa);
+        b = unpack8(wb);
+    } else {
+        a = sm.w[wave][m][n][(4 * half + j) ^ sw];
+        b = sm.w[wave][m][n][(4 * half + j + 1) ^ sw];
+    }
+}
+
+// The 8 bytes of 8-group q of block blk for row r, as the 16x16x32 MFMA's
+// operand: int4, the packed dword of the group unpacked x16; int8, the
+// group's bytes in the block's half q/2.
+template <int NM, int WB>
+__device__ __forceinline__ long w_group(const StageLds<NM, WB> &sm, int wave, int m, int r, int sw, int blk, int q)
+{
+    const char *row = reinterpret_cast<const char *>(&sm.w[wave][m][r][0]);
+    if constexpr (WB == 4) {
+        return unpack4(*reinterpret_cast<const uint32_t *>(row + 16 * (blk ^ sw) + 4 * q));
+    } else {
+        return *reinterpret_cast<const long *>(row + 16 * ((4 * (q >> 1) + blk) ^ sw) + 8 * (q & 1));
+    }
+}
+
+// One matrix over the stage's blocks, adding every block's int32 results
+// times its f64 factor into acc. m: the matrix's LDS slot; buf: the stage's
+// activation buffer; b0: its first block.
+template <bool FULL, bool NARROW, int NM, int WB>
+__device__ __forceinline__ void stage_pass(const StageLds<NM, WB> &sm, int m, double (&acc)[TileShape<NARROW>::NACC],
+                                           int buf, int b0, int nblk)
+{
+    constexpr int KS = stage_blocks<WB>();
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     if constexpr (!NARROW) {
         const v16i zero = {};
         const int n = lane & 31, half = lane >> 5;
-        const int sw = wsw(n), sx = xsw(n);
+        const int sw = wsw(n), sx = xsw<WB>(n);
         // Both MFMAs of a block pair are issued before either result is
         // rescaled: the second runs on the matrix core while the vector
         // unit converts and accumulates the first.
@@ -276,13 +348,11 @@ __device__ __forceinline__ void stage_pass(const StageLds<NM> &sm, int m, double
         for (int j = 0; j < KS; j += 2) {
             if (!FULL && b0 + j >= nblk) break;          // uniform: the stage's valid blocks
             const bool two = FULL || b0 + j + 1 < nblk;
-            const uint4 wp = as_u4(sm.w[wave][m][n][(j + half) ^ sw]);
+            v4i ua, ub;
+            w_pair<NM, WB>(sm, wave, m, n, half, sw, j, ua, ub);
             const int4 x0 = as_i4(sm.x[buf][n][(2 * j + half) ^ sx]);
             const int4 x1 = as_i4(sm.x[buf][n][(2 * j + 2 + half) ^ sx]);
-            const v2d dd = read_d2<NM>(sm, buf, n, j);
-            uint2 wa, wb;
-            split_pair(wp, wa, wb);
-            const v4i ua = unpack8(wa), ub = unpack8(wb);
+            const v2d dd = read_d2<NM, WB>(sm, buf, n, j);
             const v16i ca = __builtin_amdgcn_mfma_i32_32x32x32_i8(ua, v4i{x0.x, x0.y, x0.z, x0.w}, zero, 0, 0, 0);
             const v16i cb = two ? __builtin_amdgcn_mfma_i32_32x32x32_i8(ub, v4i{x1.x, x1.y, x1.z, x1.w}, zero, 0, 0, 0)
                                 : zero;
@@ -296,7 +366,7 @@ __device__ __forceinline__ void stage_pass(const StageLds<NM> &sm, int m, double
     } else {
         const v4i zero = {};
         const int pr = lane & 15, q = lane >> 4;
-        const int sx = xsw(pr);
+        const int sx = xsw<WB>(pr);
         const int r0 = pr, r1 = pr + 16;                 // the lane's weight rows of the two MFMAs
         const int sw0 = wsw(r0), sw1 = wsw(r1);
         // the four MFMAs of a block pair are issued before any result is
@@ -305,7 +375,7 @@ __device__ __forceinline__ void stage_pass(const StageLds<NM> &sm, int m, double
         for (int j = 0; j < KS; j += 2) {
             if (!FULL && b0 + j >= nblk) break;
             const bool two = FULL || b0 + j + 1 < nblk;
-            const v2d dd = read_d2<NM>(sm, buf, pr, j);
+            const v2d dd = read_d2<NM, WB>(sm, buf, pr, j);
             v4i c[2][2];
 #pragma unroll
             for (int jj = 0; jj < 2; ++jj) {
@@ -317,12 +387,8 @@ __device__ __forceinline__ void stage_pass(const StageLds<NM> &sm, int m, double
                 }
                 const char *xr = reinterpret_cast<const char *>(&sm.x[buf][pr][(2 * blk + (q >> 1)) ^ sx]);
                 const long B = *reinterpret_cast<const long *>(xr + 8 * (q & 1));
-                const uint32_t w0 = *reinterpret_cast<const uint32_t *>(
-                    reinterpret_cast<const char *>(&sm.w[wave][m][r0][blk ^ sw0]) + 4 * q);
-                const uint32_t w1 = *reinterpret_cast<const uint32_t *>(
-                    reinterpret_cast<const char *>(&sm.w[wave][m][r1][blk ^ sw1]) + 4 * q);
-                c[jj][0] = __builtin_amdgcn_mfma_i32_16x16x32_i8(unpack4(w0), B, zero, 0, 0, 0);
-                c[jj][1] = __builtin_amdgcn_mfma_i32_16x16x32_i8(unpack4(w1), B, zero, 0, 0, 0);
+                c[jj][0] = __builtin_amdgcn_mfma_i32_16x16x32_i8(w_group<NM, WB>(sm, wave, m, r0, sw0, blk, q), B, zero, 0, 0, 0);
+                c[jj][1] = __builtin_amdgcn_mfma_i32_16x16x32_i8(w_group<NM, WB>(sm, wave, m, r1, sw1, blk, q), B, zero, 0, 0, 0);
             }
 #pragma unroll
             for (int jj = 0; jj < 2; ++jj) {
@@ -341,20 +407,21 @@ __device__ __forceinline__ void stage_pass(const StageLds<NM> &sm, int m, double
 // need no bounds tests and the scheduler sees a stage as straight-line code
 // (held to 3 waves per SIMD, the occupancy of the general form: about 2%
 // faster at the GLM prefill shape).
-template <bool FULL, bool NARROW>
-__device__ __forceinline__ void gateup_tile(const GroupedArgs &a, StageLds<2> &sm, int e, int p0, int np, int rt,
+template <bool FULL, bool NARROW, int WB>
+__device__ __forceinline__ void gateup_tile(const GroupedArgs &a, StageLds<2, WB> &sm, int e, int p0, int np, int rt,
                                             bool rows_ok)
 {
-    constexpr int NACC = TileShape<NARROW>::NACC;
+    constexpr int NACC = TileShape<NARROW>::NACC, KS = stage_blocks<WB>(), NXL = x_loads<WB>();
     const int n_rt = a.I / QK;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int nblk = a.H / QK;
-    const long rowb = a.H / 2;
+    const long rowb = (long)a.H * WB / 8;
     const long wrow0 = (long)e * a.I + (long)min(rt, n_rt - 1) * QK + (lane >> 3);
     const uint8_t *const wrow[2] = {a.q_a + wrow0 * rowb, a.q_b + wrow0 * rowb};
-    const int8_t *const xrow[2] = {a.act + (long)a.pair_tok[p0 + stage_pair(0, np)] * a.H,
-                                   a.act + (long)a.pair_tok[p0 + stage_pair(1, np)] * a.H};
-    const int pd = (lane >> 1) < np ? (lane >> 1) : 0;
+    const int8_t *xrow[NXL];
+#pragma unroll
+    for (int i = 0; i < NXL; ++i) xrow[i] = a.act + (long)a.pair_tok[p0 + stage_pair<WB>(i, np)] * a.H;
+    const int pd = min(d_pair<WB>(lane), TILE_N - 1) < np ? min(d_pair<WB>(lane), TILE_N - 1) : 0;
     const float *drow = a.act_s + (long)a.pair_tok[p0 + pd] * nblk;   // used by wave 0
     const bool vec_scales = nblk % 4 == 0;
 
@@ -366,36 +433,41 @@ __device__ __forceinline__ void gateup_tile(const GroupedArgs &a, StageLds<2> &s
     // activations load during the gate pass, its up rows during the up pass,
     // so only one matrix's stage is ever held in registers.
     const int nst = (nblk + KS - 1) / KS;
-    v4i wn[4], xn[2];
+    v4i wn[4], xn[NXL];
     v4f dn = {};
-    load_x(xn, 0, nblk, xrow);
-    if (wave == 0) dn = load_d(0, nblk, drow, vec_scales);
-    if (rows_ok) { load_w(wn, 0, nblk, wrow[0], rowb); store_w<2>(sm, 0, wn); load_w(wn, 0, nblk, wrow[1], rowb); store_w<2>(sm, 1, wn); }
-    store_x<2>(sm, 0, xn);
-    if (wave == 0) store_d<2>(sm, 0, dn, np);
+    load_x<WB>(xn, 0, nblk, xrow);
+    if (wave == 0) dn = load_d<WB>(0, nblk, drow, vec_scales);
+    if (rows_ok) {
+        load_w<WB>(wn, 0, nblk, wrow[0], rowb);
+        store_w<2, WB>(sm, 0, wn);
+        load_w<WB>(wn, 0, nblk, wrow[1], rowb);
+        store_w<2, WB>(sm, 1, wn);
+    }
+    store_x<2, WB>(sm, 0, xn);
+    if (wave == 0) store_d<2, WB>(sm, 0, dn, np);
     __syncthreads();
     for (int s = 0; s < nst; ++s) {
         const bool more = s + 1 < nst;
         const int buf = s & 1, b0 = s * KS;
         if (more) {
-            load_x(xn, s + 1, nblk, xrow);
-            if (wave == 0) dn = load_d(s + 1, nblk, drow, vec_scales);
-            if (rows_ok) load_w(wn, s + 1, nblk, wrow[0], rowb);
+            load_x<WB>(xn, s + 1, nblk, xrow);
+            if (wave == 0) dn = load_d<WB>(s + 1, nblk, drow, vec_scales);
+            if (rows_ok) load_w<WB>(wn, s + 1, nblk, wrow[0], rowb);
         }
         issue_fence();
-        if (rows_ok) stage_pass<FULL, NARROW, 2>(sm, 0, acc_g, buf, b0, nblk);
+        if (rows_ok) stage_pass<FULL, NARROW, 2, WB>(sm, 0, acc_g, buf, b0, nblk);
         issue_fence();
         if (more && rows_ok) {
-            store_w<2>(sm, 0, wn);
-            load_w(wn, s + 1, nblk, wrow[1], rowb);
+            store_w<2, WB>(sm, 0, wn);
+            load_w<WB>(wn, s + 1, nblk, wrow[1], rowb);
         }
         issue_fence();
-        if (rows_ok) stage_pass<FULL, NARROW, 2>(sm, 1, acc_u, buf, b0, nblk);
+        if (rows_ok) stage_pass<FULL, NARROW, 2, WB>(sm, 1, acc_u, buf, b0, nblk);
         issue_fence();
         if (more) {
-            if (rows_ok) store_w<2>(sm, 1, wn);
-            store_x<2>(sm, (s + 1) & 1, xn);
-            if (wave == 0) store_d<2>(sm, (s + 1) & 1, dn, np);
+            if (rows_ok) store_w<2, WB>(sm, 1, wn);
+            store_x<2, WB>(sm, (s + 1) & 1, xn);
+            if (wave == 0) store_d<2, WB>(sm, (s + 1) & 1, dn, np);
         }
         __syncthreads();
     }
@@ -428,10 +500,10 @@ __device__ __forceinline__ void gateup_tile(const GroupedArgs &a, StageLds<2> &s
     if (lane < TileShape<NARROW>::NPAIR) a.hs[(long)(p0 + n) * n_rt + rt] = d;
 }
 
-template <bool FULL>
+template <bool FULL, int WB>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) k_gateup_mfma(GroupedArgs a)
 {
-    __shared__ StageLds<2> sm;
+    __shared__ StageLds<2, WB> sm;
     const int n_rt = a.I / QK;
     const int nrg = (n_rt + WAVES - 1) / WAVES;
     int tile, rg;
@@ -443,24 +515,25 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) k
     const int2 td = a.tiles[tile];
     const int e = td.x, p0 = td.y;
     const int np = min(TILE_N, a.expert_off[e + 1] - p0);
-    if (np <= 16) gateup_tile<FULL, true>(a, sm, e, p0, np, rt, rows_ok);
-    else gateup_tile<FULL, false>(a, sm, e, p0, np, rt, rows_ok);
+    if (np <= 16) gateup_tile<FULL, true, WB>(a, sm, e, p0, np, rt, rows_ok);
+    else gateup_tile<FULL, false, WB>(a, sm, e, p0, np, rt, rows_ok);
 }
 
-template <bool NARROW>
-__device__ __forceinline__ void down_tile(const GroupedArgs &a, StageLds<1> &sm, int e, int p0, int np, int rt,
+template <bool NARROW, int WB>
+__device__ __forceinline__ void down_tile(const GroupedArgs &a, StageLds<1, WB> &sm, int e, int p0, int np, int rt,
                                           bool rows_ok)
 {
-    constexpr int NACC = TileShape<NARROW>::NACC;
+    constexpr int NACC = TileShape<NARROW>::NACC, KS = stage_blocks<WB>(), NXL = x_loads<WB>();
     const int n_rt = a.H / QK;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int nblk = a.I / QK;
-    const long rowb = a.I / 2;
+    const long rowb = (long)a.I * WB / 8;
     const long wrow0 = (long)e * a.H + (long)min(rt, n_rt - 1) * QK + (lane >> 3);
     const uint8_t *wrow = a.q_a + wrow0 * rowb;
-    const int8_t *const xrow[2] = {a.act + (long)(p0 + stage_pair(0, np)) * a.I,
-                                   a.act + (long)(p0 + stage_pair(1, np)) * a.I};
-    const int pd = (lane >> 1) < np ? (lane >> 1) : 0;
+    const int8_t *xrow[NXL];
+#pragma unroll
+    for (int i = 0; i < NXL; ++i) xrow[i] = a.act + (long)(p0 + stage_pair<WB>(i, np)) * a.I;
+    const int pd = min(d_pair<WB>(lane), TILE_N - 1) < np ? min(d_pair<WB>(lane), TILE_N - 1) : 0;
     const float *drow = a.act_s + (long)(p0 + pd) * nblk;             // used by wave 0
     const bool vec_scales = nblk % 4 == 0;
 
@@ -469,28 +542,28 @@ __device__ __forceinline__ void down_tile(const GroupedArgs &a, StageLds<1> &sm,
     for (int i = 0; i < NACC; ++i) acc[i] = 0.0;
 
     const int nst = (nblk + KS - 1) / KS;
-    v4i wn[4], xn[2];
+    v4i wn[4], xn[NXL];
     v4f dn = {};
-    load_x(xn, 0, nblk, xrow);
-    if (wave == 0) dn = load_d(0, nblk, drow, vec_scales);
-    if (rows_ok) { load_w(wn, 0, nblk, wrow, rowb); store_w<1>(sm, 0, wn); }
-    store_x<1>(sm, 0, xn);
-    if (wave == 0) store_d<1>(sm, 0, dn, np);
+    load_x<WB>(xn, 0, nblk, xrow);
+    if (wave == 0) dn = load_d<WB>(0, nblk, drow, vec_scales);
+    if (rows_ok) { load_w<WB>(wn, 0, nblk, wrow, rowb); store_w<1, WB>(sm, 0, wn); }
+    store_x<1, WB>(sm, 0, xn);
+    if (wave == 0) store_d<1, WB>(sm, 0, dn, np);
     __syncthreads();
     for (int s = 0; s < nst; ++s) {
         const bool more = s + 1 < nst;
         if (more) {
-            load_x(xn, s + 1, nblk, xrow);
-            if (wave == 0) dn = load_d(s + 1, nblk, drow, vec_scales);
-            if (rows_ok) load_w(wn, s + 1, nblk, wrow, rowb);
+            load_x<WB>(xn, s + 1, nblk, xrow);
+            if (wave == 0) dn = load_d<WB>(s + 1, nblk, drow, vec_scales);
+            if (rows_ok) load_w<WB>(wn, s + 1, nblk, wrow, rowb);
         }
         issue_fence();
-        if (rows_ok) stage_pass<false, NARROW, 1>(sm, 0, acc, s & 1, s * KS, nblk);
+        if (rows_ok) stage_pass<false, NARROW, 1, WB>(sm, 0, acc, s & 1, s * KS, nblk);
         issue_fence();
         if (more) {
-            if (rows_ok) store_w<1>(sm, 0, wn);
-            store_x<1>(sm, (s + 1) & 1, xn);
-            if (wave == 0) store_d<1>(sm, (s + 1) & 1, dn, np);
+            if (rows_ok) store_w<1, WB>(sm, 0, wn);
+            store_x<1, WB>(sm, (s + 1) & 1, xn);
+            if (wave == 0) store_d<1, WB>(sm, (s + 1) & 1, dn, np);
         }
         __syncthreads();
     }
@@ -504,9 +577,10 @@ __device__ __forceinline__ void down_tile(const GroupedArgs &a, StageLds<1> &sm,
     for (int i = 0; i < NACC; ++i) a.ye[base + acc_row<NARROW>(i, lane)] = (float)((double)rs[i] * acc[i]);
 }
 
+template <int WB>
 __global__ void __launch_bounds__(256) k_down_mfma(GroupedArgs a)
 {
-    __shared__ StageLds<1> sm;
+    __shared__ StageLds<1, WB> sm;
     const int n_rt = a.H / QK;
     const int nrg = (n_rt + WAVES - 1) / WAVES;
     int tile, rg;
@@ -518,8 +592,8 @@ __global__ void __launch_bounds__(256) k_down_mfma(GroupedArgs a)
     const int2 td = a.tiles[tile];
     const int e = td.x, p0 = td.y;
     const int np = min(TILE_N, a.expert_off[e + 1] - p0);
-    if (np <= 16) down_tile<true>(a, sm, e, p0, np, rt, rows_ok);
-    else down_tile<false>(a, sm, e, p0, np, rt, rows_ok);
+    if (np <= 16) down_tile<true, WB>(a, sm, e, p0, np, rt, rows_ok);
+    else down_tile<false, WB>(a, sm, e, p0, np, rt, rows_ok);
 }
 
 GroupedArgs make_args(const WsLayout &lay, char *ws, const coli_moe_layer &L)
@@ -554,8 +628,14 @@ hipError_t launch_gateup_grouped(const coli_moe_layer &L, int T, const WsLayout 
     a.act_s = reinterpret_cast<const float *>(ws + lay.xs);
     const int nrg = (L.I / QK + WAVES - 1) / WAVES;
     const dim3 grid((unsigned)(max_tiles(lay, L) * nrg));
-    if ((L.H / QK) % KS == 0) COLI_LAUNCH(k_gateup_mfma<true>, grid, dim3(64 * WAVES), 0, s, a);
-    else COLI_LAUNCH(k_gateup_mfma<false>, grid, dim3(64 * WAVES), 0, s, a);
+    const int nblk = L.H / QK;
+    if (L.weight_bits == 8) {
+        if (nblk % stage_blocks<8>() == 0) COLI_LAUNCH((k_gateup_mfma<true, 8>), grid, dim3(64 * WAVES), 0, s, a);
+        else COLI_LAUNCH((k_gateup_mfma<false, 8>), grid, dim3(64 * WAVES), 0, s, a);
+    } else {
+        if (nblk % stage_blocks<4>() == 0) COLI_LAUNCH((k_gateup_mfma<true, 4>), grid, dim3(64 * WAVES), 0, s, a);
+        else COLI_LAUNCH((k_gateup_mfma<false, 4>), grid, dim3(64 * WAVES), 0, s, a);
+    }
     return hipGetLastError();
 }
 
@@ -568,7 +648,9 @@ hipError_t launch_down_grouped(const coli_moe_layer &L, int T, const WsLayout &l
     a.act = reinterpret_cast<const int8_t *>(ws + lay.hq);
     a.act_s = reinterpret_cast<const float *>(ws + lay.hs);
     const int nrg = (L.H / QK + WAVES - 1) / WAVES;
-    COLI_LAUNCH(k_down_mfma, dim3((unsigned)(max_tiles(lay, L) * nrg)), dim3(64 * WAVES), 0, s, a);
+    const dim3 grid((unsigned)(max_tiles(lay, L) * nrg));
+    if (L.weight_bits == 8) COLI_LAUNCH(k_down_mfma<8>, grid, dim3(64 * WAVES), 0, s, a);
+    else COLI_LAUNCH(k_down_mfma<4>, grid, dim3(64 * WAVES), 0, s, a);
     return hipGetLastError();
 }
 

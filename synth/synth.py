@@ -215,6 +215,9 @@ WORKLOADS = {
                                   TokenSpec(T=1, outlier_channels=61)),
     "glm52_int8_T4": Workload("glm52_int8_T4", replace(GLM52, weight_bits=8),
                               TokenSpec(T=4, rho=0.8, outlier_channels=61)),
+    # the Zipf prefill batch on int8 experts (the grouped int8-MFMA kernels)
+    "glm52_int8_prefill_T512": Workload("glm52_int8_prefill_T512", replace(GLM52, zipf_s=1.1, weight_bits=8),
+                                        TokenSpec(T=512, outlier_channels=61)),
     # the scale-granularity variant: int4 codes with one f32 scale per group of
     # 32 (or 128) columns instead of one per row (scale bytes +25% / +6%)
     "glm52_g32_decode_T1": Workload("glm52_g32_decode_T1", replace(GLM52, group_size=32),
@@ -264,7 +267,7 @@ GLM52_DENSE = DenseSpec(H=6144, I=12288, w_outlier_rate=0.001)
 DENSE_WORKLOADS = {
     "glm52_dense_T1": DenseWorkload("glm52_dense_T1", GLM52_DENSE, TokenSpec(T=1, outlier_channels=61)),
     "glm52_dense_T4": DenseWorkload("glm52_dense_T4", GLM52_DENSE, TokenSpec(T=4, rho=0.8, outlier_channels=61)),
-    # a 64-token prefill chunk through an int8 dense layer: eight 8-token GEMV passes
+    # a 64-token prefill chunk through an int8 dense layer (the grouped int8-MFMA kernels)
     "glm52_dense_T64": DenseWorkload("glm52_dense_T64", GLM52_DENSE, TokenSpec(T=64, outlier_channels=61)),
 }
 

@@ -191,17 +191,19 @@ def test_host_packer_matches_oracle_packer():
     assert np.array_equal(q, qo) and np.array_equal(s, so)
 
 
-def test_int8_experts_only_on_the_gemv_path():
-    """int8 experts run on the token-GEMV path; larger batches are refused
-    before any launch (COLI_EUNSUPPORTED), routing is not."""
+def test_int8_experts_take_both_paths():
+    """int8 experts have token-GEMV and grouped kernels: the layout of a
+    large or forced-grouped batch is the grouped one, as for int4 (no launch
+    here: the pointers are dummies)."""
     L = fake_layer(weight_bits=8)
-    p = ctypes.c_void_p(1 << 20)
-    F = lib().coli_moe_forward
-    assert ws_bytes(L, 4) > 0
-    assert F(ctypes.byref(L), p, 9, p, 0, p, 1 << 40, None) == _lib.COLI_EUNSUPPORTED      # grouped batch
-    assert F(ctypes.byref(L), p, 4, p, 4, p, 1 << 40, None) == _lib.COLI_EUNSUPPORTED      # forced grouped
-    X = lib().coli_moe_experts
-    assert X(ctypes.byref(L), p, p, p, p, 9, p, 0, p, 1 << 40, None) == _lib.COLI_EUNSUPPORTED
+    out = CWsLayout()
+    assert ws_bytes(L, 4) > 0 and ws_bytes(L, 512) == ws_bytes(fake_layer(), 512)
+    assert lib().coli_moe_workspace_layout(ctypes.byref(L), 512, 0, ctypes.byref(out)) == 0
+    assert out.path == 1
+    assert lib().coli_moe_workspace_layout(ctypes.byref(L), 4, _lib.COLI_PATH_GROUPED, ctypes.byref(out)) == 0
+    assert out.path == 1
+    assert lib().coli_moe_workspace_layout(ctypes.byref(L), 4, 0, ctypes.byref(out)) == 0
+    assert out.path == 0
 
 
 def test_group_scales_only_on_the_gemv_path():

@@ -1,6 +1,6 @@
 """GPU parity of the dense MLP (coli_dense_forward) through the C ABI against
-the oracle's O15, on both paths (token-GEMV for T <= 8, grouped MFMA above;
-int8 above 8 tokens on the token-GEMV kernels in chunks of 8),
+the oracle's O15, on both paths (token-GEMV for T <= 8, grouped MFMA above,
+for int4 and int8 weights),
 both weight formats, intermediate sizes below and above 256 blocks (for one
 token slot the down kernel then gives each thread a second block column, for
 more slots it adds waves), with the RMSNorm input and the residual added in
@@ -75,20 +75,13 @@ def test_dense_grouped_small(T, flags):
     check(SMALL, T, flags, token_set=20 + T)
 
 
-@pytest.mark.parametrize("T", [9, 16, 21])
-def test_dense_int8_chunked(T):
-    """int8 weights past 8 tokens: the token-GEMV kernels over chunks of 8
-    (a full chunk, full chunks only, a ragged last chunk), bit for bit the
-    oracle's O15 per token; an explicit grouped request is refused."""
+@pytest.mark.parametrize("T,flags", [(9, 0), (16, 0), (21, 0), (40, 0), (3, COLI_PATH_GROUPED)])
+def test_dense_int8_grouped(T, flags):
+    """int8 weights on the grouped int8-MFMA kernels (one expert holding
+    every token): past 8 tokens, and forced at T = 3."""
     from dataclasses import replace
-    from int4_quantized_expert_sigmoid_amd._lib import ColiError, COLI_EUNSUPPORTED
     spec = replace(SMALL, weight_bits=8)
-    y = check(spec, T, token_set=70 + T, accumulate=(T == 21))
-    M = device_dense(spec, 0, 0)
-    x = dev(S.tokens(S.TokenSpec(T=T, token_set=80 + T), spec.H, 0))
-    with pytest.raises(ColiError) as e:
-        api.dense_forward(M, x, api.dense_workspace(M, T), flags=COLI_PATH_GROUPED)
-    assert e.value.code == COLI_EUNSUPPORTED
+    check(spec, T, flags, token_set=70 + T, accumulate=(T == 21))
 
 
 def test_dense_paths_agree():

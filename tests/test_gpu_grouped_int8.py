@@ -1,0 +1,159 @@
+"""GPU parity of int8-weight experts on the grouped int8-MFMA path (T > 8)
+through the C ABI: tiny and odd-shaped layers in full (every token and
+pair; the odd shape runs part-filled stages and scales loaded one by one),
+the compute-bound case of full tiles, path invariance against the token-GEMV
+path, the cross-format identity on the grouped kernels (an int8 layer whose
+codes lie in [-8, 7] gives the int4 layer's outputs bit for bit), and the
+whole GLM-5.2-shaped Zipf prefill (T = 512) against the threaded oracle."""
+from dataclasses import replace
+
+import numpy as np
+import pytest
+import torch
+
+from int4_quantized_expert_sigmoid_amd import api, COLI_PATH_GEMV, COLI_PATH_GROUPED
+from int4_quantized_expert_sigmoid_amd.synthetic import device_layer
+from oracle import layers as OL
+from oracle import oracle as O
+from synth import synth as S
+
+from gpu_common import dev, rel_err, ws_views
+from test_gpu_grouped import _full_layer_check, _tiny_batch_check
+
+pytestmark = pytest.mark.gpu
+TOL = 1e-4
+TINY8 = replace(S.TINY, weight_bits=8)
+ODD8 = S.LayerSpec(H=320, I=96, E=16, top_k=4, weight_bits=8)
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    torch.cuda.set_device(0)
+
+
+@pytest.fixture(scope="module")
+def tiny8():
+    return device_layer(TINY8, 0, 0), OL.full_layer(TINY8, 0, 0)
+
+
+@pytest.mark.parametrize("T", [9, 64, 200])
+def test_grouped_int8_tiny_full_outputs(tiny8, T):
+    L, ref = tiny8
+    x = S.tokens(S.TokenSpec(T=T, token_set=900 + T), TINY8.H, 0)
+    ws = api.workspace(L, T)
+    say(f"grouped int8 tiny T={T}")
+    y = api.moe_forward(L, dev(x), ws).cpu().numpy()
+    _tiny_batch_check(TINY8, L, ref, x, ws, y, f"int8 tiny T={T}")
+
+
+@pytest.mark.parametrize("T", [9, 40, 77])
+def test_grouped_int8_odd_shape_full_outputs(T):
+    """H = 320 (10 blocks: a part-filled last stage of 4), I = 96 (3 row
+    tiles and 3 down blocks); neither block count is a multiple of 4, so the
+    scales load one by one."""
+    L, ref = device_layer(ODD8, 0, 0), OL.full_layer(ODD8, 0, 0)
+    x = S.tokens(S.TokenSpec(T=T, token_set=950 + T), ODD8.H, 0)
+    ws = api.workspace(L, T)
+    say(f"grouped int8 odd shape T={T}")
+    y = api.moe_forward(L, dev(x), ws).cpu().numpy()
+    _tiny_batch_check(ODD8, L, ref, x, ws, y, f"int8 odd T={T}")
+
+
+def test_grouped_int8_hot_experts_full_tiles():
+    spec = S.LayerSpec(H=256, I=128, E=16, top_k=2, hot_experts=2, weight_bits=8)
+    L, ref = device_layer(spec, 0, 0), OL.full_layer(spec, 0, 0)
+    T = 100
+    x = S.tokens(S.TokenSpec(T=T, token_set=17), spec.H, 0)
+    ws = api.workspace(L, T)
+    y = api.moe_forward(L, dev(x), ws).cpu().numpy()
+    _, idx_o, _ = O.moe_forward(ref, x)
+    assert len(np.unique(idx_o)) == 2
+    _tiny_batch_check(spec, L, ref, x, ws, y, f"int8 hot experts T={T}")
+
+
+@pytest.mark.parametrize("T", [1, 4, 8])
+def test_int8_path_invariance(tiny8, T):
+    """The same tokens on both paths: routing, h, Q8(h) and its scales bit
+    for bit per pair, outputs within the bar."""
+    L, _ = tiny8
+    x = S.tokens(S.TokenSpec(T=T, token_set=960 + T), TINY8.H, 0)
+    ws = api.workspace(L, T)
+    yg = api.moe_forward(L, dev(x), ws, flags=COLI_PATH_GEMV).cpu().numpy()
+    vg = ws_views(L, T, ws, COLI_PATH_GEMV)
+    ym = api.moe_forward(L, dev(x), ws, flags=COLI_PATH_GROUPED).cpu().numpy()
+    vm = ws_views(L, T, ws, COLI_PATH_GROUPED)
+    assert vg["path"] == 0 and vm["path"] == 1
+    for t in range(T):
+        for j in range(TINY8.top_k):
+            pg, pm = vg["pair_of"][t, j], vm["pair_of"][t, j]
+            assert np.array_equal(vg["h"][pg], vm["h"][pm])
+            assert np.array_equal(vg["hq"][pg], vm["hq"][pm]) and np.array_equal(vg["hs"][pg], vm["hs"][pm])
+    say(f"int8 path invariance T={T}: bit-identical outputs {np.mean(yg == ym):.4f}")
+    assert rel_err(ym, yg).max() <= TOL
+
+
+def _int8_copy_of_int4(L4, spec):
+    """An int8 layer holding the int4 layer's codes and scales, in the int8
+    layout (8-groups reordered, block halves split)."""
+    L8 = api.MoELayer.empty(spec.H, spec.I, spec.E, spec.top_k, weight_bits=8)
+    L8.router_w.copy_(L4.router_w)
+    L8.router_b.copy_(L4.router_b)
+    for name in ("gate_s", "up_s", "down_s"):
+        getattr(L8, name).copy_(getattr(L4, name))
+    for name in ("gate_q", "up_q", "down_q"):
+        b = getattr(L4, name).cpu().numpy()
+        lo = (b & 0xF).astype(np.int16)
+        hi = (b >> 4).astype(np.int16)
+        lo = np.where(lo >= 8, lo - 16, lo)
+        hi = np.where(hi >= 8, hi - 16, hi)
+        codes = np.empty(b.shape[:-1] + (2 * b.shape[-1],), np.int8)
+        codes[..., 0::2] = lo
+        codes[..., 1::2] = hi
+        n = codes.shape[-1]
+        stored = np.empty_like(codes)
+        i = np.arange(n)
+        p = (i & 31 & ~7) + np.where(i & 1, 4 + ((i & 7) >> 1), (i & 7) >> 1)     # byte in its block
+        stored[..., (p >> 4) * 16 * (n // 32) + (i >> 5) * 16 + (p & 15)] = codes
+        getattr(L8, name).copy_(torch.from_numpy(stored))
+    return L8
+
+
+@pytest.mark.parametrize("T", [9, 40, 100])
+def test_grouped_int8_equals_int4_on_shared_codes(T):
+    """Codes in [-8, 7] written both ways give the same block dots, and the
+    grouped int8 kernels scale and sum them as the int4 ones do: outputs bit
+    for bit (a wrong half order, row stride or a leftover x16 factor breaks
+    it)."""
+    sp4 = S.LayerSpec(H=256, I=128, E=16, top_k=2)
+    L4 = device_layer(sp4, 0, 0)
+    L8 = _int8_copy_of_int4(L4, sp4)
+    x = S.tokens(S.TokenSpec(T=T, token_set=970 + T), sp4.H, 0)
+    y4 = api.moe_forward(L4, dev(x), api.workspace(L4, T)).cpu().numpy()
+    y8 = api.moe_forward(L8, dev(x), api.workspace(L8, T)).cpu().numpy()
+    say(f"grouped int8 vs int4 codes T={T}: identical {np.mean(y4 == y8):.4f}")
+    assert np.array_equal(y4, y8)
+
+
+@pytest.fixture(scope="module")
+def glm8_prefill():
+    wl = S.WORKLOADS["glm52_int8_prefill_T512"]
+    say("building the GLM-5.2-shaped int8 layer with Zipf-skewed bias on device")
+    L = device_layer(wl.layer, 0, 0)
+    W, b = S.router(wl.layer, 0, 0)
+    yield wl, L, W, b
+    del L
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.timeout(900)
+def test_grouped_int8_glm_prefill_T512(glm8_prefill):
+    """All 512 tokens and all 4,608 pairs of the Zipf-routed prefill batch on
+    int8 experts."""
+    wl, L, W, b = glm8_prefill
+    st, load = _full_layer_check(wl, L, W, b, "int8 prefill T=512")
+    assert (load > 0).sum() > 100

@@ -4,7 +4,8 @@ device packer bit-exact against the host packer, and whole layers against
 the oracle (routing bit-exact, per-pair Q8(h) and its scales bit-exact,
 outputs within the bar) on the token-GEMV path, tiny and GLM-5.2-shaped, plus
 the cross-format identity on the device (an int8 layer whose codes lie in
-[-8, 7] gives the int4 layer's outputs bit for bit)."""
+[-8, 7] gives the int4 layer's outputs bit for bit). The grouped path's int8
+kernels are tested in test_gpu_grouped_int8.py."""
 import ctypes
 
 import numpy as np
@@ -12,7 +13,6 @@ import pytest
 import torch
 
 from int4_quantized_expert_sigmoid_amd import api, COLI_ACCUMULATE
-from int4_quantized_expert_sigmoid_amd._lib import ColiError, COLI_EUNSUPPORTED, COLI_PATH_GROUPED
 from int4_quantized_expert_sigmoid_amd.synthetic import device_layer
 from oracle import layers as OL
 from oracle import oracle as O
@@ -80,19 +80,6 @@ def test_forward_tiny_int8(tiny8, T):
     yd = dev(y0)
     api.moe_forward(L, dev(x), ws, y=yd, flags=COLI_ACCUMULATE)
     assert rel_err(yd.cpu().numpy(), (np.float32(0.5) + y_o).astype(np.float32)).max() <= TOL
-
-
-def test_int8_refused_off_the_gemv_path(tiny8):
-    L, _ = tiny8
-    x = S.tokens(S.TokenSpec(T=9, token_set=1), TINY8.H, 0)
-    ws = api.workspace(L, 9)
-    with pytest.raises(ColiError) as e:
-        api.moe_forward(L, dev(x), ws)
-    assert e.value.code == COLI_EUNSUPPORTED
-    ws1 = api.workspace(L, 1)
-    with pytest.raises(ColiError) as e:
-        api.moe_forward(L, dev(x[:1]), ws1, flags=COLI_PATH_GROUPED)
-    assert e.value.code == COLI_EUNSUPPORTED
 
 
 def test_int8_device_layer_equals_int4_on_shared_codes():

@@ -90,6 +90,4 @@ def test_dense_workspace_and_argument_errors():
     assert F(ctypes.byref(M), p, p, f(-1), 1, p, 0, p, big, None) == _lib.COLI_EINVAL             # eps < 0
     assert F(ctypes.byref(M), ctypes.c_void_p((1 << 20) + 8), None, f(0), 1, p, 0, p, big, None) == _lib.COLI_EINVAL
     assert F(ctypes.byref(M), p, None, f(0), 1, p, 0, p, 100, None) == _lib.COLI_EWORKSPACE
-    assert F(ctypes.byref(M), p, None, f(0), 16, p, _lib.COLI_PATH_GROUPED, p, big, None) == \
-        _lib.COLI_EUNSUPPORTED                                                                   # int8 grouped
     assert F(None, p, None, f(0), 1, p, 0, p, big, None) == _lib.COLI_EINVAL
