@@ -81,7 +81,7 @@ int status(hipError_t e) { return e == hipSuccess ? COLI_OK : COLI_EDEVICE; }
 // (not grouped).
 int format_ok(const coli_moe_layer &L, int path)
 {
-    if ((L.weight_bits == 2 || L.group_size != 0) && path != 0)   // int4 and int8 have grouped kernels
+    if (L.group_size != 0 && path != 0)    // int4, int8 and int2 have grouped kernels
         return COLI_EUNSUPPORTED;
     return COLI_OK;
 }

@@ -24,6 +24,7 @@
 namespace coli {
 namespace {
 
+typedef int v2i __attribute__((ext_vector_type(2)));
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 
@@ -132,16 +133,28 @@ __device__ __forceinline__ void split_pair(uint4 w, uint2 &A, uint2 &B)
 // halves (two 64-byte runs of the row), and a pair's activations are 128
 // bytes, whose chunk c sits at c ^ ((p >> 1) & 7) so that 16 pairs' reads of
 // one column still touch 16 different bank groups.
+//
+// int2 weights (WB = 2) hold a 32-wide block in 8 bytes, one dword per 16
+// columns, whose four 2-bit fields are the reordered activation dwords of
+// those columns (byte k: columns 2k, 2k+1, 2k+8, 2k+9). Their stages hold
+// KS = 8 blocks, 64 bytes of a row: 4 LDS chunks (chunk c: blocks 2c and
+// 2c+1), at c ^ ((n >> 2) & 3); each lane loads one block.
 template <int WB> struct Stage;
-template <> struct Stage<4> { static constexpr int KS = 8; };
-template <> struct Stage<8> { static constexpr int KS = 4; };
-constexpr int WCH = 8;         // 16-byte weight chunks per row and stage (both formats)
+template <> struct Stage<4> { static constexpr int KS = 8, WCH = 8; };
+template <> struct Stage<8> { static constexpr int KS = 4, WCH = 8; };
+template <> struct Stage<2> { static constexpr int KS = 8, WCH = 4; };
 
 template <int WB> constexpr int stage_blocks() { return Stage<WB>::KS; }
+template <int WB> constexpr int stage_wch() { return Stage<WB>::WCH; }       // 16-byte weight chunks per row and stage
 template <int WB> constexpr int stage_xc() { return 2 * Stage<WB>::KS; }   // 16-byte activation chunks per pair and stage
 
-__device__ __forceinline__ int wsw(int n) { return (n >> 1) & 7; }
-template <int WB> __device__ __forceinline__ int xsw(int p) { return WB == 4 ? (p & 15) : ((p >> 1) & 7); }
+template <int WB> __device__ __forceinline__ int wsw(int n) { return WB == 2 ? ((n >> 2) & 3) : ((n >> 1) & 7); }
+template <int WB> __device__ __forceinline__ int xsw(int p) { return stage_xc<WB>() == 16 ? (p & 15) : ((p >> 1) & 7); }
+
+// Registers of one lane's share of a stage's weight loads: 16 bytes per
+// load (int4, int8) or one 8-byte int2 block.
+template <int WB> struct WReg { typedef v4i type; };
+template <> struct WReg<2> { typedef v2i type; };
 
 // Staged data is held in clang vector types: plain loads and stores (copies
 // of the HIP vector structs become memcpys that keep a stage in scratch).
@@ -151,7 +164,7 @@ typedef double v2d __attribute__((ext_vector_type(2)));
 
 template <int NM, int WB>
 struct StageLds {
-    v4i w[WAVES][NM][QK][WCH];
+    v4i w[WAVES][NM][QK][stage_wch<WB>()];
     v4i x[2][TILE_N][stage_xc<WB>()];
     v2d d[2][stage_blocks<WB>() / 2][TILE_N];   // f64 block factors of the stage's block pairs (0 past the tile's pairs), pair-minor
 };
@@ -165,14 +178,15 @@ __device__ __forceinline__ int4 as_i4(v4i v) { return make_int4(v[0], v[1], v[2]
 // rows l/8, l/8 + 8, ...: int4, block l % 8 of the stage; int8, half
 // (l % 8) / 4 of block l % 4 (rowb: bytes per row).
 template <int WB>
-__device__ __forceinline__ void load_w(v4i (&w)[4], int s, int nblk, const uint8_t *wrow, long rowb)
+__device__ __forceinline__ void load_w(typename WReg<WB>::type (&w)[4], int s, int nblk, const uint8_t *wrow, long rowb)
 {
+    typedef typename WReg<WB>::type R;
     constexpr int KS = stage_blocks<WB>();
     const int c = threadIdx.x & 7;
-    const int blk = min(s * KS + (WB == 4 ? c : (c & 3)), nblk - 1);
-    const long off = WB == 4 ? 16 * blk : (c >> 2) * (rowb / 2) + 16 * blk;
+    const int blk = min(s * KS + (WB == 8 ? (c & 3) : c), nblk - 1);
+    const long off = WB == 4 ? 16 * blk : WB == 2 ? 8 * blk : (c >> 2) * (rowb / 2) + 16 * blk;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) w[j] = *reinterpret_cast<const v4i *>(wrow + (long)(8 * j) * rowb + off);
+    for (int j = 0; j < 4; ++j) w[j] = *reinterpret_cast<const R *>(wrow + (long)(8 * j) * rowb + off);
 }
 
 // Activation loads: 2 * KS lanes per pair row (16-byte chunk c of the
@@ -196,7 +210,7 @@ template <int WB>
 __device__ __forceinline__ v4f load_d(int s, int nblk, const float *drow, bool vec_scales)
 {
     constexpr int KS = stage_blocks<WB>();
-    const int b = s * KS + (WB == 4 ? 4 * (threadIdx.x & 1) : 0);
+    const int b = s * KS + (KS == 8 ? 4 * (threadIdx.x & 1) : 0);
     if (vec_scales) return *reinterpret_cast<const v4f *>(drow + min(b, nblk - 4));
     v4f d;
 #pragma unroll
@@ -205,12 +219,21 @@ __device__ __forceinline__ v4f load_d(int s, int nblk, const float *drow, bool v
 }
 
 template <int NM, int WB>
-__device__ __forceinline__ void store_w(StageLds<NM, WB> &sm, int m, const v4i (&w)[4])
+__device__ __forceinline__ void store_w(StageLds<NM, WB> &sm, int m, const typename WReg<WB>::type (&w)[4])
 {
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int r8 = lane >> 3;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) sm.w[wave][m][8 * j + r8][(lane & 7) ^ wsw(8 * j + r8)] = w[j];
+    for (int j = 0; j < 4; ++j) {
+        const int n = 8 * j + r8;
+        if constexpr (WB == 2) {                 // block k = lane % 8: half k % 2 of chunk k / 2
+            const int k = lane & 7;
+            char *row = reinterpret_cast<char *>(&sm.w[wave][m][n][0]);
+            *reinterpret_cast<v2i *>(row + 16 * ((k >> 1) ^ wsw<2>(n)) + 8 * (k & 1)) = w[j];
+        } else {
+            sm.w[wave][m][n][(lane & 7) ^ wsw<WB>(n)] = w[j];
+        }
+    }
 }
 
 template <int NM, int WB>
@@ -226,20 +249,21 @@ __device__ __forceinline__ void store_x(StageLds<NM, WB> &sm, int buf, const v4i
 }
 
 // Scales are staged as the f64 factors the rescale multiplies by: d_b/16
-// for int4 (the nibble trick's x16 undone, exact), d_b for int8, and 0 for
+// for int4 (the nibble trick's x16 undone, exact), d_b/64 for int2 (its
+// codes unpacked x64), d_b for int8, and 0 for
 // pairs past the tile's np, so the MFMA loops do no conversions. Kept
 // pair-minor: the lanes reading one block pair's factors read contiguous
 // bytes.
 template <int WB>
-__device__ __forceinline__ int d_pair(int lane) { return WB == 4 ? (lane >> 1) : lane; }
+__device__ __forceinline__ int d_pair(int lane) { return stage_blocks<WB>() == 8 ? (lane >> 1) : lane; }
 
 template <int NM, int WB>
 __device__ __forceinline__ void store_d(StageLds<NM, WB> &sm, int buf, v4f d, int np)
 {
     const int lane = threadIdx.x & 63;
-    const int p = d_pair<WB>(lane), jp = WB == 4 ? 2 * (lane & 1) : 0;
+    const int p = d_pair<WB>(lane), jp = stage_blocks<WB>() == 8 ? 2 * (lane & 1) : 0;
     if (p >= TILE_N) return;                     // int8: lanes 32-63 stage nothing
-    const double v = p < np ? (WB == 4 ? 0.0625 : 1.0) : 0.0;
+    const double v = p < np ? (WB == 4 ? 0.0625 : WB == 2 ? 0.015625 : 1.0) : 0.0;
     sm.d[buf][jp][p] = v2d{(double)d[0] * v, (double)d[1] * v};
     sm.d[buf][jp + 1][p] = v2d{(double)d[2] * v, (double)d[3] * v};
 }
@@ -294,6 +318,25 @@ __device__ __forceinline__ long unpack4(uint32_t w)
     return (long)(((unsigned long long)(w & m) << 32) | (unsigned long long)((w << 4) & m));
 }
 
+// One int2 dword (16 columns) as the 16 operand bytes x64, in the
+// reordered activation order: fields 0, 1, 2, 3 of its bytes are columns
+// 2k, 2k+1, 2k+8, 2k+9, i.e. the activation dwords 0..3 of those columns.
+__device__ __forceinline__ v4i unpack16_2b(uint32_t w)
+{
+    const uint32_t m = 0xC0C0C0C0u;
+    return v4i{(int)((w << 6) & m), (int)((w << 4) & m), (int)((w << 2) & m), (int)(w & m)};
+}
+
+// The same for one 8-group: the first (hi = 0) or second 8 columns of the
+// dword, as the 16x16x32 MFMA's 8-byte operand.
+__device__ __forceinline__ long unpack8_2b(uint32_t w, int hi)
+{
+    const uint32_t m = 0xC0C0C0C0u;
+    const uint32_t a = hi ? (w << 2) & m : (w << 6) & m;
+    const uint32_t b = hi ? w & m : (w << 4) & m;
+    return (long)(((unsigned long long)b << 32) | (unsigned long long)a);
+}
+
 // The 16 bytes of block j (of the stage) that lane half `half` multiplies,
 // as the 32x32x32 MFMA's operand, for blocks j and j+1: int4 chunks hold a
 // whole block (one permlane swap hands each half its 8 packed bytes of both,
@@ -308,6 +351,10 @@ __device__ __forceinline__ void w_pair(const StageLds<NM, WB> &sm, int wave, int
         split_pair(wp, wa, wb);
         a = unpack8(wa);
         b = unpack8(wb);
+    } else if constexpr (WB == 2) {              // blocks j, j+1 share chunk j/2; half h takes dword h of each
+        const char *ch = reinterpret_cast<const char *>(&sm.w[wave][m][n][(j >> 1) ^ sw]);
+        a = unpack16_2b(*reinterpret_cast<const uint32_t *>(ch + 4 * half));
+        b = unpack16_2b(*reinterpret_cast<const uint32_t *>(ch + 8 + 4 * half));
     } else {
         a = sm.w[wave][m][n][(4 * half + j) ^ sw];
         b = sm.w[wave][m][n][(4 * half + j + 1) ^ sw];
@@ -323,6 +370,9 @@ __device__ __forceinline__ long w_group(const StageLds<NM, WB> &sm, int wave, in
     const char *row = reinterpret_cast<const char *>(&sm.w[wave][m][r][0]);
     if constexpr (WB == 4) {
         return unpack4(*reinterpret_cast<const uint32_t *>(row + 16 * (blk ^ sw) + 4 * q));
+    } else if constexpr (WB == 2) {              // dword q/2 of the block; its first or second 8 columns
+        const uint32_t w = *reinterpret_cast<const uint32_t *>(row + 16 * ((blk >> 1) ^ sw) + 8 * (blk & 1) + 4 * (q >> 1));
+        return unpack8_2b(w, q & 1);
     } else {
         return *reinterpret_cast<const long *>(row + 16 * ((4 * (q >> 1) + blk) ^ sw) + 8 * (q & 1));
     }
@@ -340,7 +390,7 @@ __device__ __forceinline__ void stage_pass(const StageLds<NM, WB> &sm, int m, do
     if constexpr (!NARROW) {
         const v16i zero = {};
         const int n = lane & 31, half = lane >> 5;
-        const int sw = wsw(n), sx = xsw<WB>(n);
+        const int sw = wsw<WB>(n), sx = xsw<WB>(n);
         // Both MFMAs of a block pair are issued before either result is
         // rescaled: the second runs on the matrix core while the vector
         // unit converts and accumulates the first.
@@ -368,7 +418,7 @@ __device__ __forceinline__ void stage_pass(const StageLds<NM, WB> &sm, int m, do
         const int pr = lane & 15, q = lane >> 4;
         const int sx = xsw<WB>(pr);
         const int r0 = pr, r1 = pr + 16;                 // the lane's weight rows of the two MFMAs
-        const int sw0 = wsw(r0), sw1 = wsw(r1);
+        const int sw0 = wsw<WB>(r0), sw1 = wsw<WB>(r1);
         // the four MFMAs of a block pair are issued before any result is
         // rescaled (see the 32-pair form)
 #pragma unroll
@@ -433,7 +483,8 @@ __device__ __forceinline__ void gateup_tile(const GroupedArgs &a, StageLds<2, WB
     // activations load during the gate pass, its up rows during the up pass,
     // so only one matrix's stage is ever held in registers.
     const int nst = (nblk + KS - 1) / KS;
-    v4i wn[4], xn[NXL];
+    typename WReg<WB>::type wn[4];
+    v4i xn[NXL];
     v4f dn = {};
     load_x<WB>(xn, 0, nblk, xrow);
     if (wave == 0) dn = load_d<WB>(0, nblk, drow, vec_scales);
@@ -542,7 +593,8 @@ __device__ __forceinline__ void down_tile(const GroupedArgs &a, StageLds<1, WB> 
     for (int i = 0; i < NACC; ++i) acc[i] = 0.0;
 
     const int nst = (nblk + KS - 1) / KS;
-    v4i wn[4], xn[NXL];
+    typename WReg<WB>::type wn[4];
+    v4i xn[NXL];
     v4f dn = {};
     load_x<WB>(xn, 0, nblk, xrow);
     if (wave == 0) dn = load_d<WB>(0, nblk, drow, vec_scales);
@@ -632,6 +684,9 @@ hipError_t launch_gateup_grouped(const coli_moe_layer &L, int T, const WsLayout 
     if (L.weight_bits == 8) {
         if (nblk % stage_blocks<8>() == 0) COLI_LAUNCH((k_gateup_mfma<true, 8>), grid, dim3(64 * WAVES), 0, s, a);
         else COLI_LAUNCH((k_gateup_mfma<false, 8>), grid, dim3(64 * WAVES), 0, s, a);
+    } else if (L.weight_bits == 2) {
+        if (nblk % stage_blocks<2>() == 0) COLI_LAUNCH((k_gateup_mfma<true, 2>), grid, dim3(64 * WAVES), 0, s, a);
+        else COLI_LAUNCH((k_gateup_mfma<false, 2>), grid, dim3(64 * WAVES), 0, s, a);
     } else {
         if (nblk % stage_blocks<4>() == 0) COLI_LAUNCH((k_gateup_mfma<true, 4>), grid, dim3(64 * WAVES), 0, s, a);
         else COLI_LAUNCH((k_gateup_mfma<false, 4>), grid, dim3(64 * WAVES), 0, s, a);
@@ -650,6 +705,7 @@ hipError_t launch_down_grouped(const coli_moe_layer &L, int T, const WsLayout &l
     const int nrg = (L.H / QK + WAVES - 1) / WAVES;
     const dim3 grid((unsigned)(max_tiles(lay, L) * nrg));
     if (L.weight_bits == 8) COLI_LAUNCH(k_down_mfma<8>, grid, dim3(64 * WAVES), 0, s, a);
+    else if (L.weight_bits == 2) COLI_LAUNCH(k_down_mfma<2>, grid, dim3(64 * WAVES), 0, s, a);
     else COLI_LAUNCH(k_down_mfma<4>, grid, dim3(64 * WAVES), 0, s, a);
     return hipGetLastError();
 }

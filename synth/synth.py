@@ -231,6 +231,8 @@ WORKLOADS = {
                                      TokenSpec(T=1, outlier_channels=61)),
     "glm52_int2_verify_T4": Workload("glm52_int2_verify_T4", replace(GLM52, weight_bits=2),
                                      TokenSpec(T=4, rho=0.8, outlier_channels=61)),
+    "glm52_int2_prefill_T512": Workload("glm52_int2_prefill_T512", replace(GLM52, zipf_s=1.1, weight_bits=2),
+                                        TokenSpec(T=512, outlier_channels=61)),
 }
 
 

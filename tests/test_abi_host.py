@@ -220,13 +220,17 @@ def test_group_scales_only_on_the_gemv_path():
     assert X(ctypes.byref(L), p, p, p, p, 9, p, 0, p, 1 << 40, None) == _lib.COLI_EUNSUPPORTED
 
 
-def test_int2_experts_only_on_the_gemv_path():
+def test_int2_experts_take_both_paths():
+    """int2 experts have token-GEMV and grouped kernels: the layout of a
+    large or forced-grouped batch is the grouped one (no launch here)."""
     L = fake_layer(weight_bits=2)
     p = ctypes.c_void_p(1 << 20)
-    F = lib().coli_moe_forward
+    out = CWsLayout()
     assert ws_bytes(L, 4) > 0
-    assert F(ctypes.byref(L), p, 9, p, 0, p, 1 << 40, None) == _lib.COLI_EUNSUPPORTED      # grouped batch
-    assert F(ctypes.byref(L), p, 4, p, 4, p, 1 << 40, None) == _lib.COLI_EUNSUPPORTED      # forced grouped
+    assert lib().coli_moe_workspace_layout(ctypes.byref(L), 512, 0, ctypes.byref(out)) == 0
+    assert out.path == 1
+    assert lib().coli_moe_workspace_layout(ctypes.byref(L), 4, _lib.COLI_PATH_GROUPED, ctypes.byref(out)) == 0
+    assert out.path == 1
     P = lib().coli_pack_int2_rows_dev
     for rows, cols in ((0, 64), (4, 48), (4, 16)):
         assert P(p, rows, cols, p, p, None) == _lib.COLI_EINVAL

@@ -1,10 +1,11 @@
-"""GPU parity of int8-weight experts on the grouped int8-MFMA path (T > 8)
-through the C ABI: tiny and odd-shaped layers in full (every token and
-pair; the odd shape runs part-filled stages and scales loaded one by one),
-the compute-bound case of full tiles, path invariance against the token-GEMV
-path, the cross-format identity on the grouped kernels (an int8 layer whose
-codes lie in [-8, 7] gives the int4 layer's outputs bit for bit), and the
-whole GLM-5.2-shaped Zipf prefill (T = 512) against the threaded oracle."""
+"""GPU parity of the int8 and int2 weight formats on the grouped MFMA path
+(T > 8) through the C ABI: tiny and odd-shaped layers in full (every token
+and pair; the odd shape runs part-filled stages and scales loaded one by
+one), the compute-bound case of full tiles, path invariance against the
+token-GEMV path, the cross-format identities on the grouped kernels (int8
+or int2 layers whose codes an int4 layer holds too give the int4 layer's
+outputs bit for bit), and the whole GLM-5.2-shaped Zipf prefill (T = 512)
+against the threaded oracle."""
 from dataclasses import replace
 
 import numpy as np
@@ -19,11 +20,11 @@ from synth import synth as S
 
 from gpu_common import dev, rel_err, ws_views
 from test_gpu_grouped import _full_layer_check, _tiny_batch_check
+from test_gpu_int2 import as_int4, codes_of
 
 pytestmark = pytest.mark.gpu
 TOL = 1e-4
-TINY8 = replace(S.TINY, weight_bits=8)
-ODD8 = S.LayerSpec(H=320, I=96, E=16, top_k=4, weight_bits=8)
+BITS = [8, 2]
 
 
 def say(*a):
@@ -36,36 +37,40 @@ def gpu():
     torch.cuda.set_device(0)
 
 
-@pytest.fixture(scope="module")
-def tiny8():
-    return device_layer(TINY8, 0, 0), OL.full_layer(TINY8, 0, 0)
+@pytest.fixture(scope="module", params=BITS, ids=lambda b: f"int{b}")
+def tiny_f(request):
+    spec = replace(S.TINY, weight_bits=request.param)
+    return spec, device_layer(spec, 0, 0), OL.full_layer(spec, 0, 0)
 
 
 @pytest.mark.parametrize("T", [9, 64, 200])
-def test_grouped_int8_tiny_full_outputs(tiny8, T):
-    L, ref = tiny8
-    x = S.tokens(S.TokenSpec(T=T, token_set=900 + T), TINY8.H, 0)
+def test_grouped_tiny_full_outputs(tiny_f, T):
+    spec, L, ref = tiny_f
+    x = S.tokens(S.TokenSpec(T=T, token_set=900 + T), spec.H, 0)
     ws = api.workspace(L, T)
-    say(f"grouped int8 tiny T={T}")
+    say(f"grouped int{spec.weight_bits} tiny T={T}")
     y = api.moe_forward(L, dev(x), ws).cpu().numpy()
-    _tiny_batch_check(TINY8, L, ref, x, ws, y, f"int8 tiny T={T}")
+    _tiny_batch_check(spec, L, ref, x, ws, y, f"int{spec.weight_bits} tiny T={T}")
 
 
+@pytest.mark.parametrize("bits", BITS)
 @pytest.mark.parametrize("T", [9, 40, 77])
-def test_grouped_int8_odd_shape_full_outputs(T):
-    """H = 320 (10 blocks: a part-filled last stage of 4), I = 96 (3 row
-    tiles and 3 down blocks); neither block count is a multiple of 4, so the
-    scales load one by one."""
-    L, ref = device_layer(ODD8, 0, 0), OL.full_layer(ODD8, 0, 0)
-    x = S.tokens(S.TokenSpec(T=T, token_set=950 + T), ODD8.H, 0)
+def test_grouped_odd_shape_full_outputs(bits, T):
+    """H = 320 (10 blocks: part-filled last stages), I = 96 (3 row tiles, 3
+    down blocks); neither block count is a multiple of 4, so the scales load
+    one by one."""
+    spec = S.LayerSpec(H=320, I=96, E=16, top_k=4, weight_bits=bits)
+    L, ref = device_layer(spec, 0, 0), OL.full_layer(spec, 0, 0)
+    x = S.tokens(S.TokenSpec(T=T, token_set=950 + T), spec.H, 0)
     ws = api.workspace(L, T)
-    say(f"grouped int8 odd shape T={T}")
+    say(f"grouped int{bits} odd shape T={T}")
     y = api.moe_forward(L, dev(x), ws).cpu().numpy()
-    _tiny_batch_check(ODD8, L, ref, x, ws, y, f"int8 odd T={T}")
+    _tiny_batch_check(spec, L, ref, x, ws, y, f"int{bits} odd T={T}")
 
 
-def test_grouped_int8_hot_experts_full_tiles():
-    spec = S.LayerSpec(H=256, I=128, E=16, top_k=2, hot_experts=2, weight_bits=8)
+@pytest.mark.parametrize("bits", BITS)
+def test_grouped_hot_experts_full_tiles(bits):
+    spec = S.LayerSpec(H=256, I=128, E=16, top_k=2, hot_experts=2, weight_bits=bits)
     L, ref = device_layer(spec, 0, 0), OL.full_layer(spec, 0, 0)
     T = 100
     x = S.tokens(S.TokenSpec(T=T, token_set=17), spec.H, 0)
@@ -73,15 +78,15 @@ def test_grouped_int8_hot_experts_full_tiles():
     y = api.moe_forward(L, dev(x), ws).cpu().numpy()
     _, idx_o, _ = O.moe_forward(ref, x)
     assert len(np.unique(idx_o)) == 2
-    _tiny_batch_check(spec, L, ref, x, ws, y, f"int8 hot experts T={T}")
+    _tiny_batch_check(spec, L, ref, x, ws, y, f"int{bits} hot experts T={T}")
 
 
 @pytest.mark.parametrize("T", [1, 4, 8])
-def test_int8_path_invariance(tiny8, T):
+def test_path_invariance(tiny_f, T):
     """The same tokens on both paths: routing, h, Q8(h) and its scales bit
     for bit per pair, outputs within the bar."""
-    L, _ = tiny8
-    x = S.tokens(S.TokenSpec(T=T, token_set=960 + T), TINY8.H, 0)
+    spec, L, _ = tiny_f
+    x = S.tokens(S.TokenSpec(T=T, token_set=960 + T), spec.H, 0)
     ws = api.workspace(L, T)
     yg = api.moe_forward(L, dev(x), ws, flags=COLI_PATH_GEMV).cpu().numpy()
     vg = ws_views(L, T, ws, COLI_PATH_GEMV)
@@ -89,11 +94,11 @@ def test_int8_path_invariance(tiny8, T):
     vm = ws_views(L, T, ws, COLI_PATH_GROUPED)
     assert vg["path"] == 0 and vm["path"] == 1
     for t in range(T):
-        for j in range(TINY8.top_k):
+        for j in range(spec.top_k):
             pg, pm = vg["pair_of"][t, j], vm["pair_of"][t, j]
             assert np.array_equal(vg["h"][pg], vm["h"][pm])
             assert np.array_equal(vg["hq"][pg], vm["hq"][pm]) and np.array_equal(vg["hs"][pg], vm["hs"][pm])
-    say(f"int8 path invariance T={T}: bit-identical outputs {np.mean(yg == ym):.4f}")
+    say(f"int{spec.weight_bits} path invariance T={T}: bit-identical outputs {np.mean(yg == ym):.4f}")
     assert rel_err(ym, yg).max() <= TOL
 
 
@@ -140,9 +145,36 @@ def test_grouped_int8_equals_int4_on_shared_codes(T):
 
 
 @pytest.fixture(scope="module")
-def glm8_prefill():
-    wl = S.WORKLOADS["glm52_int8_prefill_T512"]
-    say("building the GLM-5.2-shaped int8 layer with Zipf-skewed bias on device")
+def tiny2():
+    spec = replace(S.TINY, weight_bits=2)
+    return spec, device_layer(spec, 0, 0), OL.full_layer(spec, 0, 0)
+
+
+@pytest.mark.parametrize("T", [9, 40, 100])
+def test_grouped_int2_equals_int4_on_shared_codes(tiny2, T):
+    """The int2 layer's codes written as int4 nibbles (same scales): the
+    grouped int4 kernels give the grouped int2 kernels' outputs bit for bit
+    (a wrong field order, a leftover x64 factor or a row stride of the wrong
+    format breaks it)."""
+    spec, L2, ref = tiny2
+    L4 = api.MoELayer.empty(spec.H, spec.I, spec.E, spec.top_k)
+    L4.router_w.copy_(L2.router_w)
+    L4.router_b.copy_(L2.router_b)
+    for name in ("gate_s", "up_s", "down_s"):
+        getattr(L4, name).copy_(getattr(L2, name))
+    for name in ("gate_q", "up_q", "down_q"):
+        getattr(L4, name).copy_(torch.from_numpy(as_int4(codes_of(getattr(ref, name)))))
+    x = S.tokens(S.TokenSpec(T=T, token_set=980 + T), spec.H, 0)
+    y2 = api.moe_forward(L2, dev(x), api.workspace(L2, T)).cpu().numpy()
+    y4 = api.moe_forward(L4, dev(x), api.workspace(L4, T)).cpu().numpy()
+    say(f"grouped int2 vs int4 codes T={T}: identical {np.mean(y2 == y4):.4f}")
+    assert np.array_equal(y2, y4)
+
+
+@pytest.fixture(scope="module", params=["glm52_int8_prefill_T512", "glm52_int2_prefill_T512"])
+def glm_f_prefill(request):
+    wl = S.WORKLOADS[request.param]
+    say(f"building the GLM-5.2-shaped int{wl.layer.weight_bits} layer with Zipf-skewed bias on device")
     L = device_layer(wl.layer, 0, 0)
     W, b = S.router(wl.layer, 0, 0)
     yield wl, L, W, b
@@ -151,9 +183,8 @@ def glm8_prefill():
 
 
 @pytest.mark.timeout(900)
-def test_grouped_int8_glm_prefill_T512(glm8_prefill):
-    """All 512 tokens and all 4,608 pairs of the Zipf-routed prefill batch on
-    int8 experts."""
-    wl, L, W, b = glm8_prefill
-    st, load = _full_layer_check(wl, L, W, b, "int8 prefill T=512")
+def test_grouped_glm_prefill_T512(glm_f_prefill):
+    """All 512 tokens and all 4,608 pairs of the Zipf-routed prefill batch."""
+    wl, L, W, b = glm_f_prefill
+    st, load = _full_layer_check(wl, L, W, b, f"int{wl.layer.weight_bits} prefill T=512")
     assert (load > 0).sum() > 100

@@ -4,15 +4,14 @@ device packer against the oracle's packer (the same codes and scales, in the
 library's column order), whole layers against the oracle on the token-GEMV
 path (routing, Q8(h) codes and scales bit-exact, outputs within the bar),
 tiny and GLM-5.2-shaped, the cross-format identity on the device (int2 codes
-written as int4 nibbles give the int4 kernels' outputs bit for bit), and the
-refusals off that path."""
+written as int4 nibbles give the int4 kernels' outputs bit for bit). The
+grouped path's int2 kernels are tested in test_gpu_grouped_formats.py."""
 import numpy as np
 import pytest
 import torch
 from dataclasses import replace
 
 from int4_quantized_expert_sigmoid_amd import api, COLI_ACCUMULATE
-from int4_quantized_expert_sigmoid_amd._lib import ColiError, COLI_EUNSUPPORTED, COLI_PATH_GROUPED
 from int4_quantized_expert_sigmoid_amd.synthetic import device_layer
 from oracle import layers as OL
 from oracle import oracle as O
@@ -123,18 +122,6 @@ def test_int2_device_layer_equals_int4_on_shared_codes(tiny2):
         y4 = api.moe_forward(L4, dev(x), api.workspace(L4, T)).cpu().numpy()
         say(f"int2 vs int4 codes T={T}: identical {np.mean(y2 == y4):.4f}")
         assert np.array_equal(y2, y4)
-
-
-def test_int2_refused_off_the_gemv_path(tiny2):
-    L, _ = tiny2
-    x = S.tokens(S.TokenSpec(T=9, token_set=1), TINY2.H, 0)
-    with pytest.raises(ColiError) as e:
-        api.moe_forward(L, dev(x), api.workspace(L, 9))
-    assert e.value.code == COLI_EUNSUPPORTED
-    ws1 = api.workspace(L, 1)
-    with pytest.raises(ColiError) as e:
-        api.moe_forward(L, dev(x[:1]), ws1, flags=COLI_PATH_GROUPED)
-    assert e.value.code == COLI_EUNSUPPORTED
 
 
 @pytest.fixture(scope="module")
