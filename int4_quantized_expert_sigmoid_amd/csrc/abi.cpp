@@ -77,15 +77,6 @@ int choose_path(const coli_moe_layer &L, int T, int flags)
 
 int status(hipError_t e) { return e == hipSuccess ? COLI_OK : COLI_EDEVICE; }
 
-// int8 and int2 experts and group scales run on the token-GEMV path only
-// (not grouped).
-int format_ok(const coli_moe_layer &L, int path)
-{
-    if (L.group_size != 0 && path != 0)    // int4, int8 and int2 have grouped kernels
-        return COLI_EUNSUPPORTED;
-    return COLI_OK;
-}
-
 } // namespace
 
 WsLayout make_layout(const coli_moe_layer &L, int T, int path)
@@ -254,7 +245,6 @@ static int forward_impl(const coli_moe_layer *L, const float *x, int T, float *y
     WsLayout lay;
     int rc = check_common(L, T, flags, ws, ws_bytes, path, lay);
     if (rc != COLI_OK) return rc;
-    if ((rc = format_ok(*L, path)) != COLI_OK) return rc;
     if (!al16(x) || !al16(y)) return COLI_EINVAL;
     if (gamma && (!al16(gamma) || !(eps >= 0.0f) || !std::isfinite(eps))) return COLI_EINVAL;
     hipStream_t s = (hipStream_t)stream;
@@ -489,7 +479,6 @@ int coli_moe_experts(const coli_moe_layer *L, const int8_t *xq, const float *xs,
     WsLayout lay;
     int rc = check_common(L, T, flags, ws, ws_bytes, path, lay);
     if (rc != COLI_OK) return rc;
-    if ((rc = format_ok(*L, path)) != COLI_OK) return rc;
     if (!al16(xq) || !al4(xs) || !al4(idx) || !al4(w) || !al16(y)) return COLI_EINVAL;
     hipStream_t s = (hipStream_t)stream;
     char *base = static_cast<char *>(ws);

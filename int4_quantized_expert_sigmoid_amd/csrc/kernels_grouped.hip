@@ -45,6 +45,7 @@ struct GroupedArgs {
     float *hs;
     float *ye;
     int ntiles_max;            // tiles the grid covers
+    int gsh;                   // group scales: log2(group / 32)
 };
 
 __device__ __forceinline__ v4i unpack8(uint2 w)
@@ -139,22 +140,35 @@ __device__ __forceinline__ void split_pair(uint4 w, uint2 &A, uint2 &B)
 // those columns (byte k: columns 2k, 2k+1, 2k+8, 2k+9). Their stages hold
 // KS = 8 blocks, 64 bytes of a row: 4 LDS chunks (chunk c: blocks 2c and
 // 2c+1), at c ^ ((n >> 2) & 3); each lane loads one block.
+//
+// int4 codes with one f32 scale per group of columns (format code
+// WB_GROUPS) stage 4 blocks (64 bytes of a row, each lane loading half a
+// block), so that the group scales of a stage fit beside the tiles in LDS:
+// four slots of 32 f64 scales per wave and matrix (slot k: the stage's k-th
+// group; one slot when a group spans the stage).
+constexpr int WB_GROUPS = 5;   // format code: int4 codes, a scale per group of columns
 template <int WB> struct Stage;
 template <> struct Stage<4> { static constexpr int KS = 8, WCH = 8; };
 template <> struct Stage<8> { static constexpr int KS = 4, WCH = 8; };
 template <> struct Stage<2> { static constexpr int KS = 8, WCH = 4; };
+template <> struct Stage<WB_GROUPS> { static constexpr int KS = 4, WCH = 4; };
+constexpr int GS_SLOTS = 4;    // group-scale slots per wave, matrix and stage
+
+template <int WB> constexpr bool int4_codes() { return WB == 4 || WB == WB_GROUPS; }
+template <int WB> constexpr int code_bits() { return WB == WB_GROUPS ? 4 : WB; }
 
 template <int WB> constexpr int stage_blocks() { return Stage<WB>::KS; }
 template <int WB> constexpr int stage_wch() { return Stage<WB>::WCH; }       // 16-byte weight chunks per row and stage
 template <int WB> constexpr int stage_xc() { return 2 * Stage<WB>::KS; }   // 16-byte activation chunks per pair and stage
 
-template <int WB> __device__ __forceinline__ int wsw(int n) { return WB == 2 ? ((n >> 2) & 3) : ((n >> 1) & 7); }
+template <int WB> __device__ __forceinline__ int wsw(int n) { return stage_wch<WB>() == 4 ? ((n >> 2) & 3) : ((n >> 1) & 7); }
 template <int WB> __device__ __forceinline__ int xsw(int p) { return stage_xc<WB>() == 16 ? (p & 15) : ((p >> 1) & 7); }
 
 // Registers of one lane's share of a stage's weight loads: 16 bytes per
 // load (int4, int8) or one 8-byte int2 block.
 template <int WB> struct WReg { typedef v4i type; };
 template <> struct WReg<2> { typedef v2i type; };
+template <> struct WReg<WB_GROUPS> { typedef v2i type; };
 
 // Staged data is held in clang vector types: plain loads and stores (copies
 // of the HIP vector structs become memcpys that keep a stage in scratch).
@@ -167,6 +181,7 @@ struct StageLds {
     v4i w[WAVES][NM][QK][stage_wch<WB>()];
     v4i x[2][TILE_N][stage_xc<WB>()];
     v2d d[2][stage_blocks<WB>() / 2][TILE_N];   // f64 block factors of the stage's block pairs (0 past the tile's pairs), pair-minor
+    double sg[WB == WB_GROUPS ? WAVES : 1][NM][WB == WB_GROUPS ? GS_SLOTS : 1][WB == WB_GROUPS ? QK : 1];   // group scales, row-minor
 };
 
 __device__ __forceinline__ uint4 as_u4(v4i v) { return make_uint4((uint32_t)v[0], (uint32_t)v[1], (uint32_t)v[2], (uint32_t)v[3]); }
@@ -183,8 +198,11 @@ __device__ __forceinline__ void load_w(typename WReg<WB>::type (&w)[4], int s, i
     typedef typename WReg<WB>::type R;
     constexpr int KS = stage_blocks<WB>();
     const int c = threadIdx.x & 7;
-    const int blk = min(s * KS + (WB == 8 ? (c & 3) : c), nblk - 1);
-    const long off = WB == 4 ? 16 * blk : WB == 2 ? 8 * blk : (c >> 2) * (rowb / 2) + 16 * blk;
+    const int blk = min(s * KS + (WB == 8 ? (c & 3) : WB == WB_GROUPS ? (c >> 1) : c), nblk - 1);
+    const long off = WB == 4 ? 16 * blk
+                   : WB == 2 ? 8 * blk
+                   : WB == WB_GROUPS ? 16 * blk + 8 * (c & 1)
+                   : (c >> 2) * (rowb / 2) + 16 * blk;
 #pragma unroll
     for (int j = 0; j < 4; ++j) w[j] = *reinterpret_cast<const R *>(wrow + (long)(8 * j) * rowb + off);
 }
@@ -218,6 +236,28 @@ __device__ __forceinline__ v4f load_d(int s, int nblk, const float *drow, bool v
     return d;
 }
 
+// Group scales of stage s for the wave's 32 rows: lane l takes row l % 32
+// and slots 2*(l/32), 2*(l/32)+1, i.e. groups (s*KS >> gsh) + slot of that
+// row (clamped in bounds; slots past the stage's groups are never read).
+// srow: the lane's row of scales, ngs groups long.
+typedef float v2f __attribute__((ext_vector_type(2)));
+
+template <int WB>
+__device__ __forceinline__ v2f load_s(int s, int gsh, const float *srow, int ngs)
+{
+    const int g = ((s * stage_blocks<WB>()) >> gsh) + 2 * ((threadIdx.x & 63) >> 5);
+    return v2f{srow[min(g, ngs - 1)], srow[min(g + 1, ngs - 1)]};
+}
+
+template <int NM, int WB>
+__device__ __forceinline__ void store_s(StageLds<NM, WB> &sm, int m, v2f sv)
+{
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int k = 2 * (lane >> 5), r = lane & 31;
+    sm.sg[wave][m][k][r] = (double)sv[0];
+    sm.sg[wave][m][k + 1][r] = (double)sv[1];
+}
+
 template <int NM, int WB>
 __device__ __forceinline__ void store_w(StageLds<NM, WB> &sm, int m, const typename WReg<WB>::type (&w)[4])
 {
@@ -226,7 +266,7 @@ __device__ __forceinline__ void store_w(StageLds<NM, WB> &sm, int m, const typen
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const int n = 8 * j + r8;
-        if constexpr (WB == 2) {                 // block k = lane % 8: half k % 2 of chunk k / 2
+        if constexpr (WB == 2 || WB == WB_GROUPS) {   // 8-byte piece k = lane % 8: half k % 2 of chunk k / 2
             const int k = lane & 7;
             char *row = reinterpret_cast<char *>(&sm.w[wave][m][n][0]);
             *reinterpret_cast<v2i *>(row + 16 * ((k >> 1) ^ wsw<2>(n)) + 8 * (k & 1)) = w[j];
@@ -263,7 +303,7 @@ __device__ __forceinline__ void store_d(StageLds<NM, WB> &sm, int buf, v4f d, in
     const int lane = threadIdx.x & 63;
     const int p = d_pair<WB>(lane), jp = stage_blocks<WB>() == 8 ? 2 * (lane & 1) : 0;
     if (p >= TILE_N) return;                     // int8: lanes 32-63 stage nothing
-    const double v = p < np ? (WB == 4 ? 0.0625 : WB == 2 ? 0.015625 : 1.0) : 0.0;
+    const double v = p < np ? (int4_codes<WB>() ? 0.0625 : WB == 2 ? 0.015625 : 1.0) : 0.0;
     sm.d[buf][jp][p] = v2d{(double)d[0] * v, (double)d[1] * v};
     sm.d[buf][jp + 1][p] = v2d{(double)d[2] * v, (double)d[3] * v};
 }
@@ -345,7 +385,7 @@ template <int NM, int WB>
 __device__ __forceinline__ void w_pair(const StageLds<NM, WB> &sm, int wave, int m, int n, int half, int sw, int j,
                                        v4i &a, v4i &b)
 {
-    if constexpr (WB == 4) {
+    if constexpr (int4_codes<WB>()) {
         const uint4 wp = as_u4(sm.w[wave][m][n][(j + half) ^ sw]);
         uint2 wa, wb;
         split_pair(wp, wa, wb);
@@ -368,7 +408,7 @@ template <int NM, int WB>
 __device__ __forceinline__ long w_group(const StageLds<NM, WB> &sm, int wave, int m, int r, int sw, int blk, int q)
 {
     const char *row = reinterpret_cast<const char *>(&sm.w[wave][m][r][0]);
-    if constexpr (WB == 4) {
+    if constexpr (int4_codes<WB>()) {
         return unpack4(*reinterpret_cast<const uint32_t *>(row + 16 * (blk ^ sw) + 4 * q));
     } else if constexpr (WB == 2) {              // dword q/2 of the block; its first or second 8 columns
         const uint32_t w = *reinterpret_cast<const uint32_t *>(row + 16 * ((blk >> 1) ^ sw) + 8 * (blk & 1) + 4 * (q >> 1));
@@ -378,13 +418,27 @@ __device__ __forceinline__ long w_group(const StageLds<NM, WB> &sm, int wave, in
     }
 }
 
+// Group scales: acc += s_g * (f * c), the oracle's term and order. f * c
+// (the block factor times the int32 result) is exact in f64; the product
+// with the group scale and the sum are rounded one at a time, so nothing
+// here may become an FMA.
+__device__ __forceinline__ double gs_term(double acc, int c, double f, double sg)
+{
+#pragma clang fp contract(off)
+    const double p = (double)c * f;
+    return acc + sg * p;
+}
+
 // One matrix over the stage's blocks, adding every block's int32 results
-// times its f64 factor into acc. m: the matrix's LDS slot; buf: the stage's
+// times its f64 factor into acc (with group scales, each term times its
+// row's group scale; gsh: log2(group / 32)). m: the matrix's LDS slot; buf: the stage's
 // activation buffer; b0: its first block.
 template <bool FULL, bool NARROW, int NM, int WB>
 __device__ __forceinline__ void stage_pass(const StageLds<NM, WB> &sm, int m, double (&acc)[TileShape<NARROW>::NACC],
-                                           int buf, int b0, int nblk)
+                                           int buf, int b0, int nblk, int gsh = 0)
 {
+    constexpr bool GS = WB == WB_GROUPS;
+    const int g0 = b0 >> gsh;                    // the stage's first group
     constexpr int KS = stage_blocks<WB>();
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     if constexpr (!NARROW) {
@@ -406,11 +460,22 @@ __device__ __forceinline__ void stage_pass(const StageLds<NM, WB> &sm, int m, do
             const v16i ca = __builtin_amdgcn_mfma_i32_32x32x32_i8(ua, v4i{x0.x, x0.y, x0.z, x0.w}, zero, 0, 0, 0);
             const v16i cb = two ? __builtin_amdgcn_mfma_i32_32x32x32_i8(ub, v4i{x1.x, x1.y, x1.z, x1.w}, zero, 0, 0, 0)
                                 : zero;
+            if constexpr (GS) {
+                const double *sa = sm.sg[wave][m][((b0 + j) >> gsh) - g0];
+                const double *sb = sm.sg[wave][m][((b0 + j + 1) >> gsh) - g0];
 #pragma unroll
-            for (int i = 0; i < 16; ++i) acc[i] = fma((double)ca[i], dd[0], acc[i]);
-            if (two) {
+                for (int i = 0; i < 16; ++i) acc[i] = gs_term(acc[i], ca[i], dd[0], sa[tile_row(i, half)]);
+                if (two) {
 #pragma unroll
-                for (int i = 0; i < 16; ++i) acc[i] = fma((double)cb[i], dd[1], acc[i]);
+                    for (int i = 0; i < 16; ++i) acc[i] = gs_term(acc[i], cb[i], dd[1], sb[tile_row(i, half)]);
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < 16; ++i) acc[i] = fma((double)ca[i], dd[0], acc[i]);
+                if (two) {
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) acc[i] = fma((double)cb[i], dd[1], acc[i]);
+                }
             }
         }
     } else {
@@ -443,10 +508,19 @@ __device__ __forceinline__ void stage_pass(const StageLds<NM, WB> &sm, int m, do
 #pragma unroll
             for (int jj = 0; jj < 2; ++jj) {
                 if (jj == 1 && !two) break;
+                if constexpr (GS) {
+                    const double *sr = sm.sg[wave][m][((b0 + j + jj) >> gsh) - g0];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    acc[i] = fma((double)c[jj][0][i], dd[jj], acc[i]);
-                    acc[4 + i] = fma((double)c[jj][1][i], dd[jj], acc[4 + i]);
+                    for (int i = 0; i < 4; ++i) {
+                        acc[i] = gs_term(acc[i], c[jj][0][i], dd[jj], sr[4 * q + i]);
+                        acc[4 + i] = gs_term(acc[4 + i], c[jj][1][i], dd[jj], sr[16 + 4 * q + i]);
+                    }
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        acc[i] = fma((double)c[jj][0][i], dd[jj], acc[i]);
+                        acc[4 + i] = fma((double)c[jj][1][i], dd[jj], acc[4 + i]);
+                    }
                 }
             }
         }
@@ -465,9 +539,14 @@ __device__ __forceinline__ void gateup_tile(const GroupedArgs &a, StageLds<2, WB
     const int n_rt = a.I / QK;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int nblk = a.H / QK;
-    const long rowb = (long)a.H * WB / 8;
+    constexpr bool GS = WB == WB_GROUPS;
+    const long rowb = (long)a.H * code_bits<WB>() / 8;
     const long wrow0 = (long)e * a.I + (long)min(rt, n_rt - 1) * QK + (lane >> 3);
     const uint8_t *const wrow[2] = {a.q_a + wrow0 * rowb, a.q_b + wrow0 * rowb};
+    const int ngs = nblk >> a.gsh;               // group scales per row
+    const long srow0 = ((long)e * a.I + (long)min(rt, n_rt - 1) * QK + (lane & 31)) * ngs;
+    const float *const srow[2] = {a.s_a + srow0, a.s_b + srow0};
+    v2f sn = {};
     const int8_t *xrow[NXL];
 #pragma unroll
     for (int i = 0; i < NXL; ++i) xrow[i] = a.act + (long)a.pair_tok[p0 + stage_pair<WB>(i, np)] * a.H;
@@ -490,9 +569,13 @@ __device__ __forceinline__ void gateup_tile(const GroupedArgs &a, StageLds<2, WB
     if (wave == 0) dn = load_d<WB>(0, nblk, drow, vec_scales);
     if (rows_ok) {
         load_w<WB>(wn, 0, nblk, wrow[0], rowb);
+        if constexpr (GS) sn = load_s<WB>(0, a.gsh, srow[0], ngs);
         store_w<2, WB>(sm, 0, wn);
+        if constexpr (GS) store_s<2, WB>(sm, 0, sn);
         load_w<WB>(wn, 0, nblk, wrow[1], rowb);
+        if constexpr (GS) sn = load_s<WB>(0, a.gsh, srow[1], ngs);
         store_w<2, WB>(sm, 1, wn);
+        if constexpr (GS) store_s<2, WB>(sm, 1, sn);
     }
     store_x<2, WB>(sm, 0, xn);
     if (wave == 0) store_d<2, WB>(sm, 0, dn, np);
@@ -503,20 +586,28 @@ __device__ __forceinline__ void gateup_tile(const GroupedArgs &a, StageLds<2, WB
         if (more) {
             load_x<WB>(xn, s + 1, nblk, xrow);
             if (wave == 0) dn = load_d<WB>(s + 1, nblk, drow, vec_scales);
-            if (rows_ok) load_w<WB>(wn, s + 1, nblk, wrow[0], rowb);
+            if (rows_ok) {
+                load_w<WB>(wn, s + 1, nblk, wrow[0], rowb);
+                if constexpr (GS) sn = load_s<WB>(s + 1, a.gsh, srow[0], ngs);
+            }
         }
         issue_fence();
-        if (rows_ok) stage_pass<FULL, NARROW, 2, WB>(sm, 0, acc_g, buf, b0, nblk);
+        if (rows_ok) stage_pass<FULL, NARROW, 2, WB>(sm, 0, acc_g, buf, b0, nblk, a.gsh);
         issue_fence();
         if (more && rows_ok) {
             store_w<2, WB>(sm, 0, wn);
+            if constexpr (GS) store_s<2, WB>(sm, 0, sn);
             load_w<WB>(wn, s + 1, nblk, wrow[1], rowb);
+            if constexpr (GS) sn = load_s<WB>(s + 1, a.gsh, srow[1], ngs);
         }
         issue_fence();
-        if (rows_ok) stage_pass<FULL, NARROW, 2, WB>(sm, 1, acc_u, buf, b0, nblk);
+        if (rows_ok) stage_pass<FULL, NARROW, 2, WB>(sm, 1, acc_u, buf, b0, nblk, a.gsh);
         issue_fence();
         if (more) {
-            if (rows_ok) store_w<2, WB>(sm, 1, wn);
+            if (rows_ok) {
+                store_w<2, WB>(sm, 1, wn);
+                if constexpr (GS) store_s<2, WB>(sm, 1, sn);
+            }
             store_x<2, WB>(sm, (s + 1) & 1, xn);
             if (wave == 0) store_d<2, WB>(sm, (s + 1) & 1, dn, np);
         }
@@ -530,8 +621,9 @@ __device__ __forceinline__ void gateup_tile(const GroupedArgs &a, StageLds<2, WB
 #pragma unroll
     for (int i = 0; i < NACC; ++i) {
         const long grow = (long)e * a.I + (long)rt * QK + acc_row<NARROW>(i, lane);
-        const float gf = (float)((double)a.s_a[grow] * acc_g[i]);
-        const float uf = (float)((double)a.s_b[grow] * acc_u[i]);
+        // with group scales every block term carries its scale: no row scale
+        const float gf = GS ? (float)acc_g[i] : (float)((double)a.s_a[grow] * acc_g[i]);
+        const float uf = GS ? (float)acc_u[i] : (float)((double)a.s_b[grow] * acc_u[i]);
         hv[i] = (float)(silu_f64((double)gf) * (double)uf);
         amax = fmaxf(amax, fabsf(hv[i]));
     }
@@ -578,9 +670,13 @@ __device__ __forceinline__ void down_tile(const GroupedArgs &a, StageLds<1, WB> 
     const int n_rt = a.H / QK;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int nblk = a.I / QK;
-    const long rowb = (long)a.I * WB / 8;
+    constexpr bool GS = WB == WB_GROUPS;
+    const long rowb = (long)a.I * code_bits<WB>() / 8;
     const long wrow0 = (long)e * a.H + (long)min(rt, n_rt - 1) * QK + (lane >> 3);
     const uint8_t *wrow = a.q_a + wrow0 * rowb;
+    const int ngs = nblk >> a.gsh;
+    const float *srow = a.s_a + ((long)e * a.H + (long)min(rt, n_rt - 1) * QK + (lane & 31)) * ngs;
+    v2f sn = {};
     const int8_t *xrow[NXL];
 #pragma unroll
     for (int i = 0; i < NXL; ++i) xrow[i] = a.act + (long)(p0 + stage_pair<WB>(i, np)) * a.I;
@@ -598,7 +694,12 @@ __device__ __forceinline__ void down_tile(const GroupedArgs &a, StageLds<1, WB> 
     v4f dn = {};
     load_x<WB>(xn, 0, nblk, xrow);
     if (wave == 0) dn = load_d<WB>(0, nblk, drow, vec_scales);
-    if (rows_ok) { load_w<WB>(wn, 0, nblk, wrow, rowb); store_w<1, WB>(sm, 0, wn); }
+    if (rows_ok) {
+        load_w<WB>(wn, 0, nblk, wrow, rowb);
+        if constexpr (GS) sn = load_s<WB>(0, a.gsh, srow, ngs);
+        store_w<1, WB>(sm, 0, wn);
+        if constexpr (GS) store_s<1, WB>(sm, 0, sn);
+    }
     store_x<1, WB>(sm, 0, xn);
     if (wave == 0) store_d<1, WB>(sm, 0, dn, np);
     __syncthreads();
@@ -607,13 +708,19 @@ __device__ __forceinline__ void down_tile(const GroupedArgs &a, StageLds<1, WB> 
         if (more) {
             load_x<WB>(xn, s + 1, nblk, xrow);
             if (wave == 0) dn = load_d<WB>(s + 1, nblk, drow, vec_scales);
-            if (rows_ok) load_w<WB>(wn, s + 1, nblk, wrow, rowb);
+            if (rows_ok) {
+                load_w<WB>(wn, s + 1, nblk, wrow, rowb);
+                if constexpr (GS) sn = load_s<WB>(s + 1, a.gsh, srow, ngs);
+            }
         }
         issue_fence();
-        if (rows_ok) stage_pass<false, NARROW, 1, WB>(sm, 0, acc, s & 1, s * KS, nblk);
+        if (rows_ok) stage_pass<false, NARROW, 1, WB>(sm, 0, acc, s & 1, s * KS, nblk, a.gsh);
         issue_fence();
         if (more) {
-            if (rows_ok) store_w<1, WB>(sm, 0, wn);
+            if (rows_ok) {
+                store_w<1, WB>(sm, 0, wn);
+                if constexpr (GS) store_s<1, WB>(sm, 0, sn);
+            }
             store_x<1, WB>(sm, (s + 1) & 1, xn);
             if (wave == 0) store_d<1, WB>(sm, (s + 1) & 1, dn, np);
         }
@@ -621,12 +728,17 @@ __device__ __forceinline__ void down_tile(const GroupedArgs &a, StageLds<1, WB> 
     }
     const int n = acc_pair<NARROW>(lane);
     if (!rows_ok || n >= np) return;
-    float rs[NACC];                              // row scales first: the stores below may not alias them
-#pragma unroll
-    for (int i = 0; i < NACC; ++i) rs[i] = a.s_a[(long)e * a.H + (long)rt * QK + acc_row<NARROW>(i, lane)];
     const long base = (long)(p0 + n) * a.H + (long)rt * QK;
+    if constexpr (GS) {                          // every block term carries its group scale
 #pragma unroll
-    for (int i = 0; i < NACC; ++i) a.ye[base + acc_row<NARROW>(i, lane)] = (float)((double)rs[i] * acc[i]);
+        for (int i = 0; i < NACC; ++i) a.ye[base + acc_row<NARROW>(i, lane)] = (float)acc[i];
+    } else {
+        float rs[NACC];                          // row scales first: the stores below may not alias them
+#pragma unroll
+        for (int i = 0; i < NACC; ++i) rs[i] = a.s_a[(long)e * a.H + (long)rt * QK + acc_row<NARROW>(i, lane)];
+#pragma unroll
+        for (int i = 0; i < NACC; ++i) a.ye[base + acc_row<NARROW>(i, lane)] = (float)((double)rs[i] * acc[i]);
+    }
 }
 
 template <int WB>
@@ -652,6 +764,7 @@ GroupedArgs make_args(const WsLayout &lay, char *ws, const coli_moe_layer &L)
 {
     GroupedArgs a;
     a.H = L.H; a.I = L.I;
+    a.gsh = group_shift(L);
     a.ctrl = reinterpret_cast<const int *>(ws + lay.ctrl);
     a.tiles = reinterpret_cast<const int2 *>(ws + lay.tiles);
     a.expert_off = reinterpret_cast<const int *>(ws + lay.expert_off);
@@ -681,7 +794,12 @@ hipError_t launch_gateup_grouped(const coli_moe_layer &L, int T, const WsLayout 
     const int nrg = (L.I / QK + WAVES - 1) / WAVES;
     const dim3 grid((unsigned)(max_tiles(lay, L) * nrg));
     const int nblk = L.H / QK;
-    if (L.weight_bits == 8) {
+    a.gsh = group_shift(L);
+    if (L.group_size) {
+        if (nblk % stage_blocks<WB_GROUPS>() == 0)
+            COLI_LAUNCH((k_gateup_mfma<true, WB_GROUPS>), grid, dim3(64 * WAVES), 0, s, a);
+        else COLI_LAUNCH((k_gateup_mfma<false, WB_GROUPS>), grid, dim3(64 * WAVES), 0, s, a);
+    } else if (L.weight_bits == 8) {
         if (nblk % stage_blocks<8>() == 0) COLI_LAUNCH((k_gateup_mfma<true, 8>), grid, dim3(64 * WAVES), 0, s, a);
         else COLI_LAUNCH((k_gateup_mfma<false, 8>), grid, dim3(64 * WAVES), 0, s, a);
     } else if (L.weight_bits == 2) {
@@ -704,7 +822,9 @@ hipError_t launch_down_grouped(const coli_moe_layer &L, int T, const WsLayout &l
     a.act_s = reinterpret_cast<const float *>(ws + lay.hs);
     const int nrg = (L.H / QK + WAVES - 1) / WAVES;
     const dim3 grid((unsigned)(max_tiles(lay, L) * nrg));
-    if (L.weight_bits == 8) COLI_LAUNCH(k_down_mfma<8>, grid, dim3(64 * WAVES), 0, s, a);
+    a.gsh = group_shift(L);
+    if (L.group_size) COLI_LAUNCH(k_down_mfma<WB_GROUPS>, grid, dim3(64 * WAVES), 0, s, a);
+    else if (L.weight_bits == 8) COLI_LAUNCH(k_down_mfma<8>, grid, dim3(64 * WAVES), 0, s, a);
     else if (L.weight_bits == 2) COLI_LAUNCH(k_down_mfma<2>, grid, dim3(64 * WAVES), 0, s, a);
     else COLI_LAUNCH(k_down_mfma<4>, grid, dim3(64 * WAVES), 0, s, a);
     return hipGetLastError();

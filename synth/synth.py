@@ -226,6 +226,8 @@ WORKLOADS = {
                                      TokenSpec(T=1, outlier_channels=61)),
     "glm52_g32_verify_T4": Workload("glm52_g32_verify_T4", replace(GLM52, group_size=32),
                                     TokenSpec(T=4, rho=0.8, outlier_channels=61)),
+    "glm52_g32_prefill_T512": Workload("glm52_g32_prefill_T512", replace(GLM52, zipf_s=1.1, group_size=32),
+                                       TokenSpec(T=512, outlier_channels=61)),
     # the experimental int2 experts (four codes per byte): half the int4 bytes
     "glm52_int2_decode_T1": Workload("glm52_int2_decode_T1", replace(GLM52, weight_bits=2),
                                      TokenSpec(T=1, outlier_channels=61)),

@@ -206,19 +206,18 @@ def test_int8_experts_take_both_paths():
     assert out.path == 0
 
 
-def test_group_scales_only_on_the_gemv_path():
-    """Group-scaled int4 experts: valid groups are accepted (workspace sized),
-    and like int8 they run on the token-GEMV path only."""
+def test_group_scales_take_both_paths():
+    """Group-scaled int4 experts: valid groups are accepted (workspace sized)
+    and, like every format, have token-GEMV and grouped kernels: a large or
+    forced-grouped batch gets the grouped layout (no launch here)."""
     for G in (32, 64, 128, 256, 2048):
         assert ws_bytes(fake_layer(group_size=G), 4) > 0, G
     L = fake_layer(group_size=32)
-    p = ctypes.c_void_p(1 << 20)
-    F = lib().coli_moe_forward
-    assert F(ctypes.byref(L), p, 9, p, 0, p, 1 << 40, None) == _lib.COLI_EUNSUPPORTED      # grouped batch
-    assert F(ctypes.byref(L), p, 4, p, 4, p, 1 << 40, None) == _lib.COLI_EUNSUPPORTED      # forced grouped
-    X = lib().coli_moe_experts
-    assert X(ctypes.byref(L), p, p, p, p, 9, p, 0, p, 1 << 40, None) == _lib.COLI_EUNSUPPORTED
-
+    out = CWsLayout()
+    assert lib().coli_moe_workspace_layout(ctypes.byref(L), 512, 0, ctypes.byref(out)) == 0
+    assert out.path == 1
+    assert lib().coli_moe_workspace_layout(ctypes.byref(L), 4, _lib.COLI_PATH_GROUPED, ctypes.byref(out)) == 0
+    assert out.path == 1
 
 def test_int2_experts_take_both_paths():
     """int2 experts have token-GEMV and grouped kernels: the layout of a

@@ -43,6 +43,7 @@ def _tiny_batch_check(spec, L, ref, x, ws, y, label):
     st = PR.check_free_running(spec, PR.gpu_pairs(v, spec.has_shared, y), PR.batch_pairs(o),
                                lambda e: cache[e], say)
     say(f"  {label}: max rel {st['worst_y']:.2e}, bit-identical {st['y_bit_identical']:.4f}")
+    return st
 
 
 @pytest.mark.parametrize("T", [9, 64, 200])

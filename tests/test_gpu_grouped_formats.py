@@ -1,11 +1,17 @@
-"""GPU parity of the int8 and int2 weight formats on the grouped MFMA path
-(T > 8) through the C ABI: tiny and odd-shaped layers in full (every token
-and pair; the odd shape runs part-filled stages and scales loaded one by
-one), the compute-bound case of full tiles, path invariance against the
-token-GEMV path, the cross-format identities on the grouped kernels (int8
-or int2 layers whose codes an int4 layer holds too give the int4 layer's
-outputs bit for bit), and the whole GLM-5.2-shaped Zipf prefill (T = 512)
-against the threaded oracle."""
+"""GPU parity of the int8, int2 and group-scale weight formats on the
+grouped MFMA path (T > 8) through the C ABI: tiny and odd-shaped layers in
+full (every token and pair; the odd shape runs part-filled stages and scales
+loaded one by one), the compute-bound case of full tiles, path invariance
+against the token-GEMV path, the cross-format identities on the grouped
+kernels (int8 or int2 layers whose codes an int4 layer holds too give the
+int4 layer's outputs bit for bit), and the whole GLM-5.2-shaped Zipf
+prefill (T = 512) against the threaded oracle.
+
+Group scales: the grouped kernels compute every block term as the oracle
+does, s_g * (d_b * S_b) rounded once, and sum the terms in block order, so
+their results match the oracle's bit for bit as the row formats' do; the
+token-GEMV kernels sum in another order, so the two paths agree within the
+bar there."""
 from dataclasses import replace
 
 import numpy as np
@@ -24,7 +30,12 @@ from test_gpu_int2 import as_int4, codes_of
 
 pytestmark = pytest.mark.gpu
 TOL = 1e-4
-BITS = [8, 2]
+FORMATS = [dict(weight_bits=8), dict(weight_bits=2), dict(group_size=32), dict(group_size=64),
+           dict(group_size=128)]
+
+
+def fmt_id(f):
+    return f"int{f['weight_bits']}" if "weight_bits" in f else f"g{f['group_size']}"
 
 
 def say(*a):
@@ -37,10 +48,14 @@ def gpu():
     torch.cuda.set_device(0)
 
 
-@pytest.fixture(scope="module", params=BITS, ids=lambda b: f"int{b}")
+@pytest.fixture(scope="module", params=FORMATS, ids=fmt_id)
 def tiny_f(request):
-    spec = replace(S.TINY, weight_bits=request.param)
+    spec = replace(S.TINY, **request.param)
     return spec, device_layer(spec, 0, 0), OL.full_layer(spec, 0, 0)
+
+
+def label(spec):
+    return f"g{spec.group_size}" if spec.group_size else f"int{spec.weight_bits}"
 
 
 @pytest.mark.parametrize("T", [9, 64, 200])
@@ -48,29 +63,31 @@ def test_grouped_tiny_full_outputs(tiny_f, T):
     spec, L, ref = tiny_f
     x = S.tokens(S.TokenSpec(T=T, token_set=900 + T), spec.H, 0)
     ws = api.workspace(L, T)
-    say(f"grouped int{spec.weight_bits} tiny T={T}")
+    say(f"grouped {label(spec)} tiny T={T}")
     y = api.moe_forward(L, dev(x), ws).cpu().numpy()
-    _tiny_batch_check(spec, L, ref, x, ws, y, f"int{spec.weight_bits} tiny T={T}")
+    st = _tiny_batch_check(spec, L, ref, x, ws, y, f"{label(spec)} tiny T={T}")
+    if spec.group_size:                          # the oracle's terms in the oracle's order
+        assert st["h_bit_identical"] == 1.0 and st["y_bit_identical"] == 1.0
 
 
-@pytest.mark.parametrize("bits", BITS)
+@pytest.mark.parametrize("fmt", [dict(weight_bits=8), dict(weight_bits=2), dict(group_size=32)], ids=fmt_id)
 @pytest.mark.parametrize("T", [9, 40, 77])
-def test_grouped_odd_shape_full_outputs(bits, T):
+def test_grouped_odd_shape_full_outputs(fmt, T):
     """H = 320 (10 blocks: part-filled last stages), I = 96 (3 row tiles, 3
     down blocks); neither block count is a multiple of 4, so the scales load
     one by one."""
-    spec = S.LayerSpec(H=320, I=96, E=16, top_k=4, weight_bits=bits)
+    spec = S.LayerSpec(H=320, I=96, E=16, top_k=4, **fmt)
     L, ref = device_layer(spec, 0, 0), OL.full_layer(spec, 0, 0)
     x = S.tokens(S.TokenSpec(T=T, token_set=950 + T), spec.H, 0)
     ws = api.workspace(L, T)
-    say(f"grouped int{bits} odd shape T={T}")
+    say(f"grouped {label(spec)} odd shape T={T}")
     y = api.moe_forward(L, dev(x), ws).cpu().numpy()
-    _tiny_batch_check(spec, L, ref, x, ws, y, f"int{bits} odd T={T}")
+    _tiny_batch_check(spec, L, ref, x, ws, y, f"{label(spec)} odd T={T}")
 
 
-@pytest.mark.parametrize("bits", BITS)
-def test_grouped_hot_experts_full_tiles(bits):
-    spec = S.LayerSpec(H=256, I=128, E=16, top_k=2, hot_experts=2, weight_bits=bits)
+@pytest.mark.parametrize("fmt", [dict(weight_bits=8), dict(weight_bits=2), dict(group_size=64)], ids=fmt_id)
+def test_grouped_hot_experts_full_tiles(fmt):
+    spec = S.LayerSpec(H=256, I=128, E=16, top_k=2, hot_experts=2, **fmt)
     L, ref = device_layer(spec, 0, 0), OL.full_layer(spec, 0, 0)
     T = 100
     x = S.tokens(S.TokenSpec(T=T, token_set=17), spec.H, 0)
@@ -78,13 +95,15 @@ def test_grouped_hot_experts_full_tiles(bits):
     y = api.moe_forward(L, dev(x), ws).cpu().numpy()
     _, idx_o, _ = O.moe_forward(ref, x)
     assert len(np.unique(idx_o)) == 2
-    _tiny_batch_check(spec, L, ref, x, ws, y, f"int{bits} hot experts T={T}")
+    _tiny_batch_check(spec, L, ref, x, ws, y, f"{label(spec)} hot experts T={T}")
 
 
 @pytest.mark.parametrize("T", [1, 4, 8])
 def test_path_invariance(tiny_f, T):
-    """The same tokens on both paths: routing, h, Q8(h) and its scales bit
-    for bit per pair, outputs within the bar."""
+    """The same tokens on both paths: routing bit for bit; for the row
+    formats h, Q8(h) and its scales bit for bit per pair, for group scales
+    (whose token-GEMV kernels sum in another order) h within 2 f32 ulps;
+    outputs within the bar."""
     spec, L, _ = tiny_f
     x = S.tokens(S.TokenSpec(T=T, token_set=960 + T), spec.H, 0)
     ws = api.workspace(L, T)
@@ -93,12 +112,17 @@ def test_path_invariance(tiny_f, T):
     ym = api.moe_forward(L, dev(x), ws, flags=COLI_PATH_GROUPED).cpu().numpy()
     vm = ws_views(L, T, ws, COLI_PATH_GROUPED)
     assert vg["path"] == 0 and vm["path"] == 1
+    assert np.array_equal(vg["idx"], vm["idx"])
     for t in range(T):
         for j in range(spec.top_k):
             pg, pm = vg["pair_of"][t, j], vm["pair_of"][t, j]
-            assert np.array_equal(vg["h"][pg], vm["h"][pm])
-            assert np.array_equal(vg["hq"][pg], vm["hq"][pm]) and np.array_equal(vg["hs"][pg], vm["hs"][pm])
-    say(f"int{spec.weight_bits} path invariance T={T}: bit-identical outputs {np.mean(yg == ym):.4f}")
+            if spec.group_size:
+                hg, hm = vg["h"][pg], vm["h"][pm]
+                assert np.all(np.abs(hg - hm) <= 2 * np.spacing(np.maximum(np.abs(hg), np.abs(hm))))
+            else:
+                assert np.array_equal(vg["h"][pg], vm["h"][pm])
+                assert np.array_equal(vg["hq"][pg], vm["hq"][pm]) and np.array_equal(vg["hs"][pg], vm["hs"][pm])
+    say(f"{label(spec)} path invariance T={T}: bit-identical outputs {np.mean(yg == ym):.4f}")
     assert rel_err(ym, yg).max() <= TOL
 
 
@@ -171,10 +195,10 @@ def test_grouped_int2_equals_int4_on_shared_codes(tiny2, T):
     assert np.array_equal(y2, y4)
 
 
-@pytest.fixture(scope="module", params=["glm52_int8_prefill_T512", "glm52_int2_prefill_T512"])
+@pytest.fixture(scope="module", params=["glm52_int8_prefill_T512", "glm52_int2_prefill_T512", "glm52_g32_prefill_T512"])
 def glm_f_prefill(request):
     wl = S.WORKLOADS[request.param]
-    say(f"building the GLM-5.2-shaped int{wl.layer.weight_bits} layer with Zipf-skewed bias on device")
+    say(f"building the GLM-5.2-shaped {label(wl.layer)} layer with Zipf-skewed bias on device")
     L = device_layer(wl.layer, 0, 0)
     W, b = S.router(wl.layer, 0, 0)
     yield wl, L, W, b
@@ -186,5 +210,5 @@ def glm_f_prefill(request):
 def test_grouped_glm_prefill_T512(glm_f_prefill):
     """All 512 tokens and all 4,608 pairs of the Zipf-routed prefill batch."""
     wl, L, W, b = glm_f_prefill
-    st, load = _full_layer_check(wl, L, W, b, f"int{wl.layer.weight_bits} prefill T=512")
+    st, load = _full_layer_check(wl, L, W, b, f"{label(wl.layer)} prefill T=512")
     assert (load > 0).sum() > 100

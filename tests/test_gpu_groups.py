@@ -2,7 +2,8 @@
 columns, the scale-granularity variant) through the C ABI: the device packer
 bit-exact against the oracle's packer, whole layers against the oracle on
 the token-GEMV path (tiny and GLM-5.2-shaped, groups of 32, 64 and 128),
-the expert stage fed the oracle's routing, and the refusals off that path.
+and the expert stage fed the oracle's routing. The grouped path's kernels for
+group scales are tested in test_gpu_grouped_formats.py.
 
 Every block term s_g * (d_b * S_b) is computed exactly as the oracle
 computes it, but the f64 block sums run in another order, so a row product
@@ -18,7 +19,6 @@ import torch
 from dataclasses import replace
 
 from int4_quantized_expert_sigmoid_amd import api, COLI_ACCUMULATE
-from int4_quantized_expert_sigmoid_amd._lib import ColiError, COLI_EUNSUPPORTED, COLI_PATH_GROUPED
 from int4_quantized_expert_sigmoid_amd.synthetic import device_layer
 from oracle import layers as OL
 from oracle import oracle as O
@@ -111,19 +111,6 @@ def test_groups_spanning_the_row_equal_the_row_format():
         say(f"groups spanning the row T={T}: max rel {rel_err(yb, ya).max():.2e}, identical {np.mean(ya == yb):.4f}")
         assert rel_err(yb, ya).max() <= TOL
         assert np.mean(ya == yb) >= 0.99
-
-
-def test_groups_refused_off_the_gemv_path():
-    spec = replace(S.TINY, group_size=32)
-    L = device_layer(spec, 0, 0)
-    x = S.tokens(S.TokenSpec(T=9, token_set=1), spec.H, 0)
-    with pytest.raises(ColiError) as e:
-        api.moe_forward(L, dev(x), api.workspace(L, 9))
-    assert e.value.code == COLI_EUNSUPPORTED
-    ws1 = api.workspace(L, 1)
-    with pytest.raises(ColiError) as e:
-        api.moe_forward(L, dev(x[:1]), ws1, flags=COLI_PATH_GROUPED)
-    assert e.value.code == COLI_EUNSUPPORTED
 
 
 @pytest.fixture(scope="module")
