@@ -35,7 +35,9 @@ namespace coli {
 
 #ifdef COLI_TRACE
 // Profiling builds only: per-workgroup timestamps [launch][workgroup][4] =
-// start, end of the first phase, end, XCC id (100 MHz real-time counter).
+// start, end of the first phase, end (100 MHz real-time counter), and the
+// XCC id with the HW_ID register of the first wave in the upper 32 bits
+// (its CU, shader array, shader engine and SIMD).
 static unsigned long long *g_dec_trace = nullptr;
 extern "C" void coli_trace_decode_set(void *p)
 {
@@ -49,7 +51,9 @@ __device__ __forceinline__ void trace_mark(unsigned long long *tr, int launch, i
     if (tr && threadIdx.x == 0 && blockIdx.x < TRACE_WG) {
         unsigned long long *p = tr + ((size_t)launch * TRACE_WG + blockIdx.x) * 4;
         p[slot] = __builtin_amdgcn_s_memrealtime();
-        if (slot == 2) p[3] = __builtin_amdgcn_s_getreg((3 << 11) | 20);
+        if (slot == 2)
+            p[3] = (unsigned long long)__builtin_amdgcn_s_getreg((3 << 11) | 20) |
+                   ((unsigned long long)__builtin_amdgcn_s_getreg((31 << 11) | 4) << 32);
     }
 }
 #define TRACE(args, launch, slot) trace_mark((args).trace, launch, slot)

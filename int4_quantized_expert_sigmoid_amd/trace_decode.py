@@ -16,7 +16,10 @@ in us from the router launch's first workgroup:
 The stamps are the 100 MHz real-time counter read by the first lane of
 each workgroup (10 ns resolution).
 
-    python -m int4_quantized_expert_sigmoid_amd.trace_decode [workload]
+    python -m int4_quantized_expert_sigmoid_amd.trace_decode [workload] [--dump FILE.npz]
+
+--dump also writes the raw stamps of every call (launch stamps [call][3][4096][4]
+and selection marks [call][4096][8], 100 MHz ticks) for offline analysis.
 """
 import ctypes
 import os
@@ -43,6 +46,11 @@ def main(argv):
     _lib.LIB_PATH = build.TRACE_LIB
     L = _lib.lib()
     L.coli_trace_decode_set.argtypes = [ctypes.c_void_p]
+    dump = None
+    if "--dump" in argv:
+        i = argv.index("--dump")
+        dump = argv[i + 1]
+        argv = argv[:i] + argv[i + 2:]
     name = argv[0] if argv else "glm52_decode_T1"
     wl = S.WORKLOADS[name]
     spec, T = wl.layer, wl.tokens.T
@@ -75,6 +83,8 @@ def main(argv):
         a = stamps.cpu().numpy()
         res.append((a[:3 * TRACE_WG * 4].reshape(3, TRACE_WG, 4).copy(), a[3 * TRACE_WG * 4:].reshape(TRACE_WG, 8).copy()))
 
+    if dump:
+        np.savez_compressed(dump, launches=np.stack([r[0] for r in res]), marks=np.stack([r[1] for r in res]))
     E, I, H = spec.E, spec.I, spec.H
     nrb = I // 32
     nsh = nrb if spec.has_shared else 0
