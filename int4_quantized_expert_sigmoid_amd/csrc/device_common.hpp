@@ -258,6 +258,22 @@ __device__ __forceinline__ void q8_block_reordered(const float *__restrict__ src
     *dsc = d;
 }
 
+// Q8 of one 32-wide block by the 32 lanes of an aligned half-wave, lane i
+// holding element v: absmax = fmaxf over 0 and every |v| (as q8_block_vals
+// takes it, so NaN elements are passed over alike), the same scale and
+// rounding; lane i stores its code in the reordered position and lane 0 the
+// scale. Bit for bit q8_block_reordered's output.
+__device__ __forceinline__ void q8_block_lanes(float v, int i, int8_t *__restrict__ dst, float *__restrict__ dsc)
+{
+    float a = fmaxf(0.0f, fabsf(v));
+#pragma unroll
+    for (int o = 16; o > 0; o >>= 1) a = fmaxf(a, __shfl_xor(a, o, 32));
+    float d, id;
+    q8_scale(a, d, id);
+    dst[(i & ~7) + perm8(i & 7)] = (int8_t)round_clamp(__fmul_rn(v, id), -127.0f, 127.0f);
+    if (i == 0) *dsc = d;
+}
+
 template <typename T>
 __device__ __forceinline__ T wave_max(T v, int width = 64)
 {

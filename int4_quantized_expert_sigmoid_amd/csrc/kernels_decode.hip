@@ -83,9 +83,12 @@ __global__ void __launch_bounds__(512) k_router(RouterArgs r)
 {
     __shared__ double red[8 * NT];
     TRACE(r, 0, 0);
+    // Q8(x): one block per half-wave, workgroup e taking blocks e, e + E, ...
+    // (one each at T = 1), so no workgroup's logits wait behind all of them
     const long nb = (long)r.T * (r.H / QK);
-    for (long b = (long)blockIdx.x * blockDim.x + threadIdx.x; b < nb; b += (long)r.E * blockDim.x)
-        q8_block_reordered(r.x + b * QK, r.xq + b * QK, r.xs + b);
+    const int hw = (int)(threadIdx.x >> 5), hl = (int)(threadIdx.x & 31);
+    for (long b = (long)blockIdx.x + (long)r.E * hw; b < nb; b += (long)r.E * (blockDim.x >> 5))
+        q8_block_lanes(r.x[b * QK + hl], hl, r.xq + b * QK, r.xs + b);
     logits_expert<NT>(r.W, r.x, r.T, r.H, r.E, blockIdx.x, r.z, red, r.bias, r.key, r.sig);
     TRACE(r, 0, 2);
 }
@@ -116,23 +119,18 @@ __global__ void __launch_bounds__(RMS_BLOCK) k_router_norm(RouterArgs r)
     double sc[NT];
     rms_scales<NT>(r.x, r.T, r.H, r.eps, r.vec != 0, red, sc);
 
-    // Q8 of the normalised rows, the workgroups sharing the blocks
+    // Q8 of the normalised rows: one block per half-wave, workgroup e taking
+    // blocks e, e + E, ... (one each at T = 1)
     const int nblk = r.H / QK;
     const long nb = (long)r.T * nblk;
-    for (long b = (long)e * RMS_BLOCK + tid; b < nb; b += (long)r.E * RMS_BLOCK) {
+    const int hw = tid >> 5, hl = tid & 31;
+    for (long b = (long)e + (long)r.E * hw; b < nb; b += (long)r.E * (RMS_BLOCK >> 5)) {
         const int t = (int)(b / nblk), c0 = (int)(b % nblk) * QK;
-        float v[QK];
         double st = sc[0];
 #pragma unroll
         for (int k = 1; k < NT; ++k) st = t == k ? sc[k] : st;
-#pragma unroll
-        for (int i = 0; i < QK; ++i) v[i] = rms_apply(r.x[(long)t * r.H + c0 + i], st, r.gamma[c0 + i]);
-        uint32_t o[8];
-        float d;
-        q8_block_vals(v, o, d);
-        reinterpret_cast<uint4 *>(r.xq + b * QK)[0] = make_uint4(o[0], o[1], o[2], o[3]);
-        reinterpret_cast<uint4 *>(r.xq + b * QK)[1] = make_uint4(o[4], o[5], o[6], o[7]);
-        r.xs[b] = d;
+        const float v = rms_apply(r.x[(long)t * r.H + c0 + hl], st, r.gamma[c0 + hl]);
+        q8_block_lanes(v, hl, r.xq + b * QK, r.xs + b);
     }
 
     // logits of expert e from the normalised rows, summed in logits_expert's order
