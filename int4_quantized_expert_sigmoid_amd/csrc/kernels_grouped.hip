@@ -433,7 +433,7 @@ __device__ __forceinline__ double gs_term(double acc, int c, double f, double sg
 // times its f64 factor into acc (with group scales, each term times its
 // row's group scale; gsh: log2(group / 32)). m: the matrix's LDS slot; buf: the stage's
 // activation buffer; b0: its first block.
-template <bool FULL, bool NARROW, int NM, int WB>
+template <bool FULL, bool NARROW, int NM, int WB, bool PIPE = false>
 __device__ __forceinline__ void stage_pass(const StageLds<NM, WB> &sm, int m, double (&acc)[TileShape<NARROW>::NACC],
                                            int buf, int b0, int nblk, int gsh = 0)
 {
@@ -441,7 +441,37 @@ __device__ __forceinline__ void stage_pass(const StageLds<NM, WB> &sm, int m, do
     const int g0 = b0 >> gsh;                    // the stage's first group
     constexpr int KS = stage_blocks<WB>();
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    if constexpr (!NARROW) {
+    if constexpr (PIPE && FULL && !NARROW && WB == 4) {
+        // int4, whole stages: the LDS operands of the next block pair are
+        // read while the current pair's MFMAs and rescales run, so only a
+        // stage's first pair waits out an LDS round trip
+        const v16i zero = {};
+        const int n = lane & 31, half = lane >> 5;
+        const int sw = wsw<WB>(n), sx = xsw<WB>(n);
+        v4i wr[2], xa[2], xb[2];
+        v2d dq[2];
+        auto fetch = [&](int j, int slot) {
+            wr[slot] = sm.w[wave][m][n][(j + half) ^ sw];
+            xa[slot] = sm.x[buf][n][(2 * j + half) ^ sx];
+            xb[slot] = sm.x[buf][n][(2 * j + 2 + half) ^ sx];
+            dq[slot] = read_d2<NM, WB>(sm, buf, n, j);
+        };
+        fetch(0, 0);
+#pragma unroll
+        for (int j = 0; j < KS; j += 2) {
+            const int cur = (j >> 1) & 1;
+            if (j + 2 < KS) fetch(j + 2, cur ^ 1);
+            __builtin_amdgcn_sched_barrier(0);   // keeps the next pair's reads above this pair's work
+            uint2 wa, wb;
+            split_pair(as_u4(wr[cur]), wa, wb);
+            const v16i ca = __builtin_amdgcn_mfma_i32_32x32x32_i8(unpack8(wa), xa[cur], zero, 0, 0, 0);
+            const v16i cb = __builtin_amdgcn_mfma_i32_32x32x32_i8(unpack8(wb), xb[cur], zero, 0, 0, 0);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[i] = fma((double)ca[i], dq[cur][0], acc[i]);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[i] = fma((double)cb[i], dq[cur][1], acc[i]);
+        }
+    } else if constexpr (!NARROW) {
         const v16i zero = {};
         const int n = lane & 31, half = lane >> 5;
         const int sw = wsw<WB>(n), sx = xsw<WB>(n);
@@ -528,12 +558,130 @@ __device__ __forceinline__ void stage_pass(const StageLds<NM, WB> &sm, int m, do
 }
 
 // FULL: the K blocks fill whole stages (nblk % KS == 0), so a stage's blocks
-// need no bounds tests and the scheduler sees a stage as straight-line code
-// (held to 3 waves per SIMD, the occupancy of the general form: about 2%
-// faster at the GLM prefill shape).
+// need no bounds tests and the scheduler sees a stage as straight-line code.
+//
+// Two gate/up tile forms. Paired waves (gateup_tile1): wave w runs matrix
+// w & 1 (0 gate, 1 up) of row tile rg * GU_RT + (w >> 1), so each wave holds
+// one matrix's accumulators and the four waves still share one stage of
+// activations; at the end the gate wave hands its g values to its up partner
+// through LDS. Both matrices per wave (gateup_tile2): four row tiles per
+// workgroup, each wave running the gate pass, then the up pass of a stage.
+constexpr int GU_RT = WAVES / 2;   // row tiles per gate/up workgroup of paired waves
+
 template <bool FULL, bool NARROW, int WB>
-__device__ __forceinline__ void gateup_tile(const GroupedArgs &a, StageLds<2, WB> &sm, int e, int p0, int np, int rt,
-                                            bool rows_ok)
+__device__ __forceinline__ void gateup_tile1(const GroupedArgs &a, StageLds<1, WB> &sm, int e, int p0, int np, int rt,
+                                             int mat, bool rows_ok)
+{
+    constexpr int NACC = TileShape<NARROW>::NACC, KS = stage_blocks<WB>(), NXL = x_loads<WB>();
+    const int n_rt = a.I / QK;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int nblk = a.H / QK;
+    constexpr bool GS = WB == WB_GROUPS;
+    const long rowb = (long)a.H * code_bits<WB>() / 8;
+    const long wrow0 = (long)e * a.I + (long)min(rt, n_rt - 1) * QK + (lane >> 3);
+    const uint8_t *wrow = (mat ? a.q_b : a.q_a) + wrow0 * rowb;
+    const int ngs = nblk >> a.gsh;               // group scales per row
+    const float *srow = (mat ? a.s_b : a.s_a) + ((long)e * a.I + (long)min(rt, n_rt - 1) * QK + (lane & 31)) * ngs;
+    v2f sn = {};
+    const int8_t *xrow[NXL];
+#pragma unroll
+    for (int i = 0; i < NXL; ++i) xrow[i] = a.act + (long)a.pair_tok[p0 + stage_pair<WB>(i, np)] * a.H;
+    const int pd = min(d_pair<WB>(lane), TILE_N - 1) < np ? min(d_pair<WB>(lane), TILE_N - 1) : 0;
+    const float *drow = a.act_s + (long)a.pair_tok[p0 + pd] * nblk;   // used by wave 0
+    const bool vec_scales = nblk % 4 == 0;
+
+    double acc[NACC];
+#pragma unroll
+    for (int i = 0; i < NACC; ++i) acc[i] = 0.0;
+
+    // the next stage's rows and activations load while the current one
+    // computes
+    const int nst = (nblk + KS - 1) / KS;
+    typename WReg<WB>::type wn[4];
+    v4i xn[NXL];
+    v4f dn = {};
+    load_x<WB>(xn, 0, nblk, xrow);
+    if (wave == 0) dn = load_d<WB>(0, nblk, drow, vec_scales);
+    if (rows_ok) {
+        load_w<WB>(wn, 0, nblk, wrow, rowb);
+        if constexpr (GS) sn = load_s<WB>(0, a.gsh, srow, ngs);
+        store_w<1, WB>(sm, 0, wn);
+        if constexpr (GS) store_s<1, WB>(sm, 0, sn);
+    }
+    store_x<1, WB>(sm, 0, xn);
+    if (wave == 0) store_d<1, WB>(sm, 0, dn, np);
+    __syncthreads();
+    for (int s = 0; s < nst; ++s) {
+        const bool more = s + 1 < nst;
+        if (more) {
+            load_x<WB>(xn, s + 1, nblk, xrow);
+            if (wave == 0) dn = load_d<WB>(s + 1, nblk, drow, vec_scales);
+            if (rows_ok) {
+                load_w<WB>(wn, s + 1, nblk, wrow, rowb);
+                if constexpr (GS) sn = load_s<WB>(s + 1, a.gsh, srow, ngs);
+            }
+        }
+        issue_fence();
+        if (rows_ok) stage_pass<FULL, NARROW, 1, WB, true>(sm, 0, acc, s & 1, s * KS, nblk, a.gsh);
+        issue_fence();
+        if (more) {
+            if (rows_ok) {
+                store_w<1, WB>(sm, 0, wn);
+                if constexpr (GS) store_s<1, WB>(sm, 0, sn);
+            }
+            store_x<1, WB>(sm, (s + 1) & 1, xn);
+            if (wave == 0) store_d<1, WB>(sm, (s + 1) & 1, dn, np);
+        }
+        __syncthreads();
+    }
+    // The weight stages are done with: the gate wave leaves g (f32, after
+    // its row scale) in its own weight slot, [accumulator][lane], for the up
+    // wave of the same row tile (the next wave), whose lanes hold the same
+    // (row, pair) elements.
+    float *xg = reinterpret_cast<float *>(&sm.w[wave & ~1][0][0][0]);
+    if (rows_ok && mat == 0) {
+#pragma unroll
+        for (int i = 0; i < NACC; ++i) {
+            const long grow = (long)e * a.I + (long)rt * QK + acc_row<NARROW>(i, lane);
+            // with group scales every block term carries its scale: no row scale
+            xg[i * 64 + lane] = GS ? (float)acc[i] : (float)((double)a.s_a[grow] * acc[i]);
+        }
+    }
+    __syncthreads();
+    if (!rows_ok || mat == 0) return;
+    // epilogue (up wave): h = silu(g)*u, Q8 over the tile's 32 rows per pair
+    // (held by 2 lanes of a 32-pair tile, 4 lanes of a narrow one)
+    float hv[NACC];
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < NACC; ++i) {
+        const long grow = (long)e * a.I + (long)rt * QK + acc_row<NARROW>(i, lane);
+        const float gf = xg[i * 64 + lane];
+        const float uf = GS ? (float)acc[i] : (float)((double)a.s_b[grow] * acc[i]);
+        hv[i] = (float)(silu_f64((double)gf) * (double)uf);
+        amax = fmaxf(amax, fabsf(hv[i]));
+    }
+    amax = fmaxf(amax, __shfl_xor(amax, 32));
+    if constexpr (NARROW) amax = fmaxf(amax, __shfl_xor(amax, 16));
+    const int n = acc_pair<NARROW>(lane);
+    if (n >= np) return;
+    float d, id;
+    q8_scale(amax, d, id);
+    const long base = (long)(p0 + n) * a.I + (long)rt * QK;
+#pragma unroll
+    for (int i = 0; i < NACC; ++i) {
+        const int r = acc_row<NARROW>(i, lane);
+        a.h[base + r] = hv[i];
+        a.hq[base + (r & ~7) + perm8(r & 7)] = (int8_t)round_clamp(__fmul_rn(hv[i], id), -127.0f, 127.0f);
+    }
+    if (lane < TileShape<NARROW>::NPAIR) a.hs[(long)(p0 + n) * n_rt + rt] = d;
+}
+
+// Per stage: gate pass, then up pass, each wave holding both matrices of its
+// row tile.
+template <bool FULL, bool NARROW, int WB>
+__device__ __forceinline__ void gateup_tile2(const GroupedArgs &a, StageLds<2, WB> &sm, int e, int p0, int np, int rt,
+                                             bool rows_ok)
 {
     constexpr int NACC = TileShape<NARROW>::NACC, KS = stage_blocks<WB>(), NXL = x_loads<WB>();
     const int n_rt = a.I / QK;
@@ -643,26 +791,42 @@ __device__ __forceinline__ void gateup_tile(const GroupedArgs &a, StageLds<2, WB
     if (lane < TileShape<NARROW>::NPAIR) a.hs[(long)(p0 + n) * n_rt + rt] = d;
 }
 
+// The form per weight format, as measured at the GLM-5.2 prefill shape:
+// int8 and group-scaled weights pair the waves (13-16% faster there), int4
+// and int2 keep both matrices per wave (4-6% faster there).
+template <int WB> constexpr bool gu_paired() { return WB == 8 || WB == WB_GROUPS; }
+template <int WB> constexpr int gu_row_tiles() { return gu_paired<WB>() ? GU_RT : WAVES; }
+
+template <int WB> struct GuLds { typedef StageLds<gu_paired<WB>() ? 1 : 2, WB> type; };
+
 template <bool FULL, int WB>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) k_gateup_mfma(GroupedArgs a)
 {
-    __shared__ StageLds<2, WB> sm;
+    __shared__ typename GuLds<WB>::type sm;
+    constexpr int RTW = gu_row_tiles<WB>();
     const int n_rt = a.I / QK;
-    const int nrg = (n_rt + WAVES - 1) / WAVES;
+    const int nrg = (n_rt + RTW - 1) / RTW;
     int tile, rg;
     tile_rg(blockIdx.x, nrg, a.ntiles_max, tile, rg);
     if (tile >= a.ctrl[CTRL_N_TILES_GU]) return;          // uniform over the workgroup
     const int wave = threadIdx.x >> 6;
-    const int rt = rg * WAVES + wave;
-    const bool rows_ok = rt < n_rt;                       // waves past the last row tile only stage activations
     const int2 td = a.tiles[tile];
     const int e = td.x, p0 = td.y;
     const int np = min(TILE_N, a.expert_off[e + 1] - p0);
-    if (np <= 16) gateup_tile<FULL, true, WB>(a, sm, e, p0, np, rt, rows_ok);
-    else gateup_tile<FULL, false, WB>(a, sm, e, p0, np, rt, rows_ok);
+    if constexpr (gu_paired<WB>()) {
+        const int rt = rg * GU_RT + (wave >> 1), mat = wave & 1;
+        const bool rows_ok = rt < n_rt;                   // waves past the last row tile only stage activations
+        if (np <= 16) gateup_tile1<FULL, true, WB>(a, sm, e, p0, np, rt, mat, rows_ok);
+        else gateup_tile1<FULL, false, WB>(a, sm, e, p0, np, rt, mat, rows_ok);
+    } else {
+        const int rt = rg * WAVES + wave;
+        const bool rows_ok = rt < n_rt;
+        if (np <= 16) gateup_tile2<FULL, true, WB>(a, sm, e, p0, np, rt, rows_ok);
+        else gateup_tile2<FULL, false, WB>(a, sm, e, p0, np, rt, rows_ok);
+    }
 }
 
-template <bool NARROW, int WB>
+template <bool FULL, bool NARROW, int WB>
 __device__ __forceinline__ void down_tile(const GroupedArgs &a, StageLds<1, WB> &sm, int e, int p0, int np, int rt,
                                           bool rows_ok)
 {
@@ -714,7 +878,7 @@ __device__ __forceinline__ void down_tile(const GroupedArgs &a, StageLds<1, WB> 
             }
         }
         issue_fence();
-        if (rows_ok) stage_pass<false, NARROW, 1, WB>(sm, 0, acc, s & 1, s * KS, nblk, a.gsh);
+        if (rows_ok) stage_pass<FULL, NARROW, 1, WB, true>(sm, 0, acc, s & 1, s * KS, nblk, a.gsh);
         issue_fence();
         if (more) {
             if (rows_ok) {
@@ -741,7 +905,7 @@ __device__ __forceinline__ void down_tile(const GroupedArgs &a, StageLds<1, WB> 
     }
 }
 
-template <int WB>
+template <bool FULL, int WB>
 __global__ void __launch_bounds__(256) k_down_mfma(GroupedArgs a)
 {
     __shared__ StageLds<1, WB> sm;
@@ -756,8 +920,8 @@ __global__ void __launch_bounds__(256) k_down_mfma(GroupedArgs a)
     const int2 td = a.tiles[tile];
     const int e = td.x, p0 = td.y;
     const int np = min(TILE_N, a.expert_off[e + 1] - p0);
-    if (np <= 16) down_tile<true, WB>(a, sm, e, p0, np, rt, rows_ok);
-    else down_tile<false, WB>(a, sm, e, p0, np, rt, rows_ok);
+    if (np <= 16) down_tile<FULL, true, WB>(a, sm, e, p0, np, rt, rows_ok);
+    else down_tile<FULL, false, WB>(a, sm, e, p0, np, rt, rows_ok);
 }
 
 GroupedArgs make_args(const WsLayout &lay, char *ws, const coli_moe_layer &L)
@@ -791,7 +955,8 @@ hipError_t launch_gateup_grouped(const coli_moe_layer &L, int T, const WsLayout 
     a.q_a = L.gate_q; a.s_a = L.gate_s; a.q_b = L.up_q; a.s_b = L.up_s;
     a.act = reinterpret_cast<const int8_t *>(ws + lay.xq);
     a.act_s = reinterpret_cast<const float *>(ws + lay.xs);
-    const int nrg = (L.I / QK + WAVES - 1) / WAVES;
+    const int rtw = (L.group_size || L.weight_bits == 8) ? GU_RT : WAVES;   // gu_row_tiles<WB>()
+    const int nrg = (L.I / QK + rtw - 1) / rtw;
     const dim3 grid((unsigned)(max_tiles(lay, L) * nrg));
     const int nblk = L.H / QK;
     a.gsh = group_shift(L);
@@ -823,10 +988,23 @@ hipError_t launch_down_grouped(const coli_moe_layer &L, int T, const WsLayout &l
     const int nrg = (L.H / QK + WAVES - 1) / WAVES;
     const dim3 grid((unsigned)(max_tiles(lay, L) * nrg));
     a.gsh = group_shift(L);
-    if (L.group_size) COLI_LAUNCH(k_down_mfma<WB_GROUPS>, grid, dim3(64 * WAVES), 0, s, a);
-    else if (L.weight_bits == 8) COLI_LAUNCH(k_down_mfma<8>, grid, dim3(64 * WAVES), 0, s, a);
-    else if (L.weight_bits == 2) COLI_LAUNCH(k_down_mfma<2>, grid, dim3(64 * WAVES), 0, s, a);
-    else COLI_LAUNCH(k_down_mfma<4>, grid, dim3(64 * WAVES), 0, s, a);
+    // whole stages (I/32 a multiple of the stage's blocks, as at I = 2048)
+    // drop the per-block bounds tests; int4 then also reads LDS one block
+    // pair ahead
+    const int nblk = L.I / QK;
+    if (L.group_size) {
+        if (nblk % stage_blocks<WB_GROUPS>() == 0) COLI_LAUNCH((k_down_mfma<true, WB_GROUPS>), grid, dim3(64 * WAVES), 0, s, a);
+        else COLI_LAUNCH((k_down_mfma<false, WB_GROUPS>), grid, dim3(64 * WAVES), 0, s, a);
+    } else if (L.weight_bits == 8) {
+        if (nblk % stage_blocks<8>() == 0) COLI_LAUNCH((k_down_mfma<true, 8>), grid, dim3(64 * WAVES), 0, s, a);
+        else COLI_LAUNCH((k_down_mfma<false, 8>), grid, dim3(64 * WAVES), 0, s, a);
+    } else if (L.weight_bits == 2) {
+        if (nblk % stage_blocks<2>() == 0) COLI_LAUNCH((k_down_mfma<true, 2>), grid, dim3(64 * WAVES), 0, s, a);
+        else COLI_LAUNCH((k_down_mfma<false, 2>), grid, dim3(64 * WAVES), 0, s, a);
+    } else {
+        if (nblk % stage_blocks<4>() == 0) COLI_LAUNCH((k_down_mfma<true, 4>), grid, dim3(64 * WAVES), 0, s, a);
+        else COLI_LAUNCH((k_down_mfma<false, 4>), grid, dim3(64 * WAVES), 0, s, a);
+    }
     return hipGetLastError();
 }
 
