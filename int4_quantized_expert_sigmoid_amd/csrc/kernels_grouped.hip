@@ -379,18 +379,25 @@ __device__ __forceinline__ long unpack8_2b(uint32_t w, int hi)
 
 // The 16 bytes of block j (of the stage) that lane half `half` multiplies,
 // as the 32x32x32 MFMA's operand, for blocks j and j+1: int4 chunks hold a
-// whole block (one permlane swap hands each half its 8 packed bytes of both,
-// then the nibbles are unpacked x16); int8 chunks hold one half of a block.
+// whole block (each half takes its 8 packed bytes of both, read directly or
+// by one 16-byte read and a permlane swap, then the nibbles are unpacked
+// x16); int8 chunks hold one half of a block.
 template <int NM, int WB>
 __device__ __forceinline__ void w_pair(const StageLds<NM, WB> &sm, int wave, int m, int n, int half, int sw, int j,
                                        v4i &a, v4i &b)
 {
-    if constexpr (int4_codes<WB>()) {
+    if constexpr (int4_codes<WB>() && NM == 2) {
+        // both matrices per wave: one 16-byte read and the swap (reading the
+        // two 8-byte halves directly costs that kernel 4 spilled registers)
         const uint4 wp = as_u4(sm.w[wave][m][n][(j + half) ^ sw]);
         uint2 wa, wb;
         split_pair(wp, wa, wb);
         a = unpack8(wa);
         b = unpack8(wb);
+    } else if constexpr (int4_codes<WB>()) {    // half h reads its 8 packed bytes of each block
+        const char *row = reinterpret_cast<const char *>(&sm.w[wave][m][n][0]);
+        a = unpack8(*reinterpret_cast<const uint2 *>(row + 16 * (j ^ sw) + 8 * half));
+        b = unpack8(*reinterpret_cast<const uint2 *>(row + 16 * ((j + 1) ^ sw) + 8 * half));
     } else if constexpr (WB == 2) {              // blocks j, j+1 share chunk j/2; half h takes dword h of each
         const char *ch = reinterpret_cast<const char *>(&sm.w[wave][m][n][(j >> 1) ^ sw]);
         a = unpack16_2b(*reinterpret_cast<const uint32_t *>(ch + 4 * half));
@@ -448,10 +455,13 @@ __device__ __forceinline__ void stage_pass(const StageLds<NM, WB> &sm, int m, do
         const v16i zero = {};
         const int n = lane & 31, half = lane >> 5;
         const int sw = wsw<WB>(n), sx = xsw<WB>(n);
-        v4i wr[2], xa[2], xb[2];
+        const char *wrow = reinterpret_cast<const char *>(&sm.w[wave][m][n][0]);
+        uint2 wa[2], wb[2];
+        v4i xa[2], xb[2];
         v2d dq[2];
-        auto fetch = [&](int j, int slot) {
-            wr[slot] = sm.w[wave][m][n][(j + half) ^ sw];
+        auto fetch = [&](int j, int slot) {        // half h: its 8 packed bytes of blocks j and j+1
+            wa[slot] = *reinterpret_cast<const uint2 *>(wrow + 16 * (j ^ sw) + 8 * half);
+            wb[slot] = *reinterpret_cast<const uint2 *>(wrow + 16 * ((j + 1) ^ sw) + 8 * half);
             xa[slot] = sm.x[buf][n][(2 * j + half) ^ sx];
             xb[slot] = sm.x[buf][n][(2 * j + 2 + half) ^ sx];
             dq[slot] = read_d2<NM, WB>(sm, buf, n, j);
@@ -462,10 +472,8 @@ __device__ __forceinline__ void stage_pass(const StageLds<NM, WB> &sm, int m, do
             const int cur = (j >> 1) & 1;
             if (j + 2 < KS) fetch(j + 2, cur ^ 1);
             __builtin_amdgcn_sched_barrier(0);   // keeps the next pair's reads above this pair's work
-            uint2 wa, wb;
-            split_pair(as_u4(wr[cur]), wa, wb);
-            const v16i ca = __builtin_amdgcn_mfma_i32_32x32x32_i8(unpack8(wa), xa[cur], zero, 0, 0, 0);
-            const v16i cb = __builtin_amdgcn_mfma_i32_32x32x32_i8(unpack8(wb), xb[cur], zero, 0, 0, 0);
+            const v16i ca = __builtin_amdgcn_mfma_i32_32x32x32_i8(unpack8(wa[cur]), xa[cur], zero, 0, 0, 0);
+            const v16i cb = __builtin_amdgcn_mfma_i32_32x32x32_i8(unpack8(wb[cur]), xb[cur], zero, 0, 0, 0);
 #pragma unroll
             for (int i = 0; i < 16; ++i) acc[i] = fma((double)ca[i], dq[cur][0], acc[i]);
 #pragma unroll
