@@ -1,8 +1,9 @@
-"""HIP-graph replays of the decode path for every weight format (int4 rows,
-int8, int2, int4 with group scales): a captured coli_moe_forward replayed
-several times, with the same work done eagerly between replays, gives the
-eager result bit for bit each time (the launches keep no state between
-calls that a replay could see stale)."""
+"""HIP-graph replays of the layer for every weight format (int4 rows, int8,
+int2, int4 with group scales), on the decode path (T = 1, 4) and the grouped
+MFMA path (T = 40: routing buckets, tile lists and the grouped kernels): a
+captured coli_moe_forward replayed several times, with the same work done
+eagerly between replays, gives the eager result bit for bit each time (the
+launches keep no state between calls that a replay could see stale)."""
 from dataclasses import replace
 
 import numpy as np
@@ -28,7 +29,7 @@ def gpu():
 
 
 @pytest.mark.parametrize("fmt", list(FORMATS))
-@pytest.mark.parametrize("T", [1, 4])
+@pytest.mark.parametrize("T", [1, 4, 40])
 def test_format_graph_replays(fmt, T):
     spec = FORMATS[fmt]
     L = device_layer(spec, 0, 5)

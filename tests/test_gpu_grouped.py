@@ -174,6 +174,34 @@ def test_grouped_glm_hot8_T512(glm_hot8):
     assert (load > 0).sum() == 8 and load.max() == 512
 
 
+def test_grouped_glm_prefill_graph_replays(glm_prefill):
+    """The timed prefill configuration: the T = 512 Zipf-routed layer call
+    captured in a HIP graph and replayed, with eager calls on another input
+    between replays, gives the eager output bit for bit every time."""
+    wl, L, W, b = glm_prefill
+    T = wl.tokens.T
+    x = dev(S.tokens(wl.tokens, wl.layer.H, 0))
+    x2 = dev(S.tokens(wl.tokens, wl.layer.H, 1))
+    ws = api.workspace(L, T)
+    eager = api.moe_forward(L, x, ws).clone()
+    eager2 = api.moe_forward(L, x2, ws).clone()
+    y = torch.empty_like(x)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        api.moe_forward(L, x, ws, y=y, stream=torch.cuda.current_stream())
+    say("GLM prefill T=512 graph replays")
+    for rep in range(3):
+        y.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y, eager), f"replay {rep}"
+        assert torch.equal(api.moe_forward(L, x2, ws), eager2)   # eager work between replays
+        torch.cuda.synchronize()
+    assert not torch.equal(eager, eager2)
+
+
 def test_path_invariance_glm_T4(glm_prefill):
     wl, L, W, b = glm_prefill
     x = S.tokens(S.TokenSpec(T=4, rho=0.8, outlier_channels=61), wl.layer.H, 0)
