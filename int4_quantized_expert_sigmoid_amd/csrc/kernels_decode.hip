@@ -31,6 +31,10 @@ __device__ unsigned long long *coli_sel_marks;
 #include "route_device.hpp"
 #include "internal.hpp"
 
+#include <map>
+#include <mutex>
+#include <utility>
+
 namespace coli {
 
 #ifdef COLI_TRACE
@@ -179,7 +183,7 @@ struct SelGuShared {
 };
 
 template <int NT, int KPL, int WB, bool GS>
-__global__ void __launch_bounds__(256) k_select_gateup(SelGuArgs a, GemvArgs g, int n_shared_wg)
+__global__ void __launch_bounds__(256) k_select_gateup(SelGuArgs a, GemvArgs g, int n_shared_wg, int n_routed_wg)
 {
     __shared__ GateUpShared<NT> sh;
     __shared__ SelGuShared<KPL> su;
@@ -196,7 +200,6 @@ __global__ void __launch_bounds__(256) k_select_gateup(SelGuArgs a, GemvArgs g, 
                          u, &su.kw[0][0], b == 0);
     TRACE(a, 1, 1);
     const int nrb = g.I / QK;
-    const int item = a.has_shared + b / nrb, rb = b % nrb;
     const int n_items = u.n_items;
     if (b == 0) {
         const int tid = threadIdx.x, np = a.T * a.top_k;
@@ -217,14 +220,22 @@ __global__ void __launch_bounds__(256) k_select_gateup(SelGuArgs a, GemvArgs g, 
             for (int t = tid; t < a.T; t += blockDim.x) a.shared_pair[t] = t;
         if (tid == 0) a.ctrl[CTRL_N_ITEMS] = n_items;
     }
-    if (item >= n_items) return;                 // uniform over the workgroup
-    ItemDesc it;
-    it.item = item;
-    it.e = u.item_e[item];
-    it.nt = u.item_nt[item];
+    // The routed units (item, 32-row block) of the union, workgroup b taking
+    // units b, b + n_routed_wg, ...: the grid is no larger than fits on the
+    // chip at once, so no workgroup waits for another's slot, and none
+    // routes only to find its item past the union (a batch of T tokens has
+    // up to T * k items, usually far fewer). Uniform over the workgroup.
+    const int n_units = (n_items - a.has_shared) * nrb;
+    for (int un = b; un < n_units; un += n_routed_wg) {
+        const int item = a.has_shared + un / nrb, rb = un % nrb;
+        ItemDesc it;
+        it.item = item;
+        it.e = u.item_e[item];
+        it.nt = u.item_nt[item];
 #pragma unroll
-    for (int s = 0; s < MAX_SLOTS; ++s) it.tok[s] = s < it.nt ? u.item_tok[item * MAX_SLOTS + s] : 0;
-    gateup_rows<NT, GemvTuneW<NT, WB>::RC, 1, WB, GS>(g, it, rb, sh);
+        for (int s = 0; s < MAX_SLOTS; ++s) it.tok[s] = s < it.nt ? u.item_tok[item * MAX_SLOTS + s] : 0;
+        gateup_rows<NT, GemvTuneW<NT, WB>::RC, 1, WB, GS>(g, it, rb, sh);
+    }
     TRACE(a, 1, 2);
 }
 
@@ -408,25 +419,63 @@ GemvArgs gemv_view(const coli_moe_layer &L, int T, const WsLayout &lay, char *ws
     return g;
 }
 
+// Workgroups of 256 threads of one kernel that fit on the current device at
+// once (its occupancy per CU times the CUs), queried once per (device,
+// kernel); 0 if the query fails.
+template <typename K>
+int resident_wg(K kernel)
+{
+    static std::mutex mu;
+    static std::map<std::pair<int, const void *>, int> cache;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    const auto key = std::make_pair(dev, reinterpret_cast<const void *>(kernel));
+    std::lock_guard<std::mutex> lock(mu);
+    const auto it = cache.find(key);
+    if (it != cache.end()) return it->second;
+    int ncu = 0, per_cu = 0;
+    if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 256, 0) != hipSuccess || ncu <= 0 || per_cu <= 0)
+        return 0;
+    cache[key] = ncu * per_cu;
+    return ncu * per_cu;
+}
+
+// Routed workgroups of the gate/up launch: at most one per routed unit a
+// batch can have (units_max) and, past that, no more than fit on the device
+// beside the nsh shared-expert ones (res: resident workgroups, 0 unknown).
+inline int sel_routed_wg(int res, int nsh, int units_max)
+{
+    int nrwg = units_max;
+    if (res > nsh && res - nsh < nrwg) nrwg = res - nsh;
+    return nrwg < 1 ? 1 : nrwg;
+}
+
+#define COLI_SEL_LAUNCH(KERN)                                                                                   \
+    do {                                                                                                        \
+        const int nrwg_ = sel_routed_wg(resident_wg(KERN), nsh, units_max);                                     \
+        COLI_LAUNCH(KERN, dim3((unsigned)(nsh + nrwg_)), dim3(256), 0, s, a, g, nsh, nrwg_);                     \
+        return hipGetLastError();                                                                               \
+    } while (0)
+
 // keys per lane of the selection: E <= 64 * KPL
 template <int NT, int WB, bool GS = false>
-hipError_t launch_sel_nt(int E, dim3 grid, const SelGuArgs &a, const GemvArgs &g, int nsh, hipStream_t s)
+hipError_t launch_sel_nt(int E, const SelGuArgs &a, const GemvArgs &g, int nsh, int units_max, hipStream_t s)
 {
-    if (E <= 64) COLI_LAUNCH((k_select_gateup<NT, 1, WB, GS>), grid, dim3(256), 0, s, a, g, nsh);
-    else if (E <= 128) COLI_LAUNCH((k_select_gateup<NT, 2, WB, GS>), grid, dim3(256), 0, s, a, g, nsh);
-    else if (E <= 256) COLI_LAUNCH((k_select_gateup<NT, 4, WB, GS>), grid, dim3(256), 0, s, a, g, nsh);
-    else COLI_LAUNCH((k_select_gateup<NT, 8, WB, GS>), grid, dim3(256), 0, s, a, g, nsh);
-    return hipGetLastError();
+    if (E <= 64) COLI_SEL_LAUNCH((k_select_gateup<NT, 1, WB, GS>));
+    if (E <= 128) COLI_SEL_LAUNCH((k_select_gateup<NT, 2, WB, GS>));
+    if (E <= 256) COLI_SEL_LAUNCH((k_select_gateup<NT, 4, WB, GS>));
+    COLI_SEL_LAUNCH((k_select_gateup<NT, 8, WB, GS>));
 }
 
 template <int NT>
-hipError_t launch_sel_wb(const coli_moe_layer &L, dim3 grid, const SelGuArgs &a, const GemvArgs &g, int nsh,
+hipError_t launch_sel_wb(const coli_moe_layer &L, const SelGuArgs &a, const GemvArgs &g, int nsh, int units_max,
                          hipStream_t s)
 {
-    if (L.group_size) return launch_sel_nt<NT, 4, true>(L.E, grid, a, g, nsh, s);
-    if (L.weight_bits == 2) return launch_sel_nt<NT, 2>(L.E, grid, a, g, nsh, s);
-    return L.weight_bits == 8 ? launch_sel_nt<NT, 8>(L.E, grid, a, g, nsh, s)
-                              : launch_sel_nt<NT, 4>(L.E, grid, a, g, nsh, s);
+    if (L.group_size) return launch_sel_nt<NT, 4, true>(L.E, a, g, nsh, units_max, s);
+    if (L.weight_bits == 2) return launch_sel_nt<NT, 2>(L.E, a, g, nsh, units_max, s);
+    return L.weight_bits == 8 ? launch_sel_nt<NT, 8>(L.E, a, g, nsh, units_max, s)
+                              : launch_sel_nt<NT, 4>(L.E, a, g, nsh, units_max, s);
 }
 
 template <int NT, int RPU, int WB, bool GS = false>
@@ -489,11 +538,11 @@ hipError_t launch_decode_select_gateup(const coli_moe_layer &L, int T, const WsL
 #endif
     GemvArgs g = gemv_view(L, T, lay, ws);
     const int nrb = L.I / QK, nsh = L.has_shared ? nrb : 0;
-    const dim3 grid((unsigned)(nsh + (lay.max_items - L.has_shared) * nrb));
-    if (T <= 1) return launch_sel_wb<1>(L, grid, a, g, nsh, s);
-    if (T <= 2) return launch_sel_wb<2>(L, grid, a, g, nsh, s);
-    if (T <= 4) return launch_sel_wb<4>(L, grid, a, g, nsh, s);
-    return launch_sel_wb<8>(L, grid, a, g, nsh, s);
+    const int units_max = (lay.max_items - L.has_shared) * nrb;
+    if (T <= 1) return launch_sel_wb<1>(L, a, g, nsh, units_max, s);
+    if (T <= 2) return launch_sel_wb<2>(L, a, g, nsh, units_max, s);
+    if (T <= 4) return launch_sel_wb<4>(L, a, g, nsh, units_max, s);
+    return launch_sel_wb<8>(L, a, g, nsh, units_max, s);
 }
 
 hipError_t launch_decode_down_combine(const coli_moe_layer &L, int T, const WsLayout &lay, char *ws, float *y,
