@@ -7,6 +7,10 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <map>
+#include <mutex>
+#include <utility>
+
 #include "../../include/coli_moe.h"
 
 namespace coli {
@@ -33,6 +37,28 @@ KernelTimer *&kernel_timer();    // this thread's timer, nullptr outside a timed
             hipLaunchKernelGGL(kernel, grid, block, shmem, stream, __VA_ARGS__);                            \
         }                                                                                                   \
     } while (0)
+
+// Workgroups of 256 threads of one kernel that fit on the current device at
+// once (its occupancy per CU times the CUs), queried once per (device,
+// kernel); 0 if the query fails.
+template <typename K>
+int resident_wg_256(K kernel)
+{
+    static std::mutex mu;
+    static std::map<std::pair<int, const void *>, int> cache;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    const auto key = std::make_pair(dev, reinterpret_cast<const void *>(kernel));
+    std::lock_guard<std::mutex> lock(mu);
+    const auto it = cache.find(key);
+    if (it != cache.end()) return it->second;
+    int ncu = 0, per_cu = 0;
+    if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 256, 0) != hipSuccess || ncu <= 0 || per_cu <= 0)
+        return 0;
+    cache[key] = ncu * per_cu;
+    return ncu * per_cu;
+}
 
 constexpr int QK = 32;          // activation block width (Q8_0-style)
 constexpr int MAX_SLOTS = 8;    // token slots of one expert item on the GEMV path

@@ -31,10 +31,6 @@ __device__ unsigned long long *coli_sel_marks;
 #include "route_device.hpp"
 #include "internal.hpp"
 
-#include <map>
-#include <mutex>
-#include <utility>
-
 namespace coli {
 
 #ifdef COLI_TRACE
@@ -419,28 +415,6 @@ GemvArgs gemv_view(const coli_moe_layer &L, int T, const WsLayout &lay, char *ws
     return g;
 }
 
-// Workgroups of 256 threads of one kernel that fit on the current device at
-// once (its occupancy per CU times the CUs), queried once per (device,
-// kernel); 0 if the query fails.
-template <typename K>
-int resident_wg(K kernel)
-{
-    static std::mutex mu;
-    static std::map<std::pair<int, const void *>, int> cache;
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return 0;
-    const auto key = std::make_pair(dev, reinterpret_cast<const void *>(kernel));
-    std::lock_guard<std::mutex> lock(mu);
-    const auto it = cache.find(key);
-    if (it != cache.end()) return it->second;
-    int ncu = 0, per_cu = 0;
-    if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 256, 0) != hipSuccess || ncu <= 0 || per_cu <= 0)
-        return 0;
-    cache[key] = ncu * per_cu;
-    return ncu * per_cu;
-}
-
 // Routed workgroups of the gate/up launch: at most one per routed unit a
 // batch can have (units_max) and, past that, no more than fit on the device
 // beside the nsh shared-expert ones (res: resident workgroups, 0 unknown).
@@ -453,7 +427,7 @@ inline int sel_routed_wg(int res, int nsh, int units_max)
 
 #define COLI_SEL_LAUNCH(KERN)                                                                                   \
     do {                                                                                                        \
-        const int nrwg_ = sel_routed_wg(resident_wg(KERN), nsh, units_max);                                     \
+        const int nrwg_ = sel_routed_wg(resident_wg_256(KERN), nsh, units_max);                                     \
         COLI_LAUNCH(KERN, dim3((unsigned)(nsh + nrwg_)), dim3(256), 0, s, a, g, nsh, nrwg_);                     \
         return hipGetLastError();                                                                               \
     } while (0)
