@@ -568,17 +568,17 @@ __device__ __forceinline__ void stage_pass(const StageLds<NM, WB> &sm, int m, do
 // FULL: the K blocks fill whole stages (nblk % KS == 0), so a stage's blocks
 // need no bounds tests and the scheduler sees a stage as straight-line code.
 //
-// Two gate/up tile forms. Paired waves (gateup_tile1): wave w runs matrix
+// Two gate/up tile forms. Paired waves (gateup_tile_paired): wave w runs matrix
 // w & 1 (0 gate, 1 up) of row tile rg * GU_RT + (w >> 1), so each wave holds
 // one matrix's accumulators and the four waves still share one stage of
 // activations; at the end the gate wave hands its g values to its up partner
-// through LDS. Both matrices per wave (gateup_tile2): four row tiles per
+// through LDS. Both matrices per wave (gateup_tile_both): four row tiles per
 // workgroup, each wave running the gate pass, then the up pass of a stage.
 constexpr int GU_RT = WAVES / 2;   // row tiles per gate/up workgroup of paired waves
 
 template <bool FULL, bool NARROW, int WB>
-__device__ __forceinline__ void gateup_tile1(const GroupedArgs &a, StageLds<1, WB> &sm, int e, int p0, int np, int rt,
-                                             int mat, bool rows_ok)
+__device__ __forceinline__ void gateup_tile_paired(const GroupedArgs &a, StageLds<1, WB> &sm, int e, int p0,
+                                                   int np, int rt, int mat, bool rows_ok)
 {
     constexpr int NACC = TileShape<NARROW>::NACC, KS = stage_blocks<WB>(), NXL = x_loads<WB>();
     const int n_rt = a.I / QK;
@@ -688,8 +688,8 @@ __device__ __forceinline__ void gateup_tile1(const GroupedArgs &a, StageLds<1, W
 // Per stage: gate pass, then up pass, each wave holding both matrices of its
 // row tile.
 template <bool FULL, bool NARROW, int WB>
-__device__ __forceinline__ void gateup_tile2(const GroupedArgs &a, StageLds<2, WB> &sm, int e, int p0, int np, int rt,
-                                             bool rows_ok)
+__device__ __forceinline__ void gateup_tile_both(const GroupedArgs &a, StageLds<2, WB> &sm, int e, int p0,
+                                                 int np, int rt, bool rows_ok)
 {
     constexpr int NACC = TileShape<NARROW>::NACC, KS = stage_blocks<WB>(), NXL = x_loads<WB>();
     const int n_rt = a.I / QK;
@@ -824,13 +824,13 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) k
     if constexpr (gu_paired<WB>()) {
         const int rt = rg * GU_RT + (wave >> 1), mat = wave & 1;
         const bool rows_ok = rt < n_rt;                   // waves past the last row tile only stage activations
-        if (np <= 16) gateup_tile1<FULL, true, WB>(a, sm, e, p0, np, rt, mat, rows_ok);
-        else gateup_tile1<FULL, false, WB>(a, sm, e, p0, np, rt, mat, rows_ok);
+        if (np <= 16) gateup_tile_paired<FULL, true, WB>(a, sm, e, p0, np, rt, mat, rows_ok);
+        else gateup_tile_paired<FULL, false, WB>(a, sm, e, p0, np, rt, mat, rows_ok);
     } else {
         const int rt = rg * WAVES + wave;
         const bool rows_ok = rt < n_rt;
-        if (np <= 16) gateup_tile2<FULL, true, WB>(a, sm, e, p0, np, rt, rows_ok);
-        else gateup_tile2<FULL, false, WB>(a, sm, e, p0, np, rt, rows_ok);
+        if (np <= 16) gateup_tile_both<FULL, true, WB>(a, sm, e, p0, np, rt, rows_ok);
+        else gateup_tile_both<FULL, false, WB>(a, sm, e, p0, np, rt, rows_ok);
     }
 }
 
