@@ -232,6 +232,29 @@ def test_forward_glm_mtp_verify_T4_and_batch_invariance(glm_layer):
         assert np.array_equal(y1[0], y[t]), f"token {t} differs between T=4 and T=1"
 
 
+def test_forward_glm_T8_many_units(glm_layer):
+    """Eight independent tokens at GLM shape: a union of about 60 items, so
+    the gate/up launch's routed workgroups (no more than fit on the device)
+    each take several units of the union. Every pair and token against the
+    oracle, and each token equal to its own T=1 call."""
+    L, cache, W, b = glm_layer
+    x = S.tokens(S.TokenSpec(T=8, token_set=21, outlier_channels=61), S.GLM52.H, 0)
+    ws = api.workspace(L, 8)
+    say("forward GLM T=8 independent tokens")
+    y = api.moe_forward(L, dev(x), ws).cpu().numpy()
+    toks = _glm_oracle_tokens(cache, W, b, x)
+    union = len({int(e) for t in toks for e in t.idx})
+    frac = _check_pairs(S.GLM52, L, 8, ws, y, toks, cache)
+    y_o = np.stack([t.y for t in toks])
+    err = rel_err(y, y_o).max()
+    say(f"  union {union} of 64 picks, max rel {err:.2e}, bit-identical {np.mean(y == y_o):.4f}, h {frac:.4f}")
+    assert union > 40 and err <= TOL
+    ws1 = api.workspace(L, 1)
+    for t in range(8):
+        y1 = api.moe_forward(L, dev(x[t: t + 1]), ws1).cpu().numpy()
+        assert np.array_equal(y1[0], y[t]), f"token {t} differs between T=8 and T=1"
+
+
 def test_experts_teacher_forced_glm(glm_layer):
     """Stage-isolated: the expert stage fed the GPU's own Q8(x) and the
     oracle's routing; every integer boundary bit-exact."""
