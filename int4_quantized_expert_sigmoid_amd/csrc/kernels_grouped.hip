@@ -18,6 +18,12 @@
 // so the product sums exactly the block's 32 k whatever order the matrix
 // core uses inside a lane. Output element (row, pair) sits in lane
 // pair + 32*((row/4)&1), register (row/8)*4 + row%4.
+//
+// The down kernels of the row-scale formats (int4, int2, int8; whole
+// stages) swap the operands: pairs are the A rows and weight rows the B
+// columns, so each group of four registers holds 8 pairs in every lane and
+// a tile rescales only the groups its pairs fill (the pair-row form, at
+// stage_pass_pr).
 #include "device_common.hpp"
 #include "internal.hpp"
 
@@ -46,6 +52,7 @@ struct GroupedArgs {
     float *ye;
     int ntiles_max;            // tiles the grid covers
     int gsh;                   // group scales: log2(group / 32)
+    int pair_rows;             // down: whole-stage tiles of row-scale formats take the pair-row form
 };
 
 __device__ __forceinline__ v4i unpack8(uint2 w)
@@ -297,15 +304,21 @@ __device__ __forceinline__ void store_x(StageLds<NM, WB> &sm, int buf, const v4i
 template <int WB>
 __device__ __forceinline__ int d_pair(int lane) { return stage_blocks<WB>() == 8 ? (lane >> 1) : lane; }
 
-template <int NM, int WB>
+// Slot of pair p's factors in the pair-row form (below): the lane that reads
+// them, (lane & 15) + 16 * (lane >> 5), so the 16 lanes of one LDS access
+// read 16 different slots.
+__device__ __forceinline__ int pr_slot(int p) { return (p & 3) + 4 * ((p >> 3) & 3) + 16 * ((p >> 2) & 1); }
+
+template <int NM, int WB, bool PR = false>
 __device__ __forceinline__ void store_d(StageLds<NM, WB> &sm, int buf, v4f d, int np)
 {
     const int lane = threadIdx.x & 63;
     const int p = d_pair<WB>(lane), jp = stage_blocks<WB>() == 8 ? 2 * (lane & 1) : 0;
     if (p >= TILE_N) return;                     // int8: lanes 32-63 stage nothing
     const double v = p < np ? (int4_codes<WB>() ? 0.0625 : WB == 2 ? 0.015625 : 1.0) : 0.0;
-    sm.d[buf][jp][p] = v2d{(double)d[0] * v, (double)d[1] * v};
-    sm.d[buf][jp + 1][p] = v2d{(double)d[2] * v, (double)d[3] * v};
+    const int slot = PR ? pr_slot(p) : p;
+    sm.d[buf][jp][slot] = v2d{(double)d[0] * v, (double)d[1] * v};
+    sm.d[buf][jp + 1][slot] = v2d{(double)d[2] * v, (double)d[3] * v};
 }
 
 // Factors of blocks j and j+1 (j even) of the stage for pair n.
@@ -440,7 +453,7 @@ __device__ __forceinline__ double gs_term(double acc, int c, double f, double sg
 // times its f64 factor into acc (with group scales, each term times its
 // row's group scale; gsh: log2(group / 32)). m: the matrix's LDS slot; buf: the stage's
 // activation buffer; b0: its first block.
-template <bool FULL, bool NARROW, int NM, int WB, bool PIPE = false>
+template <bool FULL, bool NARROW, int NM, int WB>
 __device__ __forceinline__ void stage_pass(const StageLds<NM, WB> &sm, int m, double (&acc)[TileShape<NARROW>::NACC],
                                            int buf, int b0, int nblk, int gsh = 0)
 {
@@ -448,38 +461,7 @@ __device__ __forceinline__ void stage_pass(const StageLds<NM, WB> &sm, int m, do
     const int g0 = b0 >> gsh;                    // the stage's first group
     constexpr int KS = stage_blocks<WB>();
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    if constexpr (PIPE && FULL && !NARROW && WB == 4) {
-        // int4, whole stages: the LDS operands of the next block pair are
-        // read while the current pair's MFMAs and rescales run, so only a
-        // stage's first pair waits out an LDS round trip
-        const v16i zero = {};
-        const int n = lane & 31, half = lane >> 5;
-        const int sw = wsw<WB>(n), sx = xsw<WB>(n);
-        const char *wrow = reinterpret_cast<const char *>(&sm.w[wave][m][n][0]);
-        uint2 wa[2], wb[2];
-        v4i xa[2], xb[2];
-        v2d dq[2];
-        auto fetch = [&](int j, int slot) {        // half h: its 8 packed bytes of blocks j and j+1
-            wa[slot] = *reinterpret_cast<const uint2 *>(wrow + 16 * (j ^ sw) + 8 * half);
-            wb[slot] = *reinterpret_cast<const uint2 *>(wrow + 16 * ((j + 1) ^ sw) + 8 * half);
-            xa[slot] = sm.x[buf][n][(2 * j + half) ^ sx];
-            xb[slot] = sm.x[buf][n][(2 * j + 2 + half) ^ sx];
-            dq[slot] = read_d2<NM, WB>(sm, buf, n, j);
-        };
-        fetch(0, 0);
-#pragma unroll
-        for (int j = 0; j < KS; j += 2) {
-            const int cur = (j >> 1) & 1;
-            if (j + 2 < KS) fetch(j + 2, cur ^ 1);
-            __builtin_amdgcn_sched_barrier(0);   // keeps the next pair's reads above this pair's work
-            const v16i ca = __builtin_amdgcn_mfma_i32_32x32x32_i8(unpack8(wa[cur]), xa[cur], zero, 0, 0, 0);
-            const v16i cb = __builtin_amdgcn_mfma_i32_32x32x32_i8(unpack8(wb[cur]), xb[cur], zero, 0, 0, 0);
-#pragma unroll
-            for (int i = 0; i < 16; ++i) acc[i] = fma((double)ca[i], dq[cur][0], acc[i]);
-#pragma unroll
-            for (int i = 0; i < 16; ++i) acc[i] = fma((double)cb[i], dq[cur][1], acc[i]);
-        }
-    } else if constexpr (!NARROW) {
+    if constexpr (!NARROW) {
         const v16i zero = {};
         const int n = lane & 31, half = lane >> 5;
         const int sw = wsw<WB>(n), sx = xsw<WB>(n);
@@ -565,6 +547,99 @@ __device__ __forceinline__ void stage_pass(const StageLds<NM, WB> &sm, int m, do
     }
 }
 
+// Pair-row form (row-scale formats, whole stages). The tile's pairs are the
+// MFMA's A rows and the weight rows its B columns, so lane l holds weight
+// row l%32 and, in accumulator i, pair 8*(i/4) + 4*(l/32) + i%4: the four
+// accumulators of group g hold pairs 8g..8g+7 in every lane, and a tile of
+// np pairs keeps and rescales only its first G = ceil(np/8) groups, where
+// the pair-column form pays for 32 (or, at most 16 pairs, 16) pair slots.
+// The factor of accumulator i belongs to one pair per 16-lane row; lane
+// (i, row) reads that pair's factors from LDS and v_fmac_f64 takes them
+// with DPP row_newbcast:i, so the rescale stays one conversion and one f64
+// FMA per element and block, with the same rounding as the other form.
+//
+// Four accumulators of group I0/4: acc += f(lane I0+k of the row) * c, one
+// fused multiply-add each. The s_nop gives the two wait states a DPP
+// operand needs after a vector write of its register.
+template <int I0>
+__device__ __forceinline__ void fmac4_bcast(double &a0, double &a1, double &a2, double &a3, double f, double c0,
+                                            double c1, double c2, double c3)
+{
+    asm("s_nop 1\n\t"
+        "v_fmac_f64_dpp %0, %4, %5 row_newbcast:%9 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f64_dpp %1, %4, %6 row_newbcast:%10 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f64_dpp %2, %4, %7 row_newbcast:%11 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f64_dpp %3, %4, %8 row_newbcast:%12 row_mask:0xf bank_mask:0xf"
+        : "+v"(a0), "+v"(a1), "+v"(a2), "+v"(a3)
+        : "v"(f), "v"(c0), "v"(c1), "v"(c2), "v"(c3), "i"(I0), "i"(I0 + 1), "i"(I0 + 2), "i"(I0 + 3));
+}
+
+// The conversions of a group stay next to its FMAs (vector instructions may
+// not cross the barriers; memory and MFMA instructions may): converted
+// ahead, a whole result would hold 32 more registers.
+constexpr int PR_CROSS = 0x3FC;
+
+template <int G>
+__device__ __forceinline__ void rescale_pr(double (&acc)[4 * G], const v16i &c, double f)
+{
+    fmac4_bcast<0>(acc[0], acc[1], acc[2], acc[3], f, (double)c[0], (double)c[1], (double)c[2], (double)c[3]);
+    __builtin_amdgcn_sched_barrier(PR_CROSS);
+    if constexpr (G > 1) {
+        fmac4_bcast<4>(acc[4], acc[5], acc[6], acc[7], f, (double)c[4], (double)c[5], (double)c[6], (double)c[7]);
+        __builtin_amdgcn_sched_barrier(PR_CROSS);
+    }
+    if constexpr (G > 2) {
+        fmac4_bcast<8>(acc[8], acc[9], acc[10], acc[11], f, (double)c[8], (double)c[9], (double)c[10], (double)c[11]);
+        __builtin_amdgcn_sched_barrier(PR_CROSS);
+    }
+    if constexpr (G > 3) {
+        fmac4_bcast<12>(acc[12], acc[13], acc[14], acc[15], f, (double)c[12], (double)c[13], (double)c[14],
+                        (double)c[15]);
+        __builtin_amdgcn_sched_barrier(PR_CROSS);
+    }
+}
+
+// The lane index, opaque to the compiler: the epilogue's store addresses
+// derive from it, so they are not computed before the K loop and held in
+// registers through it.
+__device__ __forceinline__ int after_loop(int lane)
+{
+    __asm__ volatile("" : "+v"(lane));
+    return lane;
+}
+
+// Formats the pair-row form serves: one scale per weight row (with group
+// scales each block term carries its own, which rounds apart from the FMA).
+template <int WB> constexpr bool pr_form() { return WB == 4 || WB == 2 || WB == 8; }
+
+// Pair of accumulator i of this lane in the pair-row form.
+__device__ __forceinline__ int pr_pair(int i, int lane) { return 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3); }
+
+// One matrix over a whole stage in the pair-row form (G groups); the wave's
+// LDS slot holds one matrix (int4: the two 8-byte halves of each block).
+template <int G, int WB>
+__device__ __forceinline__ void stage_pass_pr(const StageLds<1, WB> &sm, double (&acc)[4 * G], int buf)
+{
+    constexpr int KS = stage_blocks<WB>();
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int n = lane & 31, half = lane >> 5;
+    const int sw = wsw<WB>(n), sx = xsw<WB>(n);
+    const int fs = (lane & 15) + 16 * half;      // pr_slot of the pair whose factors this lane reads
+    const v16i zero = {};
+#pragma unroll
+    for (int j = 0; j < KS; j += 2) {
+        v4i ua, ub;
+        w_pair<1, WB>(sm, wave, 0, n, half, sw, j, ua, ub);
+        const v4i x0 = sm.x[buf][n][(2 * j + half) ^ sx];
+        const v4i x1 = sm.x[buf][n][(2 * j + 2 + half) ^ sx];
+        const v2d dd = sm.d[buf][j >> 1][fs];
+        const v16i ca = __builtin_amdgcn_mfma_i32_32x32x32_i8(x0, ua, zero, 0, 0, 0);
+        const v16i cb = __builtin_amdgcn_mfma_i32_32x32x32_i8(x1, ub, zero, 0, 0, 0);
+        rescale_pr<G>(acc, ca, dd[0]);
+        rescale_pr<G>(acc, cb, dd[1]);
+    }
+}
+
 // FULL: the K blocks fill whole stages (nblk % KS == 0), so a stage's blocks
 // need no bounds tests and the scheduler sees a stage as straight-line code.
 //
@@ -630,7 +705,7 @@ __device__ __forceinline__ void gateup_tile_paired(const GroupedArgs &a, StageLd
             }
         }
         issue_fence();
-        if (rows_ok) stage_pass<FULL, NARROW, 1, WB, true>(sm, 0, acc, s & 1, s * KS, nblk, a.gsh);
+        if (rows_ok) stage_pass<FULL, NARROW, 1, WB>(sm, 0, acc, s & 1, s * KS, nblk, a.gsh);
         issue_fence();
         if (more) {
             if (rows_ok) {
@@ -834,11 +909,12 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) k
     }
 }
 
-template <bool FULL, bool NARROW, int WB>
+template <bool FULL, bool NARROW, int WB, int PRG = 0>
 __device__ __forceinline__ void down_tile(const GroupedArgs &a, StageLds<1, WB> &sm, int e, int p0, int np, int rt,
                                           bool rows_ok)
 {
-    constexpr int NACC = TileShape<NARROW>::NACC, KS = stage_blocks<WB>(), NXL = x_loads<WB>();
+    static_assert(PRG == 0 || (FULL && pr_form<WB>()), "the pair-row form takes row scales in whole stages");
+    constexpr int NACC = PRG ? 4 * PRG : TileShape<NARROW>::NACC, KS = stage_blocks<WB>(), NXL = x_loads<WB>();
     const int n_rt = a.H / QK;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int nblk = a.I / QK;
@@ -873,7 +949,7 @@ __device__ __forceinline__ void down_tile(const GroupedArgs &a, StageLds<1, WB> 
         if constexpr (GS) store_s<1, WB>(sm, 0, sn);
     }
     store_x<1, WB>(sm, 0, xn);
-    if (wave == 0) store_d<1, WB>(sm, 0, dn, np);
+    if (wave == 0) store_d<1, WB, PRG != 0>(sm, 0, dn, np);
     __syncthreads();
     for (int s = 0; s < nst; ++s) {
         const bool more = s + 1 < nst;
@@ -886,7 +962,11 @@ __device__ __forceinline__ void down_tile(const GroupedArgs &a, StageLds<1, WB> 
             }
         }
         issue_fence();
-        if (rows_ok) stage_pass<FULL, NARROW, 1, WB, true>(sm, 0, acc, s & 1, s * KS, nblk, a.gsh);
+        if constexpr (PRG) {
+            if (rows_ok) stage_pass_pr<PRG, WB>(sm, acc, s & 1);
+        } else {
+            if (rows_ok) stage_pass<FULL, NARROW, 1, WB>(sm, 0, acc, s & 1, s * KS, nblk, a.gsh);
+        }
         issue_fence();
         if (more) {
             if (rows_ok) {
@@ -894,9 +974,20 @@ __device__ __forceinline__ void down_tile(const GroupedArgs &a, StageLds<1, WB> 
                 if constexpr (GS) store_s<1, WB>(sm, 0, sn);
             }
             store_x<1, WB>(sm, (s + 1) & 1, xn);
-            if (wave == 0) store_d<1, WB>(sm, (s + 1) & 1, dn, np);
+            if (wave == 0) store_d<1, WB, PRG != 0>(sm, (s + 1) & 1, dn, np);
         }
         __syncthreads();
+    }
+    if constexpr (PRG) {                         // lane l: row l%32 of the tile, its pairs per accumulator
+        if (!rows_ok) return;
+        const int ln = after_loop(lane), r = ln & 31;
+        const double rs = (double)a.s_a[(long)e * a.H + (long)rt * QK + r];
+#pragma unroll
+        for (int i = 0; i < NACC; ++i) {
+            const int pn = pr_pair(i, ln);
+            if (pn < np) a.ye[(long)(p0 + pn) * a.H + (long)rt * QK + r] = (float)(rs * acc[i]);
+        }
+        return;
     }
     const int n = acc_pair<NARROW>(lane);
     if (!rows_ok || n >= np) return;
@@ -928,14 +1019,36 @@ __global__ void __launch_bounds__(256) k_down_mfma(GroupedArgs a)
     const int2 td = a.tiles[tile];
     const int e = td.x, p0 = td.y;
     const int np = min(TILE_N, a.expert_off[e + 1] - p0);
+    if constexpr (FULL && pr_form<WB>()) {
+        if (a.pair_rows) {                               // pair-row form, the tile's 8-pair groups
+            const int ng = (np + 7) >> 3;
+            if (ng == 1) down_tile<FULL, false, WB, 1>(a, sm, e, p0, np, rt, rows_ok);
+            else if (ng == 2) down_tile<FULL, false, WB, 2>(a, sm, e, p0, np, rt, rows_ok);
+            else if (ng == 3) down_tile<FULL, false, WB, 3>(a, sm, e, p0, np, rt, rows_ok);
+            else down_tile<FULL, false, WB, 4>(a, sm, e, p0, np, rt, rows_ok);
+            return;
+        }
+    }
     if (np <= 16) down_tile<FULL, true, WB>(a, sm, e, p0, np, rt, rows_ok);
     else down_tile<FULL, false, WB>(a, sm, e, p0, np, rt, rows_ok);
+}
+
+// The pair-row form wants other waves on each SIMD to issue while one waits
+// on its MFMA results; a launch smaller than one resident round of
+// workgroups (the dense MLP's few pair tiles) runs every wave alone on its
+// SIMD, where the pair-column form hides that wait better (the int8 dense
+// 64-token chunk's down launch: 92.7 us against 97.8 in the pair-row form).
+template <int WB>
+int down_pair_rows(unsigned grid)
+{
+    return (int)grid >= resident_wg_256(k_down_mfma<true, WB>) ? 1 : 0;
 }
 
 GroupedArgs make_args(const WsLayout &lay, char *ws, const coli_moe_layer &L)
 {
     GroupedArgs a;
     a.H = L.H; a.I = L.I;
+    a.pair_rows = 0;
     a.gsh = group_shift(L);
     a.ctrl = reinterpret_cast<const int *>(ws + lay.ctrl);
     a.tiles = reinterpret_cast<const int2 *>(ws + lay.tiles);
@@ -997,9 +1110,11 @@ hipError_t launch_down_grouped(const coli_moe_layer &L, int T, const WsLayout &l
     const dim3 grid((unsigned)(max_tiles(lay, L) * nrg));
     a.gsh = group_shift(L);
     // whole stages (I/32 a multiple of the stage's blocks, as at I = 2048)
-    // drop the per-block bounds tests; int4 then also reads LDS one block
-    // pair ahead
+    // drop the per-block bounds tests; the row-scale formats then take the
+    // pair-row form when the grid fills the device
     const int nblk = L.I / QK;
+    a.pair_rows = L.group_size ? 0 : L.weight_bits == 8 ? down_pair_rows<8>(grid.x)
+                : L.weight_bits == 2 ? down_pair_rows<2>(grid.x) : down_pair_rows<4>(grid.x);
     if (L.group_size) {
         if (nblk % stage_blocks<WB_GROUPS>() == 0) COLI_LAUNCH((k_down_mfma<true, WB_GROUPS>), grid, dim3(64 * WAVES), 0, s, a);
         else COLI_LAUNCH((k_down_mfma<false, WB_GROUPS>), grid, dim3(64 * WAVES), 0, s, a);
