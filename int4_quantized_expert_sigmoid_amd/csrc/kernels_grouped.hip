@@ -19,11 +19,11 @@
 // core uses inside a lane. Output element (row, pair) sits in lane
 // pair + 32*((row/4)&1), register (row/8)*4 + row%4.
 //
-// The down kernels of the row-scale formats (int4, int2, int8; whole
-// stages) swap the operands: pairs are the A rows and weight rows the B
-// columns, so each group of four registers holds 8 pairs in every lane and
-// a tile rescales only the groups its pairs fill (the pair-row form, at
-// stage_pass_pr).
+// The down kernels of the row-scale formats (int4, int2, int8) and the
+// paired gate/up waves of int4 and int8, in whole stages, swap the
+// operands: pairs are the A rows and weight rows the B columns, so each
+// group of four registers holds 8 pairs in every lane and a tile rescales
+// only the groups its pairs fill (the pair-row form, at stage_pass_pr).
 #include "device_common.hpp"
 #include "internal.hpp"
 
@@ -651,11 +651,12 @@ __device__ __forceinline__ void stage_pass_pr(const StageLds<1, WB> &sm, double 
 // workgroup, each wave running the gate pass, then the up pass of a stage.
 constexpr int GU_RT = WAVES / 2;   // row tiles per gate/up workgroup of paired waves
 
-template <bool FULL, bool NARROW, int WB>
+template <bool FULL, bool NARROW, int WB, int PRG = 0>
 __device__ __forceinline__ void gateup_tile_paired(const GroupedArgs &a, StageLds<1, WB> &sm, int e, int p0,
                                                    int np, int rt, int mat, bool rows_ok)
 {
-    constexpr int NACC = TileShape<NARROW>::NACC, KS = stage_blocks<WB>(), NXL = x_loads<WB>();
+    static_assert(PRG == 0 || (FULL && pr_form<WB>()), "the pair-row form takes row scales in whole stages");
+    constexpr int NACC = PRG ? 4 * PRG : TileShape<NARROW>::NACC, KS = stage_blocks<WB>(), NXL = x_loads<WB>();
     const int n_rt = a.I / QK;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int nblk = a.H / QK;
@@ -692,7 +693,7 @@ __device__ __forceinline__ void gateup_tile_paired(const GroupedArgs &a, StageLd
         if constexpr (GS) store_s<1, WB>(sm, 0, sn);
     }
     store_x<1, WB>(sm, 0, xn);
-    if (wave == 0) store_d<1, WB>(sm, 0, dn, np);
+    if (wave == 0) store_d<1, WB, PRG != 0>(sm, 0, dn, np);
     __syncthreads();
     for (int s = 0; s < nst; ++s) {
         const bool more = s + 1 < nst;
@@ -705,7 +706,11 @@ __device__ __forceinline__ void gateup_tile_paired(const GroupedArgs &a, StageLd
             }
         }
         issue_fence();
-        if (rows_ok) stage_pass<FULL, NARROW, 1, WB>(sm, 0, acc, s & 1, s * KS, nblk, a.gsh);
+        if constexpr (PRG) {
+            if (rows_ok) stage_pass_pr<PRG, WB>(sm, acc, s & 1);
+        } else {
+            if (rows_ok) stage_pass<FULL, NARROW, 1, WB>(sm, 0, acc, s & 1, s * KS, nblk, a.gsh);
+        }
         issue_fence();
         if (more) {
             if (rows_ok) {
@@ -713,7 +718,7 @@ __device__ __forceinline__ void gateup_tile_paired(const GroupedArgs &a, StageLd
                 if constexpr (GS) store_s<1, WB>(sm, 0, sn);
             }
             store_x<1, WB>(sm, (s + 1) & 1, xn);
-            if (wave == 0) store_d<1, WB>(sm, (s + 1) & 1, dn, np);
+            if (wave == 0) store_d<1, WB, PRG != 0>(sm, (s + 1) & 1, dn, np);
         }
         __syncthreads();
     }
@@ -722,6 +727,43 @@ __device__ __forceinline__ void gateup_tile_paired(const GroupedArgs &a, StageLd
     // wave of the same row tile (the next wave), whose lanes hold the same
     // (row, pair) elements.
     float *xg = reinterpret_cast<float *>(&sm.w[wave & ~1][0][0][0]);
+    if constexpr (PRG) {
+        // pair-row form: one row (lane % 32) and so one row scale per lane.
+        // The up wave leaves u in its own slot too, and one copy of the
+        // SwiGLU and Q8 code (a loop, not unrolled) serves every accumulator;
+        // each accumulator's pair spans the 32 lanes of a half, which take
+        // its Q8 block together.
+        static_assert(sizeof(sm.w[0]) >= 16 * 64 * sizeof(float), "g fits a wave's weight slot");
+        const int ln = after_loop(lane), r = ln & 31;
+        const long grow = (long)e * a.I + (long)rt * QK + r;
+        if (rows_ok) {
+            const double sc = (double)(mat ? a.s_b : a.s_a)[grow];
+            float *own = reinterpret_cast<float *>(&sm.w[wave][0][0][0]);
+#pragma unroll
+            for (int i = 0; i < NACC; ++i) own[i * 64 + ln] = (float)(sc * acc[i]);
+        }
+        __syncthreads();
+        if (!rows_ok || mat == 0) return;
+        const float *xu = reinterpret_cast<const float *>(&sm.w[wave][0][0][0]);
+#pragma unroll 1
+        for (int i = 0; i < NACC; ++i) {
+            const float gf = xg[i * 64 + ln], uf = xu[i * 64 + ln];
+            const float hv = (float)(silu_f64((double)gf) * (double)uf);
+            float amax = fmaxf(0.0f, fabsf(hv));
+#pragma unroll
+            for (int o = 16; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 32));
+            const int pn = pr_pair(i, ln);
+            if (pn < np) {
+                float d, id;
+                q8_scale(amax, d, id);
+                const long base = (long)(p0 + pn) * a.I + (long)rt * QK;
+                a.h[base + r] = hv;
+                a.hq[base + (r & ~7) + perm8(r & 7)] = (int8_t)round_clamp(__fmul_rn(hv, id), -127.0f, 127.0f);
+                if (r == 0) a.hs[(long)(p0 + pn) * n_rt + rt] = d;
+            }
+        }
+        return;
+    }
     if (rows_ok && mat == 0) {
 #pragma unroll
         for (int i = 0; i < NACC; ++i) {
@@ -875,18 +917,21 @@ __device__ __forceinline__ void gateup_tile_both(const GroupedArgs &a, StageLds<
 }
 
 // The form per weight format, as measured at the GLM-5.2 prefill shape:
-// int8 and group-scaled weights pair the waves (13-16% faster there), int4
-// and int2 keep both matrices per wave (4-6% faster there).
-template <int WB> constexpr bool gu_paired() { return WB == 8 || WB == WB_GROUPS; }
-template <int WB> constexpr int gu_row_tiles() { return gu_paired<WB>() ? GU_RT : WAVES; }
+// int8 and group-scaled weights pair the waves (13-16% faster there), int2
+// keeps both matrices per wave (4-6% faster there). int4 in whole stages
+// pairs the waves in the pair-row form (as fast as both matrices per wave
+// in the pair-column form, which in the pair-row form runs out of
+// registers); int4 in part-filled stages keeps both matrices per wave.
+template <bool FULL, int WB> constexpr bool gu_paired() { return WB == 8 || WB == WB_GROUPS || (FULL && WB == 4); }
+template <bool FULL, int WB> constexpr int gu_row_tiles() { return gu_paired<FULL, WB>() ? GU_RT : WAVES; }
 
-template <int WB> struct GuLds { typedef StageLds<gu_paired<WB>() ? 1 : 2, WB> type; };
+template <bool FULL, int WB> struct GuLds { typedef StageLds<gu_paired<FULL, WB>() ? 1 : 2, WB> type; };
 
 template <bool FULL, int WB>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) k_gateup_mfma(GroupedArgs a)
 {
-    __shared__ typename GuLds<WB>::type sm;
-    constexpr int RTW = gu_row_tiles<WB>();
+    __shared__ typename GuLds<FULL, WB>::type sm;
+    constexpr int RTW = gu_row_tiles<FULL, WB>();
     const int n_rt = a.I / QK;
     const int nrg = (n_rt + RTW - 1) / RTW;
     int tile, rg;
@@ -896,11 +941,19 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) k
     const int2 td = a.tiles[tile];
     const int e = td.x, p0 = td.y;
     const int np = min(TILE_N, a.expert_off[e + 1] - p0);
-    if constexpr (gu_paired<WB>()) {
+    if constexpr (gu_paired<FULL, WB>()) {
         const int rt = rg * GU_RT + (wave >> 1), mat = wave & 1;
         const bool rows_ok = rt < n_rt;                   // waves past the last row tile only stage activations
-        if (np <= 16) gateup_tile_paired<FULL, true, WB>(a, sm, e, p0, np, rt, mat, rows_ok);
-        else gateup_tile_paired<FULL, false, WB>(a, sm, e, p0, np, rt, mat, rows_ok);
+        if constexpr (FULL && pr_form<WB>()) {           // pair-row form, the tile's 8-pair groups
+            const int ng = (np + 7) >> 3;
+            if (ng == 1) gateup_tile_paired<FULL, false, WB, 1>(a, sm, e, p0, np, rt, mat, rows_ok);
+            else if (ng == 2) gateup_tile_paired<FULL, false, WB, 2>(a, sm, e, p0, np, rt, mat, rows_ok);
+            else if (ng == 3) gateup_tile_paired<FULL, false, WB, 3>(a, sm, e, p0, np, rt, mat, rows_ok);
+            else gateup_tile_paired<FULL, false, WB, 4>(a, sm, e, p0, np, rt, mat, rows_ok);
+        } else {
+            if (np <= 16) gateup_tile_paired<FULL, true, WB>(a, sm, e, p0, np, rt, mat, rows_ok);
+            else gateup_tile_paired<FULL, false, WB>(a, sm, e, p0, np, rt, mat, rows_ok);
+        }
     } else {
         const int rt = rg * WAVES + wave;
         const bool rows_ok = rt < n_rt;
@@ -1076,10 +1129,11 @@ hipError_t launch_gateup_grouped(const coli_moe_layer &L, int T, const WsLayout 
     a.q_a = L.gate_q; a.s_a = L.gate_s; a.q_b = L.up_q; a.s_b = L.up_s;
     a.act = reinterpret_cast<const int8_t *>(ws + lay.xq);
     a.act_s = reinterpret_cast<const float *>(ws + lay.xs);
-    const int rtw = (L.group_size || L.weight_bits == 8) ? GU_RT : WAVES;   // gu_row_tiles<WB>()
+    const int nblk = L.H / QK;
+    const bool int4_full = !L.group_size && L.weight_bits == 4 && nblk % stage_blocks<4>() == 0;
+    const int rtw = (L.group_size || L.weight_bits == 8 || int4_full) ? GU_RT : WAVES;   // gu_row_tiles<FULL, WB>()
     const int nrg = (L.I / QK + rtw - 1) / rtw;
     const dim3 grid((unsigned)(max_tiles(lay, L) * nrg));
-    const int nblk = L.H / QK;
     a.gsh = group_shift(L);
     if (L.group_size) {
         if (nblk % stage_blocks<WB_GROUPS>() == 0)
