@@ -70,27 +70,11 @@ __device__ __forceinline__ int tile_row(int i, int half) { return 8 * (i >> 2) +
 
 constexpr int N_XCD = 8;       // workgroups go round-robin over the 8 XCDs by index
 
-// Tile and row group of workgroup w. Tiles of one expert are consecutive in
-// the tile list and each re-reads that expert's rows; with nrg a multiple of
-// N_XCD, XCD x (w % 8 == x) owns row groups x, x + 8, ... and walks the
-// tiles in order for each, so the tiles that share rows run together behind
-// one L2 and the repeats hit there.
-__device__ __forceinline__ void tile_rg(int w, int nrg, int ntiles, int &tile, int &rg)
-{
-    if (nrg % N_XCD == 0) {
-        const int x = w % N_XCD, j = w / N_XCD;
-        rg = (j / ntiles) * N_XCD + x;
-        tile = j % ntiles;
-    } else {
-        tile = w / nrg;
-        rg = w % nrg;
-    }
-}
-
 // Tile-major order: with nrg a multiple of N_XCD, XCD x walks its row
 // groups x, x + 8, ... for one tile before the next tile, so a tile's
 // activation rows are read from memory once per XCD (then from its L2),
-// and the tiles of one expert still follow each other.
+// and the tiles of one expert still follow each other, so each re-reads
+// that expert's rows from the L2 a few workgroups after the one before.
 __device__ __forceinline__ void tile_rg_tm(int w, int nrg, int ntiles, int &tile, int &rg)
 {
     if (nrg % N_XCD == 0) {
@@ -935,7 +919,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) k
     const int n_rt = a.I / QK;
     const int nrg = (n_rt + RTW - 1) / RTW;
     int tile, rg;
-    tile_rg(blockIdx.x, nrg, a.ntiles_max, tile, rg);
+    tile_rg_tm(blockIdx.x, nrg, a.ntiles_max, tile, rg);
     if (tile >= a.ctrl[CTRL_N_TILES_GU]) return;          // uniform over the workgroup
     const int wave = threadIdx.x >> 6;
     const int2 td = a.tiles[tile];
