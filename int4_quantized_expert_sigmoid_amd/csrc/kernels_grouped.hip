@@ -52,7 +52,6 @@ struct GroupedArgs {
     float *ye;
     int ntiles_max;            // tiles the grid covers
     int gsh;                   // group scales: log2(group / 32)
-    int pair_rows;             // down: whole-stage tiles of row-scale formats take the pair-row form
 };
 
 __device__ __forceinline__ v4i unpack8(uint2 w)
@@ -184,7 +183,7 @@ __device__ __forceinline__ int4 as_i4(v4i v) { return make_int4(v[0], v[1], v[2]
 // rows l/8, l/8 + 8, ...: int4, block l % 8 of the stage; int8, half
 // (l % 8) / 4 of block l % 4 (rowb: bytes per row).
 template <int WB>
-__device__ __forceinline__ void load_w(typename WReg<WB>::type (&w)[4], int s, int nblk, const uint8_t *wrow, long rowb)
+__device__ __forceinline__ typename WReg<WB>::type load_w_row(int s, int nblk, const uint8_t *wrow, long rowb)
 {
     typedef typename WReg<WB>::type R;
     constexpr int KS = stage_blocks<WB>();
@@ -194,8 +193,14 @@ __device__ __forceinline__ void load_w(typename WReg<WB>::type (&w)[4], int s, i
                    : WB == 2 ? 8 * blk
                    : WB == WB_GROUPS ? 16 * blk + 8 * (c & 1)
                    : (c >> 2) * (rowb / 2) + 16 * blk;
+    return *reinterpret_cast<const R *>(wrow + off);
+}
+
+template <int WB>
+__device__ __forceinline__ void load_w(typename WReg<WB>::type (&w)[4], int s, int nblk, const uint8_t *wrow, long rowb)
+{
 #pragma unroll
-    for (int j = 0; j < 4; ++j) w[j] = *reinterpret_cast<const R *>(wrow + (long)(8 * j) * rowb + off);
+    for (int j = 0; j < 4; ++j) w[j] = load_w_row<WB>(s, nblk, wrow + (long)(8 * j) * rowb, rowb);
 }
 
 // Activation loads: 2 * KS lanes per pair row (16-byte chunk c of the
@@ -249,22 +254,25 @@ __device__ __forceinline__ void store_s(StageLds<NM, WB> &sm, int m, v2f sv)
     sm.sg[wave][m][k + 1][r] = (double)sv[1];
 }
 
+// Lane l's piece (chunk l % 8) of row n of slot (wave, m).
+template <int NM, int WB>
+__device__ __forceinline__ void store_w_row(StageLds<NM, WB> &sm, int wave, int m, int n, typename WReg<WB>::type w)
+{
+    const int k = threadIdx.x & 7;
+    if constexpr (WB == 2 || WB == WB_GROUPS) {   // 8-byte piece k: half k % 2 of chunk k / 2
+        char *row = reinterpret_cast<char *>(&sm.w[wave][m][n][0]);
+        *reinterpret_cast<v2i *>(row + 16 * ((k >> 1) ^ wsw<2>(n)) + 8 * (k & 1)) = w;
+    } else {
+        sm.w[wave][m][n][k ^ wsw<WB>(n)] = w;
+    }
+}
+
 template <int NM, int WB>
 __device__ __forceinline__ void store_w(StageLds<NM, WB> &sm, int m, const typename WReg<WB>::type (&w)[4])
 {
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int r8 = lane >> 3;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int n = 8 * j + r8;
-        if constexpr (WB == 2 || WB == WB_GROUPS) {   // 8-byte piece k = lane % 8: half k % 2 of chunk k / 2
-            const int k = lane & 7;
-            char *row = reinterpret_cast<char *>(&sm.w[wave][m][n][0]);
-            *reinterpret_cast<v2i *>(row + 16 * ((k >> 1) ^ wsw<2>(n)) + 8 * (k & 1)) = w[j];
-        } else {
-            sm.w[wave][m][n][(lane & 7) ^ wsw<WB>(n)] = w[j];
-        }
-    }
+    for (int j = 0; j < 4; ++j) store_w_row<NM, WB>(sm, wave, m, 8 * j + (lane >> 3), w[j]);
 }
 
 template <int NM, int WB>
@@ -1056,36 +1064,147 @@ __global__ void __launch_bounds__(256) k_down_mfma(GroupedArgs a)
     const int2 td = a.tiles[tile];
     const int e = td.x, p0 = td.y;
     const int np = min(TILE_N, a.expert_off[e + 1] - p0);
-    if constexpr (FULL && pr_form<WB>()) {
-        if (a.pair_rows) {                               // pair-row form, the tile's 8-pair groups
-            const int ng = (np + 7) >> 3;
-            if (ng == 1) down_tile<FULL, false, WB, 1>(a, sm, e, p0, np, rt, rows_ok);
-            else if (ng == 2) down_tile<FULL, false, WB, 2>(a, sm, e, p0, np, rt, rows_ok);
-            else if (ng == 3) down_tile<FULL, false, WB, 3>(a, sm, e, p0, np, rt, rows_ok);
-            else down_tile<FULL, false, WB, 4>(a, sm, e, p0, np, rt, rows_ok);
-            return;
-        }
+    if constexpr (FULL && pr_form<WB>()) {               // pair-row form, the tile's 8-pair groups
+        const int ng = (np + 7) >> 3;
+        if (ng == 1) down_tile<FULL, false, WB, 1>(a, sm, e, p0, np, rt, rows_ok);
+        else if (ng == 2) down_tile<FULL, false, WB, 2>(a, sm, e, p0, np, rt, rows_ok);
+        else if (ng == 3) down_tile<FULL, false, WB, 3>(a, sm, e, p0, np, rt, rows_ok);
+        else down_tile<FULL, false, WB, 4>(a, sm, e, p0, np, rt, rows_ok);
+    } else {
+        if (np <= 16) down_tile<FULL, true, WB>(a, sm, e, p0, np, rt, rows_ok);
+        else down_tile<FULL, false, WB>(a, sm, e, p0, np, rt, rows_ok);
     }
-    if (np <= 16) down_tile<FULL, true, WB>(a, sm, e, p0, np, rt, rows_ok);
-    else down_tile<FULL, false, WB>(a, sm, e, p0, np, rt, rows_ok);
 }
 
-// The pair-row form wants other waves on each SIMD to issue while one waits
-// on its MFMA results; a launch smaller than one resident round of
-// workgroups (the dense MLP's few pair tiles) runs every wave alone on its
-// SIMD, where the pair-column form hides that wait better (the int8 dense
-// 64-token chunk's down launch: 92.7 us against 97.8 in the pair-row form).
-template <int WB>
-int down_pair_rows(unsigned grid)
+// Quarter-tile form (down launches smaller than one resident round of
+// workgroups, such as the dense MLP's few pair tiles, and row-scale
+// formats): one 32-row tile per workgroup instead of four, so the launch has
+// four times the workgroups and waves. Wave w takes rows 16 * (w & 1) and
+// pairs 16 * (w >> 1) of the tile, 16 x 16, on v_mfma_i32_16x16x32_i8 (lane
+// l: row and pair l % 16, the 8 k of quarter q = l / 16; result rows
+// 4q..4q+3), so each lane rescales 4 elements per block: the same vector
+// work per tile as the other forms, spread over four waves. The 32 rows are
+// staged once for the workgroup, one chunk per thread, double-buffered in
+// wave slots 0 and 1 (read by two waves each), beside the activations and
+// factors as the other forms stage them. Blocks are summed in block order.
+template <bool FULL, int WB>
+__device__ __forceinline__ void stage_pass_quad(const StageLds<1, WB> &sm, double (&acc)[4], int buf, int b0, int nblk)
 {
-    return (int)grid >= resident_wg_256(k_down_mfma<true, WB>) ? 1 : 0;
+    constexpr int KS = stage_blocks<WB>();
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int pr = lane & 15, q = lane >> 4;
+    const int r = 16 * (wave & 1) + pr, p = 16 * (wave >> 1) + pr;   // A row, B pair of this lane
+    const int sw = wsw<WB>(r), sx = xsw<WB>(p);
+    const v4i zero = {};
+#pragma unroll
+    for (int j = 0; j < KS; j += 2) {
+        if (!FULL && b0 + j >= nblk) break;
+        const bool two = FULL || b0 + j + 1 < nblk;
+        const v2d dd = read_d2<1, WB>(sm, buf, p, j);
+        v4i c[2];
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+            const int blk = j + jj;
+            if (jj == 1 && !two) {
+                c[1] = zero;
+                break;
+            }
+            const char *xr = reinterpret_cast<const char *>(&sm.x[buf][p][(2 * blk + (q >> 1)) ^ sx]);
+            const long B = *reinterpret_cast<const long *>(xr + 8 * (q & 1));
+            c[jj] = __builtin_amdgcn_mfma_i32_16x16x32_i8(w_group<1, WB>(sm, buf, 0, r, sw, blk, q), B, zero, 0, 0, 0);
+        }
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+            if (jj == 1 && !two) break;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[i] = fma((double)c[jj][i], dd[jj], acc[i]);
+        }
+    }
+}
+
+template <bool FULL, int WB>
+__device__ __forceinline__ void down_tile_quad(const GroupedArgs &a, StageLds<1, WB> &sm, int e, int p0, int np, int rt)
+{
+    constexpr int KS = stage_blocks<WB>(), NXL = x_loads<WB>();
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, t = threadIdx.x;
+    const int nblk = a.I / QK;
+    const long rowb = (long)a.I * code_bits<WB>() / 8;
+    const uint8_t *wrow = a.q_a + ((long)e * a.H + (long)rt * QK + (t >> 3)) * rowb;   // this thread's row
+    const int8_t *xrow[NXL];
+#pragma unroll
+    for (int i = 0; i < NXL; ++i) xrow[i] = a.act + (long)(p0 + stage_pair<WB>(i, np)) * a.I;
+    const int pd = min(d_pair<WB>(lane), TILE_N - 1) < np ? min(d_pair<WB>(lane), TILE_N - 1) : 0;
+    const float *drow = a.act_s + (long)(p0 + pd) * nblk;             // used by wave 0
+    const bool vec_scales = nblk % 4 == 0;
+
+    double acc[4] = {0.0, 0.0, 0.0, 0.0};
+    const int nst = (nblk + KS - 1) / KS;
+    typename WReg<WB>::type wn;
+    v4i xn[NXL];
+    v4f dn = {};
+    load_x<WB>(xn, 0, nblk, xrow);
+    if (wave == 0) dn = load_d<WB>(0, nblk, drow, vec_scales);
+    wn = load_w_row<WB>(0, nblk, wrow, rowb);
+    store_w_row<1, WB>(sm, 0, 0, t >> 3, wn);
+    store_x<1, WB>(sm, 0, xn);
+    if (wave == 0) store_d<1, WB>(sm, 0, dn, np);
+    __syncthreads();
+    for (int s = 0; s < nst; ++s) {
+        const bool more = s + 1 < nst;
+        const int buf = s & 1;
+        if (more) {
+            load_x<WB>(xn, s + 1, nblk, xrow);
+            if (wave == 0) dn = load_d<WB>(s + 1, nblk, drow, vec_scales);
+            wn = load_w_row<WB>(s + 1, nblk, wrow, rowb);
+        }
+        issue_fence();
+        stage_pass_quad<FULL, WB>(sm, acc, buf, s * KS, nblk);
+        issue_fence();
+        if (more) {                              // the other buffers, last read before the previous barrier
+            store_w_row<1, WB>(sm, buf ^ 1, 0, t >> 3, wn);
+            store_x<1, WB>(sm, buf ^ 1, xn);
+            if (wave == 0) store_d<1, WB>(sm, buf ^ 1, dn, np);
+        }
+        __syncthreads();
+    }
+    const int n = 16 * (wave >> 1) + (lane & 15);                     // this lane's pair
+    if (n >= np) return;
+    const int r0 = rt * QK + 16 * (wave & 1) + 4 * (lane >> 4);      // its first row
+    float rs[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) rs[i] = a.s_a[(long)e * a.H + r0 + i];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) a.ye[(long)(p0 + n) * a.H + r0 + i] = (float)((double)rs[i] * acc[i]);
+}
+
+template <bool FULL, int WB>
+__global__ void __launch_bounds__(256) k_down_quad(GroupedArgs a)
+{
+    static_assert(pr_form<WB>(), "row scales only: group-scaled terms are formed apart");
+    __shared__ StageLds<1, WB> sm;
+    const int n_rt = a.H / QK;
+    int tile, rt;
+    tile_rg_tm(blockIdx.x, n_rt, a.ntiles_max, tile, rt);
+    if (tile >= a.ctrl[CTRL_N_TILES_GU]) return;          // uniform over the workgroup
+    const int2 td = a.tiles[tile];
+    const int e = td.x, p0 = td.y;
+    const int np = min(TILE_N, a.expert_off[e + 1] - p0);
+    down_tile_quad<FULL, WB>(a, sm, e, p0, np, rt);
+}
+
+// The quarter-tile form for a down launch smaller than one resident round of
+// the four-row-tile kernel (measured: the int8 dense 64-token chunk's down
+// launch, 96 workgroups of four row tiles, took 91.8 us).
+template <int WB>
+bool down_small(unsigned grid)
+{
+    return (int)grid < resident_wg_256(k_down_mfma<true, WB>);
 }
 
 GroupedArgs make_args(const WsLayout &lay, char *ws, const coli_moe_layer &L)
 {
     GroupedArgs a;
     a.H = L.H; a.I = L.I;
-    a.pair_rows = 0;
     a.gsh = group_shift(L);
     a.ctrl = reinterpret_cast<const int *>(ws + lay.ctrl);
     a.tiles = reinterpret_cast<const int2 *>(ws + lay.tiles);
@@ -1101,6 +1220,14 @@ GroupedArgs make_args(const WsLayout &lay, char *ws, const coli_moe_layer &L)
 int max_tiles(const WsLayout &lay, const coli_moe_layer &L)
 {
     return (lay.n_pairs + TILE_N - 1) / TILE_N + L.E + 1;
+}
+
+template <int WB>
+void launch_down_quad(const GroupedArgs &a, const coli_moe_layer &L, const WsLayout &lay, hipStream_t s)
+{
+    const dim3 grid((unsigned)(max_tiles(lay, L) * (L.H / QK)));
+    if ((L.I / QK) % stage_blocks<WB>() == 0) COLI_LAUNCH((k_down_quad<true, WB>), grid, dim3(64 * WAVES), 0, s, a);
+    else COLI_LAUNCH((k_down_quad<false, WB>), grid, dim3(64 * WAVES), 0, s, a);
 }
 
 } // namespace
@@ -1149,10 +1276,14 @@ hipError_t launch_down_grouped(const coli_moe_layer &L, int T, const WsLayout &l
     a.gsh = group_shift(L);
     // whole stages (I/32 a multiple of the stage's blocks, as at I = 2048)
     // drop the per-block bounds tests; the row-scale formats then take the
-    // pair-row form when the grid fills the device
+    // pair-row form. A grid smaller than one resident round takes the
+    // quarter-tile form (row scales).
     const int nblk = L.I / QK;
-    a.pair_rows = L.group_size ? 0 : L.weight_bits == 8 ? down_pair_rows<8>(grid.x)
-                : L.weight_bits == 2 ? down_pair_rows<2>(grid.x) : down_pair_rows<4>(grid.x);
+    if (!L.group_size) {
+        if (L.weight_bits == 8 && down_small<8>(grid.x)) { launch_down_quad<8>(a, L, lay, s); return hipGetLastError(); }
+        if (L.weight_bits == 2 && down_small<2>(grid.x)) { launch_down_quad<2>(a, L, lay, s); return hipGetLastError(); }
+        if (L.weight_bits == 4 && down_small<4>(grid.x)) { launch_down_quad<4>(a, L, lay, s); return hipGetLastError(); }
+    }
     if (L.group_size) {
         if (nblk % stage_blocks<WB_GROUPS>() == 0) COLI_LAUNCH((k_down_mfma<true, WB_GROUPS>), grid, dim3(64 * WAVES), 0, s, a);
         else COLI_LAUNCH((k_down_mfma<false, WB_GROUPS>), grid, dim3(64 * WAVES), 0, s, a);
