@@ -1086,7 +1086,8 @@ __global__ void __launch_bounds__(256) k_down_mfma(GroupedArgs a)
 // work per tile as the other forms, spread over four waves. The 32 rows are
 // staged once for the workgroup, one chunk per thread, double-buffered in
 // wave slots 0 and 1 (read by two waves each), beside the activations and
-// factors as the other forms stage them. Blocks are summed in block order.
+// factors as the other forms stage them, with two or four stages of loads
+// in flight (a few registers here). Blocks are summed in block order.
 template <bool FULL, int WB>
 __device__ __forceinline__ void stage_pass_quad(const StageLds<1, WB> &sm, double (&acc)[4], int buf, int b0, int nblk)
 {
@@ -1139,33 +1140,42 @@ __device__ __forceinline__ void down_tile_quad(const GroupedArgs &a, StageLds<1,
 
     double acc[4] = {0.0, 0.0, 0.0, 0.0};
     const int nst = (nblk + KS - 1) / KS;
-    typename WReg<WB>::type wn;
-    v4i xn[NXL];
-    v4f dn = {};
-    load_x<WB>(xn, 0, nblk, xrow);
-    if (wave == 0) dn = load_d<WB>(0, nblk, drow, vec_scales);
-    wn = load_w_row<WB>(0, nblk, wrow, rowb);
-    store_w_row<1, WB>(sm, 0, 0, t >> 3, wn);
-    store_x<1, WB>(sm, 0, xn);
-    if (wave == 0) store_d<1, WB>(sm, 0, dn, np);
+    // QD stages of loads in flight: register set k holds stage s (s % QD ==
+    // k) from its load until its store to LDS buffer s % 2, one iteration
+    // before its compute; the loop runs QD stages per pass, so that every
+    // register index is a constant. int8 stages are half as long as int4's
+    // and hold fewer registers, so they keep twice as many in flight.
+    constexpr int QD = WB == 8 ? 4 : 2;
+    typename WReg<WB>::type wn[QD];
+    v4i xn[QD][NXL];
+    v4f dn[QD] = {};
+    auto load = [&](int k, int st) {
+        load_x<WB>(xn[k], st, nblk, xrow);
+        if (wave == 0) dn[k] = load_d<WB>(st, nblk, drow, vec_scales);
+        wn[k] = load_w_row<WB>(st, nblk, wrow, rowb);
+    };
+    auto store = [&](int k, int b) {             // buffer b was last read before the previous barrier
+        store_w_row<1, WB>(sm, b, 0, t >> 3, wn[k]);
+        store_x<1, WB>(sm, b, xn[k]);
+        if (wave == 0) store_d<1, WB>(sm, b, dn[k], np);
+    };
+#pragma unroll
+    for (int k = 0; k < QD; ++k)
+        if (k < nst) load(k, k);
+    store(0, 0);
     __syncthreads();
-    for (int s = 0; s < nst; ++s) {
-        const bool more = s + 1 < nst;
-        const int buf = s & 1;
-        if (more) {
-            load_x<WB>(xn, s + 1, nblk, xrow);
-            if (wave == 0) dn = load_d<WB>(s + 1, nblk, drow, vec_scales);
-            wn = load_w_row<WB>(s + 1, nblk, wrow, rowb);
+    for (int s0 = 0; s0 < nst; s0 += QD) {
+#pragma unroll
+        for (int k = 0; k < QD; ++k) {
+            const int st = s0 + k;
+            if (st >= nst) break;
+            if (st + QD < nst) load(k, st + QD);     // set k: its stage st is in LDS already
+            issue_fence();
+            stage_pass_quad<FULL, WB>(sm, acc, k & 1, st * KS, nblk);
+            issue_fence();
+            if (st + 1 < nst) store((k + 1) % QD, (k + 1) & 1);
+            __syncthreads();
         }
-        issue_fence();
-        stage_pass_quad<FULL, WB>(sm, acc, buf, s * KS, nblk);
-        issue_fence();
-        if (more) {                              // the other buffers, last read before the previous barrier
-            store_w_row<1, WB>(sm, buf ^ 1, 0, t >> 3, wn);
-            store_x<1, WB>(sm, buf ^ 1, xn);
-            if (wave == 0) store_d<1, WB>(sm, buf ^ 1, dn, np);
-        }
-        __syncthreads();
     }
     const int n = 16 * (wave >> 1) + (lane & 15);                     // this lane's pair
     if (n >= np) return;
