@@ -19,8 +19,8 @@
 // core uses inside a lane. Output element (row, pair) sits in lane
 // pair + 32*((row/4)&1), register (row/8)*4 + row%4.
 //
-// The down kernels of the row-scale formats (int4, int2, int8) and the
-// paired gate/up waves of int4 and int8, in whole stages, swap the
+// The down kernels of the row-scale formats (int4, int2, int8) and their
+// paired gate/up waves, in whole stages, swap the
 // operands: pairs are the A rows and weight rows the B columns, so each
 // group of four registers holds 8 pairs in every lane and a tile rescales
 // only the groups its pairs fill (the pair-row form, at stage_pass_pr).
@@ -721,22 +721,31 @@ __device__ __forceinline__ void gateup_tile_paired(const GroupedArgs &a, StageLd
     float *xg = reinterpret_cast<float *>(&sm.w[wave & ~1][0][0][0]);
     if constexpr (PRG) {
         // pair-row form: one row (lane % 32) and so one row scale per lane.
-        // The up wave leaves u in its own slot too, and one copy of the
-        // SwiGLU and Q8 code (a loop, not unrolled) serves every accumulator;
-        // each accumulator's pair spans the 32 lanes of a half, which take
-        // its Q8 block together.
-        static_assert(sizeof(sm.w[0]) >= 16 * 64 * sizeof(float), "g fits a wave's weight slot");
+        // Each wave leaves its g or u values (after the row scale, f32) in an
+        // LDS area of its own, 16 x 64 floats: its weight slot, or with int2
+        // (whose weight slot is a quarter of that) a quarter of the
+        // activation buffers, free after the last stage's barrier. One copy
+        // of the SwiGLU and Q8 code (a loop, not unrolled) then serves every
+        // accumulator; each accumulator's pair spans the 32 lanes of a half,
+        // which take its Q8 block together.
+        constexpr bool IN_X = sizeof(sm.w[0]) < 16 * 64 * sizeof(float);
+        static_assert(!IN_X || sizeof(sm.x) >= WAVES * 16 * 64 * sizeof(float), "g and u fit the activation buffers");
+        auto area = [&](int wv) -> float * {
+            return IN_X ? reinterpret_cast<float *>(&sm.x[0][0][0]) + wv * 16 * 64
+                        : reinterpret_cast<float *>(&sm.w[wv][0][0][0]);
+        };
         const int ln = after_loop(lane), r = ln & 31;
         const long grow = (long)e * a.I + (long)rt * QK + r;
         if (rows_ok) {
             const double sc = (double)(mat ? a.s_b : a.s_a)[grow];
-            float *own = reinterpret_cast<float *>(&sm.w[wave][0][0][0]);
+            float *own = area(wave);
 #pragma unroll
             for (int i = 0; i < NACC; ++i) own[i * 64 + ln] = (float)(sc * acc[i]);
         }
         __syncthreads();
         if (!rows_ok || mat == 0) return;
-        const float *xu = reinterpret_cast<const float *>(&sm.w[wave][0][0][0]);
+        xg = area(wave & ~1);
+        const float *xu = area(wave);
 #pragma unroll 1
         for (int i = 0; i < NACC; ++i) {
             const float gf = xg[i * 64 + ln], uf = xu[i * 64 + ln];
@@ -909,12 +918,12 @@ __device__ __forceinline__ void gateup_tile_both(const GroupedArgs &a, StageLds<
 }
 
 // The form per weight format, as measured at the GLM-5.2 prefill shape:
-// int8 and group-scaled weights pair the waves (13-16% faster there), int2
-// keeps both matrices per wave (4-6% faster there). int4 in whole stages
-// pairs the waves in the pair-row form (as fast as both matrices per wave
-// in the pair-column form, which in the pair-row form runs out of
-// registers); int4 in part-filled stages keeps both matrices per wave.
-template <bool FULL, int WB> constexpr bool gu_paired() { return WB == 8 || WB == WB_GROUPS || (FULL && WB == 4); }
+// int8 and group-scaled weights pair the waves (13-16% faster there); int4
+// and int2 in whole stages pair the waves in the pair-row form (int4 as fast
+// as, int2 4% faster than, both matrices per wave in the pair-column form,
+// which in the pair-row form runs out of registers); int4 and int2 in
+// part-filled stages keep both matrices per wave.
+template <bool FULL, int WB> constexpr bool gu_paired() { return WB == 8 || WB == WB_GROUPS || (FULL && (WB == 4 || WB == 2)); }
 template <bool FULL, int WB> constexpr int gu_row_tiles() { return gu_paired<FULL, WB>() ? GU_RT : WAVES; }
 
 template <bool FULL, int WB> struct GuLds { typedef StageLds<gu_paired<FULL, WB>() ? 1 : 2, WB> type; };
@@ -1251,8 +1260,8 @@ hipError_t launch_gateup_grouped(const coli_moe_layer &L, int T, const WsLayout 
     a.act = reinterpret_cast<const int8_t *>(ws + lay.xq);
     a.act_s = reinterpret_cast<const float *>(ws + lay.xs);
     const int nblk = L.H / QK;
-    const bool int4_full = !L.group_size && L.weight_bits == 4 && nblk % stage_blocks<4>() == 0;
-    const int rtw = (L.group_size || L.weight_bits == 8 || int4_full) ? GU_RT : WAVES;   // gu_row_tiles<FULL, WB>()
+    const bool pr_full = !L.group_size && (L.weight_bits == 4 || L.weight_bits == 2) && nblk % stage_blocks<4>() == 0;
+    const int rtw = (L.group_size || L.weight_bits == 8 || pr_full) ? GU_RT : WAVES;   // gu_row_tiles<FULL, WB>()
     const int nrg = (L.I / QK + rtw - 1) / rtw;
     const dim3 grid((unsigned)(max_tiles(lay, L) * nrg));
     a.gsh = group_shift(L);
