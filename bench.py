@@ -300,7 +300,7 @@ def main():
     stage_avg = np.array([[ms for _, ms in d] for d in per_call]).mean(axis=0)
     del evs
     STAGES = names
-    i_gu = next(i for i, n in enumerate(names) if n in ("k_select_gateup", "k_gateup_mfma"))
+    i_gu = next(i for i, n in enumerate(names) if n in ("k_select_gateup", "k_gateup_mfma", "k_gateup_quad"))
     i_dn = next(i for i, n in enumerate(names) if n in ("k_down_combine", "k_down_gemv", "k_down_mfma", "k_down_quad"))
     gu_bytes_avg = float(np.mean([gateup_bytes[j] for (j, _, _, _) in calls]))
     dn_bytes_avg = float(np.mean([down_bytes[j] for (j, _, _, _) in calls]))
@@ -451,7 +451,7 @@ def bench_dense(args):
     # every launch of a gate/up or down kernel reads its whole matrices: the
     # token-GEMV kernels (T <= 8) or the grouped MFMA kernels (larger T, one
     # expert holding every token)
-    GU, DN = ("k_dense_gateup", "k_gateup_mfma"), ("k_dense_down", "k_down_mfma", "k_down_quad")
+    GU, DN = ("k_dense_gateup", "k_gateup_mfma", "k_gateup_quad"), ("k_dense_down", "k_down_mfma", "k_down_quad")
     k_gu = next(n for n in names if n in GU)
     ms_gu = float(np.mean([v for n, v in zip(names, kms) if n in GU]))
     ms_dn = float(np.mean([v for n, v in zip(names, kms) if n in DN]))

@@ -1211,6 +1211,165 @@ __global__ void __launch_bounds__(256) k_down_quad(GroupedArgs a)
     down_tile_quad<FULL, WB>(a, sm, e, p0, np, rt);
 }
 
+// Quarter-tile gate/up (launches smaller than one resident round of
+// workgroups, row-scale formats): one 32-row tile per workgroup, wave w
+// running matrix w & 1 (gate, up) for pairs 16 * (w >> 1) .. + 15 of the
+// tile, as the 16-pair form runs a narrow tile (two v_mfma_i32_16x16x32_i8
+// per block, rows 0-15 and 16-31; lane l: pair l % 16, rows 4q..4q+3 of
+// each, q = l / 16). Both matrices' 32 rows are staged once for the
+// workgroup (two pieces per thread), double-buffered in wave slots 0 and 1;
+// the gate waves leave g in slots 2 and 3 for the up waves, which take
+// SwiGLU and Q8(h) as the paired waves do.
+template <bool FULL, int WB>
+__device__ __forceinline__ void stage_pass_gq(const StageLds<2, WB> &sm, double (&acc)[8], int buf, int b0, int nblk,
+                                              int mat, int ph)
+{
+    constexpr int KS = stage_blocks<WB>();
+    const int lane = threadIdx.x & 63;
+    const int pr = lane & 15, q = lane >> 4, p = ph + pr;
+    const int r0 = pr, r1 = pr + 16;
+    const int sw0 = wsw<WB>(r0), sw1 = wsw<WB>(r1), sx = xsw<WB>(p);
+    const v4i zero = {};
+#pragma unroll
+    for (int j = 0; j < KS; j += 2) {
+        if (!FULL && b0 + j >= nblk) break;
+        const bool two = FULL || b0 + j + 1 < nblk;
+        const v2d dd = read_d2<2, WB>(sm, buf, p, j);
+        v4i c[2][2];
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+            const int blk = j + jj;
+            if (jj == 1 && !two) {
+                c[1][0] = zero;
+                c[1][1] = zero;
+                break;
+            }
+            const char *xr = reinterpret_cast<const char *>(&sm.x[buf][p][(2 * blk + (q >> 1)) ^ sx]);
+            const long B = *reinterpret_cast<const long *>(xr + 8 * (q & 1));
+            c[jj][0] = __builtin_amdgcn_mfma_i32_16x16x32_i8(w_group<2, WB>(sm, buf, mat, r0, sw0, blk, q), B, zero, 0, 0, 0);
+            c[jj][1] = __builtin_amdgcn_mfma_i32_16x16x32_i8(w_group<2, WB>(sm, buf, mat, r1, sw1, blk, q), B, zero, 0, 0, 0);
+        }
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+            if (jj == 1 && !two) break;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                acc[i] = fma((double)c[jj][0][i], dd[jj], acc[i]);
+                acc[4 + i] = fma((double)c[jj][1][i], dd[jj], acc[4 + i]);
+            }
+        }
+    }
+}
+
+template <bool FULL, int WB>
+__device__ __forceinline__ void gateup_tile_gq(const GroupedArgs &a, StageLds<2, WB> &sm, int e, int p0, int np, int rt)
+{
+    constexpr int KS = stage_blocks<WB>(), NXL = x_loads<WB>();
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, t = threadIdx.x;
+    const int mat = wave & 1, ph = 16 * (wave >> 1);
+    const int n_rt = a.I / QK;
+    const int nblk = a.H / QK;
+    const long rowb = (long)a.H * code_bits<WB>() / 8;
+    const long wr = ((long)e * a.I + (long)rt * QK + (t >> 3)) * rowb;    // this thread's row of both matrices
+    const uint8_t *wg = a.q_a + wr, *wu = a.q_b + wr;
+    const int8_t *xrow[NXL];
+#pragma unroll
+    for (int i = 0; i < NXL; ++i) xrow[i] = a.act + (long)a.pair_tok[p0 + stage_pair<WB>(i, np)] * a.H;
+    const int pd = min(d_pair<WB>(lane), TILE_N - 1) < np ? min(d_pair<WB>(lane), TILE_N - 1) : 0;
+    const float *drow = a.act_s + (long)a.pair_tok[p0 + pd] * nblk;   // used by wave 0
+    const bool vec_scales = nblk % 4 == 0;
+
+    double acc[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = 0.0;
+    const int nst = (nblk + KS - 1) / KS;
+    typename WReg<WB>::type wn[2];
+    v4i xn[NXL];
+    v4f dn = {};
+    auto load = [&](int st) {
+        load_x<WB>(xn, st, nblk, xrow);
+        if (wave == 0) dn = load_d<WB>(st, nblk, drow, vec_scales);
+        wn[0] = load_w_row<WB>(st, nblk, wg, rowb);
+        wn[1] = load_w_row<WB>(st, nblk, wu, rowb);
+    };
+    auto store = [&](int b) {                    // buffer b was last read before the previous barrier
+        store_w_row<2, WB>(sm, b, 0, t >> 3, wn[0]);
+        store_w_row<2, WB>(sm, b, 1, t >> 3, wn[1]);
+        store_x<2, WB>(sm, b, xn);
+        if (wave == 0) store_d<2, WB>(sm, b, dn, np);
+    };
+    load(0);
+    store(0);
+    __syncthreads();
+    for (int s = 0; s < nst; ++s) {
+        const bool more = s + 1 < nst;
+        if (more) load(s + 1);
+        issue_fence();
+        stage_pass_gq<FULL, WB>(sm, acc, s & 1, s * KS, nblk, mat, ph);
+        issue_fence();
+        if (more) store((s + 1) & 1);
+        __syncthreads();
+    }
+    // the gate waves leave g (f32, after the row scale) in slot 2 + pair half,
+    // [accumulator][lane]; the up wave of the same pairs reads it
+    float *xg = reinterpret_cast<float *>(&sm.w[2 + (wave >> 1)][0][0][0]);
+    static_assert(sizeof(sm.w[0]) >= 8 * 64 * sizeof(float), "g fits a spare weight slot");
+    const long rbase = (long)e * a.I + (long)rt * QK;
+    if (mat == 0) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) xg[i * 64 + lane] = (float)((double)a.s_a[rbase + acc_row<true>(i, lane)] * acc[i]);
+    }
+    __syncthreads();
+    if (mat == 0) return;
+    float hv[8];
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const float gf = xg[i * 64 + lane];
+        const float uf = (float)((double)a.s_b[rbase + acc_row<true>(i, lane)] * acc[i]);
+        hv[i] = (float)(silu_f64((double)gf) * (double)uf);
+        amax = fmaxf(amax, fabsf(hv[i]));
+    }
+    amax = fmaxf(amax, __shfl_xor(amax, 32));
+    amax = fmaxf(amax, __shfl_xor(amax, 16));
+    const int n = ph + (lane & 15);
+    if (n >= np) return;
+    float d, id;
+    q8_scale(amax, d, id);
+    const long base = (long)(p0 + n) * a.I + (long)rt * QK;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int r = acc_row<true>(i, lane);
+        a.h[base + r] = hv[i];
+        a.hq[base + (r & ~7) + perm8(r & 7)] = (int8_t)round_clamp(__fmul_rn(hv[i], id), -127.0f, 127.0f);
+    }
+    if ((lane >> 4) == 0) a.hs[(long)(p0 + n) * n_rt + rt] = d;
+}
+
+template <bool FULL, int WB>
+__global__ void __launch_bounds__(256) k_gateup_quad(GroupedArgs a)
+{
+    static_assert(pr_form<WB>(), "row scales only");
+    __shared__ StageLds<2, WB> sm;
+    const int n_rt = a.I / QK;
+    int tile, rt;
+    tile_rg_tm(blockIdx.x, n_rt, a.ntiles_max, tile, rt);
+    if (tile >= a.ctrl[CTRL_N_TILES_GU]) return;          // uniform over the workgroup
+    const int2 td = a.tiles[tile];
+    const int e = td.x, p0 = td.y;
+    const int np = min(TILE_N, a.expert_off[e + 1] - p0);
+    gateup_tile_gq<FULL, WB>(a, sm, e, p0, np, rt);
+}
+
+// The launched grid counts tile slots past the batch's tiles too (their
+// workgroups exit at once), so a grid of exactly one resident round still
+// leaves CUs without work.
+template <int WB>
+bool gateup_small(unsigned grid)
+{
+    return (int)grid <= resident_wg_256(k_gateup_mfma<true, WB>);
+}
+
 // The quarter-tile form for a down launch smaller than one resident round of
 // the four-row-tile kernel (measured: the int8 dense 64-token chunk's down
 // launch, 96 workgroups of four row tiles, took 91.8 us).
@@ -1242,6 +1401,14 @@ int max_tiles(const WsLayout &lay, const coli_moe_layer &L)
 }
 
 template <int WB>
+void launch_gateup_quad(const GroupedArgs &a, const coli_moe_layer &L, const WsLayout &lay, hipStream_t s)
+{
+    const dim3 grid((unsigned)(max_tiles(lay, L) * (L.I / QK)));
+    if ((L.H / QK) % stage_blocks<WB>() == 0) COLI_LAUNCH((k_gateup_quad<true, WB>), grid, dim3(64 * WAVES), 0, s, a);
+    else COLI_LAUNCH((k_gateup_quad<false, WB>), grid, dim3(64 * WAVES), 0, s, a);
+}
+
+template <int WB>
 void launch_down_quad(const GroupedArgs &a, const coli_moe_layer &L, const WsLayout &lay, hipStream_t s)
 {
     const dim3 grid((unsigned)(max_tiles(lay, L) * (L.H / QK)));
@@ -1265,6 +1432,12 @@ hipError_t launch_gateup_grouped(const coli_moe_layer &L, int T, const WsLayout 
     const int nrg = (L.I / QK + rtw - 1) / rtw;
     const dim3 grid((unsigned)(max_tiles(lay, L) * nrg));
     a.gsh = group_shift(L);
+    // a grid smaller than one resident round takes the quarter-tile form (row scales)
+    if (!L.group_size) {
+        if (L.weight_bits == 8 && gateup_small<8>(grid.x)) { launch_gateup_quad<8>(a, L, lay, s); return hipGetLastError(); }
+        if (L.weight_bits == 2 && gateup_small<2>(grid.x)) { launch_gateup_quad<2>(a, L, lay, s); return hipGetLastError(); }
+        if (L.weight_bits == 4 && gateup_small<4>(grid.x)) { launch_gateup_quad<4>(a, L, lay, s); return hipGetLastError(); }
+    }
     if (L.group_size) {
         if (nblk % stage_blocks<WB_GROUPS>() == 0)
             COLI_LAUNCH((k_gateup_mfma<true, WB_GROUPS>), grid, dim3(64 * WAVES), 0, s, a);

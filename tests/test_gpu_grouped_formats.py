@@ -218,9 +218,9 @@ def test_grouped_glm_prefill_T512(glm_f_prefill):
 @pytest.mark.parametrize("T", [9, 40, 77])
 def test_grouped_whole_stages_small_grid(fmt, T):
     """H = I = 256: whole stages in gate/up and down for every row-scale
-    format (int4 and int8 gate/up in paired pair-row waves), and a down
-    launch small enough for the quarter-tile kernel; every token and pair
-    against the oracle, and the timed call's launches name that kernel."""
+    format, in launches small enough for the quarter-tile kernels; every
+    token and pair against the oracle, and the timed call's launches name
+    those kernels."""
     spec = S.LayerSpec(H=256, I=256, E=16, top_k=2, **fmt)
     L, ref = device_layer(spec, 0, 0), OL.full_layer(spec, 0, 0)
     x = S.tokens(S.TokenSpec(T=T, token_set=990 + T), spec.H, 0)
@@ -230,6 +230,6 @@ def test_grouped_whole_stages_small_grid(fmt, T):
     ev = api.KernelEvents(16)
     y1 = api.moe_forward_timed(L, dev(x), api.workspace(L, T), ev).cpu().numpy()
     names = [n for n, _ in ev.durations_ms()]
-    assert any("k_down_quad" in n for n in names), names
+    assert any("k_gateup_quad" in n for n in names) and any("k_down_quad" in n for n in names), names
     assert np.array_equal(y, y1)
     _tiny_batch_check(spec, L, ref, x, ws, y, f"{label(spec)} whole stages T={T}")

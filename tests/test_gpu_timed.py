@@ -60,11 +60,11 @@ def test_timed_decode_launches(tiny, T):
 
 
 def test_timed_grouped_launches(tiny):
-    # a launch this small takes the quarter-tile down kernel (fewer workgroups
-    # than one resident round of the four-row-tile one)
+    # launches this small take the quarter-tile gate/up and down kernels
+    # (no more workgroups than one resident round of the larger-tile ones)
     x = S.tokens(S.TokenSpec(T=40, token_set=79), S.TINY.H, 0)
-    names = _check(tiny, x, COLI_PATH_GROUPED, ["k_gateup_mfma", "k_down_quad", "k_combine"])
-    assert names.index([n for n in names if "k_gateup_mfma" in n][0]) < \
+    names = _check(tiny, x, COLI_PATH_GROUPED, ["k_gateup_quad", "k_down_quad", "k_combine"])
+    assert names.index([n for n in names if "k_gateup_quad" in n][0]) < \
         names.index([n for n in names if "k_down_quad" in n][0])
 
 
