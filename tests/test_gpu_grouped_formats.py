@@ -233,3 +233,26 @@ def test_grouped_whole_stages_small_grid(fmt, T):
     assert any("k_gateup_quad" in n for n in names) and any("k_down_quad" in n for n in names), names
     assert np.array_equal(y, y1)
     _tiny_batch_check(spec, L, ref, x, ws, y, f"{label(spec)} whole stages T={T}")
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("fmt", [dict(weight_bits=4), dict(weight_bits=8), dict(weight_bits=2)], ids=fmt_id)
+def test_grouped_part_stages_large_grid(fmt):
+    """H = 320, I = 96 (part-filled stages in gate/up and down) with 256
+    experts and T = 6,000: grids past one resident round, so the larger-tile
+    kernels run in their part-filled-stage forms rather than the quarter-tile
+    ones; every token and pair against the oracle, and the timed call's
+    launches name those kernels."""
+    spec = S.LayerSpec(H=320, I=96, E=256, top_k=4, **fmt)
+    L, ref = device_layer(spec, 0, 0), OL.full_layer(spec, 0, 0)
+    T = 6000
+    x = S.tokens(S.TokenSpec(T=T, token_set=1990), spec.H, 0)
+    ws = api.workspace(L, T)
+    say(f"grouped {label(spec)} part-filled stages, large grid, T={T}")
+    y = api.moe_forward(L, dev(x), ws).cpu().numpy()
+    ev = api.KernelEvents(16)
+    y1 = api.moe_forward_timed(L, dev(x), api.workspace(L, T), ev).cpu().numpy()
+    names = [n for n, _ in ev.durations_ms()]
+    assert any("k_gateup_mfma" in n for n in names) and any("k_down_mfma" in n for n in names), names
+    assert np.array_equal(y, y1)
+    _tiny_batch_check(spec, L, ref, x, ws, y, f"{label(spec)} part-filled stages T={T}")
