@@ -217,6 +217,40 @@ __device__ __forceinline__ void load_x(v4i (&x)[x_loads<WB>()], int s, int nblk,
     for (int i = 0; i < x_loads<WB>(); ++i) x[i] = *reinterpret_cast<const v4i *>(xrow[i] + 32 * xb + 16 * (c & 1));
 }
 
+// Whole stages of the row-scale formats: a stream is a base that is the
+// same for the whole wave (the expert's matrix from the wave's row tile, or
+// the activations) plus the lane's 32-bit byte offset, and a stage moves the
+// base only, so the loads take scalar bases and one vector offset each and a
+// stage costs no vector address arithmetic. The bytes are load_w's and
+// load_x's without their clamps, which whole stages never need.
+template <int WB>
+__device__ __forceinline__ uint32_t w_lane_off(long rowb)
+{
+    const int lane = threadIdx.x & 63, c = lane & 7;
+    const long o = (long)(lane >> 3) * rowb + (WB == 8 ? (c >> 2) * (rowb / 2) + 16 * (c & 3) : (WB == 4 ? 16 : 8) * c);
+    return (uint32_t)o;
+}
+
+template <int WB>
+__device__ __forceinline__ void load_w_u(typename WReg<WB>::type (&w)[4], int s, const uint8_t *base, uint32_t off,
+                                         long rowb)
+{
+    typedef typename WReg<WB>::type R;
+    constexpr long SB = (WB == 2 ? 8 : 16) * stage_blocks<WB>();   // bytes of a row (int8: of a half) per stage
+    const uint8_t *sb = base + SB * s;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) w[j] = *reinterpret_cast<const R *>(sb + (long)(8 * j) * rowb + off);
+}
+
+template <int WB>
+__device__ __forceinline__ void load_x_u(v4i (&x)[x_loads<WB>()], int s, const int8_t *act,
+                                         const uint32_t (&off)[x_loads<WB>()])
+{
+    const int8_t *sb = act + (long)(32 * stage_blocks<WB>()) * s;
+#pragma unroll
+    for (int i = 0; i < x_loads<WB>(); ++i) x[i] = *reinterpret_cast<const v4i *>(sb + off[i]);
+}
+
 // Wave 0 loads the tile's scales, 4 blocks per lane: int4, pair l/2 and
 // blocks 4*(l&1).. of the stage; int8, pair l (lanes 0-31). A 16-byte load
 // when 4 | nblk, clamped in bounds.
@@ -662,6 +696,15 @@ __device__ __forceinline__ void gateup_tile_paired(const GroupedArgs &a, StageLd
     const int8_t *xrow[NXL];
 #pragma unroll
     for (int i = 0; i < NXL; ++i) xrow[i] = a.act + (long)a.pair_tok[p0 + stage_pair<WB>(i, np)] * a.H;
+    // whole stages of the row formats: scalar-based streams (rt, mat: the same in every lane of the wave)
+    constexpr bool U = FULL && pr_form<WB>();
+    const int rtu = __builtin_amdgcn_readfirstlane(min(rt, n_rt - 1)), matu = __builtin_amdgcn_readfirstlane(mat);
+    const uint8_t *wbase = (matu ? a.q_b : a.q_a) + ((long)e * a.I + (long)rtu * QK) * rowb;
+    const uint32_t woff = w_lane_off<WB>(rowb);
+    uint32_t xoff[NXL];
+#pragma unroll
+    for (int i = 0; i < NXL; ++i)
+        xoff[i] = (uint32_t)a.pair_tok[p0 + stage_pair<WB>(i, np)] * (uint32_t)a.H + 16u * (threadIdx.x & (stage_xc<WB>() - 1));
     const int pd = min(d_pair<WB>(lane), TILE_N - 1) < np ? min(d_pair<WB>(lane), TILE_N - 1) : 0;
     const float *drow = a.act_s + (long)a.pair_tok[p0 + pd] * nblk;   // used by wave 0
     const bool vec_scales = nblk % 4 == 0;
@@ -676,10 +719,12 @@ __device__ __forceinline__ void gateup_tile_paired(const GroupedArgs &a, StageLd
     typename WReg<WB>::type wn[4];
     v4i xn[NXL];
     v4f dn = {};
-    load_x<WB>(xn, 0, nblk, xrow);
+    if constexpr (U) load_x_u<WB>(xn, 0, a.act, xoff);
+    else load_x<WB>(xn, 0, nblk, xrow);
     if (wave == 0) dn = load_d<WB>(0, nblk, drow, vec_scales);
     if (rows_ok) {
-        load_w<WB>(wn, 0, nblk, wrow, rowb);
+        if constexpr (U) load_w_u<WB>(wn, 0, wbase, woff, rowb);
+        else load_w<WB>(wn, 0, nblk, wrow, rowb);
         if constexpr (GS) sn = load_s<WB>(0, a.gsh, srow, ngs);
         store_w<1, WB>(sm, 0, wn);
         if constexpr (GS) store_s<1, WB>(sm, 0, sn);
@@ -690,10 +735,12 @@ __device__ __forceinline__ void gateup_tile_paired(const GroupedArgs &a, StageLd
     for (int s = 0; s < nst; ++s) {
         const bool more = s + 1 < nst;
         if (more) {
-            load_x<WB>(xn, s + 1, nblk, xrow);
+            if constexpr (U) load_x_u<WB>(xn, s + 1, a.act, xoff);
+            else load_x<WB>(xn, s + 1, nblk, xrow);
             if (wave == 0) dn = load_d<WB>(s + 1, nblk, drow, vec_scales);
             if (rows_ok) {
-                load_w<WB>(wn, s + 1, nblk, wrow, rowb);
+                if constexpr (U) load_w_u<WB>(wn, s + 1, wbase, woff, rowb);
+                else load_w<WB>(wn, s + 1, nblk, wrow, rowb);
                 if constexpr (GS) sn = load_s<WB>(s + 1, a.gsh, srow, ngs);
             }
         }
@@ -982,6 +1029,15 @@ __device__ __forceinline__ void down_tile(const GroupedArgs &a, StageLds<1, WB> 
     const int8_t *xrow[NXL];
 #pragma unroll
     for (int i = 0; i < NXL; ++i) xrow[i] = a.act + (long)(p0 + stage_pair<WB>(i, np)) * a.I;
+    // whole stages of the row formats: scalar-based streams (rt: the same in every lane of the wave)
+    constexpr bool U = FULL && pr_form<WB>();
+    const int rtu = __builtin_amdgcn_readfirstlane(min(rt, n_rt - 1));
+    const uint8_t *wbase = a.q_a + ((long)e * a.H + (long)rtu * QK) * rowb;
+    const uint32_t woff = w_lane_off<WB>(rowb);
+    uint32_t xoff[NXL];
+#pragma unroll
+    for (int i = 0; i < NXL; ++i)
+        xoff[i] = (uint32_t)(p0 + stage_pair<WB>(i, np)) * (uint32_t)a.I + 16u * (threadIdx.x & (stage_xc<WB>() - 1));
     const int pd = min(d_pair<WB>(lane), TILE_N - 1) < np ? min(d_pair<WB>(lane), TILE_N - 1) : 0;
     const float *drow = a.act_s + (long)(p0 + pd) * nblk;             // used by wave 0
     const bool vec_scales = nblk % 4 == 0;
@@ -994,10 +1050,12 @@ __device__ __forceinline__ void down_tile(const GroupedArgs &a, StageLds<1, WB> 
     typename WReg<WB>::type wn[4];
     v4i xn[NXL];
     v4f dn = {};
-    load_x<WB>(xn, 0, nblk, xrow);
+    if constexpr (U) load_x_u<WB>(xn, 0, a.act, xoff);
+    else load_x<WB>(xn, 0, nblk, xrow);
     if (wave == 0) dn = load_d<WB>(0, nblk, drow, vec_scales);
     if (rows_ok) {
-        load_w<WB>(wn, 0, nblk, wrow, rowb);
+        if constexpr (U) load_w_u<WB>(wn, 0, wbase, woff, rowb);
+        else load_w<WB>(wn, 0, nblk, wrow, rowb);
         if constexpr (GS) sn = load_s<WB>(0, a.gsh, srow, ngs);
         store_w<1, WB>(sm, 0, wn);
         if constexpr (GS) store_s<1, WB>(sm, 0, sn);
@@ -1008,10 +1066,12 @@ __device__ __forceinline__ void down_tile(const GroupedArgs &a, StageLds<1, WB> 
     for (int s = 0; s < nst; ++s) {
         const bool more = s + 1 < nst;
         if (more) {
-            load_x<WB>(xn, s + 1, nblk, xrow);
+            if constexpr (U) load_x_u<WB>(xn, s + 1, a.act, xoff);
+            else load_x<WB>(xn, s + 1, nblk, xrow);
             if (wave == 0) dn = load_d<WB>(s + 1, nblk, drow, vec_scales);
             if (rows_ok) {
-                load_w<WB>(wn, s + 1, nblk, wrow, rowb);
+                if constexpr (U) load_w_u<WB>(wn, s + 1, wbase, woff, rowb);
+                else load_w<WB>(wn, s + 1, nblk, wrow, rowb);
                 if constexpr (GS) sn = load_s<WB>(s + 1, a.gsh, srow, ngs);
             }
         }
