@@ -217,7 +217,7 @@ __device__ __forceinline__ void load_x(v4i (&x)[x_loads<WB>()], int s, int nblk,
     for (int i = 0; i < x_loads<WB>(); ++i) x[i] = *reinterpret_cast<const v4i *>(xrow[i] + 32 * xb + 16 * (c & 1));
 }
 
-// Whole stages of the row-scale formats: a stream is a base that is the
+// Whole stages (the row-scale formats and group scales): a stream is a base that is the
 // same for the whole wave (the expert's matrix from the wave's row tile, or
 // the activations) plus the lane's 32-bit byte offset, and a stage moves the
 // base only, so the loads take scalar bases and one vector offset each and a
@@ -696,8 +696,8 @@ __device__ __forceinline__ void gateup_tile_paired(const GroupedArgs &a, StageLd
     const int8_t *xrow[NXL];
 #pragma unroll
     for (int i = 0; i < NXL; ++i) xrow[i] = a.act + (long)a.pair_tok[p0 + stage_pair<WB>(i, np)] * a.H;
-    // whole stages of the row formats: scalar-based streams (rt, mat: the same in every lane of the wave)
-    constexpr bool U = FULL && pr_form<WB>();
+    // whole stages: scalar-based streams (rt, mat: the same in every lane of the wave)
+    constexpr bool U = FULL && (pr_form<WB>() || WB == WB_GROUPS);
     const int rtu = __builtin_amdgcn_readfirstlane(min(rt, n_rt - 1)), matu = __builtin_amdgcn_readfirstlane(mat);
     const uint8_t *wbase = (matu ? a.q_b : a.q_a) + ((long)e * a.I + (long)rtu * QK) * rowb;
     const uint32_t woff = w_lane_off<WB>(rowb);
@@ -1029,8 +1029,8 @@ __device__ __forceinline__ void down_tile(const GroupedArgs &a, StageLds<1, WB> 
     const int8_t *xrow[NXL];
 #pragma unroll
     for (int i = 0; i < NXL; ++i) xrow[i] = a.act + (long)(p0 + stage_pair<WB>(i, np)) * a.I;
-    // whole stages of the row formats: scalar-based streams (rt: the same in every lane of the wave)
-    constexpr bool U = FULL && pr_form<WB>();
+    // whole stages: scalar-based streams (rt: the same in every lane of the wave)
+    constexpr bool U = FULL && (pr_form<WB>() || WB == WB_GROUPS);
     const int rtu = __builtin_amdgcn_readfirstlane(min(rt, n_rt - 1));
     const uint8_t *wbase = a.q_a + ((long)e * a.H + (long)rtu * QK) * rowb;
     const uint32_t woff = w_lane_off<WB>(rowb);
