@@ -235,6 +235,28 @@ def test_grouped_whole_stages_small_grid(fmt, T):
     _tiny_batch_check(spec, L, ref, x, ws, y, f"{label(spec)} whole stages T={T}")
 
 
+@pytest.mark.parametrize("fmt", [dict(group_size=32), dict(group_size=128)], ids=fmt_id)
+@pytest.mark.parametrize("T", [40, 77])
+def test_grouped_groups_whole_stages(fmt, T):
+    """H = I = 256 with group scales: whole stages in gate/up and down (the
+    stage loads addressed from a wave-wide base) on ragged tiles; every token
+    and pair against the oracle, bit-identical, and the timed call's launches
+    name the grouped kernels."""
+    spec = S.LayerSpec(H=256, I=256, E=16, top_k=2, **fmt)
+    L, ref = device_layer(spec, 0, 0), OL.full_layer(spec, 0, 0)
+    x = S.tokens(S.TokenSpec(T=T, token_set=2990 + T), spec.H, 0)
+    ws = api.workspace(L, T)
+    say(f"grouped {label(spec)} whole stages with group scales, T={T}")
+    y = api.moe_forward(L, dev(x), ws).cpu().numpy()
+    ev = api.KernelEvents(16)
+    y1 = api.moe_forward_timed(L, dev(x), api.workspace(L, T), ev).cpu().numpy()
+    names = [n for n, _ in ev.durations_ms()]
+    assert any("k_gateup_mfma" in n for n in names) and any("k_down_mfma" in n for n in names), names
+    assert np.array_equal(y, y1)
+    st = _tiny_batch_check(spec, L, ref, x, ws, y, f"{label(spec)} whole stages T={T}")
+    assert st["h_bit_identical"] == 1.0 and st["y_bit_identical"] == 1.0
+
+
 @pytest.mark.timeout(600)
 @pytest.mark.parametrize("fmt", [dict(weight_bits=4), dict(weight_bits=8), dict(weight_bits=2)], ids=fmt_id)
 def test_grouped_part_stages_large_grid(fmt):
